@@ -1,0 +1,168 @@
+"""CPU oracle for the routed MoE SwiGLU FFN forward pass (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the
+``grouped_gemm_amd`` package and its HIP library) never does.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, fp32 accumulation, one
+OpenMP loop over tokens). What each function follows is stated there and in
+the docstrings below. Parity status of every function: pinned by the
+``-m "not gpu"`` tests (brute-force dense fp64 loop, the E=1/k=1 dense
+SwiGLU FFN, invariants, and the e4m3 format's own definition).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-march=x86-64-v2", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.oracle_route.argtypes = [P, i64, i32, i32, P, P, P, P]
+        lib.oracle_forward_bf16.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i64]
+        lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                          P, i64, i32]
+        lib.oracle_mx_quantize.argtypes = [P, i64, i64, P, P]
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_float
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_mx_scale_exp.argtypes = [P, ctypes.c_int]
+        lib.oracle_mx_scale_exp.restype = ctypes.c_int
+        lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def route(topk_ids: np.ndarray, E: int):
+    """Stable counting sort of pairs p = t*k + j by expert.
+
+    Returns counts [E], offsets [E+1], sorted_to_pair [P] (-1 past
+    offsets[E]), pair_to_sorted [P] (-1 for dropped routes), all int32.
+    Prime Flash MoE, section 8: routing and sorting produce the per-expert
+    row order the grouped GEMMs consume (its `offs` group offsets, section 1).
+    """
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    P = T * k
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    s2p = np.zeros(max(P, 1), np.int32)
+    p2s = np.zeros(max(P, 1), np.int32)
+    _load().oracle_route(_p(ids), T, k, E, _p(counts), _p(offsets), _p(s2p), _p(p2s))
+    return counts, offsets, s2p[:P], p2s[:P]
+
+
+def forward_bf16(x, w1, w2, topk_ids, topk_weights, tokens=None):
+    """bf16 forward: out bf16 bits [T, D] (rows not in `tokens` stay 0).
+
+    x [T, D], w1 [E, 2H, D], w2 [E, D, H] as uint16 bf16 bits; ids int32
+    [T, k]; weights fp32 [T, k]. Prime Flash MoE, section 1.
+    """
+    x, w1, w2 = _c(x, np.uint16), _c(w1, np.uint16), _c(w2, np.uint16)
+    ids, wts = _c(topk_ids, np.int32), _c(topk_weights, np.float32)
+    T, D = x.shape
+    E, H2, D1 = w1.shape
+    H = H2 // 2
+    k = ids.shape[1]
+    assert D1 == D and w2.shape == (E, D, H) and ids.shape == wts.shape == (T, k)
+    out = np.zeros((T, D), np.uint16)
+    if tokens is None:
+        tok_p, n = None, T
+    else:
+        tok = _c(tokens, np.int64)
+        tok_p, n = _p(tok), tok.size
+    _load().oracle_forward_bf16(T, D, H, E, k, _p(x), _p(w1), _p(w2), _p(ids), _p(wts), _p(out),
+                                tok_p, n)
+    return out
+
+
+def mx_quantize(src: np.ndarray):
+    """MXQ along the last dim: (codes uint8 same shape, scales uint8 [..., K/32])."""
+    src = _c(src, np.float32)
+    K = src.shape[-1]
+    assert K % 32 == 0
+    rows = src.size // K if K else 0
+    codes = np.zeros(src.shape, np.uint8)
+    scales = np.zeros(src.shape[:-1] + (K // 32,), np.uint8)
+    _load().oracle_mx_quantize(_p(src), rows, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def forward_mx(xc, xs, w1c, w1s, w2c, w2s, topk_ids, topk_weights, tokens=None, requant=True):
+    """MX-fp8 forward: out bf16 bits [T, D]. Prime Flash MoE, section 7."""
+    arrs = [_c(a, np.uint8) for a in (xc, xs, w1c, w1s, w2c, w2s)]
+    xc, xs, w1c, w1s, w2c, w2s = arrs
+    ids, wts = _c(topk_ids, np.int32), _c(topk_weights, np.float32)
+    T, D = xc.shape
+    E, H2, _ = w1c.shape
+    H = H2 // 2
+    k = ids.shape[1]
+    assert xs.shape == (T, D // 32) and w1s.shape == (E, H2, D // 32)
+    assert w2c.shape == (E, D, H) and w2s.shape == (E, D, H // 32)
+    out = np.zeros((T, D), np.uint16)
+    if tokens is None:
+        tok_p, n = None, T
+    else:
+        tok = _c(tokens, np.int64)
+        tok_p, n = _p(tok), tok.size
+    _load().oracle_forward_mx(T, D, H, E, k, _p(xc), _p(xs), _p(w1c), _p(w1s), _p(w2c), _p(w2s),
+                              _p(ids), _p(wts), _p(out), tok_p, n, 1 if requant else 0)
+    return out
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_load().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(v)))
+
+
+def mx_scale_exp(block: np.ndarray) -> int:
+    b = _c(block, np.float32)
+    return int(_load().oracle_mx_scale_exp(_p(b), b.size))
+
+
+def f32_to_bf16(v: float) -> int:
+    return int(_load().oracle_f32_to_bf16(float(v)))

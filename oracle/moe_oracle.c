@@ -1,0 +1,292 @@
+/*
+ * CPU oracle for the routed MoE SwiGLU FFN forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library. It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * What it computes follows "Prime Flash MoE - Faster MoE Kernels optimized
+ * for Blackwell", section 1 "The computation": for each routed
+ * (token, expert) pair, gate|up = W1[e] x_t with W1 stored output-major and
+ * gate rows first, act = silu(gate) * up, y = W2[e] act, and the token's
+ * output is the routing-weighted sum of its experts' y. The page's naive
+ * per-expert loop (same section) fixes the gate-first split of W1's rows
+ * and that the routing weight multiplies the expert output. Accumulation
+ * is fp32 (the page's accumulators are fp32, section 5 "The two
+ * epilogues"), summing over the contraction index in ascending order; the
+ * result is rounded once to bf16, round-to-nearest-even.
+ *
+ * The MX-fp8 variant (same page, section 7 "The MXFP8 variant") takes e4m3
+ * codes with one e8m0 scale per 32 contiguous K elements, dequantizes them
+ * exactly, and requantizes the SwiGLU output per 32 along H before the
+ * down projection (section 7, "The epilogue also quantizes"). The scale
+ * rule (MXQ) is the plain reading of "Porting Block-Scaled GEMM Kernels
+ * from Blackwell to Rubin", section 6.2 (scale byte by a round-up
+ * conversion, then scale and convert to e4m3 with saturation):
+ *   amax = max |v| over the 32 values;
+ *   amax == 0      -> s = -127;
+ *   otherwise      -> s = the smallest integer with amax <= 448 * 2^s,
+ *                     clamped to [-127, 127];
+ *   scale byte     =  s + 127;
+ *   code_i         =  e4m3fn(v_i * 2^-s), round to nearest even, values
+ *                     beyond 448 in magnitude saturate to +-448.
+ *
+ * Route maps: a stable counting sort of the pairs p = t*k + j by expert
+ * (ascending p inside each expert). Ids outside [0, E) are dropped routes:
+ * they are not counted and contribute nothing.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------- scalar formats ---------- */
+
+float oracle_bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u); /* quiet NaN */
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; largest finite magnitude 1.75 * 2^8 = 448. */
+float oracle_e4m3_decode(uint8_t c) {
+    int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+    float mag;
+    if (ex == 15 && man == 7) return NAN;
+    if (ex == 0)
+        mag = ldexpf((float)man, -9);                 /* subnormal: man/8 * 2^-6 */
+    else
+        mag = ldexpf(1.0f + (float)man / 8.0f, ex - 7);
+    return sign ? -mag : mag;
+}
+
+/* Round v (finite fp32) to the nearest e4m3fn value, ties to an even
+ * mantissa, saturating to +-448; returns the code. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7e;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                        /* a = m * 2^e, m in [0.5, 1) */
+    int unb = e - 1;                     /* a in [2^unb, 2^(unb+1)) */
+    if (unb < -6) unb = -6;              /* subnormal range shares 2^-6's quantum */
+    double quantum = ldexp(1.0, unb - 3);
+    double q = nearbyint(a / quantum);   /* default rounding: nearest, ties to even */
+    double r = q * quantum;
+    if (r >= 448.0) return sign | 0x7e;  /* can only reach 448 exactly here */
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -6)) return sign | (uint8_t)(r / ldexp(1.0, -9));
+    frexp(r, &e);
+    int ex = e - 1;                      /* r in [2^ex, 2^(ex+1)) */
+    int man = (int)((r / ldexp(1.0, ex) - 1.0) * 8.0);
+    return sign | (uint8_t)(((ex + 7) << 3) | man);
+}
+
+/* MXQ scale exponent s for one block (see the header comment). */
+int oracle_mx_scale_exp(const float* v, int n) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) return -127;
+    int e;
+    double m = frexp((double)amax, &e);  /* amax = m * 2^e; 448 = 0.875 * 2^9 */
+    int s = e - 9;                       /* 448 * 2^s = 0.875 * 2^e */
+    if (m > 0.875) s += 1;
+    if (s < -127) s = -127;
+    if (s > 127) s = 127;
+    return s;
+}
+
+/* Quantize rows x K (K a multiple of 32) of fp32 to e4m3 codes + e8m0 bytes
+ * [rows, K/32], scale blocks of 32 contiguous values along K. */
+void oracle_mx_quantize(const float* src, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const float* v = src + r * K + b * 32;
+            int s = oracle_mx_scale_exp(v, 32);
+            scales[r * (K / 32) + b] = (uint8_t)(s + 127);
+            for (int i = 0; i < 32; ++i)
+                codes[r * K + b * 32 + i] = oracle_e4m3_encode(ldexpf(v[i], -s));
+        }
+    }
+}
+
+float oracle_mx_value(uint8_t code, uint8_t scale) {
+    return ldexpf(oracle_e4m3_decode(code), (int)scale - 127);
+}
+
+/* ---------- route maps ---------- */
+
+/* counts[E], offsets[E+1] (exclusive prefix sum of counts), sorted_to_pair[P]
+ * (entries past offsets[E] are -1), pair_to_sorted[P] (-1 for dropped routes). */
+void oracle_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                  int32_t* offsets, int32_t* sorted_to_pair, int32_t* pair_to_sorted) {
+    int64_t P = T * (int64_t)k;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < P; ++p)
+        if (ids[p] >= 0 && ids[p] < E) counts[ids[p]]++;
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int32_t e = 0; e < E; ++e) next[e] = offsets[e];
+    for (int64_t i = 0; i < P; ++i) sorted_to_pair[i] = -1;
+    for (int64_t p = 0; p < P; ++p) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= E) {
+            pair_to_sorted[p] = -1;
+            continue;
+        }
+        int32_t i = next[e]++;
+        sorted_to_pair[i] = (int32_t)p;
+        pair_to_sorted[p] = i;
+    }
+    free(next);
+}
+
+/* ---------- forward ---------- */
+
+static float silu(float z) { return z / (1.0f + expf(-z)); }
+
+/* bf16 forward for the tokens listed in `tokens` (n_tok of them; NULL means
+ * all T tokens in order). out rows are written at the token's own row. */
+void oracle_forward_bf16(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint16_t* x,
+                         const uint16_t* w1, const uint16_t* w2, const int32_t* ids,
+                         const float* wts, uint16_t* out, const int64_t* tokens, int64_t n_tok) {
+    if (!tokens) n_tok = T;
+#pragma omp parallel
+    {
+        float* xv = (float*)malloc(sizeof(float) * (size_t)D);
+        float* gu = (float*)malloc(sizeof(float) * 2 * (size_t)H);
+        float* act = (float*)malloc(sizeof(float) * (size_t)H);
+        float* acc = (float*)malloc(sizeof(float) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < n_tok; ++it) {
+            int64_t t = tokens ? tokens[it] : it;
+            for (int32_t d = 0; d < D; ++d) {
+                xv[d] = oracle_bf16_to_f32(x[t * D + d]);
+                acc[d] = 0.0f;
+            }
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = ids[t * k + j];
+                if (e < 0 || e >= E) continue;
+                const uint16_t* W1 = w1 + (int64_t)e * 2 * H * D;
+                const uint16_t* W2 = w2 + (int64_t)e * D * H;
+                for (int32_t n = 0; n < 2 * H; ++n) {
+                    float s = 0.0f;
+                    for (int32_t d = 0; d < D; ++d) s += oracle_bf16_to_f32(W1[(int64_t)n * D + d]) * xv[d];
+                    gu[n] = s;
+                }
+                for (int32_t h = 0; h < H; ++h) act[h] = silu(gu[h]) * gu[H + h];
+                float w = wts[t * k + j];
+                for (int32_t d = 0; d < D; ++d) {
+                    float s = 0.0f;
+                    for (int32_t h = 0; h < H; ++h) s += oracle_bf16_to_f32(W2[(int64_t)d * H + h]) * act[h];
+                    acc[d] += w * s;
+                }
+            }
+            for (int32_t d = 0; d < D; ++d) out[t * D + d] = oracle_f32_to_bf16(acc[d]);
+        }
+        free(xv);
+        free(gu);
+        free(act);
+        free(acc);
+    }
+}
+
+/* MX-fp8 forward. x codes [T, D] + scales [T, D/32]; w1 codes [E, 2H, D] +
+ * scales [E, 2H, D/32]; w2 codes [E, D, H] + scales [E, D, H/32]. The SwiGLU
+ * output is requantized with MXQ per 32 along H when requant != 0 (the
+ * method's behaviour); requant == 0 keeps it in fp32 (used by a pin). */
+void oracle_forward_mx(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint8_t* xc,
+                       const uint8_t* xs, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
+                       const uint8_t* w2s, const int32_t* ids, const float* wts, uint16_t* out,
+                       const int64_t* tokens, int64_t n_tok, int32_t requant) {
+    if (!tokens) n_tok = T;
+    /* Both tables are exact: e4m3 values carry at most 4 significant bits and
+     * 2^(b-127) >= 2^-127, so every product lut * pow2 is an fp32 number
+     * (smallest magnitude 2^-9 * 2^-127 = 2^-136 > 2^-149). */
+    float lut[256], pow2[256];
+    for (int c = 0; c < 256; ++c) {
+        lut[c] = oracle_e4m3_decode((uint8_t)c);
+        pow2[c] = ldexpf(1.0f, c - 127);
+    }
+    const int32_t DB = D / 32, HB = H / 32;
+#pragma omp parallel
+    {
+        float* xv = (float*)malloc(sizeof(float) * (size_t)D);
+        float* gu = (float*)malloc(sizeof(float) * 2 * (size_t)H);
+        float* act = (float*)malloc(sizeof(float) * (size_t)H);
+        float* acc = (float*)malloc(sizeof(float) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < n_tok; ++it) {
+            int64_t t = tokens ? tokens[it] : it;
+            for (int32_t d = 0; d < D; ++d) {
+                xv[d] = lut[xc[t * D + d]] * pow2[xs[t * DB + d / 32]];
+                acc[d] = 0.0f;
+            }
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = ids[t * k + j];
+                if (e < 0 || e >= E) continue;
+                for (int32_t n = 0; n < 2 * H; ++n) {
+                    int64_t row = (int64_t)e * 2 * H + n;
+                    float s = 0.0f;
+                    for (int32_t d = 0; d < D; ++d)
+                        s += lut[w1c[row * D + d]] * pow2[w1s[row * DB + d / 32]] * xv[d];
+                    gu[n] = s;
+                }
+                for (int32_t h = 0; h < H; ++h) act[h] = silu(gu[h]) * gu[H + h];
+                if (requant) {
+                    for (int32_t b = 0; b < HB; ++b) {
+                        float* v = act + b * 32;
+                        int sc = oracle_mx_scale_exp(v, 32);
+                        for (int i = 0; i < 32; ++i)
+                            v[i] = lut[oracle_e4m3_encode(ldexpf(v[i], -sc))] * pow2[sc + 127];
+                    }
+                }
+                float w = wts[t * k + j];
+                for (int32_t d = 0; d < D; ++d) {
+                    int64_t row = (int64_t)e * D + d;
+                    float s = 0.0f;
+                    for (int32_t h = 0; h < H; ++h)
+                        s += lut[w2c[row * H + h]] * pow2[w2s[row * HB + h / 32]] * act[h];
+                    acc[d] += w * s;
+                }
+            }
+            for (int32_t d = 0; d < D; ++d) out[t * D + d] = oracle_f32_to_bf16(acc[d]);
+        }
+        free(xv);
+        free(gu);
+        free(act);
+        free(acc);
+    }
+}
+
+int oracle_num_threads(void) {
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
