@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE SwiGLU FFN forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode auto]
+
+One step = one whole forward pass (route -> GEMM1 + SwiGLU -> GEMM2 +
+routing weight -> combine) over one batch of seeded synthetic inputs that are
+resident in HBM before timing starts. W untimed steps, then K timed steps
+bracketed by torch.cuda.synchronize(); rank 0 (the only rank) prints one JSON
+line on stdout. The default workload is the decode shape (T=64 tokens,
+E=32 experts, top-8, D=6144, H=2048, bf16): one GPU's share of an 8-way
+expert-parallel deployment, bound by streaming the expert weights from HBM.
+
+Per-kernel durations come from HIP events that the library records on the
+pass's own stream at its stage boundaries (moe_ffn_forward_events) during
+the timed steps; the dominant kernel's roofline fraction uses its
+algorithmic bytes (weights of the experts hit + activations in and out) or
+flops (6*P*D*H split 4:2 over the two GEMMs) per launch.
+
+The CPU baseline is the oracle (oracle/, plain C, OpenMP) timed on a bounded
+sample of the same workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN fwd TFLOP/s + routed tokens/s; % of MFMA peak (prefill), % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+STAGES = {"split": ["route", "gemm1_swiglu", "gemm2_weight", "combine"],
+          "fused": ["route", "acc_fill", "fused_ffn", "acc_to_bf16"]}
+KERNEL_SOURCES = {"gemm1_swiglu": "gemm_bf16.hip", "gemm2_weight": "gemm_bf16.hip",
+                  "fused_ffn": "gemm_bf16.hip", "combine": "gemm_bf16.hip", "route": "route.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = decode")
+    ap.add_argument("--mode", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-baseline sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (PMC calibration)")
+    return ap.parse_args(argv)
+
+
+def hit_experts(ids: np.ndarray, E: int) -> int:
+    flat = ids.reshape(-1)
+    return int(np.unique(flat[(flat >= 0) & (flat < E)]).size)
+
+
+def kernel_work(cfg, mode, hit, dtype):
+    """Algorithmic bytes and flops per launch of each stage's kernel."""
+    T, D, H, P = cfg.T, cfg.D, cfg.H, cfg.P
+    e = 1 if dtype == "mxfp8" else 2                     # bytes per element of x, W, act
+    sc = (1.0 / 32) if dtype == "mxfp8" else 0.0         # e8m0 bytes per element
+    w1 = hit * 2 * H * D * (e + sc)
+    w2 = hit * D * H * (e + sc)
+    x = T * D * (e + sc)
+    act = P * H * (e + sc)
+    if mode == "split":
+        return {
+            "route": (P * 4 * 3 + cfg.E * 8, 0.0),
+            "gemm1_swiglu": (w1 + x + act, 4.0 * P * D * H),
+            "gemm2_weight": (w2 + act + P * D * 2, 2.0 * P * D * H),
+            "combine": (P * D * 2 + T * D * 2, 0.0),
+        }
+    return {
+        "route": (P * 4 * 3 + cfg.E * 8, 0.0),
+        "acc_fill": (T * D * 4, 0.0),
+        "fused_ffn": (w1 + w2 + x + T * D * 4, 6.0 * P * D * H),
+        "acc_to_bf16": (T * D * 6, 0.0),
+    }
+
+
+def source_digest(name: str) -> str:
+    path = os.path.join(ROOT, "grouped_gemm_amd", "csrc", KERNEL_SOURCES.get(name, ""))
+    if not os.path.isfile(path):
+        return ""
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current source of the kernel and the same workload; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.isfile(path):
+        return None
+    rec = json.load(open(path)).get(f"{workload}::{kernel}")
+    if not rec or rec.get("source_sha") != source_digest(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inputs, dtype, target_s):
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    order = np.arange(cfg.T)
+    n = min(cfg.T, 2)
+    while True:
+        tok = order[:n]
+        t0 = time.perf_counter()
+        if dtype == "bf16":
+            oracle.forward_bf16(inputs["x"], inputs["w1"], inputs["w2"], inputs["topk_ids"],
+                                inputs["topk_weights"], tokens=tok)
+        else:
+            oracle.forward_mx(*inputs["xq"], *inputs["w1q"], *inputs["w2q"], inputs["topk_ids"],
+                              inputs["topk_weights"], tokens=tok)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n == cfg.T:
+            break
+        n = min(cfg.T, max(n * 2, int(n * target_s / max(dt, 1e-3) * 0.9)))
+    flops = 6.0 * n * cfg.k * cfg.D * cfg.H
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens ({n * cfg.k} routed pairs) of the same workload, "
+                      f"{dt:.2f} s wall, fp32 accumulation",
+            "seconds": dt, "tokens_per_s": n / dt}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU expert-parallel layout is a design note, not built)", file=sys.stderr)
+        return 2
+    import torch
+    import moe_inputs as mi
+    import grouped_gemm_amd as g
+
+    cfg = mi.CONFIGS[args.config]
+    dtype = cfg.dtype
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name} inputs (seeded)")
+    host = {}
+    if dtype == "bf16":
+        d = mi.make_bf16(cfg, 0)
+        host.update(d)
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        w1 = torch.from_numpy(d["w1"].view(np.int16)).to(dev).view(torch.bfloat16)
+        w2 = torch.from_numpy(d["w2"].view(np.int16)).to(dev).view(torch.bfloat16)
+        scales = {}
+    else:
+        s = mi.make_mx_sources(cfg, 0)
+        host.update(topk_ids=s["topk_ids"], topk_weights=s["topk_weights"])
+        q = {}
+        for n in ("x", "w1", "w2"):
+            q[n] = g.moe_ffn_mx_quantize(torch.from_numpy(s[n]).to(dev))
+        torch.cuda.synchronize()
+        x, w1, w2 = q["x"][0], q["w1"][0], q["w2"][0]
+        scales = dict(x_scale=q["x"][1], w1_scale=q["w1"][1], w2_scale=q["w2"][1])
+        if not args.no_cpu_baseline:
+            host["xq"] = tuple(t.cpu().numpy() for t in q["x"])
+            host["w1q"] = tuple(t.cpu().numpy() for t in q["w1"])
+            host["w2q"] = tuple(t.cpu().numpy() for t in q["w2"])
+        del s
+    ids = torch.from_numpy(host["topk_ids"]).to(dev)
+    wts = torch.from_numpy(host["topk_weights"]).to(dev)
+    mode_id = g.moe_ffn_resolve_mode(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, args.mode)
+    mode = {g.MOE_FFN_FUSED: "fused", g.MOE_FFN_SPLIT: "split"}[mode_id]
+    nbytes = g.moe_ffn_workspace_bytes(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, mode)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=dev)
+
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    events = []
+    for _ in range(args.steps):
+        row = []
+        for _ in range(5):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            row.append(e.value)
+        events.append(row)
+
+    def step(ev=None):
+        g.moe_ffn_forward(x, w1, w2, ids, wts, out=out, mode=mode, workspace=ws, events=ev, **scales)
+
+    log(f"[bench] {cfg.name} mode={mode}: {args.warmup} warmup + {args.steps} timed steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+
+    names = STAGES[mode]
+    stage_ms = {n: 0.0 for n in names}
+    f = ctypes.c_float()
+    for row in events:
+        for j, n in enumerate(names):
+            assert hip.hipEventElapsedTime(ctypes.byref(f), row[j], row[j + 1]) == 0
+            stage_ms[n] += f.value / args.steps
+    for row in events:
+        for e in row:
+            hip.hipEventDestroy(e)
+
+    if args.copy_mib:
+        a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    hit = hit_experts(host["topk_ids"], cfg.E)
+    work = kernel_work(cfg, mode, hit, dtype)
+    dom = max((n for n in names if n != "route"), key=lambda n: stage_ms[n])
+    dbytes, dflops = work[dom]
+    dsec = stage_ms[dom] * 1e-3
+    peak_tf = MFMA_PEAK_TFLOPS[dtype]
+    intensity = dflops / dbytes if dbytes else 0.0
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    workload = f"{cfg.name} {dtype} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k}"
+    traffic = measured_traffic(dom, workload)
+    if intensity > ridge:
+        roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dbytes / dsec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = dbytes
+    roof["algorithmic_flops"] = dflops
+    roof["avg_launch_ms"] = stage_ms[dom]
+
+    tflops = cfg.flops / (ms * 1e-3) / 1e12
+    all_bytes = hit * 3 * cfg.H * cfg.D * (1 if dtype == "mxfp8" else 2) + 2 * cfg.T * cfg.D * 2
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8" if dtype == "mxfp8" else "bf16",
+        "data": "synthetic (seeded; routing, x and random-init expert weights of the stated shape)",
+        "config": {"workload": workload, "mode": mode, "tokens": cfg.T, "experts": cfg.E,
+                   "topk": cfg.k, "hidden": cfg.D, "ffn": cfg.H, "experts_hit": hit,
+                   "parallelism": "single GPU"},
+        "routed_tokens_per_s": cfg.P / (ms * 1e-3),
+        "tokens_per_s": cfg.T / (ms * 1e-3),
+        "pct_mfma_peak": tflops / peak_tf,
+        "effective_hbm_gbs": all_bytes / (ms * 1e-3) / 1e9,
+        "stage_ms": stage_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, host, dtype, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,222 @@
+"""MI355X (gfx950) routed MoE SwiGLU FFN forward pass: Python binding.
+
+A thin ctypes layer over ``libmoe_ffn.so`` whose functions carry the C ABI's
+names (include/moe_ffn.h). It only marshals arguments: torch tensors are
+passed as device pointers together with torch's current HIP stream; every
+step of the pass runs in the library's HIP kernels. There is no CPU or
+PyTorch fallback: if the library is missing, every call raises.
+
+    out = moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, mode="split")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_ffn.h")
+
+MOE_FFN_BF16, MOE_FFN_MXFP8 = 0, 1
+MOE_FFN_AUTO, MOE_FFN_FUSED, MOE_FFN_SPLIT = 0, 1, 2
+MOE_FFN_OK = 0
+MOE_FFN_EINVAL_SHAPE, MOE_FFN_EINVAL_PTR, MOE_FFN_EUNSUPPORTED = -1, -2, -3
+MOE_FFN_EWORKSPACE, MOE_FFN_EHIP = -4, -5
+
+_MODES = {"auto": MOE_FFN_AUTO, "fused": MOE_FFN_FUSED, "split": MOE_FFN_SPLIT}
+_DTYPES = {"bf16": MOE_FFN_BF16, "mxfp8": MOE_FFN_MXFP8}
+
+
+class MoeFfnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {moe_ffn_strerror(code)} ({code})")
+
+
+class moe_ffn_problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("x_scale", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmoe_ffn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m grouped_gemm_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        VP, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        PP = ctypes.POINTER(moe_ffn_problem)
+        lib.moe_ffn_workspace_bytes.argtypes = [PP, ctypes.c_int]
+        lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_ffn_validate.argtypes = [PP, ctypes.c_int]
+        lib.moe_ffn_validate.restype = ctypes.c_int
+        lib.moe_ffn_resolve_mode.argtypes = [PP, ctypes.c_int]
+        lib.moe_ffn_resolve_mode.restype = ctypes.c_int
+        lib.moe_ffn_forward.argtypes = [PP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP]
+        lib.moe_ffn_forward.restype = ctypes.c_int
+        lib.moe_ffn_forward_events.argtypes = [PP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP,
+                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        lib.moe_ffn_forward_events.restype = ctypes.c_int
+        lib.moe_ffn_route_workspace_bytes.argtypes = [I32, I32, I32]
+        lib.moe_ffn_route_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_ffn_route.argtypes = [VP, I32, I32, I32, VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
+        lib.moe_ffn_route.restype = ctypes.c_int
+        lib.moe_ffn_mx_quantize.argtypes = [VP, I64, I32, VP, VP, VP]
+        lib.moe_ffn_mx_quantize.restype = ctypes.c_int
+        lib.moe_ffn_strerror.argtypes = [ctypes.c_int]
+        lib.moe_ffn_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/moe_ffn.h declares."""
+    text = open(HEADER_PATH).read()
+    return re.findall(r"MOE_FFN_API\s+[\w\s\*]+?\b(moe_ffn_\w+)\s*\(", text)
+
+
+def moe_ffn_strerror(code: int) -> str:
+    return library().moe_ffn_strerror(int(code)).decode()
+
+
+def _mode(mode) -> int:
+    return _MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def _dtype(dtype) -> int:
+    return _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def make_problem(T, D, H, E, topk, dtype="bf16", x_scale=None, w1_scale=None, w2_scale=None,
+                 workspace=None) -> moe_ffn_problem:
+    p = moe_ffn_problem(int(T), int(D), int(H), int(E), int(topk), _dtype(dtype))
+    for name, t in (("x_scale", x_scale), ("w1_scale", w1_scale), ("w2_scale", w2_scale)):
+        setattr(p, name, t.data_ptr() if t is not None else None)
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    return p
+
+
+def moe_ffn_workspace_bytes(T, D, H, E, topk, dtype="bf16", mode="auto") -> int:
+    p = make_problem(T, D, H, E, topk, dtype)
+    return int(library().moe_ffn_workspace_bytes(ctypes.byref(p), _mode(mode)))
+
+
+def moe_ffn_validate(T, D, H, E, topk, dtype="bf16", mode="auto") -> int:
+    p = make_problem(T, D, H, E, topk, dtype)
+    return int(library().moe_ffn_validate(ctypes.byref(p), _mode(mode)))
+
+
+def moe_ffn_resolve_mode(T, D, H, E, topk, dtype="bf16", mode="auto") -> int:
+    p = make_problem(T, D, H, E, topk, dtype)
+    return int(library().moe_ffn_resolve_mode(ctypes.byref(p), _mode(mode)))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_scale=None,
+                    w1_scale=None, w2_scale=None, workspace=None, stream=None, events=None):
+    """out [T, D] bf16 = the routed MoE SwiGLU FFN forward pass.
+
+    bf16 path: x [T, D], w1 [E, 2H, D], w2 [E, D, H] torch.bfloat16.
+    MXFP8 path: x, w1, w2 are uint8 e4m3 codes and x_scale [T, D/32],
+    w1_scale [E, 2H, D/32], w2_scale [E, D, H/32] uint8 e8m0 scales.
+    topk_ids int32 [T, k] (int64 is converted), topk_weights fp32 [T, k].
+    events: optional 5 hipEvent_t handles (ints) recorded at the stage
+    boundaries (moe_ffn_forward_events).
+    """
+    mx = x.dtype == torch.uint8
+    if topk_ids.dtype != torch.int32:
+        topk_ids = topk_ids.to(torch.int32)
+    T, D = x.shape
+    E, H2, _ = w1.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
+    dtype = "mxfp8" if mx else "bf16"
+    p = make_problem(T, D, H2 // 2, E, k, dtype, x_scale, w1_scale, w2_scale)
+    lib = library()
+    m = _mode(mode)
+    if workspace is None:
+        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), m)
+        if nbytes == 0:
+            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m), "moe_ffn_forward")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel()
+    if events is None:
+        rc = lib.moe_ffn_forward(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                 topk_ids.data_ptr(), topk_weights.data_ptr(), out.data_ptr(), m,
+                                 _stream(stream))
+    else:
+        ev = (ctypes.c_void_p * 5)(*events)
+        rc = lib.moe_ffn_forward_events(ctypes.byref(p), x.data_ptr(), w1.data_ptr(),
+                                        w2.data_ptr(), topk_ids.data_ptr(),
+                                        topk_weights.data_ptr(), out.data_ptr(), m,
+                                        _stream(stream), ev, 5)
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_forward")
+    return out
+
+
+def moe_ffn_route(topk_ids, E, stream=None):
+    """(counts [E], offsets [E+1], sorted_to_pair [P], pair_to_sorted [P]) int32 on the GPU."""
+    if topk_ids.dtype != torch.int32:
+        topk_ids = topk_ids.to(torch.int32)
+    _check_cuda(topk_ids)
+    T, k = topk_ids.shape
+    P = T * k
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    s2p = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    p2s = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    lib = library()
+    nbytes = lib.moe_ffn_route_workspace_bytes(T, k, E)
+    if nbytes == 0:
+        raise MoeFfnError(MOE_FFN_EINVAL_SHAPE, "moe_ffn_route")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rc = lib.moe_ffn_route(topk_ids.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
+                           s2p.data_ptr(), p2s.data_ptr(), ws.data_ptr(), nbytes, _stream(stream))
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_route")
+    return counts, offsets, s2p[:P], p2s[:P]
+
+
+def moe_ffn_mx_quantize(src, stream=None):
+    """MX-fp8 quantization along the last dim: (codes uint8, scales uint8 [..., K/32])."""
+    if src.dtype != torch.float32:
+        raise ValueError("src must be float32")
+    _check_cuda(src)
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    scales = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
+    rc = library().moe_ffn_mx_quantize(src.data_ptr(), rows, K, codes.data_ptr(),
+                                       scales.data_ptr(), _stream(stream))
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_mx_quantize")
+    return codes, scales

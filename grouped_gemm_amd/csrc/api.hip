@@ -1,0 +1,272 @@
+// Host side of the C ABI declared in include/moe_ffn.h: validation,
+// workspace planning and kernel dispatch. No device memory is allocated
+// here; every buffer comes from the caller.
+#include "moe_ffn.h"
+
+#include <climits>
+
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxExperts = 8192;
+constexpr int kMaxTopk = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const moe_ffn_problem* p) {
+    if (!p) return MOE_FFN_EINVAL_PTR;
+    if (p->dtype != MOE_FFN_BF16 && p->dtype != MOE_FFN_MXFP8) return MOE_FFN_EUNSUPPORTED;
+    if (p->T < 0 || p->D < 1 || p->H < 1 || p->E < 1 || p->topk < 1) return MOE_FFN_EINVAL_SHAPE;
+    if (p->D % 128 || p->H % 128) return MOE_FFN_EINVAL_SHAPE;
+    if (p->E > kMaxExperts || p->topk > kMaxTopk || p->topk > p->E) return MOE_FFN_EINVAL_SHAPE;
+    if (static_cast<int64_t>(p->T) * p->topk > INT_MAX) return MOE_FFN_EINVAL_SHAPE;
+    return MOE_FFN_OK;
+}
+
+// AUTO: the fused pipeline while the split-K partial rows stay few (small
+// token counts), the split pipeline beyond. The threshold is the measured
+// crossover: with the current kernels the split pipeline is as fast or
+// faster at every measured size (128 to 1M routed pairs), so AUTO is SPLIT.
+constexpr int64_t kFusedMaxPairs = 0;
+
+int resolve(const moe_ffn_problem* p, int mode) {
+    if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
+    if (p->dtype == MOE_FFN_MXFP8) {
+        if (mode == MOE_FFN_FUSED) return MOE_FFN_EUNSUPPORTED;  // MX fused is not built
+        return MOE_FFN_SPLIT;
+    }
+    if (mode != MOE_FFN_AUTO) return mode;
+    return static_cast<int64_t>(p->T) * p->topk <= kFusedMaxPairs ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
+}
+
+struct RoutePlan {
+    int64_t P;
+    int32_t seg, S;
+    size_t tile_prefix, seg_counts, end;  // byte offsets from the route base
+};
+
+RoutePlan plan_route(int64_t T, int32_t k, int32_t E, size_t base) {
+    RoutePlan r;
+    r.P = T * k;
+    r.seg = 256;
+    r.S = static_cast<int32_t>((r.P + r.seg - 1) / r.seg);
+    while (static_cast<int64_t>(r.S) * E > (1 << 22)) {
+        r.seg *= 2;
+        r.S = static_cast<int32_t>((r.P + r.seg - 1) / r.seg);
+    }
+    size_t off = base;
+    r.tile_prefix = off;
+    off = align_up(off + sizeof(int32_t) * moe::kNumTileHeights * (E + 1));
+    r.seg_counts = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(r.S) * E);
+    r.end = off;
+    return r;
+}
+
+struct Plan {
+    int mode;
+    RoutePlan route;
+    size_t counts, offsets, s2p, p2s;
+    size_t act, act_s, ypair, acc32;
+    size_t total;
+};
+
+Plan make_plan(const moe_ffn_problem* p, int mode) {
+    Plan pl{};
+    pl.mode = mode;
+    const int64_t P = static_cast<int64_t>(p->T) * p->topk;
+    size_t off = 0;
+    pl.counts = off;
+    off = align_up(off + sizeof(int32_t) * p->E);
+    pl.offsets = off;
+    off = align_up(off + sizeof(int32_t) * (p->E + 1));
+    pl.s2p = off;
+    off = align_up(off + sizeof(int32_t) * P);
+    pl.p2s = off;
+    off = align_up(off + sizeof(int32_t) * P);
+    pl.route = plan_route(p->T, p->topk, p->E, off);
+    off = pl.route.end;
+    if (mode == MOE_FFN_SPLIT) {
+        const size_t act_elem = p->dtype == MOE_FFN_BF16 ? 2 : 1;
+        pl.act = off;
+        off = align_up(off + act_elem * static_cast<size_t>(P) * p->H);
+        if (p->dtype == MOE_FFN_MXFP8) {
+            pl.act_s = off;
+            off = align_up(off + static_cast<size_t>(P) * (p->H / 32));
+        }
+        pl.ypair = off;
+        off = align_up(off + 2 * static_cast<size_t>(P) * p->D);
+    } else {
+        pl.acc32 = off;
+        off = align_up(off + 4 * static_cast<size_t>(p->T) * p->D);
+    }
+    pl.total = off;
+    return pl;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_FFN_API const char* moe_ffn_strerror(int code) {
+    switch (code) {
+        case MOE_FFN_OK: return "ok";
+        case MOE_FFN_EINVAL_SHAPE: return "invalid shape";
+        case MOE_FFN_EINVAL_PTR: return "invalid (null or misaligned) pointer";
+        case MOE_FFN_EUNSUPPORTED: return "unsupported dtype or mode";
+        case MOE_FFN_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_FFN_EHIP: return "HIP launch error";
+        default: return "unknown error";
+    }
+}
+
+MOE_FFN_API int moe_ffn_validate(const moe_ffn_problem* p, int mode) {
+    int rc = check_shape(p);
+    if (rc != MOE_FFN_OK) return rc;
+    rc = resolve(p, mode);
+    return rc < 0 ? rc : MOE_FFN_OK;
+}
+
+MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode) {
+    int rc = check_shape(p);
+    if (rc != MOE_FFN_OK) return rc;
+    return resolve(p, mode);
+}
+
+MOE_FFN_API size_t moe_ffn_workspace_bytes(const moe_ffn_problem* p, int mode) {
+    if (check_shape(p) != MOE_FFN_OK) return 0;
+    const int m = resolve(p, mode);
+    if (m < 0) return 0;
+    return make_plan(p, m).total;
+}
+
+MOE_FFN_API size_t moe_ffn_route_workspace_bytes(int32_t T, int32_t topk, int32_t E) {
+    if (T < 0 || topk < 1 || E < 1 || E > kMaxExperts || topk > kMaxTopk) return 0;
+    if (static_cast<int64_t>(T) * topk > INT_MAX) return 0;
+    return plan_route(T, topk, E, 0).end;
+}
+
+MOE_FFN_API int moe_ffn_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_to_pair, int32_t* pair_to_sorted,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0 || topk < 1 || E < 1 || E > kMaxExperts || topk > kMaxTopk) return MOE_FFN_EINVAL_SHAPE;
+    if (static_cast<int64_t>(T) * topk > INT_MAX) return MOE_FFN_EINVAL_SHAPE;
+    const int64_t P = static_cast<int64_t>(T) * topk;
+    if (!counts || !offsets) return MOE_FFN_EINVAL_PTR;
+    if (P > 0 && (!topk_ids || !sorted_to_pair || !pair_to_sorted)) return MOE_FFN_EINVAL_PTR;
+    const RoutePlan rp = plan_route(T, topk, E, 0);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) || workspace_bytes < rp.end)
+        return MOE_FFN_EWORKSPACE;
+    moe::RouteBuffers b{topk_ids, P, E, rp.S, rp.seg, at<int32_t>(workspace, rp.seg_counts), counts, offsets,
+                        at<int32_t>(workspace, rp.tile_prefix), sorted_to_pair, pair_to_sorted};
+    return moe::launch_route(b, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
+}
+
+MOE_FFN_API int moe_ffn_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                                    void* stream) {
+    if (rows < 0 || K < 32 || K % 32) return MOE_FFN_EINVAL_SHAPE;
+    if (rows == 0) return MOE_FFN_OK;
+    if (!src || !codes || !scales || !aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 3u))
+        return MOE_FFN_EINVAL_PTR;
+    return moe::launch_mx_quantize(src, rows, K, codes, scales, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_FFN_OK
+               : MOE_FFN_EHIP;
+}
+
+MOE_FFN_API int moe_ffn_forward(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
+                                const int32_t* topk_ids, const float* topk_weights, void* out, int mode,
+                                void* stream) {
+    return moe_ffn_forward_events(p, x, w1, w2, topk_ids, topk_weights, out, mode, stream, nullptr, 0);
+}
+
+MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, const void* w1,
+                                       const void* w2, const int32_t* topk_ids, const float* topk_weights,
+                                       void* out, int mode, void* stream, void* const* events, int n_events) {
+    if (n_events != 0 && n_events != 5) return MOE_FFN_EINVAL_PTR;
+    if (n_events == 5 && !events) return MOE_FFN_EINVAL_PTR;
+    hipEvent_t ev[5];
+    hipEvent_t* evp = nullptr;
+    if (n_events == 5) {
+        for (int i = 0; i < 5; ++i) {
+            if (!events[i]) return MOE_FFN_EINVAL_PTR;
+            ev[i] = static_cast<hipEvent_t>(events[i]);
+        }
+        evp = ev;
+    }
+    int rc = check_shape(p);
+    if (rc != MOE_FFN_OK) return rc;
+    const int m = resolve(p, mode);
+    if (m < 0) return m;
+    if (p->T == 0) return MOE_FFN_OK;
+    const void* ptrs[] = {x, w1, w2, topk_ids, topk_weights, out};
+    for (const void* q : ptrs)
+        if (!q || !aligned16(q)) return MOE_FFN_EINVAL_PTR;
+    if (p->dtype == MOE_FFN_MXFP8) {
+        const void* sp[] = {p->x_scale, p->w1_scale, p->w2_scale};
+        for (const void* q : sp)
+            if (!q || (reinterpret_cast<uintptr_t>(q) & 3u)) return MOE_FFN_EINVAL_PTR;
+    }
+    const Plan pl = make_plan(p, m);
+    void* ws = p->workspace;
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) || p->workspace_bytes < pl.total)
+        return MOE_FFN_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t P = static_cast<int64_t>(p->T) * p->topk;
+
+    moe::RouteBuffers rb{topk_ids, P, p->E, pl.route.S, pl.route.seg, at<int32_t>(ws, pl.route.seg_counts),
+                         at<int32_t>(ws, pl.counts), at<int32_t>(ws, pl.offsets),
+                         at<int32_t>(ws, pl.route.tile_prefix), at<int32_t>(ws, pl.s2p), at<int32_t>(ws, pl.p2s)};
+    moe::record(evp, 0, st);
+    if (moe::launch_route(rb, st) != hipSuccess) return MOE_FFN_EHIP;
+    moe::record(evp, 1, st);
+    hipEvent_t* stage_ev = evp ? evp + 2 : nullptr;
+    moe::RouteView rv{rb.counts, rb.offsets, rb.tile_prefix, rb.sorted_to_pair, rb.pair_to_sorted};
+
+    hipError_t e;
+    if (p->dtype == MOE_FFN_BF16) {
+        moe::Bf16Args a{};
+        a.T = p->T; a.D = p->D; a.H = p->H; a.E = p->E; a.k = p->topk; a.P = P;
+        a.x = static_cast<const uint16_t*>(x);
+        a.w1 = static_cast<const uint16_t*>(w1);
+        a.w2 = static_cast<const uint16_t*>(w2);
+        a.wts = topk_weights;
+        a.rv = rv;
+        a.out = static_cast<uint16_t*>(out);
+        if (m == MOE_FFN_SPLIT) {
+            a.act = at<uint16_t>(ws, pl.act);
+            a.ypair = at<uint16_t>(ws, pl.ypair);
+            e = moe::launch_split_bf16(a, st, stage_ev);
+        } else {
+            a.acc32 = at<float>(ws, pl.acc32);
+            e = moe::launch_fused_bf16(a, st, stage_ev);
+        }
+    } else {
+        moe::MxArgs a{};
+        a.T = p->T; a.D = p->D; a.H = p->H; a.E = p->E; a.k = p->topk; a.P = P;
+        a.x = static_cast<const uint8_t*>(x);
+        a.xs = static_cast<const uint8_t*>(p->x_scale);
+        a.w1 = static_cast<const uint8_t*>(w1);
+        a.w1s = static_cast<const uint8_t*>(p->w1_scale);
+        a.w2 = static_cast<const uint8_t*>(w2);
+        a.w2s = static_cast<const uint8_t*>(p->w2_scale);
+        a.wts = topk_weights;
+        a.rv = rv;
+        a.act = at<uint8_t>(ws, pl.act);
+        a.act_s = at<uint8_t>(ws, pl.act_s);
+        a.ypair = at<uint16_t>(ws, pl.ypair);
+        a.out = static_cast<uint16_t*>(out);
+        e = moe::launch_split_mx(a, st, stage_ev);
+    }
+    return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
+}
+
+}  // extern "C"

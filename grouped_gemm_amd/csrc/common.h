@@ -1,0 +1,139 @@
+// Internal declarations shared by the HIP translation units of libmoe_ffn.
+// gfx950 (CDNA4) only: wave64, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+// 16-byte register chunk. A native vector type (not HIP's uint4 struct) so
+// arrays of it stay in VGPRs instead of being copied through private memory.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+// m-tile heights for which the route step writes tile prefix sums.
+constexpr int kNumTileHeights = 5;  // 16, 32, 64, 128, 256
+__host__ __device__ constexpr int tile_height_index(int bm) {
+    return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
+}
+
+// bf16 <-> fp32 (round to nearest even; inputs here are finite).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Device view of the route step's outputs inside the workspace.
+struct RouteView {
+    const int32_t* counts;        // [E]
+    const int32_t* offsets;       // [E+1]
+    const int32_t* tile_prefix;   // [kNumTileHeights][E+1]
+    const int32_t* sorted_to_pair;// [P]
+    const int32_t* pair_to_sorted;// [P]
+};
+
+// Which expert / rows an m-tile covers. Returns false past the last tile.
+struct MTile {
+    int expert;
+    int row0;   // first sorted row
+    int rows;   // valid rows (1..BM)
+    int m0;     // row offset inside the expert
+};
+
+template <int BM>
+__device__ __forceinline__ bool find_mtile(const RouteView& rv, int E, int g, MTile& t) {
+    const int32_t* tp = rv.tile_prefix + tile_height_index(BM) * (E + 1);
+    if (g >= tp[E]) return false;
+    int lo = 0, hi = E;  // tp[lo] <= g < tp[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (tp[mid] <= g) lo = mid; else hi = mid;
+    }
+    t.expert = lo;
+    t.m0 = (g - tp[lo]) * BM;
+    int c = rv.counts[lo];
+    t.rows = c - t.m0 < BM ? c - t.m0 : BM;
+    t.row0 = rv.offsets[lo] + t.m0;
+    return true;
+}
+
+// A pair index read back from the route maps, clamped into [0, P) so that a
+// wrong map can only give wrong numbers, never an out-of-bounds access.
+__device__ __forceinline__ int clamp_pair(int p, int64_t P) {
+    return p < 0 ? 0 : (p >= P ? static_cast<int>(P - 1) : p);
+}
+
+// ---- launchers (each returns hipGetLastError() after enqueueing) ----
+
+inline void record(hipEvent_t* ev, int i, hipStream_t s) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+}
+
+struct RouteBuffers {
+    const int32_t* ids;
+    int64_t P;
+    int32_t E;
+    int32_t S, seg;           // segments and pairs per segment
+    int32_t* seg_counts;      // [E][S]
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* tile_prefix;
+    int32_t* sorted_to_pair;
+    int32_t* pair_to_sorted;
+};
+hipError_t launch_route(const RouteBuffers& b, hipStream_t s);
+
+struct Bf16Args {
+    int32_t T, D, H, E, k;
+    int64_t P;
+    const uint16_t* x;
+    const uint16_t* w1;
+    const uint16_t* w2;
+    const float* wts;
+    RouteView rv;
+    uint16_t* act;     // [P, H]   split only
+    uint16_t* ypair;   // [P, D]   split only: weighted expert outputs in pair order
+    float* acc32;      // [T, D]   fused only
+    uint16_t* out;     // [T, D]
+};
+// `ev` (nullable) points at 3 events recorded after each of the launcher's
+// three kernels.
+hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
+
+struct MxArgs {
+    int32_t T, D, H, E, k;
+    int64_t P;
+    const uint8_t* x;   const uint8_t* xs;
+    const uint8_t* w1;  const uint8_t* w1s;
+    const uint8_t* w2;  const uint8_t* w2s;
+    const float* wts;
+    RouteView rv;
+    uint8_t* act;       // [P, H] e4m3 codes
+    uint8_t* act_s;     // [P, H/32] e8m0
+    uint16_t* ypair;    // [P, D]
+    uint16_t* out;      // [T, D]
+};
+hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
+
+hipError_t launch_combine(const uint16_t* ypair, const int32_t* pair_to_sorted, int32_t T, int32_t k,
+                          int32_t D, uint16_t* out, hipStream_t s);
+hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+hipError_t launch_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+
+}  // namespace moe

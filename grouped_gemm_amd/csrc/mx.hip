@@ -1,0 +1,359 @@
+// MX-fp8 pieces of the MoE SwiGLU FFN on gfx950.
+//
+// Data format ("Prime Flash MoE", section 7): e4m3 codes with one e8m0
+// scale (value 2^(byte-127)) per 32 contiguous elements along K. Scale rule
+// ("Porting Block-Scaled GEMM Kernels from Blackwell to Rubin", section
+// 6.2, read as: the scale byte is amax/448 rounded up to a power of two):
+// s = the smallest integer with amax <= 448 * 2^s, clamped to [-127, 127];
+// codes = e4m3(v * 2^-s), round to nearest even, saturating at 448.
+// s is read off amax's exponent and mantissa bits, so no division is made.
+//
+// GEMMs: v_mfma_scale_f32_32x32x64_f8f6f4 takes 32 e4m3 codes per lane for
+// A (row lane&31) and B (column lane&31) and one e8m0 scale per lane. With
+// g = lane>>5, a lane's first 16 codes are k = 16g..16g+15 of the MFMA's 64
+// (scale block 0) and its last 16 are k = 32+16g..32+16g+15 (block 1);
+// lanes of group g supply the scale of block g for their row or column
+// (layout measured on gfx950 with an in-bounds probe). Tiles are staged
+// like the bf16 kernels: 128 codes (128 bytes) of K per row per stage,
+// 16-byte chunks XOR-swizzled by (row & 7), double-buffered.
+//
+// GEMM1's epilogue computes SwiGLU in fp32, stages the act tile in LDS and
+// requantizes it per 32 along H with the same rule (section 7, "The
+// epilogue also quantizes"), writing codes [P, H] and scales [P, H/32].
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BKB = 128;  // K bytes (= codes) per stage
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ int acc_row(int lane, int v) { return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3); }
+
+// MXQ scale exponent from the block's amax (finite, >= 0).
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+    const uint32_t u = __float_as_uint(amax);
+    const int ef = static_cast<int>(u >> 23);
+    if (ef == 0) return -127;  // zero or below 2^-126: the clamp decides
+    int s = ef - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+    return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// 2^e as a float for e in [-127, 127] (2^-127 is subnormal, still exact).
+__device__ __forceinline__ float pow2f(int e) {
+    return e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// e4m3fn code of v (already divided by the block scale), nearest even,
+// saturating; the sign comes from `sign_src` so a value that underflows
+// keeps the sign of the input.
+__device__ __forceinline__ uint32_t e4m3_encode(float v, float sign_src) {
+    const uint32_t sign = (__float_as_uint(sign_src) >> 24) & 0x80u;
+    const float x = fabsf(v);
+    uint32_t code;
+    if (x >= 448.0f) {
+        code = 0x7e;
+    } else if (x < 0.015625f) {                   // below 2^-6: multiples of 2^-9
+        code = static_cast<uint32_t>(rintf(x * 512.0f));
+    } else {
+        const uint32_t u = __float_as_uint(x);
+        const uint32_t r = (u + 0x7ffffu + ((u >> 20) & 1u)) >> 20;  // exponent|3 mantissa bits, RNE
+        code = r - (120u << 3);
+        if (code > 0x7eu) code = 0x7e;
+    }
+    return sign | code;
+}
+
+// ---------------- standalone quantizer ----------------
+// 8 lanes per 32-element block, 4 values per lane.
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const float* __restrict__ src, int64_t nblk,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    const int sub = threadIdx.x & 7;
+    for (int64_t b = (blockIdx.x * 256ll + threadIdx.x) >> 3; b < nblk;
+         b += (static_cast<int64_t>(gridDim.x) * 256) >> 3) {
+        const float4 v = *reinterpret_cast<const float4*>(src + b * 32 + sub * 4);
+        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+        const int s = mx_scale_exp(amax);
+        const float inv = pow2f(-s);
+        const uint32_t c = e4m3_encode(v.x * inv, v.x) | (e4m3_encode(v.y * inv, v.y) << 8) |
+                           (e4m3_encode(v.z * inv, v.z) << 16) | (e4m3_encode(v.w * inv, v.w) << 24);
+        *reinterpret_cast<uint32_t*>(codes + b * 32 + sub * 4) = c;
+        if (sub == 0) scales[b] = static_cast<uint8_t>(s + 127);
+    }
+}
+
+// ---------------- block-scaled grouped GEMM main loop ----------------
+// acc[mi][nj] += A . B^T with e8m0 scales. aptr/bptr: this thread's 16-byte
+// chunk of stage 0 for each of its rows; asp/bsp: per (wave block, lane) the
+// scale row of that lane's A row / B row (K/32 bytes per row).
+template <int BM, int BN>
+struct MxTile {
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int MB = WM / 32, NB = WN / 32;
+    static constexpr int A_CH = BM * 8 / kThreads;
+    static constexpr int B_CH = BN * 8 / kThreads;
+    static constexpr int STAGE = (BM + BN) * BKB;  // bytes
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void mx_mainloop(uint8_t* lds, const uint8_t* const* aptr, const uint8_t* const* bptr,
+                                            const uint8_t* const* asp, const uint8_t* const* bsp, int KT,
+                                            const int* brow,
+                                            f32x16_t (&acc)[MxTile<BM, BN>::MB][MxTile<BM, BN>::NB]) {
+    using C = MxTile<BM, BN>;
+    const int tid = threadIdx.x, lane = tid & 63, wm = (tid >> 6) >> 1;
+    const int c16 = tid & 7, r16 = tid >> 3;
+    u32x4_t ra[C::A_CH], rb[C::B_CH];
+    uint32_t sa[C::MB], sb[C::NB];  // 4 scale bytes (blocks of this stage) per lane row
+    uint32_t na[C::MB], nb[C::NB];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int q = 0; q < C::A_CH; ++q) ra[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + kt * BKB);
+#pragma unroll
+        for (int q = 0; q < C::B_CH; ++q) rb[q] = *reinterpret_cast<const u32x4_t*>(bptr[q] + kt * BKB);
+#pragma unroll
+        for (int mi = 0; mi < C::MB; ++mi) na[mi] = *reinterpret_cast<const uint32_t*>(asp[mi] + kt * 4);
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj) nb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + kt * 4);
+    };
+    auto sstore = [&](int buf) {
+        uint8_t* sA = lds + buf * C::STAGE;
+        uint8_t* sB = sA + BM * BKB;
+#pragma unroll
+        for (int q = 0; q < C::A_CH; ++q) *reinterpret_cast<u32x4_t*>(sA + swz(r16 + 32 * q, c16)) = ra[q];
+#pragma unroll
+        for (int q = 0; q < C::B_CH; ++q) *reinterpret_cast<u32x4_t*>(sB + swz(r16 + 32 * q, c16)) = rb[q];
+    };
+    gload(0);
+    sstore(0);
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi) sa[mi] = na[mi];
+#pragma unroll
+    for (int nj = 0; nj < C::NB; ++nj) sb[nj] = nb[nj];
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) gload(kt + 1);
+        const uint8_t* sA = lds + (kt & 1) * C::STAGE;
+        const uint8_t* sB = sA + BM * BKB;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // 16-byte chunks of block 0 and block 1 of this 64-wide step
+            const int ch0 = 4 * kk + (lane >> 5), ch1 = ch0 + 2;
+            const int sh = 8 * (2 * kk + (lane >> 5));
+            i32x8_t af[C::MB], bfr[C::NB];
+#pragma unroll
+            for (int mi = 0; mi < C::MB; ++mi) {
+                const int r = wm * C::WM + 32 * mi + (lane & 31);
+                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sA + swz(r, ch0));
+                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sA + swz(r, ch1));
+                af[mi] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int nj = 0; nj < C::NB; ++nj) {
+                const int r = brow[nj] + (lane & 31);
+                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sB + swz(r, ch0));
+                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sB + swz(r, ch1));
+                bfr[nj] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < C::NB; ++nj)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af[mi], bfr[nj], acc[mi][nj], 0, 0, 0, static_cast<int>((sa[mi] >> sh) & 0xffu), 0,
+                        static_cast<int>((sb[nj] >> sh) & 0xffu));
+        }
+        if (kt + 1 < KT) sstore((kt + 1) & 1);
+#pragma unroll
+        for (int mi = 0; mi < C::MB; ++mi) sa[mi] = na[mi];
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj) sb[nj] = nb[nj];
+        __syncthreads();
+    }
+}
+
+// ---------------- MX GEMM1 + SwiGLU + requant ----------------
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void mx_gemm1_kernel(MxArgs a) {
+    using C = MxTile<BM, BN>;
+    static_assert(C::NB % 2 == 0, "gate and up need the same number of blocks");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
+    __shared__ int32_t sTok[BM];
+    MTile mt;
+    if (!find_mtile<BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int BH = BN / 2, h0 = blockIdx.y * BH;
+    const int DB = a.D / 32;
+    for (int r = tid; r < BM; r += kThreads)
+        sTok[r] = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P) / a.k;
+    __syncthreads();
+
+    const int c16 = tid & 7, r16 = tid >> 3;
+    const uint8_t* aptr[C::A_CH];
+    const uint8_t* bptr[C::B_CH];
+#pragma unroll
+    for (int q = 0; q < C::A_CH; ++q) aptr[q] = a.x + static_cast<int64_t>(sTok[r16 + 32 * q]) * a.D + c16 * 16;
+    const int64_t w1row0 = static_cast<int64_t>(mt.expert) * 2 * a.H;
+    auto w1row = [&](int r) { return w1row0 + (r < BH ? h0 + r : a.H + h0 + (r - BH)); };
+#pragma unroll
+    for (int q = 0; q < C::B_CH; ++q) bptr[q] = a.w1 + w1row(r16 + 32 * q) * a.D + c16 * 16;
+    int brow[C::NB];
+#pragma unroll
+    for (int nj = 0; nj < C::NB; ++nj)
+        brow[nj] = nj < C::NB / 2 ? wn * (BH / 2) + 32 * nj : BH + wn * (BH / 2) + 32 * (nj - C::NB / 2);
+    const uint8_t* asp[C::MB];
+    const uint8_t* bsp[C::NB];
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi)
+        asp[mi] = a.xs + static_cast<int64_t>(sTok[wm * C::WM + 32 * mi + (lane & 31)]) * DB;
+#pragma unroll
+    for (int nj = 0; nj < C::NB; ++nj) bsp[nj] = a.w1s + w1row(brow[nj] + (lane & 31)) * DB;
+
+    f32x16_t acc[C::MB][C::NB];
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj) acc[mi][nj] = f32x16_t{};
+    mx_mainloop<BM, BN>(lds, aptr, bptr, asp, bsp, a.D / BKB, brow, acc);
+
+    // SwiGLU in fp32 -> LDS [BM][BH + 4] floats -> requant per 32 along H.
+    constexpr int OS = BN / 2 + 4;
+    float* sO = reinterpret_cast<float*>(lds);
+    static_assert(BM * (BN / 2 + 4) * 4 <= 2 * C::STAGE, "act staging must fit the stage buffers");
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+        for (int j = 0; j < C::NB / 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = wm * C::WM + 32 * mi + acc_row(lane, v);
+                const int col = wn * (BH / 2) + 32 * j + (lane & 31);
+                const float g = acc[mi][j][v], u = acc[mi][j + C::NB / 2][v];
+                sO[m * OS + col] = g / (1.0f + __expf(-g)) * u;
+            }
+    __syncthreads();
+    const int HB = a.H / 32;
+    constexpr int BPR = BN / 2 / 32;  // scale blocks per tile row
+    const int sub = tid & 7;
+    for (int item = tid >> 3; item < BM * BPR; item += kThreads / 8) {
+        const int r = item / BPR, blk = item % BPR;
+        const float4 v = *reinterpret_cast<const float4*>(sO + r * OS + blk * 32 + sub * 4);
+        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+        const int s = mx_scale_exp(amax);
+        const float inv = pow2f(-s);
+        const uint32_t c = e4m3_encode(v.x * inv, v.x) | (e4m3_encode(v.y * inv, v.y) << 8) |
+                           (e4m3_encode(v.z * inv, v.z) << 16) | (e4m3_encode(v.w * inv, v.w) << 24);
+        if (r < mt.rows) {
+            const int64_t row = mt.row0 + r;
+            *reinterpret_cast<uint32_t*>(a.act + row * a.H + h0 + blk * 32 + sub * 4) = c;
+            if (sub == 0) a.act_s[row * HB + h0 / 32 + blk] = static_cast<uint8_t>(s + 127);
+        }
+    }
+}
+
+// ---------------- MX GEMM2 + routing weight ----------------
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void mx_gemm2_kernel(MxArgs a) {
+    using C = MxTile<BM, BN>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
+    __shared__ int32_t sPair[BM];
+    __shared__ float sW[BM];
+    MTile mt;
+    if (!find_mtile<BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.y * BN;
+    const int HB = a.H / 32;
+    for (int r = tid; r < BM; r += kThreads) {
+        const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P);
+        sPair[r] = p;
+        sW[r] = a.wts[p];
+    }
+    __syncthreads();
+    const int c16 = tid & 7, r16 = tid >> 3;
+    auto arow = [&](int r) { return static_cast<int64_t>(mt.row0 + (r < mt.rows ? r : 0)); };
+    const uint8_t* aptr[C::A_CH];
+    const uint8_t* bptr[C::B_CH];
+#pragma unroll
+    for (int q = 0; q < C::A_CH; ++q) aptr[q] = a.act + arow(r16 + 32 * q) * a.H + c16 * 16;
+    const int64_t w2row0 = static_cast<int64_t>(mt.expert) * a.D + n0;
+#pragma unroll
+    for (int q = 0; q < C::B_CH; ++q) bptr[q] = a.w2 + (w2row0 + r16 + 32 * q) * a.H + c16 * 16;
+    int brow[C::NB];
+#pragma unroll
+    for (int nj = 0; nj < C::NB; ++nj) brow[nj] = wn * C::WN + 32 * nj;
+    const uint8_t* asp[C::MB];
+    const uint8_t* bsp[C::NB];
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi) asp[mi] = a.act_s + arow(wm * C::WM + 32 * mi + (lane & 31)) * HB;
+#pragma unroll
+    for (int nj = 0; nj < C::NB; ++nj) bsp[nj] = a.w2s + (w2row0 + brow[nj] + (lane & 31)) * HB;
+
+    f32x16_t acc[C::MB][C::NB];
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj) acc[mi][nj] = f32x16_t{};
+    mx_mainloop<BM, BN>(lds, aptr, bptr, asp, bsp, a.H / BKB, brow, acc);
+
+    constexpr int OS = BN + 8;
+    uint16_t* sO = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+    for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = wm * C::WM + 32 * mi + acc_row(lane, v);
+                const int col = wn * C::WN + 32 * nj + (lane & 31);
+                sO[m * OS + col] = f32_to_bf16(acc[mi][nj][v] * sW[m]);
+            }
+    __syncthreads();
+    constexpr int CPR = BN / 8;
+    for (int idx = tid; idx < BM * CPR; idx += kThreads) {
+        const int r = idx / CPR, c = idx % CPR;
+        if (r < mt.rows)
+            *reinterpret_cast<u32x4_t*>(a.ypair + static_cast<int64_t>(sPair[r]) * a.D + n0 + c * 8) =
+                *reinterpret_cast<const u32x4_t*>(sO + r * OS + c * 8);
+    }
+}
+
+inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
+
+}  // namespace
+
+hipError_t launch_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s) {
+    const int64_t nblk = rows * (K / 32);
+    if (nblk == 0) return hipSuccess;
+    int64_t g = (nblk * 8 + 255) / 256;
+    if (g > 8192) g = 8192;
+    mx_quantize_kernel<<<static_cast<int>(g), 256, 0, s>>>(src, nblk, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev) {
+    constexpr int BM = 128, BN1 = 128, BN2 = 128;
+    dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
+    mx_gemm1_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
+    record(ev, 0, s);
+    dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
+    mx_gemm2_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
+    record(ev, 1, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_combine(a.ypair, a.rv.pair_to_sorted, a.T, a.k, a.D, a.out, s);
+    record(ev, 2, s);
+    return e;
+}
+
+}  // namespace moe

@@ -1,0 +1,190 @@
+// Route step: permute routed (token, expert) pairs by expert.
+//
+// The grouped GEMMs read the pairs of each expert as one contiguous group
+// of rows ("Prime Flash MoE", section 1: the grouped-GEMM formulation with
+// sorted rows and group offsets; section 8: routing and sorting). Here the
+// pairs p = t*k + j are sorted stably by expert id with a counting sort:
+//   1. route_count   : one workgroup per segment of `seg` pairs builds that
+//                      segment's per-expert histogram in LDS.
+//   2. route_scan    : one workgroup per expert turns its row of segment
+//                      counts into an exclusive prefix and writes counts[e].
+//   3. route_offsets : one workgroup scans counts into offsets[E+1] and the
+//                      m-tile prefix sums for the GEMMs' tile heights.
+//   4. route_scatter : one wave per segment walks its pairs in order, 64 at a
+//                      time; lanes holding the same expert find each other
+//                      with ballots over the bits of the id, so the rank of a
+//                      pair among equal ids is the popcount of lower lanes in
+//                      its group. The result does not depend on scheduling.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int t = __shfl_up(v, d, 64);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan across a block of NW waves; `sh` holds NW ints of LDS.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int& total, int* sh) {
+    const int incl = wave_incl_scan(v);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    int wbase = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        int t = sh[i];
+        wbase += i < w ? t : 0;
+        total += t;
+    }
+    __syncthreads();
+    return wbase + incl - v;
+}
+
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                          int E, int S, int seg,
+                                                          int32_t* __restrict__ seg_counts) {
+    extern __shared__ int32_t hist[];
+    const int s = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+    __syncthreads();
+    const int64_t p0 = static_cast<int64_t>(s) * seg;
+    const int64_t p1 = p0 + seg < P ? p0 + seg : P;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
+        int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) seg_counts[static_cast<int64_t>(e) * S + s] = hist[e];
+}
+
+// Exclusive prefix over segments for expert blockIdx.x, in place.
+__global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ seg_counts, int S,
+                                                         int32_t* __restrict__ counts) {
+    __shared__ int sh[4];
+    int32_t* row = seg_counts + static_cast<int64_t>(blockIdx.x) * S;
+    int carry = 0;
+    for (int base = 0; base < S; base += 256 * 4) {
+        int v[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int idx = base + threadIdx.x * 4 + i;
+            v[i] = idx < S ? row[idx] : 0;
+            local += v[i];
+        }
+        int total;
+        int ex = block_excl_scan<4>(local, total, sh) + carry;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int idx = base + threadIdx.x * 4 + i;
+            if (idx < S) row[idx] = ex;
+            ex += v[i];
+        }
+        carry += total;
+    }
+    if (threadIdx.x == 0) counts[blockIdx.x] = carry;
+}
+
+// offsets[E+1] and, for each tile height BM in {16..256}, the prefix sums of
+// ceil(counts/BM) (the m-tile index of each expert's first tile).
+__global__ __launch_bounds__(1024) void route_offsets_kernel(const int32_t* __restrict__ counts,
+                                                             int E, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tile_prefix) {
+    __shared__ int sh[16];
+    constexpr int PER = 8;  // experts per thread: E <= 8192
+    const int e0 = threadIdx.x * PER;
+    int c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c[i] = e0 + i < E ? counts[e0 + i] : 0;
+    for (int b = -1; b < kNumTileHeights; ++b) {
+        const int bm = 16 << (b < 0 ? 0 : b);
+        int v[PER], local = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            v[i] = b < 0 ? c[i] : (c[i] + bm - 1) / bm;
+            local += v[i];
+        }
+        int total;
+        int ex = block_excl_scan<16>(local, total, sh);
+        int32_t* dst = b < 0 ? offsets : tile_prefix + b * (E + 1);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (e0 + i < E) dst[e0 + i] = ex;
+            ex += v[i];
+        }
+        if (threadIdx.x == 0) dst[E] = total;
+    }
+}
+
+__global__ __launch_bounds__(64) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int E, int S, int seg, int nbits,
+    const int32_t* __restrict__ seg_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_to_pair, int32_t* __restrict__ pair_to_sorted) {
+    extern __shared__ int32_t run[];
+    const int s = blockIdx.x, lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) run[e] = offsets[e] + seg_base[static_cast<int64_t>(e) * S + s];
+    const int64_t valid_total = offsets[E];
+    __syncthreads();
+    const int64_t p0 = static_cast<int64_t>(s) * seg;
+    const int64_t p1 = p0 + seg < P ? p0 + seg : P;
+    // sorted positions past the valid pairs hold -1; this segment's index
+    // range [p0, p1) takes its share of them.
+    for (int64_t i = p0 + lane; i < p1; i += 64)
+        if (i >= valid_total) sorted_to_pair[i] = -1;
+    const uint64_t lower = (1ull << lane) - 1ull;
+    for (int64_t base = p0; base < p1; base += 64) {
+        const int64_t p = base + lane;
+        const bool in = p < p1;
+        const int e = in ? ids[p] : -1;
+        const bool valid = in && e >= 0 && e < E;
+        const int key = valid ? e : E;
+        uint64_t same = ~0ull;
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(same & lower);
+        const int cnt = __popcll(same);
+        const bool leader = (same >> lane) == 1ull;  // highest lane of its group
+        int pos = valid ? run[e] + rank : 0;
+        __syncthreads();
+        if (valid && leader) run[e] += cnt;
+        __syncthreads();
+        if (valid && pos >= 0 && pos < P) {
+            sorted_to_pair[pos] = static_cast<int32_t>(p);
+            pair_to_sorted[p] = pos;
+        } else if (in) {
+            pair_to_sorted[p] = -1;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteBuffers& b, hipStream_t st) {
+    const size_t lds = sizeof(int32_t) * static_cast<size_t>(b.E);
+    int nbits = 0;
+    while ((1 << nbits) <= b.E) ++nbits;  // enough bits for ids 0..E (E = sentinel)
+    if (b.S > 0) {
+        route_count_kernel<<<b.S, 256, lds, st>>>(b.ids, b.P, b.E, b.S, b.seg, b.seg_counts);
+    }
+    route_scan_kernel<<<b.E, 256, 0, st>>>(b.seg_counts, b.S, b.counts);
+    route_offsets_kernel<<<1, 1024, 0, st>>>(b.counts, b.E, b.offsets, b.tile_prefix);
+    if (b.S > 0) {
+        route_scatter_kernel<<<b.S, 64, lds, st>>>(b.ids, b.P, b.E, b.S, b.seg, nbits, b.seg_counts,
+                                                   b.offsets, b.sorted_to_pair, b.pair_to_sorted);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,164 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) routed MoE SwiGLU FFN forward pass.
+ *
+ * The operation ("Prime Flash MoE - Faster MoE Kernels optimized for
+ * Blackwell", section 1 "The computation"): a router has already chosen
+ * each token's top-k experts and normalized routing weights. For every
+ * routed (token t, expert e) pair,
+ *     gate|up = W1[e] x_t         (W1 [E, 2H, D], output-major, gate rows
+ *                                  [0, H) then up rows [H, 2H))
+ *     act     = silu(gate) * up   (silu(z) = z / (1 + exp(-z)))
+ *     y       = W2[e] act         (W2 [E, D, H], output-major)
+ * and out[t] = sum over the token's k slots of weight * y. The library runs
+ * it as: route (per-expert histogram, prefix sum, stable index maps) ->
+ * grouped GEMM1 with the SwiGLU epilogue -> grouped GEMM2 with the
+ * routing-weight epilogue -> combine into out.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers (HIP device memory) unless the
+ *     comment says "host". Tensors are dense and row-major (last dim
+ *     contiguous). bf16 tensors hold IEEE bfloat16 bit patterns (uint16).
+ *   - The caller owns every buffer. The library never allocates device
+ *     memory inside these calls and keeps no state between them.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously; no call synchronizes the host except where stated.
+ *   - Return value: MOE_FFN_OK (0) or a negative MOE_FFN_E* code; no
+ *     exception crosses the ABI. moe_ffn_strerror() names a code.
+ *   - Calls on distinct streams with distinct workspaces and outputs are
+ *     independent; concurrent calls that share a workspace race.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FFN_API __attribute__((visibility("default")))
+
+/* Data paths (Prime Flash MoE: "two data paths, one for bf16 and one for
+ * MXFP8", introduction). */
+enum { MOE_FFN_BF16 = 0, MOE_FFN_MXFP8 = 1 };
+
+/* Pipelines (same page, introduction and section 6): FUSED runs GEMM1,
+ * SwiGLU and GEMM2 in one kernel and never writes the activation; the down
+ * projection is then split over H slices whose partial rows are reduced
+ * into an fp32 accumulator. SPLIT writes the activation once and runs the
+ * down projection as a plain grouped GEMM. AUTO picks one from the shape. */
+enum { MOE_FFN_AUTO = 0, MOE_FFN_FUSED = 1, MOE_FFN_SPLIT = 2 };
+
+enum {
+    MOE_FFN_OK = 0,
+    MOE_FFN_EINVAL_SHAPE = -1,  /* T < 0, D/H/E/topk < 1, D or H not a multiple of 128,
+                                   topk > E or > 64, E > 8192, or sizes that overflow */
+    MOE_FFN_EINVAL_PTR = -2,    /* a required pointer is NULL or not 16-byte aligned */
+    MOE_FFN_EUNSUPPORTED = -3,  /* dtype or mode unknown, or the pair not built */
+    MOE_FFN_EWORKSPACE = -4,    /* workspace NULL, misaligned (256 B) or too small */
+    MOE_FFN_EHIP = -5           /* a HIP launch reported an error */
+};
+
+/* Problem descriptor (plain C; every pointer is caller-owned).
+ *   T, D, H, E, topk : tokens, hidden dim, FFN intermediate dim, experts, k.
+ *   dtype            : MOE_FFN_BF16 or MOE_FFN_MXFP8.
+ *   x_scale, w1_scale, w2_scale : MXFP8 only (NULL for bf16). e8m0 bytes
+ *                      (value 2^(byte-127)), one per 32 contiguous elements
+ *                      along the contraction dim (Prime Flash MoE, section
+ *                      7): x_scale [T, D/32], w1_scale [E, 2H, D/32],
+ *                      w2_scale [E, D, H/32], row-major.
+ *   workspace        : device scratch of at least moe_ffn_workspace_bytes(),
+ *                      256-byte aligned. Its contents on entry are ignored. */
+typedef struct moe_ffn_problem {
+    int32_t T, D, H, E, topk;
+    int32_t dtype;
+    const void* x_scale;
+    const void* w1_scale;
+    const void* w2_scale;
+    void* workspace;
+    size_t workspace_bytes;
+} moe_ffn_problem;
+
+/* Bytes of workspace moe_ffn_forward needs for this problem and mode
+ * (AUTO resolves as moe_ffn_forward would). Host only; 0 on invalid input. */
+MOE_FFN_API size_t moe_ffn_workspace_bytes(const moe_ffn_problem* p, int mode);
+
+/* Host-only check of shapes, dtype and mode (no pointers are checked, no
+ * GPU call is made). Returns MOE_FFN_OK or the error moe_ffn_forward would
+ * return for the same shapes. */
+MOE_FFN_API int moe_ffn_validate(const moe_ffn_problem* p, int mode);
+
+/* The pipeline AUTO resolves to for this problem (MOE_FFN_FUSED or
+ * MOE_FFN_SPLIT); a negative code on invalid input. Host only. */
+MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode);
+
+/* The forward pass.
+ *   x            : bf16 [T, D], or e4m3 codes [T, D] for MXFP8.
+ *   w1           : bf16 [E, 2H, D] (gate rows then up rows per expert), or
+ *                  e4m3 codes for MXFP8.
+ *   w2           : bf16 [E, D, H], or e4m3 codes for MXFP8.
+ *   topk_ids     : int32 [T, topk]; an id outside [0, E) is a dropped route
+ *                  that contributes nothing.
+ *   topk_weights : fp32 [T, topk], used as given (not renormalized).
+ *   out          : bf16 [T, D]; fully overwritten in every mode.
+ * Enqueues route, GEMM and combine kernels on `stream`; T == 0 is a
+ * successful no-op. */
+MOE_FFN_API int moe_ffn_forward(const moe_ffn_problem* p, const void* x, const void* w1,
+                                const void* w2, const int32_t* topk_ids,
+                                const float* topk_weights, void* out, int mode, void* stream);
+
+/* moe_ffn_forward, additionally recording caller-created HIP events
+ * (hipEvent_t, passed as void*) on `stream` at the boundaries of its four
+ * kernel stages, for per-kernel timing without a host synchronization:
+ *   events[0] before the route step        events[1] after it
+ *   events[2] after stage 2 (SPLIT: GEMM1 + SwiGLU; FUSED: accumulator fill)
+ *   events[3] after stage 3 (SPLIT: GEMM2 + weight; FUSED: fused kernel)
+ *   events[4] after stage 4 (SPLIT: combine;        FUSED: fp32 -> bf16)
+ * n_events must be 5 (or 0, which makes it moe_ffn_forward). The events
+ * stay owned by the caller. */
+MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, const void* w1,
+                                       const void* w2, const int32_t* topk_ids,
+                                       const float* topk_weights, void* out, int mode,
+                                       void* stream, void* const* events, int n_events);
+
+/* Workspace bytes moe_ffn_route needs (host only; 0 on invalid input). */
+MOE_FFN_API size_t moe_ffn_route_workspace_bytes(int32_t T, int32_t topk, int32_t E);
+
+/* The permutation step on its own (the sorted order the grouped GEMMs read:
+ * Prime Flash MoE, section 1, the `offs` group offsets of the grouped GEMM
+ * formulation, and section 8, routing and sorting). With P = T*topk and
+ * pairs p = t*topk + j:
+ *   counts         int32 [E]   : valid pairs routed to each expert.
+ *   offsets        int32 [E+1] : exclusive prefix sum of counts.
+ *   sorted_to_pair int32 [P]   : the pairs of expert 0, then expert 1, ...,
+ *                                ascending p inside each expert (a stable
+ *                                sort); entries from offsets[E] on are -1.
+ *   pair_to_sorted int32 [P]   : the inverse map; -1 for dropped routes.
+ * The result is unique, so it is bit-exact against any stable sort. */
+MOE_FFN_API int moe_ffn_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
+                              int32_t* counts, int32_t* offsets, int32_t* sorted_to_pair,
+                              int32_t* pair_to_sorted, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* MX-fp8 quantization of fp32 rows along the last dim (Prime Flash MoE,
+ * section 7: e4m3 data with one e8m0 scale per 32 contiguous K elements;
+ * the scale rule reads "Porting Block-Scaled GEMM Kernels from Blackwell to
+ * Rubin", section 6.2: the scale is amax/448 rounded up to a power of two,
+ * i.e. s = the smallest integer with amax <= 448 * 2^s, clamped to
+ * [-127, 127], s = -127 for an all-zero block; codes = e4m3(v * 2^-s) with
+ * round-to-nearest-even, saturating at +-448).
+ *   src    : fp32 [rows, K], K a multiple of 32.
+ *   codes  : uint8 [rows, K] e4m3 codes.   scales : uint8 [rows, K/32].
+ * The same rule requantizes the SwiGLU output inside the MXFP8 pass. */
+MOE_FFN_API int moe_ffn_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                                    uint8_t* scales, void* stream);
+
+/* A static string naming `code`. */
+MOE_FFN_API const char* moe_ffn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

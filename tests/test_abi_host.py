@@ -1,0 +1,106 @@
+"""The C-ABI library loads without a GPU, exports every function the header
+declares, and its host-only entry points validate shapes (no GPU call)."""
+import ctypes
+
+import pytest
+
+import grouped_gemm_amd as g
+
+
+def test_library_exports_every_header_function():
+    lib = g.library()
+    names = g.header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == {
+        "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_forward",
+        "moe_ffn_forward_events",
+        "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_strerror"}
+
+
+@pytest.mark.parametrize("shape,expect", [
+    ((64, 256, 512, 8, 2), g.MOE_FFN_OK),
+    ((0, 256, 512, 8, 2), g.MOE_FFN_OK),
+    ((-1, 256, 512, 8, 2), g.MOE_FFN_EINVAL_SHAPE),
+    ((64, 200, 512, 8, 2), g.MOE_FFN_EINVAL_SHAPE),     # D not a multiple of 128
+    ((64, 256, 500, 8, 2), g.MOE_FFN_EINVAL_SHAPE),     # H not a multiple of 128
+    ((64, 256, 512, 8, 9), g.MOE_FFN_EINVAL_SHAPE),     # k > E
+    ((64, 256, 512, 0, 1), g.MOE_FFN_EINVAL_SHAPE),
+    ((64, 256, 512, 8, 0), g.MOE_FFN_EINVAL_SHAPE),
+    ((64, 256, 512, 9000, 2), g.MOE_FFN_EINVAL_SHAPE),  # E above the route limit
+    ((1 << 30, 256, 512, 8, 4), g.MOE_FFN_EINVAL_SHAPE),  # T*k overflows int32
+])
+def test_validate_shapes(shape, expect):
+    assert g.moe_ffn_validate(*shape) == expect
+
+
+def test_validate_dtype_and_mode():
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype=7) == g.MOE_FFN_EUNSUPPORTED
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, mode=5) == g.MOE_FFN_EUNSUPPORTED
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == g.MOE_FFN_EUNSUPPORTED
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp8", mode="split") == g.MOE_FFN_OK
+    lib = g.library()
+    assert lib.moe_ffn_validate(None, 0) == g.MOE_FFN_EINVAL_PTR
+
+
+def test_resolve_mode():
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="split") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="fused") == g.MOE_FFN_FUSED
+    assert g.moe_ffn_resolve_mode(64, 6144, 2048, 32, 8, mode="auto") in (g.MOE_FFN_SPLIT, g.MOE_FFN_FUSED)
+    assert g.moe_ffn_resolve_mode(131072, 2048, 768, 128, 8, mode="auto") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, dtype="mxfp8") == g.MOE_FFN_SPLIT
+
+
+def test_workspace_sizes():
+    T, D, H, E, k = 4096, 2048, 768, 128, 8
+    P = T * k
+    split = g.moe_ffn_workspace_bytes(T, D, H, E, k, mode="split")
+    fused = g.moe_ffn_workspace_bytes(T, D, H, E, k, mode="fused")
+    assert split >= P * H * 2 + P * D * 2 + 2 * P * 4          # act + ypair + maps
+    assert fused >= T * D * 4 + 2 * P * 4                      # fp32 accumulator + maps
+    mx = g.moe_ffn_workspace_bytes(T, D, H, E, k, dtype="mxfp8", mode="split")
+    assert mx >= P * H + P * H // 32 + P * D * 2
+    assert split % 256 == 0 and fused % 256 == 0
+    assert g.moe_ffn_workspace_bytes(64, 200, 512, 8, 2) == 0   # invalid -> 0
+    assert g.library().moe_ffn_route_workspace_bytes(100, 8, 32) > 0
+    assert g.library().moe_ffn_route_workspace_bytes(100, 8, 0) == 0
+
+
+def test_forward_rejects_bad_arguments_without_gpu_work():
+    """Errors found on the host return before any launch."""
+    lib = g.library()
+    p = g.make_problem(64, 256, 512, 8, 2)
+    VP = ctypes.c_void_p
+    # null pointers
+    assert lib.moe_ffn_forward(ctypes.byref(p), None, None, None, None, None, None, 2, None) == \
+        g.MOE_FFN_EINVAL_PTR
+    # misaligned pointer
+    bad = VP(0x1001)
+    ok = VP(0x1000)
+    assert lib.moe_ffn_forward(ctypes.byref(p), bad, ok, ok, ok, ok, ok, 2, None) == g.MOE_FFN_EINVAL_PTR
+    # missing workspace
+    assert lib.moe_ffn_forward(ctypes.byref(p), ok, ok, ok, ok, ok, ok, 2, None) == g.MOE_FFN_EWORKSPACE
+    # MX path without scales
+    pm = g.make_problem(64, 256, 512, 8, 2, dtype="mxfp8")
+    assert lib.moe_ffn_forward(ctypes.byref(pm), ok, ok, ok, ok, ok, ok, 2, None) == g.MOE_FFN_EINVAL_PTR
+    # T = 0 is a no-op that touches nothing
+    p0 = g.make_problem(0, 256, 512, 8, 2)
+    assert lib.moe_ffn_forward(ctypes.byref(p0), None, None, None, None, None, None, 2, None) == g.MOE_FFN_OK
+    assert lib.moe_ffn_mx_quantize(None, 4, 48, None, None, None) == g.MOE_FFN_EINVAL_SHAPE
+    assert lib.moe_ffn_mx_quantize(None, 4, 64, None, None, None) == g.MOE_FFN_EINVAL_PTR
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, -5, -99):
+        assert isinstance(g.moe_ffn_strerror(c), str) and g.moe_ffn_strerror(c)
+
+
+def test_forward_events_argument_checks():
+    lib = g.library()
+    p = g.make_problem(64, 256, 512, 8, 2)
+    ok = ctypes.c_void_p(0x1000)
+    assert lib.moe_ffn_forward_events(ctypes.byref(p), ok, ok, ok, ok, ok, ok, 2, None, None, 3) == \
+        g.MOE_FFN_EINVAL_PTR
+    assert lib.moe_ffn_forward_events(ctypes.byref(p), ok, ok, ok, ok, ok, ok, 2, None, None, 5) == \
+        g.MOE_FFN_EINVAL_PTR

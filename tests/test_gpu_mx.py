@@ -1,0 +1,85 @@
+"""MX-fp8 path on the GPU: the quantizer must equal the oracle's MXQ bit for
+bit, and the forward pass must match the oracle within the MX tolerance.
+
+Each side quantizes the same fp32 sources with its own quantizer; the GPU
+forward consumes the GPU's codes and the oracle its own, after the test has
+checked that the two sets of codes are identical."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from tests.parity import MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, sample_tokens, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_gpu(src: np.ndarray):
+    import grouped_gemm_amd as g
+    c, s = g.moe_ffn_mx_quantize(to_gpu(src.astype(np.float32)))
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), s.cpu().numpy()
+
+
+def test_quantizer_bit_exact_random_and_edges():
+    rng = np.random.default_rng(0)
+    a = (rng.standard_normal((512, 256)) * np.exp(rng.normal(0, 4, (512, 1)))).astype(np.float32)
+    a[0] = 0.0                                        # all-zero blocks
+    a[1, :32] = 448.0                                 # amax exactly 448 * 2^0
+    a[2, :32] = np.float32(448.0) * np.float32(2.0 ** -20)
+    a[3] = -a[3]
+    a[4, 5] = 1e30                                    # huge amax in one block
+    a[5] = 1e-40                                      # subnormal inputs
+    a[6, :32] = np.array([(i - 16) * 2.0 ** -9 for i in range(32)], np.float32)
+    pos = np.array([oracle.e4m3_decode(c) for c in range(127)])
+    a[7, :126] = ((pos[1:] + pos[:-1]) / 2)[:126]     # exact ties between codes
+    a[7, 126:] = 448.0
+    c_ref, s_ref = oracle.mx_quantize(a)
+    c, s = _quant_gpu(a)
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(c, c_ref)
+
+
+def _mx_inputs(cfg, seed=0):
+    src = mi.make_mx_sources(cfg, seed)
+    q = {}
+    for n in ("x", "w1", "w2"):
+        c, s = _quant_gpu(src[n])
+        cr, sr = oracle.mx_quantize(src[n])
+        assert np.array_equal(c, cr) and np.array_equal(s, sr), n
+        q[n] = (c, s)
+    return src, q
+
+
+def _case(cfg, tokens=None, seed=0):
+    import grouped_gemm_amd as g
+    print(f"mx forward {cfg.name} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k}", flush=True)
+    src, q = _mx_inputs(cfg, seed)
+    (xc, xs), (w1c, w1s), (w2c, w2s) = q["x"], q["w1"], q["w2"]
+    out = g.moe_ffn_forward(to_gpu(xc), to_gpu(w1c), to_gpu(w2c), to_gpu(src["topk_ids"]),
+                            to_gpu(src["topk_weights"]), mode="split", x_scale=to_gpu(xs),
+                            w1_scale=to_gpu(w1s), w2_scale=to_gpu(w2s))
+    torch.cuda.synchronize()
+    out = gpu_bf16_to_f64(out)
+    ref = mi.bf16_bits_to_f32(oracle.forward_mx(xc, xs, w1c, w1s, w2c, w2s, src["topk_ids"],
+                                                src["topk_weights"], tokens=tokens))
+    if tokens is not None:
+        out, ref = out[tokens], ref[tokens]
+    rel, cos = assert_close(out, ref, tol=MX_TOL, cos_min=MX_COS, what=cfg.name)
+    print(f"  max err / max|ref| = {rel:.3e}, cosine = {cos:.7f}", flush=True)
+
+
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (64, 256, 256, 8, 2, "softmax"),
+    (300, 384, 640, 16, 4, "zipf"),
+    (1, 128, 128, 4, 2, "uniform"),
+])
+def test_mx_forward_small(T, D, H, E, k, routing):
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
+def test_mx_config_sampled():
+    cfg = mi.CONFIGS[5]
+    ids, _ = mi.routing(cfg)
+    _case(cfg, tokens=sample_tokens(cfg, ids, 24))
