@@ -17,7 +17,8 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
+# MOE_FFN_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(_HERE, "libmoe_ffn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_ffn.h")
 
 MOE_FFN_BF16, MOE_FFN_MXFP8 = 0, 1

@@ -112,6 +112,11 @@ struct Bf16Args {
 // `ev` (nullable) points at 3 events recorded after each of the launcher's
 // three kernels.
 hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
+// Decode-shaped GEMM1 / GEMM2 (weights streamed on the MFMA's wide side).
+hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s);
+hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);
+// Average rows per expert at or below which the split pipeline uses them.
+constexpr int64_t kSkinnyMaxRowsPerExpert = 32;
 hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
 
 struct MxArgs {

@@ -364,16 +364,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         const int64_t t = i / cpr;
         const int c = static_cast<int>(i - t * cpr);
         float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; ++j) {
-            const int64_t p = t * k + j;
-            if (p2s[p] < 0) continue;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ypair + p * D + c * 8);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        // slots in groups of 8 with all loads of a group issued before use
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4_t v[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                s[2 * q] += bf16_to_f32(static_cast<uint16_t>(w[q] & 0xffffu));
-                s[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(w[q] >> 16));
+            for (int j = 0; j < 8; ++j) {
+                const int64_t p = t * k + j0 + j;
+                const bool ok = j0 + j < k && p2s[p] >= 0;
+                v[j] = ok ? *reinterpret_cast<const u32x4_t*>(ypair + p * D + c * 8) : u32x4_t{0, 0, 0, 0};
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    s[2 * q] += bf16_to_f32(static_cast<uint16_t>(v[j][q] & 0xffffu));
+                    s[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(v[j][q] >> 16));
+                }
         }
         u32x4_t o;
         o.x = pack_bf16x2(s[0], s[1]);
@@ -410,11 +416,20 @@ inline int mtiles_upper(int64_t P, int E, int bm) {
 
 hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BN1 = 128, BN2 = 128;
-    dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
-    gemm1_swiglu_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
+    const bool skinny = a.P <= kSkinnyMaxRowsPerExpert * a.E;
+    if (skinny) {
+        launch_skinny_gemm1(a, s);
+    } else {
+        dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
+        gemm1_swiglu_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
+    }
     record(ev, 0, s);
-    dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
-    gemm2_weight_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
+    if (skinny) {
+        launch_skinny_gemm2(a, s);
+    } else {
+        dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
+        gemm2_weight_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
+    }
     record(ev, 1, s);
     combine_kernel<<<grid_for(static_cast<int64_t>(a.T) * a.D / 8, 256), 256, 0, s>>>(
         a.ypair, a.rv.pair_to_sorted, a.T, a.k, a.D, a.out);

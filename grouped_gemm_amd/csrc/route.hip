@@ -169,9 +169,129 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
     }
 }
 
+// The whole route step in one workgroup of 16 waves, for small problems
+// (one launch instead of four). Wave w owns the contiguous pair segment
+// [w*seg, (w+1)*seg): it counts its segment into its own LDS row cnt[w][.],
+// one scan turns the rows into per-(wave, expert) start positions, and each
+// wave then places its pairs in order with the same ballot ranking as
+// route_scatter_kernel, so the result is the same stable order.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallMaxExperts = 1024;
+constexpr int64_t kSmallMaxPairs = 16384;
+
+__global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                           int nbits, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ tile_prefix,
+                                                           int32_t* __restrict__ sorted_to_pair,
+                                                           int32_t* __restrict__ pair_to_sorted) {
+    extern __shared__ int32_t cnt[];  // [kSmallWaves][E]
+    __shared__ int sh[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < kSmallWaves * E; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    const int64_t seg = (P + kSmallWaves - 1) / kSmallWaves;
+    const int64_t p0 = w * seg, p1 = p0 + seg < P ? p0 + seg : P;
+    for (int64_t p = p0 + lane; p < p1; p += 64) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[w * E + e], 1);
+    }
+    __syncthreads();
+    // per-expert totals -> offsets and tile prefix sums; thread t owns expert t, so
+    // the scan in thread order is the scan in expert order
+    constexpr int PER = kSmallMaxExperts / 1024;
+    static_assert(PER == 1, "one expert per thread");
+    __shared__ int s_valid_total;
+    int c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = tid + 1024 * i;
+        int tot = 0;
+        if (e < E)
+            for (int v = 0; v < kSmallWaves; ++v) tot += cnt[v * E + e];
+        c[i] = tot;
+    }
+    for (int b = -1; b < kNumTileHeights; ++b) {
+        const int bm = 16 << (b < 0 ? 0 : b);
+        int v[PER], local = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            v[i] = b < 0 ? c[i] : (c[i] + bm - 1) / bm;
+            local += v[i];
+        }
+        int total;
+        int ex = block_excl_scan<16>(local, total, sh);
+        int32_t* dst = b < 0 ? offsets : tile_prefix + b * (E + 1);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + 1024 * i;
+            if (e < E) dst[e] = ex;
+            ex += v[i];
+        }
+        if (tid == 0) dst[E] = total;
+        if (b < 0) {
+            if (tid == 0) s_valid_total = total;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int e = tid + 1024 * i;
+                if (e < E) {
+                    counts[e] = c[i];
+                    // start of each wave's pairs of expert e
+                    int run = dst[e];
+                    for (int v2 = 0; v2 < kSmallWaves; ++v2) {
+                        const int t2 = cnt[v2 * E + e];
+                        cnt[v2 * E + e] = run;
+                        run += t2;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const int64_t valid_total = s_valid_total;
+    for (int64_t i = tid; i < P; i += 1024)
+        if (i >= valid_total) sorted_to_pair[i] = -1;
+    const uint64_t lower = (1ull << lane) - 1ull;
+    int32_t* run = cnt + w * E;
+    for (int64_t base = p0; base < p1; base += 64) {
+        const int64_t p = base + lane;
+        const bool in = p < p1;
+        const int e = in ? ids[p] : -1;
+        const bool valid = in && e >= 0 && e < E;
+        const int key = valid ? e : E;
+        uint64_t same = ~0ull;
+        for (int bb = 0; bb < nbits; ++bb) {
+            const bool bit = (key >> bb) & 1;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(same & lower);
+        const int n = __popcll(same);
+        const bool leader = (same >> lane) == 1ull;
+        const int pos = valid ? run[e] + rank : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid && leader) run[e] += n;
+        __builtin_amdgcn_wave_barrier();
+        if (valid && pos >= 0 && pos < P) {
+            sorted_to_pair[pos] = static_cast<int32_t>(p);
+            pair_to_sorted[p] = pos;
+        } else if (in) {
+            pair_to_sorted[p] = -1;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteBuffers& b, hipStream_t st) {
+    if (b.P <= kSmallMaxPairs && b.E <= kSmallMaxExperts) {
+        int nbits = 0;
+        while ((1 << nbits) <= b.E) ++nbits;
+        const size_t lds = sizeof(int32_t) * kSmallWaves * static_cast<size_t>(b.E);
+        route_small_kernel<<<1, 1024, lds, st>>>(b.ids, b.P, b.E, nbits, b.counts, b.offsets, b.tile_prefix,
+                                                 b.sorted_to_pair, b.pair_to_sorted);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(int32_t) * static_cast<size_t>(b.E);
     int nbits = 0;
     while ((1 << nbits) <= b.E) ++nbits;  // enough bits for ids 0..E (E = sentinel)
