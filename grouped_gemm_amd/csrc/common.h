@@ -115,6 +115,9 @@ hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
 // Decode-shaped GEMM1 / GEMM2 (weights streamed on the MFMA's wide side).
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s);
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);
+// Prefill-shaped GEMM1 / GEMM2 (256-feature tiles, 128 or 256 token rows).
+bool big_gemm_supported(const Bf16Args& a);
+hipError_t launch_big_gemm(const Bf16Args& a, bool gemm1, hipStream_t s);
 // Average rows per expert at or below which the split pipeline uses them.
 constexpr int64_t kSkinnyMaxRowsPerExpert = 32;
 hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);

@@ -22,9 +22,10 @@
 //
 // Tiling: 256 threads = 4 waves in a 2x2 grid, each wave a (BM/2)x(BN/2)
 // block of 32x32x16 bf16 MFMAs. K steps of 64 bf16 (128 bytes per row) are
-// double-buffered in LDS with 16-byte chunks XOR-swizzled by (row & 7), so
-// the MFMA operand reads (32 rows x one 16-byte chunk per half-wave) are
-// bank-conflict free.
+// double-buffered in LDS with 16-byte chunks XOR-swizzled by ((row >> 1) & 7):
+// gfx950's LDS serves 16 lanes of a 16-byte read per cycle from 64 banks, so
+// the 16 rows read together must land in 16 distinct 16-byte bank groups
+// (two 128-byte rows span 256 bytes = one pass over the banks).
 #include "common.h"
 
 namespace moe {
@@ -34,7 +35,7 @@ namespace {
 constexpr int BK = 64;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -417,8 +418,11 @@ inline int mtiles_upper(int64_t P, int E, int bm) {
 hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BN1 = 128, BN2 = 128;
     const bool skinny = a.P <= kSkinnyMaxRowsPerExpert * a.E;
+    const bool big = !skinny && big_gemm_supported(a);
     if (skinny) {
         launch_skinny_gemm1(a, s);
+    } else if (big) {
+        launch_big_gemm(a, true, s);
     } else {
         dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
         gemm1_swiglu_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
@@ -426,6 +430,8 @@ hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     record(ev, 0, s);
     if (skinny) {
         launch_skinny_gemm2(a, s);
+    } else if (big) {
+        launch_big_gemm(a, false, s);
     } else {
         dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
         gemm2_weight_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);

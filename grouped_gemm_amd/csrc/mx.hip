@@ -15,7 +15,8 @@
 // lanes of group g supply the scale of block g for their row or column
 // (layout measured on gfx950 with an in-bounds probe). Tiles are staged
 // like the bf16 kernels: 128 codes (128 bytes) of K per row per stage,
-// 16-byte chunks XOR-swizzled by (row & 7), double-buffered.
+// 16-byte chunks XOR-swizzled by ((row >> 1) & 7) (16 rows read together hit
+// 16 distinct 16-byte bank groups of gfx950's 64-bank LDS), double-buffered.
 //
 // GEMM1's epilogue computes SwiGLU in fp32, stages the act tile in LDS and
 // requantizes it per 32 along H with the same rule (section 7, "The
@@ -29,7 +30,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BKB = 128;  // K bytes (= codes) per stage
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ int acc_row(int lane, int v) { return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3); }
 

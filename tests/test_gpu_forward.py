@@ -52,6 +52,8 @@ def test_tiny_config(mode):
     (1, 128, 128, 4, 2, "uniform"),         # a single token
     (513, 128, 256, 3, 3, "uniform"),       # k = E: every token on every expert
     (260, 256, 128, 1, 1, "softmax"),       # E = 1, k = 1: a dense SwiGLU FFN
+    (700, 512, 384, 4, 2, "zipf"),          # prefill tiles of 128 rows, ragged, skewed
+    (2100, 256, 384, 3, 2, "zipf"),         # prefill tiles of 256 rows, ragged, skewed
 ])
 def test_ragged_shapes(mode, T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing), mode)
