@@ -40,8 +40,6 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
 STAGES = {"split": ["route", "gemm1_swiglu", "gemm2_weight", "combine"],
           "fused": ["route", "acc_fill", "fused_ffn", "acc_to_bf16"]}
-KERNEL_SOURCES = {"gemm1_swiglu": "gemm_bf16.hip", "gemm2_weight": "gemm_bf16.hip",
-                  "fused_ffn": "gemm_bf16.hip", "combine": "gemm_bf16.hip", "route": "route.hip"}
 
 
 def log(*a):
@@ -58,6 +56,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-baseline sample")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count T (crossover sweeps)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (PMC calibration)")
     return ap.parse_args(argv)
@@ -92,21 +92,52 @@ def kernel_work(cfg, mode, hit, dtype):
     }
 
 
-def source_digest(name: str) -> str:
-    path = os.path.join(ROOT, "grouped_gemm_amd", "csrc", KERNEL_SOURCES.get(name, ""))
-    if not os.path.isfile(path):
-        return ""
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+KERNEL_FILES = {"dma_skinny_kernel": "gemm_skinny.hip", "big_gemm_kernel": "gemm_big.hip",
+                "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
+                "gemm1_swiglu_kernel": "gemm_bf16.hip", "gemm2_weight_kernel": "gemm_bf16.hip",
+                "combine_kernel": "gemm_bf16.hip"}
 
 
-def measured_traffic(kernel: str, workload: str):
+def source_digest(symbol: str) -> str:
+    """Digest of the source file defining `symbol` plus the shared header: a
+    change to either invalidates counters stored for that kernel."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "grouped_gemm_amd", "csrc")
+    for f in ("common.h", KERNEL_FILES.get(symbol, "")):
+        path = os.path.join(d, f)
+        if f and os.path.isfile(path):
+            h.update(f.encode())
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_symbol(cfg, mode, stage):
+    """The HIP kernel a stage runs for this workload (mirrors the library's dispatch)."""
+    if mode == "fused":
+        return {"fused_ffn": "fused_bf16_kernel", "acc_fill": "fill_zero_f32_kernel",
+                "acc_to_bf16": "f32_to_bf16_kernel", "route": "route kernels"}[stage]
+    if stage == "route":
+        return "route_small_kernel" if cfg.P <= 16384 and cfg.E <= 1024 else "route_* (4 kernels)"
+    if stage == "combine":
+        return "combine_kernel"
+    g1 = stage == "gemm1_swiglu"
+    if cfg.dtype == "mxfp8":
+        return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
+    if cfg.P <= 32 * cfg.E:
+        return "dma_skinny_kernel"
+    if cfg.D % 256 == 0:
+        return "big_gemm_kernel"
+    return "gemm1_swiglu_kernel" if g1 else "gemm2_weight_kernel"
+
+
+def measured_traffic(stage: str, symbol: str, workload: str):
     """HBM bytes per launch from the committed PMC summary, if it was taken on
     the current source of the kernel and the same workload; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.isfile(path):
         return None
-    rec = json.load(open(path)).get(f"{workload}::{kernel}")
-    if not rec or rec.get("source_sha") != source_digest(kernel):
+    rec = json.load(open(path)).get(f"{workload}::{stage}")
+    if not rec or rec.get("source_sha") != source_digest(symbol):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -148,6 +179,9 @@ def main(argv=None):
     import grouped_gemm_amd as g
 
     cfg = mi.CONFIGS[args.config]
+    if args.tokens:
+        cfg = mi.custom(args.tokens, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, cfg.dtype, cid=cfg.cid,
+                        name=f"{cfg.name}_T{args.tokens}")
     dtype = cfg.dtype
     dev = torch.device("cuda:0")
     log(f"[bench] generating {cfg.name} inputs (seeded)")
@@ -234,7 +268,7 @@ def main(argv=None):
     intensity = dflops / dbytes if dbytes else 0.0
     ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     workload = f"{cfg.name} {dtype} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k}"
-    traffic = measured_traffic(dom, workload)
+    traffic = measured_traffic(dom, kernel_symbol(cfg, mode, dom), workload)
     if intensity > ridge:
         roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
     else:
@@ -242,6 +276,7 @@ def main(argv=None):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["kernel"] = dom
+    roof["kernel_symbol"] = kernel_symbol(cfg, mode, dom)
     roof["algorithmic_bytes"] = dbytes
     roof["algorithmic_flops"] = dflops
     roof["avg_launch_ms"] = stage_ms[dom]

@@ -27,11 +27,15 @@ int check_shape(const moe_ffn_problem* p) {
     return MOE_FFN_OK;
 }
 
-// AUTO: the fused pipeline while the split-K partial rows stay few (small
-// token counts), the split pipeline beyond. The threshold is the measured
-// crossover: with the current kernels the split pipeline is as fast or
-// faster at every measured size (128 to 1M routed pairs), so AUTO is SPLIT.
-constexpr int64_t kFusedMaxPairs = 0;
+// AUTO picks the fused pipeline only where it measured faster on MI355X:
+// expert weights small enough to stay cache-resident (the 8-expert,
+// D=256, H=512 case: 6 MB) and few routed pairs. With weights that stream
+// from HBM the split pipeline won at every measured token count (16 to
+// 16384 tokens at D=2048, H=768, 128 experts; and the 64-token decode
+// shape), because the fused kernel's split-K partial rows cost more
+// atomic traffic than writing the activation once.
+constexpr int64_t kFusedMaxPairs = 4096;
+constexpr int64_t kFusedMaxWeightBytes = int64_t(16) << 20;
 
 int resolve(const moe_ffn_problem* p, int mode) {
     if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
@@ -40,7 +44,9 @@ int resolve(const moe_ffn_problem* p, int mode) {
         return MOE_FFN_SPLIT;
     }
     if (mode != MOE_FFN_AUTO) return mode;
-    return static_cast<int64_t>(p->T) * p->topk <= kFusedMaxPairs ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
+    const int64_t weight_bytes = int64_t(p->E) * 3 * p->H * p->D * 2;
+    const bool small = static_cast<int64_t>(p->T) * p->topk <= kFusedMaxPairs && weight_bytes <= kFusedMaxWeightBytes;
+    return small ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
 }
 
 struct RoutePlan {
