@@ -77,7 +77,7 @@ struct Plan {
     int mode;
     RoutePlan route;
     size_t counts, offsets, s2p, p2s;
-    size_t act, act_s, ypair, acc32;
+    size_t act, act_s, ypair, acc32, mtiles;
     size_t total;
 };
 
@@ -91,7 +91,7 @@ Plan make_plan(const moe_ffn_problem* p, int mode) {
     pl.offsets = off;
     off = align_up(off + sizeof(int32_t) * (p->E + 1));
     pl.s2p = off;
-    off = align_up(off + sizeof(int32_t) * P);
+    off = align_up(off + sizeof(int32_t) * (P + moe::kRowMapPad));
     pl.p2s = off;
     off = align_up(off + sizeof(int32_t) * P);
     pl.route = plan_route(p->T, p->topk, p->E, off);
@@ -106,6 +106,10 @@ Plan make_plan(const moe_ffn_problem* p, int mode) {
         }
         pl.ypair = off;
         off = align_up(off + 2 * static_cast<size_t>(P) * p->D);
+        if (p->dtype == MOE_FFN_BF16) {
+            pl.mtiles = off;
+            off = align_up(off + 16 * static_cast<size_t>(moe::big_gemm_mtile_capacity(P, p->E)));
+        }
     } else {
         pl.acc32 = off;
         off = align_up(off + 4 * static_cast<size_t>(p->T) * p->D);
@@ -250,6 +254,7 @@ MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, 
         if (m == MOE_FFN_SPLIT) {
             a.act = at<uint16_t>(ws, pl.act);
             a.ypair = at<uint16_t>(ws, pl.ypair);
+            a.mtiles = at<int32_t>(ws, pl.mtiles);
             e = moe::launch_split_bf16(a, st, stage_ev);
         } else {
             a.acc32 = at<float>(ws, pl.acc32);

@@ -106,6 +106,7 @@ struct Bf16Args {
     RouteView rv;
     uint16_t* act;     // [P, H]   split only
     uint16_t* ypair;   // [P, D]   split only: weighted expert outputs in pair order
+    int32_t* mtiles;   // split only: m-tile table of the prefill GEMMs, big_gemm_mtile_capacity x int4
     float* acc32;      // [T, D]   fused only
     uint16_t* out;     // [T, D]
 };
@@ -117,6 +118,12 @@ hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s);
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);
 // Prefill-shaped GEMM1 / GEMM2 (256-feature tiles, 128 or 256 token rows).
 bool big_gemm_supported(const Bf16Args& a);
+// Entries (int4 each) the m-tile table needs for P routed pairs and E experts.
+int64_t big_gemm_mtile_capacity(int64_t P, int E);
+// Entries past P that sorted_to_pair in the workspace must hold (a tile's
+// row-map window may run past the last routed row; the extra entries are
+// read and clamped, never written).
+constexpr int64_t kRowMapPad = 256;
 hipError_t launch_big_gemm(const Bf16Args& a, bool gemm1, hipStream_t s);
 // Average rows per expert at or below which the split pipeline uses them.
 constexpr int64_t kSkinnyMaxRowsPerExpert = 32;

@@ -1,43 +1,59 @@
 // Prefill-shaped bf16 grouped GEMMs: many routed rows per expert.
 //
 // With hundreds to thousands of rows per expert the pass is bound by the
-// matrix cores. A workgroup (4 waves) computes a tile of BM token rows x 256
-// weight rows (GEMM1: 128 gate + 128 up rows, the gate/up pairing of "Prime
-// Flash MoE", section 2, Trick 1; GEMM2: 256 output features). The weights
-// are the MFMA's A operand (v_mfma_f32_32x32x16_bf16), so each lane's
-// results are 4 consecutive features of one token and the epilogues write
-// them as packed 8-byte rows.
+// matrix cores. A tile is BM token rows x 256 weight rows (GEMM1: 128 gate +
+// 128 up rows, the gate/up pairing of "Prime Flash MoE", section 2, Trick 1;
+// GEMM2: 256 output features). The weights are the MFMA's A operand
+// (v_mfma_f32_32x32x16_bf16), so each lane's results are 4 consecutive
+// features of one token. Eight waves (two per SIMD) split a tile into two
+// feature halves x four token groups: 128 features x BM/4 tokens per wave.
 //
-// Each wave owns 128 features x BM/2 tokens: per 16-wide k-step it reads 4
-// weight and BM/64 token fragments from LDS for 4*BM/64 MFMAs.
+// Persistent schedule. One workgroup per CU walks a list of tiles. Workgroup
+// b runs on XCD b % 8 (8 XCDs, each with its own L2); the logical tiles,
+// n-tile fastest, are split into 8 contiguous ranges, and the workgroups of
+// an XCD take every (workgroups per XCD)-th tile of that XCD's range, so the
+// n-tiles sharing a token tile run side by side and reuse it from one L2.
 //
 // K steps of 32 (64 bytes per row) go through a ring of 4 LDS stages filled
 // by global->LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at
-// base + 16*i; 16 rows x 64 bytes per instruction), so three stages are in
-// flight while one is consumed: enough lead to cover L2 misses. The 16-byte
-// chunks of a row are XOR-swizzled by ((row >> 2) & 3): gfx950's LDS serves
-// 16 lanes of a 16-byte read per cycle from 64 banks (256 bytes), and the 16
-// consecutive rows a fragment read touches then fall in 16 distinct 16-byte
-// bank groups. The four stages are distinct LDS objects and the loop is
-// unrolled by four, so the compiler sees that the fragment reads of one stage
-// never alias the DMA filling another; the waits are explicit per-wave
-// vmcnt budgets and the barrier carries no memory fence (a fence would wait
-// for every DMA in flight).
+// base + 16*i; 16 rows x 64 bytes per instruction): three stages are in
+// flight while one is consumed, and the one barrier per stage sits between
+// the MFMAs of the stage's two k-halves (see ring_step). The ring runs on
+// across tiles: the next tile's row map (and, for GEMM2, its routing
+// weights) arrive by DMA during the current tile's first steps, and its
+// first four stages are issued during the current tile's last four, so
+// neither the tile lookup nor the first loads' latency sits between two
+// tiles. Results are stored from
+// registers (8 bytes per lane; a 128-byte line is written by 8 stores of one
+// wave in a row, and the L2 merges them).
+//
+// The 16-byte chunks of a staged row are XOR-swizzled by ((row >> 2) & 3):
+// gfx950's LDS serves 16 lanes of a 16-byte read per cycle from 64 banks, and
+// the 16 consecutive rows a fragment read touches then fall in 16 distinct
+// 16-byte bank groups. The four stages are distinct LDS objects and the loop
+// is unrolled by four. The waits are explicit per-wave vmcnt budgets and the
+// barrier carries no memory fence (a fence would wait for every DMA in
+// flight).
 //
 // Token rows of GEMM1 are gathered on load (row r reads token
 // sorted_to_pair[row0 + r] / k); rows past an expert's count read a valid
-// row and are not stored. Tiles are mapped to workgroups XCD by XCD (see
-// xcd_tile) so that the tiles sharing a token tile reuse it from one L2.
+// row and are not stored.
 #include "common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BK = 32;    // K per stage
-constexpr int RB = 64;    // bytes per tile row per stage
-constexpr int BN = 256;   // weight rows per tile
+#ifndef MOE_BIG_WAVES
+#define MOE_BIG_WAVES 8
+#endif
+constexpr int W = MOE_BIG_WAVES;   // waves per workgroup (2 feature halves x W/2 token groups)
+constexpr int kThreads = 64 * W;
+constexpr int BK = 32;             // K per stage
+constexpr int RB = 64;             // bytes per tile row per stage
+constexpr int BN = 256;            // weight rows per tile
+constexpr int kInfoCap = 512;      // tile descriptors held in LDS at a time
+constexpr int kMinPipelinedKT = 8; // K steps a tile needs for the in-loop hand-over
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -49,13 +65,16 @@ __device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 2
 
 template <int BM>
 struct Big {
-    static constexpr int TB = BM / 2;          // tokens per wave
+    static constexpr int TB = BM / (W / 2);    // tokens per wave
     static constexpr int NT = TB / 32;         // token blocks per wave
     static constexpr int NF = 4;               // feature blocks per wave (128 features)
-    static constexpr int A_INS = BM / 16 / 4;  // token-row DMA instructions per wave per stage
-    static constexpr int B_INS = BN / 16 / 4;  // weight-row DMA instructions per wave per stage
+    static constexpr int A_INS = BM / 16 / W;  // token-row DMA instructions per wave per stage
+    static constexpr int B_INS = BN / 16 / W;  // weight-row DMA instructions per wave per stage
     static constexpr int L = A_INS + B_INS;    // DMA instructions per wave per stage
+    static constexpr int PW = BM / 64;         // waves that move one BM-entry int/float vector (64 per wave)
     static constexpr int TOK_BYTES = BM * RB, W_BYTES = BN * RB;
+    static_assert(NT >= 1 && A_INS >= 1 && A_INS * 16 * W == BM && B_INS * 16 * W == BN, "tile split");
+    static_assert(PW >= 1 && PW <= W, "row-vector DMA waves");
 };
 
 template <int BM>
@@ -64,30 +83,74 @@ struct StageBuf {
     uint8_t wt[Big<BM>::W_BYTES];
 };
 
-// DMA sources: wave-uniform bases plus 32-bit per-lane byte offsets (the saddr
-// form of the DMA). Token rows need one offset per instruction (they may be
-// gathered); weight rows are consecutive (instruction j reads 16 rows after
-// instruction j-1: a fixed stride).
+// Per-tile DMA sources: wave-uniform bases (scalar registers) plus 32-bit
+// per-lane byte offsets. Token rows need one offset per instruction (they may
+// be gathered); weight rows are consecutive and share `boff` + j * bstride,
+// which does not change from tile to tile.
+template <int BM>
 struct DmaSrc {
     const char* abase;
     const char* bbase;
-    uint32_t bstride;
+    uint32_t aoff[Big<BM>::A_INS];
 };
 
+// A tile of this workgroup's list.
+struct TileDesc {
+    int expert, row0, rows, ntile;
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A wave-uniform pointer moved to scalar registers. readfirstlane returns a
+// signed int: each half goes through uint32_t so the low half is not
+// sign-extended into the high one.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v))));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+    return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Global->LDS DMA instructions. They are written in assembly so that the
+// compiler's wait-count insertion does not see an LDS write in flight: it
+// cannot tell which stage buffer a DMA fills once the loop's back edge merges
+// its state, and would then make the next fragment read wait for every DMA in
+// flight, draining the ring. The explicit per-wave vmcnt waits below order
+// the ring. M0 holds the LDS address; nothing else in these kernels uses M0.
+// dma16: lane i's 16 bytes at sbase + voff land at lds + 16 * i.
+// dma4:  lane i's 4 bytes at sbase + voff land at lds + 4 * i.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int BM>
-__device__ __forceinline__ void issue_stage(StageBuf<BM>& b, const DmaSrc& src, const uint32_t* aoff, uint32_t boff,
-                                            int kt) {
+__device__ __forceinline__ void issue_stage(StageBuf<BM>& b, const DmaSrc<BM>& src, uint32_t boff, uint32_t bstride,
+                                            int kt, uint32_t wave) {
     using C = Big<BM>;
-    const int wave = threadIdx.x >> 6;
     const char* ab = src.abase + kt * RB;
     const char* bb = src.bbase + kt * RB;
+    const uint32_t tl = lds_addr(b.tok) + wave * (C::A_INS * 1024);
+    const uint32_t wl = lds_addr(b.wt) + wave * (C::B_INS * 1024);
 #pragma unroll
-    for (int j = 0; j < C::A_INS; ++j)
-        __builtin_amdgcn_global_load_lds(ab + aoff[j], (lds_ptr_t)(b.tok + (wave * C::A_INS + j) * 1024), 16, 0, 0);
+    for (int j = 0; j < C::A_INS; ++j) dma16(ab, src.aoff[j], tl + j * 1024);
 #pragma unroll
-    for (int j = 0; j < C::B_INS; ++j)
-        __builtin_amdgcn_global_load_lds(bb + (boff + j * src.bstride), (lds_ptr_t)(b.wt + (wave * C::B_INS + j) * 1024),
-                                         16, 0, 0);
+    for (int j = 0; j < C::B_INS; ++j) dma16(bb, boff + j * bstride, wl + j * 1024);
 }
 
 // wait until at most n vector-memory operations of this wave are in flight
@@ -95,6 +158,13 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// the same, and also until this wave's LDS reads have returned
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
 // s_barrier without a memory fence; the asm statements stop the compiler from
@@ -105,225 +175,408 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Fragment reads of one stage: every fragment's 32 rows start at a multiple
-// of 16, so a lane's row is (row base) + (lane & 31) and its swizzle term is
-// ((lane & 31) >> 2) & 3.
+// One 16-wide k-half of a stage in registers: 4 weight fragments (32 rows
+// each) and NT token fragments.
 template <int BM>
-__device__ __forceinline__ void compute_stage(const StageBuf<BM>& b, const int (&frow)[4], int tok_row0,
-                                              f32x16_t (&acc)[4][Big<BM>::NT]) {
+struct Frag {
+    bf16x8_t w[Big<BM>::NF];
+    bf16x8_t t[Big<BM>::NT];
+};
+
+// Fragment reads of k-half kk of a stage: every fragment's 32 rows start at a
+// multiple of 16, so a lane's row is (row base) + (lane & 31) and its swizzle
+// term is ((lane & 31) >> 2) & 3.
+template <int BM>
+__device__ __forceinline__ void read_frag(const StageBuf<BM>& b, int kk, const int (&frow)[4], int tok_row0,
+                                          Frag<BM>& f) {
     using C = Big<BM>;
     const int lane = threadIdx.x & 63;
     const int lrow = (lane & 31) * RB;
+    const int coff = swz_chunk(lane & 31, 2 * kk + (lane >> 5)) << 4;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        const int coff = swz_chunk(lane & 31, 2 * kk + (lane >> 5)) << 4;
-        bf16x8_t wf[C::NF], tf[C::NT];
+    for (int i = 0; i < C::NF; ++i) f.w[i] = *reinterpret_cast<const bf16x8_t*>(b.wt + frow[i] * RB + lrow + coff);
 #pragma unroll
-        for (int f = 0; f < C::NF; ++f) wf[f] = *reinterpret_cast<const bf16x8_t*>(b.wt + frow[f] * RB + lrow + coff);
+    for (int i = 0; i < C::NT; ++i)
+        f.t[i] = *reinterpret_cast<const bf16x8_t*>(b.tok + (tok_row0 + 32 * i) * RB + lrow + coff);
+}
+
+template <int BM>
+__device__ __forceinline__ void mfma_frag(const Frag<BM>& f, f32x16_t (&acc)[4][Big<BM>::NT]) {
+    using C = Big<BM>;
 #pragma unroll
-        for (int t = 0; t < C::NT; ++t)
-            tf[t] = *reinterpret_cast<const bf16x8_t*>(b.tok + (tok_row0 + 32 * t) * RB + lrow + coff);
+    for (int i = 0; i < C::NF; ++i)
 #pragma unroll
-        for (int f = 0; f < C::NF; ++f)
-#pragma unroll
-            for (int t = 0; t < C::NT; ++t) acc[f][t] = mfma32(wf[f], tf[t], acc[f][t]);
+        for (int t = 0; t < C::NT; ++t) acc[i][t] = mfma32(f.w[i], f.t[t], acc[i][t]);
+}
+
+// Everything a workgroup keeps across the steps of a tile.
+template <int BM>
+struct Ring {
+    DmaSrc<BM> src, nsrc;     // this tile's and the next tile's DMA sources
+    uint32_t boff, bstride;   // weight-row offsets (the same for every tile)
+    uint32_t wave;            // wave index (uniform)
+    int KT;                   // K steps per tile
+    bool pipelined;           // KT is long enough for the in-loop hand-over
+    bool has_next;
+    bool cont;                // the next tile's stages follow this tile's in the ring
+    TileDesc next;            // the next tile (valid when has_next)
+    int nb;                   // row-vector buffer of the next tile (0 or 1)
+};
+
+// DMA of a tile's row map: sorted_to_pair[row0 .. row0 + BM) -> pairs[0 .. BM).
+// The map in the workspace is padded by 256 entries, so the window never
+// leaves it; entries past the expert's rows are clamped before use.
+template <int BM>
+__device__ __forceinline__ void dma_row_map(const Bf16Args& a, int row0, int32_t* pairs, uint32_t wave) {
+    if (wave < static_cast<uint32_t>(Big<BM>::PW)) {
+        const uint32_t lane = threadIdx.x & 63;
+        dma4(uniform_ptr(a.rv.sorted_to_pair + row0), (wave * 64 + lane) * 4u, lds_addr(pairs) + wave * 256);
     }
 }
 
-// Consume stage kt from buffer `cur`, after issuing stage kt+3 into `nxt`
-// (the buffer consumed one step earlier, free once every wave has passed
-// this step's barrier). Before the barrier each wave waits until its own DMAs
-// of stage kt are done: the newer stages it has issued (kt+1, kt+2 while they
-// exist) may stay in flight.
+// DMA of a tile's routing weights: wts[pair of row r] -> w[r] (GEMM2).
 template <int BM>
-__device__ __forceinline__ void ring_step(const StageBuf<BM>& cur, StageBuf<BM>& nxt, const DmaSrc& src,
-                                          const uint32_t* aoff, uint32_t boff, int kt, int KT, const int (&frow)[4],
-                                          int tok_row0, f32x16_t (&acc)[4][Big<BM>::NT]) {
+__device__ __forceinline__ void dma_row_weights(const Bf16Args& a, const int32_t* pairs, float* w, uint32_t wave) {
+    if (wave < static_cast<uint32_t>(Big<BM>::PW)) {
+        const int lane = threadIdx.x & 63;
+        const int p = clamp_pair(pairs[wave * 64 + lane], a.P);
+        dma4(uniform_ptr(a.wts), static_cast<uint32_t>(p) * 4u, lds_addr(w) + wave * 256);
+    }
+}
+
+// DMA sources of a tile. GEMM1: token rows gathered through the row map;
+// weight rows 0..127 are gate rows h0.., 128..255 up rows H + h0.. (a wave's
+// rows never straddle the two). GEMM2: act rows in sorted order. Offsets are
+// 32-bit: the host only picks this kernel when x, act and one expert's
+// weights each span < 4 GiB. Instruction j of a wave covers tile rows
+// (wave * INS + j) * 16 + lane / 4, chunk lane & 3.
+template <int BM, bool GEMM1>
+__device__ __forceinline__ void make_src(const Bf16Args& a, const TileDesc& t, const int32_t* pairs, uint32_t wave,
+                                         DmaSrc<BM>& s) {
+    using C = Big<BM>;
+    const int lane = threadIdx.x & 63;
+    const int K = GEMM1 ? a.D : a.H;
+    s.abase = uniform_ptr(GEMM1 ? a.x : a.act + static_cast<int64_t>(t.row0) * a.H);
+#pragma unroll
+    for (int j = 0; j < C::A_INS; ++j) {
+        const int row = (static_cast<int>(wave) * C::A_INS + j) * 16 + lane / 4;
+        const uint32_t r = GEMM1 ? static_cast<uint32_t>(clamp_pair(pairs[row], a.P) / a.k) * a.D
+                                 : static_cast<uint32_t>(row < t.rows ? row : 0) * a.H;
+        s.aoff[j] = r * 2 + swz_chunk(row, lane & 3) * 16;
+    }
+    const int row0 = static_cast<int>(wave) * C::B_INS * 16;  // first weight-tile row of this wave
+    if (GEMM1) {
+        const int h0 = t.ntile * 128;
+        const int grow0 = row0 < 128 ? h0 + row0 : a.H + h0 + row0 - 128;
+        s.bbase = uniform_ptr(a.w1 + (static_cast<int64_t>(t.expert) * 2 * a.H + grow0) * K);
+    } else {
+        s.bbase = uniform_ptr(a.w2 + (static_cast<int64_t>(t.expert) * a.D + t.ntile * 256 + row0) * K);
+    }
+}
+
+// One ring step. The barrier sits in the middle of stage kt's MFMAs, so a
+// wave never comes out of it with nothing to compute:
+//   read k-half 1 of stage kt (buffer cur);  MFMAs of k-half 0 (read last step)
+//   wait for this wave's DMAs of stage kt+1 and its own LDS reads;  barrier
+//   issue stage kt+4 into cur (every wave is done reading it);
+//   read k-half 0 of stage kt+1 (buffer nxt);  MFMAs of k-half 1
+// Stage kt+4 belongs to this tile, or to the next one once this tile has
+// none left, so the ring runs on across tiles.
+//
+// Waits: before the barrier each wave waits until its own DMAs of stage kt+1
+// are done; the stages it issued after it (kt+2, kt+3, while they exist) may
+// stay in flight. Loads, LDS DMA included, complete in order, so this holds
+// with the previous tile's result stores or the few row-vector DMAs also in
+// flight: at most 2L operations outstanding leaves at least as many of this
+// wave's loads done as there were older ones.
+//
+// Hand-over (pipelined tiles): step 0 fetches the next tile's row map,
+// complete by step 3's barrier; step 3 builds the next tile's DMA sources
+// from it and fetches its routing weights (GEMM2), complete by step 6's
+// barrier; steps KT-4 .. KT-1 issue its stages 0..3.
+template <int BM, bool GEMM1>
+__device__ __forceinline__ void ring_step(const Bf16Args& a, Ring<BM>& r, StageBuf<BM>& cur,
+                                          const StageBuf<BM>& nxt, int kt, int32_t (*pairs)[BM], float (*wrow)[BM],
+                                          const int (&frow)[4], int tok_row0, Frag<BM>& f0, Frag<BM>& f1,
+                                          f32x16_t (&acc)[4][Big<BM>::NT]) {
     constexpr int L = Big<BM>::L;
-    if (kt + 2 < KT) wait_vm<2 * L>();
-    else if (kt + 1 < KT) wait_vm<L>();
-    else wait_vm<0>();
+    read_frag<BM>(cur, 1, frow, tok_row0, f1);
+    mfma_frag<BM>(f0, acc);
+    const bool more1 = kt + 1 < r.KT || r.cont;  // stage kt+1 exists
+    if (kt + 3 < r.KT || r.cont) wait_vm_lds<2 * L>();
+    else if (kt + 2 < r.KT) wait_vm_lds<L>();
+    else wait_vm_lds<0>();
     bare_barrier();
-    if (kt + 3 < KT) issue_stage<BM>(nxt, src, aoff, boff, kt + 3);
-    compute_stage<BM>(cur, frow, tok_row0, acc);
+    if (r.cont) {
+        if (kt == 0) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
+        if (kt == 3) {
+            make_src<BM, GEMM1>(a, r.next, pairs[r.nb], r.wave, r.nsrc);
+            if (!GEMM1) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
+        }
+    }
+    if (kt + 4 < r.KT) issue_stage<BM>(cur, r.src, r.boff, r.bstride, kt + 4, r.wave);
+    else if (r.cont) issue_stage<BM>(cur, r.nsrc, r.boff, r.bstride, kt + 4 - r.KT, r.wave);
+    if (more1) read_frag<BM>(nxt, 0, frow, tok_row0, f0);
+    mfma_frag<BM>(f1, acc);
 }
 
-// 1-D grid of at least (m-tiles upper bound) x NY blocks, a multiple of 8.
-// Workgroup b runs on XCD b % 8 (8 XCDs, each with its own L2). The actual
-// tile count T is read from the route step; the logical tiles, n-tile
-// fastest, are split into 8 contiguous ranges of ceil(T*NY/8), and XCD x walks
-// range x in order. The NY tiles sharing one token tile then run back to
-// back on one XCD and reuse it from that XCD's L2.
+// The stage buffers come in as restrict pointers: with them, the compiler
+// knows the fragment reads of one stage never alias the others.
+template <int BM, bool GEMM1>
+__device__ __forceinline__ void main_loop(const Bf16Args& a, Ring<BM>& r, StageBuf<BM>* __restrict__ b0,
+                                          StageBuf<BM>* __restrict__ b1, StageBuf<BM>* __restrict__ b2,
+                                          StageBuf<BM>* __restrict__ b3, int32_t (*pairs)[BM], float (*wrow)[BM],
+                                          const int (&frow)[4], int tok_row0, Frag<BM>& f0, Frag<BM>& f1,
+                                          f32x16_t (&acc)[4][Big<BM>::NT]) {
+    // KT is a multiple of 4 (K is a multiple of 128): the unrolled body needs
+    // no exit in the middle, which would make the compiler shuttle the
+    // accumulators between registers at the loop head. Every tile starts at
+    // buffer 0.
+    for (int kt = 0; kt < r.KT; kt += 4) {
+        ring_step<BM, GEMM1>(a, r, *b0, *b1, kt, pairs, wrow, frow, tok_row0, f0, f1, acc);
+        ring_step<BM, GEMM1>(a, r, *b1, *b2, kt + 1, pairs, wrow, frow, tok_row0, f0, f1, acc);
+        ring_step<BM, GEMM1>(a, r, *b2, *b3, kt + 2, pairs, wrow, frow, tok_row0, f0, f1, acc);
+        ring_step<BM, GEMM1>(a, r, *b3, *b0, kt + 3, pairs, wrow, frow, tok_row0, f0, f1, acc);
+    }
+}
+
+// Issue stages 0..3 of a tile, wait for stage 0 and read its first k-half.
 template <int BM>
-__device__ __forceinline__ bool xcd_tile(const RouteView& rv, int E, int ny, int& mtile, int& ntile) {
-    const int tiles = rv.tile_prefix[tile_height_index(BM) * (E + 1) + E];
-    const int total = tiles * ny;
-    const int per = (total + 7) / 8;
-    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if ((blockIdx.x >> 3) >= per || logical >= total) return false;
-    mtile = logical / ny;
-    ntile = logical - mtile * ny;
-    return true;
+__device__ __forceinline__ void ring_start(Ring<BM>& r, const DmaSrc<BM>& src, StageBuf<BM>& b0, StageBuf<BM>& b1,
+                                           StageBuf<BM>& b2, StageBuf<BM>& b3, const int (&frow)[4], int tok_row0,
+                                           Frag<BM>& f0) {
+    constexpr int L = Big<BM>::L;
+    issue_stage<BM>(b0, src, r.boff, r.bstride, 0, r.wave);
+    issue_stage<BM>(b1, src, r.boff, r.bstride, 1, r.wave);
+    issue_stage<BM>(b2, src, r.boff, r.bstride, 2, r.wave);
+    issue_stage<BM>(b3, src, r.boff, r.bstride, 3, r.wave);
+    wait_vm<3 * L>();
+    bare_barrier();
+    read_frag<BM>(b0, 0, frow, tok_row0, f0);
 }
 
-// Staged output rows: [tokens][128 features] bf16, 256 bytes per row, 16-byte
-// chunks XOR-swizzled by (token & 15).
-__device__ __forceinline__ int stage_off(int tok, int col) {
-    return tok * 256 + ((((col >> 3) ^ (tok & 15)) << 4) | ((col & 7) << 1));
+// Results of a tile, stored from registers. acc[f][t][4i + j] holds feature
+// frow[f] + 8i + 4*(lane>>5) + j of token row tok_row0 + 32t + (lane & 31).
+// GEMM1 writes act = silu(gate) * up (bf16) at act[row0 + row][h0 + col];
+// GEMM2 writes w * y (bf16) at ypair[pair][n0 + feature].
+template <int BM, bool GEMM1>
+__device__ __forceinline__ void epilogue(const Bf16Args& a, const TileDesc& t, const int32_t* pairs, const float* w,
+                                         int tok_row0, int wf, const f32x16_t (&acc)[4][Big<BM>::NT]) {
+    using C = Big<BM>;
+    const int lane = threadIdx.x & 63;
+    const int g4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int tb = 0; tb < C::NT; ++tb) {
+        const int row = tok_row0 + 32 * tb + (lane & 31);
+        if (row >= t.rows) continue;
+        if (GEMM1) {
+            uint16_t* dst = a.act + static_cast<int64_t>(t.row0 + row) * a.H + t.ntile * 128 + 64 * wf + g4;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = acc[f][tb][4 * i + j];
+                        v[j] = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][4 * i + j];
+                    }
+                    *reinterpret_cast<uint2*>(dst + 32 * f + 8 * i) =
+                        uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                }
+        } else {
+            const int p = clamp_pair(pairs[row], a.P);
+            const float wt = w[row];
+            uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + t.ntile * 256 + 128 * wf + g4;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x16_t& c = acc[f][tb];
+                    *reinterpret_cast<uint2*>(dst + 32 * f + 8 * i) =
+                        uint2{pack_bf16x2(c[4 * i] * wt, c[4 * i + 1] * wt),
+                              pack_bf16x2(c[4 * i + 2] * wt, c[4 * i + 3] * wt)};
+                }
+        }
+    }
+}
+
+// Descriptors of this workgroup's tiles c0 .. c0 + kInfoCap - 1 into LDS.
+__device__ __forceinline__ void load_descs(const int4* mtiles, int first, int stride, int ny, int count, int c0,
+                                           TileDesc* desc) {
+    for (int i = threadIdx.x; i < kInfoCap && c0 + i < count; i += kThreads) {
+        const int logical = first + (c0 + i) * stride;
+        const int m = logical / ny;
+        const int4 d = mtiles[m];
+        desc[i] = TileDesc{d.x, d.y, d.z, logical - m * ny};
+    }
+}
+
+__device__ __forceinline__ TileDesc uniform_desc(const TileDesc& d) {
+    return TileDesc{uniform_int(d.expert), uniform_int(d.row0), uniform_int(d.rows), uniform_int(d.ntile)};
 }
 
 template <int BM, bool GEMM1>
-__global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a) {
+__global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const int4* __restrict__ mtiles) {
     using C = Big<BM>;
-    constexpr int HALF = BM / 2;  // tokens staged in each of buffers 0 and 1
-    static_assert(HALF * 256 <= static_cast<int>(sizeof(StageBuf<BM>)), "output staging fits two stage buffers");
     __shared__ __attribute__((aligned(16))) StageBuf<BM> buf0;
     __shared__ __attribute__((aligned(16))) StageBuf<BM> buf1;
     __shared__ __attribute__((aligned(16))) StageBuf<BM> buf2;
     __shared__ __attribute__((aligned(16))) StageBuf<BM> buf3;
-    __shared__ int32_t sRow[BM];
-    __shared__ float sW[BM];
-    const int ny = GEMM1 ? a.H / 128 : a.D / 256;
-    int mtile, ntile;
-    if (!xcd_tile<BM>(a.rv, a.E, ny, mtile, ntile)) return;
-    MTile mt;
-    if (!find_mtile<BM>(a.rv, a.E, mtile, mt)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wtok = wave >> 1, wf = wave & 1;
-    for (int r = tid; r < BM; r += kThreads) {
-        const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P);
-        sRow[r] = GEMM1 ? p / a.k : p;
-        if (!GEMM1) sW[r] = a.wts[p];
-    }
-    __syncthreads();
-    const int K = GEMM1 ? a.D : a.H;
-    const int h0 = ntile * 128;  // GEMM1: act columns of this tile
-    const int n0 = ntile * 256;  // GEMM2: output features of this tile
+    __shared__ __attribute__((aligned(16))) int32_t sPair[2][BM];
+    __shared__ __attribute__((aligned(16))) float sW[2][BM];
+    __shared__ TileDesc sDesc[kInfoCap];
 
-    // DMA sources. Offsets are 32-bit: the host only picks this kernel when x,
-    // act and one expert's weights each span < 4 GiB. Instruction j of a wave
-    // covers tile rows (wave * INS + j) * 16 + lane / 4, chunk lane & 3.
-    DmaSrc src;
-    uint32_t aoff[C::A_INS];
-    src.abase = reinterpret_cast<const char*>(GEMM1 ? a.x : a.act + static_cast<int64_t>(mt.row0) * a.H);
-#pragma unroll
-    for (int j = 0; j < C::A_INS; ++j) {
-        const int row = (wave * C::A_INS + j) * 16 + lane / 4;
-        const uint32_t r = GEMM1 ? static_cast<uint32_t>(sRow[row]) * a.D
-                                 : static_cast<uint32_t>(row < mt.rows ? row : 0) * a.H;
-        aoff[j] = r * 2 + swz_chunk(row, lane & 3) * 16;
-    }
-    uint32_t boff;
-    {
-        const int row0 = wave * C::B_INS * 16;  // first weight-tile row of this wave's instructions
-        const int row = row0 + lane / 4;        // later instructions: +16 rows, same swizzle term
-        if (GEMM1) {
-            // tile rows 0..127 are gate rows h0.., 128..255 up rows H+h0..; a wave's 64 rows never straddle
-            const int64_t e0 = static_cast<int64_t>(mt.expert) * 2 * a.H;
-            const int grow0 = row0 < 128 ? h0 + row0 : a.H + h0 + row0 - 128;
-            src.bbase = reinterpret_cast<const char*>(a.w1 + (e0 + grow0) * K);
-        } else {
-            src.bbase = reinterpret_cast<const char*>(a.w2 + (static_cast<int64_t>(mt.expert) * a.D + n0 + row0) * K);
-        }
-        boff = static_cast<uint32_t>(lane / 4) * K * 2 + swz_chunk(row, lane & 3) * 16;
-        src.bstride = 16u * K * 2;
-    }
+    // This workgroup's tiles: logical tiles first, first + stride, ... of its
+    // XCD's range. The tile count comes from the route step.
+    const int ny = GEMM1 ? a.H / 128 : a.D / 256;
+    const int total = a.rv.tile_prefix[tile_height_index(BM) * (a.E + 1) + a.E] * ny;
+    const int per = (total + 7) / 8;
+    const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3;
+    const int first = xcd * per + (blockIdx.x >> 3);
+    const int end = min(total, (xcd + 1) * per);
+    const int count = first < end ? (end - first + stride - 1) / stride : 0;
+    if (count == 0) return;
+
+    const int tid = threadIdx.x, wave_v = tid >> 6;
+    const int wtok = wave_v >> 1, wf = wave_v & 1;
     int frow[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
         frow[f] = GEMM1 ? (f < 2 ? 64 * wf + 32 * f : 128 + 64 * wf + 32 * (f - 2)) : 128 * wf + 32 * f;
     const int tok_row0 = wtok * C::TB;
-    f32x16_t acc[4][C::NT];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) acc[f][t] = f32x16_t{};
 
-    // K / 32 is a multiple of 4 (K is a multiple of 128): the unrolled body
-    // needs no exit in the middle, which would make the compiler shuttle the
-    // accumulators between AGPRs and VGPRs at the loop head.
-    const int KT = K / BK;
-    issue_stage<BM>(buf0, src, aoff, boff, 0);
-    issue_stage<BM>(buf1, src, aoff, boff, 1);
-    issue_stage<BM>(buf2, src, aoff, boff, 2);
-    for (int kt = 0; kt < KT; kt += 4) {
-        ring_step<BM>(buf0, buf3, src, aoff, boff, kt, KT, frow, tok_row0, acc);
-        ring_step<BM>(buf1, buf0, src, aoff, boff, kt + 1, KT, frow, tok_row0, acc);
-        ring_step<BM>(buf2, buf1, src, aoff, boff, kt + 2, KT, frow, tok_row0, acc);
-        ring_step<BM>(buf3, buf2, src, aoff, boff, kt + 3, KT, frow, tok_row0, acc);
+    Ring<BM> r;
+    r.wave = static_cast<uint32_t>(uniform_int(wave_v));
+    const int K = GEMM1 ? a.D : a.H;
+    r.KT = K / BK;
+    r.pipelined = r.KT >= kMinPipelinedKT;
+    {
+        const int lane = tid & 63;
+        const int row = static_cast<int>(r.wave) * C::B_INS * 16 + lane / 4;  // +16 rows per instruction
+        r.boff = static_cast<uint32_t>(lane / 4) * K * 2 + swz_chunk(row, lane & 3) * 16;
+        r.bstride = 16u * K * 2;
     }
 
-    // Epilogue. acc[f][t][4i + j] holds feature frow[f] + 8i + 4*(lane>>5) + j
-    // of token tok_row0 + 32t + (lane & 31). The output rows are staged in LDS
-    // (tokens below HALF in buffer 0, the rest in buffer 1), then written as
-    // 16-byte chunks, 16 lanes per 256-byte row. GEMM2's 256 features go in two
-    // passes of 128.
-    const int g4 = 4 * (lane >> 5);
-    for (int pass = 0; pass < (GEMM1 ? 1 : 2); ++pass) {
-        __syncthreads();
-        if (GEMM1 || wf == pass) {
+    load_descs(mtiles, first, stride, ny, count, 0, sDesc);
+    __syncthreads();
+    TileDesc t = uniform_desc(sDesc[0]);
+
+    // first tile: row map (and weights) now, then its first four stages
+    int cb = 0;
+    dma_row_map<BM>(a, t.row0, sPair[0], r.wave);
+    wait_vm<0>();
+    bare_barrier();
+    make_src<BM, GEMM1>(a, t, sPair[0], r.wave, r.src);
+    if (!GEMM1) {
+        dma_row_weights<BM>(a, sPair[0], sW[0], r.wave);
+        wait_vm<0>();
+        bare_barrier();
+    }
+    Frag<BM> f0, f1;
+    ring_start<BM>(r, r.src, buf0, buf1, buf2, buf3, frow, tok_row0, f0);
+
+    f32x16_t acc[4][C::NT];
+    for (int i = 0; i < count; ++i) {
 #pragma unroll
-            for (int t = 0; t < C::NT; ++t) {
-                const int tok = tok_row0 + 32 * t + (lane & 31);
-                uint8_t* stg = reinterpret_cast<uint8_t*>(tok < HALF ? &buf0 : &buf1);
-                const int tl = tok < HALF ? tok : tok - HALF;
-                const float wt = GEMM1 ? 1.0f : sW[tok];
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                    for (int f = 0; f < (GEMM1 ? 2 : 4); ++f) {
-                        float v[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float x = acc[f][t][4 * i + j];
-                            v[j] = GEMM1 ? x / (1.0f + __expf(-x)) * acc[f + 2][t][4 * i + j] : x * wt;
-                        }
-                        // staged column: GEMM1 act column, GEMM2 feature within this pass's 128
-                        const int col = (GEMM1 ? 64 * wf + 32 * f : 32 * f) + 8 * i + g4;
-                        *reinterpret_cast<uint2*>(stg + stage_off(tl, col)) =
-                            uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                    }
-                }
+            for (int tb = 0; tb < C::NT; ++tb) acc[f][tb] = f32x16_t{};
+        r.has_next = i + 1 < count;
+        r.nb = cb ^ 1;
+        if (r.has_next) {
+            if ((i + 1) % kInfoCap == 0) {  // next descriptor chunk; t stays in registers
+                __syncthreads();
+                load_descs(mtiles, first, stride, ny, count, i + 1, sDesc);
+                __syncthreads();
             }
+            r.next = uniform_desc(sDesc[(i + 1) % kInfoCap]);
         }
-        __syncthreads();
-        for (int idx = tid; idx < BM * 16; idx += kThreads) {
-            const int r = idx >> 4, c = idx & 15;
-            if (r >= mt.rows) continue;
-            const uint8_t* stg = reinterpret_cast<const uint8_t*>(r < HALF ? &buf0 : &buf1);
-            const int rl = r < HALF ? r : r - HALF;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rl * 256 + ((c ^ (rl & 15)) << 4));
-            uint16_t* dst = GEMM1 ? a.act + static_cast<int64_t>(mt.row0 + r) * a.H + h0 + c * 8
-                                  : a.ypair + static_cast<int64_t>(sRow[r]) * a.D + n0 + 128 * pass + c * 8;
-            *reinterpret_cast<u32x4_t*>(dst) = v;
+        r.cont = r.has_next && r.pipelined;
+
+        main_loop<BM, GEMM1>(a, r, &buf0, &buf1, &buf2, &buf3, sPair, sW, frow, tok_row0, f0, f1, acc);
+
+        if (r.has_next && !r.pipelined) {
+            // short K: hand over after the ring has drained
+            dma_row_map<BM>(a, r.next.row0, sPair[r.nb], r.wave);
+            wait_vm<0>();
+            bare_barrier();
+            make_src<BM, GEMM1>(a, r.next, sPair[r.nb], r.wave, r.nsrc);
+            if (!GEMM1) {
+                dma_row_weights<BM>(a, sPair[r.nb], sW[r.nb], r.wave);
+                wait_vm<0>();
+                bare_barrier();
+            }
+            ring_start<BM>(r, r.nsrc, buf0, buf1, buf2, buf3, frow, tok_row0, f0);
         }
+        epilogue<BM, GEMM1>(a, t, sPair[cb], sW[cb], tok_row0, wf, acc);
+        if (!r.has_next) break;
+        t = r.next;
+        r.src = r.nsrc;
+        cb ^= 1;
     }
 }
 
-inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
+// One m-tile descriptor per tile of height BM: {expert, first sorted row,
+// rows, 0}, in tile order. One workgroup per expert.
+template <int BM>
+__global__ void mtile_table_kernel(RouteView rv, int E, int4* __restrict__ out) {
+    const int e = blockIdx.x;
+    const int32_t* tp = rv.tile_prefix + tile_height_index(BM) * (E + 1);
+    const int t0 = tp[e], n = tp[e + 1] - t0;
+    const int off = rv.offsets[e], cnt = rv.counts[e];
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int m0 = i * BM;
+        out[t0 + i] = int4{e, off + m0, cnt - m0 < BM ? cnt - m0 : BM, 0};
+    }
+}
+
+int num_cus() {
+    static const int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        return v;
+    }();
+    return n;
+}
 
 }  // namespace
 
 // Average rows per expert at or above which the 256-row tile is used.
 constexpr int64_t kBigTile256MinRows = 512;
 
+int64_t big_gemm_mtile_capacity(int64_t P, int E) { return (P + 127) / 128 + E; }
+
 bool big_gemm_supported(const Bf16Args& a) {
     const int64_t lim = int64_t(1) << 32;  // the DMA offsets are 32-bit
-    return a.D % 256 == 0 && a.H % 128 == 0 && int64_t(a.T) * a.D * 2 < lim && a.P * a.H * 2 < lim &&
-           int64_t(2) * a.H * a.D * 2 < lim;
+    return a.mtiles != nullptr && a.D % 256 == 0 && a.H % 128 == 0 && int64_t(a.T) * a.D * 2 < lim &&
+           a.P * a.H * 2 < lim && a.P * 4 < lim && int64_t(2) * a.H * a.D * 2 < lim;
 }
 
 hipError_t launch_big_gemm(const Bf16Args& a, bool gemm1, hipStream_t s) {
     const bool t256 = a.P >= kBigTile256MinRows * a.E;
+    const int bm = t256 ? 256 : 128;
+    int4* tiles = reinterpret_cast<int4*>(a.mtiles);
+    if (gemm1) {  // the m-tiles are the same for both GEMMs
+        if (t256) mtile_table_kernel<256><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);
+        else mtile_table_kernel<128><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);
+    }
+    // one workgroup per CU (a multiple of 8: the same number on every XCD),
+    // never many more than there can be tiles
     const int ny = gemm1 ? a.H / 128 : a.D / 256;
-    const int64_t blocks = static_cast<int64_t>(mtiles_upper(a.P, a.E, t256 ? 256 : 128)) * ny;
-    const int grid = static_cast<int>((blocks + 7) / 8 * 8);
+    const int64_t tiles_upper = ((a.P + bm - 1) / bm + a.E) * ny;
+    int64_t grid = num_cus();
+    if (grid > tiles_upper) grid = tiles_upper;
+    grid = (grid + 7) / 8 * 8;
+    const int g = static_cast<int>(grid);
     if (t256) {
-        if (gemm1) big_gemm_kernel<256, true><<<grid, kThreads, 0, s>>>(a);
-        else big_gemm_kernel<256, false><<<grid, kThreads, 0, s>>>(a);
+        if (gemm1) big_gemm_kernel<256, true><<<g, kThreads, 0, s>>>(a, tiles);
+        else big_gemm_kernel<256, false><<<g, kThreads, 0, s>>>(a, tiles);
     } else {
-        if (gemm1) big_gemm_kernel<128, true><<<grid, kThreads, 0, s>>>(a);
-        else big_gemm_kernel<128, false><<<grid, kThreads, 0, s>>>(a);
+        if (gemm1) big_gemm_kernel<128, true><<<g, kThreads, 0, s>>>(a, tiles);
+        else big_gemm_kernel<128, false><<<g, kThreads, 0, s>>>(a, tiles);
     }
     return hipGetLastError();
 }
