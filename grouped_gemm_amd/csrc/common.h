@@ -23,17 +23,18 @@ __host__ __device__ constexpr int tile_height_index(int bm) {
     return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : 4;
 }
 
-// bf16 <-> fp32 (round to nearest even; inputs here are finite).
+// bf16 <-> fp32. fp32 -> bf16 rounds to nearest even; gfx950 converts in
+// hardware (v_cvt_pk_bf16_f32, two values per instruction).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Device view of the route step's outputs inside the workspace.

@@ -23,9 +23,8 @@
 // weights) arrive by DMA during the current tile's first steps, and its
 // first four stages are issued during the current tile's last four, so
 // neither the tile lookup nor the first loads' latency sits between two
-// tiles. Results are stored from
-// registers (8 bytes per lane; a 128-byte line is written by 8 stores of one
-// wave in a row, and the L2 merges them).
+// tiles. Results leave through a small per-wave LDS area as 64-byte row
+// segments (see epilogue).
 //
 // The 16-byte chunks of a staged row are XOR-swizzled by ((row >> 2) & 3):
 // gfx950's LDS serves 16 lanes of a 16-byte read per cycle from 64 banks, and
@@ -355,48 +354,60 @@ __device__ __forceinline__ void ring_start(Ring<BM>& r, const DmaSrc<BM>& src, S
     read_frag<BM>(b0, 0, frow, tok_row0, f0);
 }
 
-// Results of a tile, stored from registers. acc[f][t][4i + j] holds feature
-// frow[f] + 8i + 4*(lane>>5) + j of token row tok_row0 + 32t + (lane & 31).
+// Results of a tile. acc[f][t][4i + j] holds feature frow[f] + 8i +
+// 4*(lane>>5) + j of token row tok_row0 + 32t + (lane & 31): a lane holds 8
+// bytes of a row per register group. Each 32-row x 32-feature block goes
+// through the wave's own 2 KB of LDS (row r at r * 64, its 16-byte chunk c
+// at (c ^ ((r >> 2) & 3)) * 16: both the 8-byte writes and the 16-byte
+// reads hit distinct banks) and leaves as 64-byte row segments, 4 lanes x 16
+// bytes each: a quarter of the write requests of storing the 8-byte pieces.
+// The area is the wave's own, so no barrier is needed; LDS accesses of one
+// wave complete in order.
 // GEMM1 writes act = silu(gate) * up (bf16) at act[row0 + row][h0 + col];
 // GEMM2 writes w * y (bf16) at ypair[pair][n0 + feature].
 template <int BM, bool GEMM1>
 __device__ __forceinline__ void epilogue(const Bf16Args& a, const TileDesc& t, const int32_t* pairs, const float* w,
-                                         int tok_row0, int wf, const f32x16_t (&acc)[4][Big<BM>::NT]) {
+                                         int tok_row0, int wf, uint8_t* stg, const f32x16_t (&acc)[4][Big<BM>::NT]) {
     using C = Big<BM>;
     const int lane = threadIdx.x & 63;
-    const int g4 = 4 * (lane >> 5);
+    const int r = lane & 31, g = lane >> 5;
+    const int wr = r * 64 + 8 * g, wsw = (r >> 2) & 3;  // staging writes: row r, half g of chunk i
+    const int rr = lane >> 2, c = lane & 3;              // staging reads: rows rr and rr + 16, chunk c
+    const int rd0 = rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4);
+    const int rd1 = (rr + 16) * 64 + ((c ^ (((rr + 16) >> 2) & 3)) << 4);
 #pragma unroll
     for (int tb = 0; tb < C::NT; ++tb) {
-        const int row = tok_row0 + 32 * tb + (lane & 31);
-        if (row >= t.rows) continue;
+        const int base = tok_row0 + 32 * tb;
+        const bool ok0 = base + rr < t.rows, ok1 = base + rr + 16 < t.rows;
+        uint16_t* d0;
+        uint16_t* d1;
         if (GEMM1) {
-            uint16_t* dst = a.act + static_cast<int64_t>(t.row0 + row) * a.H + t.ntile * 128 + 64 * wf + g4;
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float x = acc[f][tb][4 * i + j];
-                        v[j] = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][4 * i + j];
-                    }
-                    *reinterpret_cast<uint2*>(dst + 32 * f + 8 * i) =
-                        uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                }
+            const int64_t col = t.ntile * 128 + 64 * wf + 8 * c;
+            d0 = a.act + static_cast<int64_t>(t.row0 + base + rr) * a.H + col;
+            d1 = d0 + static_cast<int64_t>(16) * a.H;
         } else {
-            const int p = clamp_pair(pairs[row], a.P);
-            const float wt = w[row];
-            uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + t.ntile * 256 + 128 * wf + g4;
+            const int64_t col = t.ntile * 256 + 128 * wf + 8 * c;
+            d0 = a.ypair + static_cast<int64_t>(clamp_pair(pairs[base + rr], a.P)) * a.D + col;
+            d1 = a.ypair + static_cast<int64_t>(clamp_pair(pairs[base + rr + 16], a.P)) * a.D + col;
+        }
+        const float wt = GEMM1 ? 1.0f : w[base + r];
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < (GEMM1 ? 2 : 4); ++f) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x16_t& c = acc[f][tb];
-                    *reinterpret_cast<uint2*>(dst + 32 * f + 8 * i) =
-                        uint2{pack_bf16x2(c[4 * i] * wt, c[4 * i + 1] * wt),
-                              pack_bf16x2(c[4 * i + 2] * wt, c[4 * i + 3] * wt)};
+            for (int i = 0; i < 4; ++i) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x = acc[f][tb][4 * i + j];
+                    v[j] = GEMM1 ? x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][4 * i + j] : x * wt;
                 }
+                *reinterpret_cast<uint2*>(stg + wr + ((i ^ wsw) << 4)) =
+                    uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+            const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(stg + rd0);
+            const u32x4_t q1 = *reinterpret_cast<const u32x4_t*>(stg + rd1);
+            if (ok0) *reinterpret_cast<u32x4_t*>(d0 + 32 * f) = q0;
+            if (ok1) *reinterpret_cast<u32x4_t*>(d1 + 32 * f) = q1;
         }
     }
 }
@@ -426,6 +437,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const
     __shared__ __attribute__((aligned(16))) int32_t sPair[2][BM];
     __shared__ __attribute__((aligned(16))) float sW[2][BM];
     __shared__ TileDesc sDesc[kInfoCap];
+    __shared__ __attribute__((aligned(16))) uint8_t sOut[W][2048];  // per-wave result staging
 
     // This workgroup's tiles: logical tiles first, first + stride, ... of its
     // XCD's range. The tile count comes from the route step.
@@ -509,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const
             }
             ring_start<BM>(r, r.nsrc, buf0, buf1, buf2, buf3, frow, tok_row0, f0);
         }
-        epilogue<BM, GEMM1>(a, t, sPair[cb], sW[cb], tok_row0, wf, acc);
+        epilogue<BM, GEMM1>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
         if (!r.has_next) break;
         t = r.next;
         r.src = r.nsrc;
