@@ -106,10 +106,8 @@ Plan make_plan(const moe_ffn_problem* p, int mode) {
         }
         pl.ypair = off;
         off = align_up(off + 2 * static_cast<size_t>(P) * p->D);
-        if (p->dtype == MOE_FFN_BF16) {
-            pl.mtiles = off;
-            off = align_up(off + 16 * static_cast<size_t>(moe::big_gemm_mtile_capacity(P, p->E)));
-        }
+        pl.mtiles = off;
+        off = align_up(off + 16 * static_cast<size_t>(moe::big_gemm_mtile_capacity(P, p->E)));
     } else {
         pl.acc32 = off;
         off = align_up(off + 4 * static_cast<size_t>(p->T) * p->D);
@@ -275,6 +273,7 @@ MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, 
         a.act_s = at<uint8_t>(ws, pl.act_s);
         a.ypair = at<uint16_t>(ws, pl.ypair);
         a.out = static_cast<uint16_t*>(out);
+        a.mtiles = at<int32_t>(ws, pl.mtiles);
         e = moe::launch_split_mx(a, st, stage_ev);
     }
     return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;

@@ -142,8 +142,12 @@ struct MxArgs {
     uint8_t* act_s;     // [P, H/32] e8m0
     uint16_t* ypair;    // [P, D]
     uint16_t* out;      // [T, D]
+    int32_t* mtiles;    // m-tile table of the prefill GEMMs, big_gemm_mtile_capacity x int4
 };
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
+// Prefill-shaped MX GEMM1 / GEMM2 (the bf16 prefill kernels' ring on the scaled MFMA).
+bool big_mx_supported(const MxArgs& a);
+hipError_t launch_big_mx(const MxArgs& a, bool gemm1, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* ypair, const int32_t* pair_to_sorted, int32_t T, int32_t k,
                           int32_t D, uint16_t* out, hipStream_t s);

@@ -1,12 +1,20 @@
-// Prefill-shaped bf16 grouped GEMMs: many routed rows per expert.
+// Prefill-shaped grouped GEMMs, bf16 and MX-fp8: many routed rows per expert.
 //
 // With hundreds to thousands of rows per expert the pass is bound by the
 // matrix cores. A tile is BM token rows x 256 weight rows (GEMM1: 128 gate +
 // 128 up rows, the gate/up pairing of "Prime Flash MoE", section 2, Trick 1;
-// GEMM2: 256 output features). The weights are the MFMA's A operand
-// (v_mfma_f32_32x32x16_bf16), so each lane's results are 4 consecutive
-// features of one token. Eight waves (two per SIMD) split a tile into two
-// feature halves x four token groups: 128 features x BM/4 tokens per wave.
+// GEMM2: 256 output features). The weights are the MFMA's A operand, so each
+// lane's results are 4 consecutive features of one token. Eight waves (two
+// per SIMD) split a tile into two feature halves x four token groups: 128
+// features x BM/4 tokens per wave.
+//
+// Formats. bf16: v_mfma_f32_32x32x16_bf16, 32 elements of K per stage.
+// MX-fp8 ("Prime Flash MoE", section 7: e4m3 codes with one e8m0 scale per
+// 32 elements along K): v_mfma_scale_f32_32x32x64_f8f6f4, 64 codes of K per
+// stage, so a staged row holds 64 bytes in both formats. For the scaled
+// MFMA, lane group g = lane >> 5 supplies codes k = 16g..16g+15 and
+// 32+16g..32+16g+15 of the 64 (the row's 16-byte chunks g and 2+g) and the
+// scale of 32-block g (layout measured on gfx950 with an in-bounds probe).
 //
 // Persistent schedule. One workgroup per CU walks a list of tiles. Workgroup
 // b runs on XCD b % 8 (8 XCDs, each with its own L2); the logical tiles,
@@ -14,17 +22,17 @@
 // an XCD take every (workgroups per XCD)-th tile of that XCD's range, so the
 // n-tiles sharing a token tile run side by side and reuse it from one L2.
 //
-// K steps of 32 (64 bytes per row) go through a ring of 4 LDS stages filled
-// by global->LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at
-// base + 16*i; 16 rows x 64 bytes per instruction): three stages are in
-// flight while one is consumed, and the one barrier per stage sits between
-// the MFMAs of the stage's two k-halves (see ring_step). The ring runs on
-// across tiles: the next tile's row map (and, for GEMM2, its routing
-// weights) arrive by DMA during the current tile's first steps, and its
-// first four stages are issued during the current tile's last four, so
-// neither the tile lookup nor the first loads' latency sits between two
-// tiles. Results leave through a small per-wave LDS area as 64-byte row
-// segments (see epilogue).
+// K stages go through a ring of 4 LDS buffers filled by global->LDS DMA
+// (global_load_lds_dwordx4: lane i's 16 bytes land at base + 16*i; 16 rows x
+// 64 bytes per instruction; MX adds one dword DMA per wave with 64 rows'
+// scale bytes): three stages are in flight while one is consumed, and the
+// one barrier per stage sits between the MFMAs of the stage's two halves
+// (see ring_step). The ring runs on across tiles: the next tile's row map
+// (and, for GEMM2, its routing weights) arrive by DMA during the current
+// tile's first steps, and its first four stages are issued during the
+// current tile's last four, so neither the tile lookup nor the first loads'
+// latency sits between two tiles. Results leave through a small per-wave LDS
+// area as 64-byte row segments (see the epilogues).
 //
 // The 16-byte chunks of a staged row are XOR-swizzled by ((row >> 2) & 3):
 // gfx950's LDS serves 16 lanes of a 16-byte read per cycle from 64 banks, and
@@ -37,60 +45,96 @@
 // Token rows of GEMM1 are gathered on load (row r reads token
 // sorted_to_pair[row0 + r] / k); rows past an expert's count read a valid
 // row and are not stored.
+#include <cstdlib>
+
 #include "common.h"
+#include "mxq.h"
 
 namespace moe {
 
 namespace {
 
-#ifndef MOE_BIG_WAVES
-#define MOE_BIG_WAVES 8
-#endif
-constexpr int W = MOE_BIG_WAVES;   // waves per workgroup (2 feature halves x W/2 token groups)
+constexpr int W = 8;               // waves per workgroup
 constexpr int kThreads = 64 * W;
-constexpr int BK = 32;             // K per stage
 constexpr int RB = 64;             // bytes per tile row per stage
 constexpr int BN = 256;            // weight rows per tile
-constexpr int kInfoCap = 512;      // tile descriptors held in LDS at a time
-constexpr int kMinPipelinedKT = 8; // K steps a tile needs for the in-loop hand-over
+constexpr int kMinPipelinedKT = 8; // K stages a tile needs for the in-loop hand-over
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+// What both formats' kernels read and write. bf16: x, w1, w2 are bf16 and
+// act is bf16 [P, H]; MX: they are e4m3 codes with e8m0 scales xs, w1s, w2s
+// (one per 32 along K) and act is codes [P, H] with scales act_s [P, H/32].
+struct BigArgs {
+    int32_t T, D, H, E, k;
+    int64_t P;
+    const uint8_t* x;
+    const uint8_t* xs;
+    const uint8_t* w1;
+    const uint8_t* w1s;
+    const uint8_t* w2;
+    const uint8_t* w2s;
+    const float* wts;
+    RouteView rv;
+    uint8_t* act;
+    uint8_t* act_s;
+    uint16_t* ypair;
+};
 
-__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
+template <bool MX>
+struct Fmt {
+    static constexpr int EB = MX ? 1 : 2;           // bytes per element
+    static constexpr int KS = RB / EB;              // K elements per stage
+    static constexpr int kInfoCap = MX ? 128 : 512; // tile descriptors held in LDS at a time
+};
 
-template <int BM>
+template <int BM, bool MX>
 struct Big {
     static constexpr int TB = BM / (W / 2);    // tokens per wave
     static constexpr int NT = TB / 32;         // token blocks per wave
     static constexpr int NF = 4;               // feature blocks per wave (128 features)
     static constexpr int A_INS = BM / 16 / W;  // token-row DMA instructions per wave per stage
     static constexpr int B_INS = BN / 16 / W;  // weight-row DMA instructions per wave per stage
-    static constexpr int L = A_INS + B_INS;    // DMA instructions per wave per stage
+    static constexpr int L = A_INS + B_INS + (MX ? 1 : 0);  // DMA instructions per wave per stage
     static constexpr int PW = BM / 64;         // waves that move one BM-entry int/float vector (64 per wave)
-    static constexpr int TOK_BYTES = BM * RB, W_BYTES = BN * RB;
     static_assert(NT >= 1 && A_INS >= 1 && A_INS * 16 * W == BM && B_INS * 16 * W == BN, "tile split");
     static_assert(PW >= 1 && PW <= W, "row-vector DMA waves");
+    static_assert(!MX || BM / 64 + BN / 64 == W, "one scale-row DMA per wave");
 };
 
-template <int BM>
+// One stage of the ring. Stage buffers start on 1 KB boundaries so that a
+// DMA instruction's 1 KB lands on whole 256-byte bank rows.
+template <int BM, bool MX>
 struct StageBuf {
-    uint8_t tok[Big<BM>::TOK_BYTES];
-    uint8_t wt[Big<BM>::W_BYTES];
+    uint8_t tok[BM * RB];
+    uint8_t wt[BN * RB];
+};
+template <int BM>
+struct StageBuf<BM, true> {
+    uint8_t tok[BM * RB];
+    uint8_t wt[BN * RB];
+    uint32_t sct[BM];  // per token row, the scale dword holding this stage's two 32-blocks
+    uint32_t scw[BN];  // the same per weight row
 };
 
 // Per-tile DMA sources: wave-uniform bases (scalar registers) plus 32-bit
 // per-lane byte offsets. Token rows need one offset per instruction (they may
 // be gathered); weight rows are consecutive and share `boff` + j * bstride,
-// which does not change from tile to tile.
-template <int BM>
+// which does not change from tile to tile. MX: each wave also moves the
+// scale dword of 64 rows (waves 0..3 token rows, 4..7 weight rows).
+template <int BM, bool MX>
 struct DmaSrc {
     const char* abase;
     const char* bbase;
-    uint32_t aoff[Big<BM>::A_INS];
+    uint32_t aoff[Big<BM, MX>::A_INS];
+};
+template <int BM>
+struct DmaSrc<BM, true> {
+    const char* abase;
+    const char* bbase;
+    const char* sbase;
+    uint32_t aoff[Big<BM, true>::A_INS];
+    uint32_t soff;
 };
 
 // A tile of this workgroup's list.
@@ -138,10 +182,15 @@ __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t 
 }
 #pragma clang diagnostic pop
 
-template <int BM>
-__device__ __forceinline__ void issue_stage(StageBuf<BM>& b, const DmaSrc<BM>& src, uint32_t boff, uint32_t bstride,
-                                            int kt, uint32_t wave) {
-    using C = Big<BM>;
+__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// Stage kt of a tile: L DMA instructions per wave. The MX scale dword of a
+// row covers 32-blocks 4*(kt/2) .. 4*(kt/2)+3, of which stage kt uses
+// blocks 2kt and 2kt+1 (bytes 2*(kt&1) and 2*(kt&1)+1).
+template <int BM, bool MX>
+__device__ __forceinline__ void issue_stage(StageBuf<BM, MX>& b, const DmaSrc<BM, MX>& src, uint32_t boff,
+                                            uint32_t bstride, int kt, uint32_t wave) {
+    using C = Big<BM, MX>;
     const char* ab = src.abase + kt * RB;
     const char* bb = src.bbase + kt * RB;
     const uint32_t tl = lds_addr(b.tok) + wave * (C::A_INS * 1024);
@@ -150,6 +199,11 @@ __device__ __forceinline__ void issue_stage(StageBuf<BM>& b, const DmaSrc<BM>& s
     for (int j = 0; j < C::A_INS; ++j) dma16(ab, src.aoff[j], tl + j * 1024);
 #pragma unroll
     for (int j = 0; j < C::B_INS; ++j) dma16(bb, boff + j * bstride, wl + j * 1024);
+    if constexpr (MX) {
+        const uint32_t sl = wave < static_cast<uint32_t>(BM / 64) ? lds_addr(b.sct) + wave * 256
+                                                                   : lds_addr(b.scw) + (wave - BM / 64) * 256;
+        dma4(src.sbase, src.soff + (kt >> 1) * 4, sl);
+    }
 }
 
 // wait until at most n vector-memory operations of this wave are in flight
@@ -174,60 +228,165 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One 16-wide k-half of a stage in registers: 4 weight fragments (32 rows
-// each) and NT token fragments.
+// Half a stage in registers. bf16: the stage's k-half h (16 of its 32 K
+// elements) for all 4 weight and NT token fragments. MX: the whole 64-wide K
+// step for weight fragments 2h, 2h+1 with each row's scale byte; the token
+// fragments of a stage are held once (TokFrag).
+template <int BM, bool MX>
+struct Frag;
 template <int BM>
-struct Frag {
-    bf16x8_t w[Big<BM>::NF];
-    bf16x8_t t[Big<BM>::NT];
+struct Frag<BM, false> {
+    bf16x8_t w[4];
+    bf16x8_t t[Big<BM, false>::NT];
+};
+template <int BM>
+struct Frag<BM, true> {  // MX: two weight fragments (2h, 2h+1) with their scale bytes
+    i32x8_t w[2];
+    int sw[2];
+};
+// MX: the token fragments of a stage with their scale bytes.
+template <int BM>
+struct TokFrag {
+    i32x8_t t[Big<BM, true>::NT];
+    int st[Big<BM, true>::NT];
 };
 
-// Fragment reads of k-half kk of a stage: every fragment's 32 rows start at a
-// multiple of 16, so a lane's row is (row base) + (lane & 31) and its swizzle
-// term is ((lane & 31) >> 2) & 3.
-template <int BM>
-__device__ __forceinline__ void read_frag(const StageBuf<BM>& b, int kk, const int (&frow)[4], int tok_row0,
-                                          Frag<BM>& f) {
-    using C = Big<BM>;
-    const int lane = threadIdx.x & 63;
-    const int lrow = (lane & 31) * RB;
-    const int coff = swz_chunk(lane & 31, 2 * kk + (lane >> 5)) << 4;
+__device__ __forceinline__ i32x8_t frag32(const uint8_t* row, int lo, int hi) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(row + lo);
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(row + hi);
+    return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+}
+
+// Per-lane LDS byte offsets of a wave's fragment rows, fixed for the whole
+// kernel. A weight fragment f starts at tile row wrow0 + FROW[f] (FROW a
+// compile-time table), a token fragment t at tok_row0 + 32t; a lane reads
+// row (start) + (lane & 31). Every fragment's rows start at a multiple of
+// 16, so the swizzle term is ((lane & 31) >> 2) & 3 for all of them.
+// A lane reads 16-byte chunks g and 2 + g of a row (g = lane >> 5): the
+// bf16 k-halves 0 and 1, or the two halves of an MX operand. Their swizzled
+// offsets are kept as two values, not an array indexed by g, which the
+// compiler would put in scratch memory; a scratch load in the loop makes it
+// wait for every memory operation in flight, DMAs included.
+struct LaneOff {
+    int w, t;        // row offsets: (wrow0 + (lane & 31)) * RB, (tok_row0 + (lane & 31)) * RB
+    int clo, chi;    // swizzled offsets of chunks g and 2 + g
+    int sw, st;      // MX: scale dword offsets (wrow0 + (lane & 31)) * 4, (tok_row0 + (lane & 31)) * 4
+};
+
+template <bool GEMM1>
+__device__ __forceinline__ constexpr int frow_const(int f) {
+    // GEMM1: gate rows 0..127 and up rows 128..255, a wave's 64 of each; GEMM2: 128 consecutive rows
+    return GEMM1 ? (f < 2 ? 32 * f : 128 + 32 * (f - 2)) : 32 * f;
+}
+
+// Fragment reads. PAR is the stage's parity (which MX scale bytes).
+template <int BM, bool GEMM1, bool MX, int PAR>
+__device__ __forceinline__ void read_half(const StageBuf<BM, MX>& b, int h, const LaneOff& o, Frag<BM, MX>& f) {
+    using C = Big<BM, MX>;
+    const int g = (threadIdx.x & 63) >> 5;
+    if constexpr (!MX) {
+        const int co = h == 0 ? o.clo : o.chi;
 #pragma unroll
-    for (int i = 0; i < C::NF; ++i) f.w[i] = *reinterpret_cast<const bf16x8_t*>(b.wt + frow[i] * RB + lrow + coff);
+        for (int i = 0; i < 4; ++i)
+            f.w[i] = *reinterpret_cast<const bf16x8_t*>(b.wt + o.w + frow_const<GEMM1>(i) * RB + co);
 #pragma unroll
-    for (int i = 0; i < C::NT; ++i)
-        f.t[i] = *reinterpret_cast<const bf16x8_t*>(b.tok + (tok_row0 + 32 * i) * RB + lrow + coff);
+        for (int i = 0; i < C::NT; ++i) f.t[i] = *reinterpret_cast<const bf16x8_t*>(b.tok + o.t + 32 * i * RB + co);
+    } else {
+        const int lo = o.clo, hi = o.chi;
+        const int sh = 8 * (2 * PAR + g);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int fr = frow_const<GEMM1>(2 * h + i);
+            f.w[i] = frag32(b.wt + o.w + fr * RB, lo, hi);
+            f.sw[i] = static_cast<int>((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(b.scw) +
+                                                                           o.sw + fr * 4) >> sh) & 0xffu);
+        }
+    }
+}
+
+template <int BM, int PAR>
+__device__ __forceinline__ void read_tok(const StageBuf<BM, true>& b, const LaneOff& o, TokFrag<BM>& f) {
+    const int g = (threadIdx.x & 63) >> 5;
+    const int lo = o.clo, hi = o.chi;
+    const int sh = 8 * (2 * PAR + g);
+#pragma unroll
+    for (int i = 0; i < Big<BM, true>::NT; ++i) {
+        f.t[i] = frag32(b.tok + o.t + 32 * i * RB, lo, hi);
+        f.st[i] = static_cast<int>((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(b.sct) +
+                                                                       o.st + 32 * i * 4) >> sh) & 0xffu);
+    }
+}
+
+// Keeps the MFMAs of an MX half-stage where they are written: the empty asm
+// makes the accumulators' new values needed at this point. Without it the
+// compiler sinks the MFMAs of several steps past the barriers (their results
+// are only read after the loop), and every fragment read in between stays
+// live in registers: hundreds of spills. (The bf16 loop is left to the
+// compiler's schedule, which is faster there.)
+template <int NT>
+__device__ __forceinline__ void pin_acc(f32x16_t (&acc)[4][NT], int f0, int f1) {
+#pragma unroll
+    for (int f = f0; f < f1; ++f)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(acc[f][t]));
 }
 
 template <int BM>
-__device__ __forceinline__ void mfma_frag(const Frag<BM>& f, f32x16_t (&acc)[4][Big<BM>::NT]) {
-    using C = Big<BM>;
+__device__ __forceinline__ void mfma_half(const Frag<BM, false>& f, f32x16_t (&acc)[4][Big<BM, false>::NT]) {
 #pragma unroll
-    for (int i = 0; i < C::NF; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < C::NT; ++t) acc[i][t] = mfma32(f.w[i], f.t[t], acc[i][t]);
+        for (int t = 0; t < Big<BM, false>::NT; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[i], f.t[t], acc[i][t], 0, 0, 0);
 }
+
+template <int BM>
+__device__ __forceinline__ void mfma_mx(const Frag<BM, true>& f, const TokFrag<BM>& tf, int h,
+                                        f32x16_t (&acc)[4][Big<BM, true>::NT]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < Big<BM, true>::NT; ++t)
+            acc[2 * h + i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[i], tf.t[t], acc[2 * h + i][t], 0,
+                                                                                 0, 0, f.sw[i], 0, tf.st[t]);
+    pin_acc(acc, 2 * h, 2 * h + 2);
+}
+
+// Registers a wave carries from one ring step to the next: bf16 the two
+// k-halves of a stage; MX the two weight-fragment pairs and the stage's
+// token fragments.
+template <int BM, bool MX>
+struct Regs;
+template <int BM>
+struct Regs<BM, false> {
+    Frag<BM, false> f0, f1;
+};
+template <int BM>
+struct Regs<BM, true> {
+    Frag<BM, true> f0, f1;
+    TokFrag<BM> tf;
+};
 
 // Everything a workgroup keeps across the steps of a tile.
-template <int BM>
+template <int BM, bool MX>
 struct Ring {
-    DmaSrc<BM> src, nsrc;     // this tile's and the next tile's DMA sources
-    uint32_t boff, bstride;   // weight-row offsets (the same for every tile)
-    uint32_t wave;            // wave index (uniform)
-    int KT;                   // K steps per tile
-    bool pipelined;           // KT is long enough for the in-loop hand-over
+    DmaSrc<BM, MX> src, nsrc;  // this tile's and the next tile's DMA sources
+    uint32_t boff, bstride;    // weight-row offsets (the same for every tile)
+    uint32_t wave;             // wave index (uniform)
+    int KT;                    // K stages per tile
+    bool pipelined;            // KT is long enough for the in-loop hand-over
     bool has_next;
-    bool cont;                // the next tile's stages follow this tile's in the ring
-    TileDesc next;            // the next tile (valid when has_next)
-    int nb;                   // row-vector buffer of the next tile (0 or 1)
+    bool cont;                 // the next tile's stages follow this tile's in the ring
+    TileDesc next;             // the next tile (valid when has_next)
+    int nb;                    // row-vector buffer of the next tile (0 or 1)
 };
 
 // DMA of a tile's row map: sorted_to_pair[row0 .. row0 + BM) -> pairs[0 .. BM).
 // The map in the workspace is padded by 256 entries, so the window never
 // leaves it; entries past the expert's rows are clamped before use.
 template <int BM>
-__device__ __forceinline__ void dma_row_map(const Bf16Args& a, int row0, int32_t* pairs, uint32_t wave) {
-    if (wave < static_cast<uint32_t>(Big<BM>::PW)) {
+__device__ __forceinline__ void dma_row_map(const BigArgs& a, int row0, int32_t* pairs, uint32_t wave) {
+    if (wave < static_cast<uint32_t>(BM / 64)) {
         const uint32_t lane = threadIdx.x & 63;
         dma4(uniform_ptr(a.rv.sorted_to_pair + row0), (wave * 64 + lane) * 4u, lds_addr(pairs) + wave * 256);
     }
@@ -235,8 +394,8 @@ __device__ __forceinline__ void dma_row_map(const Bf16Args& a, int row0, int32_t
 
 // DMA of a tile's routing weights: wts[pair of row r] -> w[r] (GEMM2).
 template <int BM>
-__device__ __forceinline__ void dma_row_weights(const Bf16Args& a, const int32_t* pairs, float* w, uint32_t wave) {
-    if (wave < static_cast<uint32_t>(Big<BM>::PW)) {
+__device__ __forceinline__ void dma_row_weights(const BigArgs& a, const int32_t* pairs, float* w, uint32_t wave) {
+    if (wave < static_cast<uint32_t>(BM / 64)) {
         const int lane = threadIdx.x & 63;
         const int p = clamp_pair(pairs[wave * 64 + lane], a.P);
         dma4(uniform_ptr(a.wts), static_cast<uint32_t>(p) * 4u, lds_addr(w) + wave * 256);
@@ -246,41 +405,66 @@ __device__ __forceinline__ void dma_row_weights(const Bf16Args& a, const int32_t
 // DMA sources of a tile. GEMM1: token rows gathered through the row map;
 // weight rows 0..127 are gate rows h0.., 128..255 up rows H + h0.. (a wave's
 // rows never straddle the two). GEMM2: act rows in sorted order. Offsets are
-// 32-bit: the host only picks this kernel when x, act and one expert's
-// weights each span < 4 GiB. Instruction j of a wave covers tile rows
-// (wave * INS + j) * 16 + lane / 4, chunk lane & 3.
-template <int BM, bool GEMM1>
-__device__ __forceinline__ void make_src(const Bf16Args& a, const TileDesc& t, const int32_t* pairs, uint32_t wave,
-                                         DmaSrc<BM>& s) {
-    using C = Big<BM>;
+// 32-bit: the host only picks this kernel when each operand array (and, for
+// the weights, one expert's) spans < 4 GiB. Instruction j of a wave covers
+// tile rows (wave * INS + j) * 16 + lane / 4, chunk lane & 3.
+template <int BM, bool GEMM1, bool MX>
+__device__ __forceinline__ void make_src(const BigArgs& a, const TileDesc& t, const int32_t* pairs, uint32_t wave,
+                                         DmaSrc<BM, MX>& s) {
+    using C = Big<BM, MX>;
+    constexpr int EB = Fmt<MX>::EB;
     const int lane = threadIdx.x & 63;
     const int K = GEMM1 ? a.D : a.H;
-    s.abase = uniform_ptr(GEMM1 ? a.x : a.act + static_cast<int64_t>(t.row0) * a.H);
+    const int h0 = t.ntile * 128, n0 = t.ntile * 256;
+    s.abase = uniform_ptr(GEMM1 ? a.x : a.act + static_cast<int64_t>(t.row0) * a.H * EB);
 #pragma unroll
     for (int j = 0; j < C::A_INS; ++j) {
         const int row = (static_cast<int>(wave) * C::A_INS + j) * 16 + lane / 4;
         const uint32_t r = GEMM1 ? static_cast<uint32_t>(clamp_pair(pairs[row], a.P) / a.k) * a.D
                                  : static_cast<uint32_t>(row < t.rows ? row : 0) * a.H;
-        s.aoff[j] = r * 2 + swz_chunk(row, lane & 3) * 16;
+        s.aoff[j] = r * EB + swz_chunk(row, lane & 3) * 16;
     }
     const int row0 = static_cast<int>(wave) * C::B_INS * 16;  // first weight-tile row of this wave
+    const int64_t e2h = static_cast<int64_t>(t.expert) * 2 * a.H;
     if (GEMM1) {
-        const int h0 = t.ntile * 128;
         const int grow0 = row0 < 128 ? h0 + row0 : a.H + h0 + row0 - 128;
-        s.bbase = uniform_ptr(a.w1 + (static_cast<int64_t>(t.expert) * 2 * a.H + grow0) * K);
+        s.bbase = uniform_ptr(a.w1 + (e2h + grow0) * K * EB);
     } else {
-        s.bbase = uniform_ptr(a.w2 + (static_cast<int64_t>(t.expert) * a.D + t.ntile * 256 + row0) * K);
+        s.bbase = uniform_ptr(a.w2 + (static_cast<int64_t>(t.expert) * a.D + n0 + row0) * K * EB);
+    }
+    if constexpr (MX) {
+        const int KB = K / 32;  // scale bytes per row
+        if (wave < static_cast<uint32_t>(BM / 64)) {
+            const int r = static_cast<int>(wave) * 64 + lane;  // token row
+            if (GEMM1) {
+                s.sbase = uniform_ptr(a.xs);
+                s.soff = static_cast<uint32_t>(clamp_pair(pairs[r], a.P) / a.k) * KB;
+            } else {
+                s.sbase = uniform_ptr(a.act_s);
+                s.soff = static_cast<uint32_t>(t.row0 + (r < t.rows ? r : 0)) * KB;
+            }
+        } else {
+            const int r = (static_cast<int>(wave) - BM / 64) * 64 + lane;  // weight row
+            if (GEMM1) {
+                const int grow = r < 128 ? h0 + r : a.H + h0 + r - 128;
+                s.sbase = uniform_ptr(a.w1s);
+                s.soff = static_cast<uint32_t>(e2h + grow) * KB;
+            } else {
+                s.sbase = uniform_ptr(a.w2s);
+                s.soff = static_cast<uint32_t>(static_cast<int64_t>(t.expert) * a.D + n0 + r) * KB;
+            }
+        }
     }
 }
 
 // One ring step. The barrier sits in the middle of stage kt's MFMAs, so a
 // wave never comes out of it with nothing to compute:
-//   read k-half 1 of stage kt (buffer cur);  MFMAs of k-half 0 (read last step)
+//   read half 1 of stage kt (buffer cur);  MFMAs of half 0 (read last step)
 //   wait for this wave's DMAs of stage kt+1 and its own LDS reads;  barrier
 //   issue stage kt+4 into cur (every wave is done reading it);
-//   read k-half 0 of stage kt+1 (buffer nxt);  MFMAs of k-half 1
+//   read half 0 of stage kt+1 (buffer nxt);  MFMAs of half 1
 // Stage kt+4 belongs to this tile, or to the next one once this tile has
-// none left, so the ring runs on across tiles.
+// none left, so the ring runs on across tiles. PAR = kt & 1.
 //
 // Waits: before the barrier each wave waits until its own DMAs of stage kt+1
 // are done; the stages it issued after it (kt+2, kt+3, while they exist) may
@@ -293,14 +477,15 @@ __device__ __forceinline__ void make_src(const Bf16Args& a, const TileDesc& t, c
 // complete by step 3's barrier; step 3 builds the next tile's DMA sources
 // from it and fetches its routing weights (GEMM2), complete by step 6's
 // barrier; steps KT-4 .. KT-1 issue its stages 0..3.
-template <int BM, bool GEMM1>
-__device__ __forceinline__ void ring_step(const Bf16Args& a, Ring<BM>& r, StageBuf<BM>& cur,
-                                          const StageBuf<BM>& nxt, int kt, int32_t (*pairs)[BM], float (*wrow)[BM],
-                                          const int (&frow)[4], int tok_row0, Frag<BM>& f0, Frag<BM>& f1,
-                                          f32x16_t (&acc)[4][Big<BM>::NT]) {
-    constexpr int L = Big<BM>::L;
-    read_frag<BM>(cur, 1, frow, tok_row0, f1);
-    mfma_frag<BM>(f0, acc);
+template <int BM, bool GEMM1, bool MX, int PAR>
+__device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, StageBuf<BM, MX>& cur,
+                                          const StageBuf<BM, MX>& nxt, int kt, int32_t (*pairs)[BM],
+                                          float (*wrow)[BM], const LaneOff& o, Regs<BM, MX>& g,
+                                          f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
+    constexpr int L = Big<BM, MX>::L;
+    read_half<BM, GEMM1, MX, PAR>(cur, 1, o, g.f1);
+    if constexpr (MX) mfma_mx<BM>(g.f0, g.tf, 0, acc);
+    else mfma_half<BM>(g.f0, acc);
     const bool more1 = kt + 1 < r.KT || r.cont;  // stage kt+1 exists
     if (kt + 3 < r.KT || r.cont) wait_vm_lds<2 * L>();
     else if (kt + 2 < r.KT) wait_vm_lds<L>();
@@ -309,72 +494,91 @@ __device__ __forceinline__ void ring_step(const Bf16Args& a, Ring<BM>& r, StageB
     if (r.cont) {
         if (kt == 0) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
         if (kt == 3) {
-            make_src<BM, GEMM1>(a, r.next, pairs[r.nb], r.wave, r.nsrc);
+            make_src<BM, GEMM1, MX>(a, r.next, pairs[r.nb], r.wave, r.nsrc);
             if (!GEMM1) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
         }
     }
-    if (kt + 4 < r.KT) issue_stage<BM>(cur, r.src, r.boff, r.bstride, kt + 4, r.wave);
-    else if (r.cont) issue_stage<BM>(cur, r.nsrc, r.boff, r.bstride, kt + 4 - r.KT, r.wave);
-    if (more1) read_frag<BM>(nxt, 0, frow, tok_row0, f0);
-    mfma_frag<BM>(f1, acc);
+    if (kt + 4 < r.KT) issue_stage<BM, MX>(cur, r.src, r.boff, r.bstride, kt + 4, r.wave);
+    else if (r.cont) issue_stage<BM, MX>(cur, r.nsrc, r.boff, r.bstride, kt + 4 - r.KT, r.wave);
+    if (more1) read_half<BM, GEMM1, MX, PAR ^ 1>(nxt, 0, o, g.f0);
+    if constexpr (MX) {
+        // the token fragments of stage kt+1 go where this stage's were, once
+        // its last MFMAs have been issued
+        mfma_mx<BM>(g.f1, g.tf, 1, acc);
+        if (more1) read_tok<BM, PAR ^ 1>(nxt, o, g.tf);
+    } else {
+        mfma_half<BM>(g.f1, acc);
+    }
 }
 
 // The stage buffers come in as restrict pointers: with them, the compiler
 // knows the fragment reads of one stage never alias the others.
-template <int BM, bool GEMM1>
-__device__ __forceinline__ void main_loop(const Bf16Args& a, Ring<BM>& r, StageBuf<BM>* __restrict__ b0,
-                                          StageBuf<BM>* __restrict__ b1, StageBuf<BM>* __restrict__ b2,
-                                          StageBuf<BM>* __restrict__ b3, int32_t (*pairs)[BM], float (*wrow)[BM],
-                                          const int (&frow)[4], int tok_row0, Frag<BM>& f0, Frag<BM>& f1,
-                                          f32x16_t (&acc)[4][Big<BM>::NT]) {
-    // KT is a multiple of 4 (K is a multiple of 128): the unrolled body needs
-    // no exit in the middle, which would make the compiler shuttle the
-    // accumulators between registers at the loop head. Every tile starts at
-    // buffer 0.
-    for (int kt = 0; kt < r.KT; kt += 4) {
-        ring_step<BM, GEMM1>(a, r, *b0, *b1, kt, pairs, wrow, frow, tok_row0, f0, f1, acc);
-        ring_step<BM, GEMM1>(a, r, *b1, *b2, kt + 1, pairs, wrow, frow, tok_row0, f0, f1, acc);
-        ring_step<BM, GEMM1>(a, r, *b2, *b3, kt + 2, pairs, wrow, frow, tok_row0, f0, f1, acc);
-        ring_step<BM, GEMM1>(a, r, *b3, *b0, kt + 3, pairs, wrow, frow, tok_row0, f0, f1, acc);
+template <int BM, bool GEMM1, bool MX>
+__device__ __forceinline__ void main_loop(const BigArgs& a, Ring<BM, MX>& r, StageBuf<BM, MX>* __restrict__ b0,
+                                          StageBuf<BM, MX>* __restrict__ b1, StageBuf<BM, MX>* __restrict__ b2,
+                                          StageBuf<BM, MX>* __restrict__ b3, int32_t (*pairs)[BM],
+                                          float (*wrow)[BM], const LaneOff& o, Regs<BM, MX>& g,
+                                          f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
+    // KT is a multiple of 4: the unrolled body needs no exit in the middle,
+    // which would make the compiler shuttle the accumulators between
+    // registers at the loop head. Every tile starts at buffer 0. The body is
+    // unrolled by hand; for MX, more copies only raise register pressure.
+    if constexpr (MX) {
+#pragma clang loop unroll(disable)
+        for (int kt = 0; kt < r.KT; kt += 4) {
+            ring_step<BM, GEMM1, MX, 0>(a, r, *b0, *b1, kt, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1>(a, r, *b1, *b2, kt + 1, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 0>(a, r, *b2, *b3, kt + 2, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1>(a, r, *b3, *b0, kt + 3, pairs, wrow, o, g, acc);
+        }
+    } else {
+        for (int kt = 0; kt < r.KT; kt += 4) {
+            ring_step<BM, GEMM1, MX, 0>(a, r, *b0, *b1, kt, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1>(a, r, *b1, *b2, kt + 1, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 0>(a, r, *b2, *b3, kt + 2, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1>(a, r, *b3, *b0, kt + 3, pairs, wrow, o, g, acc);
+        }
     }
 }
 
-// Issue stages 0..3 of a tile, wait for stage 0 and read its first k-half.
-template <int BM>
-__device__ __forceinline__ void ring_start(Ring<BM>& r, const DmaSrc<BM>& src, StageBuf<BM>& b0, StageBuf<BM>& b1,
-                                           StageBuf<BM>& b2, StageBuf<BM>& b3, const int (&frow)[4], int tok_row0,
-                                           Frag<BM>& f0) {
-    constexpr int L = Big<BM>::L;
-    issue_stage<BM>(b0, src, r.boff, r.bstride, 0, r.wave);
-    issue_stage<BM>(b1, src, r.boff, r.bstride, 1, r.wave);
-    issue_stage<BM>(b2, src, r.boff, r.bstride, 2, r.wave);
-    issue_stage<BM>(b3, src, r.boff, r.bstride, 3, r.wave);
+// Issue stages 0..3 of a tile, wait for stage 0 and read its first half.
+template <int BM, bool GEMM1, bool MX>
+__device__ __forceinline__ void ring_start(Ring<BM, MX>& r, const DmaSrc<BM, MX>& src, StageBuf<BM, MX>& b0,
+                                           StageBuf<BM, MX>& b1, StageBuf<BM, MX>& b2, StageBuf<BM, MX>& b3,
+                                           const LaneOff& o, Regs<BM, MX>& g) {
+    constexpr int L = Big<BM, MX>::L;
+    issue_stage<BM, MX>(b0, src, r.boff, r.bstride, 0, r.wave);
+    issue_stage<BM, MX>(b1, src, r.boff, r.bstride, 1, r.wave);
+    issue_stage<BM, MX>(b2, src, r.boff, r.bstride, 2, r.wave);
+    issue_stage<BM, MX>(b3, src, r.boff, r.bstride, 3, r.wave);
     wait_vm<3 * L>();
     bare_barrier();
-    read_frag<BM>(b0, 0, frow, tok_row0, f0);
+    read_half<BM, GEMM1, MX, 0>(b0, 0, o, g.f0);
+    if constexpr (MX) read_tok<BM, 0>(b0, o, g.tf);
 }
 
 // Results of a tile. acc[f][t][4i + j] holds feature frow[f] + 8i +
 // 4*(lane>>5) + j of token row tok_row0 + 32t + (lane & 31): a lane holds 8
-// bytes of a row per register group. Each 32-row x 32-feature block goes
-// through the wave's own 2 KB of LDS (row r at r * 64, its 16-byte chunk c
-// at (c ^ ((r >> 2) & 3)) * 16: both the 8-byte writes and the 16-byte
-// reads hit distinct banks) and leaves as 64-byte row segments, 4 lanes x 16
-// bytes each: a quarter of the write requests of storing the 8-byte pieces.
-// The area is the wave's own, so no barrier is needed; LDS accesses of one
-// wave complete in order.
-// GEMM1 writes act = silu(gate) * up (bf16) at act[row0 + row][h0 + col];
-// GEMM2 writes w * y (bf16) at ypair[pair][n0 + feature].
-template <int BM, bool GEMM1>
-__device__ __forceinline__ void epilogue(const Bf16Args& a, const TileDesc& t, const int32_t* pairs, const float* w,
-                                         int tok_row0, int wf, uint8_t* stg, const f32x16_t (&acc)[4][Big<BM>::NT]) {
-    using C = Big<BM>;
+// bytes of a bf16 row per register group. Each 32-row block goes through
+// the wave's own 2 KB of LDS (row r at r * 64, its 16-byte chunk c at
+// (c ^ ((r >> 2) & 3)) * 16: the writes and the 16-byte reads hit distinct
+// banks) and leaves as 64-byte row segments, 4 lanes x 16 bytes each: a
+// quarter of the write requests of storing the 8-byte pieces. The area is
+// the wave's own, so no barrier is needed; LDS accesses of one wave complete
+// in order.
+__device__ __forceinline__ int stage_chunk_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+// bf16 results: GEMM1 writes act = silu(gate) * up at act[row0 + row][h0 + col];
+// GEMM2 (both formats) writes w * y at ypair[pair][n0 + feature].
+template <int BM, bool GEMM1, bool MX>
+__device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& t, const int32_t* pairs,
+                                              const float* w, int tok_row0, int wf, uint8_t* stg,
+                                              const f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
+    using C = Big<BM, MX>;
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, g = lane >> 5;
-    const int wr = r * 64 + 8 * g, wsw = (r >> 2) & 3;  // staging writes: row r, half g of chunk i
-    const int rr = lane >> 2, c = lane & 3;              // staging reads: rows rr and rr + 16, chunk c
-    const int rd0 = rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4);
-    const int rd1 = (rr + 16) * 64 + ((c ^ (((rr + 16) >> 2) & 3)) << 4);
+    const int rr = lane >> 2, c = lane & 3;  // staging reads: rows rr and rr + 16, chunk c
+    const int rd0 = stage_chunk_off(rr, c), rd1 = stage_chunk_off(rr + 16, c);
 #pragma unroll
     for (int tb = 0; tb < C::NT; ++tb) {
         const int base = tok_row0 + 32 * tb;
@@ -382,8 +586,8 @@ __device__ __forceinline__ void epilogue(const Bf16Args& a, const TileDesc& t, c
         uint16_t* d0;
         uint16_t* d1;
         if (GEMM1) {
-            const int64_t col = t.ntile * 128 + 64 * wf + 8 * c;
-            d0 = a.act + static_cast<int64_t>(t.row0 + base + rr) * a.H + col;
+            uint16_t* act = reinterpret_cast<uint16_t*>(a.act);
+            d0 = act + static_cast<int64_t>(t.row0 + base + rr) * a.H + t.ntile * 128 + 64 * wf + 8 * c;
             d1 = d0 + static_cast<int64_t>(16) * a.H;
         } else {
             const int64_t col = t.ntile * 256 + 128 * wf + 8 * c;
@@ -401,7 +605,7 @@ __device__ __forceinline__ void epilogue(const Bf16Args& a, const TileDesc& t, c
                     const float x = acc[f][tb][4 * i + j];
                     v[j] = GEMM1 ? x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][4 * i + j] : x * wt;
                 }
-                *reinterpret_cast<uint2*>(stg + wr + ((i ^ wsw) << 4)) =
+                *reinterpret_cast<uint2*>(stg + stage_chunk_off(r, i) + 8 * g) =
                     uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             }
             const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(stg + rd0);
@@ -412,10 +616,67 @@ __device__ __forceinline__ void epilogue(const Bf16Args& a, const TileDesc& t, c
     }
 }
 
-// Descriptors of this workgroup's tiles c0 .. c0 + kInfoCap - 1 into LDS.
+// MX GEMM1 results: act = silu(gate) * up in fp32, requantized per 32 act
+// columns by the MXQ rule ("Prime Flash MoE", section 7: the GEMM1
+// epilogue quantizes act for GEMM2). A 32-column block of one token sits in
+// lanes r and r + 32 (16 values each), so its amax takes one cross-lane
+// swap. Codes of the wave's 64 act columns for 32 tokens (64 bytes per
+// token) are staged and leave as 64-byte row segments; each token's two
+// scale bytes leave as one 2-byte store.
+template <int BM>
+__device__ __forceinline__ void epilogue_mx_gemm1(const BigArgs& a, const TileDesc& t, int tok_row0, int wf,
+                                                  uint8_t* stg, const f32x16_t (&acc)[4][Big<BM, true>::NT]) {
+    using C = Big<BM, true>;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31, g = lane >> 5;
+    const int rr = lane >> 2, c = lane & 3;
+    const int rd0 = stage_chunk_off(rr, c), rd1 = stage_chunk_off(rr + 16, c);
+    const int HB = a.H / 32;
+    const int col0 = t.ntile * 128 + 64 * wf;  // first act column of this wave
+#pragma unroll
+    for (int tb = 0; tb < C::NT; ++tb) {
+        const int base = tok_row0 + 32 * tb;
+        uint32_t sbytes = 0;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            float v[16];
+            float amax = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const float x = acc[f][tb][q];
+                v[q] = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][q];
+                amax = fmaxf(amax, fabsf(v[q]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int s = mx_scale_exp(amax);
+            const float inv = pow2f(-s);
+            sbytes |= static_cast<uint32_t>(s + 127) << (8 * f);
+            // act column 32f + 8i + 4g + j of the wave: 16-byte chunk 2f + (i >> 1), byte 8(i & 1) + 4g + j
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t code = e4m3_encode(v[4 * i] * inv, v[4 * i]) |
+                                      (e4m3_encode(v[4 * i + 1] * inv, v[4 * i + 1]) << 8) |
+                                      (e4m3_encode(v[4 * i + 2] * inv, v[4 * i + 2]) << 16) |
+                                      (e4m3_encode(v[4 * i + 3] * inv, v[4 * i + 3]) << 24);
+                *reinterpret_cast<uint32_t*>(stg + stage_chunk_off(r, 2 * f + (i >> 1)) + 8 * (i & 1) + 4 * g) = code;
+            }
+        }
+        if (g == 0 && base + r < t.rows)
+            *reinterpret_cast<uint16_t*>(a.act_s + static_cast<int64_t>(t.row0 + base + r) * HB + col0 / 32) =
+                static_cast<uint16_t>(sbytes);
+        const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(stg + rd0);
+        const u32x4_t q1 = *reinterpret_cast<const u32x4_t*>(stg + rd1);
+        uint8_t* d0 = a.act + static_cast<int64_t>(t.row0 + base + rr) * a.H + col0 + 16 * c;
+        if (base + rr < t.rows) *reinterpret_cast<u32x4_t*>(d0) = q0;
+        if (base + rr + 16 < t.rows) *reinterpret_cast<u32x4_t*>(d0 + static_cast<int64_t>(16) * a.H) = q1;
+    }
+}
+
+// Descriptors of this workgroup's tiles c0 .. c0 + CAP - 1 into LDS.
+template <int CAP>
 __device__ __forceinline__ void load_descs(const int4* mtiles, int first, int stride, int ny, int count, int c0,
                                            TileDesc* desc) {
-    for (int i = threadIdx.x; i < kInfoCap && c0 + i < count; i += kThreads) {
+    for (int i = threadIdx.x; i < CAP && c0 + i < count; i += kThreads) {
         const int logical = first + (c0 + i) * stride;
         const int m = logical / ny;
         const int4 d = mtiles[m];
@@ -427,16 +688,17 @@ __device__ __forceinline__ TileDesc uniform_desc(const TileDesc& d) {
     return TileDesc{uniform_int(d.expert), uniform_int(d.row0), uniform_int(d.rows), uniform_int(d.ntile)};
 }
 
-template <int BM, bool GEMM1>
-__global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const int4* __restrict__ mtiles) {
-    using C = Big<BM>;
-    __shared__ __attribute__((aligned(16))) StageBuf<BM> buf0;
-    __shared__ __attribute__((aligned(16))) StageBuf<BM> buf1;
-    __shared__ __attribute__((aligned(16))) StageBuf<BM> buf2;
-    __shared__ __attribute__((aligned(16))) StageBuf<BM> buf3;
+template <int BM, bool GEMM1, bool MX>
+__global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const int4* __restrict__ mtiles) {
+    using C = Big<BM, MX>;
+    constexpr int CAP = Fmt<MX>::kInfoCap;
+    __shared__ __attribute__((aligned(1024))) StageBuf<BM, MX> buf0;
+    __shared__ __attribute__((aligned(1024))) StageBuf<BM, MX> buf1;
+    __shared__ __attribute__((aligned(1024))) StageBuf<BM, MX> buf2;
+    __shared__ __attribute__((aligned(1024))) StageBuf<BM, MX> buf3;
     __shared__ __attribute__((aligned(16))) int32_t sPair[2][BM];
     __shared__ __attribute__((aligned(16))) float sW[2][BM];
-    __shared__ TileDesc sDesc[kInfoCap];
+    __shared__ TileDesc sDesc[CAP];
     __shared__ __attribute__((aligned(16))) uint8_t sOut[W][2048];  // per-wave result staging
 
     // This workgroup's tiles: logical tiles first, first + stride, ... of its
@@ -452,25 +714,32 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const
 
     const int tid = threadIdx.x, wave_v = tid >> 6;
     const int wtok = wave_v >> 1, wf = wave_v & 1;
-    int frow[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-        frow[f] = GEMM1 ? (f < 2 ? 64 * wf + 32 * f : 128 + 64 * wf + 32 * (f - 2)) : 128 * wf + 32 * f;
     const int tok_row0 = wtok * C::TB;
+    LaneOff o;
+    {
+        const int lane = tid & 63, lr = lane & 31;
+        const int wrow0 = (GEMM1 ? 64 : 128) * wf;
+        o.w = (wrow0 + lr) * RB;
+        o.t = (tok_row0 + lr) * RB;
+        o.clo = swz_chunk(lr, lane >> 5) << 4;
+        o.chi = swz_chunk(lr, 2 + (lane >> 5)) << 4;
+        o.sw = (wrow0 + lr) * 4;
+        o.st = (tok_row0 + lr) * 4;
+    }
 
-    Ring<BM> r;
+    Ring<BM, MX> r;
     r.wave = static_cast<uint32_t>(uniform_int(wave_v));
     const int K = GEMM1 ? a.D : a.H;
-    r.KT = K / BK;
+    r.KT = K / Fmt<MX>::KS;
     r.pipelined = r.KT >= kMinPipelinedKT;
     {
         const int lane = tid & 63;
         const int row = static_cast<int>(r.wave) * C::B_INS * 16 + lane / 4;  // +16 rows per instruction
-        r.boff = static_cast<uint32_t>(lane / 4) * K * 2 + swz_chunk(row, lane & 3) * 16;
-        r.bstride = 16u * K * 2;
+        r.boff = static_cast<uint32_t>(lane / 4) * K * Fmt<MX>::EB + swz_chunk(row, lane & 3) * 16;
+        r.bstride = 16u * K * Fmt<MX>::EB;
     }
 
-    load_descs(mtiles, first, stride, ny, count, 0, sDesc);
+    load_descs<CAP>(mtiles, first, stride, ny, count, 0, sDesc);
     __syncthreads();
     TileDesc t = uniform_desc(sDesc[0]);
 
@@ -479,14 +748,14 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const
     dma_row_map<BM>(a, t.row0, sPair[0], r.wave);
     wait_vm<0>();
     bare_barrier();
-    make_src<BM, GEMM1>(a, t, sPair[0], r.wave, r.src);
+    make_src<BM, GEMM1, MX>(a, t, sPair[0], r.wave, r.src);
     if (!GEMM1) {
         dma_row_weights<BM>(a, sPair[0], sW[0], r.wave);
         wait_vm<0>();
         bare_barrier();
     }
-    Frag<BM> f0, f1;
-    ring_start<BM>(r, r.src, buf0, buf1, buf2, buf3, frow, tok_row0, f0);
+    Regs<BM, MX> g;
+    ring_start<BM, GEMM1, MX>(r, r.src, buf0, buf1, buf2, buf3, o, g);
 
     f32x16_t acc[4][C::NT];
     for (int i = 0; i < count; ++i) {
@@ -497,31 +766,32 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(Bf16Args a, const
         r.has_next = i + 1 < count;
         r.nb = cb ^ 1;
         if (r.has_next) {
-            if ((i + 1) % kInfoCap == 0) {  // next descriptor chunk; t stays in registers
+            if ((i + 1) % CAP == 0) {  // next descriptor chunk; t stays in registers
                 __syncthreads();
-                load_descs(mtiles, first, stride, ny, count, i + 1, sDesc);
+                load_descs<CAP>(mtiles, first, stride, ny, count, i + 1, sDesc);
                 __syncthreads();
             }
-            r.next = uniform_desc(sDesc[(i + 1) % kInfoCap]);
+            r.next = uniform_desc(sDesc[(i + 1) % CAP]);
         }
         r.cont = r.has_next && r.pipelined;
 
-        main_loop<BM, GEMM1>(a, r, &buf0, &buf1, &buf2, &buf3, sPair, sW, frow, tok_row0, f0, f1, acc);
+        main_loop<BM, GEMM1, MX>(a, r, &buf0, &buf1, &buf2, &buf3, sPair, sW, o, g, acc);
 
         if (r.has_next && !r.pipelined) {
             // short K: hand over after the ring has drained
             dma_row_map<BM>(a, r.next.row0, sPair[r.nb], r.wave);
             wait_vm<0>();
             bare_barrier();
-            make_src<BM, GEMM1>(a, r.next, sPair[r.nb], r.wave, r.nsrc);
+            make_src<BM, GEMM1, MX>(a, r.next, sPair[r.nb], r.wave, r.nsrc);
             if (!GEMM1) {
                 dma_row_weights<BM>(a, sPair[r.nb], sW[r.nb], r.wave);
                 wait_vm<0>();
                 bare_barrier();
             }
-            ring_start<BM>(r, r.nsrc, buf0, buf1, buf2, buf3, frow, tok_row0, f0);
+            ring_start<BM, GEMM1, MX>(r, r.nsrc, buf0, buf1, buf2, buf3, o, g);
         }
-        epilogue<BM, GEMM1>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
+        if constexpr (GEMM1 && MX) epilogue_mx_gemm1<BM>(a, t, tok_row0, wf, sOut[wave_v], acc);
+        else epilogue_bf16<BM, GEMM1, MX>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
         if (!r.has_next) break;
         t = r.next;
         r.src = r.nsrc;
@@ -554,6 +824,30 @@ int num_cus() {
     return n;
 }
 
+// One workgroup per CU (a multiple of 8: the same number on every XCD),
+// never many more than there can be tiles. MOE_FFN_GRID_LIMIT=n caps it at n
+// (rounded up to a multiple of 8), e.g. to leave CUs to other work or to give
+// each workgroup many tiles.
+int big_grid(int64_t P, int E, int bm, int ny) {
+    const int64_t tiles_upper = ((P + bm - 1) / bm + E) * ny;
+    int64_t grid = num_cus();
+    if (const char* lim = std::getenv("MOE_FFN_GRID_LIMIT")) {
+        const long v = std::strtol(lim, nullptr, 10);
+        if (v > 0 && v < grid) grid = v;
+    }
+    if (grid > tiles_upper) grid = tiles_upper;
+    return static_cast<int>((grid + 7) / 8 * 8);
+}
+
+template <int BM, bool MX>
+hipError_t launch_big(const BigArgs& a, int4* tiles, bool gemm1, hipStream_t s) {
+    if (gemm1) mtile_table_kernel<BM><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);  // the same m-tiles for both GEMMs
+    const int g = big_grid(a.P, a.E, BM, gemm1 ? a.H / 128 : a.D / 256);
+    if (gemm1) big_gemm_kernel<BM, true, MX><<<g, kThreads, 0, s>>>(a, tiles);
+    else big_gemm_kernel<BM, false, MX><<<g, kThreads, 0, s>>>(a, tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Average rows per expert at or above which the 256-row tile is used.
@@ -567,30 +861,28 @@ bool big_gemm_supported(const Bf16Args& a) {
            a.P * a.H * 2 < lim && a.P * 4 < lim && int64_t(2) * a.H * a.D * 2 < lim;
 }
 
-hipError_t launch_big_gemm(const Bf16Args& a, bool gemm1, hipStream_t s) {
-    const bool t256 = a.P >= kBigTile256MinRows * a.E;
-    const int bm = t256 ? 256 : 128;
-    int4* tiles = reinterpret_cast<int4*>(a.mtiles);
-    if (gemm1) {  // the m-tiles are the same for both GEMMs
-        if (t256) mtile_table_kernel<256><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);
-        else mtile_table_kernel<128><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);
-    }
-    // one workgroup per CU (a multiple of 8: the same number on every XCD),
-    // never many more than there can be tiles
-    const int ny = gemm1 ? a.H / 128 : a.D / 256;
-    const int64_t tiles_upper = ((a.P + bm - 1) / bm + a.E) * ny;
-    int64_t grid = num_cus();
-    if (grid > tiles_upper) grid = tiles_upper;
-    grid = (grid + 7) / 8 * 8;
-    const int g = static_cast<int>(grid);
-    if (t256) {
-        if (gemm1) big_gemm_kernel<256, true><<<g, kThreads, 0, s>>>(a, tiles);
-        else big_gemm_kernel<256, false><<<g, kThreads, 0, s>>>(a, tiles);
-    } else {
-        if (gemm1) big_gemm_kernel<128, true><<<g, kThreads, 0, s>>>(a, tiles);
-        else big_gemm_kernel<128, false><<<g, kThreads, 0, s>>>(a, tiles);
-    }
-    return hipGetLastError();
+hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
+    BigArgs a{b.T, b.D, b.H, b.E, b.k, b.P,
+              reinterpret_cast<const uint8_t*>(b.x), nullptr,
+              reinterpret_cast<const uint8_t*>(b.w1), nullptr,
+              reinterpret_cast<const uint8_t*>(b.w2), nullptr,
+              b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair};
+    int4* tiles = reinterpret_cast<int4*>(b.mtiles);
+    if (b.P >= kBigTile256MinRows * b.E) return launch_big<256, false>(a, tiles, gemm1, s);
+    return launch_big<128, false>(a, tiles, gemm1, s);
+}
+
+// MX: 256-row tiles only (eight waves move the 512 scale rows of a stage);
+// K stages of 64 codes must come in multiples of 4 (D and H multiples of 256).
+bool big_mx_supported(const MxArgs& a) {
+    const int64_t lim = int64_t(1) << 32;
+    return a.mtiles != nullptr && a.P >= kBigTile256MinRows * a.E && a.D % 256 == 0 && a.H % 256 == 0 &&
+           int64_t(a.T) * a.D < lim && a.P * a.H < lim && a.P * 4 < lim && int64_t(a.E) * 2 * a.H * a.D < lim;
+}
+
+hipError_t launch_big_mx(const MxArgs& b, bool gemm1, hipStream_t s) {
+    BigArgs a{b.T, b.D, b.H, b.E, b.k, b.P, b.x, b.xs, b.w1, b.w1s, b.w2, b.w2s, b.wts, b.rv, b.act, b.act_s, b.ypair};
+    return launch_big<256, true>(a, reinterpret_cast<int4*>(b.mtiles), gemm1, s);
 }
 
 }  // namespace moe

@@ -22,6 +22,7 @@
 // requantizes it per 32 along H with the same rule (section 7, "The
 // epilogue also quantizes"), writing codes [P, H] and scales [P, H/32].
 #include "common.h"
+#include "mxq.h"
 
 namespace moe {
 
@@ -33,40 +34,6 @@ constexpr int BKB = 128;  // K bytes (= codes) per stage
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ int acc_row(int lane, int v) { return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3); }
-
-// MXQ scale exponent from the block's amax (finite, >= 0).
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-    const uint32_t u = __float_as_uint(amax);
-    const int ef = static_cast<int>(u >> 23);
-    if (ef == 0) return -127;  // zero or below 2^-126: the clamp decides
-    int s = ef - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
-    return s < -127 ? -127 : (s > 127 ? 127 : s);
-}
-
-// 2^e as a float for e in [-127, 127] (2^-127 is subnormal, still exact).
-__device__ __forceinline__ float pow2f(int e) {
-    return e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : __uint_as_float(0x00400000u);
-}
-
-// e4m3fn code of v (already divided by the block scale), nearest even,
-// saturating; the sign comes from `sign_src` so a value that underflows
-// keeps the sign of the input.
-__device__ __forceinline__ uint32_t e4m3_encode(float v, float sign_src) {
-    const uint32_t sign = (__float_as_uint(sign_src) >> 24) & 0x80u;
-    const float x = fabsf(v);
-    uint32_t code;
-    if (x >= 448.0f) {
-        code = 0x7e;
-    } else if (x < 0.015625f) {                   // below 2^-6: multiples of 2^-9
-        code = static_cast<uint32_t>(rintf(x * 512.0f));
-    } else {
-        const uint32_t u = __float_as_uint(x);
-        const uint32_t r = (u + 0x7ffffu + ((u >> 20) & 1u)) >> 20;  // exponent|3 mantissa bits, RNE
-        code = r - (120u << 3);
-        if (code > 0x7eu) code = 0x7e;
-    }
-    return sign | code;
-}
 
 // ---------------- standalone quantizer ----------------
 // 8 lanes per 32-element block, 4 values per lane.
@@ -344,11 +311,20 @@ hipError_t launch_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t
 
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BN1 = 128, BN2 = 128;
-    dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
-    mx_gemm1_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
+    const bool big = big_mx_supported(a);
+    if (big) {
+        launch_big_mx(a, true, s);
+    } else {
+        dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
+        mx_gemm1_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
+    }
     record(ev, 0, s);
-    dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
-    mx_gemm2_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
+    if (big) {
+        launch_big_mx(a, false, s);
+    } else {
+        dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
+        mx_gemm2_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
+    }
     record(ev, 1, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -101,6 +101,25 @@ def test_large_prefill_sampled():
     _case(cfg, "split", tokens=sample_tokens(cfg, ids, 48))
 
 
+@pytest.mark.parametrize("T,D,H,E,k", [
+    (2100, 256, 128, 3, 2),     # short K in GEMM2: hand-over after the ring drains
+    (2100, 512, 384, 3, 2),     # hand-over inside the ring
+    (700, 512, 384, 4, 2),      # 128-row tiles
+])
+def test_prefill_many_tiles_per_workgroup(T, D, H, E, k, monkeypatch):
+    # with 8 workgroups each one walks many tiles, so the cross-tile hand-over runs
+    monkeypatch.setenv("MOE_FFN_GRID_LIMIT", "8")
+    _case(mi.custom(T, D, H, E, k, "zipf"), "split")
+
+
+def test_prefill_descriptor_reload(monkeypatch):
+    # 8 workgroups x more than 512 tiles each: the tile descriptors are reloaded
+    monkeypatch.setenv("MOE_FFN_GRID_LIMIT", "8")
+    cfg = mi.custom(65536, 256, 4096, 2, 1, "uniform")
+    ids, _ = mi.routing(cfg)
+    _case(cfg, "split", tokens=sample_tokens(cfg, ids, 32))
+
+
 def test_split_is_deterministic():
     import grouped_gemm_amd as g
     d = mi.make_bf16(mi.custom(700, 256, 384, 16, 4, "zipf"), 3)

@@ -79,6 +79,26 @@ def test_mx_forward_small(T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (2100, 256, 256, 3, 2, "zipf"),     # prefill tiles, short K: hand-over after the ring drains
+    (2100, 512, 768, 3, 2, "zipf"),     # prefill tiles, hand-over inside the ring
+])
+@pytest.mark.parametrize("grid_limit", [None, "8"])
+def test_mx_forward_prefill_tiles(T, D, H, E, k, routing, grid_limit, monkeypatch):
+    # with 8 workgroups each one walks many tiles, so the cross-tile hand-over runs
+    if grid_limit:
+        monkeypatch.setenv("MOE_FFN_GRID_LIMIT", grid_limit)
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
+def test_mx_prefill_descriptor_reload(monkeypatch):
+    # 8 workgroups x more than 128 tiles each: the tile descriptors are reloaded
+    monkeypatch.setenv("MOE_FFN_GRID_LIMIT", "8")
+    cfg = mi.custom(16384, 256, 4096, 2, 1, "uniform", dtype="mxfp8")
+    ids, _ = mi.routing(cfg)
+    _case(cfg, tokens=sample_tokens(cfg, ids, 32))
+
+
 def test_mx_config_sampled():
     cfg = mi.CONFIGS[5]
     ids, _ = mi.routing(cfg)
