@@ -77,6 +77,9 @@ __device__ __forceinline__ int clamp_pair(int p, int64_t P) {
     return p < 0 ? 0 : (p >= P ? static_cast<int>(P - 1) : p);
 }
 
+// Compute units of the current device (queried once).
+int device_cu_count();
+
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----
 
 inline void record(hipEvent_t* ev, int i, hipStream_t s) {

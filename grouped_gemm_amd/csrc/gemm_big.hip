@@ -813,24 +813,13 @@ __global__ void mtile_table_kernel(RouteView rv, int E, int4* __restrict__ out) 
     }
 }
 
-int num_cus() {
-    static const int n = [] {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        return v;
-    }();
-    return n;
-}
-
 // One workgroup per CU (a multiple of 8: the same number on every XCD),
 // never many more than there can be tiles. MOE_FFN_GRID_LIMIT=n caps it at n
 // (rounded up to a multiple of 8), e.g. to leave CUs to other work or to give
 // each workgroup many tiles.
 int big_grid(int64_t P, int E, int bm, int ny) {
     const int64_t tiles_upper = ((P + bm - 1) / bm + E) * ny;
-    int64_t grid = num_cus();
+    int64_t grid = device_cu_count();
     if (const char* lim = std::getenv("MOE_FFN_GRID_LIMIT")) {
         const long v = std::strtol(lim, nullptr, 10);
         if (v > 0 && v < grid) grid = v;
@@ -849,6 +838,17 @@ hipError_t launch_big(const BigArgs& a, int4* tiles, bool gemm1, hipStream_t s) 
 }
 
 }  // namespace
+
+int device_cu_count() {
+    static const int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        return v;
+    }();
+    return n;
+}
 
 // Average rows per expert at or above which the 256-row tile is used.
 constexpr int64_t kBigTile256MinRows = 512;

@@ -306,21 +306,25 @@ inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P +
 #define MOE_DMA_KC 256
 #endif
 
-// Row groups per block: GEMM1's long rows (K = D) amortize the ring fill
-// over many groups; GEMM2's short K keeps more, smaller blocks in flight.
-#ifndef MOE_DMA_G1
-#define MOE_DMA_G1 8
-#endif
-#ifndef MOE_DMA_G2
-#define MOE_DMA_G2 1
-#endif
+// Row groups per block: as many as leave about one block per CU, so that
+// every CU fills its ring once and no second round of blocks runs on half the
+// chip. The m-tile count is estimated from the average rows per expert (the
+// real one is known only on the device).
+int groups_per_block(int groups, int64_t P, int E) {
+    const int64_t per_expert = (P / E + 31) / 32;
+    const int64_t mtiles = static_cast<int64_t>(E) * (per_expert > 0 ? per_expert : 1);
+    int64_t G = groups * mtiles / device_cu_count();
+    if (G < 1) G = 1;
+    if (G > groups) G = groups;
+    while (groups % G) --G;
+    return static_cast<int>(G);
+}
 
 hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
     constexpr int NT = 2;  // m-tiles of 32 tokens
     const int K = gemm1 ? a.D : a.H;
     const int groups = gemm1 ? a.H / 32 : a.D / 64;
-    int G = gemm1 ? MOE_DMA_G1 : MOE_DMA_G2;
-    while (groups % G) G >>= 1;
+    const int G = groups_per_block(groups, a.P, a.E);
     dim3 g(mtiles_upper(a.P, a.E, 16 * NT), groups / G);
     const bool wide = MOE_DMA_KC == 256 && K % 256 == 0;
     if (gemm1) {

@@ -48,6 +48,19 @@ def test_route_dropped_ids():
     _check(ids, 8)
 
 
+@pytest.mark.parametrize("T,E,k", [(32, 64, 8), (33, 64, 8), (20, 65, 8), (31, 64, 2)])
+def test_route_one_wave_limits(T, E, k):
+    # up to 256 pairs and 64 experts one wave routes the batch; just past either limit one workgroup does
+    ids, _ = mi.routing(mi.custom(T, 128, 128, E, k, "uniform"))
+    _check(ids, E)
+
+
+def test_route_dropped_ids_one_wave():
+    rng = np.random.default_rng(6)
+    ids = rng.integers(-3, 11, size=(60, 4)).astype(np.int32)     # E = 8, 240 pairs
+    _check(ids, 8)
+
+
 def test_route_large_segments():
     """P large enough that the segment length grows past its minimum."""
     rng = np.random.default_rng(5)
