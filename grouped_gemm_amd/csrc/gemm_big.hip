@@ -95,7 +95,14 @@ struct Big {
     static constexpr int NF = 4;               // feature blocks per wave (128 features)
     static constexpr int A_INS = BM / 16 / W;  // token-row DMA instructions per wave per stage
     static constexpr int B_INS = BN / 16 / W;  // weight-row DMA instructions per wave per stage
-    static constexpr int L = A_INS + B_INS + (MX ? 1 : 0);  // DMA instructions per wave per stage
+    static constexpr int L = A_INS + B_INS;    // code DMA instructions per wave per stage
+    // MX adds one scale DMA per wave on even stages (its dword covers the
+    // stage pair). Outstanding operations younger than a stage kt when the
+    // next one, two or three stages are in flight: any two consecutive
+    // stages hold one even stage.
+    static constexpr int Y1 = L;
+    static constexpr int Y2 = 2 * L + (MX ? 1 : 0);
+    static constexpr int Y3 = 3 * L + (MX ? 1 : 0);
     static constexpr int PW = BM / 64;         // waves that move one BM-entry int/float vector (64 per wave)
     static_assert(NT >= 1 && A_INS >= 1 && A_INS * 16 * W == BM && B_INS * 16 * W == BN, "tile split");
     static_assert(PW >= 1 && PW <= W, "row-vector DMA waves");
@@ -109,12 +116,16 @@ struct StageBuf {
     uint8_t tok[BM * RB];
     uint8_t wt[BN * RB];
 };
+constexpr int kScaleSlots = 4;
+// MX scale ring: slot (pair & 3) holds, per token row and per weight row,
+// the scale dword of stage pair `pair` (32-blocks 4*pair .. 4*pair+3: the
+// stage pair's two stages use two blocks each). The pair counter runs on
+// across tiles, so a new tile's pairs never land in a slot still being read.
+// A pair's dword is fetched once, with its even stage.
 template <int BM>
-struct StageBuf<BM, true> {
-    uint8_t tok[BM * RB];
-    uint8_t wt[BN * RB];
-    uint32_t sct[BM];  // per token row, the scale dword holding this stage's two 32-blocks
-    uint32_t scw[BN];  // the same per weight row
+struct ScaleSlot {
+    uint32_t tok[BM];
+    uint32_t wt[BN];
 };
 
 // Per-tile DMA sources: wave-uniform bases (scalar registers) plus 32-bit
@@ -184,12 +195,11 @@ __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t 
 
 __device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
 
-// Stage kt of a tile: L DMA instructions per wave. The MX scale dword of a
-// row covers 32-blocks 4*(kt/2) .. 4*(kt/2)+3, of which stage kt uses
-// blocks 2kt and 2kt+1 (bytes 2*(kt&1) and 2*(kt&1)+1).
+// Stage kt of a tile: L code DMA instructions per wave, plus (MX, even kt)
+// the scale dword of the stage pair into `scale` (nullptr for bf16).
 template <int BM, bool MX>
 __device__ __forceinline__ void issue_stage(StageBuf<BM, MX>& b, const DmaSrc<BM, MX>& src, uint32_t boff,
-                                            uint32_t bstride, int kt, uint32_t wave) {
+                                            uint32_t bstride, int kt, uint32_t wave, ScaleSlot<BM>* scale) {
     using C = Big<BM, MX>;
     const char* ab = src.abase + kt * RB;
     const char* bb = src.bbase + kt * RB;
@@ -200,9 +210,11 @@ __device__ __forceinline__ void issue_stage(StageBuf<BM, MX>& b, const DmaSrc<BM
 #pragma unroll
     for (int j = 0; j < C::B_INS; ++j) dma16(bb, boff + j * bstride, wl + j * 1024);
     if constexpr (MX) {
-        const uint32_t sl = wave < static_cast<uint32_t>(BM / 64) ? lds_addr(b.sct) + wave * 256
-                                                                   : lds_addr(b.scw) + (wave - BM / 64) * 256;
-        dma4(src.sbase, src.soff + (kt >> 1) * 4, sl);
+        if ((kt & 1) == 0) {
+            const uint32_t sl = wave < static_cast<uint32_t>(BM / 64) ? lds_addr(scale->tok) + wave * 256
+                                                                       : lds_addr(scale->wt) + (wave - BM / 64) * 256;
+            dma4(src.sbase, src.soff + (kt >> 1) * 4, sl);
+        }
     }
 }
 
@@ -281,7 +293,8 @@ __device__ __forceinline__ constexpr int frow_const(int f) {
 
 // Fragment reads. PAR is the stage's parity (which MX scale bytes).
 template <int BM, bool GEMM1, bool MX, int PAR>
-__device__ __forceinline__ void read_half(const StageBuf<BM, MX>& b, int h, const LaneOff& o, Frag<BM, MX>& f) {
+__device__ __forceinline__ void read_half(const StageBuf<BM, MX>& b, const ScaleSlot<BM>* sc, int h, const LaneOff& o,
+                                          Frag<BM, MX>& f) {
     using C = Big<BM, MX>;
     const int g = (threadIdx.x & 63) >> 5;
     if constexpr (!MX) {
@@ -298,21 +311,22 @@ __device__ __forceinline__ void read_half(const StageBuf<BM, MX>& b, int h, cons
         for (int i = 0; i < 2; ++i) {
             const int fr = frow_const<GEMM1>(2 * h + i);
             f.w[i] = frag32(b.wt + o.w + fr * RB, lo, hi);
-            f.sw[i] = static_cast<int>((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(b.scw) +
+            f.sw[i] = static_cast<int>((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(sc->wt) +
                                                                            o.sw + fr * 4) >> sh) & 0xffu);
         }
     }
 }
 
 template <int BM, int PAR>
-__device__ __forceinline__ void read_tok(const StageBuf<BM, true>& b, const LaneOff& o, TokFrag<BM>& f) {
+__device__ __forceinline__ void read_tok(const StageBuf<BM, true>& b, const ScaleSlot<BM>* sc, const LaneOff& o,
+                                         TokFrag<BM>& f) {
     const int g = (threadIdx.x & 63) >> 5;
     const int lo = o.clo, hi = o.chi;
     const int sh = 8 * (2 * PAR + g);
 #pragma unroll
     for (int i = 0; i < Big<BM, true>::NT; ++i) {
         f.t[i] = frag32(b.tok + o.t + 32 * i * RB, lo, hi);
-        f.st[i] = static_cast<int>((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(b.sct) +
+        f.st[i] = static_cast<int>((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(sc->tok) +
                                                                        o.st + 32 * i * 4) >> sh) & 0xffu);
     }
 }
@@ -379,6 +393,13 @@ struct Ring {
     bool cont;                 // the next tile's stages follow this tile's in the ring
     TileDesc next;             // the next tile (valid when has_next)
     int nb;                    // row-vector buffer of the next tile (0 or 1)
+    ScaleSlot<BM>* scales;     // MX: the kScaleSlots scale slots
+    int pair0;                 // MX: running stage-pair index of this tile's stage 0
+    // MX: the scale slot of stage s of this tile (next = false) or of the next tile
+    __device__ __forceinline__ ScaleSlot<BM>* slot(int s, bool next = false) const {
+        if constexpr (!MX) return nullptr;
+        else return scales + ((pair0 + (next ? KT / 2 : 0) + (s >> 1)) & (kScaleSlots - 1));
+    }
 };
 
 // DMA of a tile's row map: sorted_to_pair[row0 .. row0 + BM) -> pairs[0 .. BM).
@@ -482,13 +503,13 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
                                           const StageBuf<BM, MX>& nxt, int kt, int32_t (*pairs)[BM],
                                           float (*wrow)[BM], const LaneOff& o, Regs<BM, MX>& g,
                                           f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
-    constexpr int L = Big<BM, MX>::L;
-    read_half<BM, GEMM1, MX, PAR>(cur, 1, o, g.f1);
+    using C = Big<BM, MX>;
+    read_half<BM, GEMM1, MX, PAR>(cur, r.slot(kt), 1, o, g.f1);
     if constexpr (MX) mfma_mx<BM>(g.f0, g.tf, 0, acc);
     else mfma_half<BM>(g.f0, acc);
     const bool more1 = kt + 1 < r.KT || r.cont;  // stage kt+1 exists
-    if (kt + 3 < r.KT || r.cont) wait_vm_lds<2 * L>();
-    else if (kt + 2 < r.KT) wait_vm_lds<L>();
+    if (kt + 3 < r.KT || r.cont) wait_vm_lds<C::Y2>();
+    else if (kt + 2 < r.KT) wait_vm_lds<C::Y1>();
     else wait_vm_lds<0>();
     bare_barrier();
     if (r.cont) {
@@ -498,14 +519,16 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
             if (!GEMM1) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
         }
     }
-    if (kt + 4 < r.KT) issue_stage<BM, MX>(cur, r.src, r.boff, r.bstride, kt + 4, r.wave);
-    else if (r.cont) issue_stage<BM, MX>(cur, r.nsrc, r.boff, r.bstride, kt + 4 - r.KT, r.wave);
-    if (more1) read_half<BM, GEMM1, MX, PAR ^ 1>(nxt, 0, o, g.f0);
+    if (kt + 4 < r.KT) issue_stage<BM, MX>(cur, r.src, r.boff, r.bstride, kt + 4, r.wave, r.slot(kt + 4));
+    else if (r.cont)
+        issue_stage<BM, MX>(cur, r.nsrc, r.boff, r.bstride, kt + 4 - r.KT, r.wave, r.slot(kt + 4 - r.KT, true));
+    ScaleSlot<BM>* nsc = kt + 1 < r.KT ? r.slot(kt + 1) : r.slot(0, true);  // scales of stage kt+1
+    if (more1) read_half<BM, GEMM1, MX, PAR ^ 1>(nxt, nsc, 0, o, g.f0);
     if constexpr (MX) {
         // the token fragments of stage kt+1 go where this stage's were, once
         // its last MFMAs have been issued
         mfma_mx<BM>(g.f1, g.tf, 1, acc);
-        if (more1) read_tok<BM, PAR ^ 1>(nxt, o, g.tf);
+        if (more1) read_tok<BM, PAR ^ 1>(nxt, nsc, o, g.tf);
     } else {
         mfma_half<BM>(g.f1, acc);
     }
@@ -541,20 +564,20 @@ __device__ __forceinline__ void main_loop(const BigArgs& a, Ring<BM, MX>& r, Sta
     }
 }
 
-// Issue stages 0..3 of a tile, wait for stage 0 and read its first half.
+// Issue stages 0..3 of a tile (this one, or the next one: `next`), wait for
+// stage 0 and read its first half.
 template <int BM, bool GEMM1, bool MX>
-__device__ __forceinline__ void ring_start(Ring<BM, MX>& r, const DmaSrc<BM, MX>& src, StageBuf<BM, MX>& b0,
-                                           StageBuf<BM, MX>& b1, StageBuf<BM, MX>& b2, StageBuf<BM, MX>& b3,
-                                           const LaneOff& o, Regs<BM, MX>& g) {
-    constexpr int L = Big<BM, MX>::L;
-    issue_stage<BM, MX>(b0, src, r.boff, r.bstride, 0, r.wave);
-    issue_stage<BM, MX>(b1, src, r.boff, r.bstride, 1, r.wave);
-    issue_stage<BM, MX>(b2, src, r.boff, r.bstride, 2, r.wave);
-    issue_stage<BM, MX>(b3, src, r.boff, r.bstride, 3, r.wave);
-    wait_vm<3 * L>();
+__device__ __forceinline__ void ring_start(Ring<BM, MX>& r, const DmaSrc<BM, MX>& src, bool next,
+                                           StageBuf<BM, MX>& b0, StageBuf<BM, MX>& b1, StageBuf<BM, MX>& b2,
+                                           StageBuf<BM, MX>& b3, const LaneOff& o, Regs<BM, MX>& g) {
+    issue_stage<BM, MX>(b0, src, r.boff, r.bstride, 0, r.wave, r.slot(0, next));
+    issue_stage<BM, MX>(b1, src, r.boff, r.bstride, 1, r.wave, r.slot(1, next));
+    issue_stage<BM, MX>(b2, src, r.boff, r.bstride, 2, r.wave, r.slot(2, next));
+    issue_stage<BM, MX>(b3, src, r.boff, r.bstride, 3, r.wave, r.slot(3, next));
+    wait_vm<Big<BM, MX>::Y3>();
     bare_barrier();
-    read_half<BM, GEMM1, MX, 0>(b0, 0, o, g.f0);
-    if constexpr (MX) read_tok<BM, 0>(b0, o, g.tf);
+    read_half<BM, GEMM1, MX, 0>(b0, r.slot(0, next), 0, o, g.f0);
+    if constexpr (MX) read_tok<BM, 0>(b0, r.slot(0, next), o, g.tf);
 }
 
 // Results of a tile. acc[f][t][4i + j] holds feature frow[f] + 8i +
@@ -700,6 +723,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
     __shared__ __attribute__((aligned(16))) float sW[2][BM];
     __shared__ TileDesc sDesc[CAP];
     __shared__ __attribute__((aligned(16))) uint8_t sOut[W][2048];  // per-wave result staging
+    __shared__ __attribute__((aligned(16))) ScaleSlot<BM> sScale[MX ? kScaleSlots : 1];
 
     // This workgroup's tiles: logical tiles first, first + stride, ... of its
     // XCD's range. The tile count comes from the route step.
@@ -729,6 +753,8 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
 
     Ring<BM, MX> r;
     r.wave = static_cast<uint32_t>(uniform_int(wave_v));
+    r.scales = sScale;
+    r.pair0 = 0;
     const int K = GEMM1 ? a.D : a.H;
     r.KT = K / Fmt<MX>::KS;
     r.pipelined = r.KT >= kMinPipelinedKT;
@@ -755,7 +781,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
         bare_barrier();
     }
     Regs<BM, MX> g;
-    ring_start<BM, GEMM1, MX>(r, r.src, buf0, buf1, buf2, buf3, o, g);
+    ring_start<BM, GEMM1, MX>(r, r.src, false, buf0, buf1, buf2, buf3, o, g);
 
     f32x16_t acc[4][C::NT];
     for (int i = 0; i < count; ++i) {
@@ -788,13 +814,14 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
                 wait_vm<0>();
                 bare_barrier();
             }
-            ring_start<BM, GEMM1, MX>(r, r.nsrc, buf0, buf1, buf2, buf3, o, g);
+            ring_start<BM, GEMM1, MX>(r, r.nsrc, true, buf0, buf1, buf2, buf3, o, g);
         }
         if constexpr (GEMM1 && MX) epilogue_mx_gemm1<BM>(a, t, tok_row0, wf, sOut[wave_v], acc);
         else epilogue_bf16<BM, GEMM1, MX>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
         if (!r.has_next) break;
         t = r.next;
         r.src = r.nsrc;
+        r.pair0 += r.KT / 2;
         cb ^= 1;
     }
 }
