@@ -198,6 +198,15 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
     }
     const int r = lane & 15, kg = lane >> 4;
     const int KIT = K / KC, NIT = G * KIT;
+    // GEMM2: each block walks its G groups starting at a different one.
+    // Groups are 64 rows apart, so if every block visited them in the same
+    // order, all blocks would read rows at the same offsets mod 64 rows at the
+    // same time and, with rows a power of two of bytes apart (GEMM2's K = H:
+    // 4 KB), pile onto the same subset of HBM channels; counters showed 18x
+    // the DRAM credit stalls of GEMM1, and the rotation takes GEMM2 from 161
+    // to 152 us on the decode workload. (GEMM1's 12 KB rows already spread
+    // over the channels; rotating them measured 2% slower.)
+    const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;
     f32x4_t acc[NB][NT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -205,14 +214,14 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
         for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
 #pragma unroll
     for (int j = 0; j < S - 1; ++j)
-        if (j < NIT) dma_issue<NT, KC, S>(ring, j, j / KIT, j % KIT, group_stride, wsrc, tsrc);
+        if (j < NIT) dma_issue<NT, KC, S>(ring, j, (j / KIT + rot) % G, j % KIT, group_stride, wsrc, tsrc);
     for (int it = 0; it < NIT; ++it) {
         if (it + S - 2 < NIT) wait_vm<(S - 2) * (T::W_INS + T::T_INS)>();
         else wait_vm<0>();
         ring_barrier();
         if (it + S - 1 < NIT) {
             const int nx = it + S - 1;
-            dma_issue<NT, KC, S>(ring, nx, nx / KIT, nx % KIT, group_stride, wsrc, tsrc);
+            dma_issue<NT, KC, S>(ring, nx, (nx / KIT + rot) % G, nx % KIT, group_stride, wsrc, tsrc);
         }
         uint8_t* slot = ring + (it % S) * T::STAGE;
 #pragma unroll
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
                     }
         }
         // epilogue: wave w stores token tile w (acc[b][t][v]: row 16b + 4kg + v, token 16t + r)
-        const int g = grp0 + it / KIT;
+        const int g = grp0 + (it / KIT + rot) % G;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int m = 16 * t + r;
