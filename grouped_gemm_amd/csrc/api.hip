@@ -107,7 +107,7 @@ Plan make_plan(const moe_ffn_problem* p, int mode) {
         pl.ypair = off;
         off = align_up(off + 2 * static_cast<size_t>(P) * p->D);
         pl.mtiles = off;
-        off = align_up(off + 16 * static_cast<size_t>(moe::big_gemm_mtile_capacity(P, p->E)));
+        off = align_up(off + static_cast<size_t>(moe::big_gemm_workspace_bytes(P, p->E)));
     } else {
         pl.acc32 = off;
         off = align_up(off + 4 * static_cast<size_t>(p->T) * p->D);

@@ -110,7 +110,7 @@ struct Bf16Args {
     RouteView rv;
     uint16_t* act;     // [P, H]   split only
     uint16_t* ypair;   // [P, D]   split only: weighted expert outputs in pair order
-    int32_t* mtiles;   // split only: m-tile table of the prefill GEMMs, big_gemm_mtile_capacity x int4
+    int32_t* mtiles;   // split only: big_gemm_workspace_bytes for the prefill GEMMs
     float* acc32;      // [T, D]   fused only
     uint16_t* out;     // [T, D]
 };
@@ -124,6 +124,9 @@ hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);
 bool big_gemm_supported(const Bf16Args& a);
 // Entries (int4 each) the m-tile table needs for P routed pairs and E experts.
 int64_t big_gemm_mtile_capacity(int64_t P, int E);
+// Workspace bytes at `mtiles` the prefill GEMMs use: the m-tile table, then
+// a 1 MB sink for the result stores of rows past an expert's count.
+int64_t big_gemm_workspace_bytes(int64_t P, int E);
 // Entries past P that sorted_to_pair in the workspace must hold (a tile's
 // row-map window may run past the last routed row; the extra entries are
 // read and clamped, never written).
@@ -145,7 +148,7 @@ struct MxArgs {
     uint8_t* act_s;     // [P, H/32] e8m0
     uint16_t* ypair;    // [P, D]
     uint16_t* out;      // [T, D]
-    int32_t* mtiles;    // m-tile table of the prefill GEMMs, big_gemm_mtile_capacity x int4
+    int32_t* mtiles;    // big_gemm_workspace_bytes for the prefill GEMMs
 };
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
 // Prefill-shaped MX GEMM1 / GEMM2 (the bf16 prefill kernels' ring on the scaled MFMA).

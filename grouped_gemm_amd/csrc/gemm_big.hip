@@ -59,6 +59,12 @@ constexpr int kThreads = 64 * W;
 constexpr int RB = 64;             // bytes per tile row per stage
 constexpr int BN = 256;            // weight rows per tile
 constexpr int kMinPipelinedKT = 8; // K stages a tile needs for the in-loop hand-over
+// Result stores of rows past an expert's count go to a sink in the workspace
+// instead of being skipped (see the epilogues): one area per wave of a
+// workgroup slot, one 1 KB line per store of an epilogue.
+constexpr int kSinkSlots = 8;
+constexpr int kSinkWaveBytes = 16 * 1024;
+constexpr int64_t kSinkBytes = int64_t(kSinkSlots) * W * kSinkWaveBytes;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -79,6 +85,7 @@ struct BigArgs {
     uint8_t* act;
     uint8_t* act_s;
     uint16_t* ypair;
+    uint8_t* sink;  // kSinkBytes
 };
 
 template <bool MX>
@@ -106,6 +113,11 @@ struct Big {
     static constexpr int PW = BM / 64;         // waves that move one BM-entry int/float vector (64 per wave)
     static_assert(NT >= 1 && A_INS >= 1 && A_INS * 16 * W == BM && B_INS * 16 * W == BN, "tile split");
     static_assert(PW >= 1 && PW <= W, "row-vector DMA waves");
+    // 16-byte result stores each wave issues per tile (epilogue_bf16, or the
+    // code stores of epilogue_mx_gemm1)
+    template <bool GEMM1>
+    static constexpr int stores() { return NT * (GEMM1 ? (MX ? 2 : 4) : 8); }
+    static_assert(stores<false>() * 1024 <= kSinkWaveBytes, "sink lines per wave");
     static_assert(!MX || BM / 64 + BN / 64 == W, "one scale-row DMA per wave");
 };
 
@@ -489,15 +501,24 @@ __device__ __forceinline__ void make_src(const BigArgs& a, const TileDesc& t, co
 //
 // Waits: before the barrier each wave waits until its own DMAs of stage kt+1
 // are done; the stages it issued after it (kt+2, kt+3, while they exist) may
-// stay in flight. Loads, LDS DMA included, complete in order, so this holds
-// with the previous tile's result stores or the few row-vector DMAs also in
-// flight: at most 2L operations outstanding leaves at least as many of this
-// wave's loads done as there were older ones.
+// stay in flight. Vector-memory operations of a wave (loads, LDS DMA and
+// stores) leave the count in issue order, so a budget of n outstanding
+// guarantees every operation older than the last n. Extra younger operations
+// (the few row-vector DMAs) only make a wait stricter. The previous tile's
+// result stores are younger than stages 1..3 of this one: in steps 0..2 the
+// budget grows by their exact number, so those steps wait for their stage
+// and not for the stores; step 3's stage was issued after the stores.
 //
 // Hand-over (pipelined tiles): step 0 fetches the next tile's row map,
 // complete by step 3's barrier; step 3 builds the next tile's DMA sources
 // from it and fetches its routing weights (GEMM2), complete by step 6's
 // barrier; steps KT-4 .. KT-1 issue its stages 0..3.
+template <int N, int EX>
+__device__ __forceinline__ void wait_budget(bool extra) {
+    if (extra) wait_vm_lds<N + EX>();
+    else wait_vm_lds<N>();
+}
+
 template <int BM, bool GEMM1, bool MX, int PAR>
 __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, StageBuf<BM, MX>& cur,
                                           const StageBuf<BM, MX>& nxt, int kt, int32_t (*pairs)[BM],
@@ -508,9 +529,11 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
     if constexpr (MX) mfma_mx<BM>(g.f0, g.tf, 0, acc);
     else mfma_half<BM>(g.f0, acc);
     const bool more1 = kt + 1 < r.KT || r.cont;  // stage kt+1 exists
-    if (kt + 3 < r.KT || r.cont) wait_vm_lds<C::Y2>();
-    else if (kt + 2 < r.KT) wait_vm_lds<C::Y1>();
-    else wait_vm_lds<0>();
+    constexpr int S = C::template stores<GEMM1>();
+    const bool after_stores = kt < 3;  // the previous tile's stores are in flight
+    if (kt + 3 < r.KT || r.cont) wait_budget<C::Y2, S>(after_stores);
+    else if (kt + 2 < r.KT) wait_budget<C::Y1, S>(after_stores);
+    else wait_budget<0, S>(after_stores);
     bare_barrier();
     if (r.cont) {
         if (kt == 0) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
@@ -544,8 +567,10 @@ __device__ __forceinline__ void main_loop(const BigArgs& a, Ring<BM, MX>& r, Sta
                                           f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
     // KT is a multiple of 4: the unrolled body needs no exit in the middle,
     // which would make the compiler shuttle the accumulators between
-    // registers at the loop head. Every tile starts at buffer 0. The body is
-    // unrolled by hand; for MX, more copies only raise register pressure.
+    // registers at the loop head. Every tile starts at buffer 0, with the
+    // previous tile's result stores (or the first tile's sink stores) in
+    // flight. The body is unrolled by hand; for MX, more copies only raise
+    // register pressure.
     if constexpr (MX) {
 #pragma clang loop unroll(disable)
         for (int kt = 0; kt < r.KT; kt += 4) {
@@ -589,7 +614,28 @@ __device__ __forceinline__ void ring_start(Ring<BM, MX>& r, const DmaSrc<BM, MX>
 // quarter of the write requests of storing the 8-byte pieces. The area is
 // the wave's own, so no barrier is needed; LDS accesses of one wave complete
 // in order.
+//
+// Every wave issues exactly Big::stores() 16-byte stores per tile with all
+// lanes on: a lane whose row is past the tile's count writes into the wave's
+// sink area instead (its row pointer moves there). The next tile's first
+// waits count on that number.
 __device__ __forceinline__ int stage_chunk_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ uint8_t* wave_sink(const BigArgs& a) {
+    return a.sink + ((blockIdx.x & (kSinkSlots - 1)) * W + (threadIdx.x >> 6)) * kSinkWaveBytes +
+           (threadIdx.x & 63) * 16;
+}
+
+__device__ __forceinline__ void store16(void* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+// The stores a wave's first tile finds in flight in place of a previous
+// tile's: Big::stores() zero lines to its sink area.
+template <int BM, bool GEMM1, bool MX>
+__device__ __forceinline__ void sink_stores(const BigArgs& a) {
+    uint8_t* sink = wave_sink(a);
+#pragma unroll
+    for (int j = 0; j < Big<BM, MX>::template stores<GEMM1>(); ++j) store16(sink + 1024 * j, u32x4_t{0, 0, 0, 0});
+}
 
 // bf16 results: GEMM1 writes act = silu(gate) * up at act[row0 + row][h0 + col];
 // GEMM2 (both formats) writes w * y at ypair[pair][n0 + feature].
@@ -602,6 +648,7 @@ __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& 
     const int r = lane & 31, g = lane >> 5;
     const int rr = lane >> 2, c = lane & 3;  // staging reads: rows rr and rr + 16, chunk c
     const int rd0 = stage_chunk_off(rr, c), rd1 = stage_chunk_off(rr + 16, c);
+    uint16_t* sink = reinterpret_cast<uint16_t*>(wave_sink(a));
 #pragma unroll
     for (int tb = 0; tb < C::NT; ++tb) {
         const int base = tok_row0 + 32 * tb;
@@ -617,6 +664,8 @@ __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& 
             d0 = a.ypair + static_cast<int64_t>(clamp_pair(pairs[base + rr], a.P)) * a.D + col;
             d1 = a.ypair + static_cast<int64_t>(clamp_pair(pairs[base + rr + 16], a.P)) * a.D + col;
         }
+        d0 = ok0 ? d0 : sink;
+        d1 = ok1 ? d1 : sink;
         const float wt = GEMM1 ? 1.0f : w[base + r];
 #pragma unroll
         for (int f = 0; f < (GEMM1 ? 2 : 4); ++f) {
@@ -633,8 +682,8 @@ __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& 
             }
             const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(stg + rd0);
             const u32x4_t q1 = *reinterpret_cast<const u32x4_t*>(stg + rd1);
-            if (ok0) *reinterpret_cast<u32x4_t*>(d0 + 32 * f) = q0;
-            if (ok1) *reinterpret_cast<u32x4_t*>(d1 + 32 * f) = q1;
+            store16(d0 + 32 * f, q0);
+            store16(d1 + 32 * f, q1);
         }
     }
 }
@@ -656,6 +705,7 @@ __device__ __forceinline__ void epilogue_mx_gemm1(const BigArgs& a, const TileDe
     const int rd0 = stage_chunk_off(rr, c), rd1 = stage_chunk_off(rr + 16, c);
     const int HB = a.H / 32;
     const int col0 = t.ntile * 128 + 64 * wf;  // first act column of this wave
+    uint8_t* sink = wave_sink(a);
 #pragma unroll
     for (int tb = 0; tb < C::NT; ++tb) {
         const int base = tok_row0 + 32 * tb;
@@ -690,8 +740,9 @@ __device__ __forceinline__ void epilogue_mx_gemm1(const BigArgs& a, const TileDe
         const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(stg + rd0);
         const u32x4_t q1 = *reinterpret_cast<const u32x4_t*>(stg + rd1);
         uint8_t* d0 = a.act + static_cast<int64_t>(t.row0 + base + rr) * a.H + col0 + 16 * c;
-        if (base + rr < t.rows) *reinterpret_cast<u32x4_t*>(d0) = q0;
-        if (base + rr + 16 < t.rows) *reinterpret_cast<u32x4_t*>(d0 + static_cast<int64_t>(16) * a.H) = q1;
+        uint8_t* d1 = d0 + static_cast<int64_t>(16) * a.H;
+        store16(base + rr < t.rows ? d0 : sink, q0);
+        store16(base + rr + 16 < t.rows ? d1 : sink, q1);
     }
 }
 
@@ -782,6 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
     }
     Regs<BM, MX> g;
     ring_start<BM, GEMM1, MX>(r, r.src, false, buf0, buf1, buf2, buf3, o, g);
+    sink_stores<BM, GEMM1, MX>(a);
 
     f32x16_t acc[4][C::NT];
     for (int i = 0; i < count; ++i) {
@@ -882,6 +934,13 @@ constexpr int64_t kBigTile256MinRows = 512;
 
 int64_t big_gemm_mtile_capacity(int64_t P, int E) { return (P + 127) / 128 + E; }
 
+namespace {
+int64_t table_bytes(int64_t P, int E) { return (16 * big_gemm_mtile_capacity(P, E) + 255) / 256 * 256; }
+uint8_t* sink_of(int32_t* mtiles, int64_t P, int E) { return reinterpret_cast<uint8_t*>(mtiles) + table_bytes(P, E); }
+}  // namespace
+
+int64_t big_gemm_workspace_bytes(int64_t P, int E) { return table_bytes(P, E) + kSinkBytes; }
+
 bool big_gemm_supported(const Bf16Args& a) {
     const int64_t lim = int64_t(1) << 32;  // the DMA offsets are 32-bit
     return a.mtiles != nullptr && a.D % 256 == 0 && a.H % 128 == 0 && int64_t(a.T) * a.D * 2 < lim &&
@@ -893,7 +952,7 @@ hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
               reinterpret_cast<const uint8_t*>(b.x), nullptr,
               reinterpret_cast<const uint8_t*>(b.w1), nullptr,
               reinterpret_cast<const uint8_t*>(b.w2), nullptr,
-              b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair};
+              b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair, sink_of(b.mtiles, b.P, b.E)};
     int4* tiles = reinterpret_cast<int4*>(b.mtiles);
     if (b.P >= kBigTile256MinRows * b.E) return launch_big<256, false>(a, tiles, gemm1, s);
     return launch_big<128, false>(a, tiles, gemm1, s);
@@ -908,7 +967,8 @@ bool big_mx_supported(const MxArgs& a) {
 }
 
 hipError_t launch_big_mx(const MxArgs& b, bool gemm1, hipStream_t s) {
-    BigArgs a{b.T, b.D, b.H, b.E, b.k, b.P, b.x, b.xs, b.w1, b.w1s, b.w2, b.w2s, b.wts, b.rv, b.act, b.act_s, b.ypair};
+    BigArgs a{b.T,   b.D,   b.H,     b.E,  b.k,  b.P,      b.x,     b.xs,    b.w1,
+              b.w1s, b.w2,  b.w2s,   b.wts, b.rv, b.act,   b.act_s, b.ypair, sink_of(b.mtiles, b.P, b.E)};
     return launch_big<256, true>(a, reinterpret_cast<int4*>(b.mtiles), gemm1, s);
 }
 
