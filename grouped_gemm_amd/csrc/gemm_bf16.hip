@@ -356,6 +356,9 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(Bf16Args a) {
 // ---------------- combine / conversions ----------------
 
 // out[t, :] = bf16( sum over valid slots j of ypair[t*k + j, :] ), 8 columns per thread.
+// Every ypair byte is read once and every out byte written once: both go
+// through nontemporal accesses (streamed past the caches), launched with
+// one item per thread for all but huge T.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ ypair,
                                                       const int32_t* __restrict__ p2s, int32_t T,
                                                       int32_t k, int32_t D, uint16_t* __restrict__ out) {
@@ -372,7 +375,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
             for (int j = 0; j < 8; ++j) {
                 const int64_t p = t * k + j0 + j;
                 const bool ok = j0 + j < k && p2s[p] >= 0;
-                v[j] = ok ? *reinterpret_cast<const u32x4_t*>(ypair + p * D + c * 8) : u32x4_t{0, 0, 0, 0};
+                v[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ypair + p * D + c * 8))
+                          : u32x4_t{0, 0, 0, 0};
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         o.y = pack_bf16x2(s[2], s[3]);
         o.z = pack_bf16x2(s[4], s[5]);
         o.w = pack_bf16x2(s[6], s[7]);
-        *reinterpret_cast<u32x4_t*>(out + t * D + c * 8) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + t * D + c * 8));
     }
 }
 
@@ -403,11 +407,12 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* src, uin
     }
 }
 
-inline int grid_for(int64_t work, int per_block) {
+inline int grid_for(int64_t work, int per_block, int64_t cap = 256 * 32) {
     int64_t g = (work + per_block - 1) / per_block;
-    if (g > 256 * 32) g = 256 * 32;
+    if (g > cap) g = cap;
     return static_cast<int>(g < 1 ? 1 : g);
 }
+constexpr int64_t kCombineMaxBlocks = int64_t(1) << 20;
 
 inline int mtiles_upper(int64_t P, int E, int bm) {
     return static_cast<int>((P + bm - 1) / bm + E);
@@ -437,7 +442,7 @@ hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
         gemm2_weight_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
     }
     record(ev, 1, s);
-    combine_kernel<<<grid_for(static_cast<int64_t>(a.T) * a.D / 8, 256), 256, 0, s>>>(
+    combine_kernel<<<grid_for(static_cast<int64_t>(a.T) * a.D / 8, 256, kCombineMaxBlocks), 256, 0, s>>>(
         a.ypair, a.rv.pair_to_sorted, a.T, a.k, a.D, a.out);
     record(ev, 2, s);
     return hipGetLastError();
@@ -459,7 +464,8 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
 
 hipError_t launch_combine(const uint16_t* ypair, const int32_t* p2s, int32_t T, int32_t k, int32_t D,
                           uint16_t* out, hipStream_t s) {
-    combine_kernel<<<grid_for(static_cast<int64_t>(T) * D / 8, 256), 256, 0, s>>>(ypair, p2s, T, k, D, out);
+    combine_kernel<<<grid_for(static_cast<int64_t>(T) * D / 8, 256, kCombineMaxBlocks), 256, 0, s>>>(ypair, p2s, T,
+                                                                                                     k, D, out);
     return hipGetLastError();
 }
 
