@@ -33,7 +33,8 @@ gate and up projections concatenated along W1's output dimension).
 
 softmax-top-k: logits ~ N(0, 1) [T, E] -> softmax -> the k largest
 probabilities in descending order (ties to the lower expert id) ->
-renormalized to sum to 1, cast to fp32.
+renormalized to sum to 1, cast to fp32. For the pass that starts from the
+router's logits, router_logits() hands out the logits alone.
 """
 from __future__ import annotations
 
@@ -175,6 +176,18 @@ def routing(cfg: Config, seed: int = 0):
     w = w / w.sum(axis=1, keepdims=True)
     return (np.ascontiguousarray(ids.astype(np.int32)),
             np.ascontiguousarray(w.astype(np.float32)))
+
+
+def router_logits(cfg: Config, seed: int = 0) -> np.ndarray:
+    """Router logits fp32 [T, E] of the recipe above, for the pass that starts
+    from logits: the draws routing() makes for softmax and Zipf configs (the
+    same stream, so the routes agree up to fp32 rounding of near-ties), N(0, 1)
+    for the others. The softmax/top-k itself is not done here."""
+    rng = _rng(cfg, ROLE_ROUTING, seed)
+    logits = rng.standard_normal((cfg.T, cfg.E))
+    if cfg.routing == "zipf":
+        logits = logits - cfg.zipf_s * np.log(np.arange(1, cfg.E + 1, dtype=np.float64))[None, :]
+    return np.ascontiguousarray(logits.astype(np.float32))
 
 
 def _tensors(cfg: Config, seed: int, bf16: bool):

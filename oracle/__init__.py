@@ -44,6 +44,7 @@ def _load():
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.oracle_route.argtypes = [P, i64, i32, i32, P, P, P, P]
+        lib.oracle_router.argtypes = [P, i64, i32, i32, P, P]
         lib.oracle_forward_bf16.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i64]
         lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                           P, i64, i32]
@@ -91,6 +92,25 @@ def route(topk_ids: np.ndarray, E: int):
     p2s = np.zeros(max(P, 1), np.int32)
     _load().oracle_route(_p(ids), T, k, E, _p(counts), _p(offsets), _p(s2p), _p(p2s))
     return counts, offsets, s2p[:P], p2s[:P]
+
+
+def router(logits: np.ndarray, k: int):
+    """Softmax -> top-k -> renormalize: (topk_ids int32 [T, k], topk_weights fp32 [T, k]).
+
+    Prime Flash MoE, section 1: the pass starts from each token's top-k
+    experts and normalized routing weights. Order: largest logit first, ties
+    to the lower expert id (softmax is increasing in the logit); weights are
+    the selected softmax probabilities divided by their sum, in double,
+    rounded once to fp32.
+    """
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    assert 1 <= k <= E
+    ids = np.zeros((T, k), np.int32)
+    wts = np.zeros((T, k), np.float32)
+    if T:
+        _load().oracle_router(_p(lg), T, E, k, _p(ids), _p(wts))
+    return ids, wts
 
 
 def forward_bf16(x, w1, w2, topk_ids, topk_weights, tokens=None):

@@ -158,6 +158,66 @@ void oracle_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* 
     free(next);
 }
 
+/* ---------- router ---------- */
+
+/* The router the pass starts from ("Prime Flash MoE", section 1 "The
+ * computation": each token arrives with its top-k experts and normalized
+ * routing weights): probabilities p = softmax(logits) over the E experts;
+ * the k most probable experts, most probable first, ties to the lower
+ * expert id; their probabilities renormalized to sum to 1.
+ *
+ * Softmax is strictly increasing in the logit, so "most probable" is
+ * "largest logit": the order is taken on the fp32 logits themselves, which
+ * fixes the ids exactly (two distinct logits never tie, whatever the
+ * rounding of their probabilities). p is evaluated in double as
+ * exp(l - max l) / sum, and each weight is rounded once to fp32. */
+typedef struct {
+    float v;
+    int32_t id;
+} oracle_scored;
+
+static int oracle_scored_cmp(const void* a, const void* b) {
+    const oracle_scored* x = (const oracle_scored*)a;
+    const oracle_scored* y = (const oracle_scored*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+void oracle_router(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* wts) {
+#pragma omp parallel
+    {
+        oracle_scored* s = (oracle_scored*)malloc(sizeof(oracle_scored) * (size_t)E);
+        double* p = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const float* l = logits + t * E;
+            float m = l[0];
+            for (int32_t e = 1; e < E; ++e)
+                if (l[e] > m) m = l[e];
+            double z = 0.0;
+            for (int32_t e = 0; e < E; ++e) {
+                p[e] = exp((double)l[e] - (double)m);
+                z += p[e];
+            }
+            for (int32_t e = 0; e < E; ++e) {
+                p[e] /= z;
+                s[e].v = l[e];
+                s[e].id = e;
+            }
+            qsort(s, (size_t)E, sizeof(oracle_scored), oracle_scored_cmp);
+            double sel = 0.0;
+            for (int32_t j = 0; j < k; ++j) sel += p[s[j].id];
+            for (int32_t j = 0; j < k; ++j) {
+                ids[t * k + j] = s[j].id;
+                wts[t * k + j] = (float)(p[s[j].id] / sel);
+            }
+        }
+        free(s);
+        free(p);
+    }
+}
+
 /* ---------- forward ---------- */
 
 static float silu(float z) { return z / (1.0f + expf(-z)); }
