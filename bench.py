@@ -60,6 +60,9 @@ def parse_args(argv=None):
                     help="override the workload's token count T (crossover sweeps)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--logits", action="store_true",
+                    help="start each step from router logits (moe_ffn_forward_logits): the router's "
+                         "softmax/top-k runs inside the timed pass, fused with the route step")
     return ap.parse_args(argv)
 
 
@@ -117,11 +120,15 @@ def kernel_symbol(cfg, mode, stage):
         return {"fused_ffn": "fused_bf16_kernel", "acc_fill": "fill_zero_f32_kernel",
                 "acc_to_bf16": "f32_to_bf16_kernel", "route": "route kernels"}[stage]
     if stage == "route":
+        if cfg.P <= 256 and cfg.E <= 64:
+            return "route_wave_kernel"
         return "route_small_kernel" if cfg.P <= 16384 and cfg.E <= 1024 else "route_* (4 kernels)"
     if stage == "combine":
         return "combine_kernel"
     g1 = stage == "gemm1_swiglu"
     if cfg.dtype == "mxfp8":
+        if cfg.P >= 512 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
+            return "big_gemm_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.P <= 32 * cfg.E:
         return "dma_skinny_kernel"
@@ -209,6 +216,11 @@ def main(argv=None):
         del s
     ids = torch.from_numpy(host["topk_ids"]).to(dev)
     wts = torch.from_numpy(host["topk_weights"]).to(dev)
+    logits = None
+    if args.logits:
+        # the pass routes from these logits; ids / wts become its outputs
+        host["logits"] = mi.router_logits(cfg, 0)
+        logits = torch.from_numpy(host["logits"]).to(dev)
     mode_id = g.moe_ffn_resolve_mode(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, args.mode)
     mode = {g.MOE_FFN_FUSED: "fused", g.MOE_FFN_SPLIT: "split"}[mode_id]
     nbytes = g.moe_ffn_workspace_bytes(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, mode)
@@ -229,7 +241,11 @@ def main(argv=None):
         events.append(row)
 
     def step(ev=None):
-        g.moe_ffn_forward(x, w1, w2, ids, wts, out=out, mode=mode, workspace=ws, events=ev, **scales)
+        if logits is not None:
+            g.moe_ffn_forward_logits(x, w1, w2, logits, cfg.k, out=out, mode=mode, workspace=ws, topk_ids=ids,
+                                     topk_weights=wts, events=ev, **scales)
+        else:
+            g.moe_ffn_forward(x, w1, w2, ids, wts, out=out, mode=mode, workspace=ws, events=ev, **scales)
 
     log(f"[bench] {cfg.name} mode={mode}: {args.warmup} warmup + {args.steps} timed steps")
     for _ in range(args.warmup):
@@ -242,7 +258,9 @@ def main(argv=None):
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
 
-    names = STAGES[mode]
+    names = list(STAGES[mode])
+    if logits is not None:
+        names[0] = "router_route"
     stage_ms = {n: 0.0 for n in names}
     f = ctypes.c_float()
     for row in events:
@@ -259,15 +277,19 @@ def main(argv=None):
         b.copy_(a)
         torch.cuda.synchronize()
 
+    if logits is not None:
+        host["topk_ids"] = ids.cpu().numpy()  # the routes the timed passes took
     hit = hit_experts(host["topk_ids"], cfg.E)
     work = kernel_work(cfg, mode, hit, dtype)
-    dom = max((n for n in names if n != "route"), key=lambda n: stage_ms[n])
+    dom = max(names[1:], key=lambda n: stage_ms[n])
     dbytes, dflops = work[dom]
     dsec = stage_ms[dom] * 1e-3
     peak_tf = MFMA_PEAK_TFLOPS[dtype]
     intensity = dflops / dbytes if dbytes else 0.0
     ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     workload = f"{cfg.name} {dtype} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k}"
+    if logits is not None:
+        workload += " from router logits"
     traffic = measured_traffic(dom, kernel_symbol(cfg, mode, dom), workload)
     if intensity > ridge:
         roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
@@ -308,6 +330,9 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
+        if logits is not None:
+            import oracle
+            host["topk_ids"], host["topk_weights"] = oracle.router(host["logits"], cfg.k)
         result["cpu_baseline"] = cpu_baseline(cfg, host, dtype, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None

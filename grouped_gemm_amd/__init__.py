@@ -69,6 +69,11 @@ def library() -> ctypes.CDLL:
         lib.moe_ffn_forward_events.argtypes = [PP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP,
                                                ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         lib.moe_ffn_forward_events.restype = ctypes.c_int
+        lib.moe_ffn_router.argtypes = [VP, I32, I32, I32, VP, VP, VP]
+        lib.moe_ffn_router.restype = ctypes.c_int
+        lib.moe_ffn_forward_logits.argtypes = [PP, VP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP,
+                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        lib.moe_ffn_forward_logits.restype = ctypes.c_int
         lib.moe_ffn_route_workspace_bytes.argtypes = [I32, I32, I32]
         lib.moe_ffn_route_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_ffn_route.argtypes = [VP, I32, I32, I32, VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
@@ -181,6 +186,61 @@ def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward")
     return out
+
+
+def moe_ffn_router(logits, k, stream=None):
+    """(topk_ids int32 [T, k], topk_weights fp32 [T, k]) from fp32 logits [T, E] on the GPU:
+    softmax, the k most probable experts (ties to the lower id), renormalized."""
+    if logits.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    _check_cuda(logits)
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    rc = library().moe_ffn_router(logits.data_ptr(), T, E, k, ids.data_ptr(), wts.data_ptr(), _stream(stream))
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_router")
+    return ids, wts
+
+
+def moe_ffn_forward_logits(x, w1, w2, logits, k, out=None, mode="auto", x_scale=None, w1_scale=None,
+                           w2_scale=None, workspace=None, topk_ids=None, topk_weights=None, stream=None,
+                           events=None):
+    """(out, topk_ids, topk_weights): the router on fp32 logits [T, E], then the pass
+    (moe_ffn_forward_logits). Tensors as in moe_ffn_forward; ids/weights are
+    written into `topk_ids` / `topk_weights` when given."""
+    mx = x.dtype == torch.uint8
+    if logits.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    T, D = x.shape
+    E, H2, _ = w1.shape
+    if logits.shape != (T, E):
+        raise ValueError("logits must be [T, E]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check_cuda(x, w1, w2, logits, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
+    p = make_problem(T, D, H2 // 2, E, k, "mxfp8" if mx else "bf16", x_scale, w1_scale, w2_scale)
+    lib = library()
+    m = _mode(mode)
+    if workspace is None:
+        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), m)
+        if nbytes == 0:
+            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m), "moe_ffn_forward_logits")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel()
+    ev, n = (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
+    rc = lib.moe_ffn_forward_logits(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                    logits.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(),
+                                    out.data_ptr(), m, _stream(stream), ev, n)
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_forward_logits")
+    return out, topk_ids, topk_weights
 
 
 def moe_ffn_route(topk_ids, E, stream=None):

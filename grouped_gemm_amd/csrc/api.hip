@@ -190,15 +190,54 @@ MOE_FFN_API int moe_ffn_mx_quantize(const float* src, int64_t rows, int32_t K, u
                : MOE_FFN_EHIP;
 }
 
+MOE_FFN_API int moe_ffn_router(const float* logits, int32_t T, int32_t E, int32_t topk, int32_t* topk_ids,
+                               float* topk_weights, void* stream) {
+    if (T < 0 || E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk || topk > E) return MOE_FFN_EINVAL_SHAPE;
+    if (static_cast<int64_t>(T) * topk > INT_MAX) return MOE_FFN_EINVAL_SHAPE;
+    if (T == 0) return MOE_FFN_OK;
+    if (!logits || !topk_ids || !topk_weights || (reinterpret_cast<uintptr_t>(logits) & 3u) ||
+        (reinterpret_cast<uintptr_t>(topk_ids) & 3u) || (reinterpret_cast<uintptr_t>(topk_weights) & 3u))
+        return MOE_FFN_EINVAL_PTR;
+    return moe::launch_router(logits, T, E, topk, topk_ids, topk_weights, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? MOE_FFN_OK
+               : MOE_FFN_EHIP;
+}
+
 MOE_FFN_API int moe_ffn_forward(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
                                 const int32_t* topk_ids, const float* topk_weights, void* out, int mode,
                                 void* stream) {
     return moe_ffn_forward_events(p, x, w1, w2, topk_ids, topk_weights, out, mode, stream, nullptr, 0);
 }
 
+namespace {
+int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2, const float* logits,
+                 const int32_t* topk_ids, const float* topk_weights, void* out, int mode, void* stream,
+                 void* const* events, int n_events);
+}  // namespace
+
 MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, const void* w1,
                                        const void* w2, const int32_t* topk_ids, const float* topk_weights,
                                        void* out, int mode, void* stream, void* const* events, int n_events) {
+    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, out, mode, stream, events, n_events);
+}
+
+MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
+                                       const float* logits, int32_t* topk_ids, float* topk_weights, void* out,
+                                       int mode, void* stream, void* const* events, int n_events) {
+    if (p && p->T > 0 && (!logits || (reinterpret_cast<uintptr_t>(logits) & 3u))) return MOE_FFN_EINVAL_PTR;
+    return forward_impl(p, x, w1, w2, p && p->T > 0 ? logits : nullptr, topk_ids, topk_weights, out, mode, stream,
+                        events, n_events);
+}
+
+}  // extern "C"
+
+namespace {
+// The pass from given routes (logits == NULL) or from router logits, which
+// then fill topk_ids / topk_weights on the way.
+int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2, const float* logits,
+                 const int32_t* topk_ids, const float* topk_weights, void* out, int mode, void* stream,
+                 void* const* events, int n_events) {
     if (n_events != 0 && n_events != 5) return MOE_FFN_EINVAL_PTR;
     if (n_events == 5 && !events) return MOE_FFN_EINVAL_PTR;
     hipEvent_t ev[5];
@@ -234,7 +273,10 @@ MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, 
                          at<int32_t>(ws, pl.counts), at<int32_t>(ws, pl.offsets),
                          at<int32_t>(ws, pl.route.tile_prefix), at<int32_t>(ws, pl.s2p), at<int32_t>(ws, pl.p2s)};
     moe::record(evp, 0, st);
-    if (moe::launch_route(rb, st) != hipSuccess) return MOE_FFN_EHIP;
+    const hipError_t re = logits ? moe::launch_router_route(logits, p->T, p->E, p->topk, const_cast<int32_t*>(topk_ids),
+                                                            const_cast<float*>(topk_weights), rb, st)
+                                 : moe::launch_route(rb, st);
+    if (re != hipSuccess) return MOE_FFN_EHIP;
     moe::record(evp, 1, st);
     hipEvent_t* stage_ev = evp ? evp + 2 : nullptr;
     moe::RouteView rv{rb.counts, rb.offsets, rb.tile_prefix, rb.sorted_to_pair, rb.pair_to_sorted};
@@ -278,5 +320,4 @@ MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, 
     }
     return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
 }
-
-}  // extern "C"
+}  // namespace

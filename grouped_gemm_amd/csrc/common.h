@@ -99,6 +99,16 @@ struct RouteBuffers {
     int32_t* pair_to_sorted;
 };
 hipError_t launch_route(const RouteBuffers& b, hipStream_t s);
+// True when launch_route takes its multi-kernel path (segment histogram,
+// scan, offsets, scatter); launch_route_after_count runs all but the first.
+bool route_counts_separately(const RouteBuffers& b);
+hipError_t launch_route_after_count(const RouteBuffers& b, hipStream_t s);
+// Router: logits fp32 [T, E] -> ids int32 [T, k], weights fp32 [T, k].
+hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* wts, hipStream_t s);
+// Router, then the route step on its ids (b.ids must be `ids`); on the
+// multi-kernel path the router also builds the segment histogram.
+hipError_t launch_router_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* wts,
+                               const RouteBuffers& b, hipStream_t s);
 
 struct Bf16Args {
     int32_t T, D, H, E, k;

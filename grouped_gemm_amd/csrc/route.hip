@@ -369,6 +369,24 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
 
 }  // namespace
 
+bool route_counts_separately(const RouteBuffers& b) {
+    return !(b.P <= kWaveMaxPairs && b.E <= kWaveMaxExperts) && !(b.P <= kSmallMaxPairs && b.E <= kSmallMaxExperts);
+}
+
+// Steps 2..4 of the multi-kernel route, from the segment histogram.
+hipError_t launch_route_after_count(const RouteBuffers& b, hipStream_t st) {
+    const size_t lds = sizeof(int32_t) * static_cast<size_t>(b.E);
+    int nbits = 0;
+    while ((1 << nbits) <= b.E) ++nbits;  // enough bits for ids 0..E (E = sentinel)
+    route_scan_kernel<<<b.E, 256, 0, st>>>(b.seg_counts, b.S, b.counts);
+    route_offsets_kernel<<<1, 1024, 0, st>>>(b.counts, b.E, b.offsets, b.tile_prefix);
+    if (b.S > 0) {
+        route_scatter_kernel<<<b.S, 64, lds, st>>>(b.ids, b.P, b.E, b.S, b.seg, nbits, b.seg_counts,
+                                                   b.offsets, b.sorted_to_pair, b.pair_to_sorted);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteBuffers& b, hipStream_t st) {
     if (b.P <= kWaveMaxPairs && b.E <= kWaveMaxExperts) {
         int nbits = 0;
@@ -385,19 +403,11 @@ hipError_t launch_route(const RouteBuffers& b, hipStream_t st) {
                                                  b.sorted_to_pair, b.pair_to_sorted);
         return hipGetLastError();
     }
-    const size_t lds = sizeof(int32_t) * static_cast<size_t>(b.E);
-    int nbits = 0;
-    while ((1 << nbits) <= b.E) ++nbits;  // enough bits for ids 0..E (E = sentinel)
     if (b.S > 0) {
+        const size_t lds = sizeof(int32_t) * static_cast<size_t>(b.E);
         route_count_kernel<<<b.S, 256, lds, st>>>(b.ids, b.P, b.E, b.S, b.seg, b.seg_counts);
     }
-    route_scan_kernel<<<b.E, 256, 0, st>>>(b.seg_counts, b.S, b.counts);
-    route_offsets_kernel<<<1, 1024, 0, st>>>(b.counts, b.E, b.offsets, b.tile_prefix);
-    if (b.S > 0) {
-        route_scatter_kernel<<<b.S, 64, lds, st>>>(b.ids, b.P, b.E, b.S, b.seg, nbits, b.seg_counts,
-                                                   b.offsets, b.sorted_to_pair, b.pair_to_sorted);
-    }
-    return hipGetLastError();
+    return launch_route_after_count(b, st);
 }
 
 }  // namespace moe

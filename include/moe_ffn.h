@@ -122,6 +122,38 @@ MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, 
                                        const float* topk_weights, void* out, int mode,
                                        void* stream, void* const* events, int n_events);
 
+/* The router ahead of the pass (Prime Flash MoE, section 1 "The
+ * computation": the pass starts from each token's top-k experts and their
+ * normalized routing weights): softmax over each token's E logits, the k
+ * most probable experts, most probable first with ties to the lower expert
+ * id, and their probabilities renormalized to sum to 1. Softmax is strictly
+ * increasing, so the order is that of the fp32 logits themselves and the
+ * ids are exact; weights are within a few fp32 ulps of
+ * exp(l_j - l_max) / sum over the picks of exp(l_i - l_max).
+ *   logits       : fp32 [T, E], 4-byte aligned. -inf ranks after every
+ *                  finite logit (a masked expert: picked only if fewer
+ *                  than k are finite, with weight 0); -0 equals +0; a NaN
+ *                  ranks below everything else (NaNs by id) and, if
+ *                  picked, makes the token's weights NaN. Each token needs
+ *                  at least one finite logit for finite weights.
+ *   topk_ids     : int32 [T, topk] (output).
+ *   topk_weights : fp32 [T, topk] (output).
+ * 1 <= topk <= min(E, 64), E <= 8192. T == 0 is a successful no-op. */
+MOE_FFN_API int moe_ffn_router(const float* logits, int32_t T, int32_t E, int32_t topk,
+                               int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* moe_ffn_forward_events starting from router logits: the router above
+ * writes topk_ids / topk_weights (outputs here, [T, topk] each, 16-byte
+ * aligned) and the route step reads them; on the multi-kernel route path
+ * the router kernel also builds the route's per-segment expert histogram,
+ * so the ids are read back only once. The same workspace as
+ * moe_ffn_forward. events[0..1] bracket router and route together;
+ * n_events is 0 or 5 as for moe_ffn_forward_events. */
+MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, const void* w1,
+                                       const void* w2, const float* logits, int32_t* topk_ids,
+                                       float* topk_weights, void* out, int mode, void* stream,
+                                       void* const* events, int n_events);
+
 /* Workspace bytes moe_ffn_route needs (host only; 0 on invalid input). */
 MOE_FFN_API size_t moe_ffn_route_workspace_bytes(int32_t T, int32_t topk, int32_t E);
 

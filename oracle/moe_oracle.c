@@ -169,8 +169,14 @@ void oracle_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* 
  * Softmax is strictly increasing in the logit, so "most probable" is
  * "largest logit": the order is taken on the fp32 logits themselves, which
  * fixes the ids exactly (two distinct logits never tie, whatever the
- * rounding of their probabilities). p is evaluated in double as
- * exp(l - max l) / sum, and each weight is rounded once to fp32. */
+ * rounding of their probabilities). The weights are the picks'
+ * probabilities divided by their sum; the softmax normalizer cancels in
+ * that ratio, so they are evaluated in double as exp(l_j - max l) over the
+ * sum of the picks' exp(l_i - max l), each rounded once to fp32.
+ * Inputs the definition leaves open: -0 and +0 are equal logits; a NaN
+ * logit ranks below every other logit (-inf included), NaNs among
+ * themselves by id, and a NaN among the picks makes the token's weights
+ * NaN. */
 typedef struct {
     float v;
     int32_t id;
@@ -179,6 +185,9 @@ typedef struct {
 static int oracle_scored_cmp(const void* a, const void* b) {
     const oracle_scored* x = (const oracle_scored*)a;
     const oracle_scored* y = (const oracle_scored*)b;
+    const int xn = isnan(x->v), yn = isnan(y->v);
+    if (xn != yn) return xn - yn;
+    if (xn) return (x->id > y->id) - (x->id < y->id);
     if (x->v > y->v) return -1;
     if (x->v < y->v) return 1;
     return (x->id > y->id) - (x->id < y->id);
@@ -192,16 +201,11 @@ void oracle_router(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
 #pragma omp for schedule(static)
         for (int64_t t = 0; t < T; ++t) {
             const float* l = logits + t * E;
-            float m = l[0];
-            for (int32_t e = 1; e < E; ++e)
+            float m = -INFINITY;
+            for (int32_t e = 0; e < E; ++e)
                 if (l[e] > m) m = l[e];
-            double z = 0.0;
             for (int32_t e = 0; e < E; ++e) {
                 p[e] = exp((double)l[e] - (double)m);
-                z += p[e];
-            }
-            for (int32_t e = 0; e < E; ++e) {
-                p[e] /= z;
                 s[e].v = l[e];
                 s[e].id = e;
             }

@@ -15,7 +15,7 @@ def test_library_exports_every_header_function():
         assert hasattr(lib, n), n
     assert set(names) == {
         "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_forward",
-        "moe_ffn_forward_events",
+        "moe_ffn_forward_events", "moe_ffn_router", "moe_ffn_forward_logits",
         "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_strerror"}
 
 
@@ -107,3 +107,33 @@ def test_forward_events_argument_checks():
         g.MOE_FFN_EINVAL_PTR
     assert lib.moe_ffn_forward_events(ctypes.byref(p), ok, ok, ok, ok, ok, ok, 2, None, None, 5) == \
         g.MOE_FFN_EINVAL_PTR
+
+
+@pytest.mark.parametrize("T,E,k,expect", [
+    (0, 8, 2, g.MOE_FFN_OK),                 # empty: a no-op before any pointer check
+    (-1, 8, 2, g.MOE_FFN_EINVAL_SHAPE),
+    (4, 0, 1, g.MOE_FFN_EINVAL_SHAPE),
+    (4, 8, 0, g.MOE_FFN_EINVAL_SHAPE),
+    (4, 8, 9, g.MOE_FFN_EINVAL_SHAPE),       # k > E
+    (4, 100, 65, g.MOE_FFN_EINVAL_SHAPE),    # k > 64
+    (4, 9000, 2, g.MOE_FFN_EINVAL_SHAPE),    # E > 8192
+    (4, 8, 2, g.MOE_FFN_EINVAL_PTR),         # null buffers
+])
+def test_router_argument_checks(T, E, k, expect):
+    """Host-side checks of moe_ffn_router: they return before any GPU call."""
+    assert g.library().moe_ffn_router(None, T, E, k, None, None, None) == expect
+
+
+def test_forward_logits_argument_checks():
+    lib = g.library()
+    p = g.make_problem(4, 256, 512, 8, 2)
+    # null logits with tokens to route
+    assert lib.moe_ffn_forward_logits(ctypes.byref(p), None, None, None, None, None, None, None, 0, None,
+                                      None, 0) == g.MOE_FFN_EINVAL_PTR
+    bad = g.make_problem(4, 200, 512, 8, 2)  # D not a multiple of 128
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_ffn_forward_logits(ctypes.byref(bad), None, None, None, fake, None, None, None, 0, None,
+                                      None, 0) == g.MOE_FFN_EINVAL_SHAPE
+    empty = g.make_problem(0, 256, 512, 8, 2)
+    assert lib.moe_ffn_forward_logits(ctypes.byref(empty), None, None, None, None, None, None, None, 0, None,
+                                      None, 0) == g.MOE_FFN_OK

@@ -50,6 +50,23 @@ def test_router_ties_go_to_the_lower_id():
     np.testing.assert_array_equal(ids, np.argsort(-many, axis=1, kind="stable")[:, :7])
 
 
+def test_router_special_values():
+    """-inf ranks after finite logits; NaN after everything (numpy's sort
+    agrees); -0 and +0 tie and go to the lower id."""
+    logits = np.array([[np.nan, 1.0, -np.inf, 0.0],
+                       [-0.0, 0.0, -1.0, np.nan],
+                       [0.0, -0.0, np.nan, np.nan]], np.float32)
+    ids, wts = oracle.router(logits, 4)
+    np.testing.assert_array_equal(ids, np.argsort(-logits, axis=1, kind="stable"))
+    np.testing.assert_array_equal(ids, [[1, 3, 2, 0], [0, 1, 2, 3], [0, 1, 2, 3]])
+    assert np.isnan(wts).all()                   # a NaN among the picks
+    ids, wts = oracle.router(logits, 3)
+    np.testing.assert_array_equal(ids[0], [1, 3, 2])
+    e = np.e
+    np.testing.assert_allclose(wts[0], [e / (e + 1), 1 / (e + 1), 0.0], rtol=1e-7)
+    np.testing.assert_allclose(wts[1], np.array([1, 1, np.exp(-1.0)]) / (2 + np.exp(-1.0)), rtol=1e-7)
+
+
 def test_router_closed_forms():
     rng = np.random.default_rng(11)
     logits = rng.normal(0.0, 3.0, size=(100, 16)).astype(np.float32)
