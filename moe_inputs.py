@@ -44,6 +44,7 @@ import os
 import numpy as np
 
 ROLE_ROUTING, ROLE_X, ROLE_W1, ROLE_W2 = 0, 1, 2, 3
+ROLE_WS1, ROLE_WS2 = 5, 6  # shared expert
 
 
 @dataclasses.dataclass(frozen=True)
@@ -176,6 +177,14 @@ def routing(cfg: Config, seed: int = 0):
     w = w / w.sum(axis=1, keepdims=True)
     return (np.ascontiguousarray(ids.astype(np.int32)),
             np.ascontiguousarray(w.astype(np.float32)))
+
+
+def shared_expert(cfg: Config, Hs: int, seed: int = 0):
+    """One shared expert's weights as bf16 bits: ws1 [2Hs, D] ~ N(0, 1/D) (gate
+    rows, then up rows) and ws2 [D, Hs] ~ N(0, 1/Hs), from streams of their own."""
+    ws1 = _normal(cfg, ROLE_WS1, seed * 1000003 + Hs, (2 * Hs, cfg.D), 1.0 / np.sqrt(cfg.D), True)
+    ws2 = _normal(cfg, ROLE_WS2, seed * 1000003 + Hs, (cfg.D, Hs), 1.0 / np.sqrt(Hs), True)
+    return ws1, ws2
 
 
 def router_logits(cfg: Config, seed: int = 0) -> np.ndarray:

@@ -46,6 +46,8 @@ def _load():
         lib.oracle_route.argtypes = [P, i64, i32, i32, P, P, P, P]
         lib.oracle_router.argtypes = [P, i64, i32, i32, P, P]
         lib.oracle_forward_bf16.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i64]
+        lib.oracle_forward_bf16_shared.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P, P,
+                                                   i64]
         lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                           P, i64, i32]
         lib.oracle_mx_quantize.argtypes = [P, i64, i64, P, P]
@@ -113,11 +115,13 @@ def router(logits: np.ndarray, k: int):
     return ids, wts
 
 
-def forward_bf16(x, w1, w2, topk_ids, topk_weights, tokens=None):
+def forward_bf16(x, w1, w2, topk_ids, topk_weights, tokens=None, shared=None):
     """bf16 forward: out bf16 bits [T, D] (rows not in `tokens` stay 0).
 
     x [T, D], w1 [E, 2H, D], w2 [E, D, H] as uint16 bf16 bits; ids int32
     [T, k]; weights fp32 [T, k]. Prime Flash MoE, section 1.
+    shared = (ws1 [2Hs, D], ws2 [D, Hs]) adds one shared expert on every
+    token with weight 1 ("GC-MoE on SM120", section 4.7).
     """
     x, w1, w2 = _c(x, np.uint16), _c(w1, np.uint16), _c(w2, np.uint16)
     ids, wts = _c(topk_ids, np.int32), _c(topk_weights, np.float32)
@@ -132,8 +136,15 @@ def forward_bf16(x, w1, w2, topk_ids, topk_weights, tokens=None):
     else:
         tok = _c(tokens, np.int64)
         tok_p, n = _p(tok), tok.size
-    _load().oracle_forward_bf16(T, D, H, E, k, _p(x), _p(w1), _p(w2), _p(ids), _p(wts), _p(out),
-                                tok_p, n)
+    if shared is None:
+        _load().oracle_forward_bf16(T, D, H, E, k, _p(x), _p(w1), _p(w2), _p(ids), _p(wts), _p(out),
+                                    tok_p, n)
+    else:
+        ws1, ws2 = _c(shared[0], np.uint16), _c(shared[1], np.uint16)
+        Hs = ws1.shape[0] // 2
+        assert ws1.shape == (2 * Hs, D) and ws2.shape == (D, Hs)
+        _load().oracle_forward_bf16_shared(T, D, H, E, k, _p(x), _p(w1), _p(w2), _p(ids), _p(wts), _p(ws1),
+                                           _p(ws2), Hs, _p(out), tok_p, n)
     return out
 
 

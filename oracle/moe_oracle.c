@@ -226,17 +226,42 @@ void oracle_router(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
 
 static float silu(float z) { return z / (1.0f + expf(-z)); }
 
+/* One expert on one token, accumulated into acc: gate|up = W1 x (W1
+ * [2H, D], gate rows first), act = silu(gate) * up, acc += w * (W2 act)
+ * (W2 [D, H]). gu holds 2H floats, act H. */
+static void expert_ffn(const float* xv, const uint16_t* W1, const uint16_t* W2, int32_t D, int32_t H, float w,
+                       float* gu, float* act, float* acc) {
+    for (int32_t n = 0; n < 2 * H; ++n) {
+        float s = 0.0f;
+        for (int32_t d = 0; d < D; ++d) s += oracle_bf16_to_f32(W1[(int64_t)n * D + d]) * xv[d];
+        gu[n] = s;
+    }
+    for (int32_t h = 0; h < H; ++h) act[h] = silu(gu[h]) * gu[H + h];
+    for (int32_t d = 0; d < D; ++d) {
+        float s = 0.0f;
+        for (int32_t h = 0; h < H; ++h) s += oracle_bf16_to_f32(W2[(int64_t)d * H + h]) * act[h];
+        acc[d] += w * s;
+    }
+}
+
 /* bf16 forward for the tokens listed in `tokens` (n_tok of them; NULL means
- * all T tokens in order). out rows are written at the token's own row. */
-void oracle_forward_bf16(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint16_t* x,
-                         const uint16_t* w1, const uint16_t* w2, const int32_t* ids,
-                         const float* wts, uint16_t* out, const int64_t* tokens, int64_t n_tok) {
+ * all T tokens in order). out rows are written at the token's own row.
+ * With ws1 != NULL, one shared expert (ws1 [2Hs, D], ws2 [D, Hs]) runs on
+ * every token and its output joins the token's sum with weight 1 after the
+ * k routed slots ("GC-MoE on SM120", section 4.7: a shared expert is
+ * applied to every token, and its output is added into the same fp32 sum
+ * that folds the k routed slots). */
+void oracle_forward_bf16_shared(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint16_t* x,
+                                const uint16_t* w1, const uint16_t* w2, const int32_t* ids, const float* wts,
+                                const uint16_t* ws1, const uint16_t* ws2, int32_t Hs, uint16_t* out,
+                                const int64_t* tokens, int64_t n_tok) {
     if (!tokens) n_tok = T;
+    const int32_t Hm = ws1 && Hs > H ? Hs : H;
 #pragma omp parallel
     {
         float* xv = (float*)malloc(sizeof(float) * (size_t)D);
-        float* gu = (float*)malloc(sizeof(float) * 2 * (size_t)H);
-        float* act = (float*)malloc(sizeof(float) * (size_t)H);
+        float* gu = (float*)malloc(sizeof(float) * 2 * (size_t)Hm);
+        float* act = (float*)malloc(sizeof(float) * (size_t)Hm);
         float* acc = (float*)malloc(sizeof(float) * (size_t)D);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t it = 0; it < n_tok; ++it) {
@@ -248,21 +273,10 @@ void oracle_forward_bf16(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, 
             for (int32_t j = 0; j < k; ++j) {
                 int32_t e = ids[t * k + j];
                 if (e < 0 || e >= E) continue;
-                const uint16_t* W1 = w1 + (int64_t)e * 2 * H * D;
-                const uint16_t* W2 = w2 + (int64_t)e * D * H;
-                for (int32_t n = 0; n < 2 * H; ++n) {
-                    float s = 0.0f;
-                    for (int32_t d = 0; d < D; ++d) s += oracle_bf16_to_f32(W1[(int64_t)n * D + d]) * xv[d];
-                    gu[n] = s;
-                }
-                for (int32_t h = 0; h < H; ++h) act[h] = silu(gu[h]) * gu[H + h];
-                float w = wts[t * k + j];
-                for (int32_t d = 0; d < D; ++d) {
-                    float s = 0.0f;
-                    for (int32_t h = 0; h < H; ++h) s += oracle_bf16_to_f32(W2[(int64_t)d * H + h]) * act[h];
-                    acc[d] += w * s;
-                }
+                expert_ffn(xv, w1 + (int64_t)e * 2 * H * D, w2 + (int64_t)e * D * H, D, H, wts[t * k + j], gu, act,
+                           acc);
             }
+            if (ws1) expert_ffn(xv, ws1, ws2, D, Hs, 1.0f, gu, act, acc);
             for (int32_t d = 0; d < D; ++d) out[t * D + d] = oracle_f32_to_bf16(acc[d]);
         }
         free(xv);
@@ -270,6 +284,12 @@ void oracle_forward_bf16(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, 
         free(act);
         free(acc);
     }
+}
+
+void oracle_forward_bf16(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint16_t* x,
+                         const uint16_t* w1, const uint16_t* w2, const int32_t* ids,
+                         const float* wts, uint16_t* out, const int64_t* tokens, int64_t n_tok) {
+    oracle_forward_bf16_shared(T, D, H, E, k, x, w1, w2, ids, wts, NULL, NULL, 0, out, tokens, n_tok);
 }
 
 /* MX-fp8 forward. x codes [T, D] + scales [T, D/32]; w1 codes [E, 2H, D] +
