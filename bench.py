@@ -60,6 +60,9 @@ def parse_args(argv=None):
                     help="override the workload's token count T (crossover sweeps)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--shared-ffn", type=int, default=0, metavar="HS",
+                    help="add one shared expert of intermediate size HS on every token "
+                         "(moe_ffn_forward_shared; bf16 only)")
     ap.add_argument("--logits", action="store_true",
                     help="start each step from router logits (moe_ffn_forward_logits): the router's "
                          "softmax/top-k runs inside the timed pass, fused with the route step")
@@ -160,7 +163,7 @@ def cpu_baseline(cfg, inputs, dtype, target_s):
         t0 = time.perf_counter()
         if dtype == "bf16":
             oracle.forward_bf16(inputs["x"], inputs["w1"], inputs["w2"], inputs["topk_ids"],
-                                inputs["topk_weights"], tokens=tok)
+                                inputs["topk_weights"], tokens=tok, shared=inputs.get("shared"))
         else:
             oracle.forward_mx(*inputs["xq"], *inputs["w1q"], *inputs["w2q"], inputs["topk_ids"],
                               inputs["topk_weights"], tokens=tok)
@@ -169,6 +172,8 @@ def cpu_baseline(cfg, inputs, dtype, target_s):
             break
         n = min(cfg.T, max(n * 2, int(n * target_s / max(dt, 1e-3) * 0.9)))
     flops = 6.0 * n * cfg.k * cfg.D * cfg.H
+    if inputs.get("shared") is not None:
+        flops += 6.0 * n * cfg.D * inputs["shared"][1].shape[1]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens ({n * cfg.k} routed pairs) of the same workload, "
                       f"{dt:.2f} s wall, fp32 accumulation",
@@ -216,6 +221,13 @@ def main(argv=None):
         del s
     ids = torch.from_numpy(host["topk_ids"]).to(dev)
     wts = torch.from_numpy(host["topk_weights"]).to(dev)
+    shared = None
+    if args.shared_ffn:
+        if args.logits or dtype != "bf16":
+            print("bench.py: --shared-ffn runs the bf16 pass from given routes only", file=sys.stderr)
+            return 2
+        host["shared"] = mi.shared_expert(cfg, args.shared_ffn, 0)
+        shared = tuple(torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16) for a in host["shared"])
     logits = None
     if args.logits:
         # the pass routes from these logits; ids / wts become its outputs
@@ -224,6 +236,10 @@ def main(argv=None):
     mode_id = g.moe_ffn_resolve_mode(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, args.mode)
     mode = {g.MOE_FFN_FUSED: "fused", g.MOE_FFN_SPLIT: "split"}[mode_id]
     nbytes = g.moe_ffn_workspace_bytes(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, mode)
+    if args.shared_ffn:
+        import ctypes as _ct
+        pr = g.make_problem(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype)
+        nbytes = g.library().moe_ffn_shared_workspace_bytes(_ct.byref(pr), args.shared_ffn, mode_id)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=dev)
 
@@ -241,7 +257,10 @@ def main(argv=None):
         events.append(row)
 
     def step(ev=None):
-        if logits is not None:
+        if shared is not None:
+            g.moe_ffn_forward_shared(x, w1, w2, ids, wts, shared[0], shared[1], out=out, mode=mode, workspace=ws,
+                                     events=ev)
+        elif logits is not None:
             g.moe_ffn_forward_logits(x, w1, w2, logits, cfg.k, out=out, mode=mode, workspace=ws, topk_ids=ids,
                                      topk_weights=wts, events=ev, **scales)
         else:
@@ -261,6 +280,8 @@ def main(argv=None):
     names = list(STAGES[mode])
     if logits is not None:
         names[0] = "router_route"
+    if shared is not None:
+        names[0] = "shared_expert_route"
     stage_ms = {n: 0.0 for n in names}
     f = ctypes.c_float()
     for row in events:
@@ -290,6 +311,8 @@ def main(argv=None):
     workload = f"{cfg.name} {dtype} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k}"
     if logits is not None:
         workload += " from router logits"
+    if shared is not None:
+        workload += f" + shared expert Hs={args.shared_ffn}"
     traffic = measured_traffic(dom, kernel_symbol(cfg, mode, dom), workload)
     if intensity > ridge:
         roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
@@ -303,7 +326,8 @@ def main(argv=None):
     roof["algorithmic_flops"] = dflops
     roof["avg_launch_ms"] = stage_ms[dom]
 
-    tflops = cfg.flops / (ms * 1e-3) / 1e12
+    flops = cfg.flops + (6.0 * cfg.T * cfg.D * args.shared_ffn if shared is not None else 0.0)
+    tflops = flops / (ms * 1e-3) / 1e12
     all_bytes = hit * 3 * cfg.H * cfg.D * (1 if dtype == "mxfp8" else 2) + 2 * cfg.T * cfg.D * 2
     result = {
         "metric": METRIC,

@@ -74,6 +74,11 @@ def library() -> ctypes.CDLL:
         lib.moe_ffn_forward_logits.argtypes = [PP, VP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP,
                                                ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         lib.moe_ffn_forward_logits.restype = ctypes.c_int
+        lib.moe_ffn_shared_workspace_bytes.argtypes = [PP, I32, ctypes.c_int]
+        lib.moe_ffn_shared_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_ffn_forward_shared.argtypes = [PP, VP, VP, VP, VP, VP, VP, VP, I32, VP, ctypes.c_int, VP,
+                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        lib.moe_ffn_forward_shared.restype = ctypes.c_int
         lib.moe_ffn_route_workspace_bytes.argtypes = [I32, I32, I32]
         lib.moe_ffn_route_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_ffn_route.argtypes = [VP, I32, I32, I32, VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
@@ -241,6 +246,41 @@ def moe_ffn_forward_logits(x, w1, w2, logits, k, out=None, mode="auto", x_scale=
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward_logits")
     return out, topk_ids, topk_weights
+
+
+def moe_ffn_forward_shared(x, w1, w2, topk_ids, topk_weights, shared_w1, shared_w2, out=None, mode="auto",
+                           workspace=None, stream=None, events=None):
+    """out [T, D] bf16 = the routed pass plus one shared expert on every token
+    (shared_w1 [2Hs, D], shared_w2 [D, Hs] bf16), added with weight 1."""
+    if topk_ids.dtype != torch.int32:
+        topk_ids = topk_ids.to(torch.int32)
+    T, D = x.shape
+    E, H2, _ = w1.shape
+    k = topk_ids.shape[1]
+    Hs = shared_w1.shape[0] // 2
+    if tuple(shared_w1.shape) != (2 * Hs, D) or tuple(shared_w2.shape) != (D, Hs):
+        raise ValueError("shared_w1 must be [2Hs, D] and shared_w2 [D, Hs]")
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, shared_w1, shared_w2, out)
+    p = make_problem(T, D, H2 // 2, E, k, "bf16")
+    lib = library()
+    m = _mode(mode)
+    if workspace is None:
+        nbytes = lib.moe_ffn_shared_workspace_bytes(ctypes.byref(p), Hs, m)
+        if nbytes == 0:
+            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m) or MOE_FFN_EINVAL_SHAPE,
+                              "moe_ffn_forward_shared")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel()
+    ev, n = (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
+    rc = lib.moe_ffn_forward_shared(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                    topk_ids.data_ptr(), topk_weights.data_ptr(), shared_w1.data_ptr(),
+                                    shared_w2.data_ptr(), Hs, out.data_ptr(), m, _stream(stream), ev, n)
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_forward_shared")
+    return out
 
 
 def moe_ffn_route(topk_ids, E, stream=None):

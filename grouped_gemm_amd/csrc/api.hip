@@ -211,33 +211,77 @@ MOE_FFN_API int moe_ffn_forward(const moe_ffn_problem* p, const void* x, const v
 }
 
 namespace {
+struct SharedExpert {
+    const void* w1;  // bf16 [2Hs, D]
+    const void* w2;  // bf16 [D, Hs]
+    int32_t Hs;
+};
 int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2, const float* logits,
-                 const int32_t* topk_ids, const float* topk_weights, void* out, int mode, void* stream,
-                 void* const* events, int n_events);
+                 const int32_t* topk_ids, const float* topk_weights, const SharedExpert* sh, void* out, int mode,
+                 void* stream, void* const* events, int n_events);
+
+// The shared expert as its own split pass of one expert with k = 1.
+moe_ffn_problem shared_problem(const moe_ffn_problem* p, int32_t Hs) {
+    moe_ffn_problem q = *p;
+    q.H = Hs;
+    q.E = 1;
+    q.topk = 1;
+    q.dtype = MOE_FFN_BF16;
+    q.x_scale = q.w1_scale = q.w2_scale = nullptr;
+    return q;
+}
+// Workspace after the routed pass's plan: the shared pass's plan, then the
+// unit weights of its identity routing.
+size_t shared_bytes(const moe_ffn_problem* p, int32_t Hs) {
+    const moe_ffn_problem q = shared_problem(p, Hs);
+    return make_plan(&q, MOE_FFN_SPLIT).total + align_up(sizeof(float) * static_cast<size_t>(p->T));
+}
+int check_shared(const moe_ffn_problem* p, int32_t Hs) {
+    if (p->dtype != MOE_FFN_BF16) return MOE_FFN_EUNSUPPORTED;  // an MX shared expert is not built
+    if (Hs < 1 || Hs % 128) return MOE_FFN_EINVAL_SHAPE;
+    return MOE_FFN_OK;
+}
 }  // namespace
 
 MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, const void* w1,
                                        const void* w2, const int32_t* topk_ids, const float* topk_weights,
                                        void* out, int mode, void* stream, void* const* events, int n_events) {
-    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, out, mode, stream, events, n_events);
+    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, nullptr, out, mode, stream, events,
+                        n_events);
+}
+
+MOE_FFN_API size_t moe_ffn_shared_workspace_bytes(const moe_ffn_problem* p, int32_t Hs, int mode) {
+    if (check_shape(p) != MOE_FFN_OK || check_shared(p, Hs) != MOE_FFN_OK) return 0;
+    const int m = resolve(p, mode);
+    if (m < 0) return 0;
+    return make_plan(p, m).total + shared_bytes(p, Hs);
+}
+
+MOE_FFN_API int moe_ffn_forward_shared(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
+                                       const int32_t* topk_ids, const float* topk_weights, const void* shared_w1,
+                                       const void* shared_w2, int32_t Hs, void* out, int mode, void* stream,
+                                       void* const* events, int n_events) {
+    const SharedExpert sh{shared_w1, shared_w2, Hs};
+    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, &sh, out, mode, stream, events, n_events);
 }
 
 MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
                                        const float* logits, int32_t* topk_ids, float* topk_weights, void* out,
                                        int mode, void* stream, void* const* events, int n_events) {
     if (p && p->T > 0 && (!logits || (reinterpret_cast<uintptr_t>(logits) & 3u))) return MOE_FFN_EINVAL_PTR;
-    return forward_impl(p, x, w1, w2, p && p->T > 0 ? logits : nullptr, topk_ids, topk_weights, out, mode, stream,
-                        events, n_events);
+    return forward_impl(p, x, w1, w2, p && p->T > 0 ? logits : nullptr, topk_ids, topk_weights, nullptr, out, mode,
+                        stream, events, n_events);
 }
 
 }  // extern "C"
 
 namespace {
 // The pass from given routes (logits == NULL) or from router logits, which
-// then fill topk_ids / topk_weights on the way.
+// then fill topk_ids / topk_weights on the way; with `sh`, a shared expert
+// runs first and its output joins the combine.
 int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2, const float* logits,
-                 const int32_t* topk_ids, const float* topk_weights, void* out, int mode, void* stream,
-                 void* const* events, int n_events) {
+                 const int32_t* topk_ids, const float* topk_weights, const SharedExpert* sh, void* out, int mode,
+                 void* stream, void* const* events, int n_events) {
     if (n_events != 0 && n_events != 5) return MOE_FFN_EINVAL_PTR;
     if (n_events == 5 && !events) return MOE_FFN_EINVAL_PTR;
     hipEvent_t ev[5];
@@ -251,12 +295,14 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
     }
     int rc = check_shape(p);
     if (rc != MOE_FFN_OK) return rc;
+    if (sh && (rc = check_shared(p, sh->Hs)) != MOE_FFN_OK) return rc;
     const int m = resolve(p, mode);
     if (m < 0) return m;
     if (p->T == 0) return MOE_FFN_OK;
     const void* ptrs[] = {x, w1, w2, topk_ids, topk_weights, out};
     for (const void* q : ptrs)
         if (!q || !aligned16(q)) return MOE_FFN_EINVAL_PTR;
+    if (sh && (!sh->w1 || !sh->w2 || !aligned16(sh->w1) || !aligned16(sh->w2))) return MOE_FFN_EINVAL_PTR;
     if (p->dtype == MOE_FFN_MXFP8) {
         const void* sp[] = {p->x_scale, p->w1_scale, p->w2_scale};
         for (const void* q : sp)
@@ -264,15 +310,42 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
     }
     const Plan pl = make_plan(p, m);
     void* ws = p->workspace;
-    if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) || p->workspace_bytes < pl.total)
+    const size_t need = pl.total + (sh ? shared_bytes(p, sh->Hs) : 0);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) || p->workspace_bytes < need)
         return MOE_FFN_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t P = static_cast<int64_t>(p->T) * p->topk;
 
+    moe::record(evp, 0, st);
+    const uint16_t* shared_y = nullptr;
+    if (sh) {
+        // the shared expert: one group of all T tokens through the split GEMMs
+        const moe_ffn_problem q = shared_problem(p, sh->Hs);
+        const Plan sp = make_plan(&q, MOE_FFN_SPLIT);
+        void* sws = static_cast<char*>(ws) + pl.total;
+        float* ones = at<float>(sws, sp.total);
+        int32_t* tp = at<int32_t>(sws, sp.route.tile_prefix);
+        if (moe::launch_identity_route(p->T, at<int32_t>(sws, sp.counts), at<int32_t>(sws, sp.offsets), tp,
+                                       at<int32_t>(sws, sp.s2p), at<int32_t>(sws, sp.p2s), ones, st) != hipSuccess)
+            return MOE_FFN_EHIP;
+        moe::Bf16Args b{};
+        b.T = p->T; b.D = p->D; b.H = sh->Hs; b.E = 1; b.k = 1; b.P = p->T;
+        b.x = static_cast<const uint16_t*>(x);
+        b.w1 = static_cast<const uint16_t*>(sh->w1);
+        b.w2 = static_cast<const uint16_t*>(sh->w2);
+        b.wts = ones;
+        b.rv = moe::RouteView{at<int32_t>(sws, sp.counts), at<int32_t>(sws, sp.offsets), tp, at<int32_t>(sws, sp.s2p),
+                              at<int32_t>(sws, sp.p2s)};
+        b.act = at<uint16_t>(sws, sp.act);
+        b.ypair = at<uint16_t>(sws, sp.ypair);
+        b.mtiles = at<int32_t>(sws, sp.mtiles);
+        if (moe::launch_gemms_bf16(b, st, nullptr) != hipSuccess) return MOE_FFN_EHIP;
+        shared_y = b.ypair;  // [T, D]: pair t of the identity routing is token t
+    }
+
     moe::RouteBuffers rb{topk_ids, P, p->E, pl.route.S, pl.route.seg, at<int32_t>(ws, pl.route.seg_counts),
                          at<int32_t>(ws, pl.counts), at<int32_t>(ws, pl.offsets),
                          at<int32_t>(ws, pl.route.tile_prefix), at<int32_t>(ws, pl.s2p), at<int32_t>(ws, pl.p2s)};
-    moe::record(evp, 0, st);
     const hipError_t re = logits ? moe::launch_router_route(logits, p->T, p->E, p->topk, const_cast<int32_t*>(topk_ids),
                                                             const_cast<float*>(topk_weights), rb, st)
                                  : moe::launch_route(rb, st);
@@ -291,6 +364,7 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
         a.wts = topk_weights;
         a.rv = rv;
         a.out = static_cast<uint16_t*>(out);
+        a.shared_y = shared_y;
         if (m == MOE_FFN_SPLIT) {
             a.act = at<uint16_t>(ws, pl.act);
             a.ypair = at<uint16_t>(ws, pl.ypair);

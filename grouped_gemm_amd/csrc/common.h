@@ -123,10 +123,19 @@ struct Bf16Args {
     int32_t* mtiles;   // split only: big_gemm_workspace_bytes for the prefill GEMMs
     float* acc32;      // [T, D]   fused only
     uint16_t* out;     // [T, D]
+    const uint16_t* shared_y;  // [T, D] or null: a shared expert's output, added to each token's sum
 };
 // `ev` (nullable) points at 3 events recorded after each of the launcher's
 // three kernels.
 hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
+// The split pipeline's two grouped GEMMs alone (ypair filled, no combine);
+// `ev` (nullable) gets 2 events, after each GEMM.
+hipError_t launch_gemms_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
+// Route maps of T tokens each with one slot on expert 0 (the shared
+// expert as a grouped GEMM of one group): counts, offsets, tile prefix
+// sums, the identity maps, and `ones` [T] = 1.0f as the routing weights.
+hipError_t launch_identity_route(int64_t T, int32_t* counts, int32_t* offsets, int32_t* tile_prefix,
+                                 int32_t* sorted_to_pair, int32_t* pair_to_sorted, float* ones, hipStream_t s);
 // Decode-shaped GEMM1 / GEMM2 (weights streamed on the MFMA's wide side).
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s);
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);

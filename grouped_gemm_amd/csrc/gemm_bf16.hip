@@ -355,13 +355,15 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(Bf16Args a) {
 
 // ---------------- combine / conversions ----------------
 
-// out[t, :] = bf16( sum over valid slots j of ypair[t*k + j, :] ), 8 columns per thread.
-// Every ypair byte is read once and every out byte written once: both go
-// through nontemporal accesses (streamed past the caches), launched with
+// out[t, :] = bf16( sum over valid slots j of ypair[t*k + j, :] [+ shared_y[t, :]] ),
+// 8 columns per thread; the shared expert's row (if any) joins the fp32 sum
+// last. Every ypair byte is read once and every out byte written once: both
+// go through nontemporal accesses (streamed past the caches), launched with
 // one item per thread for all but huge T.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ ypair,
                                                       const int32_t* __restrict__ p2s, int32_t T,
-                                                      int32_t k, int32_t D, uint16_t* __restrict__ out) {
+                                                      int32_t k, int32_t D, const uint16_t* __restrict__ shared_y,
+                                                      uint16_t* __restrict__ out) {
     const int cpr = D / 8;
     const int64_t n = static_cast<int64_t>(T) * cpr;
     for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
@@ -386,6 +388,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                     s[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(v[j][q] >> 16));
                 }
         }
+        if (shared_y) {
+            const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(shared_y + t * D + c * 8));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s[2 * q] += bf16_to_f32(static_cast<uint16_t>(v[q] & 0xffffu));
+                s[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(v[q] >> 16));
+            }
+        }
         u32x4_t o;
         o.x = pack_bf16x2(s[0], s[1]);
         o.y = pack_bf16x2(s[2], s[3]);
@@ -400,10 +410,42 @@ __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float4* p, int64_t n
         p[i] = float4{0.f, 0.f, 0.f, 0.f};
 }
 
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* src, uint2* dst, int64_t n4) {
+// dst = bf16(src [+ extra]), 4 values per thread; extra (nullable) is bf16.
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* src, const uint2* extra, uint2* dst,
+                                                          int64_t n4) {
     for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
-        const float4 v = src[i];
+        float4 v = src[i];
+        if (extra) {
+            const uint2 e = extra[i];
+            v.x += bf16_to_f32(static_cast<uint16_t>(e.x & 0xffffu));
+            v.y += bf16_to_f32(static_cast<uint16_t>(e.x >> 16));
+            v.z += bf16_to_f32(static_cast<uint16_t>(e.y & 0xffffu));
+            v.w += bf16_to_f32(static_cast<uint16_t>(e.y >> 16));
+        }
         dst[i] = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    }
+}
+
+// Route maps of the identity routing (T tokens, one slot each, expert 0).
+__global__ __launch_bounds__(256) void identity_route_kernel(int64_t T, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tile_prefix,
+                                                             int32_t* __restrict__ s2p, int32_t* __restrict__ p2s,
+                                                             float* __restrict__ ones) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < T; i += static_cast<int64_t>(gridDim.x) * 256) {
+        s2p[i] = static_cast<int32_t>(i);
+        p2s[i] = static_cast<int32_t>(i);
+        ones[i] = 1.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        counts[0] = static_cast<int32_t>(T);
+        offsets[0] = 0;
+        offsets[1] = static_cast<int32_t>(T);
+        for (int b = 0; b < kNumTileHeights; ++b) {  // [kNumTileHeights][E + 1] with E = 1
+            const int64_t bm = 16 << b;
+            tile_prefix[b * 2] = 0;
+            tile_prefix[b * 2 + 1] = static_cast<int32_t>((T + bm - 1) / bm);
+        }
     }
 }
 
@@ -420,9 +462,14 @@ inline int mtiles_upper(int64_t P, int E, int bm) {
 
 }  // namespace
 
-hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
+hipError_t launch_gemms_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BN1 = 128, BN2 = 128;
-    const bool skinny = a.P <= kSkinnyMaxRowsPerExpert * a.E;
+    // The skinny kernels stream the weights once per 32-row m-tile. A single
+    // group (one expert: a shared expert, a dense FFN) with few rows would
+    // give the prefill ring fewer tiles than half the CUs, so it streams too.
+    const int64_t ring_tiles = (a.P / 128 + a.E) * (a.H / 128);
+    const bool skinny =
+        a.P <= kSkinnyMaxRowsPerExpert * a.E || (a.E == 1 && ring_tiles < device_cu_count() / 2);
     const bool big = !skinny && big_gemm_supported(a);
     if (skinny) {
         launch_skinny_gemm1(a, s);
@@ -442,9 +489,22 @@ hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
         gemm2_weight_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
     }
     record(ev, 1, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
+    const hipError_t e = launch_gemms_bf16(a, s, ev);
+    if (e != hipSuccess) return e;
     combine_kernel<<<grid_for(static_cast<int64_t>(a.T) * a.D / 8, 256, kCombineMaxBlocks), 256, 0, s>>>(
-        a.ypair, a.rv.pair_to_sorted, a.T, a.k, a.D, a.out);
+        a.ypair, a.rv.pair_to_sorted, a.T, a.k, a.D, a.shared_y, a.out);
     record(ev, 2, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_identity_route(int64_t T, int32_t* counts, int32_t* offsets, int32_t* tile_prefix,
+                                 int32_t* sorted_to_pair, int32_t* pair_to_sorted, float* ones, hipStream_t s) {
+    identity_route_kernel<<<grid_for(T, 256), 256, 0, s>>>(T, counts, offsets, tile_prefix, sorted_to_pair,
+                                                          pair_to_sorted, ones);
     return hipGetLastError();
 }
 
@@ -457,6 +517,7 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     fused_bf16_kernel<BM, BH><<<g, kThreads, 0, s>>>(a);
     record(ev, 1, s);
     f32_to_bf16_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(a.acc32),
+                                                             reinterpret_cast<const uint2*>(a.shared_y),
                                                              reinterpret_cast<uint2*>(a.out), n / 4);
     record(ev, 2, s);
     return hipGetLastError();
@@ -464,8 +525,8 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
 
 hipError_t launch_combine(const uint16_t* ypair, const int32_t* p2s, int32_t T, int32_t k, int32_t D,
                           uint16_t* out, hipStream_t s) {
-    combine_kernel<<<grid_for(static_cast<int64_t>(T) * D / 8, 256, kCombineMaxBlocks), 256, 0, s>>>(ypair, p2s, T,
-                                                                                                     k, D, out);
+    combine_kernel<<<grid_for(static_cast<int64_t>(T) * D / 8, 256, kCombineMaxBlocks), 256, 0, s>>>(
+        ypair, p2s, T, k, D, nullptr, out);
     return hipGetLastError();
 }
 
@@ -475,7 +536,7 @@ hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
-    f32_to_bf16_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(src),
+    f32_to_bf16_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(src), nullptr,
                                                             reinterpret_cast<uint2*>(dst), n / 4);
     return hipGetLastError();
 }

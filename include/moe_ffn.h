@@ -154,6 +154,26 @@ MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, 
                                        float* topk_weights, void* out, int mode, void* stream,
                                        void* const* events, int n_events);
 
+/* One shared expert next to the routed ones ("GC-MoE on SM120", section
+ * 4.7: a shared expert runs on every token, and its output is added into
+ * the same fp32 sum that folds the token's k routed slots):
+ *     out[t] = sum_j w[t,j] * y(t, ids[t,j]) + W2s (silu(W1s_gate x_t) * W1s_up x_t)
+ *   shared_w1 : bf16 [2Hs, D] (gate rows, then up rows), 16-byte aligned.
+ *   shared_w2 : bf16 [D, Hs].
+ *   Hs        : the shared expert's intermediate size, a multiple of 128.
+ * The shared expert runs first, as a grouped GEMM of one group of all T
+ * tokens; the combine (split) or the accumulator conversion (fused) adds
+ * its rows. bf16 only (MXFP8 returns MOE_FFN_EUNSUPPORTED). The workspace
+ * must hold moe_ffn_shared_workspace_bytes(); events as for
+ * moe_ffn_forward_events, with events[0..1] bracketing the shared expert
+ * and the route step together. */
+MOE_FFN_API size_t moe_ffn_shared_workspace_bytes(const moe_ffn_problem* p, int32_t Hs, int mode);
+MOE_FFN_API int moe_ffn_forward_shared(const moe_ffn_problem* p, const void* x, const void* w1,
+                                       const void* w2, const int32_t* topk_ids,
+                                       const float* topk_weights, const void* shared_w1,
+                                       const void* shared_w2, int32_t Hs, void* out, int mode,
+                                       void* stream, void* const* events, int n_events);
+
 /* Workspace bytes moe_ffn_route needs (host only; 0 on invalid input). */
 MOE_FFN_API size_t moe_ffn_route_workspace_bytes(int32_t T, int32_t topk, int32_t E);
 

@@ -16,6 +16,7 @@ def test_library_exports_every_header_function():
     assert set(names) == {
         "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_forward",
         "moe_ffn_forward_events", "moe_ffn_router", "moe_ffn_forward_logits",
+        "moe_ffn_shared_workspace_bytes", "moe_ffn_forward_shared",
         "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_strerror"}
 
 
@@ -137,3 +138,18 @@ def test_forward_logits_argument_checks():
     empty = g.make_problem(0, 256, 512, 8, 2)
     assert lib.moe_ffn_forward_logits(ctypes.byref(empty), None, None, None, None, None, None, None, 0, None,
                                       None, 0) == g.MOE_FFN_OK
+
+
+def test_shared_expert_host_checks():
+    lib = g.library()
+    p = g.make_problem(64, 256, 512, 8, 2)
+    base = lib.moe_ffn_workspace_bytes(ctypes.byref(p), g.MOE_FFN_SPLIT)
+    with_shared = lib.moe_ffn_shared_workspace_bytes(ctypes.byref(p), 384, g.MOE_FFN_SPLIT)
+    assert with_shared > base > 0
+    assert lib.moe_ffn_shared_workspace_bytes(ctypes.byref(p), 100, g.MOE_FFN_SPLIT) == 0   # Hs % 128
+    mx = g.make_problem(64, 256, 512, 8, 2, "mxfp8")
+    assert lib.moe_ffn_shared_workspace_bytes(ctypes.byref(mx), 256, g.MOE_FFN_SPLIT) == 0
+    assert lib.moe_ffn_forward_shared(ctypes.byref(mx), None, None, None, None, None, None, None, 256, None, 0,
+                                      None, None, 0) == g.MOE_FFN_EUNSUPPORTED
+    assert lib.moe_ffn_forward_shared(ctypes.byref(p), None, None, None, None, None, None, None, 200, None, 0,
+                                      None, None, 0) == g.MOE_FFN_EINVAL_SHAPE
