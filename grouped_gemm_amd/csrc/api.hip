@@ -39,10 +39,7 @@ constexpr int64_t kFusedMaxWeightBytes = int64_t(16) << 20;
 
 int resolve(const moe_ffn_problem* p, int mode) {
     if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
-    if (p->dtype == MOE_FFN_MXFP8) {
-        if (mode == MOE_FFN_FUSED) return MOE_FFN_EUNSUPPORTED;  // MX fused is not built
-        return MOE_FFN_SPLIT;
-    }
+    if (p->dtype == MOE_FFN_MXFP8) return mode == MOE_FFN_FUSED ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
     if (mode != MOE_FFN_AUTO) return mode;
     const int64_t weight_bytes = int64_t(p->E) * 3 * p->H * p->D * 2;
     const bool small = static_cast<int64_t>(p->T) * p->topk <= kFusedMaxPairs && weight_bytes <= kFusedMaxWeightBytes;
@@ -385,12 +382,17 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
         a.w2s = static_cast<const uint8_t*>(p->w2_scale);
         a.wts = topk_weights;
         a.rv = rv;
-        a.act = at<uint8_t>(ws, pl.act);
-        a.act_s = at<uint8_t>(ws, pl.act_s);
-        a.ypair = at<uint16_t>(ws, pl.ypair);
         a.out = static_cast<uint16_t*>(out);
-        a.mtiles = at<int32_t>(ws, pl.mtiles);
-        e = moe::launch_split_mx(a, st, stage_ev);
+        if (m == MOE_FFN_SPLIT) {
+            a.act = at<uint8_t>(ws, pl.act);
+            a.act_s = at<uint8_t>(ws, pl.act_s);
+            a.ypair = at<uint16_t>(ws, pl.ypair);
+            a.mtiles = at<int32_t>(ws, pl.mtiles);
+            e = moe::launch_split_mx(a, st, stage_ev);
+        } else {
+            a.acc32 = at<float>(ws, pl.acc32);
+            e = moe::launch_fused_mx(a, st, stage_ev);
+        }
     }
     return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
 }

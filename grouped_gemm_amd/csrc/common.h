@@ -168,8 +168,13 @@ struct MxArgs {
     uint16_t* ypair;    // [P, D]
     uint16_t* out;      // [T, D]
     int32_t* mtiles;    // big_gemm_workspace_bytes for the prefill GEMMs
+    float* acc32;       // [T, D] fused only
 };
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
+// Fused MX pipeline: GEMM1, SwiGLU and the act requantization in LDS, then a
+// split-K down projection over each 64-wide H slice into acc32 (fp32
+// atomics), then the conversion to bf16; `ev` (nullable) gets 3 events.
+hipError_t launch_fused_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
 // Prefill-shaped MX GEMM1 / GEMM2 (the bf16 prefill kernels' ring on the scaled MFMA).
 bool big_mx_supported(const MxArgs& a);
 hipError_t launch_big_mx(const MxArgs& a, bool gemm1, hipStream_t s);

@@ -295,9 +295,209 @@ __global__ __launch_bounds__(kThreads) void mx_gemm2_kernel(MxArgs a) {
     }
 }
 
+// ---------------- fused MX: GEMM1 -> SwiGLU -> requant in LDS -> split-K GEMM2 ----------------
+// One workgroup per (m-tile of BM rows, 64-wide H slice): the GEMM1 tile
+// (64 gate + 64 up rows), SwiGLU in fp32, the act requantized per 32 along H
+// by MXQ into LDS (two scale blocks per row: exactly one K step of the
+// scaled MFMA), then the down projection over that slice for 128 output
+// features at a time, w * partial added into acc32 with fp32 atomics
+// ("Prime Flash MoE", section 7: the fused MX path quantizes act in the
+// epilogue and runs the down projection split over H).
+constexpr int kFusedSlice = 64;        // act columns per workgroup (one scaled-MFMA K step)
+constexpr int kFusedRowBytes = 64;     // act / W2 slice row in LDS: 64 codes, four 16-byte chunks
+
+// 64-byte rows, 16-byte chunk c of row r at (c ^ ((r >> 2) & 3)): the 16 rows
+// a fragment read touches fall in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * kFusedRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// 32 codes of one row for the scaled MFMA: chunks g and g + 2 of the row
+// (k = 16g..16g+15 and 32+16g..32+16g+15), g = lane >> 5.
+__device__ __forceinline__ i32x8_t frag64(const uint8_t* base, int row, int g) {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + swz64(row, g));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + swz64(row, g + 2));
+    return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int BM>
+__global__ __launch_bounds__(kThreads) void mx_fused_kernel(MxArgs a) {
+    constexpr int BN = 2 * kFusedSlice;
+    using C = MxTile<BM, BN>;
+    constexpr int OS = kFusedSlice + 4;  // fp32 act staging row
+    static_assert(BM * OS * 4 <= 2 * C::STAGE, "act staging must fit the stage buffers");
+    static_assert(2 * 128 * kFusedRowBytes <= 2 * C::STAGE, "W2 slices must fit the stage buffers");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t sAct[BM * kFusedRowBytes];
+    __shared__ uint8_t sActS[BM][2];
+    __shared__ uint8_t sW2S[2][128][2];
+    __shared__ int32_t sTok[BM];
+    __shared__ float sW[BM];
+    MTile mt;
+    if (!find_mtile<BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int g = lane >> 5;
+    const int h0 = blockIdx.y * kFusedSlice;
+    const int DB = a.D / 32, HB = a.H / 32;
+    for (int r = tid; r < BM; r += kThreads) {
+        const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P);
+        sTok[r] = p / a.k;
+        sW[r] = r < mt.rows ? a.wts[p] : 0.0f;
+    }
+    __syncthreads();
+
+    // GEMM1 tile: gate rows h0.. and up rows H + h0.. of W1[e]
+    const int c16 = tid & 7, r16 = tid >> 3;
+    {
+        constexpr int BH = kFusedSlice;
+        const uint8_t* aptr[C::A_CH];
+        const uint8_t* bptr[C::B_CH];
+#pragma unroll
+        for (int q = 0; q < C::A_CH; ++q) aptr[q] = a.x + static_cast<int64_t>(sTok[r16 + 32 * q]) * a.D + c16 * 16;
+        const int64_t w1row0 = static_cast<int64_t>(mt.expert) * 2 * a.H;
+        auto w1row = [&](int r) { return w1row0 + (r < BH ? h0 + r : a.H + h0 + (r - BH)); };
+#pragma unroll
+        for (int q = 0; q < C::B_CH; ++q) bptr[q] = a.w1 + w1row(r16 + 32 * q) * a.D + c16 * 16;
+        int brow[C::NB];
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj)
+            brow[nj] = nj < C::NB / 2 ? wn * (BH / 2) + 32 * nj : BH + wn * (BH / 2) + 32 * (nj - C::NB / 2);
+        const uint8_t* asp[C::MB];
+        const uint8_t* bsp[C::NB];
+#pragma unroll
+        for (int mi = 0; mi < C::MB; ++mi)
+            asp[mi] = a.xs + static_cast<int64_t>(sTok[wm * C::WM + 32 * mi + (lane & 31)]) * DB;
+#pragma unroll
+        for (int nj = 0; nj < C::NB; ++nj) bsp[nj] = a.w1s + w1row(brow[nj] + (lane & 31)) * DB;
+        f32x16_t acc[C::MB][C::NB];
+#pragma unroll
+        for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < C::NB; ++nj) acc[mi][nj] = f32x16_t{};
+        mx_mainloop<BM, BN>(lds, aptr, bptr, asp, bsp, a.D / BKB, brow, acc);
+
+        // SwiGLU in fp32 into the (now idle) stage buffers
+        float* sO = reinterpret_cast<float*>(lds);
+#pragma unroll
+        for (int mi = 0; mi < C::MB; ++mi)
+#pragma unroll
+            for (int j = 0; j < C::NB / 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = wm * C::WM + 32 * mi + acc_row(lane, v);
+                    const int col = wn * (BH / 2) + 32 * j + (lane & 31);
+                    const float gt = acc[mi][j][v], up = acc[mi][j + C::NB / 2][v];
+                    sO[m * OS + col] = gt / (1.0f + __expf(-gt)) * up;
+                }
+    }
+    __syncthreads();
+    // MXQ per 32 act columns: 8 lanes per block, 4 values each -> codes and
+    // scale bytes in LDS (the down projection's A operand)
+    {
+        const float* sO = reinterpret_cast<const float*>(lds);
+        const int sub = tid & 7;
+        for (int item = tid >> 3; item < BM * 2; item += kThreads / 8) {
+            const int r = item >> 1, blk = item & 1;
+            const float4 v = *reinterpret_cast<const float4*>(sO + r * OS + blk * 32 + sub * 4);
+            float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+            amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+            const int sc = mx_scale_exp(amax);
+            const float inv = pow2f(-sc);
+            const uint32_t c = e4m3_encode(v.x * inv, v.x) | (e4m3_encode(v.y * inv, v.y) << 8) |
+                               (e4m3_encode(v.z * inv, v.z) << 16) | (e4m3_encode(v.w * inv, v.w) << 24);
+            // byte 32*blk + 4*sub of the row: chunk 2*blk + sub/4, offset 4*(sub&3)
+            *reinterpret_cast<uint32_t*>(sAct + swz64(r, 2 * blk + (sub >> 2)) + 4 * (sub & 3)) = c;
+            if (sub == 0) sActS[r][blk] = static_cast<uint8_t>(sc + 127);
+        }
+    }
+    __syncthreads();
+
+    // Down projection over this slice, 128 output features per step; W2
+    // slices (128 rows x 64 codes + 2 scale bytes per row) double-buffered
+    // in the stage buffers through registers.
+    const uint8_t* w2e = a.w2 + static_cast<int64_t>(mt.expert) * a.D * a.H + h0;
+    const uint8_t* w2se = a.w2s + static_cast<int64_t>(mt.expert) * a.D * HB + h0 / 32;
+    const int NT = a.D / 128;
+    const int wr = tid >> 2, wc = tid & 3;  // W2 load: rows wr, wr + 64; chunk wc
+    u32x4_t rb[2];
+    uint16_t rs = 0;
+    auto gload = [&](int nt) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            rb[q] = *reinterpret_cast<const u32x4_t*>(w2e + static_cast<int64_t>(nt * 128 + wr + 64 * q) * a.H + wc * 16);
+        if (tid < 128) rs = *reinterpret_cast<const uint16_t*>(w2se + static_cast<int64_t>(nt * 128 + tid) * HB);
+    };
+    auto sstore = [&](int buf) {
+        uint8_t* sB = lds + buf * 128 * kFusedRowBytes;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4_t*>(sB + swz64(wr + 64 * q, wc)) = rb[q];
+        if (tid < 128) {
+            sW2S[buf][tid][0] = static_cast<uint8_t>(rs & 0xffu);
+            sW2S[buf][tid][1] = static_cast<uint8_t>(rs >> 8);
+        }
+    };
+    // this wave's act fragments and scales, fixed for every step
+    constexpr int MB2 = BM / 2 / 32;
+    i32x8_t af[MB2];
+    int as[MB2];
+#pragma unroll
+    for (int mi = 0; mi < MB2; ++mi) {
+        const int r = wm * (BM / 2) + 32 * mi + (lane & 31);
+        af[mi] = frag64(sAct, r, g);
+        as[mi] = sActS[r][g];
+    }
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int nt = 0; nt < NT; ++nt) {
+        if (nt + 1 < NT) gload(nt + 1);
+        const uint8_t* sB = lds + (nt & 1) * 128 * kFusedRowBytes;
+        f32x16_t acc2[MB2][2];
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj) {
+            const int col = wn * 64 + 32 * nj + (lane & 31);
+            const i32x8_t bf = frag64(sB, col, g);
+            const int bs = sW2S[nt & 1][col][g];
+#pragma unroll
+            for (int mi = 0; mi < MB2; ++mi)
+                acc2[mi][nj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf, f32x16_t{}, 0, 0, 0, as[mi],
+                                                                              0, bs);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MB2; ++mi)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = wm * (BM / 2) + 32 * mi + acc_row(lane, v);
+                if (m < mt.rows) {
+                    float* dst = a.acc32 + static_cast<int64_t>(sTok[m]) * a.D + nt * 128 + wn * 64 + (lane & 31);
+#pragma unroll
+                    for (int nj = 0; nj < 2; ++nj) unsafeAtomicAdd(dst + 32 * nj, sW[m] * acc2[mi][nj][v]);
+                }
+            }
+        if (nt + 1 < NT) sstore((nt + 1) & 1);
+        __syncthreads();
+    }
+}
+
 inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
 
 }  // namespace
+
+hipError_t launch_fused_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev) {
+    constexpr int BM = 128;
+    const int64_t n = static_cast<int64_t>(a.T) * a.D;
+    hipError_t e = launch_fill_zero_f32(a.acc32, n, s);
+    if (e != hipSuccess) return e;
+    record(ev, 0, s);
+    dim3 g(mtiles_upper(a.P, a.E, BM), a.H / kFusedSlice);
+    mx_fused_kernel<BM><<<g, kThreads, 0, s>>>(a);
+    record(ev, 1, s);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_f32_to_bf16(a.acc32, a.out, n, s);
+    record(ev, 2, s);
+    return e;
+}
 
 hipError_t launch_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                               hipStream_t s) {

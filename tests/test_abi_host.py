@@ -39,7 +39,8 @@ def test_validate_shapes(shape, expect):
 def test_validate_dtype_and_mode():
     assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype=7) == g.MOE_FFN_EUNSUPPORTED
     assert g.moe_ffn_validate(64, 256, 512, 8, 2, mode=5) == g.MOE_FFN_EUNSUPPORTED
-    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == g.MOE_FFN_EUNSUPPORTED
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == g.MOE_FFN_OK
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, dtype="mxfp8", mode="auto") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp8", mode="split") == g.MOE_FFN_OK
     lib = g.library()
     assert lib.moe_ffn_validate(None, 0) == g.MOE_FFN_EINVAL_PTR

@@ -52,13 +52,13 @@ def _mx_inputs(cfg, seed=0):
     return src, q
 
 
-def _case(cfg, tokens=None, seed=0):
+def _case(cfg, tokens=None, seed=0, mode="split"):
     import grouped_gemm_amd as g
-    print(f"mx forward {cfg.name} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k}", flush=True)
+    print(f"mx forward {cfg.name} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k} mode={mode}", flush=True)
     src, q = _mx_inputs(cfg, seed)
     (xc, xs), (w1c, w1s), (w2c, w2s) = q["x"], q["w1"], q["w2"]
     out = g.moe_ffn_forward(to_gpu(xc), to_gpu(w1c), to_gpu(w2c), to_gpu(src["topk_ids"]),
-                            to_gpu(src["topk_weights"]), mode="split", x_scale=to_gpu(xs),
+                            to_gpu(src["topk_weights"]), mode=mode, x_scale=to_gpu(xs),
                             w1_scale=to_gpu(w1s), w2_scale=to_gpu(w2s))
     torch.cuda.synchronize()
     out = gpu_bf16_to_f64(out)
@@ -103,3 +103,22 @@ def test_mx_config_sampled():
     cfg = mi.CONFIGS[5]
     ids, _ = mi.routing(cfg)
     _case(cfg, tokens=sample_tokens(cfg, ids, 24))
+
+
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (64, 256, 256, 8, 2, "softmax"),    # the tiny workload's size class
+    (300, 384, 640, 16, 4, "zipf"),     # ragged m-tiles, skew, H slices of 64 over 640
+    (1, 128, 128, 4, 2, "uniform"),     # a single token
+    (513, 128, 256, 3, 3, "uniform"),   # k = E
+    (700, 512, 384, 5, 3, "zipf"),
+])
+def test_mx_forward_fused(T, D, H, E, k, routing):
+    """The fused MX pipeline: the act requantized in LDS feeds a split-K down
+    projection per 64-wide H slice (two scale blocks: one scaled-MFMA K step)."""
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"), mode="fused")
+
+
+def test_mx_fused_config_sampled():
+    cfg = mi.CONFIGS[5]
+    ids, _ = mi.routing(cfg)
+    _case(cfg, tokens=sample_tokens(cfg, ids, 24), mode="fused")
