@@ -13,9 +13,13 @@ expert-parallel deployment, bound by streaming the expert weights from HBM.
 
 Per-kernel durations come from HIP events that the library records on the
 pass's own stream at its stage boundaries (moe_ffn_forward_events) during
-the timed steps; the dominant kernel's roofline fraction uses its
-algorithmic bytes (weights of the experts hit + activations in and out) or
-flops (6*P*D*H split 4:2 over the two GEMMs) per launch.
+the timed steps: every --event-every-th timed step (default 8, starting with
+the first) carries the five events and the others run bare, because each
+event record adds a gap to the stream (about 14 us per step on the decode
+pass when every step carries them). The dominant kernel's roofline fraction
+uses its algorithmic bytes (weights of the experts hit + activations in and
+out) or flops (6*P*D*H split 4:2 over the two GEMMs) per launch, over the
+instrumented steps.
 
 The CPU baseline is the oracle (oracle/, plain C, OpenMP) timed on a bounded
 sample of the same workload on the host's cores.
@@ -60,6 +64,8 @@ def parse_args(argv=None):
                     help="override the workload's token count T (crossover sweeps)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--event-every", type=int, default=8, metavar="N",
+                    help="record the stage events on every N-th timed step (1 = all)")
     ap.add_argument("--shared-ffn", type=int, default=0, metavar="HS",
                     help="add one shared expert of intermediate size HS on every token "
                          "(moe_ffn_forward_shared; bf16 only)")
@@ -182,6 +188,7 @@ def cpu_baseline(cfg, inputs, dtype, target_s):
 
 def main(argv=None):
     args = parse_args(argv)
+    args.event_every = max(1, args.event_every)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU expert-parallel layout is a design note, not built)", file=sys.stderr)
@@ -272,7 +279,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events[i] if i % args.event_every == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
@@ -284,10 +291,11 @@ def main(argv=None):
         names[0] = "shared_expert_route"
     stage_ms = {n: 0.0 for n in names}
     f = ctypes.c_float()
-    for row in events:
+    timed = [events[i] for i in range(args.steps) if i % args.event_every == 0]
+    for row in timed:
         for j, n in enumerate(names):
             assert hip.hipEventElapsedTime(ctypes.byref(f), row[j], row[j + 1]) == 0
-            stage_ms[n] += f.value / args.steps
+            stage_ms[n] += f.value / len(timed)
     for row in events:
         for e in row:
             hip.hipEventDestroy(e)
@@ -350,6 +358,7 @@ def main(argv=None):
         "pct_mfma_peak": tflops / peak_tf,
         "effective_hbm_gbs": all_bytes / (ms * 1e-3) / 1e9,
         "stage_ms": stage_ms,
+        "stage_events_every": args.event_every,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
