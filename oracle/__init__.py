@@ -46,6 +46,8 @@ def _load():
         lib.oracle_route.argtypes = [P, i64, i32, i32, P, P, P, P]
         lib.oracle_router.argtypes = [P, i64, i32, i32, P, P]
         lib.oracle_forward_bf16.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i64]
+        lib.oracle_forward_bf16_act.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, i32, ctypes.c_float, P,
+                                                i32, P, P, i64]
         lib.oracle_forward_bf16_shared.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P, P,
                                                    i64]
         lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
@@ -145,6 +147,32 @@ def forward_bf16(x, w1, w2, topk_ids, topk_weights, tokens=None, shared=None):
         assert ws1.shape == (2 * Hs, D) and ws2.shape == (D, Hs)
         _load().oracle_forward_bf16_shared(T, D, H, E, k, _p(x), _p(w1), _p(w2), _p(ids), _p(wts), _p(ws1),
                                            _p(ws2), Hs, _p(out), tok_p, n)
+    return out
+
+
+def forward_bf16_act(x, w1, w2, topk_ids, topk_weights, kind=0, limit=0.0, alpha=None,
+                     weight_before_act=False, tokens=None):
+    """bf16 forward with the activation variant: kind 0 = SwiGLU, 1 = SwiGLU on
+    gate clamped from above and up clamped on both sides at `limit`; gate
+    and up scaled first by alpha[e] (per expert, fp32) and, with
+    weight_before_act, by the routing weight, which then does not scale the
+    expert output ("Porting Block-Scaled GEMM Kernels from Blackwell to
+    Rubin", section 5.3; "GC-MoE on SM120", section 4.8)."""
+    x, w1, w2 = _c(x, np.uint16), _c(w1, np.uint16), _c(w2, np.uint16)
+    ids, wts = _c(topk_ids, np.int32), _c(topk_weights, np.float32)
+    T, D = x.shape
+    E, H2, _ = w1.shape
+    H = H2 // 2
+    k = ids.shape[1]
+    out = np.zeros((T, D), np.uint16)
+    al = None if alpha is None else _c(alpha, np.float32)
+    if tokens is None:
+        tok_p, n = None, T
+    else:
+        tok = _c(tokens, np.int64)
+        tok_p, n = _p(tok), tok.size
+    _load().oracle_forward_bf16_act(T, D, H, E, k, _p(x), _p(w1), _p(w2), _p(ids), _p(wts), int(kind), float(limit),
+                                    None if al is None else _p(al), 1 if weight_before_act else 0, _p(out), tok_p, n)
     return out
 
 

@@ -244,6 +244,75 @@ static void expert_ffn(const float* xv, const uint16_t* W1, const uint16_t* W2, 
     }
 }
 
+/* The activation variant ("Porting Block-Scaled GEMM Kernels from Blackwell
+ * to Rubin", section 5.3, and "GC-MoE on SM120", sections 4.8 and 5.4):
+ * gate and up are first scaled by the expert's global scale alpha[e] (1
+ * when alpha is NULL) and, with weight_before_act, by the pair's routing
+ * weight, which then no longer scales the expert's output. kind 0 is the
+ * plain SwiGLU; kind 1 clamps in the gpt-oss style, the gate from above
+ * only and up on both sides, at `limit`, and computes up * silu(gate):
+ *   s   = alpha[e] * (weight_before_act ? w : 1)
+ *   g'  = s * g,  u' = s * u
+ *   act = silu(min(g', limit)) * max(min(u', limit), -limit)   (kind 1)
+ *   acc += (weight_before_act ? 1 : w) * (W2 act). */
+static void expert_ffn_act(const float* xv, const uint16_t* W1, const uint16_t* W2, int32_t D, int32_t H, float w,
+                           int32_t kind, float limit, float alpha_e, int32_t wba, float* gu, float* act,
+                           float* acc) {
+    for (int32_t n = 0; n < 2 * H; ++n) {
+        float s = 0.0f;
+        for (int32_t d = 0; d < D; ++d) s += oracle_bf16_to_f32(W1[(int64_t)n * D + d]) * xv[d];
+        gu[n] = s;
+    }
+    const float s_in = wba ? alpha_e * w : alpha_e;
+    const float s_out = wba ? 1.0f : w;
+    for (int32_t h = 0; h < H; ++h) {
+        float g = s_in * gu[h], u = s_in * gu[H + h];
+        if (kind == 1) {
+            g = fminf(g, limit);
+            u = fmaxf(fminf(u, limit), -limit);
+        }
+        act[h] = silu(g) * u;
+    }
+    for (int32_t d = 0; d < D; ++d) {
+        float s = 0.0f;
+        for (int32_t h = 0; h < H; ++h) s += oracle_bf16_to_f32(W2[(int64_t)d * H + h]) * act[h];
+        acc[d] += s_out * s;
+    }
+}
+
+void oracle_forward_bf16_act(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint16_t* x,
+                             const uint16_t* w1, const uint16_t* w2, const int32_t* ids, const float* wts,
+                             int32_t kind, float limit, const float* alpha, int32_t wba, uint16_t* out,
+                             const int64_t* tokens, int64_t n_tok) {
+    if (!tokens) n_tok = T;
+#pragma omp parallel
+    {
+        float* xv = (float*)malloc(sizeof(float) * (size_t)D);
+        float* gu = (float*)malloc(sizeof(float) * 2 * (size_t)H);
+        float* act = (float*)malloc(sizeof(float) * (size_t)H);
+        float* acc = (float*)malloc(sizeof(float) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < n_tok; ++it) {
+            int64_t t = tokens ? tokens[it] : it;
+            for (int32_t d = 0; d < D; ++d) {
+                xv[d] = oracle_bf16_to_f32(x[t * D + d]);
+                acc[d] = 0.0f;
+            }
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = ids[t * k + j];
+                if (e < 0 || e >= E) continue;
+                expert_ffn_act(xv, w1 + (int64_t)e * 2 * H * D, w2 + (int64_t)e * D * H, D, H, wts[t * k + j], kind,
+                               limit, alpha ? alpha[e] : 1.0f, wba, gu, act, acc);
+            }
+            for (int32_t d = 0; d < D; ++d) out[t * D + d] = oracle_f32_to_bf16(acc[d]);
+        }
+        free(xv);
+        free(gu);
+        free(act);
+        free(acc);
+    }
+}
+
 /* bf16 forward for the tokens listed in `tokens` (n_tok of them; NULL means
  * all T tokens in order). out rows are written at the token's own row.
  * With ws1 != NULL, one shared expert (ws1 [2Hs, D], ws2 [D, Hs]) runs on
