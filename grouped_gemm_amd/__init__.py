@@ -26,6 +26,7 @@ MOE_FFN_AUTO, MOE_FFN_FUSED, MOE_FFN_SPLIT = 0, 1, 2
 MOE_FFN_OK = 0
 MOE_FFN_EINVAL_SHAPE, MOE_FFN_EINVAL_PTR, MOE_FFN_EUNSUPPORTED = -1, -2, -3
 MOE_FFN_EWORKSPACE, MOE_FFN_EHIP = -4, -5
+MOE_FFN_ACT_SWIGLU, MOE_FFN_ACT_CLAMPED_SWIGLU = 0, 1
 
 _MODES = {"auto": MOE_FFN_AUTO, "fused": MOE_FFN_FUSED, "split": MOE_FFN_SPLIT}
 _DTYPES = {"bf16": MOE_FFN_BF16, "mxfp8": MOE_FFN_MXFP8}
@@ -45,6 +46,12 @@ class moe_ffn_problem(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+
+class moe_ffn_activation(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("limit", ctypes.c_float), ("alpha", ctypes.c_void_p),
+                ("weight_before_act", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -58,35 +65,32 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         VP, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         PP = ctypes.POINTER(moe_ffn_problem)
-        lib.moe_ffn_workspace_bytes.argtypes = [PP, ctypes.c_int]
-        lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
-        lib.moe_ffn_validate.argtypes = [PP, ctypes.c_int]
-        lib.moe_ffn_validate.restype = ctypes.c_int
-        lib.moe_ffn_resolve_mode.argtypes = [PP, ctypes.c_int]
-        lib.moe_ffn_resolve_mode.restype = ctypes.c_int
-        lib.moe_ffn_forward.argtypes = [PP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP]
-        lib.moe_ffn_forward.restype = ctypes.c_int
-        lib.moe_ffn_forward_events.argtypes = [PP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP,
-                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
-        lib.moe_ffn_forward_events.restype = ctypes.c_int
-        lib.moe_ffn_router.argtypes = [VP, I32, I32, I32, VP, VP, VP]
-        lib.moe_ffn_router.restype = ctypes.c_int
-        lib.moe_ffn_forward_logits.argtypes = [PP, VP, VP, VP, VP, VP, VP, VP, ctypes.c_int, VP,
-                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
-        lib.moe_ffn_forward_logits.restype = ctypes.c_int
-        lib.moe_ffn_shared_workspace_bytes.argtypes = [PP, I32, ctypes.c_int]
-        lib.moe_ffn_shared_workspace_bytes.restype = ctypes.c_size_t
-        lib.moe_ffn_forward_shared.argtypes = [PP, VP, VP, VP, VP, VP, VP, VP, I32, VP, ctypes.c_int, VP,
-                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
-        lib.moe_ffn_forward_shared.restype = ctypes.c_int
-        lib.moe_ffn_route_workspace_bytes.argtypes = [I32, I32, I32]
-        lib.moe_ffn_route_workspace_bytes.restype = ctypes.c_size_t
-        lib.moe_ffn_route.argtypes = [VP, I32, I32, I32, VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
-        lib.moe_ffn_route.restype = ctypes.c_int
-        lib.moe_ffn_mx_quantize.argtypes = [VP, I64, I32, VP, VP, VP]
-        lib.moe_ffn_mx_quantize.restype = ctypes.c_int
-        lib.moe_ffn_strerror.argtypes = [ctypes.c_int]
-        lib.moe_ffn_strerror.restype = ctypes.c_char_p
+        EV = ctypes.POINTER(ctypes.c_void_p)
+        INT, SZ = ctypes.c_int, ctypes.c_size_t
+        signatures = {
+            "moe_ffn_workspace_bytes": ([PP, INT], SZ),
+            "moe_ffn_validate": ([PP, INT], INT),
+            "moe_ffn_resolve_mode": ([PP, INT], INT),
+            "moe_ffn_forward": ([PP, VP, VP, VP, VP, VP, VP, INT, VP], INT),
+            "moe_ffn_forward_events": ([PP, VP, VP, VP, VP, VP, VP, INT, VP, EV, INT], INT),
+            "moe_ffn_router": ([VP, I32, I32, I32, VP, VP, VP], INT),
+            "moe_ffn_forward_logits": ([PP, VP, VP, VP, VP, VP, VP, VP, INT, VP, EV, INT], INT),
+            "moe_ffn_shared_workspace_bytes": ([PP, I32, INT], SZ),
+            "moe_ffn_forward_shared": ([PP, VP, VP, VP, VP, VP, VP, VP, I32, VP, INT, VP, EV, INT], INT),
+            "moe_ffn_forward_act": ([PP, VP, VP, VP, VP, VP, ctypes.POINTER(moe_ffn_activation), VP, INT, VP, EV,
+                                     INT], INT),
+            "moe_ffn_route_workspace_bytes": ([I32, I32, I32], SZ),
+            "moe_ffn_route": ([VP, I32, I32, I32, VP, VP, VP, VP, VP, SZ, VP], INT),
+            "moe_ffn_mx_quantize": ([VP, I64, I32, VP, VP, VP], INT),
+            "moe_ffn_strerror": ([INT], ctypes.c_char_p),
+        }
+        for name, (args, res) in signatures.items():
+            # a MOE_FFN_LIB build of an older source may lack newer entry points
+            # (calling one then raises); the in-tree library must have them all
+            if os.environ.get("MOE_FFN_LIB") and not hasattr(lib, name):
+                continue
+            fn = getattr(lib, name)
+            fn.argtypes, fn.restype = args, res
         _lib = lib
     return _lib
 
@@ -280,6 +284,42 @@ def moe_ffn_forward_shared(x, w1, w2, topk_ids, topk_weights, shared_w1, shared_
                                     shared_w2.data_ptr(), Hs, out.data_ptr(), m, _stream(stream), ev, n)
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward_shared")
+    return out
+
+
+def moe_ffn_forward_act(x, w1, w2, topk_ids, topk_weights, kind="clamped_swiglu", limit=0.0, alpha=None,
+                        weight_before_act=False, out=None, mode="split", workspace=None, stream=None, events=None):
+    """out [T, D] bf16 = the pass with the activation variant (moe_ffn_forward_act):
+    gate/up scaled by alpha [E] fp32 (or 1) and, with weight_before_act, by the
+    routing weight; kind "clamped_swiglu" clamps gate from above and up on both
+    sides at `limit`."""
+    if topk_ids.dtype != torch.int32:
+        topk_ids = topk_ids.to(torch.int32)
+    T, D = x.shape
+    E, H2, _ = w1.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, alpha)
+    kinds = {"swiglu": MOE_FFN_ACT_SWIGLU, "clamped_swiglu": MOE_FFN_ACT_CLAMPED_SWIGLU}
+    act = moe_ffn_activation(kinds.get(kind, kind) if isinstance(kind, str) else kind, float(limit),
+                             alpha.data_ptr() if alpha is not None else None, 1 if weight_before_act else 0)
+    p = make_problem(T, D, H2 // 2, E, k, "bf16")
+    lib = library()
+    m = _mode(mode)
+    if workspace is None:
+        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), MOE_FFN_SPLIT)
+        if nbytes == 0:
+            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m), "moe_ffn_forward_act")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel()
+    ev, n = (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
+    rc = lib.moe_ffn_forward_act(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(), topk_ids.data_ptr(),
+                                 topk_weights.data_ptr(), ctypes.byref(act), out.data_ptr(), m, _stream(stream), ev,
+                                 n)
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_forward_act")
     return out
 
 

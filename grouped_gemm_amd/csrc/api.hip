@@ -214,8 +214,19 @@ struct SharedExpert {
     int32_t Hs;
 };
 int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2, const float* logits,
-                 const int32_t* topk_ids, const float* topk_weights, const SharedExpert* sh, void* out, int mode,
-                 void* stream, void* const* events, int n_events);
+                 const int32_t* topk_ids, const float* topk_weights, const SharedExpert* sh,
+                 const moe_ffn_activation* act, void* out, int mode, void* stream, void* const* events, int n_events);
+
+// The activation variant's own checks (bf16, the split pipeline).
+int check_act(const moe_ffn_problem* p, const moe_ffn_activation* act, int mode) {
+    if (act->kind != MOE_FFN_ACT_SWIGLU && act->kind != MOE_FFN_ACT_CLAMPED_SWIGLU) return MOE_FFN_EUNSUPPORTED;
+    if (act->kind == MOE_FFN_ACT_CLAMPED_SWIGLU && !(act->limit > 0.0f && act->limit <= 3.0e38f))
+        return MOE_FFN_EINVAL_SHAPE;
+    if (act->weight_before_act != 0 && act->weight_before_act != 1) return MOE_FFN_EINVAL_SHAPE;
+    if (act->alpha && (reinterpret_cast<uintptr_t>(act->alpha) & 3u)) return MOE_FFN_EINVAL_PTR;
+    if (p->dtype != MOE_FFN_BF16 || mode == MOE_FFN_FUSED) return MOE_FFN_EUNSUPPORTED;
+    return MOE_FFN_OK;
+}
 
 // The shared expert as its own split pass of one expert with k = 1.
 moe_ffn_problem shared_problem(const moe_ffn_problem* p, int32_t Hs) {
@@ -243,7 +254,15 @@ int check_shared(const moe_ffn_problem* p, int32_t Hs) {
 MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, const void* w1,
                                        const void* w2, const int32_t* topk_ids, const float* topk_weights,
                                        void* out, int mode, void* stream, void* const* events, int n_events) {
-    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, nullptr, out, mode, stream, events,
+    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, nullptr, nullptr, out, mode, stream, events,
+                        n_events);
+}
+
+MOE_FFN_API int moe_ffn_forward_act(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
+                                    const int32_t* topk_ids, const float* topk_weights, const moe_ffn_activation* act,
+                                    void* out, int mode, void* stream, void* const* events, int n_events) {
+    if (!act) return MOE_FFN_EINVAL_PTR;
+    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, nullptr, act, out, mode, stream, events,
                         n_events);
 }
 
@@ -259,15 +278,16 @@ MOE_FFN_API int moe_ffn_forward_shared(const moe_ffn_problem* p, const void* x, 
                                        const void* shared_w2, int32_t Hs, void* out, int mode, void* stream,
                                        void* const* events, int n_events) {
     const SharedExpert sh{shared_w1, shared_w2, Hs};
-    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, &sh, out, mode, stream, events, n_events);
+    return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, &sh, nullptr, out, mode, stream, events,
+                        n_events);
 }
 
 MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
                                        const float* logits, int32_t* topk_ids, float* topk_weights, void* out,
                                        int mode, void* stream, void* const* events, int n_events) {
     if (p && p->T > 0 && (!logits || (reinterpret_cast<uintptr_t>(logits) & 3u))) return MOE_FFN_EINVAL_PTR;
-    return forward_impl(p, x, w1, w2, p && p->T > 0 ? logits : nullptr, topk_ids, topk_weights, nullptr, out, mode,
-                        stream, events, n_events);
+    return forward_impl(p, x, w1, w2, p && p->T > 0 ? logits : nullptr, topk_ids, topk_weights, nullptr, nullptr,
+                        out, mode, stream, events, n_events);
 }
 
 }  // extern "C"
@@ -277,8 +297,9 @@ namespace {
 // then fill topk_ids / topk_weights on the way; with `sh`, a shared expert
 // runs first and its output joins the combine.
 int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2, const float* logits,
-                 const int32_t* topk_ids, const float* topk_weights, const SharedExpert* sh, void* out, int mode,
-                 void* stream, void* const* events, int n_events) {
+                 const int32_t* topk_ids, const float* topk_weights, const SharedExpert* sh,
+                 const moe_ffn_activation* act, void* out, int mode, void* stream, void* const* events,
+                 int n_events) {
     if (n_events != 0 && n_events != 5) return MOE_FFN_EINVAL_PTR;
     if (n_events == 5 && !events) return MOE_FFN_EINVAL_PTR;
     hipEvent_t ev[5];
@@ -293,8 +314,10 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
     int rc = check_shape(p);
     if (rc != MOE_FFN_OK) return rc;
     if (sh && (rc = check_shared(p, sh->Hs)) != MOE_FFN_OK) return rc;
-    const int m = resolve(p, mode);
+    if (act && (rc = check_act(p, act, mode)) != MOE_FFN_OK) return rc;
+    int m = resolve(p, mode);
     if (m < 0) return m;
+    if (act) m = MOE_FFN_SPLIT;  // AUTO: the variant runs on the split pipeline
     if (p->T == 0) return MOE_FFN_OK;
     const void* ptrs[] = {x, w1, w2, topk_ids, topk_weights, out};
     for (const void* q : ptrs)
@@ -362,6 +385,7 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
         a.rv = rv;
         a.out = static_cast<uint16_t*>(out);
         a.shared_y = shared_y;
+        if (act) a.av = moe::ActVariant{act->kind, act->limit, act->alpha, act->weight_before_act};
         if (m == MOE_FFN_SPLIT) {
             a.act = at<uint16_t>(ws, pl.act);
             a.ypair = at<uint16_t>(ws, pl.ypair);

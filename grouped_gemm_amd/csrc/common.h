@@ -37,6 +37,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Activation variant of the GEMM1 epilogues ("Porting Block-Scaled GEMM
+// Kernels from Blackwell to Rubin", section 5.3; "GC-MoE on SM120", section
+// 4.8): gate and up scaled by the expert's global scale alpha[e] and, with
+// wba, by the pair's routing weight (which then does not scale y); kind 1
+// clamps the gate from above and up on both sides at `limit`. All zero is
+// the plain SwiGLU, which the kernels keep on their own code path.
+struct ActVariant {
+    int32_t kind;         // 0 SwiGLU, 1 clamped SwiGLU
+    float limit;
+    const float* alpha;   // [E] or null (1.0)
+    int32_t wba;          // routing weight before the activation
+    __host__ __device__ bool on() const { return kind != 0 || alpha != nullptr || wba != 0; }
+};
+
+// act of one (gate, up) pair under the variant; s = alpha[e] * (wba ? w : 1)
+__device__ __forceinline__ float act_variant(float g, float u, float s, int kind, float limit) {
+    g *= s;
+    u *= s;
+    if (kind == 1) {
+        g = fminf(g, limit);
+        u = fmaxf(fminf(u, limit), -limit);
+    }
+    return g / (1.0f + __expf(-g)) * u;
+}
+
 // Device view of the route step's outputs inside the workspace.
 struct RouteView {
     const int32_t* counts;        // [E]
@@ -124,6 +149,7 @@ struct Bf16Args {
     float* acc32;      // [T, D]   fused only
     uint16_t* out;     // [T, D]
     const uint16_t* shared_y;  // [T, D] or null: a shared expert's output, added to each token's sum
+    ActVariant av;             // zero: the plain SwiGLU
 };
 // `ev` (nullable) points at 3 events recorded after each of the launcher's
 // three kernels.

@@ -115,12 +115,20 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(Bf16Args a) {
     static_assert(C::NB % 2 == 0, "gate and up need the same number of blocks");
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::STAGE];
     __shared__ int32_t sTok[BM];
+    __shared__ float sScale[BM];  // activation variant: alpha[e] * (wba ? w : 1) per row
     MTile mt;
     if (!find_mtile<BM>(a.rv, a.E, blockIdx.x, mt)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const int BH = BN / 2, h0 = blockIdx.y * BH;
-    for (int r = tid; r < BM; r += kThreads)
-        sTok[r] = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P) / a.k;
+    const bool variant = a.av.on();
+    for (int r = tid; r < BM; r += kThreads) {
+        const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P);
+        sTok[r] = p / a.k;
+        if (variant) {
+            const float al = a.av.alpha ? a.av.alpha[mt.expert] : 1.0f;
+            sScale[r] = a.av.wba ? al * a.wts[p] : al;
+        }
+    }
     __syncthreads();
 
     const int c16 = tid & 7, r16 = tid >> 3;
@@ -159,7 +167,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(Bf16Args a) {
             for (int v = 0; v < 16; ++v) {
                 const int m = wm * C::WM + 32 * mi + acc_row(lane, v);
                 const int col = wn * (BH / 2) + 32 * j + (lane & 31);
-                sO[m * OS + col] = f32_to_bf16(silu_mul(acc[mi][j][v], acc[mi][j + C::NB / 2][v]));
+                const float g = acc[mi][j][v], u = acc[mi][j + C::NB / 2][v];
+                sO[m * OS + col] =
+                    f32_to_bf16(variant ? act_variant(g, u, sScale[m], a.av.kind, a.av.limit) : silu_mul(g, u));
             }
     __syncthreads();
     constexpr int CPR = BH / 8;
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weight_kernel(Bf16Args a) {
     for (int r = tid; r < BM; r += kThreads) {
         const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (r < mt.rows ? r : 0)], a.P);
         sPair[r] = p;
-        sW[r] = a.wts[p];
+        sW[r] = a.av.wba ? 1.0f : a.wts[p];  // with the weight applied before the activation, y is not scaled
     }
     __syncthreads();
 

@@ -86,6 +86,7 @@ struct BigArgs {
     uint8_t* act_s;
     uint16_t* ypair;
     uint8_t* sink;  // kSinkBytes
+    ActVariant av;  // bf16 only; zero: the plain SwiGLU
 };
 
 template <bool MX>
@@ -519,7 +520,7 @@ __device__ __forceinline__ void wait_budget(bool extra) {
     else wait_vm_lds<N>();
 }
 
-template <int BM, bool GEMM1, bool MX, int PAR>
+template <int BM, bool GEMM1, bool MX, int PAR, bool VAR>
 __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, StageBuf<BM, MX>& cur,
                                           const StageBuf<BM, MX>& nxt, int kt, int32_t (*pairs)[BM],
                                           float (*wrow)[BM], const LaneOff& o, Regs<BM, MX>& g,
@@ -539,7 +540,7 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
         if (kt == 0) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
         if (kt == 3) {
             make_src<BM, GEMM1, MX>(a, r.next, pairs[r.nb], r.wave, r.nsrc);
-            if (!GEMM1) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
+            if (!GEMM1 || (VAR && a.av.wba)) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
         }
     }
     if (kt + 4 < r.KT) issue_stage<BM, MX>(cur, r.src, r.boff, r.bstride, kt + 4, r.wave, r.slot(kt + 4));
@@ -559,7 +560,7 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
 
 // The stage buffers come in as restrict pointers: with them, the compiler
 // knows the fragment reads of one stage never alias the others.
-template <int BM, bool GEMM1, bool MX>
+template <int BM, bool GEMM1, bool MX, bool VAR>
 __device__ __forceinline__ void main_loop(const BigArgs& a, Ring<BM, MX>& r, StageBuf<BM, MX>* __restrict__ b0,
                                           StageBuf<BM, MX>* __restrict__ b1, StageBuf<BM, MX>* __restrict__ b2,
                                           StageBuf<BM, MX>* __restrict__ b3, int32_t (*pairs)[BM],
@@ -574,17 +575,17 @@ __device__ __forceinline__ void main_loop(const BigArgs& a, Ring<BM, MX>& r, Sta
     if constexpr (MX) {
 #pragma clang loop unroll(disable)
         for (int kt = 0; kt < r.KT; kt += 4) {
-            ring_step<BM, GEMM1, MX, 0>(a, r, *b0, *b1, kt, pairs, wrow, o, g, acc);
-            ring_step<BM, GEMM1, MX, 1>(a, r, *b1, *b2, kt + 1, pairs, wrow, o, g, acc);
-            ring_step<BM, GEMM1, MX, 0>(a, r, *b2, *b3, kt + 2, pairs, wrow, o, g, acc);
-            ring_step<BM, GEMM1, MX, 1>(a, r, *b3, *b0, kt + 3, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 0, VAR>(a, r, *b0, *b1, kt, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1, VAR>(a, r, *b1, *b2, kt + 1, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 0, VAR>(a, r, *b2, *b3, kt + 2, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1, VAR>(a, r, *b3, *b0, kt + 3, pairs, wrow, o, g, acc);
         }
     } else {
         for (int kt = 0; kt < r.KT; kt += 4) {
-            ring_step<BM, GEMM1, MX, 0>(a, r, *b0, *b1, kt, pairs, wrow, o, g, acc);
-            ring_step<BM, GEMM1, MX, 1>(a, r, *b1, *b2, kt + 1, pairs, wrow, o, g, acc);
-            ring_step<BM, GEMM1, MX, 0>(a, r, *b2, *b3, kt + 2, pairs, wrow, o, g, acc);
-            ring_step<BM, GEMM1, MX, 1>(a, r, *b3, *b0, kt + 3, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 0, VAR>(a, r, *b0, *b1, kt, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1, VAR>(a, r, *b1, *b2, kt + 1, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 0, VAR>(a, r, *b2, *b3, kt + 2, pairs, wrow, o, g, acc);
+            ring_step<BM, GEMM1, MX, 1, VAR>(a, r, *b3, *b0, kt + 3, pairs, wrow, o, g, acc);
         }
     }
 }
@@ -639,7 +640,7 @@ __device__ __forceinline__ void sink_stores(const BigArgs& a) {
 
 // bf16 results: GEMM1 writes act = silu(gate) * up at act[row0 + row][h0 + col];
 // GEMM2 (both formats) writes w * y at ypair[pair][n0 + feature].
-template <int BM, bool GEMM1, bool MX>
+template <int BM, bool GEMM1, bool MX, bool VAR>
 __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& t, const int32_t* pairs,
                                               const float* w, int tok_row0, int wf, uint8_t* stg,
                                               const f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
@@ -649,6 +650,9 @@ __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& 
     const int rr = lane >> 2, c = lane & 3;  // staging reads: rows rr and rr + 16, chunk c
     const int rd0 = stage_chunk_off(rr, c), rd1 = stage_chunk_off(rr + 16, c);
     uint16_t* sink = reinterpret_cast<uint16_t*>(wave_sink(a));
+    // the activation variant (bf16 only; the VAR = false kernels keep the plain path)
+    const bool variant = VAR && GEMM1 && !MX && a.av.on();
+    const float alpha_e = variant && a.av.alpha ? a.av.alpha[t.expert] : 1.0f;
 #pragma unroll
     for (int tb = 0; tb < C::NT; ++tb) {
         const int base = tok_row0 + 32 * tb;
@@ -666,7 +670,10 @@ __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& 
         }
         d0 = ok0 ? d0 : sink;
         d1 = ok1 ? d1 : sink;
-        const float wt = GEMM1 ? 1.0f : w[base + r];
+        // GEMM2: the routing weight (1 when it went before the activation);
+        // GEMM1 with the activation variant: its gate/up scale
+        const float wt = GEMM1 ? (variant ? (a.av.wba ? alpha_e * w[base + r] : alpha_e) : 1.0f)
+                               : ((VAR && a.av.wba) ? 1.0f : w[base + r]);
 #pragma unroll
         for (int f = 0; f < (GEMM1 ? 2 : 4); ++f) {
 #pragma unroll
@@ -675,7 +682,11 @@ __device__ __forceinline__ void epilogue_bf16(const BigArgs& a, const TileDesc& 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float x = acc[f][tb][4 * i + j];
-                    v[j] = GEMM1 ? x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][4 * i + j] : x * wt;
+                    if (GEMM1 && variant)
+                        v[j] = act_variant(x, acc[f + 2][tb][4 * i + j], wt, a.av.kind, a.av.limit);
+                    else
+                        v[j] = GEMM1 ? x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)) * acc[f + 2][tb][4 * i + j]
+                                     : x * wt;
                 }
                 *reinterpret_cast<uint2*>(stg + stage_chunk_off(r, i) + 8 * g) =
                     uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -762,7 +773,7 @@ __device__ __forceinline__ TileDesc uniform_desc(const TileDesc& d) {
     return TileDesc{uniform_int(d.expert), uniform_int(d.row0), uniform_int(d.rows), uniform_int(d.ntile)};
 }
 
-template <int BM, bool GEMM1, bool MX>
+template <int BM, bool GEMM1, bool MX, bool VAR>
 __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const int4* __restrict__ mtiles) {
     using C = Big<BM, MX>;
     constexpr int CAP = Fmt<MX>::kInfoCap;
@@ -826,7 +837,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
     wait_vm<0>();
     bare_barrier();
     make_src<BM, GEMM1, MX>(a, t, sPair[0], r.wave, r.src);
-    if (!GEMM1) {
+    if (!GEMM1 || (VAR && a.av.wba)) {
         dma_row_weights<BM>(a, sPair[0], sW[0], r.wave);
         wait_vm<0>();
         bare_barrier();
@@ -853,7 +864,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
         }
         r.cont = r.has_next && r.pipelined;
 
-        main_loop<BM, GEMM1, MX>(a, r, &buf0, &buf1, &buf2, &buf3, sPair, sW, o, g, acc);
+        main_loop<BM, GEMM1, MX, VAR>(a, r, &buf0, &buf1, &buf2, &buf3, sPair, sW, o, g, acc);
 
         if (r.has_next && !r.pipelined) {
             // short K: hand over after the ring has drained
@@ -861,7 +872,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
             wait_vm<0>();
             bare_barrier();
             make_src<BM, GEMM1, MX>(a, r.next, sPair[r.nb], r.wave, r.nsrc);
-            if (!GEMM1) {
+            if (!GEMM1 || (VAR && a.av.wba)) {
                 dma_row_weights<BM>(a, sPair[r.nb], sW[r.nb], r.wave);
                 wait_vm<0>();
                 bare_barrier();
@@ -869,7 +880,7 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
             ring_start<BM, GEMM1, MX>(r, r.nsrc, true, buf0, buf1, buf2, buf3, o, g);
         }
         if constexpr (GEMM1 && MX) epilogue_mx_gemm1<BM>(a, t, tok_row0, wf, sOut[wave_v], acc);
-        else epilogue_bf16<BM, GEMM1, MX>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
+        else epilogue_bf16<BM, GEMM1, MX, VAR>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
         if (!r.has_next) break;
         t = r.next;
         r.src = r.nsrc;
@@ -911,8 +922,14 @@ template <int BM, bool MX>
 hipError_t launch_big(const BigArgs& a, int4* tiles, bool gemm1, hipStream_t s) {
     if (gemm1) mtile_table_kernel<BM><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);  // the same m-tiles for both GEMMs
     const int g = big_grid(a.P, a.E, BM, gemm1 ? a.H / 128 : a.D / 256);
-    if (gemm1) big_gemm_kernel<BM, true, MX><<<g, kThreads, 0, s>>>(a, tiles);
-    else big_gemm_kernel<BM, false, MX><<<g, kThreads, 0, s>>>(a, tiles);
+    const bool var = !MX && a.av.on();  // the activation variant has kernels of its own
+    if (gemm1) {
+        if (var) big_gemm_kernel<BM, true, MX, !MX><<<g, kThreads, 0, s>>>(a, tiles);
+        else big_gemm_kernel<BM, true, MX, false><<<g, kThreads, 0, s>>>(a, tiles);
+    } else {
+        if (var) big_gemm_kernel<BM, false, MX, !MX><<<g, kThreads, 0, s>>>(a, tiles);
+        else big_gemm_kernel<BM, false, MX, false><<<g, kThreads, 0, s>>>(a, tiles);
+    }
     return hipGetLastError();
 }
 
@@ -952,7 +969,7 @@ hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
               reinterpret_cast<const uint8_t*>(b.x), nullptr,
               reinterpret_cast<const uint8_t*>(b.w1), nullptr,
               reinterpret_cast<const uint8_t*>(b.w2), nullptr,
-              b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair, sink_of(b.mtiles, b.P, b.E)};
+              b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair, sink_of(b.mtiles, b.P, b.E), b.av};
     int4* tiles = reinterpret_cast<int4*>(b.mtiles);
     if (b.P >= kBigTile256MinRows * b.E) return launch_big<256, false>(a, tiles, gemm1, s);
     return launch_big<128, false>(a, tiles, gemm1, s);

@@ -279,6 +279,19 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
             if (t != wave || m >= mt.rows) continue;
             if (GEMM1) {
                 uint16_t* dst = a.act + static_cast<int64_t>(mt.row0 + m) * a.H + g * 32 + 4 * kg;
+                if (a.av.on()) {
+                    const float al = a.av.alpha ? a.av.alpha[mt.expert] : 1.0f;
+                    const float sc =
+                        a.av.wba ? al * a.wts[clamp_pair(a.rv.sorted_to_pair[mt.row0 + m], a.P)] : al;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        float v[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = act_variant(acc[j][t][q], acc[j + 2][t][q], sc, a.av.kind, a.av.limit);
+                        *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     float v[4];
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
                 }
             } else {
                 const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + m], a.P);
-                const float wt = a.wts[p];
+                const float wt = a.av.wba ? 1.0f : a.wts[p];
                 uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + g * 64 + 4 * kg;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {

@@ -174,6 +174,38 @@ MOE_FFN_API int moe_ffn_forward_shared(const moe_ffn_problem* p, const void* x, 
                                        const void* shared_w2, int32_t Hs, void* out, int mode,
                                        void* stream, void* const* events, int n_events);
 
+/* Activation variant ("Porting Block-Scaled GEMM Kernels from Blackwell
+ * to Rubin", section 5.3: gate and up scaled by the expert's global scale
+ * alpha, clamped in the gpt-oss style -- the gate from above only, up on
+ * both sides -- then up * silu(gate); "GC-MoE on SM120", section 4.8: the
+ * route weight multiplies gate and up before the activation):
+ *     s   = alpha[e] * (weight_before_act ? w : 1)
+ *     act = silu(min(s*gate, limit)) * clamp(s*up, -limit, limit)   (CLAMPED)
+ *     act = silu(s*gate) * (s*up)                                  (SWIGLU)
+ *     y   = W2[e] act, summed with weight (weight_before_act ? 1 : w).
+ *   kind              : MOE_FFN_ACT_SWIGLU or MOE_FFN_ACT_CLAMPED_SWIGLU.
+ *   limit             : the clamp bound (finite, > 0) for CLAMPED.
+ *   alpha             : fp32 [E] device array of per-expert scales, or NULL
+ *                       (1.0 for every expert); 4-byte aligned.
+ *   weight_before_act : 0 or 1. */
+enum { MOE_FFN_ACT_SWIGLU = 0, MOE_FFN_ACT_CLAMPED_SWIGLU = 1 };
+typedef struct moe_ffn_activation {
+    int32_t kind;
+    float limit;
+    const float* alpha;
+    int32_t weight_before_act;
+} moe_ffn_activation;
+
+/* moe_ffn_forward_events with an activation variant. bf16 only, on the
+ * split pipeline: AUTO runs SPLIT (size the workspace with
+ * moe_ffn_workspace_bytes(p, MOE_FFN_SPLIT)); FUSED or MXFP8 return
+ * MOE_FFN_EUNSUPPORTED. */
+MOE_FFN_API int moe_ffn_forward_act(const moe_ffn_problem* p, const void* x, const void* w1,
+                                    const void* w2, const int32_t* topk_ids,
+                                    const float* topk_weights, const moe_ffn_activation* act,
+                                    void* out, int mode, void* stream, void* const* events,
+                                    int n_events);
+
 /* Workspace bytes moe_ffn_route needs (host only; 0 on invalid input). */
 MOE_FFN_API size_t moe_ffn_route_workspace_bytes(int32_t T, int32_t topk, int32_t E);
 

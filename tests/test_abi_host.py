@@ -16,7 +16,7 @@ def test_library_exports_every_header_function():
     assert set(names) == {
         "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_forward",
         "moe_ffn_forward_events", "moe_ffn_router", "moe_ffn_forward_logits",
-        "moe_ffn_shared_workspace_bytes", "moe_ffn_forward_shared",
+        "moe_ffn_shared_workspace_bytes", "moe_ffn_forward_shared", "moe_ffn_forward_act",
         "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_strerror"}
 
 
@@ -154,3 +154,21 @@ def test_shared_expert_host_checks():
                                       None, None, 0) == g.MOE_FFN_EUNSUPPORTED
     assert lib.moe_ffn_forward_shared(ctypes.byref(p), None, None, None, None, None, None, None, 200, None, 0,
                                       None, None, 0) == g.MOE_FFN_EINVAL_SHAPE
+
+
+@pytest.mark.parametrize("kind,limit,mode,dtype,expect", [
+    (1, 0.0, "split", "bf16", g.MOE_FFN_EINVAL_SHAPE),       # the clamp needs a positive limit
+    (1, float("inf"), "split", "bf16", g.MOE_FFN_EINVAL_SHAPE),
+    (2, 1.0, "split", "bf16", g.MOE_FFN_EUNSUPPORTED),        # unknown kind
+    (1, 7.0, "fused", "bf16", g.MOE_FFN_EUNSUPPORTED),        # the variant runs on the split pipeline
+    (1, 7.0, "split", "mxfp8", g.MOE_FFN_EUNSUPPORTED),
+    (1, 7.0, "split", "bf16", g.MOE_FFN_EINVAL_PTR),          # valid: null tensors are rejected next
+])
+def test_activation_variant_host_checks(kind, limit, mode, dtype, expect):
+    lib = g.library()
+    p = g.make_problem(4, 256, 512, 8, 2, dtype)
+    act = g.moe_ffn_activation(kind, limit, None, 0)
+    assert lib.moe_ffn_forward_act(ctypes.byref(p), None, None, None, None, None, ctypes.byref(act), None,
+                                   g._mode(mode), None, None, 0) == expect
+    assert lib.moe_ffn_forward_act(ctypes.byref(p), None, None, None, None, None, None, None, 0, None, None,
+                                   0) == g.MOE_FFN_EINVAL_PTR
