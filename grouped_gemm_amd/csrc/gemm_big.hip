@@ -245,6 +245,9 @@ __device__ __forceinline__ void wait_vm_lds() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// until this wave's LDS reads have returned (vector memory not waited for)
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8)); }
+
 // s_barrier without a memory fence; the asm statements stop the compiler from
 // moving LDS accesses across it.
 __device__ __forceinline__ void bare_barrier() {
@@ -535,6 +538,10 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
     if (kt + 3 < r.KT || r.cont) wait_budget<C::Y2, S>(after_stores);
     else if (kt + 2 < r.KT) wait_budget<C::Y1, S>(after_stores);
     else wait_budget<0, S>(after_stores);
+    // The budgets above already wait for the LDS reads; repeating that outside
+    // the branches lets the compiler see it on every path, so it does not hold
+    // the MFMAs of half 1 for the reads issued after the barrier.
+    wait_lds();
     bare_barrier();
     if (r.cont) {
         if (kt == 0) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
@@ -889,6 +896,268 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 with 128-byte stages. A stage holds 64 elements of K per tile row, so
+// every row's piece of a stage is one whole 128-byte line: half the memory
+// requests of the 64-byte stages above for the same bytes. Two stage buffers
+// (2 x 64 KB for 256-row tiles) make a double-buffered ring: while stage kt
+// is consumed, stage kt + 1 is in flight, and one barrier per stage (a K
+// step of 64) guards both buffers. Tiles, waves and epilogues are those of
+// the kernel above; the ring runs on across tiles the same way.
+//
+// Swizzle: 16-byte chunk c of row r sits at chunk position c ^ ((r >> 1) & 7)
+// of its 128-byte LDS row. A fragment read has 16 lanes read the same chunk
+// of 16 consecutive rows; the rows of one parity then take 8 distinct chunk
+// positions, and the two parities sit in different 128-byte halves of the
+// 256-byte bank row, so the 16 reads hit 16 distinct bank groups.
+constexpr int RB2 = 128;  // bytes per tile row per stage
+
+template <int BM>
+struct StageBuf2 {
+    uint8_t tok[BM * RB2];
+    uint8_t wt[BN * RB2];
+};
+
+template <int BM>
+struct Deep {
+    static constexpr int NT = Big<BM, false>::NT;
+    static constexpr int A_INS = BM / 8 / W;  // token-row DMA instructions per wave per stage (8 rows each)
+    static constexpr int B_INS = BN / 8 / W;  // weight-row DMA instructions per wave per stage
+    static_assert(A_INS >= 1 && A_INS * 8 * W == BM && B_INS * 8 * W == BN, "tile split");
+    static_assert(B_INS % 2 == 0, "weight-row offsets alternate with the instruction's parity");
+};
+
+__device__ __forceinline__ int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+template <int BM>
+struct DmaSrc2 {
+    const char* abase;
+    const char* bbase;
+    uint32_t aoff[Deep<BM>::A_INS];
+};
+
+// Per-lane LDS offsets of the fragment rows and of the four quarters' chunks
+// (quarter q: K elements 16q .. 16q + 15, chunks 2q and 2q + 1; lane group
+// g = lane >> 5 reads chunk 2q + g).
+struct LaneOff2 {
+    int w, t;
+    int c0, c1, c2, c3;
+};
+
+template <int BM>
+struct Ring2 {
+    DmaSrc2<BM> src, nsrc;
+    uint32_t boff0, boff1, bstride;  // weight-row offsets of even and odd instructions (the same for every tile)
+    uint32_t wave;
+    int KT;
+    bool has_next, cont;
+    TileDesc next;
+    int nb;
+};
+
+// Instruction j of a wave covers tile rows (wave * INS + j) * 8 + lane / 8;
+// lane i's 16 bytes land at chunk position i & 7 of that row, so it fetches
+// the global chunk that the swizzle puts there.
+template <int BM, bool GEMM1>
+__device__ __forceinline__ void make_src2(const BigArgs& a, const TileDesc& t, const int32_t* pairs, uint32_t wave,
+                                          DmaSrc2<BM>& s) {
+    using C = Deep<BM>;
+    const int lane = threadIdx.x & 63;
+    const int K = GEMM1 ? a.D : a.H;
+    const int h0 = t.ntile * 128, n0 = t.ntile * 256;
+    s.abase = uniform_ptr(GEMM1 ? a.x : a.act + static_cast<int64_t>(t.row0) * a.H * 2);
+#pragma unroll
+    for (int j = 0; j < C::A_INS; ++j) {
+        const int row = (static_cast<int>(wave) * C::A_INS + j) * 8 + lane / 8;
+        const uint32_t r = GEMM1 ? static_cast<uint32_t>(clamp_pair(pairs[row], a.P) / a.k) * a.D
+                                 : static_cast<uint32_t>(row < t.rows ? row : 0) * a.H;
+        s.aoff[j] = r * 2 + swz8(row, lane & 7) * 16;
+    }
+    const int row0 = static_cast<int>(wave) * C::B_INS * 8;  // 32 weight rows per wave, never across gate/up
+    if (GEMM1) {
+        const int grow0 = row0 < 128 ? h0 + row0 : a.H + h0 + row0 - 128;
+        s.bbase = uniform_ptr(a.w1 + (static_cast<int64_t>(t.expert) * 2 * a.H + grow0) * K * 2);
+    } else {
+        s.bbase = uniform_ptr(a.w2 + (static_cast<int64_t>(t.expert) * a.D + n0 + row0) * K * 2);
+    }
+}
+
+template <int BM>
+__device__ __forceinline__ void issue2(StageBuf2<BM>& b, const DmaSrc2<BM>& src, const Ring2<BM>& r, int kt) {
+    using C = Deep<BM>;
+    const char* ab = src.abase + kt * RB2;
+    const char* bb = src.bbase + kt * RB2;
+    const uint32_t tl = lds_addr(b.tok) + r.wave * (C::A_INS * 1024);
+    const uint32_t wl = lds_addr(b.wt) + r.wave * (C::B_INS * 1024);
+#pragma unroll
+    for (int j = 0; j < C::A_INS; ++j) dma16(ab, src.aoff[j], tl + j * 1024);
+#pragma unroll
+    for (int j = 0; j < C::B_INS; ++j) dma16(bb, ((j & 1) ? r.boff1 : r.boff0) + j * r.bstride, wl + j * 1024);
+}
+
+template <int BM, bool GEMM1, int Q>
+__device__ __forceinline__ void read_q(const StageBuf2<BM>& b, const LaneOff2& o, Frag<BM, false>& f) {
+    const int co = Q == 0 ? o.c0 : Q == 1 ? o.c1 : Q == 2 ? o.c2 : o.c3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        f.w[i] = *reinterpret_cast<const bf16x8_t*>(b.wt + o.w + frow_const<GEMM1>(i) * RB2 + co);
+#pragma unroll
+    for (int i = 0; i < Deep<BM>::NT; ++i) f.t[i] = *reinterpret_cast<const bf16x8_t*>(b.tok + o.t + 32 * i * RB2 + co);
+}
+
+// One stage (K step of 64) of the double-buffered ring:
+//   wait for this wave's DMAs of stage kt and its LDS reads;  barrier
+//   (FIRST) hand-over work for the next tile;  issue stage kt + 1 into the
+//   other buffer (every wave is done reading it: stage kt - 1);
+//   read quarter 0 of stage kt;  MFMAs of quarter 3 of stage kt - 1;
+//   read q1, MFMAs q0;  read q2, MFMAs q1;  read q3, MFMAs q2.
+// Quarter 3's MFMAs move past the next barrier, so no wave comes out of it
+// with nothing to compute. Waits: a wave's vector-memory operations complete
+// in issue order. In a tile's step 0 the previous tile's result stores (or
+// the first tile's sink stores), issued after stage 0, may stay in flight;
+// every later step waits for everything: the only operations younger than
+// stage kt then are none. Hand-over: step 0 fetches the next tile's row map
+// (landed by step 1's barrier), step 1 builds its DMA sources and fetches its
+// routing weights, and step KT - 1 issues its stage 0.
+template <int BM, bool GEMM1, bool VAR, bool FIRST, bool SECOND>
+__device__ __forceinline__ void deep_step(const BigArgs& a, Ring2<BM>& r, const StageBuf2<BM>& cur,
+                                          StageBuf2<BM>& oth, int kt, int32_t (*pairs)[BM], float (*wrow)[BM],
+                                          const LaneOff2& o, Frag<BM, false>& x, Frag<BM, false>& y,
+                                          f32x16_t (&acc)[4][Deep<BM>::NT]) {
+    constexpr int S = Big<BM, false>::template stores<GEMM1>();
+    if (FIRST) wait_vm_lds<S>();
+    else wait_vm_lds<0>();
+    bare_barrier();
+    if (FIRST && r.cont) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
+    if (SECOND && r.cont) {
+        make_src2<BM, GEMM1>(a, r.next, pairs[r.nb], r.wave, r.nsrc);
+        if (!GEMM1 || (VAR && a.av.wba)) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
+    }
+    if (kt + 1 < r.KT) issue2<BM>(oth, r.src, r, kt + 1);
+    else if (r.cont) issue2<BM>(oth, r.nsrc, r, 0);
+    read_q<BM, GEMM1, 0>(cur, o, x);
+    if (!FIRST) mfma_half<BM>(y, acc);
+    read_q<BM, GEMM1, 1>(cur, o, y);
+    mfma_half<BM>(x, acc);
+    read_q<BM, GEMM1, 2>(cur, o, x);
+    mfma_half<BM>(y, acc);
+    read_q<BM, GEMM1, 3>(cur, o, y);
+    mfma_half<BM>(x, acc);
+    // Keep that order: each quarter's fragment reads go out as a group ahead
+    // of the previous quarter's MFMAs, which hide their latency. Left alone,
+    // the scheduler moves each read next to its first use.
+    constexpr int R = 4 + Deep<BM>::NT, M = 4 * Deep<BM>::NT;
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    if (!FIRST) __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    }
+}
+
+template <int BM, bool GEMM1, bool VAR>
+__global__ __launch_bounds__(kThreads, 1) void big_deep_kernel(BigArgs a, const int4* __restrict__ mtiles) {
+    using C = Deep<BM>;
+    constexpr int CAP = Fmt<false>::kInfoCap;
+    __shared__ __attribute__((aligned(1024))) StageBuf2<BM> buf0;
+    __shared__ __attribute__((aligned(1024))) StageBuf2<BM> buf1;
+    __shared__ __attribute__((aligned(16))) int32_t sPair[2][BM];
+    __shared__ __attribute__((aligned(16))) float sW[2][BM];
+    __shared__ TileDesc sDesc[CAP];
+    __shared__ __attribute__((aligned(16))) uint8_t sOut[W][2048];  // per-wave result staging
+
+    const int ny = GEMM1 ? a.H / 128 : a.D / 256;
+    const int total = a.rv.tile_prefix[tile_height_index(BM) * (a.E + 1) + a.E] * ny;
+    const int per = (total + 7) / 8;
+    const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3;
+    const int first = xcd * per + (blockIdx.x >> 3);
+    const int end = min(total, (xcd + 1) * per);
+    const int count = first < end ? (end - first + stride - 1) / stride : 0;
+    if (count == 0) return;
+
+    const int tid = threadIdx.x, wave_v = tid >> 6;
+    const int wtok = wave_v >> 1, wf = wave_v & 1;
+    const int tok_row0 = wtok * Big<BM, false>::TB;
+    LaneOff2 o;
+    {
+        const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+        const int wrow0 = (GEMM1 ? 64 : 128) * wf;
+        o.w = (wrow0 + lr) * RB2;
+        o.t = (tok_row0 + lr) * RB2;
+        // fragment rows start at multiples of 32: the swizzle term is ((lane & 31) >> 1) & 7
+        o.c0 = swz8(lr, g) << 4;
+        o.c1 = swz8(lr, 2 + g) << 4;
+        o.c2 = swz8(lr, 4 + g) << 4;
+        o.c3 = swz8(lr, 6 + g) << 4;
+    }
+
+    Ring2<BM> r;
+    r.wave = static_cast<uint32_t>(uniform_int(wave_v));
+    const int K = GEMM1 ? a.D : a.H;
+    r.KT = K / 64;
+    {
+        // weight row of instruction j: wave * 8 * B_INS + 8j + lane / 8; with
+        // B_INS even its swizzle term is 4 (j & 1) + lane / 16
+        const int lane = tid & 63;
+        const uint32_t rowoff = static_cast<uint32_t>(lane / 8) * K * 2;
+        r.boff0 = rowoff + (((lane & 7) ^ (lane >> 4)) << 4);
+        r.boff1 = rowoff + (((lane & 7) ^ (4 + (lane >> 4))) << 4);
+        r.bstride = 8u * K * 2;
+    }
+
+    load_descs<CAP>(mtiles, first, stride, ny, count, 0, sDesc);
+    __syncthreads();
+    TileDesc t = uniform_desc(sDesc[0]);
+    int cb = 0;
+    dma_row_map<BM>(a, t.row0, sPair[0], r.wave);
+    wait_vm<0>();
+    bare_barrier();
+    make_src2<BM, GEMM1>(a, t, sPair[0], r.wave, r.src);
+    if (!GEMM1 || (VAR && a.av.wba)) {
+        dma_row_weights<BM>(a, sPair[0], sW[0], r.wave);
+        wait_vm<0>();
+        bare_barrier();
+    }
+    issue2<BM>(buf0, r.src, r, 0);
+    sink_stores<BM, GEMM1, false>(a);
+
+    Frag<BM, false> x, y;
+    f32x16_t acc[4][C::NT];
+    for (int i = 0; i < count; ++i) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int tb = 0; tb < C::NT; ++tb) acc[f][tb] = f32x16_t{};
+        r.has_next = i + 1 < count;
+        r.nb = cb ^ 1;
+        if (r.has_next) {
+            if ((i + 1) % CAP == 0) {  // next descriptor chunk; t stays in registers
+                __syncthreads();
+                load_descs<CAP>(mtiles, first, stride, ny, count, i + 1, sDesc);
+                __syncthreads();
+            }
+            r.next = uniform_desc(sDesc[(i + 1) % CAP]);
+        }
+        r.cont = r.has_next;
+
+        // KT is even: every tile starts in buffer 0
+        deep_step<BM, GEMM1, VAR, true, false>(a, r, buf0, buf1, 0, sPair, sW, o, x, y, acc);
+        deep_step<BM, GEMM1, VAR, false, true>(a, r, buf1, buf0, 1, sPair, sW, o, x, y, acc);
+        for (int kt = 2; kt < r.KT; kt += 2) {
+            deep_step<BM, GEMM1, VAR, false, false>(a, r, buf0, buf1, kt, sPair, sW, o, x, y, acc);
+            deep_step<BM, GEMM1, VAR, false, false>(a, r, buf1, buf0, kt + 1, sPair, sW, o, x, y, acc);
+        }
+        mfma_half<BM>(y, acc);  // quarter 3 of the last stage
+
+        epilogue_bf16<BM, GEMM1, false, VAR>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);
+        if (!r.has_next) break;
+        t = r.next;
+        r.src = r.nsrc;
+        cb ^= 1;
+    }
+}
+
 // One m-tile descriptor per tile of height BM: {expert, first sorted row,
 // rows, 0}, in tile order. One workgroup per expert.
 template <int BM>
@@ -922,13 +1191,18 @@ template <int BM, bool MX>
 hipError_t launch_big(const BigArgs& a, int4* tiles, bool gemm1, hipStream_t s) {
     if (gemm1) mtile_table_kernel<BM><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);  // the same m-tiles for both GEMMs
     const int g = big_grid(a.P, a.E, BM, gemm1 ? a.H / 128 : a.D / 256);
-    const bool var = !MX && a.av.on();  // the activation variant has kernels of its own
-    if (gemm1) {
-        if (var) big_gemm_kernel<BM, true, MX, !MX><<<g, kThreads, 0, s>>>(a, tiles);
-        else big_gemm_kernel<BM, true, MX, false><<<g, kThreads, 0, s>>>(a, tiles);
+    if constexpr (MX) {
+        if (gemm1) big_gemm_kernel<BM, true, true, false><<<g, kThreads, 0, s>>>(a, tiles);
+        else big_gemm_kernel<BM, false, true, false><<<g, kThreads, 0, s>>>(a, tiles);
     } else {
-        if (var) big_gemm_kernel<BM, false, MX, !MX><<<g, kThreads, 0, s>>>(a, tiles);
-        else big_gemm_kernel<BM, false, MX, false><<<g, kThreads, 0, s>>>(a, tiles);
+        const bool var = a.av.on();  // the activation variant has kernels of its own
+        if (gemm1) {
+            if (var) big_deep_kernel<BM, true, true><<<g, kThreads, 0, s>>>(a, tiles);
+            else big_deep_kernel<BM, true, false><<<g, kThreads, 0, s>>>(a, tiles);
+        } else {
+            if (var) big_deep_kernel<BM, false, true><<<g, kThreads, 0, s>>>(a, tiles);
+            else big_deep_kernel<BM, false, false><<<g, kThreads, 0, s>>>(a, tiles);
+        }
     }
     return hipGetLastError();
 }
