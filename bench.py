@@ -105,7 +105,6 @@ def kernel_work(cfg, mode, hit, dtype):
 
 
 KERNEL_FILES = {"dma_skinny_kernel": "gemm_skinny.hip", "big_gemm_kernel": "gemm_big.hip",
-                "big_deep_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
                 "gemm1_swiglu_kernel": "gemm_bf16.hip", "gemm2_weight_kernel": "gemm_bf16.hip",
                 "combine_kernel": "gemm_bf16.hip"}
@@ -143,7 +142,7 @@ def kernel_symbol(cfg, mode, stage):
     if cfg.P <= 32 * cfg.E:
         return "dma_skinny_kernel"
     if cfg.D % 256 == 0:
-        return "big_deep_kernel"
+        return "big_gemm_kernel"
     return "gemm1_swiglu_kernel" if g1 else "gemm2_weight_kernel"
 
 
