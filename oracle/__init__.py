@@ -52,7 +52,16 @@ def _load():
                                                    i64]
         lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                           P, i64, i32]
+        lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                           P, i64, i32]
         lib.oracle_mx_quantize.argtypes = [P, i64, i64, P, P]
+        lib.oracle_mx4_quantize.argtypes = [P, i64, i64, P, P]
+        lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_decode.restype = ctypes.c_float
+        lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_mx4_scale_exp.argtypes = [P, ctypes.c_int]
+        lib.oracle_mx4_scale_exp.restype = ctypes.c_int
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_decode.restype = ctypes.c_float
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -208,6 +217,55 @@ def forward_mx(xc, xs, w1c, w1s, w2c, w2s, topk_ids, topk_weights, tokens=None, 
     _load().oracle_forward_mx(T, D, H, E, k, _p(xc), _p(xs), _p(w1c), _p(w1s), _p(w2c), _p(w2s),
                               _p(ids), _p(wts), _p(out), tok_p, n, 1 if requant else 0)
     return out
+
+
+def mx4_quantize(src: np.ndarray):
+    """MXQ4 along the last dim: (packed e2m1 codes uint8 [..., K/2], even index in the low nibble;
+    scales uint8 [..., K/32]). GC-MoE on SM120, scale formats; the rule is MXQ with 6 for 448."""
+    src = _c(src, np.float32)
+    K = src.shape[-1]
+    assert K % 32 == 0
+    rows = src.size // K if K else 0
+    codes = np.zeros(src.shape[:-1] + (K // 2,), np.uint8)
+    scales = np.zeros(src.shape[:-1] + (K // 32,), np.uint8)
+    _load().oracle_mx4_quantize(_p(src), rows, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def forward_mx4(xc, xs, w1c, w1s, w2c, w2s, topk_ids, topk_weights, tokens=None, requant=True):
+    """MXFP4-weight forward (e2m1 weights, e4m3 activations): out bf16 bits [T, D].
+    w1c packed [E, 2H, D/2], w2c packed [E, D, H/2]; scales as for forward_mx."""
+    arrs = [_c(a, np.uint8) for a in (xc, xs, w1c, w1s, w2c, w2s)]
+    xc, xs, w1c, w1s, w2c, w2s = arrs
+    ids, wts = _c(topk_ids, np.int32), _c(topk_weights, np.float32)
+    T, D = xc.shape
+    E, H2, _ = w1c.shape
+    H = H2 // 2
+    k = ids.shape[1]
+    assert w1c.shape == (E, H2, D // 2) and xs.shape == (T, D // 32) and w1s.shape == (E, H2, D // 32)
+    assert w2c.shape == (E, D, H // 2) and w2s.shape == (E, D, H // 32)
+    out = np.zeros((T, D), np.uint16)
+    if tokens is None:
+        tok_p, n = None, T
+    else:
+        tok = _c(tokens, np.int64)
+        tok_p, n = _p(tok), tok.size
+    _load().oracle_forward_mx4(T, D, H, E, k, _p(xc), _p(xs), _p(w1c), _p(w1s), _p(w2c), _p(w2s),
+                               _p(ids), _p(wts), _p(out), tok_p, n, 1 if requant else 0)
+    return out
+
+
+def e2m1_decode(code: int) -> float:
+    return float(_load().oracle_e2m1_decode(int(code)))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(_load().oracle_e2m1_encode(float(v)))
+
+
+def mx4_scale_exp(block: np.ndarray) -> int:
+    b = _c(block, np.float32)
+    return int(_load().oracle_mx4_scale_exp(_p(b), b.size))
 
 
 def e4m3_decode(code: int) -> float:

@@ -32,6 +32,16 @@
  *   code_i         =  e4m3fn(v_i * 2^-s), round to nearest even, values
  *                     beyond 448 in magnitude saturate to +-448.
  *
+ * MXFP4 weights ("GC-MoE on SM120", section on scale formats: a 4-bit E2M1
+ * code with a shared UE8M0 exponent per 32 contiguous elements; activations
+ * stay MX-fp8): e2m1 has 1 sign bit, 2 exponent bits (bias 1) and 1
+ * mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, no infinities or
+ * NaN. Two codes share a byte, the even K index in the low nibble. The
+ * pages give no scale rule for fp4; MXQ4 reads MXQ with 6 in place of 448:
+ * s = the smallest integer with amax <= 6 * 2^s (clamped to [-127, 127],
+ * amax == 0 -> -127), codes e2m1(v_i * 2^-s) rounded to nearest, ties to
+ * an even code, saturating at 6.
+ *
  * Route maps: a stable counting sort of the pairs p = t*k + j by expert
  * (ascending p inside each expert). Ids outside [0, E) are dropped routes:
  * they are not counted and contribute nothing.
@@ -128,6 +138,67 @@ void oracle_mx_quantize(const float* src, int64_t rows, int64_t K, uint8_t* code
 
 float oracle_mx_value(uint8_t code, uint8_t scale) {
     return ldexpf(oracle_e4m3_decode(code), (int)scale - 127);
+}
+
+/* e2m1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa; exponent 0
+ * is subnormal (mantissa * 0.5). */
+float oracle_e2m1_decode(uint8_t c) {
+    int sign = (c >> 3) & 1, ex = (c >> 1) & 3, man = c & 1;
+    float mag = ex == 0 ? 0.5f * (float)man : ldexpf(1.0f + 0.5f * (float)man, ex - 1);
+    return sign ? -mag : mag;
+}
+
+/* Nearest e2m1 value to v (finite), ties to the even code (mantissa bit 0),
+ * saturating to +-6; returns the 4-bit code. A search over the 8 codes. */
+uint8_t oracle_e2m1_encode(float v) {
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    if (a >= 6.0) return sign | 7;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs(a - (double)oracle_e2m1_decode((uint8_t)c));
+        if (d < best_d || (d == best_d && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* MXQ4 scale exponent s for one block (see the header comment). */
+int oracle_mx4_scale_exp(const float* v, int n) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) return -127;
+    int e;
+    double m = frexp((double)amax, &e);  /* amax = m * 2^e; 6 = 0.75 * 2^3 */
+    int s = e - 3;                       /* 6 * 2^s = 0.75 * 2^e */
+    if (m > 0.75) s += 1;
+    if (s < -127) s = -127;
+    if (s > 127) s = 127;
+    return s;
+}
+
+/* Quantize rows x K (K a multiple of 32) of fp32 to packed e2m1 codes
+ * [rows, K/2] (even index in the low nibble) + e8m0 bytes [rows, K/32]. */
+void oracle_mx4_quantize(const float* src, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const float* v = src + r * K + b * 32;
+            int s = oracle_mx4_scale_exp(v, 32);
+            scales[r * (K / 32) + b] = (uint8_t)(s + 127);
+            for (int i = 0; i < 32; i += 2) {
+                uint8_t lo = oracle_e2m1_encode(ldexpf(v[i], -s));
+                uint8_t hi = oracle_e2m1_encode(ldexpf(v[i + 1], -s));
+                codes[r * (K / 2) + (b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
 }
 
 /* ---------- route maps ---------- */
@@ -361,23 +432,34 @@ void oracle_forward_bf16(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, 
     oracle_forward_bf16_shared(T, D, H, E, k, x, w1, w2, ids, wts, NULL, NULL, 0, out, tokens, n_tok);
 }
 
-/* MX-fp8 forward. x codes [T, D] + scales [T, D/32]; w1 codes [E, 2H, D] +
- * scales [E, 2H, D/32]; w2 codes [E, D, H] + scales [E, D, H/32]. The SwiGLU
- * output is requantized with MXQ per 32 along H when requant != 0 (the
+/* MX forward. x codes [T, D] + scales [T, D/32]; w1 codes [E, 2H, D] +
+ * scales [E, 2H, D/32]; w2 codes [E, D, H] + scales [E, D, H/32] (w4: the
+ * weight codes packed e2m1, half the bytes per row). The SwiGLU output is
+ * requantized with MXQ (e4m3) per 32 along H when requant != 0 (the
  * method's behaviour); requant == 0 keeps it in fp32 (used by a pin). */
-void oracle_forward_mx(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint8_t* xc,
-                       const uint8_t* xs, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
-                       const uint8_t* w2s, const int32_t* ids, const float* wts, uint16_t* out,
-                       const int64_t* tokens, int64_t n_tok, int32_t requant) {
+/* Weight element idx of a row of K: e4m3 codes [.., K] (w4 == 0) or packed
+ * e2m1 codes [.., K/2] (w4 != 0), without its scale. */
+static float weight_code_value(const uint8_t* codes, int64_t row, int32_t K, int32_t idx, int32_t w4,
+                               const float* lut8, const float* lut4) {
+    if (!w4) return lut8[codes[row * K + idx]];
+    uint8_t byte = codes[row * (K / 2) + idx / 2];
+    return lut4[(idx & 1) ? (byte >> 4) : (byte & 15)];
+}
+
+static void forward_mx_any(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint8_t* xc,
+                           const uint8_t* xs, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
+                           const uint8_t* w2s, const int32_t* ids, const float* wts, uint16_t* out,
+                           const int64_t* tokens, int64_t n_tok, int32_t requant, int32_t w4) {
     if (!tokens) n_tok = T;
-    /* Both tables are exact: e4m3 values carry at most 4 significant bits and
-     * 2^(b-127) >= 2^-127, so every product lut * pow2 is an fp32 number
-     * (smallest magnitude 2^-9 * 2^-127 = 2^-136 > 2^-149). */
-    float lut[256], pow2[256];
+    /* The tables are exact: e4m3 and e2m1 values carry at most 4 significant
+     * bits and 2^(b-127) >= 2^-127, so every product lut * pow2 is an fp32
+     * number (smallest magnitude 2^-9 * 2^-127 = 2^-136 > 2^-149). */
+    float lut[256], lut4[16], pow2[256];
     for (int c = 0; c < 256; ++c) {
         lut[c] = oracle_e4m3_decode((uint8_t)c);
         pow2[c] = ldexpf(1.0f, c - 127);
     }
+    for (int c = 0; c < 16; ++c) lut4[c] = oracle_e2m1_decode((uint8_t)c);
     const int32_t DB = D / 32, HB = H / 32;
 #pragma omp parallel
     {
@@ -399,7 +481,7 @@ void oracle_forward_mx(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, co
                     int64_t row = (int64_t)e * 2 * H + n;
                     float s = 0.0f;
                     for (int32_t d = 0; d < D; ++d)
-                        s += lut[w1c[row * D + d]] * pow2[w1s[row * DB + d / 32]] * xv[d];
+                        s += weight_code_value(w1c, row, D, d, w4, lut, lut4) * pow2[w1s[row * DB + d / 32]] * xv[d];
                     gu[n] = s;
                 }
                 for (int32_t h = 0; h < H; ++h) act[h] = silu(gu[h]) * gu[H + h];
@@ -416,7 +498,7 @@ void oracle_forward_mx(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, co
                     int64_t row = (int64_t)e * D + d;
                     float s = 0.0f;
                     for (int32_t h = 0; h < H; ++h)
-                        s += lut[w2c[row * H + h]] * pow2[w2s[row * HB + h / 32]] * act[h];
+                        s += weight_code_value(w2c, row, H, h, w4, lut, lut4) * pow2[w2s[row * HB + h / 32]] * act[h];
                     acc[d] += w * s;
                 }
             }
@@ -427,6 +509,23 @@ void oracle_forward_mx(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, co
         free(act);
         free(acc);
     }
+}
+
+void oracle_forward_mx(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint8_t* xc,
+                       const uint8_t* xs, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
+                       const uint8_t* w2s, const int32_t* ids, const float* wts, uint16_t* out,
+                       const int64_t* tokens, int64_t n_tok, int32_t requant) {
+    forward_mx_any(T, D, H, E, k, xc, xs, w1c, w1s, w2c, w2s, ids, wts, out, tokens, n_tok, requant, 0);
+}
+
+/* MXFP4-weight forward: as oracle_forward_mx, with w1 packed e2m1 codes
+ * [E, 2H, D/2] and w2 [E, D, H/2] (scales as for MX-fp8); x and the
+ * requantized act stay e4m3. */
+void oracle_forward_mx4(int64_t T, int32_t D, int32_t H, int32_t E, int32_t k, const uint8_t* xc,
+                        const uint8_t* xs, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
+                        const uint8_t* w2s, const int32_t* ids, const float* wts, uint16_t* out,
+                        const int64_t* tokens, int64_t n_tok, int32_t requant) {
+    forward_mx_any(T, D, H, E, k, xc, xs, w1c, w1s, w2c, w2s, ids, wts, out, tokens, n_tok, requant, 1);
 }
 
 int oracle_num_threads(void) {
