@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(_HERE, "libmoe_ffn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_ffn.h")
 
-MOE_FFN_BF16, MOE_FFN_MXFP8 = 0, 1
+MOE_FFN_BF16, MOE_FFN_MXFP8, MOE_FFN_MXFP4 = 0, 1, 2
 MOE_FFN_AUTO, MOE_FFN_FUSED, MOE_FFN_SPLIT = 0, 1, 2
 MOE_FFN_OK = 0
 MOE_FFN_EINVAL_SHAPE, MOE_FFN_EINVAL_PTR, MOE_FFN_EUNSUPPORTED = -1, -2, -3
@@ -29,7 +29,7 @@ MOE_FFN_EWORKSPACE, MOE_FFN_EHIP = -4, -5
 MOE_FFN_ACT_SWIGLU, MOE_FFN_ACT_CLAMPED_SWIGLU = 0, 1
 
 _MODES = {"auto": MOE_FFN_AUTO, "fused": MOE_FFN_FUSED, "split": MOE_FFN_SPLIT}
-_DTYPES = {"bf16": MOE_FFN_BF16, "mxfp8": MOE_FFN_MXFP8}
+_DTYPES = {"bf16": MOE_FFN_BF16, "mxfp8": MOE_FFN_MXFP8, "mxfp4": MOE_FFN_MXFP4}
 
 
 class MoeFfnError(RuntimeError):
@@ -82,6 +82,7 @@ def library() -> ctypes.CDLL:
             "moe_ffn_route_workspace_bytes": ([I32, I32, I32], SZ),
             "moe_ffn_route": ([VP, I32, I32, I32, VP, VP, VP, VP, VP, SZ, VP], INT),
             "moe_ffn_mx_quantize": ([VP, I64, I32, VP, VP, VP], INT),
+            "moe_ffn_mxfp4_quantize": ([VP, I64, I32, VP, VP, VP], INT),
             "moe_ffn_strerror": ([INT], ctypes.c_char_p),
         }
         for name, (args, res) in signatures.items():
@@ -111,6 +112,13 @@ def _mode(mode) -> int:
 
 def _dtype(dtype) -> int:
     return _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _data_path(x, w1) -> str:
+    """bf16 tensors: "bf16"; uint8 codes: "mxfp4" when w1 rows hold D/2 bytes (packed e2m1), else "mxfp8"."""
+    if x.dtype != torch.uint8:
+        return "bf16"
+    return "mxfp4" if w1.shape[-1] * 2 == x.shape[1] else "mxfp8"
 
 
 def make_problem(T, D, H, E, topk, dtype="bf16", x_scale=None, w1_scale=None, w2_scale=None,
@@ -158,11 +166,12 @@ def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_
     bf16 path: x [T, D], w1 [E, 2H, D], w2 [E, D, H] torch.bfloat16.
     MXFP8 path: x, w1, w2 are uint8 e4m3 codes and x_scale [T, D/32],
     w1_scale [E, 2H, D/32], w2_scale [E, D, H/32] uint8 e8m0 scales.
+    MXFP4 path: as MXFP8, with w1 [E, 2H, D/2] and w2 [E, D, H/2] packed e2m1
+    codes (moe_ffn_mxfp4_quantize); x stays e4m3.
     topk_ids int32 [T, k] (int64 is converted), topk_weights fp32 [T, k].
     events: optional 5 hipEvent_t handles (ints) recorded at the stage
     boundaries (moe_ffn_forward_events).
     """
-    mx = x.dtype == torch.uint8
     if topk_ids.dtype != torch.int32:
         topk_ids = topk_ids.to(torch.int32)
     T, D = x.shape
@@ -171,8 +180,7 @@ def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
     _check_cuda(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
-    dtype = "mxfp8" if mx else "bf16"
-    p = make_problem(T, D, H2 // 2, E, k, dtype, x_scale, w1_scale, w2_scale)
+    p = make_problem(T, D, H2 // 2, E, k, _data_path(x, w1), x_scale, w1_scale, w2_scale)
     lib = library()
     m = _mode(mode)
     if workspace is None:
@@ -218,7 +226,6 @@ def moe_ffn_forward_logits(x, w1, w2, logits, k, out=None, mode="auto", x_scale=
     """(out, topk_ids, topk_weights): the router on fp32 logits [T, E], then the pass
     (moe_ffn_forward_logits). Tensors as in moe_ffn_forward; ids/weights are
     written into `topk_ids` / `topk_weights` when given."""
-    mx = x.dtype == torch.uint8
     if logits.dtype != torch.float32:
         raise ValueError("logits must be float32")
     T, D = x.shape
@@ -233,7 +240,7 @@ def moe_ffn_forward_logits(x, w1, w2, logits, k, out=None, mode="auto", x_scale=
     if topk_weights is None:
         topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check_cuda(x, w1, w2, logits, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
-    p = make_problem(T, D, H2 // 2, E, k, "mxfp8" if mx else "bf16", x_scale, w1_scale, w2_scale)
+    p = make_problem(T, D, H2 // 2, E, k, _data_path(x, w1), x_scale, w1_scale, w2_scale)
     lib = library()
     m = _mode(mode)
     if workspace is None:
@@ -360,4 +367,21 @@ def moe_ffn_mx_quantize(src, stream=None):
                                        scales.data_ptr(), _stream(stream))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_mx_quantize")
+    return codes, scales
+
+
+def moe_ffn_mxfp4_quantize(src, stream=None):
+    """MXFP4 quantization along the last dim (expert weights): (packed e2m1 codes uint8 [..., K/2],
+    even index in the low nibble; scales uint8 [..., K/32])."""
+    if src.dtype != torch.float32:
+        raise ValueError("src must be float32")
+    _check_cuda(src)
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    codes = torch.empty(src.shape[:-1] + (K // 2,), dtype=torch.uint8, device=src.device)
+    scales = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
+    rc = library().moe_ffn_mxfp4_quantize(src.data_ptr(), rows, K, codes.data_ptr(),
+                                          scales.data_ptr(), _stream(stream))
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_mxfp4_quantize")
     return codes, scales

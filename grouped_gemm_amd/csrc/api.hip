@@ -19,7 +19,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_shape(const moe_ffn_problem* p) {
     if (!p) return MOE_FFN_EINVAL_PTR;
-    if (p->dtype != MOE_FFN_BF16 && p->dtype != MOE_FFN_MXFP8) return MOE_FFN_EUNSUPPORTED;
+    if (p->dtype != MOE_FFN_BF16 && p->dtype != MOE_FFN_MXFP8 && p->dtype != MOE_FFN_MXFP4)
+        return MOE_FFN_EUNSUPPORTED;
     if (p->T < 0 || p->D < 1 || p->H < 1 || p->E < 1 || p->topk < 1) return MOE_FFN_EINVAL_SHAPE;
     if (p->D % 128 || p->H % 128) return MOE_FFN_EINVAL_SHAPE;
     if (p->E > kMaxExperts || p->topk > kMaxTopk || p->topk > p->E) return MOE_FFN_EINVAL_SHAPE;
@@ -40,6 +41,7 @@ constexpr int64_t kFusedMaxWeightBytes = int64_t(16) << 20;
 int resolve(const moe_ffn_problem* p, int mode) {
     if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
     if (p->dtype == MOE_FFN_MXFP8) return mode == MOE_FFN_FUSED ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
+    if (p->dtype == MOE_FFN_MXFP4) return mode == MOE_FFN_FUSED ? MOE_FFN_EUNSUPPORTED : MOE_FFN_SPLIT;
     if (mode != MOE_FFN_AUTO) return mode;
     const int64_t weight_bytes = int64_t(p->E) * 3 * p->H * p->D * 2;
     const bool small = static_cast<int64_t>(p->T) * p->topk <= kFusedMaxPairs && weight_bytes <= kFusedMaxWeightBytes;
@@ -97,7 +99,7 @@ Plan make_plan(const moe_ffn_problem* p, int mode) {
         const size_t act_elem = p->dtype == MOE_FFN_BF16 ? 2 : 1;
         pl.act = off;
         off = align_up(off + act_elem * static_cast<size_t>(P) * p->H);
-        if (p->dtype == MOE_FFN_MXFP8) {
+        if (p->dtype != MOE_FFN_BF16) {
             pl.act_s = off;
             off = align_up(off + static_cast<size_t>(P) * (p->H / 32));
         }
@@ -183,6 +185,17 @@ MOE_FFN_API int moe_ffn_mx_quantize(const float* src, int64_t rows, int32_t K, u
     if (!src || !codes || !scales || !aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 3u))
         return MOE_FFN_EINVAL_PTR;
     return moe::launch_mx_quantize(src, rows, K, codes, scales, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_FFN_OK
+               : MOE_FFN_EHIP;
+}
+
+MOE_FFN_API int moe_ffn_mxfp4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                                       void* stream) {
+    if (rows < 0 || K < 32 || K % 32) return MOE_FFN_EINVAL_SHAPE;
+    if (rows == 0) return MOE_FFN_OK;
+    if (!src || !codes || !scales || !aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 3u))
+        return MOE_FFN_EINVAL_PTR;
+    return moe::launch_mx4_quantize(src, rows, K, codes, scales, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_FFN_OK
                : MOE_FFN_EHIP;
 }
@@ -323,7 +336,7 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
     for (const void* q : ptrs)
         if (!q || !aligned16(q)) return MOE_FFN_EINVAL_PTR;
     if (sh && (!sh->w1 || !sh->w2 || !aligned16(sh->w1) || !aligned16(sh->w2))) return MOE_FFN_EINVAL_PTR;
-    if (p->dtype == MOE_FFN_MXFP8) {
+    if (p->dtype != MOE_FFN_BF16) {
         const void* sp[] = {p->x_scale, p->w1_scale, p->w2_scale};
         for (const void* q : sp)
             if (!q || (reinterpret_cast<uintptr_t>(q) & 3u)) return MOE_FFN_EINVAL_PTR;
@@ -407,6 +420,7 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
         a.wts = topk_weights;
         a.rv = rv;
         a.out = static_cast<uint16_t*>(out);
+        a.w4 = p->dtype == MOE_FFN_MXFP4;
         if (m == MOE_FFN_SPLIT) {
             a.act = at<uint8_t>(ws, pl.act);
             a.act_s = at<uint8_t>(ws, pl.act_s);

@@ -195,8 +195,12 @@ struct MxArgs {
     uint16_t* out;      // [T, D]
     int32_t* mtiles;    // big_gemm_workspace_bytes for the prefill GEMMs
     float* acc32;       // [T, D] fused only
+    bool w4;            // MXFP4 weights: w1, w2 packed e2m1 [E, 2H, D/2], [E, D, H/2]
 };
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
+// MXQ4: fp32 [rows, K] -> packed e2m1 codes [rows, K/2] + e8m0 [rows, K/32].
+hipError_t launch_mx4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s);
 // Fused MX pipeline: GEMM1, SwiGLU and the act requantization in LDS, then a
 // split-K down projection over each 64-wide H slice into acc32 (fp32
 // atomics), then the conversion to bf16; `ev` (nullable) gets 3 events.

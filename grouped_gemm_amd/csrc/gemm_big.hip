@@ -890,7 +890,7 @@ hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
 // a tile takes an even number of K stages of 128 codes (D and H multiples of 256).
 bool big_mx_supported(const MxArgs& a) {
     const int64_t lim = int64_t(1) << 32;
-    return a.mtiles != nullptr && a.P >= kBigTile256MinRows * a.E && a.D % 256 == 0 && a.H % 256 == 0 &&
+    return !a.w4 && a.mtiles != nullptr && a.P >= kBigTile256MinRows * a.E && a.D % 256 == 0 && a.H % 256 == 0 &&
            int64_t(a.T) * a.D < lim && a.P * a.H < lim && a.P * 4 < lim && int64_t(a.E) * 2 * a.H * a.D < lim;
 }
 

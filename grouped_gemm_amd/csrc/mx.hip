@@ -57,27 +57,61 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float* __restric
     }
 }
 
+// MXQ4 quantizer (packed e2m1 codes, even index in the low nibble): 8 lanes
+// per 32-element block, 4 values (2 bytes) per lane.
+__global__ __launch_bounds__(256) void mx4_quantize_kernel(const float* __restrict__ src, int64_t nblk,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+    const int sub = threadIdx.x & 7;
+    for (int64_t b = (blockIdx.x * 256ll + threadIdx.x) >> 3; b < nblk;
+         b += (static_cast<int64_t>(gridDim.x) * 256) >> 3) {
+        const float4 v = *reinterpret_cast<const float4*>(src + b * 32 + sub * 4);
+        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+        const int s = mx4_scale_exp(amax);
+        const float inv = pow2f(-s);
+        const uint32_t c = e2m1_encode(v.x * inv, v.x) | (e2m1_encode(v.y * inv, v.y) << 4) |
+                           (e2m1_encode(v.z * inv, v.z) << 8) | (e2m1_encode(v.w * inv, v.w) << 12);
+        *reinterpret_cast<uint16_t*>(codes + b * 16 + sub * 2) = static_cast<uint16_t>(c);
+        if (sub == 0) scales[b] = static_cast<uint8_t>(s + 127);
+    }
+}
+
 // ---------------- block-scaled grouped GEMM main loop ----------------
 // acc[mi][nj] += A . B^T with e8m0 scales. aptr/bptr: this thread's 16-byte
 // chunk of stage 0 for each of its rows; asp/bsp: per (wave block, lane) the
 // scale row of that lane's A row / B row (K/32 bytes per row).
-template <int BM, int BN>
+//
+// W4: B holds MXFP4 weights, packed e2m1 codes (64 bytes per row per stage
+// of 128 K values; staged rows of 64 bytes with their four 16-byte chunks
+// swizzled by ((row >> 2) & 3)). For an e2m1 operand the scaled MFMA takes
+// 32 contiguous values per lane: lane group g holds k = 32g..32g+31 of the
+// 64-wide step, 16 bytes (measured on gfx950 with an in-bounds probe).
+template <int BM, int BN, bool W4 = false>
 struct MxTile {
     static constexpr int WM = BM / 2, WN = BN / 2;
     static constexpr int MB = WM / 32, NB = WN / 32;
+    static constexpr int BRB = W4 ? BKB / 2 : BKB;  // B bytes per row per stage
     static constexpr int A_CH = BM * 8 / kThreads;
-    static constexpr int B_CH = BN * 8 / kThreads;
-    static constexpr int STAGE = (BM + BN) * BKB;  // bytes
+    static constexpr int B_CH = BN * (BRB / 16) / kThreads;
+    static constexpr int STAGE = BM * BKB + BN * BRB;  // bytes
 };
 
-template <int BM, int BN>
+// 64-byte staged rows, 16-byte chunk c of row r at (c ^ ((r >> 2) & 3)): the 16
+// rows a fragment read touches fall in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+template <int BM, int BN, bool W4>
 __device__ __forceinline__ void mx_mainloop(uint8_t* lds, const uint8_t* const* aptr, const uint8_t* const* bptr,
                                             const uint8_t* const* asp, const uint8_t* const* bsp, int KT,
                                             const int* brow,
-                                            f32x16_t (&acc)[MxTile<BM, BN>::MB][MxTile<BM, BN>::NB]) {
-    using C = MxTile<BM, BN>;
+                                            f32x16_t (&acc)[MxTile<BM, BN, W4>::MB][MxTile<BM, BN, W4>::NB]) {
+    using C = MxTile<BM, BN, W4>;
     const int tid = threadIdx.x, lane = tid & 63, wm = (tid >> 6) >> 1;
     const int c16 = tid & 7, r16 = tid >> 3;
+    const int c4 = tid & 3, r4 = tid >> 2;  // W4: chunk and row of this thread's B loads
     u32x4_t ra[C::A_CH], rb[C::B_CH];
     uint32_t sa[C::MB], sb[C::NB];  // 4 scale bytes (blocks of this stage) per lane row
     uint32_t na[C::MB], nb[C::NB];
@@ -85,7 +119,7 @@ __device__ __forceinline__ void mx_mainloop(uint8_t* lds, const uint8_t* const* 
 #pragma unroll
         for (int q = 0; q < C::A_CH; ++q) ra[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + kt * BKB);
 #pragma unroll
-        for (int q = 0; q < C::B_CH; ++q) rb[q] = *reinterpret_cast<const u32x4_t*>(bptr[q] + kt * BKB);
+        for (int q = 0; q < C::B_CH; ++q) rb[q] = *reinterpret_cast<const u32x4_t*>(bptr[q] + kt * C::BRB);
 #pragma unroll
         for (int mi = 0; mi < C::MB; ++mi) na[mi] = *reinterpret_cast<const uint32_t*>(asp[mi] + kt * 4);
 #pragma unroll
@@ -97,7 +131,10 @@ __device__ __forceinline__ void mx_mainloop(uint8_t* lds, const uint8_t* const* 
 #pragma unroll
         for (int q = 0; q < C::A_CH; ++q) *reinterpret_cast<u32x4_t*>(sA + swz(r16 + 32 * q, c16)) = ra[q];
 #pragma unroll
-        for (int q = 0; q < C::B_CH; ++q) *reinterpret_cast<u32x4_t*>(sB + swz(r16 + 32 * q, c16)) = rb[q];
+        for (int q = 0; q < C::B_CH; ++q) {
+            if constexpr (W4) *reinterpret_cast<u32x4_t*>(sB + swz64(r4 + 64 * q, c4)) = rb[q];
+            else *reinterpret_cast<u32x4_t*>(sB + swz(r16 + 32 * q, c16)) = rb[q];
+        }
     };
     gload(0);
     sstore(0);
@@ -126,16 +163,22 @@ __device__ __forceinline__ void mx_mainloop(uint8_t* lds, const uint8_t* const* 
 #pragma unroll
             for (int nj = 0; nj < C::NB; ++nj) {
                 const int r = brow[nj] + (lane & 31);
-                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sB + swz(r, ch0));
-                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sB + swz(r, ch1));
-                bfr[nj] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if constexpr (W4) {
+                    // e2m1: 16 bytes, chunk 2kk + g of the 64-byte row (the upper half of the operand is unused)
+                    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sB + swz64(r, 2 * kk + (lane >> 5)));
+                    bfr[nj] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+                } else {
+                    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sB + swz(r, ch0));
+                    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sB + swz(r, ch1));
+                    bfr[nj] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                }
             }
 #pragma unroll
             for (int mi = 0; mi < C::MB; ++mi)
 #pragma unroll
                 for (int nj = 0; nj < C::NB; ++nj)
                     acc[mi][nj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[mi], bfr[nj], acc[mi][nj], 0, 0, 0, static_cast<int>((sa[mi] >> sh) & 0xffu), 0,
+                        af[mi], bfr[nj], acc[mi][nj], 0, W4 ? 4 : 0, 0, static_cast<int>((sa[mi] >> sh) & 0xffu), 0,
                         static_cast<int>((sb[nj] >> sh) & 0xffu));
         }
         if (kt + 1 < KT) sstore((kt + 1) & 1);
@@ -148,9 +191,10 @@ __device__ __forceinline__ void mx_mainloop(uint8_t* lds, const uint8_t* const* 
 }
 
 // ---------------- MX GEMM1 + SwiGLU + requant ----------------
-template <int BM, int BN>
+// W4: w1 is packed e2m1 [E, 2H, D/2] (MXFP4 weights).
+template <int BM, int BN, bool W4>
 __global__ __launch_bounds__(kThreads) void mx_gemm1_kernel(MxArgs a) {
-    using C = MxTile<BM, BN>;
+    using C = MxTile<BM, BN, W4>;
     static_assert(C::NB % 2 == 0, "gate and up need the same number of blocks");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
     __shared__ int32_t sTok[BM];
@@ -170,8 +214,10 @@ __global__ __launch_bounds__(kThreads) void mx_gemm1_kernel(MxArgs a) {
     for (int q = 0; q < C::A_CH; ++q) aptr[q] = a.x + static_cast<int64_t>(sTok[r16 + 32 * q]) * a.D + c16 * 16;
     const int64_t w1row0 = static_cast<int64_t>(mt.expert) * 2 * a.H;
     auto w1row = [&](int r) { return w1row0 + (r < BH ? h0 + r : a.H + h0 + (r - BH)); };
+    const int c4 = tid & 3, r4 = tid >> 2;
 #pragma unroll
-    for (int q = 0; q < C::B_CH; ++q) bptr[q] = a.w1 + w1row(r16 + 32 * q) * a.D + c16 * 16;
+    for (int q = 0; q < C::B_CH; ++q)
+        bptr[q] = W4 ? a.w1 + w1row(r4 + 64 * q) * (a.D / 2) + c4 * 16 : a.w1 + w1row(r16 + 32 * q) * a.D + c16 * 16;
     int brow[C::NB];
 #pragma unroll
     for (int nj = 0; nj < C::NB; ++nj)
@@ -189,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm1_kernel(MxArgs a) {
     for (int mi = 0; mi < C::MB; ++mi)
 #pragma unroll
         for (int nj = 0; nj < C::NB; ++nj) acc[mi][nj] = f32x16_t{};
-    mx_mainloop<BM, BN>(lds, aptr, bptr, asp, bsp, a.D / BKB, brow, acc);
+    mx_mainloop<BM, BN, W4>(lds, aptr, bptr, asp, bsp, a.D / BKB, brow, acc);
 
     // SwiGLU in fp32 -> LDS [BM][BH + 4] floats -> requant per 32 along H.
     constexpr int OS = BN / 2 + 4;
@@ -230,9 +276,10 @@ __global__ __launch_bounds__(kThreads) void mx_gemm1_kernel(MxArgs a) {
 }
 
 // ---------------- MX GEMM2 + routing weight ----------------
-template <int BM, int BN>
+// W4: w2 is packed e2m1 [E, D, H/2] (MXFP4 weights).
+template <int BM, int BN, bool W4>
 __global__ __launch_bounds__(kThreads) void mx_gemm2_kernel(MxArgs a) {
-    using C = MxTile<BM, BN>;
+    using C = MxTile<BM, BN, W4>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
     __shared__ int32_t sPair[BM];
     __shared__ float sW[BM];
@@ -254,8 +301,10 @@ __global__ __launch_bounds__(kThreads) void mx_gemm2_kernel(MxArgs a) {
 #pragma unroll
     for (int q = 0; q < C::A_CH; ++q) aptr[q] = a.act + arow(r16 + 32 * q) * a.H + c16 * 16;
     const int64_t w2row0 = static_cast<int64_t>(mt.expert) * a.D + n0;
+    const int c4 = tid & 3, r4 = tid >> 2;
 #pragma unroll
-    for (int q = 0; q < C::B_CH; ++q) bptr[q] = a.w2 + (w2row0 + r16 + 32 * q) * a.H + c16 * 16;
+    for (int q = 0; q < C::B_CH; ++q)
+        bptr[q] = W4 ? a.w2 + (w2row0 + r4 + 64 * q) * (a.H / 2) + c4 * 16 : a.w2 + (w2row0 + r16 + 32 * q) * a.H + c16 * 16;
     int brow[C::NB];
 #pragma unroll
     for (int nj = 0; nj < C::NB; ++nj) brow[nj] = wn * C::WN + 32 * nj;
@@ -271,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm2_kernel(MxArgs a) {
     for (int mi = 0; mi < C::MB; ++mi)
 #pragma unroll
         for (int nj = 0; nj < C::NB; ++nj) acc[mi][nj] = f32x16_t{};
-    mx_mainloop<BM, BN>(lds, aptr, bptr, asp, bsp, a.H / BKB, brow, acc);
+    mx_mainloop<BM, BN, W4>(lds, aptr, bptr, asp, bsp, a.H / BKB, brow, acc);
 
     constexpr int OS = BN + 8;
     uint16_t* sO = reinterpret_cast<uint16_t*>(lds);
@@ -304,11 +353,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm2_kernel(MxArgs a) {
 // ("Prime Flash MoE", section 7: the fused MX path quantizes act in the
 // epilogue and runs the down projection split over H).
 constexpr int kFusedSlice = 64;        // act columns per workgroup (one scaled-MFMA K step)
-constexpr int kFusedRowBytes = 64;     // act / W2 slice row in LDS: 64 codes, four 16-byte chunks
-
-// 64-byte rows, 16-byte chunk c of row r at (c ^ ((r >> 2) & 3)): the 16 rows
-// a fragment read touches fall in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz64(int row, int chunk) { return row * kFusedRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
+constexpr int kFusedRowBytes = 64;     // act / W2 slice row in LDS: 64 codes, four 16-byte chunks (swz64)
 
 // 32 codes of one row for the scaled MFMA: chunks g and g + 2 of the row
 // (k = 16g..16g+15 and 32+16g..32+16g+15), g = lane >> 5.
@@ -372,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void mx_fused_kernel(MxArgs a) {
         for (int mi = 0; mi < C::MB; ++mi)
 #pragma unroll
             for (int nj = 0; nj < C::NB; ++nj) acc[mi][nj] = f32x16_t{};
-        mx_mainloop<BM, BN>(lds, aptr, bptr, asp, bsp, a.D / BKB, brow, acc);
+        mx_mainloop<BM, BN, false>(lds, aptr, bptr, asp, bsp, a.D / BKB, brow, acc);
 
         // SwiGLU in fp32 into the (now idle) stage buffers
         float* sO = reinterpret_cast<float*>(lds);
@@ -509,22 +554,28 @@ hipError_t launch_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t
     return hipGetLastError();
 }
 
+hipError_t launch_mx4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s) {
+    const int64_t nblk = rows * (K / 32);
+    if (nblk == 0) return hipSuccess;
+    int64_t g = (nblk * 8 + 255) / 256;
+    if (g > 8192) g = 8192;
+    mx4_quantize_kernel<<<static_cast<int>(g), 256, 0, s>>>(src, nblk, codes, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BN1 = 128, BN2 = 128;
     const bool big = big_mx_supported(a);
-    if (big) {
-        launch_big_mx(a, true, s);
-    } else {
-        dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
-        mx_gemm1_kernel<BM, BN1><<<g1, kThreads, 0, s>>>(a);
-    }
+    const dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
+    const dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
+    if (big) launch_big_mx(a, true, s);
+    else if (a.w4) mx_gemm1_kernel<BM, BN1, true><<<g1, kThreads, 0, s>>>(a);
+    else mx_gemm1_kernel<BM, BN1, false><<<g1, kThreads, 0, s>>>(a);
     record(ev, 0, s);
-    if (big) {
-        launch_big_mx(a, false, s);
-    } else {
-        dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
-        mx_gemm2_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
-    }
+    if (big) launch_big_mx(a, false, s);
+    else if (a.w4) mx_gemm2_kernel<BM, BN2, true><<<g2, kThreads, 0, s>>>(a);
+    else mx_gemm2_kernel<BM, BN2, false><<<g2, kThreads, 0, s>>>(a);
     record(ev, 1, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -48,4 +48,36 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v, float sign_src) {
     return sign | code;
 }
 
+// MXFP4 weights ("GC-MoE on SM120", scale formats: a 4-bit E2M1 code with a
+// shared UE8M0 exponent per 32 contiguous elements). e2m1: 1 sign bit, 2
+// exponent bits (bias 1), 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6. Scale rule MXQ4, the MX-fp8 rule with 6 in place of 448: s = the
+// smallest integer with amax <= 6 * 2^s, clamped to [-127, 127]; codes
+// e2m1(v * 2^-s), nearest with ties to the even code, saturating at 6.
+
+// MXQ4 scale exponent from the block's amax (finite, >= 0): amax = 1.m * 2^E
+// needs s = E - 2 while 1.m <= 1.5, else E - 1.
+__device__ __forceinline__ int mx4_scale_exp(float amax) {
+    const uint32_t u = __float_as_uint(amax);
+    const int ef = static_cast<int>(u >> 23);
+    if (ef == 0) return -127;  // zero or below 2^-126: the clamp decides
+    int s = ef - 129 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+    return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// e2m1 code of v (already divided by the block scale). On [0, 2] the values
+// are the multiples of 0.5 (code = 2x), on [2, 4] of 1 (code = x + 2), on
+// [4, 6] of 2 (code = x/2 + 4); rintf rounds ties to even, and on each
+// piece an even integer is an even code. The sign comes from `sign_src`.
+__device__ __forceinline__ uint32_t e2m1_encode(float v, float sign_src) {
+    const uint32_t sign = (__float_as_uint(sign_src) >> 28) & 0x8u;
+    const float x = fabsf(v);
+    uint32_t code;
+    if (x < 2.0f) code = static_cast<uint32_t>(rintf(x * 2.0f));
+    else if (x < 4.0f) code = static_cast<uint32_t>(rintf(x)) + 2u;
+    else if (x < 6.0f) code = static_cast<uint32_t>(rintf(x * 0.5f)) + 4u;
+    else code = 7u;
+    return sign | code;
+}
+
 }  // namespace moe

@@ -40,8 +40,13 @@ extern "C" {
 #define MOE_FFN_API __attribute__((visibility("default")))
 
 /* Data paths (Prime Flash MoE: "two data paths, one for bf16 and one for
- * MXFP8", introduction). */
-enum { MOE_FFN_BF16 = 0, MOE_FFN_MXFP8 = 1 };
+ * MXFP8", introduction). MOE_FFN_MXFP4 is the MXFP4-weight path of
+ * "GC-MoE on SM120" (scale formats): expert weights as 4-bit E2M1 codes
+ * with a shared UE8M0 exponent per 32 contiguous elements along K, two
+ * codes per byte with the even K index in the low nibble; x and the
+ * activation stay MX-fp8 (e4m3 codes, e8m0 scales) as in MOE_FFN_MXFP8.
+ * SPLIT (and AUTO) only. */
+enum { MOE_FFN_BF16 = 0, MOE_FFN_MXFP8 = 1, MOE_FFN_MXFP4 = 2 };
 
 /* Pipelines (same page, introduction and section 6): FUSED runs GEMM1,
  * SwiGLU and GEMM2 in one kernel and never writes the activation; the down
@@ -62,8 +67,8 @@ enum {
 
 /* Problem descriptor (plain C; every pointer is caller-owned).
  *   T, D, H, E, topk : tokens, hidden dim, FFN intermediate dim, experts, k.
- *   dtype            : MOE_FFN_BF16 or MOE_FFN_MXFP8.
- *   x_scale, w1_scale, w2_scale : MXFP8 only (NULL for bf16). e8m0 bytes
+ *   dtype            : MOE_FFN_BF16, MOE_FFN_MXFP8 or MOE_FFN_MXFP4.
+ *   x_scale, w1_scale, w2_scale : MXFP8 and MXFP4 (NULL for bf16). e8m0 bytes
  *                      (value 2^(byte-127)), one per 32 contiguous elements
  *                      along the contraction dim (Prime Flash MoE, section
  *                      7): x_scale [T, D/32], w1_scale [E, 2H, D/32],
@@ -94,10 +99,12 @@ MOE_FFN_API int moe_ffn_validate(const moe_ffn_problem* p, int mode);
 MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode);
 
 /* The forward pass.
- *   x            : bf16 [T, D], or e4m3 codes [T, D] for MXFP8.
+ *   x            : bf16 [T, D], or e4m3 codes [T, D] for MXFP8 and MXFP4.
  *   w1           : bf16 [E, 2H, D] (gate rows then up rows per expert), or
- *                  e4m3 codes for MXFP8.
- *   w2           : bf16 [E, D, H], or e4m3 codes for MXFP8.
+ *                  e4m3 codes for MXFP8, or packed e2m1 codes [E, 2H, D/2]
+ *                  for MXFP4.
+ *   w2           : bf16 [E, D, H], or e4m3 codes for MXFP8, or packed e2m1
+ *                  codes [E, D, H/2] for MXFP4.
  *   topk_ids     : int32 [T, topk]; an id outside [0, E) is a dropped route
  *                  that contributes nothing.
  *   topk_weights : fp32 [T, topk], used as given (not renormalized).
@@ -237,6 +244,21 @@ MOE_FFN_API int moe_ffn_route(const int32_t* topk_ids, int32_t T, int32_t topk, 
  * The same rule requantizes the SwiGLU output inside the MXFP8 pass. */
 MOE_FFN_API int moe_ffn_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes,
                                     uint8_t* scales, void* stream);
+
+/* MXFP4 quantization of fp32 rows along the last dim, for expert weights
+ * ("GC-MoE on SM120", scale formats: E2M1 codes with a UE8M0 exponent per
+ * 32 contiguous elements). The pages give no fp4 scale rule; this reads the
+ * MX-fp8 rule above with E2M1's largest magnitude 6 in place of 448:
+ * s = the smallest integer with amax <= 6 * 2^s, clamped to [-127, 127]
+ * (-127 for an all-zero block); codes = e2m1(v * 2^-s), nearest value with
+ * ties to the even code, saturating at +-6.
+ *   src    : fp32 [rows, K], K a multiple of 32, 16-byte aligned.
+ *   codes  : uint8 [rows, K/2], two codes per byte, even K index in the low
+ *            nibble, 4-byte aligned.
+ *   scales : uint8 [rows, K/32].
+ * Asynchronous on `stream`; MOE_FFN_EINVAL_SHAPE / _PTR on bad arguments. */
+MOE_FFN_API int moe_ffn_mxfp4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes,
+                                       uint8_t* scales, void* stream);
 
 /* A static string naming `code`. */
 MOE_FFN_API const char* moe_ffn_strerror(int code);

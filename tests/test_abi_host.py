@@ -17,7 +17,8 @@ def test_library_exports_every_header_function():
         "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_forward",
         "moe_ffn_forward_events", "moe_ffn_router", "moe_ffn_forward_logits",
         "moe_ffn_shared_workspace_bytes", "moe_ffn_forward_shared", "moe_ffn_forward_act",
-        "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_strerror"}
+        "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_mxfp4_quantize",
+        "moe_ffn_strerror"}
 
 
 @pytest.mark.parametrize("shape,expect", [
@@ -38,6 +39,12 @@ def test_validate_shapes(shape, expect):
 
 def test_validate_dtype_and_mode():
     assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype=7) == g.MOE_FFN_EUNSUPPORTED
+    # MXFP4 weights: split (AUTO resolves to it), no fused pipeline; workspace as for MX-fp8
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp4", mode="split") == g.MOE_FFN_OK
+    assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp4", mode="fused") == g.MOE_FFN_EUNSUPPORTED
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, dtype="mxfp4") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_workspace_bytes(64, 256, 512, 8, 2, "mxfp4", "split") == \
+        g.moe_ffn_workspace_bytes(64, 256, 512, 8, 2, "mxfp8", "split")
     assert g.moe_ffn_validate(64, 256, 512, 8, 2, mode=5) == g.MOE_FFN_EUNSUPPORTED
     assert g.moe_ffn_validate(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == g.MOE_FFN_OK
     assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, dtype="mxfp8", mode="auto") == g.MOE_FFN_SPLIT
@@ -94,6 +101,13 @@ def test_forward_rejects_bad_arguments_without_gpu_work():
     assert lib.moe_ffn_forward(ctypes.byref(p0), None, None, None, None, None, None, 2, None) == g.MOE_FFN_OK
     assert lib.moe_ffn_mx_quantize(None, 4, 48, None, None, None) == g.MOE_FFN_EINVAL_SHAPE
     assert lib.moe_ffn_mx_quantize(None, 4, 64, None, None, None) == g.MOE_FFN_EINVAL_PTR
+    assert lib.moe_ffn_mxfp4_quantize(None, 4, 48, None, None, None) == g.MOE_FFN_EINVAL_SHAPE
+    assert lib.moe_ffn_mxfp4_quantize(None, 4, 64, None, None, None) == g.MOE_FFN_EINVAL_PTR
+    assert lib.moe_ffn_mxfp4_quantize(None, 0, 64, None, None, None) == g.MOE_FFN_OK
+    # MXFP4 path without scales, and in the fused pipeline
+    p4 = g.make_problem(64, 256, 512, 8, 2, dtype="mxfp4")
+    assert lib.moe_ffn_forward(ctypes.byref(p4), ok, ok, ok, ok, ok, ok, 2, None) == g.MOE_FFN_EINVAL_PTR
+    assert lib.moe_ffn_forward(ctypes.byref(p4), ok, ok, ok, ok, ok, ok, 1, None) == g.MOE_FFN_EUNSUPPORTED
 
 
 def test_strerror():
