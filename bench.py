@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE FFN fwd TFLOP/s + routed tokens/s; % of MFMA peak (prefill), % HBM BW (decode)"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+# MXFP4 weights meet MX-fp8 activations in the scaled MFMA, which then runs at the fp8 rate.
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 5000.0}
 STAGES = {"split": ["route", "gemm1_swiglu", "gemm2_weight", "combine"],
           "fused": ["route", "acc_fill", "fused_ffn", "acc_to_bf16"]}
 
@@ -69,6 +70,9 @@ def parse_args(argv=None):
     ap.add_argument("--shared-ffn", type=int, default=0, metavar="HS",
                     help="add one shared expert of intermediate size HS on every token "
                          "(moe_ffn_forward_shared; bf16 only)")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="MXFP4 expert weights (e2m1 codes, e8m0 scale per 32; moe_ffn_mxfp4_quantize) "
+                         "with MX-fp8 x and activations, on the chosen workload's dims")
     ap.add_argument("--logits", action="store_true",
                     help="start each step from router logits (moe_ffn_forward_logits): the router's "
                          "softmax/top-k runs inside the timed pass, fused with the route step")
@@ -83,10 +87,11 @@ def hit_experts(ids: np.ndarray, E: int) -> int:
 def kernel_work(cfg, mode, hit, dtype):
     """Algorithmic bytes and flops per launch of each stage's kernel."""
     T, D, H, P = cfg.T, cfg.D, cfg.H, cfg.P
-    e = 1 if dtype == "mxfp8" else 2                     # bytes per element of x, W, act
-    sc = (1.0 / 32) if dtype == "mxfp8" else 0.0         # e8m0 bytes per element
-    w1 = hit * 2 * H * D * (e + sc)
-    w2 = hit * D * H * (e + sc)
+    e = 2 if dtype == "bf16" else 1                      # bytes per element of x and act
+    we = {"bf16": 2, "mxfp8": 1, "mxfp4": 0.5}[dtype]    # bytes per weight element
+    sc = 0.0 if dtype == "bf16" else 1.0 / 32            # e8m0 bytes per element
+    w1 = hit * 2 * H * D * (we + sc)
+    w2 = hit * D * H * (we + sc)
     x = T * D * (e + sc)
     act = P * H * (e + sc)
     if mode == "split":
@@ -135,6 +140,8 @@ def kernel_symbol(cfg, mode, stage):
     if stage == "combine":
         return "combine_kernel"
     g1 = stage == "gemm1_swiglu"
+    if cfg.dtype == "mxfp4":
+        return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.dtype == "mxfp8":
         if cfg.P >= 512 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
@@ -170,6 +177,9 @@ def cpu_baseline(cfg, inputs, dtype, target_s):
         if dtype == "bf16":
             oracle.forward_bf16(inputs["x"], inputs["w1"], inputs["w2"], inputs["topk_ids"],
                                 inputs["topk_weights"], tokens=tok, shared=inputs.get("shared"))
+        elif dtype == "mxfp4":
+            oracle.forward_mx4(*inputs["xq"], *inputs["w1q"], *inputs["w2q"], inputs["topk_ids"],
+                               inputs["topk_weights"], tokens=tok)
         else:
             oracle.forward_mx(*inputs["xq"], *inputs["w1q"], *inputs["w2q"], inputs["topk_ids"],
                               inputs["topk_weights"], tokens=tok)
@@ -201,6 +211,8 @@ def main(argv=None):
     if args.tokens:
         cfg = mi.custom(args.tokens, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, cfg.dtype, cid=cfg.cid,
                         name=f"{cfg.name}_T{args.tokens}")
+    if args.mxfp4:
+        cfg = mi.custom(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, "mxfp4", cid=cfg.cid, name=cfg.name)
     dtype = cfg.dtype
     dev = torch.device("cuda:0")
     log(f"[bench] generating {cfg.name} inputs (seeded)")
@@ -217,7 +229,8 @@ def main(argv=None):
         host.update(topk_ids=s["topk_ids"], topk_weights=s["topk_weights"])
         q = {}
         for n in ("x", "w1", "w2"):
-            q[n] = g.moe_ffn_mx_quantize(torch.from_numpy(s[n]).to(dev))
+            quant = g.moe_ffn_mxfp4_quantize if (dtype == "mxfp4" and n != "x") else g.moe_ffn_mx_quantize
+            q[n] = quant(torch.from_numpy(s[n]).to(dev))
         torch.cuda.synchronize()
         x, w1, w2 = q["x"][0], q["w1"][0], q["w2"][0]
         scales = dict(x_scale=q["x"][1], w1_scale=q["w1"][1], w2_scale=q["w2"][1])
@@ -336,7 +349,7 @@ def main(argv=None):
 
     flops = cfg.flops + (6.0 * cfg.T * cfg.D * args.shared_ffn if shared is not None else 0.0)
     tflops = flops / (ms * 1e-3) / 1e12
-    all_bytes = hit * 3 * cfg.H * cfg.D * (1 if dtype == "mxfp8" else 2) + 2 * cfg.T * cfg.D * 2
+    all_bytes = hit * 3 * cfg.H * cfg.D * {"bf16": 2, "mxfp8": 1, "mxfp4": 0.5}[dtype] + 2 * cfg.T * cfg.D * 2
     result = {
         "metric": METRIC,
         "value": tflops,
@@ -348,7 +361,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if dtype == "mxfp8" else "bf16",
+        "dtype": dtype,
         "data": "synthetic (seeded; routing, x and random-init expert weights of the stated shape)",
         "config": {"workload": workload, "mode": mode, "tokens": cfg.T, "experts": cfg.E,
                    "topk": cfg.k, "hidden": cfg.D, "ffn": cfg.H, "experts_hit": hit,

@@ -57,7 +57,7 @@ class Config:
     E: int
     k: int
     routing: str          # "softmax" | "uniform" | "zipf"
-    dtype: str = "bf16"   # "bf16" | "mxfp8"
+    dtype: str = "bf16"   # "bf16" | "mxfp8" | "mxfp4" (fp4 weights, MX-fp8 activations)
     zipf_s: float = 1.1
 
     @property
