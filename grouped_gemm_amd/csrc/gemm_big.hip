@@ -89,6 +89,7 @@ struct BigArgs {
     uint16_t* ypair;
     uint8_t* sink;  // kSinkBytes
     ActVariant av;  // bf16 only; zero: the plain SwiGLU
+    bool w4;        // MX: the weights are MXFP4 (packed e2m1, half the bytes per row)
 };
 
 template <bool MX>
@@ -103,6 +104,7 @@ struct Big {
     static constexpr int NT = TB / 32;        // token blocks per wave
     static constexpr int A_INS = BM / 8 / W;  // token-row DMA instructions per wave per stage (8 rows each)
     static constexpr int B_INS = BN / 8 / W;  // weight-row DMA instructions per wave per stage
+    static constexpr int B_INS4 = BN / 16 / W; // the same for MXFP4 weights (64-byte rows: 16 rows each)
     static constexpr int PW = BM / 64;        // waves that move one BM-entry int/float vector (64 per wave)
     static_assert(NT >= 1 && A_INS >= 1 && A_INS * 8 * W == BM && B_INS * 8 * W == BN, "tile split");
     static_assert(B_INS % 2 == 0, "weight-row offsets alternate with the instruction's parity");
@@ -276,16 +278,27 @@ __device__ __forceinline__ void read_q(const uint8_t* tok, const uint8_t* wt, co
 // MX reads of K half H: weight fragments 2P, 2P + 1 with their scale bytes
 // (32-block 2H + g of the stage: byte 2H + g of the row's scale dword), or
 // the token fragments with theirs.
-template <int BM, bool GEMM1, int H, int P>
+// W4: the weights are MXFP4, staged as 64-byte rows (128 e2m1 codes) with
+// their four 16-byte chunks swizzled by ((row >> 2) & 3); the e2m1 operand
+// takes 16 contiguous bytes per lane, K values 32g..32g+31 of the 64-wide
+// step (chunk 2H + g), and the upper half of the operand is unused.
+template <int BM, bool GEMM1, int H, int P, bool W4>
 __device__ __forceinline__ void read_w_mx(const uint8_t* wt, const ScaleSlot<BM>& sc, const LaneOff& o,
                                           Frag<BM, true>& f) {
     const int g = (threadIdx.x & 63) >> 5;
     const int lo = o.c0 ^ (H << 6), hi = lo ^ 32;
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(sc.wt) + (o.w >> 5) + g;  // byte g of the row's dword
+    // W4: row (o.w / 128) at (o.w / 2), chunk (2H + g) ^ ((row >> 2) & 3)
+    const int c4 = ((2 * H + g) ^ (((threadIdx.x & 31) >> 2) & 3)) << 4;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int fr = frow_const<GEMM1>(2 * P + i);
-        f.w[i] = frag32(wt + o.w + fr * RB, lo, hi);
+        if constexpr (W4) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wt + (o.w >> 1) + fr * 64 + c4);
+            f.w[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        } else {
+            f.w[i] = frag32(wt + o.w + fr * RB, lo, hi);
+        }
         f.sw[i] = sb[fr * 4 + 2 * H];
     }
 }
@@ -326,15 +339,15 @@ __device__ __forceinline__ void mfma_half(const Frag<BM, false>& f, f32x16_t (&a
 }
 
 // MFMAs of weight fragments 2P, 2P + 1 against the token fragments
-template <int BM, int P>
+template <int BM, int P, bool W4>
 __device__ __forceinline__ void mfma_mx(const Frag<BM, true>& f, const TokFrag<BM>& tf,
                                         f32x16_t (&acc)[4][Big<BM, true>::NT]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int t = 0; t < Big<BM, true>::NT; ++t)
-            acc[2 * P + i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[i], tf.t[t], acc[2 * P + i][t], 0,
-                                                                                0, 0, f.sw[i], 0, tf.st[t]);
+            acc[2 * P + i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f.w[i], tf.t[t], acc[2 * P + i][t], W4 ? 4 : 0, 0, 0, f.sw[i], 0, tf.st[t]);
     pin_acc(acc, 2 * P, 2 * P + 2);
 }
 
@@ -397,11 +410,12 @@ __device__ __forceinline__ void dma_row_weights(const BigArgs& a, const int32_t*
 // Instruction j of a wave covers tile rows (wave * INS + j) * 8 + lane / 8;
 // lane i's 16 bytes land at chunk position i & 7 of that row, so it fetches
 // the global chunk that the swizzle puts there.
-template <int BM, bool GEMM1, bool MX>
+template <int BM, bool GEMM1, bool MX, bool W4>
 __device__ __forceinline__ void make_src(const BigArgs& a, const TileDesc& t, const int32_t* pairs, uint32_t wave,
                                          DmaSrc<BM, MX>& s) {
     using C = Big<BM, MX>;
     constexpr int EB = Fmt<MX>::EB;
+    const int64_t wrow = W4 ? (GEMM1 ? a.D : a.H) / 2 : (GEMM1 ? a.D : a.H) * EB;  // weight row bytes
     const int lane = fresh_lane();
     const int K = GEMM1 ? a.D : a.H;
     const int h0 = t.ntile * 128, n0 = t.ntile * 256;
@@ -417,9 +431,9 @@ __device__ __forceinline__ void make_src(const BigArgs& a, const TileDesc& t, co
     const int64_t e2h = static_cast<int64_t>(t.expert) * 2 * a.H;
     if (GEMM1) {
         const int grow0 = row0 < 128 ? h0 + row0 : a.H + h0 + row0 - 128;
-        s.bbase = uniform_ptr(a.w1 + (e2h + grow0) * K * EB);
+        s.bbase = uniform_ptr(a.w1 + (e2h + grow0) * wrow);
     } else {
-        s.bbase = uniform_ptr(a.w2 + (static_cast<int64_t>(t.expert) * a.D + n0 + row0) * K * EB);
+        s.bbase = uniform_ptr(a.w2 + (static_cast<int64_t>(t.expert) * a.D + n0 + row0) * wrow);
     }
     if constexpr (MX) {
         // scale rows: waves 0 .. BM/64 - 1 take the token rows, the rest the weight rows
@@ -447,23 +461,31 @@ __device__ __forceinline__ void make_src(const BigArgs& a, const TileDesc& t, co
     }
 }
 
-template <int BM, bool MX>
+template <int BM, bool MX, bool W4>
 __device__ __forceinline__ void issue_stage(uint8_t* tok, uint8_t* wt, ScaleSlot<BM>* sc, const DmaSrc<BM, MX>& src,
                                             const Ring<BM, MX>& r, int kt) {
     using C = Big<BM, MX>;
     const char* ab = src.abase + kt * RB;
-    const char* bb = src.bbase + kt * RB;
+    const char* bb = src.bbase + kt * (W4 ? 64 : RB);
     const uint32_t tl = lds_addr(tok) + r.wave * (C::A_INS * 1024);
-    const uint32_t wl = lds_addr(wt) + r.wave * (C::B_INS * 1024);
-    // weight row of instruction j: wave * 8 * B_INS + 8j + lane / 8; with
-    // B_INS even its swizzle term is 4 (j & 1) + lane / 16 (odd j: chunk ^ 4).
-    // The offset is recomputed here rather than kept: registers are scarce.
+    const uint32_t wl = lds_addr(wt) + r.wave * ((W4 ? C::B_INS4 : C::B_INS) * 1024);
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t boff = (lane / 8) * (r.bstride / 8) + (((lane & 7) ^ (lane >> 4)) << 4);
 #pragma unroll
     for (int j = 0; j < C::A_INS; ++j) dma16(ab, src.aoff[j], tl + j * 1024);
+    if constexpr (W4) {
+        // weight row of instruction j: wave * 32 + 16j + lane / 4, 64 bytes; its
+        // swizzle term ((row >> 2) & 3) is (lane >> 4) & 3 for every j.
+        const uint32_t boff = (lane / 4) * (r.bstride / 16) + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
 #pragma unroll
-    for (int j = 0; j < C::B_INS; ++j) dma16(bb, ((j & 1) ? boff ^ 64u : boff) + j * r.bstride, wl + j * 1024);
+        for (int j = 0; j < C::B_INS4; ++j) dma16(bb, boff + j * r.bstride, wl + j * 1024);
+    } else {
+        // weight row of instruction j: wave * 8 * B_INS + 8j + lane / 8; with
+        // B_INS even its swizzle term is 4 (j & 1) + lane / 16 (odd j: chunk ^ 4).
+        // The offset is recomputed here rather than kept: registers are scarce.
+        const uint32_t boff = (lane / 8) * (r.bstride / 8) + (((lane & 7) ^ (lane >> 4)) << 4);
+#pragma unroll
+        for (int j = 0; j < C::B_INS; ++j) dma16(bb, ((j & 1) ? boff ^ 64u : boff) + j * r.bstride, wl + j * 1024);
+    }
     if constexpr (MX) {
         const uint32_t sl = r.wave < static_cast<uint32_t>(BM / 64) ? lds_addr(sc->tok) + r.wave * 256
                                                                      : lds_addr(sc->wt) + (r.wave - BM / 64) * 256;
@@ -491,7 +513,7 @@ __device__ __forceinline__ void issue_stage(uint8_t* tok, uint8_t* wt, ScaleSlot
 // every later step waits for everything. Hand-over: step 0 fetches the next
 // tile's row map (landed by step 1's barrier), step 1 its routing weights,
 // and step KT - 1 builds its DMA sources and issues its stage 0.
-template <int BM, bool GEMM1, bool MX, bool VAR, int B, bool FIRST, bool SECOND>
+template <int BM, bool GEMM1, bool MX, bool VAR, bool W4, int B, bool FIRST, bool SECOND>
 __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, StageBufs<BM>& L, ScaleSlot<BM>* sc,
                                           int kt, int32_t (*pairs)[BM], float (*wrow)[BM], const LaneOff& o,
                                           Regs<BM, MX>& g, f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
@@ -507,12 +529,12 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
     if (FIRST && r.cont) dma_row_map<BM>(a, r.next.row0, pairs[r.nb], r.wave);
     if (SECOND && r.cont && (!GEMM1 || (VAR && a.av.wba))) dma_row_weights<BM>(a, pairs[r.nb], wrow[r.nb], r.wave);
     if (kt + 1 < r.KT) {
-        issue_stage<BM, MX>(L.tok[B ^ 1], L.wt[B ^ 1], osc, r.src, r, kt + 1);
+        issue_stage<BM, MX, W4>(L.tok[B ^ 1], L.wt[B ^ 1], osc, r.src, r, kt + 1);
     } else if (r.cont) {
         // the next tile's sources are built here, where they are used, so
         // they hold no registers through the tile's steps
-        make_src<BM, GEMM1, MX>(a, r.next, pairs[r.nb], r.wave, r.src);
-        issue_stage<BM, MX>(L.tok[B ^ 1], L.wt[B ^ 1], osc, r.src, r, 0);
+        make_src<BM, GEMM1, MX, W4>(a, r.next, pairs[r.nb], r.wave, r.src);
+        issue_stage<BM, MX, W4>(L.tok[B ^ 1], L.wt[B ^ 1], osc, r.src, r, 0);
     }
     if constexpr (!MX) {
         read_q<BM, GEMM1, 0>(ct, cw, o, g.x);
@@ -524,16 +546,16 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
         read_q<BM, GEMM1, 3>(ct, cw, o, g.y);
         mfma_half<BM>(g.x, acc);
     } else {
-        if (!FIRST) mfma_mx<BM, 1>(g.wb, g.t, acc);
+        if (!FIRST) mfma_mx<BM, 1, W4>(g.wb, g.t, acc);
         read_t_mx<BM, 0>(ct, csc, o, g.t);
-        read_w_mx<BM, GEMM1, 0, 0>(cw, csc, o, g.wa);
-        read_w_mx<BM, GEMM1, 0, 1>(cw, csc, o, g.wb);
-        mfma_mx<BM, 0>(g.wa, g.t, acc);
-        read_w_mx<BM, GEMM1, 1, 0>(cw, csc, o, g.wa);
-        mfma_mx<BM, 1>(g.wb, g.t, acc);
+        read_w_mx<BM, GEMM1, 0, 0, W4>(cw, csc, o, g.wa);
+        read_w_mx<BM, GEMM1, 0, 1, W4>(cw, csc, o, g.wb);
+        mfma_mx<BM, 0, W4>(g.wa, g.t, acc);
+        read_w_mx<BM, GEMM1, 1, 0, W4>(cw, csc, o, g.wa);
+        mfma_mx<BM, 1, W4>(g.wb, g.t, acc);
         read_t_mx<BM, 1>(ct, csc, o, g.t);
-        read_w_mx<BM, GEMM1, 1, 1>(cw, csc, o, g.wb);
-        mfma_mx<BM, 0>(g.wa, g.t, acc);
+        read_w_mx<BM, GEMM1, 1, 1, W4>(cw, csc, o, g.wb);
+        mfma_mx<BM, 0, W4>(g.wa, g.t, acc);
     }
 }
 
@@ -703,7 +725,7 @@ __device__ __forceinline__ TileDesc uniform_desc(const TileDesc& d) {
     return TileDesc{uniform_int(d.expert), uniform_int(d.row0), uniform_int(d.rows), uniform_int(d.ntile)};
 }
 
-template <int BM, bool GEMM1, bool MX, bool VAR>
+template <int BM, bool GEMM1, bool MX, bool VAR, bool W4>
 __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const int4* __restrict__ mtiles) {
     using C = Big<BM, MX>;
     constexpr int CAP = Fmt<MX>::kInfoCap;
@@ -739,7 +761,8 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
     r.wave = static_cast<uint32_t>(uniform_int(wave_v));
     const int K = GEMM1 ? a.D : a.H;
     r.KT = K * Fmt<MX>::EB / RB;
-    r.bstride = 8u * K * Fmt<MX>::EB;
+    // bytes between the first rows of consecutive weight DMA instructions
+    r.bstride = W4 ? 16u * (K / 2) : 8u * K * Fmt<MX>::EB;
 
     load_descs<CAP>(mtiles, first, stride, ny, count, 0, sDesc);
     __syncthreads();
@@ -748,13 +771,13 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
     dma_row_map<BM>(a, t.row0, sPair[0], r.wave);
     wait_vm<0>();
     bare_barrier();
-    make_src<BM, GEMM1, MX>(a, t, sPair[0], r.wave, r.src);
+    make_src<BM, GEMM1, MX, W4>(a, t, sPair[0], r.wave, r.src);
     if (!GEMM1 || (VAR && a.av.wba)) {
         dma_row_weights<BM>(a, sPair[0], sW[0], r.wave);
         wait_vm<0>();
         bare_barrier();
     }
-    issue_stage<BM, MX>(L.tok[0], L.wt[0], &sSc[0], r.src, r, 0);
+    issue_stage<BM, MX, W4>(L.tok[0], L.wt[0], &sSc[0], r.src, r, 0);
     sink_stores<BM, GEMM1, MX>(a);
 
     Regs<BM, MX> g;
@@ -777,14 +800,14 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
         r.cont = r.has_next;
 
         // KT is even: every tile starts in buffer 0
-        ring_step<BM, GEMM1, MX, VAR, 0, true, false>(a, r, L, sSc, 0, sPair, sW, o, g, acc);
-        ring_step<BM, GEMM1, MX, VAR, 1, false, true>(a, r, L, sSc, 1, sPair, sW, o, g, acc);
+        ring_step<BM, GEMM1, MX, VAR, W4, 0, true, false>(a, r, L, sSc, 0, sPair, sW, o, g, acc);
+        ring_step<BM, GEMM1, MX, VAR, W4, 1, false, true>(a, r, L, sSc, 1, sPair, sW, o, g, acc);
         for (int kt = 2; kt < r.KT; kt += 2) {
-            ring_step<BM, GEMM1, MX, VAR, 0, false, false>(a, r, L, sSc, kt, sPair, sW, o, g, acc);
-            ring_step<BM, GEMM1, MX, VAR, 1, false, false>(a, r, L, sSc, kt + 1, sPair, sW, o, g, acc);
+            ring_step<BM, GEMM1, MX, VAR, W4, 0, false, false>(a, r, L, sSc, kt, sPair, sW, o, g, acc);
+            ring_step<BM, GEMM1, MX, VAR, W4, 1, false, false>(a, r, L, sSc, kt + 1, sPair, sW, o, g, acc);
         }
         // the last unit of the last stage
-        if constexpr (MX) mfma_mx<BM, 1>(g.wb, g.t, acc);
+        if constexpr (MX) mfma_mx<BM, 1, W4>(g.wb, g.t, acc);
         else mfma_half<BM>(g.y, acc);
 
         if constexpr (GEMM1 && MX) epilogue_mx_gemm1<BM>(a, t, tok_row0, wf, sOut[wave_v], acc);
@@ -829,16 +852,21 @@ hipError_t launch_big(const BigArgs& a, int4* tiles, bool gemm1, hipStream_t s) 
     if (gemm1) mtile_table_kernel<BM><<<a.E, 64, 0, s>>>(a.rv, a.E, tiles);  // the same m-tiles for both GEMMs
     const int g = big_grid(a.P, a.E, BM, gemm1 ? a.H / 128 : a.D / 256);
     if constexpr (MX) {
-        if (gemm1) big_gemm_kernel<BM, true, true, false><<<g, kThreads, 0, s>>>(a, tiles);
-        else big_gemm_kernel<BM, false, true, false><<<g, kThreads, 0, s>>>(a, tiles);
+        if (a.w4) {
+            if (gemm1) big_gemm_kernel<BM, true, true, false, true><<<g, kThreads, 0, s>>>(a, tiles);
+            else big_gemm_kernel<BM, false, true, false, true><<<g, kThreads, 0, s>>>(a, tiles);
+        } else {
+            if (gemm1) big_gemm_kernel<BM, true, true, false, false><<<g, kThreads, 0, s>>>(a, tiles);
+            else big_gemm_kernel<BM, false, true, false, false><<<g, kThreads, 0, s>>>(a, tiles);
+        }
     } else {
         const bool var = a.av.on();  // the activation variant has kernels of its own
         if (gemm1) {
-            if (var) big_gemm_kernel<BM, true, false, true><<<g, kThreads, 0, s>>>(a, tiles);
-            else big_gemm_kernel<BM, true, false, false><<<g, kThreads, 0, s>>>(a, tiles);
+            if (var) big_gemm_kernel<BM, true, false, true, false><<<g, kThreads, 0, s>>>(a, tiles);
+            else big_gemm_kernel<BM, true, false, false, false><<<g, kThreads, 0, s>>>(a, tiles);
         } else {
-            if (var) big_gemm_kernel<BM, false, false, true><<<g, kThreads, 0, s>>>(a, tiles);
-            else big_gemm_kernel<BM, false, false, false><<<g, kThreads, 0, s>>>(a, tiles);
+            if (var) big_gemm_kernel<BM, false, false, true, false><<<g, kThreads, 0, s>>>(a, tiles);
+            else big_gemm_kernel<BM, false, false, false, false><<<g, kThreads, 0, s>>>(a, tiles);
         }
     }
     return hipGetLastError();
@@ -890,13 +918,14 @@ hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
 // a tile takes an even number of K stages of 128 codes (D and H multiples of 256).
 bool big_mx_supported(const MxArgs& a) {
     const int64_t lim = int64_t(1) << 32;
-    return !a.w4 && a.mtiles != nullptr && a.P >= kBigTile256MinRows * a.E && a.D % 256 == 0 && a.H % 256 == 0 &&
+    return a.mtiles != nullptr && a.P >= kBigTile256MinRows * a.E && a.D % 256 == 0 && a.H % 256 == 0 &&
            int64_t(a.T) * a.D < lim && a.P * a.H < lim && a.P * 4 < lim && int64_t(a.E) * 2 * a.H * a.D < lim;
 }
 
 hipError_t launch_big_mx(const MxArgs& b, bool gemm1, hipStream_t s) {
     BigArgs a{b.T,   b.D,   b.H,     b.E,  b.k,  b.P,      b.x,     b.xs,    b.w1,
               b.w1s, b.w2,  b.w2s,   b.wts, b.rv, b.act,   b.act_s, b.ypair, sink_of(b.mtiles, b.P, b.E)};
+    a.w4 = b.w4;
     return launch_big<256, true>(a, reinterpret_cast<int4*>(b.mtiles), gemm1, s);
 }
 
