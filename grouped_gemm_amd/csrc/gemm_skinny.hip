@@ -30,6 +30,7 @@
 // group; the epilogue scales by the routing weight and writes the pair's
 // row for the segmented combine.
 #include "common.h"
+#include "mxq.h"
 
 namespace moe {
 
@@ -364,5 +365,262 @@ hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s) { return launch_dma(a, true, s); }
 
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s) { return launch_dma(a, false, s); }
+
+// ---------------------------------------------------------------------------
+// Decode-shaped MXFP4-weight GEMMs ("GC-MoE on SM120", scale formats: E2M1
+// weights with a UE8M0 exponent per 32 along K; MX-fp8 activations). The
+// same streaming design as above: weights on the MFMA's row side, a ring of
+// S stages filled by global->LDS DMA of whole row segments, one barrier per
+// stage, the four waves splitting each stage's K steps and meeting in LDS at
+// the end of a row group. MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with the
+// e2m1 weights as A (16 contiguous bytes per lane: K values 32g..32g+31 of
+// the 64-wide step, g = lane >> 5) and the e4m3 tokens as B (16-byte chunks
+// g and 2 + g of the step); lane group g supplies the scale of 32-block g
+// (layouts measured on gfx950 with in-bounds probes).
+//
+// Stage (K step of KC = 512 values): 64 weight rows x 256 bytes, 32 token
+// rows x 512 bytes, and each row's 16 scale bytes. Chunks are XOR-swizzled
+// by the row (weights: ^ (row & 15) over 16 chunks, tokens: ^ (row & 31)
+// over 32), so the 16 rows a fragment read touches hit 16 distinct bank
+// groups. Waves 0 and 1 also move the stage's scale rows (weights, tokens).
+namespace {
+
+constexpr int kMx4KC = 512;             // K values per stage
+constexpr int kMx4R = 64;               // weight rows per block
+constexpr int kMx4BM = 32;              // token rows per m-tile
+constexpr int kMx4WRB = kMx4KC / 2;     // weight bytes per row per stage (256)
+constexpr int kMx4TRB = kMx4KC;         // token bytes per row per stage (512)
+constexpr int kMx4WB = kMx4R * kMx4WRB;               // 16 KB
+constexpr int kMx4TB = kMx4BM * kMx4TRB;              // 16 KB
+constexpr int kMx4SW = kMx4WB + kMx4TB;               // weight scale rows (64 x 16 B)
+constexpr int kMx4ST = kMx4SW + 64 * 16;              // token scale rows (32 x 16 B + 32 x 16 B pad)
+constexpr int kMx4Stage = kMx4ST + 64 * 16;           // 34 KB
+constexpr int kMx4S = 4;                              // ring stages
+constexpr int kMx4WIns = kMx4WB / 1024 / 4;           // weight DMA instructions per wave per stage (4)
+constexpr int kMx4TIns = kMx4TB / 1024 / 4;           // token DMA instructions per wave per stage (4)
+static_assert(kMx4S * kMx4Stage <= 160 * 1024, "ring must fit the LDS of a CU");
+static_assert(4 * 32 * 64 * 4 <= kMx4Stage, "the group reduction must fit one ring slot");
+
+// this wave's DMAs of ring stage `it` (row group grp relative to the
+// block's first, K step kit) into slot it % S
+__device__ __forceinline__ void mx4_dma_issue(uint8_t* ring, int it, int grp, int kit, int64_t wgroup_stride,
+                                              int64_t sgroup_stride, const char* const* wsrc,
+                                              const char* const* tsrc, const char* ssrc) {
+    const int wave = threadIdx.x >> 6;
+    uint8_t* slot = ring + (it % kMx4S) * kMx4Stage;
+    const int64_t wb = static_cast<int64_t>(kit) * kMx4WRB + grp * wgroup_stride;
+    const int64_t tb = static_cast<int64_t>(kit) * kMx4TRB;
+#pragma unroll
+    for (int j = 0; j < kMx4WIns; ++j)
+        __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * kMx4WIns + j) * 1024), 16, 0,
+                                         MOE_DMA_AUX);
+#pragma unroll
+    for (int j = 0; j < kMx4TIns; ++j)
+        __builtin_amdgcn_global_load_lds(tsrc[j] + tb, (lds_ptr_t)(slot + kMx4WB + (wave * kMx4TIns + j) * 1024), 16, 0,
+                                         0);
+    // wave 0: the 64 weight rows' scale bytes of this K step; wave 1: the tokens'
+    if (wave == 0)
+        __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16 + grp * sgroup_stride,
+                                         (lds_ptr_t)(slot + kMx4SW), 16, 0, 0);
+    else if (wave == 1)
+        __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16, (lds_ptr_t)(slot + kMx4ST), 16, 0, 0);
+}
+
+// One K step's operands for one wave: two weight fragments (row blocks 0 and
+// 1, e2m1), the token fragment (two 16-byte chunks, e4m3) and the three
+// scale bytes, then a wait for them; asm for the same reason as lds_read6.
+__device__ __forceinline__ void mx4_lds_read(u32x4_t& w0, u32x4_t& w1, u32x4_t& tlo, u32x4_t& thi, uint32_t& s0,
+                                             uint32_t& s1, uint32_t& st, uint32_t aw0, uint32_t aw1, uint32_t atl,
+                                             uint32_t ath, uint32_t as0, uint32_t as1, uint32_t ast) {
+    asm volatile(
+        "ds_read_b128 %0, %7\n\t"
+        "ds_read_b128 %1, %8\n\t"
+        "ds_read_b128 %2, %9\n\t"
+        "ds_read_b128 %3, %10\n\t"
+        "ds_read_u8 %4, %11\n\t"
+        "ds_read_u8 %5, %12\n\t"
+        "ds_read_u8 %6, %13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w0), "=&v"(w1), "=&v"(tlo), "=&v"(thi), "=&v"(s0), "=&v"(s1), "=&v"(st)
+        : "v"(aw0), "v"(aw1), "v"(atl), "v"(ath), "v"(as0), "v"(as1), "v"(ast)
+        : "memory");
+}
+
+// grid: (m-tiles of 32 rows, row groups / G). GEMM1: a group is 32 act
+// columns h..h+31 (gate rows h.., up rows H+h..), requantized to MX-fp8 in
+// the epilogue (its 32 columns are exactly one scale block); GEMM2: 64
+// output features, scaled by the routing weight into ypair.
+template <bool GEMM1>
+__global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kMx4S * kMx4Stage];
+    MTile mt;
+    if (!find_mtile<kMx4BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = GEMM1 ? a.D : a.H;
+    const int KB = K / 32;  // scale bytes per row
+    const int grp0 = blockIdx.y * G;
+    const uint8_t* wbase = GEMM1 ? a.w1 : a.w2;
+    const uint8_t* wsbase = GEMM1 ? a.w1s : a.w2s;
+    auto wrow = [&](int row) -> int64_t {  // expert weight row of block row `row` in group grp0
+        if (GEMM1) {
+            const int h0 = grp0 * 32;
+            return static_cast<int64_t>(mt.expert) * 2 * a.H + (row < 32 ? h0 + row : a.H + h0 + row - 32);
+        }
+        return static_cast<int64_t>(mt.expert) * a.D + grp0 * 64 + row;
+    };
+    // weight DMA: instruction j of a wave covers rows (wave * 4 + j) * 4 + lane / 16, 16 chunks each
+    const char* wsrc[kMx4WIns];
+#pragma unroll
+    for (int j = 0; j < kMx4WIns; ++j) {
+        const int row = (wave * kMx4WIns + j) * 4 + lane / 16;
+        const int c = (lane & 15) ^ (row & 15);
+        wsrc[j] = reinterpret_cast<const char*>(wbase) + wrow(row) * (K / 2) + c * 16;
+    }
+    // token DMA: rows (wave * 4 + j) * 2 + lane / 32, 32 chunks each
+    auto trow = [&](int m) -> int64_t {
+        const int mm = m < mt.rows ? m : 0;
+        if (GEMM1) return clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
+        return mt.row0 + mm;
+    };
+    const uint8_t* tbase = GEMM1 ? a.x : a.act;
+    const uint8_t* tsbase = GEMM1 ? a.xs : a.act_s;
+    const char* tsrc[kMx4TIns];
+#pragma unroll
+    for (int j = 0; j < kMx4TIns; ++j) {
+        const int m = (wave * kMx4TIns + j) * 2 + lane / 32;
+        const int c = (lane & 31) ^ (m & 31);
+        tsrc[j] = reinterpret_cast<const char*>(tbase) + trow(m) * K + c * 16;
+    }
+    // scale DMA source: wave 0 lane i -> weight row i; wave 1 lane i -> token row i & 31
+    const char* ssrc = wave == 0 ? reinterpret_cast<const char*>(wsbase) + wrow(lane) * KB
+                                 : reinterpret_cast<const char*>(tsbase) + trow(lane & 31) * KB;
+    const int64_t wgroup_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * (K / 2);
+    const int64_t sgroup_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * KB;
+    const int KIT = K / kMx4KC, NIT = G * KIT;
+    // GEMM2 rotates the order of its groups per block (see dma_skinny_kernel)
+    const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;
+    const int nins = kMx4WIns + kMx4TIns + (wave < 2 ? 1 : 0);  // this wave's DMAs per stage
+
+    const int lr = lane & 31, g = lane >> 5;
+    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int j = 0; j < kMx4S - 1; ++j)
+        if (j < NIT)
+            mx4_dma_issue(ring, j, (j / KIT + rot) % G, j % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc, ssrc);
+    for (int it = 0; it < NIT; ++it) {
+        if (it + kMx4S - 2 < NIT) {
+            if (nins == kMx4WIns + kMx4TIns + 1) wait_vm<(kMx4S - 2) * (kMx4WIns + kMx4TIns + 1)>();
+            else wait_vm<(kMx4S - 2) * (kMx4WIns + kMx4TIns)>();
+        } else {
+            wait_vm<0>();
+        }
+        ring_barrier();
+        if (it + kMx4S - 1 < NIT) {
+            const int nx = it + kMx4S - 1;
+            mx4_dma_issue(ring, nx, (nx / KIT + rot) % G, nx % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc, ssrc);
+        }
+        uint8_t* slot = ring + (it % kMx4S) * kMx4Stage;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int s = 2 * wave + q;  // this wave's 64-wide K step of the stage
+            const int cw = 2 * s + g;    // weight chunk (16 bytes = 32 e2m1 values)
+            const int ct = 4 * s + g;    // token chunks ct and ct + 2
+            u32x4_t w0, w1, tlo, thi;
+            uint32_t s0, s1, st;
+            mx4_lds_read(w0, w1, tlo, thi, s0, s1, st,
+                         lds_addr(slot + lr * kMx4WRB + ((cw ^ (lr & 15)) << 4)),
+                         lds_addr(slot + (32 + lr) * kMx4WRB + ((cw ^ ((32 + lr) & 15)) << 4)),
+                         lds_addr(slot + kMx4WB + lr * kMx4TRB + ((ct ^ lr) << 4)),
+                         lds_addr(slot + kMx4WB + lr * kMx4TRB + (((ct + 2) ^ lr) << 4)),
+                         lds_addr(slot + kMx4SW + lr * 16 + 2 * s + g),
+                         lds_addr(slot + kMx4SW + (32 + lr) * 16 + 2 * s + g),
+                         lds_addr(slot + kMx4ST + lr * 16 + 2 * s + g));
+            const i32x8_t bt{(int)tlo.x, (int)tlo.y, (int)tlo.z, (int)tlo.w, (int)thi.x, (int)thi.y, (int)thi.z, (int)thi.w};
+            const i32x8_t a0{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, 0, 0, 0, 0};
+            const i32x8_t a1{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w, 0, 0, 0, 0};
+            acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bt, acc[0], 4, 0, 0, (int)s0, 0, (int)st);
+            acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bt, acc[1], 4, 0, 0, (int)s1, 0, (int)st);
+        }
+        if (it % KIT != KIT - 1) continue;
+        // group finished: the four waves' partial sums meet in this slot
+        float* red = reinterpret_cast<float*>(slot);
+        lds_barrier();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) red[(wave * 32 + b * 16 + v) * 64 + lane] = acc[b][v];
+        lds_barrier();
+        const int gidx = grp0 + (it / KIT + rot) % G;
+        const int tok = lr;  // acc[b][v]: token lr, weight row 32b + 8(v/4) + 4g + (v%4)
+        if ((GEMM1 ? wave == 0 : wave < 2) && tok < mt.rows) {
+            if (GEMM1) {
+                float act[16];
+                float amax = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float gt = 0.0f, up = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        gt += red[(w * 32 + v) * 64 + lane];
+                        up += red[(w * 32 + 16 + v) * 64 + lane];
+                    }
+                    act[v] = gt / (1.0f + __expf(-gt)) * up;
+                    amax = fmaxf(amax, fabsf(act[v]));
+                }
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int sc = mx_scale_exp(amax);
+                const float inv = pow2f(-sc);
+                const int64_t row = mt.row0 + tok;
+                uint8_t* dst = a.act + row * a.H + gidx * 32 + 4 * g;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint32_t code = e4m3_encode(act[4 * q4] * inv, act[4 * q4]) |
+                                          (e4m3_encode(act[4 * q4 + 1] * inv, act[4 * q4 + 1]) << 8) |
+                                          (e4m3_encode(act[4 * q4 + 2] * inv, act[4 * q4 + 2]) << 16) |
+                                          (e4m3_encode(act[4 * q4 + 3] * inv, act[4 * q4 + 3]) << 24);
+                    *reinterpret_cast<uint32_t*>(dst + 8 * q4) = code;
+                }
+                if (g == 0) a.act_s[row * (a.H / 32) + gidx] = static_cast<uint8_t>(sc + 127);
+            } else {
+                const int b = wave;  // wave 0: features 0..31 of the group, wave 1: 32..63
+                const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + tok], a.P);
+                const float wt = a.wts[p];
+                uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + gidx * 64 + 32 * b + 4 * g;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    float y[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int v = 4 * q4 + j;
+                        y[j] = ((red[(0 * 32 + b * 16 + v) * 64 + lane] + red[(1 * 32 + b * 16 + v) * 64 + lane]) +
+                                (red[(2 * 32 + b * 16 + v) * 64 + lane] + red[(3 * 32 + b * 16 + v) * 64 + lane])) *
+                               wt;
+                    }
+                    *reinterpret_cast<uint2*>(dst + 8 * q4) =
+                        uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                }
+            }
+        }
+        acc[0] = f32x16_t{};
+        acc[1] = f32x16_t{};
+    }
+}
+
+}  // namespace
+
+// Decode-shaped MXFP4 GEMMs: up to 32 rows per expert on average, K (D for
+// GEMM1, H for GEMM2) a multiple of the 512-value stage.
+bool skinny_mx4_supported(const MxArgs& a) {
+    return a.w4 && a.P <= int64_t(32) * a.E && a.D % kMx4KC == 0 && a.H % kMx4KC == 0;
+}
+
+hipError_t launch_skinny_mx4(const MxArgs& a, bool gemm1, hipStream_t s) {
+    const int groups = gemm1 ? a.H / 32 : a.D / 64;
+    const int G = groups_per_block(groups, a.P, a.E);
+    dim3 g(mtiles_upper(a.P, a.E, kMx4BM), groups / G);
+    if (gemm1) mx4_skinny_kernel<true><<<g, kThreads, 0, s>>>(a, G);
+    else mx4_skinny_kernel<false><<<g, kThreads, 0, s>>>(a, G);
+    return hipGetLastError();
+}
 
 }  // namespace moe

@@ -99,6 +99,32 @@ def test_mxfp4_forward_matches_oracle(T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (64, 512, 512, 8, 2, "softmax"),     # decode kernel: one K stage per 512, one group per block
+    (1, 512, 512, 4, 2, "uniform"),      # one token
+    (100, 1024, 512, 16, 4, "zipf"),     # ragged, several K stages
+    (256, 512, 1024, 16, 2, "zipf"),     # skewed: experts with several 32-row m-tiles
+    (64, 512, 512, 32, 8, "softmax"),    # several row groups per block (GEMM1)
+])
+def test_mxfp4_decode_kernel_matches_oracle(T, D, H, E, k, routing):
+    """Shapes the decode-shaped MXFP4 kernel takes (<= 32 rows per expert on average, D and H multiples of 512)."""
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
+def test_mxfp4_decode_workload_in_full():
+    """The decode workload's dims (T=64, D=6144, H=2048, E=32, top-8) with fp4 weights, every token."""
+    _case(mi.CONFIGS[2])
+
+
+def test_mxfp4_decode_kernel_dropped_routes():
+    cfg = mi.custom(96, 512, 512, 8, 3, "softmax", dtype="mxfp8")
+    ids, _ = mi.routing(cfg, 0)
+    ids = ids.copy()
+    ids[::5, 0] = -1
+    ids[::9, 2] = cfg.E + 3
+    _case(cfg, ids=ids)
+
+
 def test_mxfp4_forward_dropped_routes():
     cfg = mi.custom(200, 256, 256, 8, 3, "softmax", dtype="mxfp8")
     ids, _ = mi.routing(cfg, 0)
