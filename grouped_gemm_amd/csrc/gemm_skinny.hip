@@ -378,60 +378,70 @@ hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s) { return launch
 // g and 2 + g of the step); lane group g supplies the scale of 32-block g
 // (layouts measured on gfx950 with in-bounds probes).
 //
-// Stage (K step of KC = 512 values): 64 weight rows x 256 bytes, 32 token
-// rows x 512 bytes, and each row's 16 scale bytes. Chunks are XOR-swizzled
-// by the row (weights: ^ (row & 15) over 16 chunks, tokens: ^ (row & 31)
-// over 32), so the 16 rows a fragment read touches hit 16 distinct bank
-// groups. Waves 0 and 1 also move the stage's scale rows (weights, tokens).
+// Stage (K step of KC = 512 values): R weight rows x 256 bytes, 32 token
+// rows x 512 bytes, and each row's 16 scale bytes. With R = 128 a stage
+// carries twice the weight bytes of its token bytes (R = 64: as many), so
+// more of the ring's bytes in flight are weights. Chunks are XOR-swizzled by
+// the row (weights: ^ (row & 15) over 16 chunks, tokens: ^ (row & 31) over
+// 32), so the 16 rows a fragment read touches hit 16 distinct bank groups.
+// Waves 0 .. R/64 - 1 also move the weight rows' scales, wave R/64 the
+// tokens'.
 namespace {
 
-constexpr int kMx4KC = 512;             // K values per stage
-constexpr int kMx4R = 64;               // weight rows per block
-constexpr int kMx4BM = 32;              // token rows per m-tile
-constexpr int kMx4WRB = kMx4KC / 2;     // weight bytes per row per stage (256)
-constexpr int kMx4TRB = kMx4KC;         // token bytes per row per stage (512)
-constexpr int kMx4WB = kMx4R * kMx4WRB;               // 16 KB
-constexpr int kMx4TB = kMx4BM * kMx4TRB;              // 16 KB
-constexpr int kMx4SW = kMx4WB + kMx4TB;               // weight scale rows (64 x 16 B)
-constexpr int kMx4ST = kMx4SW + 64 * 16;              // token scale rows (32 x 16 B + 32 x 16 B pad)
-constexpr int kMx4Stage = kMx4ST + 64 * 16;           // 34 KB
-constexpr int kMx4S = 4;                              // ring stages
-constexpr int kMx4WIns = kMx4WB / 1024 / 4;           // weight DMA instructions per wave per stage (4)
-constexpr int kMx4TIns = kMx4TB / 1024 / 4;           // token DMA instructions per wave per stage (4)
-static_assert(kMx4S * kMx4Stage <= 160 * 1024, "ring must fit the LDS of a CU");
-static_assert(4 * 32 * 64 * 4 <= kMx4Stage, "the group reduction must fit one ring slot");
+constexpr int kMx4KC = 512;   // K values per stage
+constexpr int kMx4BM = 32;    // token rows per m-tile
+
+template <int R>
+struct Mx4 {
+    static constexpr int NB = R / 32;                 // weight row blocks (32-row MFMA tiles)
+    static constexpr int WRB = kMx4KC / 2;            // weight bytes per row per stage (256)
+    static constexpr int TRB = kMx4KC;                // token bytes per row per stage (512)
+    static constexpr int WB = R * WRB;
+    static constexpr int TB = kMx4BM * TRB;           // 16 KB
+    static constexpr int SW = WB + TB;                // weight scale rows (R x 16 bytes)
+    static constexpr int ST = SW + R * 16;            // token scale rows (32 x 16 bytes, then a 512-byte pad)
+    static constexpr int STAGE = ST + 64 * 16;
+    static constexpr int S = R == 64 ? 4 : 3;         // ring stages
+    static constexpr int WINS = WB / 1024 / 4;        // weight DMA instructions per wave per stage
+    static constexpr int TINS = TB / 1024 / 4;        // token DMA instructions per wave per stage
+    static constexpr int SWAVES = R / 64;             // waves that move weight scale rows
+    static_assert(S * STAGE <= 160 * 1024, "ring must fit the LDS of a CU");
+    static_assert(4 * 2 * 16 * 64 * 4 <= STAGE, "a two-block pass of the group reduction must fit one ring slot");
+};
 
 // this wave's DMAs of ring stage `it` (row group grp relative to the
 // block's first, K step kit) into slot it % S
+template <int R>
 __device__ __forceinline__ void mx4_dma_issue(uint8_t* ring, int it, int grp, int kit, int64_t wgroup_stride,
                                               int64_t sgroup_stride, const char* const* wsrc,
                                               const char* const* tsrc, const char* ssrc) {
+    using C = Mx4<R>;
     const int wave = threadIdx.x >> 6;
-    uint8_t* slot = ring + (it % kMx4S) * kMx4Stage;
-    const int64_t wb = static_cast<int64_t>(kit) * kMx4WRB + grp * wgroup_stride;
-    const int64_t tb = static_cast<int64_t>(kit) * kMx4TRB;
+    uint8_t* slot = ring + (it % C::S) * C::STAGE;
+    const int64_t wb = static_cast<int64_t>(kit) * C::WRB + grp * wgroup_stride;
+    const int64_t tb = static_cast<int64_t>(kit) * C::TRB;
 #pragma unroll
-    for (int j = 0; j < kMx4WIns; ++j)
-        __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * kMx4WIns + j) * 1024), 16, 0,
+    for (int j = 0; j < C::WINS; ++j)
+        __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * C::WINS + j) * 1024), 16, 0,
                                          MOE_DMA_AUX);
 #pragma unroll
-    for (int j = 0; j < kMx4TIns; ++j)
-        __builtin_amdgcn_global_load_lds(tsrc[j] + tb, (lds_ptr_t)(slot + kMx4WB + (wave * kMx4TIns + j) * 1024), 16, 0,
+    for (int j = 0; j < C::TINS; ++j)
+        __builtin_amdgcn_global_load_lds(tsrc[j] + tb, (lds_ptr_t)(slot + C::WB + (wave * C::TINS + j) * 1024), 16, 0,
                                          0);
-    // wave 0: the 64 weight rows' scale bytes of this K step; wave 1: the tokens'
-    if (wave == 0)
+    // waves 0 .. SWAVES-1: 64 weight rows' scale bytes of this K step each; wave SWAVES: the tokens'
+    if (wave < C::SWAVES)
         __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16 + grp * sgroup_stride,
-                                         (lds_ptr_t)(slot + kMx4SW), 16, 0, 0);
-    else if (wave == 1)
-        __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16, (lds_ptr_t)(slot + kMx4ST), 16, 0, 0);
+                                         (lds_ptr_t)(slot + C::SW + wave * 1024), 16, 0, 0);
+    else if (wave == C::SWAVES)
+        __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16, (lds_ptr_t)(slot + C::ST), 16, 0, 0);
 }
 
-// One K step's operands for one wave: two weight fragments (row blocks 0 and
-// 1, e2m1), the token fragment (two 16-byte chunks, e4m3) and the three
-// scale bytes, then a wait for them; asm for the same reason as lds_read6.
-__device__ __forceinline__ void mx4_lds_read(u32x4_t& w0, u32x4_t& w1, u32x4_t& tlo, u32x4_t& thi, uint32_t& s0,
-                                             uint32_t& s1, uint32_t& st, uint32_t aw0, uint32_t aw1, uint32_t atl,
-                                             uint32_t ath, uint32_t as0, uint32_t as1, uint32_t ast) {
+// One K step's operands for one wave: NB weight fragments (e2m1), the token
+// fragment (two 16-byte chunks, e4m3) and the NB + 1 scale bytes, then a
+// wait for them; asm for the same reason as lds_read6.
+__device__ __forceinline__ void mx4_lds_read(u32x4_t (&w)[2], u32x4_t& tlo, u32x4_t& thi, uint32_t (&sw)[2],
+                                             uint32_t& st, const uint32_t (&aw)[2], uint32_t atl, uint32_t ath,
+                                             const uint32_t (&as)[2], uint32_t ast) {
     asm volatile(
         "ds_read_b128 %0, %7\n\t"
         "ds_read_b128 %1, %8\n\t"
@@ -441,18 +451,42 @@ __device__ __forceinline__ void mx4_lds_read(u32x4_t& w0, u32x4_t& w1, u32x4_t& 
         "ds_read_u8 %5, %12\n\t"
         "ds_read_u8 %6, %13\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w0), "=&v"(w1), "=&v"(tlo), "=&v"(thi), "=&v"(s0), "=&v"(s1), "=&v"(st)
-        : "v"(aw0), "v"(aw1), "v"(atl), "v"(ath), "v"(as0), "v"(as1), "v"(ast)
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(tlo), "=&v"(thi), "=&v"(sw[0]), "=&v"(sw[1]), "=&v"(st)
+        : "v"(aw[0]), "v"(aw[1]), "v"(atl), "v"(ath), "v"(as[0]), "v"(as[1]), "v"(ast)
+        : "memory");
+}
+__device__ __forceinline__ void mx4_lds_read(u32x4_t (&w)[4], u32x4_t& tlo, u32x4_t& thi, uint32_t (&sw)[4],
+                                             uint32_t& st, const uint32_t (&aw)[4], uint32_t atl, uint32_t ath,
+                                             const uint32_t (&as)[4], uint32_t ast) {
+    asm volatile(
+        "ds_read_b128 %0, %11\n\t"
+        "ds_read_b128 %1, %12\n\t"
+        "ds_read_b128 %2, %13\n\t"
+        "ds_read_b128 %3, %14\n\t"
+        "ds_read_b128 %4, %15\n\t"
+        "ds_read_b128 %5, %16\n\t"
+        "ds_read_u8 %6, %17\n\t"
+        "ds_read_u8 %7, %18\n\t"
+        "ds_read_u8 %8, %19\n\t"
+        "ds_read_u8 %9, %20\n\t"
+        "ds_read_u8 %10, %21\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(tlo), "=&v"(thi), "=&v"(sw[0]), "=&v"(sw[1]),
+          "=&v"(sw[2]), "=&v"(sw[3]), "=&v"(st)
+        : "v"(aw[0]), "v"(aw[1]), "v"(aw[2]), "v"(aw[3]), "v"(atl), "v"(ath), "v"(as[0]), "v"(as[1]), "v"(as[2]),
+          "v"(as[3]), "v"(ast)
         : "memory");
 }
 
-// grid: (m-tiles of 32 rows, row groups / G). GEMM1: a group is 32 act
-// columns h..h+31 (gate rows h.., up rows H+h..), requantized to MX-fp8 in
-// the epilogue (its 32 columns are exactly one scale block); GEMM2: 64
-// output features, scaled by the routing weight into ypair.
-template <bool GEMM1>
+// grid: (m-tiles of 32 rows, row groups / G). GEMM1: a group is R/2 act
+// columns h..h+R/2-1 (gate rows h.., up rows H+h..), requantized to MX-fp8 in
+// the epilogue (each 32 columns are one scale block); GEMM2: R output
+// features, scaled by the routing weight into ypair.
+template <int R, bool GEMM1>
 __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kMx4S * kMx4Stage];
+    using C = Mx4<R>;
+    constexpr int NB = C::NB, HALF = R / 2;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[C::S * C::STAGE];
     MTile mt;
     if (!find_mtile<kMx4BM>(a.rv, a.E, blockIdx.x, mt)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -463,20 +497,20 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
     const uint8_t* wsbase = GEMM1 ? a.w1s : a.w2s;
     auto wrow = [&](int row) -> int64_t {  // expert weight row of block row `row` in group grp0
         if (GEMM1) {
-            const int h0 = grp0 * 32;
-            return static_cast<int64_t>(mt.expert) * 2 * a.H + (row < 32 ? h0 + row : a.H + h0 + row - 32);
+            const int h0 = grp0 * HALF;
+            return static_cast<int64_t>(mt.expert) * 2 * a.H + (row < HALF ? h0 + row : a.H + h0 + row - HALF);
         }
-        return static_cast<int64_t>(mt.expert) * a.D + grp0 * 64 + row;
+        return static_cast<int64_t>(mt.expert) * a.D + grp0 * R + row;
     };
-    // weight DMA: instruction j of a wave covers rows (wave * 4 + j) * 4 + lane / 16, 16 chunks each
-    const char* wsrc[kMx4WIns];
+    // weight DMA: instruction j of a wave covers rows (wave * WINS + j) * 4 + lane / 16, 16 chunks each
+    const char* wsrc[C::WINS];
 #pragma unroll
-    for (int j = 0; j < kMx4WIns; ++j) {
-        const int row = (wave * kMx4WIns + j) * 4 + lane / 16;
+    for (int j = 0; j < C::WINS; ++j) {
+        const int row = (wave * C::WINS + j) * 4 + lane / 16;
         const int c = (lane & 15) ^ (row & 15);
         wsrc[j] = reinterpret_cast<const char*>(wbase) + wrow(row) * (K / 2) + c * 16;
     }
-    // token DMA: rows (wave * 4 + j) * 2 + lane / 32, 32 chunks each
+    // token DMA: rows (wave * TINS + j) * 2 + lane / 32, 32 chunks each
     auto trow = [&](int m) -> int64_t {
         const int mm = m < mt.rows ? m : 0;
         if (GEMM1) return clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
@@ -484,142 +518,155 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
     };
     const uint8_t* tbase = GEMM1 ? a.x : a.act;
     const uint8_t* tsbase = GEMM1 ? a.xs : a.act_s;
-    const char* tsrc[kMx4TIns];
+    const char* tsrc[C::TINS];
 #pragma unroll
-    for (int j = 0; j < kMx4TIns; ++j) {
-        const int m = (wave * kMx4TIns + j) * 2 + lane / 32;
+    for (int j = 0; j < C::TINS; ++j) {
+        const int m = (wave * C::TINS + j) * 2 + lane / 32;
         const int c = (lane & 31) ^ (m & 31);
         tsrc[j] = reinterpret_cast<const char*>(tbase) + trow(m) * K + c * 16;
     }
-    // scale DMA source: wave 0 lane i -> weight row i; wave 1 lane i -> token row i & 31
-    const char* ssrc = wave == 0 ? reinterpret_cast<const char*>(wsbase) + wrow(lane) * KB
-                                 : reinterpret_cast<const char*>(tsbase) + trow(lane & 31) * KB;
-    const int64_t wgroup_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * (K / 2);
-    const int64_t sgroup_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * KB;
+    // scale DMA source: wave w < SWAVES lane i -> weight row 64w + i; wave SWAVES lane i -> token row i & 31
+    const char* ssrc = wave < C::SWAVES ? reinterpret_cast<const char*>(wsbase) + wrow(64 * wave + lane) * KB
+                                        : reinterpret_cast<const char*>(tsbase) + trow(lane & 31) * KB;
+    const int64_t wgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * (K / 2);
+    const int64_t sgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * KB;
     const int KIT = K / kMx4KC, NIT = G * KIT;
     // GEMM2 rotates the order of its groups per block (see dma_skinny_kernel)
     const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;
-    const int nins = kMx4WIns + kMx4TIns + (wave < 2 ? 1 : 0);  // this wave's DMAs per stage
+    const bool scale_wave = wave <= C::SWAVES;  // moves one scale DMA per stage
 
     const int lr = lane & 31, g = lane >> 5;
-    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t acc[NB];
 #pragma unroll
-    for (int j = 0; j < kMx4S - 1; ++j)
+    for (int b = 0; b < NB; ++b) acc[b] = f32x16_t{};
+#pragma unroll
+    for (int j = 0; j < C::S - 1; ++j)
         if (j < NIT)
-            mx4_dma_issue(ring, j, (j / KIT + rot) % G, j % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc, ssrc);
+            mx4_dma_issue<R>(ring, j, (j / KIT + rot) % G, j % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc, ssrc);
     for (int it = 0; it < NIT; ++it) {
-        if (it + kMx4S - 2 < NIT) {
-            if (nins == kMx4WIns + kMx4TIns + 1) wait_vm<(kMx4S - 2) * (kMx4WIns + kMx4TIns + 1)>();
-            else wait_vm<(kMx4S - 2) * (kMx4WIns + kMx4TIns)>();
+        if (it + C::S - 2 < NIT) {
+            if (scale_wave) wait_vm<(C::S - 2) * (C::WINS + C::TINS + 1)>();
+            else wait_vm<(C::S - 2) * (C::WINS + C::TINS)>();
         } else {
             wait_vm<0>();
         }
         ring_barrier();
-        if (it + kMx4S - 1 < NIT) {
-            const int nx = it + kMx4S - 1;
-            mx4_dma_issue(ring, nx, (nx / KIT + rot) % G, nx % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc, ssrc);
+        if (it + C::S - 1 < NIT) {
+            const int nx = it + C::S - 1;
+            mx4_dma_issue<R>(ring, nx, (nx / KIT + rot) % G, nx % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc,
+                             ssrc);
         }
-        uint8_t* slot = ring + (it % kMx4S) * kMx4Stage;
+        uint8_t* slot = ring + (it % C::S) * C::STAGE;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int s = 2 * wave + q;  // this wave's 64-wide K step of the stage
             const int cw = 2 * s + g;    // weight chunk (16 bytes = 32 e2m1 values)
             const int ct = 4 * s + g;    // token chunks ct and ct + 2
-            u32x4_t w0, w1, tlo, thi;
-            uint32_t s0, s1, st;
-            mx4_lds_read(w0, w1, tlo, thi, s0, s1, st,
-                         lds_addr(slot + lr * kMx4WRB + ((cw ^ (lr & 15)) << 4)),
-                         lds_addr(slot + (32 + lr) * kMx4WRB + ((cw ^ ((32 + lr) & 15)) << 4)),
-                         lds_addr(slot + kMx4WB + lr * kMx4TRB + ((ct ^ lr) << 4)),
-                         lds_addr(slot + kMx4WB + lr * kMx4TRB + (((ct + 2) ^ lr) << 4)),
-                         lds_addr(slot + kMx4SW + lr * 16 + 2 * s + g),
-                         lds_addr(slot + kMx4SW + (32 + lr) * 16 + 2 * s + g),
-                         lds_addr(slot + kMx4ST + lr * 16 + 2 * s + g));
+            u32x4_t w[NB], tlo, thi;
+            uint32_t sw[NB], st, aw[NB], as[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int row = 32 * b + lr;
+                aw[b] = lds_addr(slot + row * C::WRB + ((cw ^ (row & 15)) << 4));
+                as[b] = lds_addr(slot + C::SW + row * 16 + 2 * s + g);
+            }
+            mx4_lds_read(w, tlo, thi, sw, st, aw, lds_addr(slot + C::WB + lr * C::TRB + ((ct ^ lr) << 4)),
+                         lds_addr(slot + C::WB + lr * C::TRB + (((ct + 2) ^ lr) << 4)), as,
+                         lds_addr(slot + C::ST + lr * 16 + 2 * s + g));
             const i32x8_t bt{(int)tlo.x, (int)tlo.y, (int)tlo.z, (int)tlo.w, (int)thi.x, (int)thi.y, (int)thi.z, (int)thi.w};
-            const i32x8_t a0{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, 0, 0, 0, 0};
-            const i32x8_t a1{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w, 0, 0, 0, 0};
-            acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bt, acc[0], 4, 0, 0, (int)s0, 0, (int)st);
-            acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bt, acc[1], 4, 0, 0, (int)s1, 0, (int)st);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const i32x8_t aa{(int)w[b].x, (int)w[b].y, (int)w[b].z, (int)w[b].w, 0, 0, 0, 0};
+                acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aa, bt, acc[b], 4, 0, 0, (int)sw[b], 0, (int)st);
+            }
         }
         if (it % KIT != KIT - 1) continue;
-        // group finished: the four waves' partial sums meet in this slot
+        // group finished: the four waves' partial sums meet in this slot, two
+        // row blocks per pass. acc[b][v]: token lr, row 32b + 8(v/4) + 4g + (v%4).
         float* red = reinterpret_cast<float*>(slot);
-        lds_barrier();
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) red[(wave * 32 + b * 16 + v) * 64 + lane] = acc[b][v];
-        lds_barrier();
         const int gidx = grp0 + (it / KIT + rot) % G;
-        const int tok = lr;  // acc[b][v]: token lr, weight row 32b + 8(v/4) + 4g + (v%4)
-        if ((GEMM1 ? wave == 0 : wave < 2) && tok < mt.rows) {
-            if (GEMM1) {
-                float act[16];
-                float amax = 0.0f;
+        const int tok = lr;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    float gt = 0.0f, up = 0.0f;
+        for (int pass = 0; pass < NB / 2; ++pass) {
+            // GEMM1 pass p holds the gate and up blocks of act columns 32p..32p+31
+            // (blocks p and NB/2 + p); GEMM2 pass p holds blocks 2p and 2p + 1
+            const int b0 = GEMM1 ? pass : 2 * pass, b1 = GEMM1 ? NB / 2 + pass : 2 * pass + 1;
+            lds_barrier();
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        gt += red[(w * 32 + v) * 64 + lane];
-                        up += red[(w * 32 + 16 + v) * 64 + lane];
+            for (int v = 0; v < 16; ++v) {
+                red[(wave * 32 + v) * 64 + lane] = acc[b0][v];
+                red[(wave * 32 + 16 + v) * 64 + lane] = acc[b1][v];
+            }
+            lds_barrier();
+            auto sum = [&](int i) {  // i: 0..31 (16 * half + v)
+                return (red[(0 * 32 + i) * 64 + lane] + red[(1 * 32 + i) * 64 + lane]) +
+                       (red[(2 * 32 + i) * 64 + lane] + red[(3 * 32 + i) * 64 + lane]);
+            };
+            if ((GEMM1 ? wave == 0 : wave < 2) && tok < mt.rows) {
+                if (GEMM1) {
+                    float act[16];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float gt = sum(v), up = sum(16 + v);
+                        act[v] = gt / (1.0f + __expf(-gt)) * up;
+                        amax = fmaxf(amax, fabsf(act[v]));
                     }
-                    act[v] = gt / (1.0f + __expf(-gt)) * up;
-                    amax = fmaxf(amax, fabsf(act[v]));
-                }
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                const int sc = mx_scale_exp(amax);
-                const float inv = pow2f(-sc);
-                const int64_t row = mt.row0 + tok;
-                uint8_t* dst = a.act + row * a.H + gidx * 32 + 4 * g;
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    const int sc = mx_scale_exp(amax);
+                    const float inv = pow2f(-sc);
+                    const int64_t row = mt.row0 + tok;
+                    const int col0 = gidx * HALF + 32 * pass;  // this pass's 32 act columns: one scale block
+                    uint8_t* dst = a.act + row * a.H + col0 + 4 * g;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const uint32_t code = e4m3_encode(act[4 * q4] * inv, act[4 * q4]) |
-                                          (e4m3_encode(act[4 * q4 + 1] * inv, act[4 * q4 + 1]) << 8) |
-                                          (e4m3_encode(act[4 * q4 + 2] * inv, act[4 * q4 + 2]) << 16) |
-                                          (e4m3_encode(act[4 * q4 + 3] * inv, act[4 * q4 + 3]) << 24);
-                    *reinterpret_cast<uint32_t*>(dst + 8 * q4) = code;
-                }
-                if (g == 0) a.act_s[row * (a.H / 32) + gidx] = static_cast<uint8_t>(sc + 127);
-            } else {
-                const int b = wave;  // wave 0: features 0..31 of the group, wave 1: 32..63
-                const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + tok], a.P);
-                const float wt = a.wts[p];
-                uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + gidx * 64 + 32 * b + 4 * g;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    float y[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int v = 4 * q4 + j;
-                        y[j] = ((red[(0 * 32 + b * 16 + v) * 64 + lane] + red[(1 * 32 + b * 16 + v) * 64 + lane]) +
-                                (red[(2 * 32 + b * 16 + v) * 64 + lane] + red[(3 * 32 + b * 16 + v) * 64 + lane])) *
-                               wt;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const uint32_t code = e4m3_encode(act[4 * q4] * inv, act[4 * q4]) |
+                                              (e4m3_encode(act[4 * q4 + 1] * inv, act[4 * q4 + 1]) << 8) |
+                                              (e4m3_encode(act[4 * q4 + 2] * inv, act[4 * q4 + 2]) << 16) |
+                                              (e4m3_encode(act[4 * q4 + 3] * inv, act[4 * q4 + 3]) << 24);
+                        *reinterpret_cast<uint32_t*>(dst + 8 * q4) = code;
                     }
-                    *reinterpret_cast<uint2*>(dst + 8 * q4) =
-                        uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                    if (g == 0) a.act_s[row * (a.H / 32) + col0 / 32] = static_cast<uint8_t>(sc + 127);
+                } else {
+                    const int half = wave;  // wave 0: block b0, wave 1: block b1
+                    const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + tok], a.P);
+                    const float wt = a.wts[p];
+                    uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + gidx * R + 32 * (half ? b1 : b0) + 4 * g;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        float y[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) y[j] = sum(16 * half + 4 * q4 + j) * wt;
+                        *reinterpret_cast<uint2*>(dst + 8 * q4) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                    }
                 }
             }
         }
-        acc[0] = f32x16_t{};
-        acc[1] = f32x16_t{};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = f32x16_t{};
     }
 }
+
+#ifndef MOE_MX4_ROWS
+#define MOE_MX4_ROWS 128
+#endif
 
 }  // namespace
 
 // Decode-shaped MXFP4 GEMMs: up to 32 rows per expert on average, K (D for
-// GEMM1, H for GEMM2) a multiple of the 512-value stage.
+// GEMM1, H for GEMM2) a multiple of the 512-value stage, and whole row groups.
 bool skinny_mx4_supported(const MxArgs& a) {
-    return a.w4 && a.P <= int64_t(32) * a.E && a.D % kMx4KC == 0 && a.H % kMx4KC == 0;
+    return a.w4 && a.P <= int64_t(32) * a.E && a.D % kMx4KC == 0 && a.H % kMx4KC == 0 &&
+           a.H % (MOE_MX4_ROWS / 2) == 0 && a.D % MOE_MX4_ROWS == 0;
 }
 
 hipError_t launch_skinny_mx4(const MxArgs& a, bool gemm1, hipStream_t s) {
-    const int groups = gemm1 ? a.H / 32 : a.D / 64;
+    constexpr int R = MOE_MX4_ROWS;
+    const int groups = gemm1 ? a.H / (R / 2) : a.D / R;
     const int G = groups_per_block(groups, a.P, a.E);
     dim3 g(mtiles_upper(a.P, a.E, kMx4BM), groups / G);
-    if (gemm1) mx4_skinny_kernel<true><<<g, kThreads, 0, s>>>(a, G);
-    else mx4_skinny_kernel<false><<<g, kThreads, 0, s>>>(a, G);
+    if (gemm1) mx4_skinny_kernel<R, true><<<g, kThreads, 0, s>>>(a, G);
+    else mx4_skinny_kernel<R, false><<<g, kThreads, 0, s>>>(a, G);
     return hipGetLastError();
 }
 
