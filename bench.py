@@ -23,6 +23,10 @@ instrumented steps.
 
 The CPU baseline is the oracle (oracle/, plain C, OpenMP) timed on a bounded
 sample of the same workload on the host's cores.
+
+After the timed steps, the same pass is captured once in a HIP graph and
+replayed K times (`graph_replay_ms`, median and mean of the replays); this
+is reported beside `value`, which stays the eager rate (--no-graph skips it).
 """
 from __future__ import annotations
 
@@ -73,6 +77,8 @@ def parse_args(argv=None):
     ap.add_argument("--mxfp4", action="store_true",
                     help="MXFP4 expert weights (e2m1 codes, e8m0 scale per 32; moe_ffn_mxfp4_quantize) "
                          "with MX-fp8 x and activations, on the chosen workload's dims")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing that follows the timed eager steps")
     ap.add_argument("--logits", action="store_true",
                     help="start each step from router logits (moe_ffn_forward_logits): the router's "
                          "softmax/top-k runs inside the timed pass, fused with the route step")
@@ -201,6 +207,35 @@ def cpu_baseline(cfg, inputs, dtype, target_s):
             "seconds": dt, "tokens_per_s": n / dt}
 
 
+def graph_replay_ms(step, n):
+    """The same pass captured once in a HIP graph and replayed n times after the
+    timed eager steps (not part of `value`): median and mean of the replays,
+    each bracketed by events on the replaying stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in marks:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in marks)
+    del graph
+    return {"median": t[len(t) // 2], "mean": sum(t) / len(t), "replays": n}
+
+
 def main(argv=None):
     args = parse_args(argv)
     args.event_every = max(1, args.event_every)
@@ -318,6 +353,10 @@ def main(argv=None):
         for e in row:
             hip.hipEventDestroy(e)
 
+    graph_ms = None
+    if not args.no_graph and shared is None and logits is None:
+        graph_ms = graph_replay_ms(step, args.steps)
+
     if args.copy_mib:
         a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -376,6 +415,7 @@ def main(argv=None):
         "pct_mfma_peak": tflops / peak_tf,
         "effective_hbm_gbs": all_bytes / (ms * 1e-3) / 1e9,
         "stage_ms": stage_ms,
+        "graph_replay_ms": graph_ms,
         "stage_events_every": args.event_every,
         "roofline": roof,
     }
