@@ -115,7 +115,8 @@ def kernel_work(cfg, mode, hit, dtype):
     }
 
 
-KERNEL_FILES = {"dma_skinny_kernel": "gemm_skinny.hip", "mx4_skinny_kernel": "gemm_skinny.hip",
+KERNEL_FILES = {"dma_split_kernel": "gemm_skinny.hip", "dma_skinny_kernel": "gemm_skinny.hip",
+                "mx4_skinny_kernel": "gemm_skinny.hip",
                 "big_gemm_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
                 "gemm1_swiglu_kernel": "gemm_bf16.hip", "gemm2_weight_kernel": "gemm_bf16.hip",
@@ -158,7 +159,7 @@ def kernel_symbol(cfg, mode, stage):
             return "big_gemm_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.P <= 32 * cfg.E:
-        return "dma_skinny_kernel"
+        return "dma_split_kernel" if (cfg.D if g1 else cfg.H) % 256 == 0 else "dma_skinny_kernel"
     if cfg.D % 256 == 0:
         return "big_gemm_kernel"
     return "gemm1_swiglu_kernel" if g1 else "gemm2_weight_kernel"

@@ -148,6 +148,99 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
 }
 
+// The epilogue's per-token values for token 16 * (wave & 1) + (lane & 15) of
+// the m-tile (the token tile waves 0-1 store): its pair index and its scale
+// (GEMM2: the routing weight, or 1 when it was applied before the
+// activation; GEMM1: the activation variant's scale). Loaded once, before
+// the ring starts, and waited for here: a global load in the loop would come
+// with a vmcnt(0) wait that drains the wave's DMAs in flight.
+template <bool GEMM1>
+__device__ __forceinline__ void dma_epilogue_token(const Bf16Args& a, const MTile& mt, int wave, int lane, int& ep,
+                                                   float& esc) {
+    const int m = 16 * (wave & 1) + (lane & 15);
+    ep = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
+    if (GEMM1)
+        esc = a.av.on() ? (a.av.alpha ? a.av.alpha[mt.expert] : 1.0f) * (a.av.wba ? a.wts[ep] : 1.0f) : 1.0f;
+    else
+        esc = a.av.wba ? 1.0f : a.wts[ep];
+    asm volatile("" : "+v"(ep), "+v"(esc));
+}
+
+// End of a row group: sum the four waves' partials (acc[b][t][v]: row 16b +
+// 4kg + v, token 16t + r) in `red` (a just-consumed ring slot of SLOT bytes,
+// PB row blocks per pass, LDS-only barriers so the DMAs in flight keep
+// running), then wave t stores token tile t of group g: GEMM1 the act
+// columns g*32.. (silu(gate) * up, or the activation variant), GEMM2 the
+// weighted outputs g*64.. of the pair's ypair row.
+template <int SLOT, bool GEMM1>
+__device__ __forceinline__ void dma_group_end(const Bf16Args& a, f32x4_t (&acc)[4][2], float* red, const MTile& mt,
+                                              int g, int wave, int lane, int ep, float esc) {
+    constexpr int NB = 4, NT = 2, NV = NB * NT * 4;
+    constexpr int PB = (4 * NV * 64 * 4 <= SLOT) ? NB : (4 * (NV / 2) * 64 * 4 <= SLOT ? NB / 2 : 1);
+    static_assert(4 * PB * NT * 4 * 64 * 4 <= SLOT, "reduction pass must fit one ring slot");
+    const int r = lane & 15, kg = lane >> 4;
+    constexpr int PV = PB * NT * 4;  // floats per lane per pass
+#pragma unroll
+    for (int b0 = 0; b0 < NB; b0 += PB) {
+        lds_barrier();
+#pragma unroll
+        for (int b = 0; b < PB; ++b)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[((wave * PV) + (b * NT + t) * 4 + v) * 64 + lane] = acc[b0 + b][t][v];
+        lds_barrier();
+#pragma unroll
+        for (int b = 0; b < PB; ++b)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = ((b * NT + t) * 4 + v) * 64 + lane;
+                    acc[b0 + b][t][v] =
+                        (red[i] + red[PV * 64 + i]) + (red[2 * PV * 64 + i] + red[3 * PV * 64 + i]);
+                }
+    }
+    // epilogue: wave w stores token tile w (acc[b][t][v]: row 16b + 4kg + v, token 16t + r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int m = 16 * t + r;
+        if (t != wave || m >= mt.rows) continue;
+        if (GEMM1) {
+            uint16_t* dst = a.act + static_cast<int64_t>(mt.row0 + m) * a.H + g * 32 + 4 * kg;
+            if (a.av.on()) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = act_variant(acc[j][t][q], acc[j + 2][t][q], esc, a.av.kind, a.av.limit);
+                    *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                }
+                continue;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float gt = acc[j][t][q], u = acc[j + 2][t][q];
+                    v[q] = gt / (1.0f + __expf(-gt)) * u;
+                }
+                *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+        } else {
+            uint16_t* dst = a.ypair + static_cast<int64_t>(ep) * a.D + g * 64 + 4 * kg;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const f32x4_t& cc = acc[b][t];
+                *reinterpret_cast<uint2*>(dst + 16 * b) =
+                    uint2{pack_bf16x2(cc[0] * esc, cc[1] * esc), pack_bf16x2(cc[2] * esc, cc[3] * esc)};
+            }
+        }
+    }
+}
+
 // grid: (m-tiles of 16*NT rows, row groups / G). A block walks G consecutive
 // 64-row weight groups (GEMM1: 32 act columns = gate rows h..h+31 and up
 // rows H+h..H+h+31; GEMM2: 64 output features) through one continuous ring,
@@ -161,9 +254,6 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
     constexpr int NB = 4, NV = NB * NT * 4;
     static_assert(NT == 2, "written for two token tiles");
     static_assert(T::NS % 4 == 0, "k-steps must split evenly over the four waves");
-    // the group reduction reuses one ring slot, PB row blocks at a time
-    constexpr int PB = (4 * NV * 64 * 4 <= T::STAGE) ? NB : (4 * (NV / 2) * 64 * 4 <= T::STAGE ? NB / 2 : 1);
-    static_assert(4 * PB * NT * 4 * 64 * 4 <= T::STAGE, "reduction pass must fit one ring slot");
     __shared__ __attribute__((aligned(16))) uint8_t ring[S * T::STAGE];
     MTile mt;
     if (!find_mtile<T::BM>(a.rv, a.E, blockIdx.x, mt)) return;
@@ -213,6 +303,9 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
+    int ep;
+    float esc;
+    dma_epilogue_token<GEMM1>(a, mt, wave, lane, ep, esc);
 #pragma unroll
     for (int j = 0; j < S - 1; ++j)
         if (j < NIT) dma_issue<NT, KC, S>(ring, j, (j / KIT + rot) % G, j % KIT, group_stride, wsrc, tsrc);
@@ -247,74 +340,155 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
                 for (int t = 0; t < NT; ++t) acc[b][t] = mfma16(w[b], tk[t], acc[b][t]);
         }
         if (it % KIT != KIT - 1) continue;
-        // group finished: sum the four waves' partials in this slot, PB row blocks per pass
-        float* red = reinterpret_cast<float*>(slot);
-        constexpr int PV = PB * NT * 4;  // floats per lane per pass
+        dma_group_end<T::STAGE, GEMM1>(a, acc, reinterpret_cast<float*>(slot), mt, grp0 + (it / KIT + rot) % G, wave,
+                                       lane, ep, esc);
 #pragma unroll
-        for (int b0 = 0; b0 < NB; b0 += PB) {
-            lds_barrier();
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int b = 0; b < PB; ++b)
+            for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
+    }
+}
+
+// The split-ring kernel's DMAs of stage `it` for this wave (one of the pair
+// that moves them, mw = 0 or 1): weight rows into weight slot it % SW, or
+// token rows into token slot it % 2.
+template <int KC, int SW>
+__device__ __forceinline__ void split_issue_w(uint8_t* lds, int it, int KIT, int G, int rot, int64_t group_stride,
+                                              int mw, const char* const* src) {
+    using T = DmaTile<2, KC, 2>;
+    constexpr int W_INS = 2 * T::W_INS;
+    const int64_t off = static_cast<int64_t>(it % KIT) * T::RB + ((it / KIT + rot) % G) * group_stride;
+    uint8_t* slot = lds + (it % SW) * T::W_BYTES;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
+    for (int j = 0; j < W_INS; ++j)
+        __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
+                                         MOE_DMA_AUX);
+}
+template <int KC>
+__device__ __forceinline__ void split_issue_t(uint8_t* tring, int it, int KIT, int mw, const char* const* src) {
+    using T = DmaTile<2, KC, 2>;
+    constexpr int T_INS = 2 * T::T_INS;
+    const int64_t off = static_cast<int64_t>(it % KIT) * T::RB;
+    uint8_t* slot = tring + (it & 1) * T::T_BYTES;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        red[((wave * PV) + (b * NT + t) * 4 + v) * 64 + lane] = acc[b0 + b][t][v];
-            lds_barrier();
+    for (int j = 0; j < T_INS; ++j)
+        __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * T_INS + j) * 1024), 16, 0, 0);
+}
+
+// The same GEMMs with the weights and the tokens on separate rings: waves 0-1
+// move the weight rows through an SW-stage ring, waves 2-3 the token rows
+// through a 2-stage ring (tokens come from L2, one stage ahead is enough).
+// s_waitcnt vmcnt counts a wave's own loads in issue order, so when every
+// wave moves both (dma_skinny_kernel) a wait for the next stage's tokens is
+// also a wait for every weight stage issued before them; split by wave, the
+// weight waves keep SW - 1 stages in flight while the token waves wait for
+// their own stage alone. SW = 4: 4 x 32 KB of weights + 2 x 16 KB of tokens,
+// the whole 160 KB of LDS. Same fragments, split-K over the waves, group
+// reduction and epilogue as dma_skinny_kernel (32 token rows, KC = 256).
+template <int KC, int SW, bool GEMM1>
+__global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) {
+    using T = DmaTile<2, KC, 2>;
+    constexpr int NB = 4, NT = 2;
+    constexpr int W_INS = 2 * T::W_INS, T_INS = 2 * T::T_INS;  // per wave of the pair that moves them
+    constexpr int NI = W_INS > T_INS ? W_INS : T_INS;
+    static_assert(T::RPI * T::RB == 1024, "one DMA instruction fills 1 KB of LDS");
+    static_assert(T::NS % 4 == 0, "k-steps must split evenly over the four waves");
+    static_assert(SW * T::W_BYTES + 2 * T::T_BYTES <= 160 * 1024 && SW >= 2, "rings must fit the LDS of a CU");
+    static_assert((SW - 2) * W_INS < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES];
+    uint8_t* const tring = lds + SW * T::W_BYTES;
+    MTile mt;
+    if (!find_mtile<T::BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool wmover = wave < 2;
+    const int mw = wave & 1;  // this wave's half of what its pair moves
+    const int K = GEMM1 ? a.D : a.H;
+    const int grp0 = blockIdx.y * G;
+    const int pc = lane % T::CPR;
+    const char* src[NI];
+    if (wmover) {
 #pragma unroll
-            for (int b = 0; b < PB; ++b)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int i = ((b * NT + t) * 4 + v) * 64 + lane;
-                        acc[b0 + b][t][v] =
-                            (red[i] + red[PV * 64 + i]) + (red[2 * PV * 64 + i] + red[3 * PV * 64 + i]);
-                    }
-        }
-        // epilogue: wave w stores token tile w (acc[b][t][v]: row 16b + 4kg + v, token 16t + r)
-        const int g = grp0 + (it / KIT + rot) % G;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int m = 16 * t + r;
-            if (t != wave || m >= mt.rows) continue;
+        for (int j = 0; j < W_INS; ++j) {
+            const int row = (mw * W_INS + j) * T::RPI + lane / T::CPR;
+            const int c = pc ^ (row & (T::CPR - 1));
+            int64_t grow;
             if (GEMM1) {
-                uint16_t* dst = a.act + static_cast<int64_t>(mt.row0 + m) * a.H + g * 32 + 4 * kg;
-                if (a.av.on()) {
-                    const float al = a.av.alpha ? a.av.alpha[mt.expert] : 1.0f;
-                    const float sc =
-                        a.av.wba ? al * a.wts[clamp_pair(a.rv.sorted_to_pair[mt.row0 + m], a.P)] : al;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        float v[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] = act_variant(acc[j][t][q], acc[j + 2][t][q], sc, a.av.kind, a.av.limit);
-                        *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                    }
-                    continue;
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float gt = acc[j][t][q], u = acc[j + 2][t][q];
-                        v[q] = gt / (1.0f + __expf(-gt)) * u;
-                    }
-                    *reinterpret_cast<uint2*>(dst + 16 * j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                }
+                const int h0 = grp0 * 32;
+                grow = static_cast<int64_t>(mt.expert) * 2 * a.H + (row < 32 ? h0 + row : a.H + h0 + row - 32);
             } else {
-                const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + m], a.P);
-                const float wt = a.av.wba ? 1.0f : a.wts[p];
-                uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + g * 64 + 4 * kg;
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const f32x4_t& cc = acc[b][t];
-                    *reinterpret_cast<uint2*>(dst + 16 * b) =
-                        uint2{pack_bf16x2(cc[0] * wt, cc[1] * wt), pack_bf16x2(cc[2] * wt, cc[3] * wt)};
-                }
+                grow = static_cast<int64_t>(mt.expert) * a.D + grp0 * 64 + row;
             }
+            src[j] = reinterpret_cast<const char*>(GEMM1 ? a.w1 : a.w2) + grow * K * 2 + c * 16;
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int m = (mw * T_INS + (j < T_INS ? j : 0)) * T::RPI + lane / T::CPR;
+            const int c = pc ^ (m & (T::CPR - 1));
+            const int mm = m < mt.rows ? m : 0;
+            int64_t grow;
+            if (GEMM1) grow = clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
+            else grow = mt.row0 + mm;
+            src[j] = reinterpret_cast<const char*>(GEMM1 ? a.x : a.act) + grow * K * 2 + c * 16;
+        }
+    }
+    const int64_t group_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * K * 2;
+    const int r = lane & 15, kg = lane >> 4;
+    const int KIT = K / KC, NIT = G * KIT;
+    const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;  // as in dma_skinny_kernel
+    f32x4_t acc[NB][NT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
+    int ep;
+    float esc;
+    dma_epilogue_token<GEMM1>(a, mt, wave, lane, ep, esc);
+    if (wmover) {
+#pragma unroll
+        for (int j = 0; j < SW - 1; ++j)
+            if (j < NIT) split_issue_w<KC, SW>(lds, j, KIT, G, rot, group_stride, mw, src);
+    } else {
+        split_issue_t<KC>(tring, 0, KIT, mw, src);
+    }
+    for (int it = 0; it < NIT; ++it) {
+        if (!wmover || it + SW - 2 >= NIT) wait_vm<0>();
+        else wait_vm<(SW - 2) * W_INS>();
+        ring_barrier();
+        if (wmover) {
+            if (it + SW - 1 < NIT) split_issue_w<KC, SW>(lds, it + SW - 1, KIT, G, rot, group_stride, mw, src);
+        } else if (it + 1 < NIT) {
+            split_issue_t<KC>(tring, it + 1, KIT, mw, src);
+        }
+        uint8_t* wslot = lds + (it % SW) * T::W_BYTES;
+        uint8_t* tslot = tring + (it & 1) * T::T_BYTES;
+#pragma unroll
+        for (int q = 0; q < T::NS / 4; ++q) {
+            const int c = 4 * (wave * (T::NS / 4) + q) + kg;  // logical chunk of this lane's k-group
+            uint32_t pw[4], pt[2];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int row = 16 * b + r;
+                pw[b] = lds_addr(wslot + row * T::RB + ((c ^ (row & (T::CPR - 1))) << 4));
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int m = 16 * t + r;
+                pt[t] = lds_addr(tslot + m * T::RB + ((c ^ (m & (T::CPR - 1))) << 4));
+            }
+            bf16x8_t w[NB], tk[NT];
+            lds_read6(w, tk, pw, pt);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[b][t] = mfma16(w[b], tk[t], acc[b][t]);
+        }
+        if (it % KIT != KIT - 1) continue;
+        // the result stores of waves 0-1 queue behind their weight DMAs, so the
+        // next weight wait covers them at the cost of a few instructions of the
+        // stage after next
+        dma_group_end<T::W_BYTES, GEMM1>(a, acc, reinterpret_cast<float*>(wslot), mt,
+                                         grp0 + (it / KIT + rot) % G, wave, lane, ep, esc);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -325,9 +499,6 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
 inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
 
 
-#ifndef MOE_DMA_KC
-#define MOE_DMA_KC 256
-#endif
 
 // Row groups per block: as many as leave about one block per CU, so that
 // every CU fills its ring once and no second round of blocks runs on half the
@@ -349,14 +520,14 @@ hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
     const int groups = gemm1 ? a.H / 32 : a.D / 64;
     const int G = groups_per_block(groups, a.P, a.E);
     dim3 g(mtiles_upper(a.P, a.E, 16 * NT), groups / G);
-    const bool wide = MOE_DMA_KC == 256 && K % 256 == 0;
-    if (gemm1) {
-        if (wide) dma_skinny_kernel<NT, 256, 3, true><<<g, kThreads, 0, s>>>(a, G);
-        else dma_skinny_kernel<NT, 128, 6, true><<<g, kThreads, 0, s>>>(a, G);
-    } else {
-        if (wide) dma_skinny_kernel<NT, 256, 3, false><<<g, kThreads, 0, s>>>(a, G);
-        else dma_skinny_kernel<NT, 128, 6, false><<<g, kThreads, 0, s>>>(a, G);
+    const bool wide = K % 256 == 0;
+    if (wide) {
+        if (gemm1) dma_split_kernel<256, 4, true><<<g, kThreads, 0, s>>>(a, G);
+        else dma_split_kernel<256, 4, false><<<g, kThreads, 0, s>>>(a, G);
+        return hipGetLastError();
     }
+    if (gemm1) dma_skinny_kernel<NT, 128, 6, true><<<g, kThreads, 0, s>>>(a, G);
+    else dma_skinny_kernel<NT, 128, 6, false><<<g, kThreads, 0, s>>>(a, G);
     return hipGetLastError();
 }
 
@@ -536,6 +707,16 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
     const bool scale_wave = wave <= C::SWAVES;  // moves one scale DMA per stage
 
     const int lr = lane & 31, g = lane >> 5;
+    // GEMM2 epilogue values of token lr (pair index, routing weight), loaded
+    // before the ring starts (a global load in the loop would come with a
+    // vmcnt(0) wait that drains the wave's DMAs in flight)
+    int ep = 0;
+    float wt = 1.0f;
+    if (!GEMM1) {
+        ep = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (lr < mt.rows ? lr : 0)], a.P);
+        wt = a.wts[ep];
+        asm volatile("" : "+v"(ep), "+v"(wt));
+    }
     f32x16_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x16_t{};
@@ -629,9 +810,7 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
                     if (g == 0) a.act_s[row * (a.H / 32) + col0 / 32] = static_cast<uint8_t>(sc + 127);
                 } else {
                     const int half = wave;  // wave 0: block b0, wave 1: block b1
-                    const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + tok], a.P);
-                    const float wt = a.wts[p];
-                    uint16_t* dst = a.ypair + static_cast<int64_t>(p) * a.D + gidx * R + 32 * (half ? b1 : b0) + 4 * g;
+                    uint16_t* dst = a.ypair + static_cast<int64_t>(ep) * a.D + gidx * R + 32 * (half ? b1 : b0) + 4 * g;
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         float y[4];
