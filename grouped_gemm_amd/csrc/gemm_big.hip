@@ -885,7 +885,12 @@ int device_cu_count() {
     return n;
 }
 
-// Average rows per expert at or above which the 256-row tile is used.
+// Average rows per expert at or above which the 256-row tile is used: bf16
+// from 256 (an expert of 256-270 rows then takes one full tile and one short
+// one instead of two or three 128-row tiles that each stream all its weights;
+// 7% faster on the mid-prefill workload, 256 rows per expert), MX from 512
+// (below that the generic MX kernels run).
+constexpr int64_t kBigTile256MinRowsBf16 = 256;
 constexpr int64_t kBigTile256MinRows = 512;
 
 int64_t big_gemm_mtile_capacity(int64_t P, int E) { return (P + 127) / 128 + E; }
@@ -910,7 +915,7 @@ hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
               reinterpret_cast<const uint8_t*>(b.w2), nullptr,
               b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair, sink_of(b.mtiles, b.P, b.E), b.av};
     int4* tiles = reinterpret_cast<int4*>(b.mtiles);
-    if (b.P >= kBigTile256MinRows * b.E) return launch_big<256, false>(a, tiles, gemm1, s);
+    if (b.P >= kBigTile256MinRowsBf16 * b.E) return launch_big<256, false>(a, tiles, gemm1, s);
     return launch_big<128, false>(a, tiles, gemm1, s);
 }
 
