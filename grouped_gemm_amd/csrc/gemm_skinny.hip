@@ -166,10 +166,10 @@ __device__ __forceinline__ void dma_epilogue_token(const Bf16Args& a, const MTil
     asm volatile("" : "+v"(ep), "+v"(esc));
 }
 
-// End of a row group: sum the four waves' partials (acc[b][t][v]: row 16b +
-// 4kg + v, token 16t + r) in `red` (a just-consumed ring slot of SLOT bytes,
-// PB row blocks per pass, LDS-only barriers so the DMAs in flight keep
-// running), then wave t stores token tile t of group g: GEMM1 the act
+// End of a row group: the four waves' partials (acc[b][t][v]: row 16b +
+// 4kg + v, token 16t + r) meet in `red` (a just-consumed ring slot of SLOT
+// bytes, PB row blocks per pass, LDS-only barriers so the DMAs in flight
+// keep running); wave t sums and stores token tile t of group g: GEMM1 the act
 // columns g*32.. (silu(gate) * up, or the activation variant), GEMM2 the
 // weighted outputs g*64.. of the pair's ypair row.
 template <int SLOT, bool GEMM1>
@@ -191,16 +191,21 @@ __device__ __forceinline__ void dma_group_end(const Bf16Args& a, f32x4_t (&acc)[
                 for (int v = 0; v < 4; ++v)
                     red[((wave * PV) + (b * NT + t) * 4 + v) * 64 + lane] = acc[b0 + b][t][v];
         lds_barrier();
+        // only wave t stores token tile t, so only it sums that tile
+        if (wave < NT) {
 #pragma unroll
-        for (int b = 0; b < PB; ++b)
+            for (int t = 0; t < NT; ++t) {
+                if (t != wave) continue;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+                for (int b = 0; b < PB; ++b)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = ((b * NT + t) * 4 + v) * 64 + lane;
-                    acc[b0 + b][t][v] =
-                        (red[i] + red[PV * 64 + i]) + (red[2 * PV * 64 + i] + red[3 * PV * 64 + i]);
-                }
+                    for (int v = 0; v < 4; ++v) {
+                        const int i = ((b * NT + t) * 4 + v) * 64 + lane;
+                        acc[b0 + b][t][v] =
+                            (red[i] + red[PV * 64 + i]) + (red[2 * PV * 64 + i] + red[3 * PV * 64 + i]);
+                    }
+            }
+        }
     }
     // epilogue: wave w stores token tile w (acc[b][t][v]: row 16b + 4kg + v, token 16t + r)
 #pragma unroll
