@@ -35,6 +35,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -123,16 +124,25 @@ KERNEL_FILES = {"dma_split_kernel": "gemm_skinny.hip", "dma_skinny_kernel": "gem
                 "combine_kernel": "gemm_bf16.hip"}
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and blank space removed (string literals in
+    these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(symbol: str) -> str:
-    """Digest of the source file defining `symbol` plus the shared header: a
-    change to either invalidates counters stored for that kernel."""
+    """Digest of the code (comments and spacing aside) of the source file
+    defining `symbol` plus the shared header: a change to either invalidates
+    counters stored for that kernel."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "grouped_gemm_amd", "csrc")
     for f in ("common.h", KERNEL_FILES.get(symbol, "")):
         path = os.path.join(d, f)
         if f and os.path.isfile(path):
             h.update(f.encode())
-            h.update(open(path, "rb").read())
+            h.update(_code_only(open(path, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -489,9 +489,9 @@ __global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) 
                 for (int t = 0; t < NT; ++t) acc[b][t] = mfma16(w[b], tk[t], acc[b][t]);
         }
         if (it % KIT != KIT - 1) continue;
-        // the result stores of waves 0-1 queue behind their weight DMAs, so the
-        // next weight wait covers them at the cost of a few instructions of the
-        // stage after next
+        // the result stores of waves 0-1 count in their vmcnt too: the next
+        // weight wait may then also wait for a few DMAs of the stage after the
+        // one it needs, never for fewer than that stage's
         dma_group_end<T::W_BYTES, GEMM1>(a, acc, reinterpret_cast<float*>(wslot), mt,
                                          grp0 + (it / KIT + rot) % G, wave, lane, ep, esc);
 #pragma unroll
