@@ -21,7 +21,10 @@
 //  * a multi-stage LDS ring whose waits are explicit: a fence-free barrier
 //    and per-wave vmcnt budgets keep the later stages in flight (the
 //    __syncthreads() fence, or a compiler-inserted wait before an LDS read
-//    it cannot tell apart from the slots being filled, would drain it).
+//    it cannot tell apart from the slots being filled, would drain it);
+//    with the weights and the tokens on rings of their own, moved by
+//    different waves, the weight ring keeps three stages in flight
+//    (dma_split_kernel).
 //
 // GEMM1: a block owns 32 act columns h..h+31 of one expert per row group:
 // gate rows h..h+31 and up rows H+h..H+h+31 of W1 (the gate/up pairing of
