@@ -117,7 +117,7 @@ def kernel_work(cfg, mode, hit, dtype):
 
 
 KERNEL_FILES = {"dma_split_kernel": "gemm_skinny.hip", "dma_skinny_kernel": "gemm_skinny.hip",
-                "mx4_skinny_kernel": "gemm_skinny.hip",
+                "mx_skinny_kernel": "gemm_skinny.hip",
                 "big_gemm_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
                 "gemm1_swiglu_kernel": "gemm_bf16.hip", "gemm2_weight_kernel": "gemm_bf16.hip",
@@ -162,11 +162,13 @@ def kernel_symbol(cfg, mode, stage):
         if cfg.P >= 512 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
         if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
-            return "mx4_skinny_kernel"
+            return "mx_skinny_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.dtype == "mxfp8":
         if cfg.P >= 512 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
+        if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
+            return "mx_skinny_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.P <= 32 * cfg.E:
         return "dma_split_kernel" if (cfg.D if g1 else cfg.H) % 256 == 0 else "dma_skinny_kernel"

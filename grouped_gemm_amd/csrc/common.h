@@ -198,9 +198,9 @@ struct MxArgs {
     bool w4;            // MXFP4 weights: w1, w2 packed e2m1 [E, 2H, D/2], [E, D, H/2]
 };
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
-// Decode-shaped MXFP4-weight GEMM1 / GEMM2 (weights streamed on the MFMA's row side).
-bool skinny_mx4_supported(const MxArgs& a);
-hipError_t launch_skinny_mx4(const MxArgs& a, bool gemm1, hipStream_t s);
+// Decode-shaped MX GEMM1 / GEMM2, e2m1 or e4m3 weights (streamed on the MFMA's row side).
+bool skinny_mx_supported(const MxArgs& a);
+hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s);
 // MXQ4: fp32 [rows, K] -> packed e2m1 codes [rows, K/2] + e8m0 [rows, K/32].
 hipError_t launch_mx4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);

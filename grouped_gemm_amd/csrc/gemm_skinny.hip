@@ -546,55 +546,58 @@ hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s) { return launch
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s) { return launch_dma(a, false, s); }
 
 // ---------------------------------------------------------------------------
-// Decode-shaped MXFP4-weight GEMMs ("GC-MoE on SM120", scale formats: E2M1
-// weights with a UE8M0 exponent per 32 along K; MX-fp8 activations). The
-// same streaming design as above: weights on the MFMA's row side, a ring of
-// S stages filled by global->LDS DMA of whole row segments, one barrier per
-// stage, the four waves splitting each stage's K steps and meeting in LDS at
-// the end of a row group. MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with the
-// e2m1 weights as A (16 contiguous bytes per lane: K values 32g..32g+31 of
-// the 64-wide step, g = lane >> 5) and the e4m3 tokens as B (16-byte chunks
-// g and 2 + g of the step); lane group g supplies the scale of 32-block g
-// (layouts measured on gfx950 with in-bounds probes).
+// Decode-shaped MX GEMMs: MX-fp8 activations ("Prime Flash MoE", section
+// 7) against e2m1 weights ("GC-MoE on SM120", scale formats: a UE8M0
+// exponent per 32 along K) or e4m3 weights. The same streaming design as
+// above: weights on the MFMA's row side, a ring of S stages filled by
+// global->LDS DMA of whole row segments, one barrier per stage, the four
+// waves splitting each stage's K steps and meeting in LDS at the end of a
+// row group. MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with the weights as A
+// (e2m1: 16 contiguous bytes per lane, K values 32g..32g+31 of the 64-wide
+// step, g = lane >> 5; e4m3: 16-byte chunks g and 2 + g of the step) and the
+// e4m3 tokens as B (chunks g and 2 + g); lane group g supplies the scale of
+// 32-block g (layouts measured on gfx950 with in-bounds probes).
 //
-// Stage (K step of KC = 512 values): R weight rows x 256 bytes, 32 token
-// rows x 512 bytes, and each row's 16 scale bytes. With R = 128 a stage
-// carries twice the weight bytes of its token bytes (R = 64: as many), so
-// more of the ring's bytes in flight are weights. Chunks are XOR-swizzled by
-// the row (weights: ^ (row & 15) over 16 chunks, tokens: ^ (row & 31) over
-// 32), so the 16 rows a fragment read touches hit 16 distinct bank groups.
-// Waves 0 .. R/64 - 1 also move the weight rows' scales, wave R/64 the
-// tokens'.
+// Stage (K step of KC = 512 values): R weight rows x 256 (e2m1) or 512
+// (e4m3) bytes, 32 token rows x 512 bytes, and each row's 16 scale bytes.
+// R = 128 e2m1 rows or 64 e4m3 rows make 32 KB of weights per stage, twice
+// the token bytes, so most of the ring's bytes in flight are weights.
+// Chunks are XOR-swizzled by the row over the row's chunks (^ (row & 15) or
+// ^ (row & 31)), so the rows a fragment read touches hit distinct bank
+// groups. Waves 0 .. R/64 - 1 also move the weight rows' scales, wave R/64
+// the tokens'.
 namespace {
 
 constexpr int kMx4KC = 512;   // K values per stage
 constexpr int kMx4BM = 32;    // token rows per m-tile
 
-template <int R>
+template <int R, bool W4>
 struct Mx4 {
     static constexpr int NB = R / 32;                 // weight row blocks (32-row MFMA tiles)
-    static constexpr int WRB = kMx4KC / 2;            // weight bytes per row per stage (256)
+    static constexpr int WRB = W4 ? kMx4KC / 2 : kMx4KC;  // weight bytes per row per stage (256 or 512)
+    static constexpr int WCH = WRB / 16;              // 16-byte chunks per weight row per stage
+    static constexpr int WRPI = 64 / WCH;             // weight rows per DMA instruction
     static constexpr int TRB = kMx4KC;                // token bytes per row per stage (512)
     static constexpr int WB = R * WRB;
     static constexpr int TB = kMx4BM * TRB;           // 16 KB
     static constexpr int SW = WB + TB;                // weight scale rows (R x 16 bytes)
     static constexpr int ST = SW + R * 16;            // token scale rows (32 x 16 bytes, then a 512-byte pad)
     static constexpr int STAGE = ST + 64 * 16;
-    static constexpr int S = R == 64 ? 4 : 3;         // ring stages
+    static constexpr int S = 160 * 1024 / STAGE < 4 ? 160 * 1024 / STAGE : 4;  // ring stages
     static constexpr int WINS = WB / 1024 / 4;        // weight DMA instructions per wave per stage
     static constexpr int TINS = TB / 1024 / 4;        // token DMA instructions per wave per stage
     static constexpr int SWAVES = R / 64;             // waves that move weight scale rows
-    static_assert(S * STAGE <= 160 * 1024, "ring must fit the LDS of a CU");
+    static_assert(S >= 3, "the ring needs three stages");
     static_assert(4 * 2 * 16 * 64 * 4 <= STAGE, "a two-block pass of the group reduction must fit one ring slot");
 };
 
 // this wave's DMAs of ring stage `it` (row group grp relative to the
 // block's first, K step kit) into slot it % S
-template <int R>
+template <int R, bool W4>
 __device__ __forceinline__ void mx4_dma_issue(uint8_t* ring, int it, int grp, int kit, int64_t wgroup_stride,
                                               int64_t sgroup_stride, const char* const* wsrc,
                                               const char* const* tsrc, const char* ssrc) {
-    using C = Mx4<R>;
+    using C = Mx4<R, W4>;
     const int wave = threadIdx.x >> 6;
     uint8_t* slot = ring + (it % C::S) * C::STAGE;
     const int64_t wb = static_cast<int64_t>(kit) * C::WRB + grp * wgroup_stride;
@@ -657,13 +660,36 @@ __device__ __forceinline__ void mx4_lds_read(u32x4_t (&w)[4], u32x4_t& tlo, u32x
         : "memory");
 }
 
+// The same for e4m3 weights (two 16-byte chunks per row block, as the tokens).
+__device__ __forceinline__ void mx8_lds_read(u32x4_t (&wlo)[2], u32x4_t (&whi)[2], u32x4_t& tlo, u32x4_t& thi,
+                                             uint32_t (&sw)[2], uint32_t& st, const uint32_t (&awl)[2],
+                                             const uint32_t (&awh)[2], uint32_t atl, uint32_t ath,
+                                             const uint32_t (&as)[2], uint32_t ast) {
+    asm volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b128 %1, %10\n\t"
+        "ds_read_b128 %2, %11\n\t"
+        "ds_read_b128 %3, %12\n\t"
+        "ds_read_b128 %4, %13\n\t"
+        "ds_read_b128 %5, %14\n\t"
+        "ds_read_u8 %6, %15\n\t"
+        "ds_read_u8 %7, %16\n\t"
+        "ds_read_u8 %8, %17\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(wlo[0]), "=&v"(whi[0]), "=&v"(wlo[1]), "=&v"(whi[1]), "=&v"(tlo), "=&v"(thi), "=&v"(sw[0]),
+          "=&v"(sw[1]), "=&v"(st)
+        : "v"(awl[0]), "v"(awh[0]), "v"(awl[1]), "v"(awh[1]), "v"(atl), "v"(ath), "v"(as[0]), "v"(as[1]), "v"(ast)
+        : "memory");
+}
+
 // grid: (m-tiles of 32 rows, row groups / G). GEMM1: a group is R/2 act
 // columns h..h+R/2-1 (gate rows h.., up rows H+h..), requantized to MX-fp8 in
 // the epilogue (each 32 columns are one scale block); GEMM2: R output
 // features, scaled by the routing weight into ypair.
-template <int R, bool GEMM1>
-__global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
-    using C = Mx4<R>;
+template <int R, bool GEMM1, bool W4>
+__global__ __launch_bounds__(kThreads) void mx_skinny_kernel(MxArgs a, int G) {
+    using C = Mx4<R, W4>;
+    static_assert(W4 || R == 64, "e4m3 weights: 64 rows per block");
     constexpr int NB = C::NB, HALF = R / 2;
     __shared__ __attribute__((aligned(16))) uint8_t ring[C::S * C::STAGE];
     MTile mt;
@@ -681,13 +707,14 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
         }
         return static_cast<int64_t>(mt.expert) * a.D + grp0 * R + row;
     };
-    // weight DMA: instruction j of a wave covers rows (wave * WINS + j) * 4 + lane / 16, 16 chunks each
+    // weight DMA: instruction j of a wave covers rows (wave * WINS + j) * WRPI + lane / WCH, WCH chunks each
+    const int64_t rowb = W4 ? K / 2 : K;  // weight row bytes
     const char* wsrc[C::WINS];
 #pragma unroll
     for (int j = 0; j < C::WINS; ++j) {
-        const int row = (wave * C::WINS + j) * 4 + lane / 16;
-        const int c = (lane & 15) ^ (row & 15);
-        wsrc[j] = reinterpret_cast<const char*>(wbase) + wrow(row) * (K / 2) + c * 16;
+        const int row = (wave * C::WINS + j) * C::WRPI + lane / C::WCH;
+        const int c = (lane & (C::WCH - 1)) ^ (row & (C::WCH - 1));
+        wsrc[j] = reinterpret_cast<const char*>(wbase) + wrow(row) * rowb + c * 16;
     }
     // token DMA: rows (wave * TINS + j) * 2 + lane / 32, 32 chunks each
     auto trow = [&](int m) -> int64_t {
@@ -707,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
     // scale DMA source: wave w < SWAVES lane i -> weight row 64w + i; wave SWAVES lane i -> token row i & 31
     const char* ssrc = wave < C::SWAVES ? reinterpret_cast<const char*>(wsbase) + wrow(64 * wave + lane) * KB
                                         : reinterpret_cast<const char*>(tsbase) + trow(lane & 31) * KB;
-    const int64_t wgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * (K / 2);
+    const int64_t wgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * rowb;
     const int64_t sgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * KB;
     const int KIT = K / kMx4KC, NIT = G * KIT;
     // GEMM2 rotates the order of its groups per block (see dma_skinny_kernel)
@@ -731,7 +758,8 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
 #pragma unroll
     for (int j = 0; j < C::S - 1; ++j)
         if (j < NIT)
-            mx4_dma_issue<R>(ring, j, (j / KIT + rot) % G, j % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc, ssrc);
+            mx4_dma_issue<R, W4>(ring, j, (j / KIT + rot) % G, j % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc,
+                                 ssrc);
     for (int it = 0; it < NIT; ++it) {
         if (it + C::S - 2 < NIT) {
             if (scale_wave) wait_vm<(C::S - 2) * (C::WINS + C::TINS + 1)>();
@@ -742,32 +770,54 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
         ring_barrier();
         if (it + C::S - 1 < NIT) {
             const int nx = it + C::S - 1;
-            mx4_dma_issue<R>(ring, nx, (nx / KIT + rot) % G, nx % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc,
-                             ssrc);
+            mx4_dma_issue<R, W4>(ring, nx, (nx / KIT + rot) % G, nx % KIT, wgroup_stride, sgroup_stride, wsrc,
+                                 tsrc, ssrc);
         }
         uint8_t* slot = ring + (it % C::S) * C::STAGE;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int s = 2 * wave + q;  // this wave's 64-wide K step of the stage
-            const int cw = 2 * s + g;    // weight chunk (16 bytes = 32 e2m1 values)
-            const int ct = 4 * s + g;    // token chunks ct and ct + 2
-            u32x4_t w[NB], tlo, thi;
-            uint32_t sw[NB], st, aw[NB], as[NB];
+            const int ct = 4 * s + g;    // token chunks ct and ct + 2 (and e4m3 weight chunks)
+            uint32_t sw[NB], st, as[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int row = 32 * b + lr;
-                aw[b] = lds_addr(slot + row * C::WRB + ((cw ^ (row & 15)) << 4));
-                as[b] = lds_addr(slot + C::SW + row * 16 + 2 * s + g);
+            for (int b = 0; b < NB; ++b) as[b] = lds_addr(slot + C::SW + (32 * b + lr) * 16 + 2 * s + g);
+            const uint32_t atl = lds_addr(slot + C::WB + lr * C::TRB + ((ct ^ lr) << 4));
+            const uint32_t ath = lds_addr(slot + C::WB + lr * C::TRB + (((ct + 2) ^ lr) << 4));
+            const uint32_t ast = lds_addr(slot + C::ST + lr * 16 + 2 * s + g);
+            u32x4_t tlo, thi;
+            i32x8_t aa[NB];
+            if constexpr (W4) {
+                const int cw = 2 * s + g;  // weight chunk (16 bytes = 32 e2m1 values)
+                u32x4_t w[NB];
+                uint32_t aw[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int row = 32 * b + lr;
+                    aw[b] = lds_addr(slot + row * C::WRB + ((cw ^ (row & (C::WCH - 1))) << 4));
+                }
+                mx4_lds_read(w, tlo, thi, sw, st, aw, atl, ath, as, ast);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) aa[b] = i32x8_t{(int)w[b].x, (int)w[b].y, (int)w[b].z, (int)w[b].w, 0, 0, 0, 0};
+            } else {
+                u32x4_t wlo[NB], whi[NB];
+                uint32_t awl[NB], awh[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int row = 32 * b + lr;
+                    awl[b] = lds_addr(slot + row * C::WRB + ((ct ^ (row & (C::WCH - 1))) << 4));
+                    awh[b] = lds_addr(slot + row * C::WRB + (((ct + 2) ^ (row & (C::WCH - 1))) << 4));
+                }
+                mx8_lds_read(wlo, whi, tlo, thi, sw, st, awl, awh, atl, ath, as, ast);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    aa[b] = i32x8_t{(int)wlo[b].x, (int)wlo[b].y, (int)wlo[b].z, (int)wlo[b].w,
+                                    (int)whi[b].x, (int)whi[b].y, (int)whi[b].z, (int)whi[b].w};
             }
-            mx4_lds_read(w, tlo, thi, sw, st, aw, lds_addr(slot + C::WB + lr * C::TRB + ((ct ^ lr) << 4)),
-                         lds_addr(slot + C::WB + lr * C::TRB + (((ct + 2) ^ lr) << 4)), as,
-                         lds_addr(slot + C::ST + lr * 16 + 2 * s + g));
             const i32x8_t bt{(int)tlo.x, (int)tlo.y, (int)tlo.z, (int)tlo.w, (int)thi.x, (int)thi.y, (int)thi.z, (int)thi.w};
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const i32x8_t aa{(int)w[b].x, (int)w[b].y, (int)w[b].z, (int)w[b].w, 0, 0, 0, 0};
-                acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aa, bt, acc[b], 4, 0, 0, (int)sw[b], 0, (int)st);
-            }
+            for (int b = 0; b < NB; ++b)
+                acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aa[b], bt, acc[b], W4 ? 4 : 0, 0, 0, (int)sw[b],
+                                                                         0, (int)st);
         }
         if (it % KIT != KIT - 1) continue;
         // group finished: the four waves' partial sums meet in this slot, two
@@ -834,26 +884,29 @@ __global__ __launch_bounds__(kThreads) void mx4_skinny_kernel(MxArgs a, int G) {
     }
 }
 
-#ifndef MOE_MX4_ROWS
-#define MOE_MX4_ROWS 128
-#endif
-
 }  // namespace
 
-// Decode-shaped MXFP4 GEMMs: up to 32 rows per expert on average, K (D for
-// GEMM1, H for GEMM2) a multiple of the 512-value stage, and whole row groups.
-bool skinny_mx4_supported(const MxArgs& a) {
-    return a.w4 && a.P <= int64_t(32) * a.E && a.D % kMx4KC == 0 && a.H % kMx4KC == 0 &&
-           a.H % (MOE_MX4_ROWS / 2) == 0 && a.D % MOE_MX4_ROWS == 0;
+// Decode-shaped MX GEMMs: up to 32 rows per expert on average, K (D for
+// GEMM1, H for GEMM2) a multiple of the 512-value stage, and whole row
+// groups (e2m1 weights: 128 rows per block, e4m3: 64).
+bool skinny_mx_supported(const MxArgs& a) {
+    const int R = a.w4 ? 128 : 64;
+    return a.P <= int64_t(32) * a.E && a.D % kMx4KC == 0 && a.H % kMx4KC == 0 && a.H % (R / 2) == 0 &&
+           a.D % R == 0;
 }
 
-hipError_t launch_skinny_mx4(const MxArgs& a, bool gemm1, hipStream_t s) {
-    constexpr int R = MOE_MX4_ROWS;
+hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s) {
+    const int R = a.w4 ? 128 : 64;
     const int groups = gemm1 ? a.H / (R / 2) : a.D / R;
     const int G = groups_per_block(groups, a.P, a.E);
     dim3 g(mtiles_upper(a.P, a.E, kMx4BM), groups / G);
-    if (gemm1) mx4_skinny_kernel<R, true><<<g, kThreads, 0, s>>>(a, G);
-    else mx4_skinny_kernel<R, false><<<g, kThreads, 0, s>>>(a, G);
+    if (a.w4) {
+        if (gemm1) mx_skinny_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G);
+        else mx_skinny_kernel<128, false, true><<<g, kThreads, 0, s>>>(a, G);
+    } else {
+        if (gemm1) mx_skinny_kernel<64, true, false><<<g, kThreads, 0, s>>>(a, G);
+        else mx_skinny_kernel<64, false, false><<<g, kThreads, 0, s>>>(a, G);
+    }
     return hipGetLastError();
 }
 

@@ -569,14 +569,14 @@ hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev) {
     const bool big = big_mx_supported(a);
     const dim3 g1(mtiles_upper(a.P, a.E, BM), a.H / (BN1 / 2));
     const dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
-    const bool skinny = !big && skinny_mx4_supported(a);
+    const bool skinny = !big && skinny_mx_supported(a);
     if (big) launch_big_mx(a, true, s);
-    else if (skinny) launch_skinny_mx4(a, true, s);
+    else if (skinny) launch_skinny_mx(a, true, s);
     else if (a.w4) mx_gemm1_kernel<BM, BN1, true><<<g1, kThreads, 0, s>>>(a);
     else mx_gemm1_kernel<BM, BN1, false><<<g1, kThreads, 0, s>>>(a);
     record(ev, 0, s);
     if (big) launch_big_mx(a, false, s);
-    else if (skinny) launch_skinny_mx4(a, false, s);
+    else if (skinny) launch_skinny_mx(a, false, s);
     else if (a.w4) mx_gemm2_kernel<BM, BN2, true><<<g2, kThreads, 0, s>>>(a);
     else mx_gemm2_kernel<BM, BN2, false><<<g2, kThreads, 0, s>>>(a);
     record(ev, 1, s);

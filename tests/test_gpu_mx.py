@@ -52,10 +52,12 @@ def _mx_inputs(cfg, seed=0):
     return src, q
 
 
-def _case(cfg, tokens=None, seed=0, mode="split"):
+def _case(cfg, tokens=None, seed=0, mode="split", ids=None):
     import grouped_gemm_amd as g
     print(f"mx forward {cfg.name} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k} mode={mode}", flush=True)
     src, q = _mx_inputs(cfg, seed)
+    if ids is not None:
+        src["topk_ids"] = ids
     (xc, xs), (w1c, w1s), (w2c, w2s) = q["x"], q["w1"], q["w2"]
     out = g.moe_ffn_forward(to_gpu(xc), to_gpu(w1c), to_gpu(w2c), to_gpu(src["topk_ids"]),
                             to_gpu(src["topk_weights"]), mode=mode, x_scale=to_gpu(xs),
@@ -89,6 +91,34 @@ def test_mx_forward_prefill_tiles(T, D, H, E, k, routing, grid_limit, monkeypatc
     if grid_limit:
         monkeypatch.setenv("MOE_FFN_GRID_LIMIT", grid_limit)
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (64, 512, 512, 8, 2, "softmax"),     # decode kernel: one K stage per 512, one row group per block
+    (1, 512, 512, 4, 2, "uniform"),      # one token
+    (100, 1024, 512, 16, 4, "zipf"),     # ragged, several K stages
+    (256, 512, 1024, 16, 2, "zipf"),     # skewed: experts with several 32-row m-tiles
+    (64, 512, 512, 32, 8, "softmax"),    # several row groups per block
+])
+def test_mx_decode_kernel(T, D, H, E, k, routing):
+    """Shapes the decode-shaped MX kernel takes with e4m3 weights (<= 32 rows per
+    expert on average, D and H multiples of 512)."""
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
+def test_mx_decode_dims_in_full():
+    """The MX workload's dims at 64 tokens (D=4096, H=1536, E=64, top-6): the
+    decode kernel on every token."""
+    _case(mi.custom(64, 4096, 1536, 64, 6, "softmax", dtype="mxfp8"))
+
+
+def test_mx_decode_kernel_dropped_routes():
+    cfg = mi.custom(96, 512, 512, 8, 3, "softmax", dtype="mxfp8")
+    ids, _ = mi.routing(cfg, 0)
+    ids = ids.copy()
+    ids[::5, 0] = -1                     # dropped routes contribute nothing
+    ids[::9, 2] = cfg.E + 3
+    _case(cfg, ids=ids)
 
 
 def test_mx_prefill_descriptor_reload(monkeypatch):
