@@ -159,13 +159,13 @@ def kernel_symbol(cfg, mode, stage):
         return "combine_kernel"
     g1 = stage == "gemm1_swiglu"
     if cfg.dtype == "mxfp4":
-        if cfg.P >= 512 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
+        if cfg.P >= 128 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
         if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
             return "mx_skinny_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.dtype == "mxfp8":
-        if cfg.P >= 512 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
+        if cfg.P >= 128 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
         if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
             return "mx_skinny_kernel"
