@@ -170,7 +170,7 @@ def kernel_symbol(cfg, mode, stage):
         if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
             return "mx_skinny_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
-    if cfg.P <= 32 * cfg.E:
+    if cfg.P <= 24 * cfg.E:
         return "dma_split_kernel" if (cfg.D if g1 else cfg.H) % 256 == 0 else "dma_skinny_kernel"
     if cfg.D % 256 == 0:
         return "big_gemm_kernel"

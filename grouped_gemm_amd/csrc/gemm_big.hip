@@ -886,13 +886,14 @@ int device_cu_count() {
 }
 
 // Average rows per expert at or above which the 256-row tile is used: bf16
-// from 256 (an expert of 256-270 rows then takes one full tile and one short
-// one instead of two or three 128-row tiles that each stream all its weights;
-// 7% faster on the mid-prefill workload, 256 rows per expert). MX has only
+// from 128 (an expert of 128-256 rows then takes one 256-row tile instead of
+// two 128-row tiles that each stream all its weights: 7% faster at 256 rows
+// per expert, 6% at 128; at 64 rows per expert the 128-row tile is 20%
+// faster). MX has only
 // the 256-row tile here and takes it from 128 rows per expert (the generic
 // MX kernels below that): measured 28-38% faster than the generic kernels at
 // 192-384 rows per expert, within 3% at 48-96.
-constexpr int64_t kBigTile256MinRowsBf16 = 256;
+constexpr int64_t kBigTile256MinRowsBf16 = 128;
 constexpr int64_t kBigMxMinRows = 128;
 
 int64_t big_gemm_mtile_capacity(int64_t P, int E) { return (P + 127) / 128 + E; }
