@@ -34,6 +34,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -146,6 +147,28 @@ def source_digest(symbol: str) -> str:
     return h.hexdigest()[:16]
 
 
+def decode_kernels_fit(T, k, E):
+    """Mirror of the library's rule for the decode-shaped kernels: fewer than
+    0.5 experts expected past 32 rows with uniformly spread routes."""
+    if T <= 0 or k <= 0 or E <= 0 or k > E:
+        return False
+    p = k / E
+    if T * p > 32.0:
+        return False
+    if T <= 32:
+        return True
+    if p >= 1.0:
+        return False
+    lp, lq = math.log(p), math.log1p(-p)
+    tail = 0.0
+    for x in range(33, T + 1):
+        t = math.exp(math.lgamma(T + 1) - math.lgamma(x + 1) - math.lgamma(T - x + 1) + x * lp + (T - x) * lq)
+        tail += t
+        if t < 1e-12 * (tail + 1e-300) and x > 33 + 4 * math.sqrt(T * p):
+            break
+    return E * tail < 0.5
+
+
 def kernel_symbol(cfg, mode, stage):
     """The HIP kernel a stage runs for this workload (mirrors the library's dispatch)."""
     if mode == "fused":
@@ -161,16 +184,16 @@ def kernel_symbol(cfg, mode, stage):
     if cfg.dtype == "mxfp4":
         if cfg.P >= 128 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
-        if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
+        if decode_kernels_fit(cfg.T, cfg.k, cfg.E) and cfg.D % 512 == 0 and cfg.H % 512 == 0:
             return "mx_skinny_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
     if cfg.dtype == "mxfp8":
         if cfg.P >= 128 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
             return "big_gemm_kernel"
-        if cfg.P <= 32 * cfg.E and cfg.D % 512 == 0 and cfg.H % 512 == 0:
+        if decode_kernels_fit(cfg.T, cfg.k, cfg.E) and cfg.D % 512 == 0 and cfg.H % 512 == 0:
             return "mx_skinny_kernel"
         return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
-    if cfg.P <= 24 * cfg.E:
+    if decode_kernels_fit(cfg.T, cfg.k, cfg.E):
         return "dma_split_kernel" if (cfg.D if g1 else cfg.H) % 256 == 0 else "dma_skinny_kernel"
     if cfg.D % 256 == 0:
         return "big_gemm_kernel"

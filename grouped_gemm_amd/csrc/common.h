@@ -177,13 +177,17 @@ int64_t big_gemm_workspace_bytes(int64_t P, int E);
 // read and clamped, never written).
 constexpr int64_t kRowMapPad = 256;
 hipError_t launch_big_gemm(const Bf16Args& a, bool gemm1, hipStream_t s);
-// Average rows per expert at or below which the split pipeline uses them.
-// The decode kernels take 32-row m-tiles and about one block per CU; near 32
-// rows per expert on average some experts need a second m-tile, and the
-// blocks past one per CU run as a second round (measured at 32 rows per
-// expert: 0.71 ms against 0.56 with the prefill kernels at the decode
-// workload's dims). At 20-24 rows per expert they are 21% faster there.
-constexpr int64_t kSkinnyMaxRowsPerExpert = 24;
+// Whether the decode-shaped kernels suit a batch of T tokens with k routes
+// each over E experts. They take 32-row m-tiles and about one block per CU
+// (the row groups per block are chosen for that), so every expert past 32
+// rows adds a second m-tile, and the blocks past one per CU run as a second
+// round. They are used while, with routes spread uniformly (each token's k
+// experts distinct), fewer than 0.5 experts are expected past 32 rows:
+// E * P(Binomial(T, k/E) > 32) < 0.5. Measured against the prefill or
+// generic kernels: 21% faster at 20-24 rows per expert with 32 experts,
+// 19% at 18 with 64; 20-26% slower at 24 with 64 or 128 experts and at 32
+// with 32 or 64.
+bool decode_kernels_fit(int64_t T, int k, int E);
 hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
 
 struct MxArgs {

@@ -479,7 +479,7 @@ hipError_t launch_gemms_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     // give the prefill ring fewer tiles than half the CUs, so it streams too.
     const int64_t ring_tiles = (a.P / 128 + a.E) * (a.H / 128);
     const bool skinny =
-        a.P <= kSkinnyMaxRowsPerExpert * a.E || (a.E == 1 && ring_tiles < device_cu_count() / 2);
+        decode_kernels_fit(a.T, a.k, a.E) || (a.E == 1 && ring_tiles < device_cu_count() / 2);
     const bool big = !skinny && big_gemm_supported(a);
     if (skinny) {
         launch_skinny_gemm1(a, s);

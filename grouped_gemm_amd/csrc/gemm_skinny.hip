@@ -32,6 +32,8 @@
 // on the accumulators. GEMM2: a block owns 64 output features per row
 // group; the epilogue scales by the routing weight and writes the pair's
 // row for the segmented combine.
+#include <cmath>
+
 #include "common.h"
 #include "mxq.h"
 
@@ -886,12 +888,31 @@ __global__ __launch_bounds__(kThreads) void mx_skinny_kernel(MxArgs a, int G) {
 
 }  // namespace
 
-// Decode-shaped MX GEMMs: up to 32 rows per expert on average, K (D for
+bool decode_kernels_fit(int64_t T, int k, int E) {
+    if (T <= 0 || k <= 0 || E <= 0 || k > E) return false;
+    const double p = static_cast<double>(k) / E;
+    if (static_cast<double>(T) * p > 32.0) return false;
+    if (T <= 32) return true;
+    if (p >= 1.0) return false;
+    // upper tail of Binomial(T, p) from 33, summed in log space until it stops mattering
+    const double lp = std::log(p), lq = std::log1p(-p);
+    double tail = 0.0;
+    for (int64_t x = 33; x <= T; ++x) {
+        const double lpmf = std::lgamma(static_cast<double>(T) + 1) - std::lgamma(static_cast<double>(x) + 1) -
+                            std::lgamma(static_cast<double>(T - x) + 1) + x * lp + (T - x) * lq;
+        const double t = std::exp(lpmf);
+        tail += t;
+        if (t < 1e-12 * (tail + 1e-300) && x > 33 + 4 * std::sqrt(static_cast<double>(T) * p)) break;
+    }
+    return E * tail < 0.5;
+}
+
+// Decode-shaped MX GEMMs: few rows per expert (decode_kernels_fit), K (D for
 // GEMM1, H for GEMM2) a multiple of the 512-value stage, and whole row
 // groups (e2m1 weights: 128 rows per block, e4m3: 64).
 bool skinny_mx_supported(const MxArgs& a) {
     const int R = a.w4 ? 128 : 64;
-    return a.P <= int64_t(32) * a.E && a.D % kMx4KC == 0 && a.H % kMx4KC == 0 && a.H % (R / 2) == 0 &&
+    return decode_kernels_fit(a.T, a.k, a.E) && a.D % kMx4KC == 0 && a.H % kMx4KC == 0 && a.H % (R / 2) == 0 &&
            a.D % R == 0;
 }
 

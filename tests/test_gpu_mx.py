@@ -96,13 +96,13 @@ def test_mx_forward_prefill_tiles(T, D, H, E, k, routing, grid_limit, monkeypatc
 @pytest.mark.parametrize("T,D,H,E,k,routing", [
     (64, 512, 512, 8, 2, "softmax"),     # decode kernel: one K stage per 512, one row group per block
     (1, 512, 512, 4, 2, "uniform"),      # one token
-    (100, 1024, 512, 16, 4, "zipf"),     # ragged, several K stages
-    (256, 512, 1024, 16, 2, "zipf"),     # skewed: experts with several 32-row m-tiles
+    (60, 1024, 512, 16, 4, "zipf"),      # ragged, several K stages
+    (128, 512, 1024, 16, 2, "zipf"),     # skewed: experts with several 32-row m-tiles
     (64, 512, 512, 32, 8, "softmax"),    # several row groups per block
 ])
 def test_mx_decode_kernel(T, D, H, E, k, routing):
-    """Shapes the decode-shaped MX kernel takes with e4m3 weights (<= 32 rows per
-    expert on average, D and H multiples of 512)."""
+    """Shapes the decode-shaped MX kernel takes with e4m3 weights (fewer than 0.5
+    experts expected past 32 rows, D and H multiples of 512)."""
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
@@ -113,7 +113,7 @@ def test_mx_decode_dims_in_full():
 
 
 def test_mx_decode_kernel_dropped_routes():
-    cfg = mi.custom(96, 512, 512, 8, 3, "softmax", dtype="mxfp8")
+    cfg = mi.custom(64, 512, 512, 8, 3, "softmax", dtype="mxfp8")
     ids, _ = mi.routing(cfg, 0)
     ids = ids.copy()
     ids[::5, 0] = -1                     # dropped routes contribute nothing
