@@ -34,7 +34,6 @@ import argparse
 import ctypes
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -118,6 +117,7 @@ def kernel_work(cfg, mode, hit, dtype):
 
 
 KERNEL_FILES = {"dma_split_kernel": "gemm_skinny.hip", "dma_skinny_kernel": "gemm_skinny.hip",
+                "mx_fused_kernel": "mx.hip",
                 "mx_skinny_kernel": "gemm_skinny.hip",
                 "big_gemm_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
@@ -147,57 +147,23 @@ def source_digest(symbol: str) -> str:
     return h.hexdigest()[:16]
 
 
-def decode_kernels_fit(T, k, E):
-    """Mirror of the library's rule for the decode-shaped kernels: fewer than
-    0.5 experts expected past 32 rows with uniformly spread routes."""
-    if T <= 0 or k <= 0 or E <= 0 or k > E:
-        return False
-    p = k / E
-    if T * p > 32.0:
-        return False
-    if T <= 32:
-        return True
-    if p >= 1.0:
-        return False
-    lp, lq = math.log(p), math.log1p(-p)
-    tail = 0.0
-    for x in range(33, T + 1):
-        t = math.exp(math.lgamma(T + 1) - math.lgamma(x + 1) - math.lgamma(T - x + 1) + x * lp + (T - x) * lq)
-        tail += t
-        if t < 1e-12 * (tail + 1e-300) and x > 33 + 4 * math.sqrt(T * p):
-            break
-    return E * tail < 0.5
-
-
 def kernel_symbol(cfg, mode, stage):
-    """The HIP kernel a stage runs for this workload (mirrors the library's dispatch)."""
-    if mode == "fused":
-        return {"fused_ffn": "fused_bf16_kernel", "acc_fill": "fill_zero_f32_kernel",
-                "acc_to_bf16": "f32_to_bf16_kernel", "route": "route kernels"}[stage]
+    """The HIP kernel a stage runs for this workload (the GEMM stages ask the
+    library's own dispatch, moe_ffn_gemm_kernel)."""
+    if mode == "fused" and stage != "fused_ffn":
+        return {"acc_fill": "fill_zero_f32_kernel", "acc_to_bf16": "f32_to_bf16_kernel",
+                "route": "route kernels"}[stage]
     if stage == "route":
         if cfg.P <= 256 and cfg.E <= 64:
             return "route_wave_kernel"
         return "route_small_kernel" if cfg.P <= 16384 and cfg.E <= 1024 else "route_* (4 kernels)"
     if stage == "combine":
         return "combine_kernel"
-    g1 = stage == "gemm1_swiglu"
-    if cfg.dtype == "mxfp4":
-        if cfg.P >= 128 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
-            return "big_gemm_kernel"
-        if decode_kernels_fit(cfg.T, cfg.k, cfg.E) and cfg.D % 512 == 0 and cfg.H % 512 == 0:
-            return "mx_skinny_kernel"
-        return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
-    if cfg.dtype == "mxfp8":
-        if cfg.P >= 128 * cfg.E and cfg.D % 256 == 0 and cfg.H % 256 == 0:
-            return "big_gemm_kernel"
-        if decode_kernels_fit(cfg.T, cfg.k, cfg.E) and cfg.D % 512 == 0 and cfg.H % 512 == 0:
-            return "mx_skinny_kernel"
-        return "mx_gemm1_kernel" if g1 else "mx_gemm2_kernel"
-    if decode_kernels_fit(cfg.T, cfg.k, cfg.E):
-        return "dma_split_kernel" if (cfg.D if g1 else cfg.H) % 256 == 0 else "dma_skinny_kernel"
-    if cfg.D % 256 == 0:
-        return "big_gemm_kernel"
-    return "gemm1_swiglu_kernel" if g1 else "gemm2_weight_kernel"
+    # the library reports the kernel its dispatch picks for this shape
+    import grouped_gemm_amd as g
+    name = g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, cfg.dtype, mode,
+                                 2 if stage == "gemm2_weight" else 1)
+    return name.split("<")[0] if name else "unknown"
 
 
 def measured_traffic(stage: str, symbol: str, workload: str):

@@ -71,6 +71,7 @@ def library() -> ctypes.CDLL:
             "moe_ffn_workspace_bytes": ([PP, INT], SZ),
             "moe_ffn_validate": ([PP, INT], INT),
             "moe_ffn_resolve_mode": ([PP, INT], INT),
+            "moe_ffn_gemm_kernel": ([PP, INT, INT], ctypes.c_char_p),
             "moe_ffn_forward": ([PP, VP, VP, VP, VP, VP, VP, INT, VP], INT),
             "moe_ffn_forward_events": ([PP, VP, VP, VP, VP, VP, VP, INT, VP, EV, INT], INT),
             "moe_ffn_router": ([VP, I32, I32, I32, VP, VP, VP], INT),
@@ -145,6 +146,14 @@ def moe_ffn_validate(T, D, H, E, topk, dtype="bf16", mode="auto") -> int:
 def moe_ffn_resolve_mode(T, D, H, E, topk, dtype="bf16", mode="auto") -> int:
     p = make_problem(T, D, H, E, topk, dtype)
     return int(library().moe_ffn_resolve_mode(ctypes.byref(p), _mode(mode)))
+
+
+def moe_ffn_gemm_kernel(T, D, H, E, topk, dtype="bf16", mode="auto", gemm=1):
+    """Name of the kernel family the forward pass runs for GEMM1 or GEMM2 on
+    this shape (host only), or None for an invalid problem."""
+    p = make_problem(T, D, H, E, topk, dtype)
+    name = library().moe_ffn_gemm_kernel(ctypes.byref(p), _mode(mode), int(gemm))
+    return name.decode() if name is not None else None
 
 
 def _stream(stream):

@@ -149,6 +149,38 @@ MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode) {
     return resolve(p, mode);
 }
 
+MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, int gemm) {
+    if ((gemm != 1 && gemm != 2) || check_shape(p) != MOE_FFN_OK) return nullptr;
+    const int m = resolve(p, mode);
+    if (m < 0) return nullptr;
+    if (p->T == 0) return "none";
+    const bool g1 = gemm == 1;
+    // the predicates below only test the m-tile table pointer for null; the
+    // split pipeline's workspace always holds the table
+    static int32_t table_stand_in;
+    if (p->dtype == MOE_FFN_BF16) {
+        if (m == MOE_FFN_FUSED) return "fused_bf16_kernel";
+        moe::Bf16Args a{};
+        a.T = p->T; a.D = p->D; a.H = p->H; a.E = p->E; a.k = p->topk;
+        a.P = static_cast<int64_t>(p->T) * p->topk;
+        a.mtiles = &table_stand_in;
+        if (moe::bf16_uses_decode_kernels(a))
+            return (g1 ? p->D : p->H) % 256 == 0 ? "dma_split_kernel" : "dma_skinny_kernel";
+        if (moe::big_gemm_supported(a))
+            return moe::big_gemm_tile_rows(a) == 256 ? "big_gemm_kernel<256>" : "big_gemm_kernel<128>";
+        return g1 ? "gemm1_swiglu_kernel" : "gemm2_weight_kernel";
+    }
+    if (m == MOE_FFN_FUSED) return "mx_fused_kernel";
+    moe::MxArgs a{};
+    a.T = p->T; a.D = p->D; a.H = p->H; a.E = p->E; a.k = p->topk;
+    a.P = static_cast<int64_t>(p->T) * p->topk;
+    a.w4 = p->dtype == MOE_FFN_MXFP4;
+    a.mtiles = &table_stand_in;
+    if (moe::big_mx_supported(a)) return "big_gemm_kernel<256>";
+    if (moe::skinny_mx_supported(a)) return "mx_skinny_kernel";
+    return g1 ? "mx_gemm1_kernel" : "mx_gemm2_kernel";
+}
+
 MOE_FFN_API size_t moe_ffn_workspace_bytes(const moe_ffn_problem* p, int mode) {
     if (check_shape(p) != MOE_FFN_OK) return 0;
     const int m = resolve(p, mode);

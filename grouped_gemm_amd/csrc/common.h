@@ -163,6 +163,10 @@ hipError_t launch_gemms_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_identity_route(int64_t T, int32_t* counts, int32_t* offsets, int32_t* tile_prefix,
                                  int32_t* sorted_to_pair, int32_t* pair_to_sorted, float* ones, hipStream_t s);
 // Decode-shaped GEMM1 / GEMM2 (weights streamed on the MFMA's wide side).
+// Whether the bf16 split pipeline runs the decode-shaped GEMMs (host only).
+bool bf16_uses_decode_kernels(const Bf16Args& a);
+// Token rows per tile of the bf16 prefill GEMMs (128 or 256).
+int big_gemm_tile_rows(const Bf16Args& a);
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s);
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);
 // Prefill-shaped GEMM1 / GEMM2 (256-feature tiles, 128 or 256 token rows).

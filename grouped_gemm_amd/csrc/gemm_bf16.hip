@@ -472,14 +472,17 @@ inline int mtiles_upper(int64_t P, int E, int bm) {
 
 }  // namespace
 
+// The skinny kernels stream the weights once per 32-row m-tile. A single
+// group (one expert: a shared expert, a dense FFN) with few rows would give
+// the prefill ring fewer tiles than half the CUs, so it streams too.
+bool bf16_uses_decode_kernels(const Bf16Args& a) {
+    const int64_t ring_tiles = (a.P / 128 + a.E) * (a.H / 128);
+    return decode_kernels_fit(a.T, a.k, a.E) || (a.E == 1 && ring_tiles < device_cu_count() / 2);
+}
+
 hipError_t launch_gemms_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BN1 = 128, BN2 = 128;
-    // The skinny kernels stream the weights once per 32-row m-tile. A single
-    // group (one expert: a shared expert, a dense FFN) with few rows would
-    // give the prefill ring fewer tiles than half the CUs, so it streams too.
-    const int64_t ring_tiles = (a.P / 128 + a.E) * (a.H / 128);
-    const bool skinny =
-        decode_kernels_fit(a.T, a.k, a.E) || (a.E == 1 && ring_tiles < device_cu_count() / 2);
+    const bool skinny = bf16_uses_decode_kernels(a);
     const bool big = !skinny && big_gemm_supported(a);
     if (skinny) {
         launch_skinny_gemm1(a, s);

@@ -911,6 +911,8 @@ bool big_gemm_supported(const Bf16Args& a) {
            a.P * a.H * 2 < lim && a.P * 4 < lim && int64_t(2) * a.H * a.D * 2 < lim;
 }
 
+int big_gemm_tile_rows(const Bf16Args& a) { return a.P >= kBigTile256MinRowsBf16 * a.E ? 256 : 128; }
+
 hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
     BigArgs a{b.T, b.D, b.H, b.E, b.k, b.P,
               reinterpret_cast<const uint8_t*>(b.x), nullptr,
@@ -918,7 +920,7 @@ hipError_t launch_big_gemm(const Bf16Args& b, bool gemm1, hipStream_t s) {
               reinterpret_cast<const uint8_t*>(b.w2), nullptr,
               b.wts, b.rv, reinterpret_cast<uint8_t*>(b.act), nullptr, b.ypair, sink_of(b.mtiles, b.P, b.E), b.av};
     int4* tiles = reinterpret_cast<int4*>(b.mtiles);
-    if (b.P >= kBigTile256MinRowsBf16 * b.E) return launch_big<256, false>(a, tiles, gemm1, s);
+    if (big_gemm_tile_rows(b) == 256) return launch_big<256, false>(a, tiles, gemm1, s);
     return launch_big<128, false>(a, tiles, gemm1, s);
 }
 

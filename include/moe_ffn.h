@@ -98,6 +98,20 @@ MOE_FFN_API int moe_ffn_validate(const moe_ffn_problem* p, int mode);
  * MOE_FFN_SPLIT); a negative code on invalid input. Host only. */
 MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode);
 
+/* The kernel family moe_ffn_forward runs for GEMM1 (gemm = 1, with the
+ * activation) or GEMM2 (gemm = 2, with the routing weight) on this problem in
+ * the pipeline `mode` resolves to, as a static NUL-terminated name (owned by
+ * the library, never freed): "dma_split_kernel", "dma_skinny_kernel",
+ * "big_gemm_kernel<128>", "big_gemm_kernel<256>", "gemm1_swiglu_kernel",
+ * "gemm2_weight_kernel", "mx_skinny_kernel", "mx_gemm1_kernel",
+ * "mx_gemm2_kernel", "fused_bf16_kernel", "mx_fused_kernel", or "none" for
+ * T = 0. NULL on an invalid problem, mode or gemm. Host only: it evaluates
+ * the same dispatch rules as the launch, which depend on the shapes only
+ * (the routing itself is not known before the route step). Not defined by
+ * the pages; it exists so that callers and tests can see which path a
+ * shape takes. */
+MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, int gemm);
+
 /* The forward pass.
  *   x            : bf16 [T, D], or e4m3 codes [T, D] for MXFP8 and MXFP4.
  *   w1           : bf16 [E, 2H, D] (gate rows then up rows per expert), or

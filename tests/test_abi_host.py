@@ -14,7 +14,7 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == {
-        "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_forward",
+        "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_gemm_kernel", "moe_ffn_forward",
         "moe_ffn_forward_events", "moe_ffn_router", "moe_ffn_forward_logits",
         "moe_ffn_shared_workspace_bytes", "moe_ffn_forward_shared", "moe_ffn_forward_act",
         "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_mxfp4_quantize",

@@ -103,6 +103,9 @@ def test_mx_forward_prefill_tiles(T, D, H, E, k, routing, grid_limit, monkeypatc
 def test_mx_decode_kernel(T, D, H, E, k, routing):
     """Shapes the decode-shaped MX kernel takes with e4m3 weights (fewer than 0.5
     experts expected past 32 rows, D and H multiples of 512)."""
+    import grouped_gemm_amd as g
+    for gemm in (1, 2):
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp8", "split", gemm) == "mx_skinny_kernel"
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 

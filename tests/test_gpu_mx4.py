@@ -109,6 +109,9 @@ def test_mxfp4_forward_matches_oracle(T, D, H, E, k, routing):
 def test_mxfp4_decode_kernel_matches_oracle(T, D, H, E, k, routing):
     """Shapes the decode-shaped MXFP4 kernel takes (fewer than 0.5 experts expected
     past 32 rows, D and H multiples of 512)."""
+    import grouped_gemm_amd as g
+    for gemm in (1, 2):
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp4", "split", gemm) == "mx_skinny_kernel"
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
