@@ -10,6 +10,7 @@ PyTorch fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -17,8 +18,7 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_FFN_LIB selects another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(_HERE, "libmoe_ffn.so")
+LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_ffn.h")
 
 MOE_FFN_BF16, MOE_FFN_MXFP8, MOE_FFN_MXFP4 = 0, 1, 2
@@ -87,10 +87,6 @@ def library() -> ctypes.CDLL:
             "moe_ffn_strerror": ([INT], ctypes.c_char_p),
         }
         for name, (args, res) in signatures.items():
-            # a MOE_FFN_LIB build of an older source may lack newer entry points
-            # (calling one then raises); the in-tree library must have them all
-            if os.environ.get("MOE_FFN_LIB") and not hasattr(lib, name):
-                continue
             fn = getattr(lib, name)
             fn.argtypes, fn.restype = args, res
         _lib = lib
@@ -156,16 +152,96 @@ def moe_ffn_gemm_kernel(T, D, H, E, topk, dtype="bf16", mode="auto", gemm=1):
     return name.decode() if name is not None else None
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
+@contextlib.contextmanager
+def _on(stream):
+    """Make `stream` current for the wrapper's own allocations and its int64 ->
+    int32 id conversion, after the work already queued on the caller's
+    current stream. torch's caching allocator hands a freed block out again
+    only on the stream it was allocated on, so the temporaries (workspace,
+    converted ids) cannot be reused while the pass still reads them."""
+    cur = torch.cuda.current_stream()
+    if stream is None or stream == cur:
+        yield cur
+        return
+    stream.wait_stream(cur)
+    with torch.cuda.stream(stream):
+        yield stream
+
+
+def _sp(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _check_cuda(*ts):
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous and on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must be on one device")
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+
+
+def _pass_shapes(x, w1, w2, topk_ids, topk_weights, out, x_scale=None, w1_scale=None, w2_scale=None):
+    """(T, D, H, E, k, data path) of a pass, after checking every tensor's
+    shape and dtype against them: the C ABI sees only pointers, so this is
+    where a short `out` or a narrow `topk_weights` is caught."""
+    if x.dim() != 2 or w1.dim() != 3 or w2.dim() != 3 or topk_ids.dim() != 2:
+        raise ValueError("x must be [T, D], w1 [E, 2H, D(/2)], w2 [E, D, H(/2)], topk_ids [T, k]")
+    T, D = x.shape
+    E, H2 = w1.shape[0], w1.shape[1]
+    H = H2 // 2
+    k = topk_ids.shape[1]
+    path = _data_path(x, w1)
+    if topk_ids.shape[0] != T or topk_ids.dtype not in (torch.int32, torch.int64):
+        raise ValueError("topk_ids must be int32 (or int64) [T, k]")
+    _expect(topk_weights, (T, k), torch.float32, "topk_weights")
+    if out is not None:
+        _expect(out, (T, D), torch.bfloat16, "out")
+    if H2 % 2:
+        raise ValueError("w1 must hold 2H rows per expert")
+    if path == "bf16":
+        _expect(x, (T, D), torch.bfloat16, "x")
+        _expect(w1, (E, H2, D), torch.bfloat16, "w1")
+        _expect(w2, (E, D, H), torch.bfloat16, "w2")
+        if any(t is not None for t in (x_scale, w1_scale, w2_scale)):
+            raise ValueError("the bf16 path takes no scales")
+    else:
+        wk = 2 if path == "mxfp4" else 1
+        if D % 32 or H % 32:
+            raise ValueError("MX paths need D and H multiples of 32")
+        _expect(w1, (E, H2, D // wk), torch.uint8, "w1")
+        _expect(w2, (E, D, H // wk), torch.uint8, "w2")
+        _expect(x_scale, (T, D // 32), torch.uint8, "x_scale")
+        _expect(w1_scale, (E, H2, D // 32), torch.uint8, "w1_scale")
+        _expect(w2_scale, (E, D, H // 32), torch.uint8, "w2_scale")
+    return T, D, H, E, k, path
+
+
+def _ids32(topk_ids):
+    return topk_ids if topk_ids.dtype == torch.int32 else topk_ids.to(torch.int32)
+
+
+def _workspace(lib, p, m, dev, what, nbytes=None):
+    if nbytes is None:
+        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), m)
+    if nbytes == 0:
+        raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m) or MOE_FFN_EINVAL_SHAPE, what)
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def _events(events):
+    return (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
 
 
 def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_scale=None,
@@ -178,37 +254,30 @@ def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_
     MXFP4 path: as MXFP8, with w1 [E, 2H, D/2] and w2 [E, D, H/2] packed e2m1
     codes (moe_ffn_mxfp4_quantize); x stays e4m3.
     topk_ids int32 [T, k] (int64 is converted), topk_weights fp32 [T, k].
+    stream: the torch stream to run on (default: the current one); the
+    wrapper's temporaries are allocated on it.
     events: optional 5 hipEvent_t handles (ints) recorded at the stage
     boundaries (moe_ffn_forward_events).
     """
-    if topk_ids.dtype != torch.int32:
-        topk_ids = topk_ids.to(torch.int32)
-    T, D = x.shape
-    E, H2, _ = w1.shape
-    k = topk_ids.shape[1]
-    if out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
-    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
-    p = make_problem(T, D, H2 // 2, E, k, _data_path(x, w1), x_scale, w1_scale, w2_scale)
+    T, D, H, E, k, path = _pass_shapes(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale, workspace)
     lib = library()
     m = _mode(mode)
-    if workspace is None:
-        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), m)
-        if nbytes == 0:
-            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m), "moe_ffn_forward")
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel()
-    if events is None:
-        rc = lib.moe_ffn_forward(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
-                                 topk_ids.data_ptr(), topk_weights.data_ptr(), out.data_ptr(), m,
-                                 _stream(stream))
-    else:
-        ev = (ctypes.c_void_p * 5)(*events)
-        rc = lib.moe_ffn_forward_events(ctypes.byref(p), x.data_ptr(), w1.data_ptr(),
-                                        w2.data_ptr(), topk_ids.data_ptr(),
-                                        topk_weights.data_ptr(), out.data_ptr(), m,
-                                        _stream(stream), ev, 5)
+    with _on(stream) as s:
+        topk_ids = _ids32(topk_ids)
+        if out is None:
+            out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        p = make_problem(T, D, H, E, k, path, x_scale, w1_scale, w2_scale)
+        if workspace is None:
+            workspace = _workspace(lib, p, m, x.device, "moe_ffn_forward")
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+        args = (ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(), topk_ids.data_ptr(),
+                topk_weights.data_ptr(), out.data_ptr(), m, _sp(s))
+        if events is None:
+            rc = lib.moe_ffn_forward(*args)
+        else:
+            rc = lib.moe_ffn_forward_events(*args, *_events(events))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward")
     return out
@@ -217,13 +286,14 @@ def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_
 def moe_ffn_router(logits, k, stream=None):
     """(topk_ids int32 [T, k], topk_weights fp32 [T, k]) from fp32 logits [T, E] on the GPU:
     softmax, the k most probable experts (ties to the lower id), renormalized."""
-    if logits.dtype != torch.float32:
-        raise ValueError("logits must be float32")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be float32 [T, E]")
     _check_cuda(logits)
     T, E = logits.shape
-    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-    wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
-    rc = library().moe_ffn_router(logits.data_ptr(), T, E, k, ids.data_ptr(), wts.data_ptr(), _stream(stream))
+    with _on(stream) as s:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+        rc = library().moe_ffn_router(logits.data_ptr(), T, E, k, ids.data_ptr(), wts.data_ptr(), _sp(s))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_router")
     return ids, wts
@@ -238,31 +308,34 @@ def moe_ffn_forward_logits(x, w1, w2, logits, k, out=None, mode="auto", x_scale=
     if logits.dtype != torch.float32:
         raise ValueError("logits must be float32")
     T, D = x.shape
-    E, H2, _ = w1.shape
-    if logits.shape != (T, E):
+    E = w1.shape[0]
+    if tuple(logits.shape) != (T, E):
         raise ValueError("logits must be [T, E]")
     dev = x.device
-    if out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    if topk_ids is None:
-        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    if topk_weights is None:
-        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
-    _check_cuda(x, w1, w2, logits, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
-    p = make_problem(T, D, H2 // 2, E, k, _data_path(x, w1), x_scale, w1_scale, w2_scale)
-    lib = library()
-    m = _mode(mode)
-    if workspace is None:
-        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), m)
-        if nbytes == 0:
-            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m), "moe_ffn_forward_logits")
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel()
-    ev, n = (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
-    rc = lib.moe_ffn_forward_logits(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
-                                    logits.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(),
-                                    out.data_ptr(), m, _stream(stream), ev, n)
+    with _on(stream) as s:
+        if topk_ids is None:
+            topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        if topk_weights is None:
+            topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+        if topk_ids.dtype != torch.int32:
+            raise ValueError("topk_ids (an output here) must be int32")
+        _T, _D, H, _E, _k, path = _pass_shapes(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale,
+                                               w2_scale)
+        if _k != k:
+            raise ValueError("topk_ids must be [T, k]")
+        _check_cuda(x, w1, w2, logits, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale, workspace)
+        if out is None:
+            out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        p = make_problem(T, D, H, E, k, path, x_scale, w1_scale, w2_scale)
+        lib = library()
+        m = _mode(mode)
+        if workspace is None:
+            workspace = _workspace(lib, p, m, dev, "moe_ffn_forward_logits")
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.moe_ffn_forward_logits(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                        logits.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(),
+                                        out.data_ptr(), m, _sp(s), *_events(events))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward_logits")
     return out, topk_ids, topk_weights
@@ -272,32 +345,28 @@ def moe_ffn_forward_shared(x, w1, w2, topk_ids, topk_weights, shared_w1, shared_
                            workspace=None, stream=None, events=None):
     """out [T, D] bf16 = the routed pass plus one shared expert on every token
     (shared_w1 [2Hs, D], shared_w2 [D, Hs] bf16), added with weight 1."""
-    if topk_ids.dtype != torch.int32:
-        topk_ids = topk_ids.to(torch.int32)
-    T, D = x.shape
-    E, H2, _ = w1.shape
-    k = topk_ids.shape[1]
+    T, D, H, E, k, path = _pass_shapes(x, w1, w2, topk_ids, topk_weights, out)
+    if path != "bf16":
+        raise MoeFfnError(MOE_FFN_EUNSUPPORTED, "moe_ffn_forward_shared")
     Hs = shared_w1.shape[0] // 2
-    if tuple(shared_w1.shape) != (2 * Hs, D) or tuple(shared_w2.shape) != (D, Hs):
-        raise ValueError("shared_w1 must be [2Hs, D] and shared_w2 [D, Hs]")
-    if out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
-    _check_cuda(x, w1, w2, topk_ids, topk_weights, shared_w1, shared_w2, out)
-    p = make_problem(T, D, H2 // 2, E, k, "bf16")
+    _expect(shared_w1, (2 * Hs, D), torch.bfloat16, "shared_w1")
+    _expect(shared_w2, (D, Hs), torch.bfloat16, "shared_w2")
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, shared_w1, shared_w2, out, workspace)
     lib = library()
     m = _mode(mode)
-    if workspace is None:
-        nbytes = lib.moe_ffn_shared_workspace_bytes(ctypes.byref(p), Hs, m)
-        if nbytes == 0:
-            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m) or MOE_FFN_EINVAL_SHAPE,
-                              "moe_ffn_forward_shared")
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel()
-    ev, n = (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
-    rc = lib.moe_ffn_forward_shared(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
-                                    topk_ids.data_ptr(), topk_weights.data_ptr(), shared_w1.data_ptr(),
-                                    shared_w2.data_ptr(), Hs, out.data_ptr(), m, _stream(stream), ev, n)
+    with _on(stream) as s:
+        topk_ids = _ids32(topk_ids)
+        if out is None:
+            out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        p = make_problem(T, D, H, E, k, "bf16")
+        if workspace is None:
+            workspace = _workspace(lib, p, m, x.device, "moe_ffn_forward_shared",
+                                   lib.moe_ffn_shared_workspace_bytes(ctypes.byref(p), Hs, m))
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.moe_ffn_forward_shared(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                        topk_ids.data_ptr(), topk_weights.data_ptr(), shared_w1.data_ptr(),
+                                        shared_w2.data_ptr(), Hs, out.data_ptr(), m, _sp(s), *_events(events))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward_shared")
     return out
@@ -309,31 +378,29 @@ def moe_ffn_forward_act(x, w1, w2, topk_ids, topk_weights, kind="clamped_swiglu"
     gate/up scaled by alpha [E] fp32 (or 1) and, with weight_before_act, by the
     routing weight; kind "clamped_swiglu" clamps gate from above and up on both
     sides at `limit`."""
-    if topk_ids.dtype != torch.int32:
-        topk_ids = topk_ids.to(torch.int32)
-    T, D = x.shape
-    E, H2, _ = w1.shape
-    k = topk_ids.shape[1]
-    if out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
-    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, alpha)
+    T, D, H, E, k, path = _pass_shapes(x, w1, w2, topk_ids, topk_weights, out)
+    if path != "bf16":
+        raise MoeFfnError(MOE_FFN_EUNSUPPORTED, "moe_ffn_forward_act")
+    if alpha is not None:
+        _expect(alpha, (E,), torch.float32, "alpha")
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, alpha, workspace)
     kinds = {"swiglu": MOE_FFN_ACT_SWIGLU, "clamped_swiglu": MOE_FFN_ACT_CLAMPED_SWIGLU}
     act = moe_ffn_activation(kinds.get(kind, kind) if isinstance(kind, str) else kind, float(limit),
                              alpha.data_ptr() if alpha is not None else None, 1 if weight_before_act else 0)
-    p = make_problem(T, D, H2 // 2, E, k, "bf16")
     lib = library()
     m = _mode(mode)
-    if workspace is None:
-        nbytes = lib.moe_ffn_workspace_bytes(ctypes.byref(p), MOE_FFN_SPLIT)
-        if nbytes == 0:
-            raise MoeFfnError(lib.moe_ffn_validate(ctypes.byref(p), m), "moe_ffn_forward_act")
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel()
-    ev, n = (None, 0) if events is None else ((ctypes.c_void_p * 5)(*events), 5)
-    rc = lib.moe_ffn_forward_act(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(), topk_ids.data_ptr(),
-                                 topk_weights.data_ptr(), ctypes.byref(act), out.data_ptr(), m, _stream(stream), ev,
-                                 n)
+    with _on(stream) as s:
+        topk_ids = _ids32(topk_ids)
+        if out is None:
+            out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        p = make_problem(T, D, H, E, k, "bf16")
+        if workspace is None:
+            workspace = _workspace(lib, p, MOE_FFN_SPLIT, x.device, "moe_ffn_forward_act")
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.moe_ffn_forward_act(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                     topk_ids.data_ptr(), topk_weights.data_ptr(), ctypes.byref(act),
+                                     out.data_ptr(), m, _sp(s), *_events(events))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward_act")
     return out
@@ -341,56 +408,51 @@ def moe_ffn_forward_act(x, w1, w2, topk_ids, topk_weights, kind="clamped_swiglu"
 
 def moe_ffn_route(topk_ids, E, stream=None):
     """(counts [E], offsets [E+1], sorted_to_pair [P], pair_to_sorted [P]) int32 on the GPU."""
-    if topk_ids.dtype != torch.int32:
-        topk_ids = topk_ids.to(torch.int32)
+    if topk_ids.dim() != 2 or topk_ids.dtype not in (torch.int32, torch.int64):
+        raise ValueError("topk_ids must be int32 (or int64) [T, k]")
     _check_cuda(topk_ids)
     T, k = topk_ids.shape
     P = T * k
     dev = topk_ids.device
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    s2p = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
-    p2s = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
     lib = library()
     nbytes = lib.moe_ffn_route_workspace_bytes(T, k, E)
     if nbytes == 0:
         raise MoeFfnError(MOE_FFN_EINVAL_SHAPE, "moe_ffn_route")
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    rc = lib.moe_ffn_route(topk_ids.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
-                           s2p.data_ptr(), p2s.data_ptr(), ws.data_ptr(), nbytes, _stream(stream))
+    with _on(stream) as s:
+        topk_ids = _ids32(topk_ids)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        s2p = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+        p2s = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        rc = lib.moe_ffn_route(topk_ids.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
+                               s2p.data_ptr(), p2s.data_ptr(), ws.data_ptr(), nbytes, _sp(s))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_route")
     return counts, offsets, s2p[:P], p2s[:P]
 
 
-def moe_ffn_mx_quantize(src, stream=None):
-    """MX-fp8 quantization along the last dim: (codes uint8, scales uint8 [..., K/32])."""
-    if src.dtype != torch.float32:
+def _quantize(fn, src, code_cols, what, stream):
+    if src.dtype != torch.float32 or src.dim() < 1:
         raise ValueError("src must be float32")
     _check_cuda(src)
     K = src.shape[-1]
     rows = src.numel() // K if K else 0
-    codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
-    scales = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
-    rc = library().moe_ffn_mx_quantize(src.data_ptr(), rows, K, codes.data_ptr(),
-                                       scales.data_ptr(), _stream(stream))
+    with _on(stream) as s:
+        codes = torch.empty(src.shape[:-1] + (code_cols(K),), dtype=torch.uint8, device=src.device)
+        scales = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
+        rc = fn(src.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(), _sp(s))
     if rc != MOE_FFN_OK:
-        raise MoeFfnError(rc, "moe_ffn_mx_quantize")
+        raise MoeFfnError(rc, what)
     return codes, scales
+
+
+def moe_ffn_mx_quantize(src, stream=None):
+    """MX-fp8 quantization along the last dim: (codes uint8, scales uint8 [..., K/32])."""
+    return _quantize(library().moe_ffn_mx_quantize, src, lambda K: K, "moe_ffn_mx_quantize", stream)
 
 
 def moe_ffn_mxfp4_quantize(src, stream=None):
     """MXFP4 quantization along the last dim (expert weights): (packed e2m1 codes uint8 [..., K/2],
     even index in the low nibble; scales uint8 [..., K/32])."""
-    if src.dtype != torch.float32:
-        raise ValueError("src must be float32")
-    _check_cuda(src)
-    K = src.shape[-1]
-    rows = src.numel() // K if K else 0
-    codes = torch.empty(src.shape[:-1] + (K // 2,), dtype=torch.uint8, device=src.device)
-    scales = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
-    rc = library().moe_ffn_mxfp4_quantize(src.data_ptr(), rows, K, codes.data_ptr(),
-                                          scales.data_ptr(), _stream(stream))
-    if rc != MOE_FFN_OK:
-        raise MoeFfnError(rc, "moe_ffn_mxfp4_quantize")
-    return codes, scales
+    return _quantize(library().moe_ffn_mxfp4_quantize, src, lambda K: K // 2, "moe_ffn_mxfp4_quantize", stream)

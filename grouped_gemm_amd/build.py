@@ -30,21 +30,22 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
-    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD, defines=()) -> str:
-    """Compile every csrc/*.hip and link `out`; `defines` are extra -D macros."""
-    os.makedirs(build_dir, exist_ok=True)
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip and link libmoe_ffn.so."""
+    os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+        objs = list(ex.map(_compile, srcs))
+    out = LIB
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -88,9 +88,9 @@ __device__ __forceinline__ void lds_barrier() {
 // 16*NT token rows x RB bytes; the four waves split the stage's k-steps and
 // the partial sums meet in LDS at the end. Ring of S stages, one barrier per
 // stage, each wave waits only for its own DMAs of the stage it consumes.
-#ifndef MOE_DMA_AUX
-#define MOE_DMA_AUX 2   // cache policy bits of the weight DMA: 2 = nontemporal (streamed once)
-#endif
+// Cache policy bits of the weight DMA: 2 = nontemporal (each weight byte is
+// streamed once).
+constexpr int kWeightDmaAux = 2;
 
 template <int NT, int KC, int S>
 struct DmaTile {
@@ -121,7 +121,7 @@ __device__ __forceinline__ void dma_issue(uint8_t* ring, int it, int grp, int ki
 #pragma unroll
     for (int j = 0; j < T::W_INS; ++j)
         __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * T::W_INS + j) * 1024), 16, 0,
-                                         MOE_DMA_AUX);
+                                         kWeightDmaAux);
 #pragma unroll
     for (int j = 0; j < T::T_INS; ++j)
         __builtin_amdgcn_global_load_lds(tsrc[j] + kb, (lds_ptr_t)(slot + T::W_BYTES + (wave * T::T_INS + j) * 1024),
@@ -372,7 +372,7 @@ __device__ __forceinline__ void split_issue_w(uint8_t* lds, int it, int KIT, int
 #pragma unroll
     for (int j = 0; j < W_INS; ++j)
         __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
-                                         MOE_DMA_AUX);
+                                         kWeightDmaAux);
 }
 template <int KC>
 __device__ __forceinline__ void split_issue_t(uint8_t* tring, int it, int KIT, int mw, const char* const* src) {
@@ -607,7 +607,7 @@ __device__ __forceinline__ void mx4_dma_issue(uint8_t* ring, int it, int grp, in
 #pragma unroll
     for (int j = 0; j < C::WINS; ++j)
         __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * C::WINS + j) * 1024), 16, 0,
-                                         MOE_DMA_AUX);
+                                         kWeightDmaAux);
 #pragma unroll
     for (int j = 0; j < C::TINS; ++j)
         __builtin_amdgcn_global_load_lds(tsrc[j] + tb, (lds_ptr_t)(slot + C::WB + (wave * C::TINS + j) * 1024), 16, 0,

@@ -48,8 +48,8 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v, float sign_src) {
     return sign | code;
 }
 
-// MXFP4 weights ("GC-MoE on SM120", scale formats: a 4-bit E2M1 code with a
-// shared UE8M0 exponent per 32 contiguous elements). e2m1: 1 sign bit, 2
+// MXFP4 weights ("GC-MoE on SM120", scale formats: 4-bit E2M1 codes in
+// blocks of 32 along K, one UE8M0 power-of-two scale per block). e2m1: 1 sign bit, 2
 // exponent bits (bias 1), 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3,
 // 4, 6. Scale rule MXQ4, the MX-fp8 rule with 6 in place of 448: s = the
 // smallest integer with amax <= 6 * 2^s, clamped to [-127, 127]; codes

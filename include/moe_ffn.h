@@ -2,9 +2,9 @@
  * moe_ffn.h -- C ABI of the MI355X (gfx950) routed MoE SwiGLU FFN forward pass.
  *
  * The operation ("Prime Flash MoE - Faster MoE Kernels optimized for
- * Blackwell", section 1 "The computation"): a router has already chosen
- * each token's top-k experts and normalized routing weights. For every
- * routed (token t, expert e) pair,
+ * Blackwell", section 1 "The computation"): the pass is handed each
+ * token's k experts and their normalized weights by an upstream router.
+ * For every routed (token t, expert e) pair,
  *     gate|up = W1[e] x_t         (W1 [E, 2H, D], output-major, gate rows
  *                                  [0, H) then up rows [H, 2H))
  *     act     = silu(gate) * up   (silu(z) = z / (1 + exp(-z)))
@@ -39,10 +39,10 @@ extern "C" {
 
 #define MOE_FFN_API __attribute__((visibility("default")))
 
-/* Data paths (Prime Flash MoE: "two data paths, one for bf16 and one for
- * MXFP8", introduction). MOE_FFN_MXFP4 is the MXFP4-weight path of
- * "GC-MoE on SM120" (scale formats): expert weights as 4-bit E2M1 codes
- * with a shared UE8M0 exponent per 32 contiguous elements along K, two
+/* Data paths (Prime Flash MoE, introduction: a bf16 path and an MXFP8 path
+ * of the same structure). MOE_FFN_MXFP4 is the MXFP4-weight path of
+ * "GC-MoE on SM120" (scale formats): expert weights as 4-bit E2M1 codes in
+ * blocks of 32 along K, each block with one UE8M0 power-of-two scale, two
  * codes per byte with the even K index in the low nibble; x and the
  * activation stay MX-fp8 (e4m3 codes, e8m0 scales) as in MOE_FFN_MXFP8.
  * SPLIT (and AUTO) only. */
@@ -107,9 +107,12 @@ MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode);
  * "mx_gemm2_kernel", "fused_bf16_kernel", "mx_fused_kernel", or "none" for
  * T = 0. NULL on an invalid problem, mode or gemm. Host only: it evaluates
  * the same dispatch rules as the launch, which depend on the shapes only
- * (the routing itself is not known before the route step). Not defined by
- * the pages; it exists so that callers and tests can see which path a
- * shape takes. */
+ * (the routing itself is not known before the route step), except for
+ * E == 1: a single group of few rows streams its weights through the decode
+ * kernels while the prefill kernels would get fewer tiles than half the
+ * current device's compute units (256 on MI355X; 256 is also assumed when
+ * no device is visible). Not defined by the pages; it exists so that
+ * callers and tests can see which path a shape takes. */
 MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, int gemm);
 
 /* The forward pass.

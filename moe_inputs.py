@@ -4,9 +4,9 @@ This module is shared by the CPU oracle's tests and by the GPU path's tests
 and benchmark. It holds no arithmetic of the pass itself (no GEMM, no
 SwiGLU, no combine, no quantization): it draws random tensors, rounds
 them to bf16 storage, and draws the router's choices that the pass takes as
-given inputs ("a router has already selected the top-k experts for each
-token, together with normalized routing weights" -- Prime Flash MoE,
-section 1 "The computation").
+given inputs (Prime Flash MoE, section 1 "The computation": the pass
+starts from each token's k chosen experts and their normalized weights,
+which a router upstream produced).
 
 Each tensor role (routing, x, W1, W2) has its own numpy PCG64 stream keyed
 by (config id, role, seed), so a change of shape in one tensor does not

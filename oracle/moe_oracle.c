@@ -32,9 +32,9 @@
  *   code_i         =  e4m3fn(v_i * 2^-s), round to nearest even, values
  *                     beyond 448 in magnitude saturate to +-448.
  *
- * MXFP4 weights ("GC-MoE on SM120", section on scale formats: a 4-bit E2M1
- * code with a shared UE8M0 exponent per 32 contiguous elements; activations
- * stay MX-fp8): e2m1 has 1 sign bit, 2 exponent bits (bias 1) and 1
+ * MXFP4 weights ("GC-MoE on SM120", section on scale formats: 4-bit E2M1
+ * codes in blocks of 32 along K, each block with one UE8M0 power-of-two
+ * scale; activations stay MX-fp8): e2m1 has 1 sign bit, 2 exponent bits (bias 1) and 1
  * mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, no infinities or
  * NaN. Two codes share a byte, the even K index in the low nibble. The
  * pages give no scale rule for fp4; MXQ4 reads MXQ with 6 in place of 448:

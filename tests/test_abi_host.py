@@ -186,3 +186,57 @@ def test_activation_variant_host_checks(kind, limit, mode, dtype, expect):
                                    g._mode(mode), None, None, 0) == expect
     assert lib.moe_ffn_forward_act(ctypes.byref(p), None, None, None, None, None, None, None, 0, None, None,
                                    0) == g.MOE_FFN_EINVAL_PTR
+
+
+# ---- the binding's own shape and dtype checks (CPU tensors: nothing is launched) ----
+
+def _cpu_pass(T=8, D=128, H=128, E=4, k=2):
+    import torch
+    return dict(x=torch.zeros((T, D), dtype=torch.bfloat16), w1=torch.zeros((E, 2 * H, D), dtype=torch.bfloat16),
+                w2=torch.zeros((E, D, H), dtype=torch.bfloat16), topk_ids=torch.zeros((T, k), dtype=torch.int32),
+                topk_weights=torch.zeros((T, k), dtype=torch.float32))
+
+
+@pytest.mark.parametrize("name,shape,dtype", [
+    ("out", (7, 128), "bfloat16"),             # one row short
+    ("out", (8, 128), "float32"),
+    ("topk_weights", (8, 1), "float32"),       # narrower than topk_ids
+    ("topk_weights", (8, 2), "float64"),
+    ("w2", (4, 128, 64), "bfloat16"),          # H of w1 is 128
+    ("w1", (4, 256, 64), "bfloat16"),          # D of x is 128
+    ("x", (8, 128), "float16"),
+])
+def test_binding_rejects_mismatched_tensors(name, shape, dtype):
+    import torch
+    import grouped_gemm_amd as g
+    t = _cpu_pass()
+    bad = torch.zeros(shape, dtype=getattr(torch, dtype))
+    kw = {} if name == "out" else {}
+    if name == "out":
+        kw["out"] = bad
+    else:
+        t[name] = bad
+    with pytest.raises(ValueError, match=name if name != "x" else "x|w1"):
+        g.moe_ffn_forward(t["x"], t["w1"], t["w2"], t["topk_ids"], t["topk_weights"], **kw)
+
+
+def test_binding_rejects_mx_scale_shapes():
+    import torch
+    import grouped_gemm_amd as g
+    T, D, H, E, k = 8, 128, 128, 4, 2
+    u8 = torch.uint8
+    x, w1, w2 = torch.zeros((T, D), dtype=u8), torch.zeros((E, 2 * H, D), dtype=u8), torch.zeros((E, D, H), dtype=u8)
+    ids, w = torch.zeros((T, k), dtype=torch.int32), torch.zeros((T, k))
+    good = dict(x_scale=torch.zeros((T, D // 32), dtype=u8), w1_scale=torch.zeros((E, 2 * H, D // 32), dtype=u8),
+                w2_scale=torch.zeros((E, D, H // 32), dtype=u8))
+    for name in good:
+        kw = dict(good)
+        kw[name] = torch.zeros((1, 1), dtype=u8)
+        with pytest.raises(ValueError, match=name):
+            g.moe_ffn_forward(x, w1, w2, ids, w, **kw)
+        kw[name] = None
+        with pytest.raises(ValueError, match=name):
+            g.moe_ffn_forward(x, w1, w2, ids, w, **kw)
+    # matching shapes reach the device check (CPU tensors), not a launch
+    with pytest.raises(ValueError, match="GPU"):
+        g.moe_ffn_forward(x, w1, w2, ids, w, **good)

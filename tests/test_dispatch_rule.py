@@ -41,6 +41,12 @@ def test_workload_paths():
     assert _kernel(64, 4096, 1536, 64, 6, dtype="mxfp8") == "mx_skinny_kernel"
     assert _kernel(64, 6144, 2048, 32, 8, dtype="mxfp4", gemm=2) == "mx_skinny_kernel"
     assert _kernel(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == "mx_fused_kernel"
+    # E = 1 (one group of every token): the decode kernels while the prefill
+    # ring would get fewer tiles than half of the 256 compute units
+    assert _kernel(260, 256, 128, 1, 1) == "dma_split_kernel"              # 3 ring tiles
+    assert _kernel(260, 256, 128, 1, 1, gemm=2) == "dma_skinny_kernel"     # K = H = 128
+    assert _kernel(2048, 256, 512, 1, 1) == "dma_split_kernel"             # (16 + 1) x 4 = 68 ring tiles
+    assert _kernel(4096, 256, 1024, 1, 1) == "big_gemm_kernel<256>"        # (32 + 1) x 8 = 264 ring tiles
     assert _kernel(0, 256, 512, 8, 2) == "none"
     assert _kernel(64, 256, 512, 8, 2, gemm=3) is None
     assert _kernel(64, 250, 512, 8, 2) is None                              # invalid shape

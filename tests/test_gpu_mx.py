@@ -10,7 +10,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from tests.parity import MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, sample_tokens, to_gpu
+from tests.parity import MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, cover_sample, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -129,13 +129,13 @@ def test_mx_prefill_descriptor_reload(monkeypatch):
     monkeypatch.setenv("MOE_FFN_GRID_LIMIT", "8")
     cfg = mi.custom(16384, 256, 4096, 2, 1, "uniform", dtype="mxfp8")
     ids, _ = mi.routing(cfg)
-    _case(cfg, tokens=sample_tokens(cfg, ids, 32))
+    _case(cfg, tokens=cover_sample(cfg, ids, "split", extra=16))
 
 
 def test_mx_config_sampled():
     cfg = mi.CONFIGS[5]
     ids, _ = mi.routing(cfg)
-    _case(cfg, tokens=sample_tokens(cfg, ids, 24))
+    _case(cfg, tokens=cover_sample(cfg, ids, "split", extra=16))
 
 
 @pytest.mark.parametrize("T,D,H,E,k,routing", [
@@ -154,4 +154,23 @@ def test_mx_forward_fused(T, D, H, E, k, routing):
 def test_mx_fused_config_sampled():
     cfg = mi.CONFIGS[5]
     ids, _ = mi.routing(cfg)
-    _case(cfg, tokens=sample_tokens(cfg, ids, 24), mode="fused")
+    _case(cfg, tokens=cover_sample(cfg, ids, "fused", extra=16), mode="fused")
+
+
+@pytest.mark.parametrize("mode", ["split", "fused"])
+@pytest.mark.parametrize("T,D,H,E,k,kernel", [
+    (32, 512, 512, 8, 3, "mx_skinny_kernel"),       # decode kernel
+    (2100, 256, 512, 3, 2, "big_gemm_kernel<256>"), # prefill ring
+    (300, 384, 640, 16, 4, "mx_gemm1_kernel"),      # generic kernels
+])
+def test_mx_duplicate_expert_ids(mode, T, D, H, E, k, kernel):
+    """The same expert in several slots of one token counts once per slot."""
+    import grouped_gemm_amd as g
+    cfg = mi.custom(T, D, H, E, k, "zipf", dtype="mxfp8")
+    assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp8", "split", 1) == kernel
+    ids, _ = mi.routing(cfg, 0)
+    ids = ids.copy()
+    ids[::2, 1] = ids[::2, 0]
+    ids[::3, k - 1] = ids[::3, 0]
+    ids[5, :] = ids[5, 0]
+    _case(cfg, ids=ids, mode=mode)

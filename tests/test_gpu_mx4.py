@@ -12,7 +12,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from tests.parity import MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, sample_tokens, to_gpu
+from tests.parity import MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, cover_sample, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -142,7 +142,7 @@ def test_mxfp4_forward_mx_workload_sampled():
     """The MX workload's dims (T=16384, D=4096, H=1536, E=64, top-6) with fp4 weights; sampled tokens."""
     cfg = mi.CONFIGS[5]
     ids, _ = mi.routing(cfg, 0)
-    _case(cfg, tokens=sample_tokens(cfg, ids, 12))
+    _case(cfg, tokens=cover_sample(cfg, ids, "split", dtype="mxfp4", extra=8))
 
 
 def test_mxfp4_fused_mode_is_unsupported():

@@ -15,7 +15,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from tests.parity import (MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, sample_tokens, to_gpu,
+from tests.parity import (MX_COS, MX_TOL, assert_close, gpu_bf16_to_f64, cover_sample, to_gpu,
                           upload_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -119,7 +119,7 @@ def test_forward_logits_large_prefill_sampled():
     rid, rw = oracle.router(logits, cfg.k)
     np.testing.assert_array_equal(ids, rid)
     assert np.abs(wts.astype(np.float64) - rw).max() <= W_TOL
-    tokens = sample_tokens(cfg, rid, 24)
+    tokens = cover_sample(cfg, rid, "split", extra=16)
     ref = mi.bf16_bits_to_f32(oracle.forward_bf16(d["x"], d["w1"], d["w2"], rid, rw, tokens=tokens))
     rel, cos = assert_close(out[tokens], ref[tokens].astype(np.float64), what="large_prefill/logits")
     print(f"  max err / max|ref| = {rel:.3e}, cosine = {cos:.7f}", flush=True)

@@ -11,7 +11,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from tests.parity import assert_close, bf16_to_gpu, gpu_bf16_to_f64, sample_tokens, upload_bf16
+from tests.parity import assert_close, bf16_to_gpu, gpu_bf16_to_f64, cover_sample, upload_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def _case(cfg, Hs, mode, tokens=None):
     (64, 256, 512, 8, 2, 256),      # the tiny workload's shape
     (20, 256, 256, 4, 2, 384),      # shared pass on the skinny kernel (T <= 32)
     (300, 384, 256, 6, 3, 256),     # D not a multiple of 256: the generic GEMM kernels
-    (700, 512, 384, 4, 2, 128),     # prefill ring, 128-row tiles
+    (500, 512, 384, 8, 2, 128),     # prefill ring, 128-row tiles
     (2100, 256, 256, 3, 2, 640),    # prefill ring, 256-row tiles; Hs > H
 ])
 def test_shared_expert_matches_oracle(mode, T, D, H, E, k, Hs):
@@ -53,7 +53,7 @@ def test_shared_expert_decode():
 def test_shared_expert_large_prefill_sampled():
     cfg = mi.CONFIGS[4]
     ids, _ = mi.routing(cfg, 0)
-    _case(cfg, 768, "split", tokens=sample_tokens(cfg, ids, 16))
+    _case(cfg, 768, "split", tokens=cover_sample(cfg, ids, "split", extra=8, dense_bm=256))
 
 
 def test_shared_expert_rejects_mx_and_bad_sizes():

@@ -4,8 +4,9 @@ over the 8 magnitudes, the MXQ4 scale rule, the nibble packing, and the
 fp4-weight forward against the already pinned MX-fp8 forward on weights
 that both formats hold exactly.
 
-MXFP4 ("GC-MoE on SM120", scale formats): a 4-bit E2M1 code with a shared
-UE8M0 exponent per 32 contiguous elements; activations stay MX-fp8. The
+MXFP4 ("GC-MoE on SM120", scale formats): weights as E2M1 codes (4 bits
+each) in blocks of 32 along K, each block carrying one UE8M0 power-of-two
+scale; activations stay MX-fp8. The
 pages give no fp4 scale rule; MXQ4 reads the MX-fp8 rule with E2M1's
 largest magnitude 6 in place of 448: s = the smallest integer with
 amax <= 6 * 2^s, codes e2m1(v * 2^-s), nearest with ties to the even code.

@@ -180,6 +180,28 @@ def test_out_of_range_ids_are_dropped(oracle_lib):
     _check_close_to_fp64(out, ref)
 
 
+def test_duplicate_ids_count_once_per_slot(oracle_lib):
+    """The same expert in several slots of one token: the pass sums over the
+    token's slots, so expert e's output enters once per slot with that slot's
+    weight (the dense reference's M[t, e] adds the weights of every slot on e)."""
+    cfg = mi.custom(24, 64, 96, 5, 4, "uniform")
+    d = mi.make_bf16(cfg, seed=13)
+    ids = d["topk_ids"].copy()
+    ids[::2, 1] = ids[::2, 0]
+    ids[::3, 3] = ids[::3, 0]
+    ids[5, :] = 2
+    out = oracle_lib.forward_bf16(d["x"], d["w1"], d["w2"], ids, d["topk_weights"])
+    _check_close_to_fp64(out, dense_reference_fp64(d["x"], d["w1"], d["w2"], ids, d["topk_weights"]))
+    # one expert in every slot with weights summing to 1 is that expert's
+    # output alone (up to fp32 rounding of the four products' sum)
+    one = np.zeros((24, 1), np.int32) + 2
+    single = oracle_lib.forward_bf16(d["x"], d["w1"], d["w2"], one, np.ones((24, 1), np.float32))
+    w5 = d["topk_weights"][5].astype(np.float64)
+    assert abs(w5.sum() - 1.0) < 1e-6
+    a, b = _f32(out[5]), _f32(single[5])
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-6 * np.abs(b).max())
+
+
 def test_sampled_tokens_match_full_run(oracle_lib):
     cfg = mi.custom(40, 64, 64, 5, 2)
     d = mi.make_bf16(cfg, seed=12)
