@@ -25,7 +25,8 @@ MOE_FFN_BF16, MOE_FFN_MXFP8, MOE_FFN_MXFP4 = 0, 1, 2
 MOE_FFN_AUTO, MOE_FFN_FUSED, MOE_FFN_SPLIT = 0, 1, 2
 MOE_FFN_OK = 0
 MOE_FFN_EINVAL_SHAPE, MOE_FFN_EINVAL_PTR, MOE_FFN_EUNSUPPORTED = -1, -2, -3
-MOE_FFN_EWORKSPACE, MOE_FFN_EHIP = -4, -5
+MOE_FFN_EWORKSPACE, MOE_FFN_EHIP, MOE_FFN_ESCRATCH = -4, -5, -6
+MOE_FFN_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_FFN_ACT_SWIGLU, MOE_FFN_ACT_CLAMPED_SWIGLU = 0, 1
 
 _MODES = {"auto": MOE_FFN_AUTO, "fused": MOE_FFN_FUSED, "split": MOE_FFN_SPLIT}
@@ -74,6 +75,7 @@ def library() -> ctypes.CDLL:
             "moe_ffn_gemm_kernel": ([PP, INT, INT], ctypes.c_char_p),
             "moe_ffn_forward": ([PP, VP, VP, VP, VP, VP, VP, INT, VP], INT),
             "moe_ffn_forward_events": ([PP, VP, VP, VP, VP, VP, VP, INT, VP, EV, INT], INT),
+            "moe_ffn_forward_noalloc": ([PP, VP, VP, VP, VP, VP, VP, INT, VP], INT),
             "moe_ffn_router": ([VP, I32, I32, I32, VP, VP, VP], INT),
             "moe_ffn_forward_logits": ([PP, VP, VP, VP, VP, VP, VP, VP, INT, VP, EV, INT], INT),
             "moe_ffn_shared_workspace_bytes": ([PP, I32, INT], SZ),
@@ -280,6 +282,27 @@ def moe_ffn_forward(x, w1, w2, topk_ids, topk_weights, out=None, mode="auto", x_
             rc = lib.moe_ffn_forward_events(*args, *_events(events))
     if rc != MOE_FFN_OK:
         raise MoeFfnError(rc, "moe_ffn_forward")
+    return out
+
+
+def moe_ffn_forward_noalloc(x, w1, w2, topk_ids, topk_weights, out, mode="auto", x_scale=None, w1_scale=None,
+                            w2_scale=None, stream=None):
+    """moe_ffn_forward on the library's static scratch array (moe_ffn_forward_noalloc):
+    neither the library nor this wrapper allocates, so `out` must be given and
+    topk_ids must already be int32. Raises MoeFfnError (MOE_FFN_ESCRATCH) for a
+    problem whose workspace exceeds MOE_FFN_NOALLOC_SCRATCH_BYTES. Calls that
+    overlap on one GPU share the array and race."""
+    if out is None or topk_ids.dtype != torch.int32:
+        raise ValueError("moe_ffn_forward_noalloc needs `out` and int32 topk_ids (it allocates nothing)")
+    T, D, H, E, k, path = _pass_shapes(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
+    _check_cuda(x, w1, w2, topk_ids, topk_weights, out, x_scale, w1_scale, w2_scale)
+    p = make_problem(T, D, H, E, k, path, x_scale, w1_scale, w2_scale)
+    s = torch.cuda.current_stream() if stream is None else stream
+    rc = library().moe_ffn_forward_noalloc(ctypes.byref(p), x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                                           topk_ids.data_ptr(), topk_weights.data_ptr(), out.data_ptr(),
+                                           _mode(mode), _sp(s))
+    if rc != MOE_FFN_OK:
+        raise MoeFfnError(rc, "moe_ffn_forward_noalloc")
     return out
 
 

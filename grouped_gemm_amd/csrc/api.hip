@@ -4,8 +4,16 @@
 #include "moe_ffn.h"
 
 #include <climits>
+#include <mutex>
 
 #include "common.h"
+
+// Scratch memory of moe_ffn_forward_noalloc: one array per device (each GPU
+// the library runs on holds its own copy from module load until the process
+// ends). In host code `scratch` names a host-side stand-in, not device
+// memory: host code only ever uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_FFN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -132,6 +140,7 @@ MOE_FFN_API const char* moe_ffn_strerror(int code) {
         case MOE_FFN_EUNSUPPORTED: return "unsupported dtype or mode";
         case MOE_FFN_EWORKSPACE: return "workspace missing, misaligned or too small";
         case MOE_FFN_EHIP: return "HIP launch error";
+        case MOE_FFN_ESCRATCH: return "problem needs more scratch than the library's static buffer holds";
         default: return "unknown error";
     }
 }
@@ -325,6 +334,41 @@ MOE_FFN_API int moe_ffn_forward_shared(const moe_ffn_problem* p, const void* x, 
     const SharedExpert sh{shared_w1, shared_w2, Hs};
     return forward_impl(p, x, w1, w2, nullptr, topk_ids, topk_weights, &sh, nullptr, out, mode, stream, events,
                         n_events);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL if the lookup failed.
+static void* scratch_address() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
+MOE_FFN_API int moe_ffn_forward_noalloc(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,
+                                        const int32_t* topk_ids, const float* topk_weights, void* out, int mode,
+                                        void* stream) {
+    int rc = check_shape(p);
+    if (rc != MOE_FFN_OK) return rc;
+    const int m = resolve(p, mode);
+    if (m < 0) return m;
+    if (make_plan(p, m).total > static_cast<size_t>(MOE_FFN_NOALLOC_SCRATCH_BYTES)) return MOE_FFN_ESCRATCH;
+    if (p->T == 0) return MOE_FFN_OK;
+    void* ws = scratch_address();
+    if (!ws) return MOE_FFN_EHIP;
+    moe_ffn_problem q = *p;
+    q.workspace = ws;
+    q.workspace_bytes = MOE_FFN_NOALLOC_SCRATCH_BYTES;
+    return forward_impl(&q, x, w1, w2, nullptr, topk_ids, topk_weights, nullptr, nullptr, out, m, stream, nullptr,
+                        0);
 }
 
 MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, const void* w1, const void* w2,

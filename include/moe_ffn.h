@@ -19,7 +19,8 @@
  *     comment says "host". Tensors are dense and row-major (last dim
  *     contiguous). bf16 tensors hold IEEE bfloat16 bit patterns (uint16).
  *   - The caller owns every buffer. The library never allocates device
- *     memory inside these calls and keeps no state between them.
+ *     memory inside these calls and keeps no state between them (the one
+ *     exception is the static scratch array of moe_ffn_forward_noalloc).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; no call synchronizes the host except where stated.
  *   - Return value: MOE_FFN_OK (0) or a negative MOE_FFN_E* code; no
@@ -62,7 +63,9 @@ enum {
     MOE_FFN_EINVAL_PTR = -2,    /* a required pointer is NULL or not 16-byte aligned */
     MOE_FFN_EUNSUPPORTED = -3,  /* dtype or mode unknown, or the pair not built */
     MOE_FFN_EWORKSPACE = -4,    /* workspace NULL, misaligned (256 B) or too small */
-    MOE_FFN_EHIP = -5           /* a HIP launch reported an error */
+    MOE_FFN_EHIP = -5,          /* a HIP launch reported an error */
+    MOE_FFN_ESCRATCH = -6       /* moe_ffn_forward_noalloc: the problem needs more
+                                   than MOE_FFN_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /* Problem descriptor (plain C; every pointer is caller-owned).
@@ -145,6 +148,29 @@ MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, 
                                        const void* w2, const int32_t* topk_ids,
                                        const float* topk_weights, void* out, int mode,
                                        void* stream, void* const* events, int n_events);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_ffn_forward with the workspace taken from a static device array of
+ * the library instead of p->workspace (which is ignored, as is
+ * p->workspace_bytes). The array is MOE_FFN_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per device; each GPU the library runs on holds it from the first call on
+ * that device until the process ends. The call allocates nothing and calls
+ * no allocating routine. A problem whose workspace (moe_ffn_workspace_bytes
+ * for the mode AUTO resolves to) exceeds the array returns MOE_FFN_ESCRATCH
+ * before anything is enqueued; 64 MiB holds the decode-shaped passes (the
+ * 64-token, 32-expert, D=6144, H=2048 split pass needs about 10 MB) and the
+ * fused pipeline up to about 4M tokens x D of fp32 accumulator. Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be ordered
+ * by the caller. The pass writes every scratch region before reading it, so
+ * what an earlier call left there does not matter. The current device must
+ * be the one `stream` belongs to. Other arguments as for moe_ffn_forward. */
+#define MOE_FFN_NOALLOC_SCRATCH_BYTES (64ll << 20)
+MOE_FFN_API int moe_ffn_forward_noalloc(const moe_ffn_problem* p, const void* x, const void* w1,
+                                        const void* w2, const int32_t* topk_ids,
+                                        const float* topk_weights, void* out, int mode,
+                                        void* stream);
 
 /* The router ahead of the pass (Prime Flash MoE, section 1 "The
  * computation": the pass starts from each token's top-k experts and their

@@ -15,7 +15,7 @@ def test_library_exports_every_header_function():
         assert hasattr(lib, n), n
     assert set(names) == {
         "moe_ffn_workspace_bytes", "moe_ffn_validate", "moe_ffn_resolve_mode", "moe_ffn_gemm_kernel", "moe_ffn_forward",
-        "moe_ffn_forward_events", "moe_ffn_router", "moe_ffn_forward_logits",
+        "moe_ffn_forward_events", "moe_ffn_forward_noalloc", "moe_ffn_router", "moe_ffn_forward_logits",
         "moe_ffn_shared_workspace_bytes", "moe_ffn_forward_shared", "moe_ffn_forward_act",
         "moe_ffn_route_workspace_bytes", "moe_ffn_route", "moe_ffn_mx_quantize", "moe_ffn_mxfp4_quantize",
         "moe_ffn_strerror"}
@@ -240,3 +240,16 @@ def test_binding_rejects_mx_scale_shapes():
     # matching shapes reach the device check (CPU tensors), not a launch
     with pytest.raises(ValueError, match="GPU"):
         g.moe_ffn_forward(x, w1, w2, ids, w, **good)
+
+
+def test_noalloc_limit_and_error_code():
+    # a problem beyond the static scratch array is refused by its size alone,
+    # before any pointer is looked at (so NULL pointers are fine here)
+    p = g.make_problem(4096, 2048, 768, 128, 8, "bf16")
+    assert g.moe_ffn_workspace_bytes(4096, 2048, 768, 128, 8, "bf16", "split") > g.MOE_FFN_NOALLOC_SCRATCH_BYTES
+    rc = g.library().moe_ffn_forward_noalloc(ctypes.byref(p), None, None, None, None, None, None,
+                                            g.MOE_FFN_SPLIT, None)
+    assert rc == g.MOE_FFN_ESCRATCH
+    assert "scratch" in g.moe_ffn_strerror(g.MOE_FFN_ESCRATCH)
+    # the decode workload fits
+    assert g.moe_ffn_workspace_bytes(64, 6144, 2048, 32, 8, "bf16", "split") < g.MOE_FFN_NOALLOC_SCRATCH_BYTES
