@@ -7,26 +7,37 @@ One step = one whole forward pass (route -> GEMM1 + SwiGLU -> GEMM2 +
 routing weight -> combine) over one batch of seeded synthetic inputs that are
 resident in HBM before timing starts. W untimed steps, then K timed steps
 bracketed by torch.cuda.synchronize(); rank 0 (the only rank) prints one JSON
-line on stdout. The default workload is the decode shape (T=64 tokens,
+line on stdout. The headline workload is the decode shape (T=64 tokens,
 E=32 experts, top-8, D=6144, H=2048, bf16): one GPU's share of an 8-way
 expert-parallel deployment, bound by streaming the expert weights from HBM.
+
+The same line carries a "configs" object with the prefill-shaped workloads,
+each timed the same way on inputs of its own: the mid prefill (T=4096,
+D=2048, H=768, E=128, top-8) in the split and the fused pipeline, the large
+prefill (T=131072, same dims, Zipf-skewed routing) and the MX-fp8 workload
+(T=16384, D=4096, H=1536, E=64, top-6), each with its roofline fraction and a
+CPU-oracle sample (--no-extra leaves them out).
 
 Per-kernel durations come from HIP events that the library records on the
 pass's own stream at its stage boundaries (moe_ffn_forward_events) during
 the timed steps: every --event-every-th timed step (default 8, starting with
 the first) carries the five events and the others run bare, because each
-event record adds a gap to the stream (about 14 us per step on the decode
-pass when every step carries them). The dominant kernel's roofline fraction
-uses its algorithmic bytes (weights of the experts hit + activations in and
-out) or flops (6*P*D*H split 4:2 over the two GEMMs) per launch, over the
-instrumented steps.
+event record adds a gap to the stream. The dominant kernel's roofline
+fraction uses its algorithmic bytes (weights of the experts hit +
+activations in and out) or flops (6*P*D*H split 4:2 over the two GEMMs) per
+launch, over the instrumented steps.
 
-The CPU baseline is the oracle (oracle/, plain C, OpenMP) timed on a bounded
-sample of the same workload on the host's cores.
+The CPU baseline is the oracle (oracle/, plain C, OpenMP), built for the
+host with -O3 -march=native, timed on a bounded sample of the same workload
+on all the host's cores (and, for the headline, on one core).
+--cpu-plan runs the fuller CPU timing plan instead of the GPU bench: every
+workload, median of 3 runs on the three smaller ones, one-thread runs of the
+tiny and decode workloads.
 
 After the timed steps, the same pass is captured once in a HIP graph and
-replayed K times (`graph_replay_ms`, median and mean of the replays); this
-is reported beside `value`, which stays the eager rate (--no-graph skips it).
+replayed K times between one pair of events (`graph_replay_ms`: the mean
+replay); this is reported beside `value`, which stays the eager rate
+(--no-graph skips it).
 """
 from __future__ import annotations
 
@@ -36,6 +47,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -50,6 +62,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 5000.0}
 STAGES = {"split": ["route", "gemm1_swiglu", "gemm2_weight", "combine"],
           "fused": ["route", "acc_fill", "fused_ffn", "acc_to_bf16"]}
+# (workload id, mode) of the prefill-shaped workloads timed beside the headline
+EXTRA = [(3, "split"), (3, "fused"), (4, "split"), (5, "split")]
 
 
 def log(*a):
@@ -65,7 +79,12 @@ def parse_args(argv=None):
     ap.add_argument("--mode", default="auto", choices=["auto", "split", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target wall time of the CPU-baseline sample")
+                    help="target wall time of the headline's CPU-baseline sample")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave out the prefill-shaped workloads timed beside the headline")
+    ap.add_argument("--extra-steps", type=int, default=20, help="timed steps of each extra workload")
+    ap.add_argument("--cpu-plan", action="store_true",
+                    help="time the CPU oracle on every workload (no GPU) and print one JSON line")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (crossover sweeps)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -178,41 +197,96 @@ def measured_traffic(stage: str, symbol: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inputs, dtype, target_s):
-    import oracle
-    oracle.build(force=False)
-    threads = oracle.num_threads()
-    order = np.arange(cfg.T)
-    n = min(cfg.T, 2)
-    while True:
-        tok = order[:n]
-        t0 = time.perf_counter()
-        if dtype == "bf16":
-            oracle.forward_bf16(inputs["x"], inputs["w1"], inputs["w2"], inputs["topk_ids"],
-                                inputs["topk_weights"], tokens=tok, shared=inputs.get("shared"))
-        elif dtype == "mxfp4":
-            oracle.forward_mx4(*inputs["xq"], *inputs["w1q"], *inputs["w2q"], inputs["topk_ids"],
-                               inputs["topk_weights"], tokens=tok)
-        else:
-            oracle.forward_mx(*inputs["xq"], *inputs["w1q"], *inputs["w2q"], inputs["topk_ids"],
-                              inputs["topk_weights"], tokens=tok)
-        dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or n == cfg.T:
-            break
-        n = min(cfg.T, max(n * 2, int(n * target_s / max(dt, 1e-3) * 0.9)))
-    flops = 6.0 * n * cfg.k * cfg.D * cfg.H
-    if inputs.get("shared") is not None:
-        flops += 6.0 * n * cfg.D * inputs["shared"][1].shape[1]
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {cfg.T} tokens ({n * cfg.k} routed pairs) of the same workload, "
-                      f"{dt:.2f} s wall, fp32 accumulation",
-            "seconds": dt, "tokens_per_s": n / dt}
+# ---------------- the CPU oracle, timed ----------------
 
+def _oracle_forward(cfg, host, dtype, tok):
+    import oracle
+    if dtype == "bf16":
+        oracle.forward_bf16(host["x"], host["w1"], host["w2"], host["topk_ids"], host["topk_weights"],
+                            tokens=tok, shared=host.get("shared"))
+    elif dtype == "mxfp4":
+        oracle.forward_mx4(*host["xq"], *host["w1q"], *host["w2q"], host["topk_ids"], host["topk_weights"],
+                           tokens=tok)
+    else:
+        oracle.forward_mx(*host["xq"], *host["w1q"], *host["w2q"], host["topk_ids"], host["topk_weights"],
+                          tokens=tok)
+
+
+def cpu_baseline(cfg, host, dtype, target_s, threads=None, repeats=1, max_tokens=None):
+    """The oracle (native build) on the first n tokens of the workload, n grown
+    until one run takes about target_s / 4 or more; then `repeats` runs of
+    those n tokens (median reported) on `threads` threads (default: all)."""
+    import oracle
+    oracle.use_native_build()
+    all_threads = oracle.num_threads()
+    oracle.set_num_threads(threads or all_threads)
+    used = oracle.num_threads()
+    cap = min(cfg.T, max_tokens or cfg.T)
+    n = min(cap, 2)
+    try:
+        while True:
+            t0 = time.perf_counter()
+            _oracle_forward(cfg, host, dtype, np.arange(n))
+            dt = time.perf_counter() - t0
+            if dt >= target_s / 4 or n == cap:
+                break
+            n = min(cap, max(n * 2, int(n * target_s / max(dt, 1e-3) * 0.9)))
+        runs = [dt]
+        for _ in range(repeats - 1):
+            t0 = time.perf_counter()
+            _oracle_forward(cfg, host, dtype, np.arange(n))
+            runs.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_num_threads(all_threads)
+    dt = statistics.median(runs)
+    flops = 6.0 * n * cfg.k * cfg.D * cfg.H
+    if host.get("shared") is not None:
+        flops += 6.0 * n * cfg.D * host["shared"][1].shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens ({n * cfg.k} routed pairs) of the same workload, "
+                      f"{'median of %d runs, ' % repeats if repeats > 1 else ''}{dt:.2f} s wall, fp32 accumulation",
+            "seconds": dt, "runs_s": runs, "tokens": n, "tokens_per_s": n / dt,
+            "routed_pairs_per_s": n * cfg.k / dt, "cpu_model": oracle.cpu_model(),
+            "build": "gcc -O3 -march=native -fopenmp -ffp-contract=off"}
+
+
+def cpu_plan():
+    """Every workload's oracle timing on this host: median of 3 on the tiny,
+    decode and mid prefill workloads (whole batches where they fit a few
+    seconds), one run on a sample of the large prefill and the MX workload,
+    and one-thread runs of the tiny and decode workloads."""
+    import moe_inputs as mi
+    import oracle
+    plan = {1: dict(target=8.0, repeats=3, single=True), 2: dict(target=12.0, repeats=3, single=True),
+            3: dict(target=12.0, repeats=3), 4: dict(target=30.0, repeats=1), 5: dict(target=30.0, repeats=1)}
+    out = {}
+    for cid, p in plan.items():
+        cfg = mi.CONFIGS[cid]
+        log(f"[cpu-plan] {cfg.name}: generating inputs")
+        if cfg.dtype == "bf16":
+            host = mi.make_bf16(cfg, 0)
+        else:
+            s = mi.make_mx_sources(cfg, 0)
+            host = dict(topk_ids=s["topk_ids"], topk_weights=s["topk_weights"],
+                        xq=oracle.mx_quantize(s["x"]), w1q=oracle.mx_quantize(s["w1"]),
+                        w2q=oracle.mx_quantize(s["w2"]))
+            del s
+        log(f"[cpu-plan] {cfg.name}: timing")
+        rec = {"all_threads": cpu_baseline(cfg, host, cfg.dtype, p["target"], repeats=p["repeats"])}
+        if p.get("single"):
+            rec["one_thread"] = cpu_baseline(cfg, host, cfg.dtype, p["target"] / 2, threads=1, repeats=1)
+        out[cfg.name] = rec
+        del host
+    return {"kind": "cpu_oracle_plan", "cpu_model": oracle.cpu_model(), "nproc": os.cpu_count(),
+            "workloads": out}
+
+
+# ---------------- one workload on the GPU ----------------
 
 def graph_replay_ms(step, n):
     """The same pass captured once in a HIP graph and replayed n times after the
-    timed eager steps (not part of `value`): median and mean of the replays,
-    each bracketed by events on the replaying stream."""
+    timed eager steps (not part of `value`), between one pair of events on the
+    replaying stream: the mean replay time."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -227,37 +301,55 @@ def graph_replay_ms(step, n):
     for _ in range(3):
         graph.replay()
     torch.cuda.synchronize()
-    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in marks:
-        a.record()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
         graph.replay()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) for a, b in marks)
+    ms = a.elapsed_time(b) / n
     del graph
-    return {"median": t[len(t) // 2], "mean": sum(t) / len(t), "replays": n}
+    return {"mean": ms, "replays": n}
 
 
-def main(argv=None):
-    args = parse_args(argv)
-    args.event_every = max(1, args.event_every)
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU expert-parallel layout is a design note, not built)", file=sys.stderr)
-        return 2
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def rows(self, n):
+        out = []
+        for _ in range(n):
+            row = []
+            for _ in range(5):
+                e = ctypes.c_void_p()
+                assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+                row.append(e.value)
+            out.append(row)
+        return out
+
+    def elapsed(self, a, b):
+        f = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, rows):
+        for row in rows:
+            for e in row:
+                self.hip.hipEventDestroy(e)
+
+
+def run_workload(cfg, mode_req, steps, warmup, event_every, hip, dev, shared_hs=0, use_logits=False,
+                 want_graph=True, cpu_target=0.0, cpu_single=False, copy_mib=0):
+    """Time one workload on the GPU; returns its result fields."""
     import torch
     import moe_inputs as mi
     import grouped_gemm_amd as g
 
-    cfg = mi.CONFIGS[args.config]
-    if args.tokens:
-        cfg = mi.custom(args.tokens, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, cfg.dtype, cid=cfg.cid,
-                        name=f"{cfg.name}_T{args.tokens}")
-    if args.mxfp4:
-        cfg = mi.custom(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, "mxfp4", cid=cfg.cid, name=cfg.name)
     dtype = cfg.dtype
-    dev = torch.device("cuda:0")
-    log(f"[bench] generating {cfg.name} inputs (seeded)")
+    log(f"[bench] generating {cfg.name} {dtype} inputs (seeded)")
     host = {}
     if dtype == "bf16":
         d = mi.make_bf16(cfg, 0)
@@ -272,11 +364,13 @@ def main(argv=None):
         q = {}
         for n in ("x", "w1", "w2"):
             quant = g.moe_ffn_mxfp4_quantize if (dtype == "mxfp4" and n != "x") else g.moe_ffn_mx_quantize
-            q[n] = quant(torch.from_numpy(s[n]).to(dev))
+            src = torch.from_numpy(s[n]).to(dev)
+            q[n] = quant(src)
+            del src
         torch.cuda.synchronize()
         x, w1, w2 = q["x"][0], q["w1"][0], q["w2"][0]
         scales = dict(x_scale=q["x"][1], w1_scale=q["w1"][1], w2_scale=q["w2"][1])
-        if not args.no_cpu_baseline:
+        if cpu_target > 0:
             host["xq"] = tuple(t.cpu().numpy() for t in q["x"])
             host["w1q"] = tuple(t.cpu().numpy() for t in q["w1"])
             host["w2q"] = tuple(t.cpu().numpy() for t in q["w2"])
@@ -284,39 +378,22 @@ def main(argv=None):
     ids = torch.from_numpy(host["topk_ids"]).to(dev)
     wts = torch.from_numpy(host["topk_weights"]).to(dev)
     shared = None
-    if args.shared_ffn:
-        if args.logits or dtype != "bf16":
-            print("bench.py: --shared-ffn runs the bf16 pass from given routes only", file=sys.stderr)
-            return 2
-        host["shared"] = mi.shared_expert(cfg, args.shared_ffn, 0)
+    if shared_hs:
+        host["shared"] = mi.shared_expert(cfg, shared_hs, 0)
         shared = tuple(torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16) for a in host["shared"])
     logits = None
-    if args.logits:
+    if use_logits:
         # the pass routes from these logits; ids / wts become its outputs
         host["logits"] = mi.router_logits(cfg, 0)
         logits = torch.from_numpy(host["logits"]).to(dev)
-    mode_id = g.moe_ffn_resolve_mode(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, args.mode)
+    mode_id = g.moe_ffn_resolve_mode(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, mode_req)
     mode = {g.MOE_FFN_FUSED: "fused", g.MOE_FFN_SPLIT: "split"}[mode_id]
     nbytes = g.moe_ffn_workspace_bytes(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype, mode)
-    if args.shared_ffn:
-        import ctypes as _ct
+    if shared_hs:
         pr = g.make_problem(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, dtype)
-        nbytes = g.library().moe_ffn_shared_workspace_bytes(_ct.byref(pr), args.shared_ffn, mode_id)
+        nbytes = g.library().moe_ffn_shared_workspace_bytes(ctypes.byref(pr), shared_hs, mode_id)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.D), dtype=torch.bfloat16, device=dev)
-
-    hip = ctypes.CDLL("libamdhip64.so.7")
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    events = []
-    for _ in range(args.steps):
-        row = []
-        for _ in range(5):
-            e = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(e)) == 0
-            row.append(e.value)
-        events.append(row)
 
     def step(ev=None):
         if shared is not None:
@@ -328,16 +405,16 @@ def main(argv=None):
         else:
             g.moe_ffn_forward(x, w1, w2, ids, wts, out=out, mode=mode, workspace=ws, events=ev, **scales)
 
-    log(f"[bench] {cfg.name} mode={mode}: {args.warmup} warmup + {args.steps} timed steps")
-    for _ in range(args.warmup):
+    events = hip.rows(steps)
+    log(f"[bench] {cfg.name} mode={mode}: {warmup} warmup + {steps} timed steps")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i] if i % args.event_every == 0 else None)
+    for i in range(steps):
+        step(events[i] if i % event_every == 0 else None)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed / args.steps * 1e3
+    ms = (time.perf_counter() - t0) / steps * 1e3
 
     names = list(STAGES[mode])
     if logits is not None:
@@ -345,25 +422,22 @@ def main(argv=None):
     if shared is not None:
         names[0] = "shared_expert_route"
     stage_ms = {n: 0.0 for n in names}
-    f = ctypes.c_float()
-    timed = [events[i] for i in range(args.steps) if i % args.event_every == 0]
+    timed = [events[i] for i in range(steps) if i % event_every == 0]
     for row in timed:
         for j, n in enumerate(names):
-            assert hip.hipEventElapsedTime(ctypes.byref(f), row[j], row[j + 1]) == 0
-            stage_ms[n] += f.value / len(timed)
-    for row in events:
-        for e in row:
-            hip.hipEventDestroy(e)
+            stage_ms[n] += hip.elapsed(row[j], row[j + 1]) / len(timed)
+    hip.destroy(events)
 
     graph_ms = None
-    if not args.no_graph and shared is None and logits is None:
-        graph_ms = graph_replay_ms(step, args.steps)
+    if want_graph and shared is None and logits is None:
+        graph_ms = graph_replay_ms(step, steps)
 
-    if args.copy_mib:
-        a = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+    if copy_mib:
+        a = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     if logits is not None:
         host["topk_ids"] = ids.cpu().numpy()  # the routes the timed passes took
@@ -379,56 +453,105 @@ def main(argv=None):
     if logits is not None:
         workload += " from router logits"
     if shared is not None:
-        workload += f" + shared expert Hs={args.shared_ffn}"
-    traffic = measured_traffic(dom, kernel_symbol(cfg, mode, dom), workload)
+        workload += f" + shared expert Hs={shared_hs}"
+    symbol = kernel_symbol(cfg, mode, dom)
     if intensity > ridge:
         roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": dbytes / dsec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic
+    roof["traffic"] = measured_traffic(dom, symbol, workload)
     roof["kernel"] = dom
-    roof["kernel_symbol"] = kernel_symbol(cfg, mode, dom)
+    roof["kernel_symbol"] = symbol
     roof["algorithmic_bytes"] = dbytes
     roof["algorithmic_flops"] = dflops
     roof["avg_launch_ms"] = stage_ms[dom]
 
-    flops = cfg.flops + (6.0 * cfg.T * cfg.D * args.shared_ffn if shared is not None else 0.0)
+    flops = cfg.flops + (6.0 * cfg.T * cfg.D * shared_hs if shared is not None else 0.0)
     tflops = flops / (ms * 1e-3) / 1e12
     all_bytes = hit * 3 * cfg.H * cfg.D * {"bf16": 2, "mxfp8": 1, "mxfp4": 0.5}[dtype] + 2 * cfg.T * cfg.D * 2
+    res = {
+        "workload": workload, "mode": mode, "dtype": dtype, "ms_per_step": ms, "tflops": tflops,
+        "routed_tokens_per_s": cfg.P / (ms * 1e-3), "tokens_per_s": cfg.T / (ms * 1e-3),
+        "pct_mfma_peak": tflops / peak_tf, "effective_hbm_gbs": all_bytes / (ms * 1e-3) / 1e9,
+        "pct_hbm_peak": all_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stage_ms": stage_ms, "graph_replay_ms": graph_ms, "stage_events_every": event_every,
+        "roofline": roof, "experts_hit": hit, "steps": steps, "warmup": warmup,
+    }
+    del x, w1, w2, ws, out, ids, wts, scales, shared, logits
+    torch.cuda.empty_cache()
+    if cpu_target > 0:
+        log(f"[bench] timing the CPU oracle on a sample of {cfg.name}")
+        if use_logits:
+            import oracle
+            host["topk_ids"], host["topk_weights"] = oracle.router(host["logits"], cfg.k)
+        res["cpu_baseline"] = cpu_baseline(cfg, host, dtype, cpu_target)
+        if cpu_single:
+            res["cpu_baseline"]["one_thread"] = cpu_baseline(cfg, host, dtype, cpu_target / 4, threads=1)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    args.event_every = max(1, args.event_every)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU expert-parallel layout is a design note, not built)", file=sys.stderr)
+        return 2
+    if args.cpu_plan:
+        print(json.dumps(cpu_plan()), flush=True)
+        return 0
+    import torch
+    import moe_inputs as mi
+
+    cfg = mi.CONFIGS[args.config]
+    if args.tokens:
+        cfg = mi.custom(args.tokens, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, cfg.dtype, cid=cfg.cid,
+                        name=f"{cfg.name}_T{args.tokens}")
+    if args.mxfp4:
+        cfg = mi.custom(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, "mxfp4", cid=cfg.cid, name=cfg.name)
+    if args.shared_ffn and (args.logits or cfg.dtype != "bf16"):
+        print("bench.py: --shared-ffn runs the bf16 pass from given routes only", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    hip = HipEvents()
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    head = run_workload(cfg, args.mode, args.steps, args.warmup, args.event_every, hip, dev,
+                        shared_hs=args.shared_ffn, use_logits=args.logits, want_graph=not args.no_graph,
+                        cpu_target=cpu, cpu_single=True, copy_mib=args.copy_mib)
+
     result = {
         "metric": METRIC,
-        "value": tflops,
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic (seeded; routing, x and random-init expert weights of the stated shape)",
-        "config": {"workload": workload, "mode": mode, "tokens": cfg.T, "experts": cfg.E,
-                   "topk": cfg.k, "hidden": cfg.D, "ffn": cfg.H, "experts_hit": hit,
+        "config": {"workload": head["workload"], "mode": head["mode"], "tokens": cfg.T, "experts": cfg.E,
+                   "topk": cfg.k, "hidden": cfg.D, "ffn": cfg.H, "experts_hit": head["experts_hit"],
                    "parallelism": "single GPU"},
-        "routed_tokens_per_s": cfg.P / (ms * 1e-3),
-        "tokens_per_s": cfg.T / (ms * 1e-3),
-        "pct_mfma_peak": tflops / peak_tf,
-        "effective_hbm_gbs": all_bytes / (ms * 1e-3) / 1e9,
-        "stage_ms": stage_ms,
-        "graph_replay_ms": graph_ms,
-        "stage_events_every": args.event_every,
-        "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        if logits is not None:
-            import oracle
-            host["topk_ids"], host["topk_weights"] = oracle.router(host["logits"], cfg.k)
-        result["cpu_baseline"] = cpu_baseline(cfg, host, dtype, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
+    for key in ("routed_tokens_per_s", "tokens_per_s", "pct_mfma_peak", "effective_hbm_gbs", "pct_hbm_peak",
+                "stage_ms", "graph_replay_ms", "stage_events_every", "roofline", "cpu_baseline"):
+        result[key] = head[key]
+
+    plain = not (args.tokens or args.mxfp4 or args.shared_ffn or args.logits or args.config != 2)
+    if plain and not args.no_extra:
+        extra = {}
+        for cid, mode in EXTRA:
+            c = mi.CONFIGS[cid]
+            r = run_workload(c, mode, args.extra_steps, 3, 4, hip, dev, want_graph=not args.no_graph,
+                             cpu_target=0.0 if args.no_cpu_baseline else 4.0)
+            extra[f"{c.name}_{mode}"] = r
+        result["configs"] = extra
     print(json.dumps(result), flush=True)
     return 0
 

@@ -21,17 +21,27 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# The same source built for the host it runs on, for the CPU-baseline timing
+# only (-O3 -march=native; still no fast-math and no FMA contraction, so the
+# results are the checker's bit for bit).
+_NATIVE_LIB = os.path.join(_HERE, "libmoe_oracle_native.so")
+_FLAGS = ["-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 _lib = None
+_native = None
+
+
+def _compile(out: str, opt) -> str:
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *opt, *_FLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math, no FMA contraction)."""
+    """Compile the checker build of the oracle with gcc (-O2, portable x86-64-v2,
+    OpenMP, no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-march=x86-64-v2", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
+        _compile(_LIB, ["-O2", "-march=x86-64-v2"])
     return _LIB
 
 
@@ -40,39 +50,68 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build()
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        i32, i64 = ctypes.c_int32, ctypes.c_int64
-        lib.oracle_route.argtypes = [P, i64, i32, i32, P, P, P, P]
-        lib.oracle_router.argtypes = [P, i64, i32, i32, P, P]
-        lib.oracle_forward_bf16.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i64]
-        lib.oracle_forward_bf16_act.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, i32, ctypes.c_float, P,
-                                                i32, P, P, i64]
-        lib.oracle_forward_bf16_shared.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P, P,
-                                                   i64]
-        lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
-                                          P, i64, i32]
-        lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
-                                           P, i64, i32]
-        lib.oracle_mx_quantize.argtypes = [P, i64, i64, P, P]
-        lib.oracle_mx4_quantize.argtypes = [P, i64, i64, P, P]
-        lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
-        lib.oracle_e2m1_decode.restype = ctypes.c_float
-        lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
-        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
-        lib.oracle_mx4_scale_exp.argtypes = [P, ctypes.c_int]
-        lib.oracle_mx4_scale_exp.restype = ctypes.c_int
-        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
-        lib.oracle_e4m3_decode.restype = ctypes.c_float
-        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
-        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
-        lib.oracle_mx_scale_exp.argtypes = [P, ctypes.c_int]
-        lib.oracle_mx_scale_exp.restype = ctypes.c_int
-        lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
-        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        lib.oracle_num_threads.restype = ctypes.c_int
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
+
+
+def use_native_build() -> None:
+    """Route the forward functions below through the -O3 -march=native build of
+    the same source, compiled here for this host (the CPU-baseline timing)."""
+    global _native, _lib
+    if _native is None:
+        _native = _bind(ctypes.CDLL(_compile(_NATIVE_LIB, ["-O3", "-march=native"])))
+    _load()
+    _lib = _native
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def _bind(lib):
+    """Declare the C signatures on a loaded build of moe_oracle.c."""
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_route.argtypes = [P, i64, i32, i32, P, P, P, P]
+    lib.oracle_router.argtypes = [P, i64, i32, i32, P, P]
+    lib.oracle_forward_bf16.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i64]
+    lib.oracle_forward_bf16_act.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, i32, ctypes.c_float, P,
+                                            i32, P, P, i64]
+    lib.oracle_forward_bf16_shared.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P, P,
+                                               i64]
+    lib.oracle_forward_mx.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                      P, i64, i32]
+    lib.oracle_forward_mx4.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                       P, i64, i32]
+    lib.oracle_mx_quantize.argtypes = [P, i64, i64, P, P]
+    lib.oracle_mx4_quantize.argtypes = [P, i64, i64, P, P]
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_decode.restype = ctypes.c_float
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.oracle_mx4_scale_exp.argtypes = [P, ctypes.c_int]
+    lib.oracle_mx4_scale_exp.restype = ctypes.c_int
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_float
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_mx_scale_exp.argtypes = [P, ctypes.c_int]
+    lib.oracle_mx_scale_exp.restype = ctypes.c_int
+    lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    return lib
 
 
 def _p(a: np.ndarray):

@@ -542,3 +542,14 @@ int oracle_num_threads(void) {
     }
     return n;
 }
+
+/* Threads for the OpenMP loops that follow (the CPU-baseline timing runs the
+ * oracle on one thread as well as on all of them). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
