@@ -85,6 +85,9 @@ def parse_args(argv=None):
     ap.add_argument("--extra-steps", type=int, default=20, help="timed steps of each extra workload")
     ap.add_argument("--cpu-plan", action="store_true",
                     help="time the CPU oracle on every workload (no GPU) and print one JSON line")
+    ap.add_argument("--crossover", default="", metavar="T1,T2,...",
+                    help="time both pipelines of the --config workload's dims at these token counts "
+                         "(graph replays and stage events) and print one JSON line instead of the bench")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (crossover sweeps)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -136,7 +139,7 @@ def kernel_work(cfg, mode, hit, dtype):
 
 
 KERNEL_FILES = {"dma_split_kernel": "gemm_skinny.hip", "dma_skinny_kernel": "gemm_skinny.hip",
-                "mx_fused_kernel": "mx.hip",
+                "mx_fused_kernel": "mx.hip", "fused_dma_kernel": "gemm_skinny.hip",
                 "mx_skinny_kernel": "gemm_skinny.hip",
                 "big_gemm_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
@@ -517,6 +520,25 @@ def main(argv=None):
         return 2
     dev = torch.device("cuda:0")
     hip = HipEvents()
+    if args.crossover:
+        import grouped_gemm_amd as g
+        rows = []
+        for T in (int(t) for t in args.crossover.split(",")):
+            c = mi.custom(T, cfg.D, cfg.H, cfg.E, cfg.k, cfg.routing, cfg.dtype, cid=cfg.cid, name=f"{cfg.name}_T{T}")
+            row = {"T": T, "pairs": c.P}
+            for mode in ("split", "fused"):
+                r = run_workload(c, mode, args.steps, args.warmup, args.event_every, hip, dev)
+                row[mode] = {"ms_per_step": r["ms_per_step"], "graph_replay_ms": r["graph_replay_ms"]["mean"],
+                             "stage_ms": r["stage_ms"],
+                             "kernel": g.moe_ffn_gemm_kernel(T, c.D, c.H, c.E, c.k, c.dtype, mode, 1)}
+            row["auto"] = {g.MOE_FFN_FUSED: "fused", g.MOE_FFN_SPLIT: "split"}[
+                g.moe_ffn_resolve_mode(T, c.D, c.H, c.E, c.k, c.dtype, "auto")]
+            log(f"[crossover] T={T}: split {row['split']['graph_replay_ms']:.3f} ms, "
+                f"fused {row['fused']['graph_replay_ms']:.3f} ms (graph replays)")
+            rows.append(row)
+        print(json.dumps({"kind": "crossover", "dims": f"D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k} {cfg.dtype}",
+                          "routing": cfg.routing, "steps": args.steps, "rows": rows}), flush=True)
+        return 0
     cpu = 0.0 if args.no_cpu_baseline else args.cpu_seconds
     head = run_workload(cfg, args.mode, args.steps, args.warmup, args.event_every, hip, dev,
                         shared_hs=args.shared_ffn, use_logits=args.logits, want_graph=not args.no_graph,

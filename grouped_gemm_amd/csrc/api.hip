@@ -168,10 +168,10 @@ MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, 
     // split pipeline's workspace always holds the table
     static int32_t table_stand_in;
     if (p->dtype == MOE_FFN_BF16) {
-        if (m == MOE_FFN_FUSED) return "fused_bf16_kernel";
         moe::Bf16Args a{};
         a.T = p->T; a.D = p->D; a.H = p->H; a.E = p->E; a.k = p->topk;
         a.P = static_cast<int64_t>(p->T) * p->topk;
+        if (m == MOE_FFN_FUSED) return moe::fused_decode_supported(a) ? "fused_dma_kernel" : "fused_bf16_kernel";
         a.mtiles = &table_stand_in;
         if (moe::bf16_uses_decode_kernels(a))
             return (g1 ? p->D : p->H) % 256 == 0 ? "dma_split_kernel" : "dma_skinny_kernel";

@@ -193,6 +193,11 @@ hipError_t launch_big_gemm(const Bf16Args& a, bool gemm1, hipStream_t s);
 // with 32 or 64.
 bool decode_kernels_fit(int64_t T, int k, int E);
 hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
+// The fused pass on the decode kernels' rings (32-row m-tiles, 256-wide
+// slices of the intermediate dimension); D and H multiples of 256, no
+// activation variant. Adds into a.acc32, which must hold zeros.
+bool fused_decode_supported(const Bf16Args& a);
+hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s);
 
 struct MxArgs {
     int32_t T, D, H, E, k;

@@ -526,8 +526,12 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     const int64_t n = static_cast<int64_t>(a.T) * a.D;
     fill_zero_f32_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<float4*>(a.acc32), n / 4);
     record(ev, 0, s);
-    dim3 g(mtiles_upper(a.P, a.E, BM), a.H / BH);
-    fused_bf16_kernel<BM, BH><<<g, kThreads, 0, s>>>(a);
+    if (fused_decode_supported(a)) {
+        launch_fused_decode(a, s);
+    } else {
+        dim3 g(mtiles_upper(a.P, a.E, BM), a.H / BH);
+        fused_bf16_kernel<BM, BH><<<g, kThreads, 0, s>>>(a);
+    }
     record(ev, 1, s);
     f32_to_bf16_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(a.acc32),
                                                              reinterpret_cast<const uint2*>(a.shared_y),

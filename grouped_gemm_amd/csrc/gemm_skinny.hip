@@ -174,16 +174,12 @@ __device__ __forceinline__ void dma_epilogue_token(const Bf16Args& a, const MTil
 // End of a row group: the four waves' partials (acc[b][t][v]: row 16b +
 // 4kg + v, token 16t + r) meet in `red` (a just-consumed ring slot of SLOT
 // bytes, PB row blocks per pass, LDS-only barriers so the DMAs in flight
-// keep running); wave t sums and stores token tile t of group g: GEMM1 the act
-// columns g*32.. (silu(gate) * up, or the activation variant), GEMM2 the
-// weighted outputs g*64.. of the pair's ypair row.
-template <int SLOT, bool GEMM1>
-__device__ __forceinline__ void dma_group_end(const Bf16Args& a, f32x4_t (&acc)[4][2], float* red, const MTile& mt,
-                                              int g, int wave, int lane, int ep, float esc) {
+// keep running); wave t (t < 2) is left holding the sums of token tile t.
+template <int SLOT>
+__device__ __forceinline__ void group_reduce(f32x4_t (&acc)[4][2], float* red, int wave, int lane) {
     constexpr int NB = 4, NT = 2, NV = NB * NT * 4;
     constexpr int PB = (4 * NV * 64 * 4 <= SLOT) ? NB : (4 * (NV / 2) * 64 * 4 <= SLOT ? NB / 2 : 1);
     static_assert(4 * PB * NT * 4 * 64 * 4 <= SLOT, "reduction pass must fit one ring slot");
-    const int r = lane & 15, kg = lane >> 4;
     constexpr int PV = PB * NT * 4;  // floats per lane per pass
 #pragma unroll
     for (int b0 = 0; b0 < NB; b0 += PB) {
@@ -212,6 +208,17 @@ __device__ __forceinline__ void dma_group_end(const Bf16Args& a, f32x4_t (&acc)[
             }
         }
     }
+}
+
+// The split pipeline's group end: wave t stores token tile t of group g:
+// GEMM1 the act columns g*32.. (silu(gate) * up, or the activation variant),
+// GEMM2 the weighted outputs g*64.. of the pair's ypair row.
+template <int SLOT, bool GEMM1>
+__device__ __forceinline__ void dma_group_end(const Bf16Args& a, f32x4_t (&acc)[4][2], float* red, const MTile& mt,
+                                              int g, int wave, int lane, int ep, float esc) {
+    constexpr int NB = 4, NT = 2;
+    const int r = lane & 15, kg = lane >> 4;
+    group_reduce<SLOT>(acc, red, wave, lane);
     // epilogue: wave w stores token tile w (acc[b][t][v]: row 16b + 4kg + v, token 16t + r)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -506,29 +513,328 @@ __global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) 
     }
 }
 
+// ---------------- fused pass for few rows per expert ----------------
+// The fused pipeline ("Prime Flash MoE", section 2 "Trick 2": the down
+// projection split over slices of the intermediate dimension, each slice's
+// partial added into a global accumulator) on the decode kernels' rings. A
+// block owns one 32-row m-tile and a slice of BH act columns h0 .. h0 + BH - 1:
+//   phase 1 streams the slice's gate and up rows of W1 (BH/32 row groups of
+//     32 act columns, as GEMM1 of dma_split_kernel) and leaves silu(gate) * up
+//     as bf16 in LDS;
+//   phase 2 streams the slice's columns of every W2 row (groups of R2 output
+//     features, one 32 KB stage each) against that act tile and adds
+//     weight * partial into acc32 [T, D] (fp32).
+// The weight waves (0-1) run one continuous ring through both phases, so
+// phase 2's first W2 stages are in flight while phase 1 drains. In phase 2
+// each wave owns a quarter of a group's output rows over the whole slice (no
+// cross-wave reduction); the result goes through an LDS staging tile so that
+// each atomic instruction covers 64 consecutive floats of one token row (two
+// whole cache lines: MI355X's L2 atomics cost per line touched), and only the
+// token waves (2-3), which move nothing in phase 2, issue the atomics, so the
+// weight waves' vmcnt budgets count their DMAs alone. The blocks of one
+// m-tile's slices are consecutive in the grid, so they run side by side:
+// their phase-2 reads of W2 fall in the same rows at about the same time,
+// and the m-tile's token rows come from L2.
+template <int BH>
+struct FusedTile {
+    static constexpr int G1 = BH / 32;       // GEMM1 row groups per slice
+    static constexpr int RB2 = 2 * BH;       // bytes of a W2 row per stage (the slice)
+    static constexpr int R2 = 32768 / RB2;   // W2 rows per stage (32 KB)
+    static constexpr int CPR2 = RB2 / 16;    // 16-byte chunks per W2 (and act) row
+    static constexpr int RPI2 = 1024 / RB2;  // W2 rows per DMA instruction
+    static constexpr int NS2 = BH / 32;      // k-steps per phase-2 stage
+    static constexpr int NB2 = R2 / 64;      // 16-row blocks of a wave in phase 2
+    static constexpr int ACT = 32 * RB2;     // act tile [32 tokens][BH] bf16
+    static constexpr int STG_ROW = R2 + 4;   // staging row in floats (padded: conflict-free writes)
+    static constexpr int STG = 32 * STG_ROW * 4;
+    static_assert(BH == 128 || BH == 256, "128- or 256-wide slices");
+};
+
+__device__ __forceinline__ void lds_read3(bf16x8_t (&f)[3], const uint32_t (&p)[3]) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2])
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_read4(bf16x8_t (&f)[4], const uint32_t (&p)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+
+// grid: (m-tiles x slices), the slices of one m-tile consecutive.
+template <int BH, int SW>
+__global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
+    using T = DmaTile<2, 256, 2>;  // phase 1: 512-byte row segments, KC = 256 values per stage
+    using F = FusedTile<BH>;
+    constexpr int NB = 4, NT = 2;
+    constexpr int W_INS = 2 * T::W_INS, T_INS = 2 * T::T_INS;  // per wave of the pair that moves them
+    static_assert(W_INS * 1024 * 2 == T::W_BYTES, "a stage is the two weight waves' DMAs");
+    static_assert(SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT + F::STG <= 160 * 1024 - 512, "LDS of a CU");
+    static_assert((SW - 1) * W_INS < 64, "vmcnt range");
+    static_assert(2 * T::T_BYTES == T::W_BYTES, "the token ring holds one weight stage in phase 2");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT + F::STG];
+    __shared__ int64_t sRow[32];  // acc32 row offset (token * D) of each m-tile row
+    __shared__ float sW[32];      // its routing weight (0 past the tile's rows)
+    uint8_t* const tring = lds + SW * T::W_BYTES;
+    uint8_t* const act = tring + 2 * T::T_BYTES;
+    float* const stg = reinterpret_cast<float*>(act + F::ACT);
+    const int nslices = a.H / BH;
+    const int slice = blockIdx.x % nslices;
+    MTile mt;
+    if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool wmover = wave < 2;
+    const int mw = wave & 1;
+    const int h0 = slice * BH;
+    const int KIT1 = a.D / 256, NIT1 = F::G1 * KIT1, NG2 = a.D / F::R2, NIT = NIT1 + NG2;
+    const int rot = (blockIdx.x / nslices + slice) % NG2;  // spread the blocks' W2 reads over HBM channels
+    if (threadIdx.x < 32) {
+        const int m = threadIdx.x;
+        const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
+        sRow[m] = static_cast<int64_t>(p / a.k) * a.D;
+        sW[m] = m < mt.rows ? a.wts[p] : 0.0f;
+    }
+    const char* src[W_INS];
+    if (wmover) {
+        const int pc = lane % T::CPR;
+#pragma unroll
+        for (int j = 0; j < W_INS; ++j) {
+            const int row = (mw * W_INS + j) * T::RPI + lane / T::CPR;
+            const int c = pc ^ (row & (T::CPR - 1));
+            const int64_t grow = static_cast<int64_t>(mt.expert) * 2 * a.H + (row < 32 ? h0 + row : a.H + h0 + row - 32);
+            src[j] = reinterpret_cast<const char*>(a.w1) + grow * a.D * 2 + c * 16;
+        }
+    } else {
+        const int pc = lane % T::CPR;
+#pragma unroll
+        for (int j = 0; j < W_INS; ++j) {
+            const int m = (mw * T_INS + (j < T_INS ? j : 0)) * T::RPI + lane / T::CPR;
+            const int c = pc ^ (m & (T::CPR - 1));
+            const int mm = m < mt.rows ? m : 0;
+            const int64_t tok = clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
+            src[j] = reinterpret_cast<const char*>(a.x) + tok * a.D * 2 + c * 16;
+        }
+    }
+    __syncthreads();  // sRow / sW, and every wave's index loads done before the ring starts
+    const int64_t gstride1 = static_cast<int64_t>(32) * a.D * 2, gstride2 = static_cast<int64_t>(F::R2) * a.H * 2;
+    // LDS slot of weight stage `it`: phase 1 cycles over the SW weight slots;
+    // phase 2, which no longer needs the token ring, cycles over SW + 1 slots
+    // (the next SW weight slots in order, then the token ring's 32 KB), so it
+    // keeps SW - 1 stages in flight instead of SW - 2
+    auto wslot_of = [&](int it) -> uint8_t* {
+        if (it < NIT1) return lds + (it % SW) * T::W_BYTES;
+        const int i2 = (it - NIT1) % (SW + 1);
+        return i2 == SW ? tring : lds + ((NIT1 + i2) % SW) * T::W_BYTES;
+    };
+    // weight stage `it`: phase 1 (W1 rows of group it / KIT1, K step it % KIT1)
+    // or phase 2 (R2 W2 rows of group (it - NIT1 + rot) % NG2, the slice's columns)
+    auto issue_w = [&](int it) {
+        if (it == NIT1) {
+            const int pc = lane % F::CPR2;
+#pragma unroll
+            for (int j = 0; j < W_INS; ++j) {
+                const int row = (mw * W_INS + j) * F::RPI2 + lane / F::CPR2;
+                const int c = pc ^ (row & (F::CPR2 - 1));
+                src[j] = reinterpret_cast<const char*>(a.w2) +
+                         ((static_cast<int64_t>(mt.expert) * a.D + row) * a.H + h0) * 2 + c * 16;
+            }
+        }
+        const int64_t off = it < NIT1 ? static_cast<int64_t>(it % KIT1) * T::RB + (it / KIT1) * gstride1
+                                      : ((it - NIT1 + rot) % NG2) * gstride2;
+        uint8_t* slot = wslot_of(it);
+#pragma unroll
+        for (int j = 0; j < W_INS; ++j)
+            __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
+                                             kWeightDmaAux);
+    };
+    auto issue_t = [&](int it) {
+        const int64_t off = static_cast<int64_t>(it % KIT1) * T::RB;
+        uint8_t* slot = tring + (it & 1) * T::T_BYTES;
+#pragma unroll
+        for (int j = 0; j < T_INS; ++j)
+            __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * T_INS + j) * 1024), 16, 0, 0);
+    };
+    const int r = lane & 15, kg = lane >> 4;
+    f32x4_t acc[NB][NT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
+    if (wmover) {
+#pragma unroll
+        for (int j = 0; j < SW - 1; ++j) issue_w(j);
+    } else {
+        issue_t(0);
+    }
+    for (int it = 0; it < NIT; ++it) {
+        if (wmover) {
+            // stages issued so far: through it + SW - 2 (phase 1 and the
+            // first phase-2 iteration), through it + SW - 1 after that
+            const int ahead = (it > NIT1 ? it + SW - 1 : it + SW - 2) - it;
+            const int left = NIT - 1 - it;
+            const int n = ahead < left ? ahead : left;
+            if (n >= SW - 1) wait_vm<(SW - 1) * W_INS>();
+            else if (n == SW - 2) wait_vm<(SW - 2) * W_INS>();
+            else wait_vm<0>();
+        } else if (it < NIT1) {
+            wait_vm<0>();
+        }
+        if (it == NIT1) lds_barrier();  // the act tile's last LDS writes are complete
+        else ring_barrier();
+        if (wmover) {
+            if (it < NIT1) {
+                if (it + SW - 1 < NIT) issue_w(it + SW - 1);
+            } else {
+                if (it == NIT1 && it + SW - 1 < NIT) issue_w(it + SW - 1);  // the token ring is free from here
+                if (it + SW < NIT) issue_w(it + SW);
+            }
+        } else if (it + 1 < NIT1) {
+            issue_t(it + 1);
+        }
+        uint8_t* wslot = wslot_of(it);
+        if (it < NIT1) {
+            // phase 1: GEMM1 with the stage's k-steps split over the four waves
+            uint8_t* tslot = tring + (it & 1) * T::T_BYTES;
+#pragma unroll
+            for (int q = 0; q < T::NS / 4; ++q) {
+                const int c = 4 * (wave * (T::NS / 4) + q) + kg;
+                uint32_t pw[4], pt[2];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int row = 16 * b + r;
+                    pw[b] = lds_addr(wslot + row * T::RB + ((c ^ (row & (T::CPR - 1))) << 4));
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int m = 16 * t + r;
+                    pt[t] = lds_addr(tslot + m * T::RB + ((c ^ (m & (T::CPR - 1))) << 4));
+                }
+                bf16x8_t w[NB], tk[NT];
+                lds_read6(w, tk, pw, pt);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[b][t] = mfma16(w[b], tk[t], acc[b][t]);
+            }
+            if (it % KIT1 != KIT1 - 1) continue;
+            // group end: silu(gate) * up of act columns 32g .. 32g + 31 into the act tile
+            group_reduce<T::W_BYTES>(acc, reinterpret_cast<float*>(wslot), wave, lane);
+            const int g = it / KIT1;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t != wave) continue;
+                const int m = 16 * t + r;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float gt = acc[j][t][q], u = acc[j + 2][t][q];
+                        v[q] = gt / (1.0f + __expf(-gt)) * u;
+                    }
+                    const int h = 32 * g + 16 * j + 4 * kg;  // act columns h .. h + 3 of the slice
+                    *reinterpret_cast<uint2*>(act + m * F::RB2 + (((h >> 3) ^ (m & (F::CPR2 - 1))) << 4) +
+                                              (h & 7) * 2) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
+            continue;
+        }
+        // phase 2: wave w owns the group's rows R2/4 * w .. R2/4 * (w + 1) - 1 over the whole slice
+        f32x4_t y[F::NB2][NT];
+#pragma unroll
+        for (int b = 0; b < F::NB2; ++b)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) y[b][t] = f32x4_t{};
+#pragma unroll
+        for (int q = 0; q < F::NS2; ++q) {
+            const int c = 4 * q + kg;
+            constexpr int NR = F::NB2 + NT;
+            uint32_t p[NR];
+#pragma unroll
+            for (int b = 0; b < F::NB2; ++b) {
+                const int row = F::R2 / 4 * wave + 16 * b + r;
+                p[b] = lds_addr(wslot + row * F::RB2 + ((c ^ (row & (F::CPR2 - 1))) << 4));
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int m = 16 * t + r;
+                p[F::NB2 + t] = lds_addr(act + m * F::RB2 + ((c ^ (m & (F::CPR2 - 1))) << 4));
+            }
+            bf16x8_t f[NR];
+            if constexpr (NR == 3) lds_read3(f, p);
+            else lds_read4(f, p);
+#pragma unroll
+            for (int b = 0; b < F::NB2; ++b)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) y[b][t] = mfma16(f[b], f[F::NB2 + t], y[b][t]);
+        }
+        // stage the R2 x 32 tile as [token][output] and add weight * y with
+        // atomics of 64 consecutive floats per instruction
+#pragma unroll
+        for (int b = 0; b < F::NB2; ++b)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4_t*>(stg + (16 * t + r) * F::STG_ROW + F::R2 / 4 * wave + 16 * b + 4 * kg) =
+                    y[b][t];
+        lds_barrier();
+        if (!wmover) {
+            const int d0 = ((it - NIT1 + rot) % NG2) * F::R2;
+            const int i = threadIdx.x - 128;
+#pragma unroll 4
+            for (int j = 0; j < F::R2 / 4; ++j) {
+                const int idx = j * 128 + i, m = idx / F::R2, d = idx % F::R2;
+                if (m < mt.rows) unsafeAtomicAdd(a.acc32 + sRow[m] + d0 + d, sW[m] * stg[m * F::STG_ROW + d]);
+            }
+        }
+    }
+}
+
 inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
 
 
 
+// 32-row m-tiles expected for T tokens with k routes each over E experts,
+// routes spread uniformly: the experts hit, each with ceil(rows / 32) tiles.
+double expected_mtiles32(int64_t T, int k, int E) {
+    const double hit = E * (1.0 - std::pow(1.0 - static_cast<double>(k) / E, static_cast<double>(T)));
+    const double per = std::ceil(static_cast<double>(T) * k / E / 32.0);
+    return hit * (per > 1.0 ? per : 1.0);
+}
+
 // Row groups per block: as many as leave about one block per CU, so that
 // every CU fills its ring once and no second round of blocks runs on half the
-// chip. The m-tile count is estimated from the average rows per expert (the
-// real one is known only on the device).
-int groups_per_block(int groups, int64_t P, int E) {
-    const int64_t per_expert = (P / E + 31) / 32;
-    const int64_t mtiles = static_cast<int64_t>(E) * (per_expert > 0 ? per_expert : 1);
-    int64_t G = groups * mtiles / device_cu_count();
-    if (G < 1) G = 1;
-    if (G > groups) G = groups;
-    while (groups % G) --G;
-    return static_cast<int>(G);
+// chip. The m-tile count is estimated from the routes spread uniformly (the
+// real one is known only on the device): with fewer tokens than experts,
+// only the experts hit hold m-tiles.
+// G is the smallest divisor of the group count whose blocks fit in one round.
+int groups_per_block(int groups, int64_t T, int k, int E) {
+    const double mtiles = std::ceil(expected_mtiles32(T, k, E));
+    for (int G = 1; G < groups; ++G)
+        if (groups % G == 0 && mtiles * (groups / G) <= device_cu_count()) return G;
+    return groups;
 }
 
 hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
     constexpr int NT = 2;  // m-tiles of 32 tokens
     const int K = gemm1 ? a.D : a.H;
     const int groups = gemm1 ? a.H / 32 : a.D / 64;
-    const int G = groups_per_block(groups, a.P, a.E);
+    const int G = groups_per_block(groups, a.T, a.k, a.E);
     dim3 g(mtiles_upper(a.P, a.E, 16 * NT), groups / G);
     const bool wide = K % 256 == 0;
     if (wide) {
@@ -542,6 +848,36 @@ hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
 }
 
 }  // namespace
+
+bool fused_decode_supported(const Bf16Args& a) {
+    return a.D % 256 == 0 && a.H % 128 == 0 && !a.av.on();
+}
+
+// Slice width of the fused kernel: a block (m-tile, slice) is the unit of
+// work, and the blocks run about one per CU, so the width whose block count
+// fills whole rounds of the CUs best wins; 256 (half the atomics, and
+// 512-byte W2 row segments) unless 128 fills the rounds clearly better.
+// Measured at D=2048, H=768, E=128, k=8: 16 tokens (about 250 blocks of
+// 256) 0.164 ms with 256 against 0.18 with 128; 32 tokens (about 340 of
+// 256, 680 of 128) 0.30 against 0.27; the decode shape (256 blocks of 256)
+// 0.50 against 0.58.
+int fused_slice(const Bf16Args& a) {
+    if (a.H % 256) return 128;
+    const double mt = expected_mtiles32(a.T, a.k, a.E), cus = device_cu_count();
+    auto fill = [&](int bh) {
+        const double units = mt * (a.H / bh);
+        return units / (std::ceil(units / cus) * cus);
+    };
+    return fill(256) >= fill(128) - 0.05 ? 256 : 128;
+}
+
+hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s) {
+    const int bh = fused_slice(a);
+    const int64_t blocks = static_cast<int64_t>(mtiles_upper(a.P, a.E, 32)) * (a.H / bh);
+    if (bh == 256) fused_dma_kernel<256, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
+    else fused_dma_kernel<128, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s) { return launch_dma(a, true, s); }
 
@@ -919,7 +1255,7 @@ bool skinny_mx_supported(const MxArgs& a) {
 hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s) {
     const int R = a.w4 ? 128 : 64;
     const int groups = gemm1 ? a.H / (R / 2) : a.D / R;
-    const int G = groups_per_block(groups, a.P, a.E);
+    const int G = groups_per_block(groups, a.T, a.k, a.E);
     dim3 g(mtiles_upper(a.P, a.E, kMx4BM), groups / G);
     if (a.w4) {
         if (gemm1) mx_skinny_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G);

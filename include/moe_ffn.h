@@ -107,7 +107,8 @@ MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode);
  * the library, never freed): "dma_split_kernel", "dma_skinny_kernel",
  * "big_gemm_kernel<128>", "big_gemm_kernel<256>", "gemm1_swiglu_kernel",
  * "gemm2_weight_kernel", "mx_skinny_kernel", "mx_gemm1_kernel",
- * "mx_gemm2_kernel", "fused_bf16_kernel", "mx_fused_kernel", or "none" for
+ * "mx_gemm2_kernel", "fused_dma_kernel", "fused_bf16_kernel",
+ * "mx_fused_kernel", or "none" for
  * T = 0. NULL on an invalid problem, mode or gemm. Host only: it evaluates
  * the same dispatch rules as the launch, which depend on the shapes only
  * (the routing itself is not known before the route step), except for

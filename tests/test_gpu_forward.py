@@ -196,3 +196,18 @@ def test_side_stream_with_int64_ids():
         out = g.moe_ffn_forward(t["x"], t["w1"], t["w2"], ids64, t["topk_weights"], mode=mode, stream=side)
         side.synchronize()
         assert_close(gpu_bf16_to_f64(out), ref, what=f"side stream/{mode}")
+
+
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (2100, 256, 512, 3, 2, "zipf"),     # many 32-row m-tiles per expert, ragged last tiles
+    (96, 512, 768, 16, 4, "softmax"),   # three 256-wide slices of H, eight W2 row groups
+    (1, 256, 256, 4, 2, "uniform"),     # a single token
+    (64, 256, 256, 4, 4, "uniform"),    # k = E
+    (4096, 256, 512, 8, 2, "zipf"),     # enough m-tiles for 256-wide slices
+])
+def test_fused_decode_kernel(T, D, H, E, k, routing):
+    """The fused pass on the decode kernels' rings (32-row m-tiles, act slice in
+    LDS, split-K down projection added into the fp32 accumulator)."""
+    import grouped_gemm_amd as g
+    assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", "fused", 1) == "fused_dma_kernel"
+    _case(mi.custom(T, D, H, E, k, routing), "fused")
