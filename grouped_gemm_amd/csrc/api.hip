@@ -30,7 +30,10 @@ int check_shape(const moe_ffn_problem* p) {
     if (p->dtype != MOE_FFN_BF16 && p->dtype != MOE_FFN_MXFP8 && p->dtype != MOE_FFN_MXFP4)
         return MOE_FFN_EUNSUPPORTED;
     if (p->T < 0 || p->D < 1 || p->H < 1 || p->E < 1 || p->topk < 1) return MOE_FFN_EINVAL_SHAPE;
-    if (p->D % 128 || p->H % 128) return MOE_FFN_EINVAL_SHAPE;
+    // bf16: multiples of 64 (one 64-element K step of the generic kernels);
+    // MX: multiples of 128 (the MX kernels stage K in 128-code steps)
+    const int mult = p->dtype == MOE_FFN_BF16 ? 64 : 128;
+    if (p->D % mult || p->H % mult) return MOE_FFN_EINVAL_SHAPE;
     if (p->E > kMaxExperts || p->topk > kMaxTopk || p->topk > p->E) return MOE_FFN_EINVAL_SHAPE;
     if (static_cast<int64_t>(p->T) * p->topk > INT_MAX) return MOE_FFN_EINVAL_SHAPE;
     return MOE_FFN_OK;
@@ -300,7 +303,7 @@ size_t shared_bytes(const moe_ffn_problem* p, int32_t Hs) {
 }
 int check_shared(const moe_ffn_problem* p, int32_t Hs) {
     if (p->dtype != MOE_FFN_BF16) return MOE_FFN_EUNSUPPORTED;  // an MX shared expert is not built
-    if (Hs < 1 || Hs % 128) return MOE_FFN_EINVAL_SHAPE;
+    if (Hs < 1 || Hs % 64) return MOE_FFN_EINVAL_SHAPE;
     return MOE_FFN_OK;
 }
 }  // namespace

@@ -247,11 +247,12 @@ __global__ __launch_bounds__(kThreads) void gemm2_weight_kernel(Bf16Args a) {
 // ---------------- fused GEMM1 -> SwiGLU -> split-K GEMM2 ----------------
 // grid: (m-tile upper bound, H / BH). BM = 128, BH = 64 (GEMM1 N-tile 128),
 // down-projection N-chunks of 128 over D with K = BH.
-template <int BM, int BH>
+template <int BM, int BH, int BN2>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(Bf16Args a) {
     constexpr int BN = 2 * BH;
     using C = Tile<BM, BN>;
-    using C2 = Tile<BM, 128>;
+    using C2 = Tile<BM, BN2>;
+    static_assert(2 * BN2 * BK <= 2 * C::STAGE, "W2 chunks must fit the stage buffers");
     static_assert(BH == BK, "the act slice is exactly one K step of the down projection");
     // one LDS array: two GEMM stages, then the act tile (A operand of the
     // down projection)
@@ -307,17 +308,17 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(Bf16Args a) {
                         f32_to_bf16(silu_mul(acc[mi][j][v], acc[mi][j + C::NB / 2][v]));
                 }
     }
-    // Down projection over this H slice, 128 output columns at a time.
+    // Down projection over this H slice, BN2 output columns at a time.
     const uint16_t* w2e = a.w2 + static_cast<int64_t>(mt.expert) * a.D * a.H + h0 + c16 * 8;
-    const int NT = a.D / 128;
+    const int NT = a.D / BN2;
     u32x4_t rb[C2::B_CH];
     auto gload = [&](int nt) {
 #pragma unroll
         for (int q = 0; q < C2::B_CH; ++q)
-            rb[q] = *reinterpret_cast<const u32x4_t*>(w2e + static_cast<int64_t>(nt * 128 + r16 + 32 * q) * a.H);
+            rb[q] = *reinterpret_cast<const u32x4_t*>(w2e + static_cast<int64_t>(nt * BN2 + r16 + 32 * q) * a.H);
     };
     auto sstore = [&](int buf) {
-        uint16_t* sB = lds + buf * 128 * BK;
+        uint16_t* sB = lds + buf * BN2 * BK;
 #pragma unroll
         for (int q = 0; q < C2::B_CH; ++q) *reinterpret_cast<u32x4_t*>(sB + swz(r16 + 32 * q, c16)) = rb[q];
     };
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(Bf16Args a) {
     __syncthreads();
     for (int nt = 0; nt < NT; ++nt) {
         if (nt + 1 < NT) gload(nt + 1);
-        const uint16_t* sB = lds + (nt & 1) * 128 * BK;
+        const uint16_t* sB = lds + (nt & 1) * BN2 * BK;
         f32x16_t acc2[C2::MB][C2::NB];
 #pragma unroll
         for (int mi = 0; mi < C2::MB; ++mi)
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(Bf16Args a) {
             for (int v = 0; v < 16; ++v) {
                 const int m = wm * C2::WM + 32 * mi + acc_row(lane, v);
                 if (m < mt.rows) {
-                    float* dst = a.acc32 + static_cast<int64_t>(sTok[m]) * a.D + nt * 128 + wn * C2::WN + (lane & 31);
+                    float* dst = a.acc32 + static_cast<int64_t>(sTok[m]) * a.D + nt * BN2 + wn * C2::WN + (lane & 31);
 #pragma unroll
                     for (int nj = 0; nj < C2::NB; ++nj) unsafeAtomicAdd(dst + 32 * nj, sW[m] * acc2[mi][nj][v]);
                 }
@@ -476,6 +477,7 @@ inline int mtiles_upper(int64_t P, int E, int bm) {
 // group (one expert: a shared expert, a dense FFN) with few rows would give
 // the prefill ring fewer tiles than half the CUs, so it streams too.
 bool bf16_uses_decode_kernels(const Bf16Args& a) {
+    if (a.D % 128 || a.H % 128) return false;  // their K stages are 128 or 256 values
     const int64_t ring_tiles = (a.P / 128 + a.E) * (a.H / 128);
     return decode_kernels_fit(a.T, a.k, a.E) || (a.E == 1 && ring_tiles < device_cu_count() / 2);
 }
@@ -497,9 +499,12 @@ hipError_t launch_gemms_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
         launch_skinny_gemm2(a, s);
     } else if (big) {
         launch_big_gemm(a, false, s);
-    } else {
+    } else if (a.D % BN2 == 0) {
         dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / BN2);
         gemm2_weight_kernel<BM, BN2><<<g2, kThreads, 0, s>>>(a);
+    } else {  // D a multiple of 64 only
+        dim3 g2(mtiles_upper(a.P, a.E, BM), a.D / 64);
+        gemm2_weight_kernel<BM, 64><<<g2, kThreads, 0, s>>>(a);
     }
     record(ev, 1, s);
     return hipGetLastError();
@@ -530,7 +535,8 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
         launch_fused_decode(a, s);
     } else {
         dim3 g(mtiles_upper(a.P, a.E, BM), a.H / BH);
-        fused_bf16_kernel<BM, BH><<<g, kThreads, 0, s>>>(a);
+        if (a.D % 128 == 0) fused_bf16_kernel<BM, BH, 128><<<g, kThreads, 0, s>>>(a);
+        else fused_bf16_kernel<BM, BH, 64><<<g, kThreads, 0, s>>>(a);
     }
     record(ev, 1, s);
     f32_to_bf16_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(a.acc32),

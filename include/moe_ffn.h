@@ -58,8 +58,9 @@ enum { MOE_FFN_AUTO = 0, MOE_FFN_FUSED = 1, MOE_FFN_SPLIT = 2 };
 
 enum {
     MOE_FFN_OK = 0,
-    MOE_FFN_EINVAL_SHAPE = -1,  /* T < 0, D/H/E/topk < 1, D or H not a multiple of 128,
-                                   topk > E or > 64, E > 8192, or sizes that overflow */
+    MOE_FFN_EINVAL_SHAPE = -1,  /* T < 0, D/H/E/topk < 1, D or H not a multiple of 64
+                                   (bf16) or of 128 (MXFP8, MXFP4), topk > E or > 64,
+                                   E > 8192, or sizes that overflow */
     MOE_FFN_EINVAL_PTR = -2,    /* a required pointer is NULL or not 16-byte aligned */
     MOE_FFN_EUNSUPPORTED = -3,  /* dtype or mode unknown, or the pair not built */
     MOE_FFN_EWORKSPACE = -4,    /* workspace NULL, misaligned (256 B) or too small */
@@ -211,7 +212,7 @@ MOE_FFN_API int moe_ffn_forward_logits(const moe_ffn_problem* p, const void* x, 
  *     out[t] = sum_j w[t,j] * y(t, ids[t,j]) + W2s (silu(W1s_gate x_t) * W1s_up x_t)
  *   shared_w1 : bf16 [2Hs, D] (gate rows, then up rows), 16-byte aligned.
  *   shared_w2 : bf16 [D, Hs].
- *   Hs        : the shared expert's intermediate size, a multiple of 128.
+ *   Hs        : the shared expert's intermediate size, a multiple of 64.
  * The shared expert runs first, as a grouped GEMM of one group of all T
  * tokens; the combine (split) or the accumulator conversion (fused) adds
  * its rows. bf16 only (MXFP8 returns MOE_FFN_EUNSUPPORTED). The workspace

@@ -25,8 +25,10 @@ def test_library_exports_every_header_function():
     ((64, 256, 512, 8, 2), g.MOE_FFN_OK),
     ((0, 256, 512, 8, 2), g.MOE_FFN_OK),
     ((-1, 256, 512, 8, 2), g.MOE_FFN_EINVAL_SHAPE),
-    ((64, 200, 512, 8, 2), g.MOE_FFN_EINVAL_SHAPE),     # D not a multiple of 128
-    ((64, 256, 500, 8, 2), g.MOE_FFN_EINVAL_SHAPE),     # H not a multiple of 128
+    ((64, 200, 512, 8, 2), g.MOE_FFN_EINVAL_SHAPE),     # D not a multiple of 64
+    ((64, 256, 500, 8, 2), g.MOE_FFN_EINVAL_SHAPE),     # H not a multiple of 64
+    ((64, 192, 320, 8, 2), g.MOE_FFN_OK),               # bf16: multiples of 64
+    ((64, 64, 64, 8, 2), g.MOE_FFN_OK),
     ((64, 256, 512, 8, 9), g.MOE_FFN_EINVAL_SHAPE),     # k > E
     ((64, 256, 512, 0, 1), g.MOE_FFN_EINVAL_SHAPE),
     ((64, 256, 512, 8, 0), g.MOE_FFN_EINVAL_SHAPE),
@@ -253,3 +255,20 @@ def test_noalloc_limit_and_error_code():
     assert "scratch" in g.moe_ffn_strerror(g.MOE_FFN_ESCRATCH)
     # the decode workload fits
     assert g.moe_ffn_workspace_bytes(64, 6144, 2048, 32, 8, "bf16", "split") < g.MOE_FFN_NOALLOC_SCRATCH_BYTES
+
+
+def test_mx_shapes_are_multiples_of_128():
+    # the MX kernels stage K in 128-code steps: bf16 takes multiples of 64, MX of 128
+    for dt in ("mxfp8", "mxfp4"):
+        assert g.moe_ffn_validate(64, 192, 256, 8, 2, dtype=dt, mode="split") == g.MOE_FFN_EINVAL_SHAPE
+        assert g.moe_ffn_validate(64, 256, 320, 8, 2, dtype=dt, mode="split") == g.MOE_FFN_EINVAL_SHAPE
+        assert g.moe_ffn_validate(64, 384, 640, 8, 2, dtype=dt, mode="split") == g.MOE_FFN_OK
+
+
+def test_64_multiples_take_the_generic_kernels():
+    # D or H a multiple of 64 but not 128: neither the decode nor the prefill ring kernels
+    assert g.moe_ffn_gemm_kernel(64, 192, 320, 8, 2, "bf16", "split", 1) == "gemm1_swiglu_kernel"
+    assert g.moe_ffn_gemm_kernel(64, 192, 320, 8, 2, "bf16", "split", 2) == "gemm2_weight_kernel"
+    assert g.moe_ffn_gemm_kernel(64, 192, 320, 8, 2, "bf16", "fused", 1) == "fused_bf16_kernel"
+    assert g.moe_ffn_gemm_kernel(4096, 320, 192, 8, 2, "bf16", "split", 1) == "gemm1_swiglu_kernel"
+    assert g.moe_ffn_workspace_bytes(64, 192, 320, 8, 2, "bf16", "split") > 0

@@ -50,6 +50,7 @@ def _case(cfg, kind, limit, use_alpha, wba, tokens=None):
     (300, 384, 256, 6, 3, "zipf"),        # generic kernels (D = 384)
     (500, 512, 384, 8, 2, "zipf"),        # prefill ring, 128-row tiles
     (2100, 256, 512, 3, 2, "zipf"),       # prefill ring, 256-row tiles
+    (97, 192, 320, 6, 3, "softmax"),      # D and H multiples of 64 only
 ])
 def test_variant_matches_oracle(T, D, H, E, k, routing, variant):
     _case(mi.custom(T, D, H, E, k, routing), *variant)

@@ -54,6 +54,9 @@ def test_tiny_config(mode):
     (260, 256, 128, 1, 1, "softmax"),       # E = 1, k = 1: a dense SwiGLU FFN
     (500, 512, 384, 8, 2, "zipf"),          # prefill tiles of 128 rows, ragged, skewed
     (2100, 256, 384, 3, 2, "zipf"),         # prefill tiles of 256 rows, ragged, skewed
+    (97, 192, 320, 6, 3, "softmax"),        # D and H multiples of 64 only
+    (640, 320, 192, 5, 2, "zipf"),          # the same, several m-tiles per expert
+    (7, 64, 64, 4, 2, "uniform"),           # the smallest dims
 ])
 def test_ragged_shapes(mode, T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing), mode)

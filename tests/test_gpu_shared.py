@@ -41,6 +41,7 @@ def _case(cfg, Hs, mode, tokens=None):
     (300, 384, 256, 6, 3, 256),     # D not a multiple of 256: the generic GEMM kernels
     (500, 512, 384, 8, 2, 128),     # prefill ring, 128-row tiles
     (2100, 256, 256, 3, 2, 640),    # prefill ring, 256-row tiles; Hs > H
+    (90, 192, 320, 4, 2, 192),      # D, H and Hs multiples of 64 only (generic kernels)
 ])
 def test_shared_expert_matches_oracle(mode, T, D, H, E, k, Hs):
     _case(mi.custom(T, D, H, E, k, "zipf"), Hs, mode)
