@@ -214,3 +214,23 @@ def test_fused_decode_kernel(T, D, H, E, k, routing):
     import grouped_gemm_amd as g
     assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", "fused", 1) == "fused_dma_kernel"
     _case(mi.custom(T, D, H, E, k, routing), "fused")
+
+
+def test_skewed_decode_batch():
+    """A decode-shaped batch whose routing is skewed: expert 5 takes 56 or more of
+    the 64 tokens, so it holds two 32-row m-tiles and the other experts few rows.
+    The dispatch sees the shape only, so the decode kernels run, with the
+    extra m-tiles of the hot expert."""
+    import grouped_gemm_amd as g
+    cfg = mi.custom(64, 512, 512, 16, 4, "uniform")
+    assert g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, "bf16", "split", 1) == "dma_split_kernel"
+    assert g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, "bf16", "split", 2) == "dma_split_kernel"
+    d = mi.make_bf16(cfg, 8)
+    ids = d["topk_ids"]
+    hot = np.arange(64) < 56
+    ids[hot, 0] = 5
+    ids[hot, 1:] = np.where(ids[hot, 1:] == 5, 6, ids[hot, 1:])   # expert 5 once per hot token
+    assert mi.expert_histogram(ids, cfg.E)[5] >= 56
+    for mode in MODES:
+        rel, cos = assert_close(_run(d, mode), _ref(d), what=f"skewed decode/{mode}")
+        print(f"  {mode}: max err / max|ref| = {rel:.3e}, cosine = {cos:.7f}", flush=True)
