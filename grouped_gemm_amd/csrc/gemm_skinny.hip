@@ -258,7 +258,19 @@ __device__ __forceinline__ void dma_group_end(const Bf16Args& a, f32x4_t (&acc)[
     }
 }
 
-// grid: (m-tiles of 16*NT rows, row groups / G). A block walks G consecutive
+// A decode kernel's block index: the row-group chunks of one m-tile are
+// consecutive (1-D grid, chunk fastest), so the blocks of the m-tiles that
+// exist, which come first, are dispatched before the ones past the m-tile
+// count (the grid is sized for the most m-tiles the routes could produce;
+// those blocks exit at once).
+struct BlockPos {
+    int mtile, chunk;
+};
+__device__ __forceinline__ BlockPos block_pos(int nchunks) {
+    return BlockPos{static_cast<int>(blockIdx.x) / nchunks, static_cast<int>(blockIdx.x) % nchunks};
+}
+
+// grid: m-tiles of 16*NT rows x (row groups / G) chunks, 1-D (block_pos). A block walks G consecutive
 // 64-row weight groups (GEMM1: 32 act columns = gate rows h..h+31 and up
 // rows H+h..H+h+31; GEMM2: 64 output features) through one continuous ring,
 // so the ring's fill and drain are paid once per block. The four waves split
@@ -273,10 +285,11 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
     static_assert(T::NS % 4 == 0, "k-steps must split evenly over the four waves");
     __shared__ __attribute__((aligned(16))) uint8_t ring[S * T::STAGE];
     MTile mt;
-    if (!find_mtile<T::BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const BlockPos bp = block_pos((GEMM1 ? a.H / 32 : a.D / 64) / G);
+    if (!find_mtile<T::BM>(a.rv, a.E, bp.mtile, mt)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = GEMM1 ? a.D : a.H;
-    const int grp0 = blockIdx.y * G;  // first row group of this block
+    const int grp0 = bp.chunk * G;  // first row group of this block
     const char* wsrc[T::W_INS];
     const char* tsrc[T::T_INS];
     const int pc = lane % T::CPR;
@@ -314,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
     // the DRAM credit stalls of GEMM1, and the rotation takes GEMM2 from 161
     // to 152 us on the decode workload. (GEMM1's 12 KB rows already spread
     // over the channels; rotating them measured 2% slower.)
-    const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;
+    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;
     f32x4_t acc[NB][NT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -415,12 +428,13 @@ __global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) 
     __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES];
     uint8_t* const tring = lds + SW * T::W_BYTES;
     MTile mt;
-    if (!find_mtile<T::BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const BlockPos bp = block_pos((GEMM1 ? a.H / 32 : a.D / 64) / G);
+    if (!find_mtile<T::BM>(a.rv, a.E, bp.mtile, mt)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool wmover = wave < 2;
     const int mw = wave & 1;  // this wave's half of what its pair moves
     const int K = GEMM1 ? a.D : a.H;
-    const int grp0 = blockIdx.y * G;
+    const int grp0 = bp.chunk * G;
     const int pc = lane % T::CPR;
     const char* src[NI];
     if (wmover) {
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) 
     const int64_t group_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * K * 2;
     const int r = lane & 15, kg = lane >> 4;
     const int KIT = K / KC, NIT = G * KIT;
-    const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;  // as in dma_skinny_kernel
+    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;  // as in dma_skinny_kernel
     f32x4_t acc[NB][NT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -835,7 +849,7 @@ hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
     const int K = gemm1 ? a.D : a.H;
     const int groups = gemm1 ? a.H / 32 : a.D / 64;
     const int G = groups_per_block(groups, a.T, a.k, a.E);
-    dim3 g(mtiles_upper(a.P, a.E, 16 * NT), groups / G);
+    const unsigned g = static_cast<unsigned>(mtiles_upper(a.P, a.E, 16 * NT)) * (groups / G);
     const bool wide = K % 256 == 0;
     if (wide) {
         if (gemm1) dma_split_kernel<256, 4, true><<<g, kThreads, 0, s>>>(a, G);
@@ -1031,11 +1045,12 @@ __global__ __launch_bounds__(kThreads) void mx_skinny_kernel(MxArgs a, int G) {
     constexpr int NB = C::NB, HALF = R / 2;
     __shared__ __attribute__((aligned(16))) uint8_t ring[C::S * C::STAGE];
     MTile mt;
-    if (!find_mtile<kMx4BM>(a.rv, a.E, blockIdx.x, mt)) return;
+    const BlockPos bp = block_pos((GEMM1 ? a.H / HALF : a.D / R) / G);
+    if (!find_mtile<kMx4BM>(a.rv, a.E, bp.mtile, mt)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = GEMM1 ? a.D : a.H;
     const int KB = K / 32;  // scale bytes per row
-    const int grp0 = blockIdx.y * G;
+    const int grp0 = bp.chunk * G;
     const uint8_t* wbase = GEMM1 ? a.w1 : a.w2;
     const uint8_t* wsbase = GEMM1 ? a.w1s : a.w2s;
     auto wrow = [&](int row) -> int64_t {  // expert weight row of block row `row` in group grp0
@@ -1076,7 +1091,7 @@ __global__ __launch_bounds__(kThreads) void mx_skinny_kernel(MxArgs a, int G) {
     const int64_t sgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * KB;
     const int KIT = K / kMx4KC, NIT = G * KIT;
     // GEMM2 rotates the order of its groups per block (see dma_skinny_kernel)
-    const int rot = GEMM1 ? 0 : (blockIdx.x + blockIdx.y) % G;
+    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;
     const bool scale_wave = wave <= C::SWAVES;  // moves one scale DMA per stage
 
     const int lr = lane & 31, g = lane >> 5;
@@ -1256,7 +1271,7 @@ hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s) {
     const int R = a.w4 ? 128 : 64;
     const int groups = gemm1 ? a.H / (R / 2) : a.D / R;
     const int G = groups_per_block(groups, a.T, a.k, a.E);
-    dim3 g(mtiles_upper(a.P, a.E, kMx4BM), groups / G);
+    const unsigned g = static_cast<unsigned>(mtiles_upper(a.P, a.E, kMx4BM)) * (groups / G);
     if (a.w4) {
         if (gemm1) mx_skinny_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G);
         else mx_skinny_kernel<128, false, true><<<g, kThreads, 0, s>>>(a, G);
