@@ -39,24 +39,18 @@ int check_shape(const moe_ffn_problem* p) {
     return MOE_FFN_OK;
 }
 
-// AUTO picks the fused pipeline only where it measured faster on MI355X:
-// expert weights small enough to stay cache-resident (the 8-expert,
-// D=256, H=512 case: 6 MB) and few routed pairs. With weights that stream
-// from HBM the split pipeline won at every measured token count (16 to
-// 16384 tokens at D=2048, H=768, 128 experts; and the 64-token decode
-// shape), because the fused kernel's split-K partial rows cost more
-// atomic traffic than writing the activation once.
-constexpr int64_t kFusedMaxPairs = 4096;
-constexpr int64_t kFusedMaxWeightBytes = int64_t(16) << 20;
-
+// AUTO resolves to the split pipeline: it measured faster than the fused one
+// at every token count tried on MI355X (4 to 4096 tokens at D=2048, H=768,
+// 128 experts; 8 to 128 at the 6144/2048/32-expert decode dims; 16 to 4096
+// at D=256, H=512, 8 experts, where the two are within 5% up to 256 tokens).
+// The fused pipeline's split-K partial rows cost fp32 atomic adds into the
+// accumulator (P * H/slice * D of them), and MI355X's L2 atomics run at
+// about 330 G adds/s, while the split pipeline's decode kernels already
+// stream the weights at close to the HBM rate.
 int resolve(const moe_ffn_problem* p, int mode) {
     if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
-    if (p->dtype == MOE_FFN_MXFP8) return mode == MOE_FFN_FUSED ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
     if (p->dtype == MOE_FFN_MXFP4) return mode == MOE_FFN_FUSED ? MOE_FFN_EUNSUPPORTED : MOE_FFN_SPLIT;
-    if (mode != MOE_FFN_AUTO) return mode;
-    const int64_t weight_bytes = int64_t(p->E) * 3 * p->H * p->D * 2;
-    const bool small = static_cast<int64_t>(p->T) * p->topk <= kFusedMaxPairs && weight_bytes <= kFusedMaxWeightBytes;
-    return small ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
+    return mode == MOE_FFN_FUSED ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
 }
 
 struct RoutePlan {

@@ -58,8 +58,8 @@ def test_validate_dtype_and_mode():
 def test_resolve_mode():
     assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="split") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="fused") == g.MOE_FFN_FUSED
-    # measured crossover: fused only for cache-resident weights and small batches
-    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_FUSED
+    # measured crossover: the split pipeline is faster at every measured size
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(64, 6144, 2048, 32, 8, mode="auto") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(16, 2048, 768, 128, 8, mode="auto") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(131072, 2048, 768, 128, 8, mode="auto") == g.MOE_FFN_SPLIT
