@@ -171,7 +171,7 @@ MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, 
         if (m == MOE_FFN_FUSED) return moe::fused_decode_supported(a) ? "fused_dma_kernel" : "fused_bf16_kernel";
         a.mtiles = &table_stand_in;
         if (moe::bf16_uses_decode_kernels(a))
-            return (g1 ? p->D : p->H) % 256 == 0 ? "dma_split_kernel" : "dma_skinny_kernel";
+            return moe::decode_kernel_name(a, g1);
         if (moe::big_gemm_supported(a))
             return moe::big_gemm_tile_rows(a) == 256 ? "big_gemm_kernel<256>" : "big_gemm_kernel<128>";
         return g1 ? "gemm1_swiglu_kernel" : "gemm2_weight_kernel";

@@ -167,6 +167,8 @@ hipError_t launch_identity_route(int64_t T, int32_t* counts, int32_t* offsets, i
 bool bf16_uses_decode_kernels(const Bf16Args& a);
 // Token rows per tile of the bf16 prefill GEMMs (128 or 256).
 int big_gemm_tile_rows(const Bf16Args& a);
+// Name of the decode kernel launch_skinny_gemm1 (gemm1) / 2 runs for `a`.
+const char* decode_kernel_name(const Bf16Args& a, bool gemm1);
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s);
 hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s);
 // Prefill-shaped GEMM1 / GEMM2 (256-feature tiles, 128 or 256 token rows).

@@ -527,6 +527,231 @@ __global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) 
     }
 }
 
+// Eight 16-byte LDS reads and a wait for them, in one asm statement (as
+// lds_read6, so that no vmcnt wait for the DMAs in flight comes before them).
+__device__ __forceinline__ void lds_read8(bf16x8_t (&v)[8], const uint32_t (&p)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+        : "memory");
+}
+
+// Most row groups a k-major block keeps accumulators for at once.
+constexpr int kKmajorGroups = 12;
+
+// A k-major block's G row groups cut into nsg super-groups of `base` or
+// base + 1 groups (the first `rem` get one more); each super-group walks
+// its K in 256-value chunks, and each chunk its groups: stage s is group gi
+// of super-group sg at chunk kc.
+struct KmajorPlan {
+    int base, rem, kit;
+    __device__ int first(int sg) const { return sg * base + (sg < rem ? sg : rem); }
+    __device__ int size(int sg) const { return base + (sg < rem ? 1 : 0); }
+    __device__ void locate(int s, int& sg, int& kc, int& gi) const {
+        const int big = rem * (base + 1) * kit;
+        int r;
+        if (s < big) {
+            sg = s / ((base + 1) * kit);
+            r = s - sg * (base + 1) * kit;
+        } else {
+            const int q = (s - big) / (base * kit);
+            sg = rem + q;
+            r = s - big - q * base * kit;
+        }
+        const int gs = size(sg);
+        kc = r / gs;
+        gi = r - kc * gs;
+    }
+};
+
+// The decode GEMMs, k-major: a block (m-tile, G row groups) walks K in
+// 256-value chunks and, within a chunk, up to kKmajorGroups groups, so each
+// chunk of the m-tile's 32 token rows (16 KB) is fetched once per chunk
+// instead of once per group (with the token rows fetched per group, their
+// L2 traffic was half the weights' and held HBM streaming about 10% below
+// what the weights alone reach). A stage is one group's 64 weight rows x
+// 512 bytes (32 KB, a 4-slot ring); the token chunk rides with the first
+// stage of its chunk into a 2-slot token ring (the next chunk's tokens
+// overwrite a slot only after two stages, so every super-group has at
+// least two groups). Each wave owns 16 of a group's 64 rows for every
+// k-step (no split-K, no cross-wave reduction) and keeps its fragments of
+// the token chunk in registers across the chunk's groups. GEMM1's rows are
+// laid out in the slot so that each 16-row block holds 8 gate rows and the
+// 8 up rows of the same act columns: an MFMA lane holding gate rows finds
+// the matching up rows 32 lanes away.
+template <bool GEMM1>
+__global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a, int G, int nsg) {
+    using T = DmaTile<2, 256, 2>;  // 512-byte row segments: 32 KB weight stages, 16 KB token chunks
+    constexpr int SW = 4, NT = 2, NS = T::NS, GSM = kKmajorGroups;
+    constexpr int W_INS = T::W_INS, T_INS = T::T_INS;  // per wave per stage / per chunk
+    static_assert(NS == 8 && T::CPR == 32 && T::RPI * T::RB == 1024, "512-byte segments, 8 k-steps per stage");
+    static_assert(SW * T::W_BYTES + 2 * T::T_BYTES <= 160 * 1024, "rings must fit the LDS of a CU");
+    static_assert((SW - 2) * W_INS < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES];
+    uint8_t* const tring = lds + SW * T::W_BYTES;
+    MTile mt;
+    const BlockPos bp = block_pos((GEMM1 ? a.H / 32 : a.D / 64) / G);
+    if (!find_mtile<T::BM>(a.rv, a.E, bp.mtile, mt)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, kg = lane >> 4;
+    const int K = GEMM1 ? a.D : a.H;
+    const int grp0 = bp.chunk * G;
+    const int pc = lane % T::CPR;
+    const char* wsrc[W_INS];
+#pragma unroll
+    for (int j = 0; j < W_INS; ++j) {
+        const int row = (wave * W_INS + j) * T::RPI + lane / T::CPR;  // slot row 0..63
+        const int c = pc ^ (row & (T::CPR - 1));
+        int64_t grow;
+        if (GEMM1) {
+            const int jj = row & 15, h = grp0 * 32 + 8 * (row >> 4) + (jj & 7);
+            grow = static_cast<int64_t>(mt.expert) * 2 * a.H + (jj < 8 ? h : a.H + h);
+        } else {
+            grow = static_cast<int64_t>(mt.expert) * a.D + grp0 * 64 + row;
+        }
+        wsrc[j] = reinterpret_cast<const char*>(GEMM1 ? a.w1 : a.w2) + grow * K * 2 + c * 16;
+    }
+    const char* tsrc[T_INS];
+#pragma unroll
+    for (int j = 0; j < T_INS; ++j) {
+        const int m = (wave * T_INS + j) * T::RPI + lane / T::CPR;  // token row 0..31
+        const int c = pc ^ (m & (T::CPR - 1));
+        const int mm = m < mt.rows ? m : 0;
+        const int64_t grow = GEMM1 ? clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k : mt.row0 + mm;
+        tsrc[j] = reinterpret_cast<const char*>(GEMM1 ? a.x : a.act) + grow * K * 2 + c * 16;
+    }
+    const int64_t group_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * K * 2;
+    const int KIT = K / 256, NIT = G * KIT;
+    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;  // as in dma_skinny_kernel
+    // The K chunks are walked from chunk kc0 on, wrapping: the blocks run in
+    // near lockstep, and if every block read the same 512-byte column of its
+    // rows at once, the reads would crowd a few HBM channels.
+    const int kc0 = static_cast<int>(blockIdx.x) % KIT;
+    const KmajorPlan pl{G / nsg, G % nsg, KIT};
+    // epilogue values of tokens r and 16 + r (every wave stores both tiles)
+    int ep[NT];
+    float esc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int m = 16 * t + r;
+        ep[t] = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
+        if (GEMM1)
+            esc[t] = a.av.on() ? (a.av.alpha ? a.av.alpha[mt.expert] : 1.0f) * (a.av.wba ? a.wts[ep[t]] : 1.0f) : 1.0f;
+        else
+            esc[t] = a.av.wba ? 1.0f : a.wts[ep[t]];
+    }
+    asm volatile("" : "+v"(ep[0]), "+v"(ep[1]), "+v"(esc[0]), "+v"(esc[1]));
+    auto issue = [&](int st) {
+        int sg, kc, gi;
+        pl.locate(st, sg, kc, gi);
+        const int g = (pl.first(sg) + gi + rot) % G;
+        const int kr = (kc + kc0) % KIT;
+        const int64_t off = static_cast<int64_t>(kr) * T::RB + g * group_stride;
+        uint8_t* slot = lds + (st % SW) * T::W_BYTES;
+#pragma unroll
+        for (int j = 0; j < W_INS; ++j)
+            __builtin_amdgcn_global_load_lds(wsrc[j] + off, (lds_ptr_t)(slot + (wave * W_INS + j) * 1024), 16, 0,
+                                             kWeightDmaAux);
+        if (gi == 0) {
+            uint8_t* ts = tring + ((sg * KIT + kc) & 1) * T::T_BYTES;
+#pragma unroll
+            for (int j = 0; j < T_INS; ++j)
+                __builtin_amdgcn_global_load_lds(tsrc[j] + static_cast<int64_t>(kr) * T::RB,
+                                                 (lds_ptr_t)(ts + (wave * T_INS + j) * 1024), 16, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < SW - 1; ++j)
+        if (j < NIT) issue(j);
+    int s = 0;
+    for (int sg = 0; sg < nsg; ++sg) {
+        const int gs = pl.size(sg), gfirst = pl.first(sg);
+        f32x4_t acc[GSM][NT];
+#pragma unroll
+        for (int gi = 0; gi < GSM; ++gi)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[gi][t] = f32x4_t{};
+        for (int kc = 0; kc < KIT; ++kc) {
+            bf16x8_t tk0[NS], tk1[NS];
+#pragma unroll
+            for (int gi = 0; gi < GSM; ++gi) {
+                if (gi >= gs) continue;
+                // the stage's DMAs (and, at gi = 0, the chunk's token DMAs issued with them) are this
+                // wave's oldest; later stages hold at least W_INS each
+                if (s + SW - 2 < NIT) wait_vm<(SW - 2) * W_INS>();
+                else wait_vm<0>();
+                ring_barrier();
+                if (s + SW - 1 < NIT) issue(s + SW - 1);
+                if (gi == 0) {
+                    const uint8_t* ts = tring + ((sg * KIT + kc) & 1) * T::T_BYTES;
+                    uint32_t p0[NS], p1[NS];
+#pragma unroll
+                    for (int ks = 0; ks < NS; ++ks) {
+                        const int c = 4 * ks + kg;
+                        p0[ks] = lds_addr(ts + r * T::RB + ((c ^ r) << 4));
+                        p1[ks] = lds_addr(ts + (16 + r) * T::RB + ((c ^ (16 + r)) << 4));
+                    }
+                    lds_read8(tk0, p0);
+                    lds_read8(tk1, p1);
+                }
+                const uint8_t* slot = lds + (s % SW) * T::W_BYTES;
+                const int row = 16 * wave + r;
+                uint32_t pw[NS];
+#pragma unroll
+                for (int ks = 0; ks < NS; ++ks) pw[ks] = lds_addr(slot + row * T::RB + (((4 * ks + kg) ^ (row & 31)) << 4));
+                bf16x8_t w[NS];
+                lds_read8(w, pw);
+#pragma unroll
+                for (int ks = 0; ks < NS; ++ks) {
+                    acc[gi][0] = mfma16(w[ks], tk0[ks], acc[gi][0]);
+                    acc[gi][1] = mfma16(w[ks], tk1[ks], acc[gi][1]);
+                }
+                ++s;
+            }
+        }
+        // epilogue (acc[gi][t][v]: slot row 16 * wave + 4kg + v, token 16t + r)
+#pragma unroll
+        for (int gi = 0; gi < GSM; ++gi) {
+            if (gi >= gs) continue;
+            const int g = grp0 + (gfirst + gi + rot) % G;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int m = 16 * t + r;
+                if (GEMM1) {
+                    float up[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) up[q] = __shfl_xor(acc[gi][t][q], 32);
+                    if (kg >= 2 || m >= mt.rows) continue;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float gt = acc[gi][t][q];
+                        v[q] = a.av.on() ? act_variant(gt, up[q], esc[t], a.av.kind, a.av.limit)
+                                         : gt / (1.0f + __expf(-gt)) * up[q];
+                    }
+                    uint16_t* dst = a.act + static_cast<int64_t>(mt.row0 + m) * a.H + g * 32 + 8 * wave + 4 * kg;
+                    *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                } else {
+                    if (m >= mt.rows) continue;
+                    const f32x4_t& cc = acc[gi][t];
+                    uint16_t* dst = a.ypair + static_cast<int64_t>(ep[t]) * a.D + g * 64 + 16 * wave + 4 * kg;
+                    *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(cc[0] * esc[t], cc[1] * esc[t]),
+                                                           pack_bf16x2(cc[2] * esc[t], cc[3] * esc[t])};
+                }
+            }
+        }
+    }
+}
+
 // ---------------- fused pass for few rows per expert ----------------
 // The fused pipeline ("Prime Flash MoE", section 2 "Trick 2": the down
 // projection split over slices of the intermediate dimension, each slice's
@@ -844,14 +1069,27 @@ int groups_per_block(int groups, int64_t T, int k, int E) {
     return groups;
 }
 
+// Which decode kernel a GEMM runs: 0 dma_kmajor_kernel (K a multiple of
+// 256, at least 2 row groups per block), 1 dma_split_kernel (K a multiple
+// of 256, one group per block), 2 dma_skinny_kernel (128-value stages).
+int decode_kernel(const Bf16Args& a, bool gemm1, int G) {
+    if ((gemm1 ? a.D : a.H) % 256) return 2;
+    return G >= 2 ? 0 : 1;
+}
+
 hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
     constexpr int NT = 2;  // m-tiles of 32 tokens
-    const int K = gemm1 ? a.D : a.H;
     const int groups = gemm1 ? a.H / 32 : a.D / 64;
     const int G = groups_per_block(groups, a.T, a.k, a.E);
     const unsigned g = static_cast<unsigned>(mtiles_upper(a.P, a.E, 16 * NT)) * (groups / G);
-    const bool wide = K % 256 == 0;
-    if (wide) {
+    const int kind = decode_kernel(a, gemm1, G);
+    if (kind == 0) {
+        const int nsg = (G + kKmajorGroups - 1) / kKmajorGroups;
+        if (gemm1) dma_kmajor_kernel<true><<<g, kThreads, 0, s>>>(a, G, nsg);
+        else dma_kmajor_kernel<false><<<g, kThreads, 0, s>>>(a, G, nsg);
+        return hipGetLastError();
+    }
+    if (kind == 1) {
         if (gemm1) dma_split_kernel<256, 4, true><<<g, kThreads, 0, s>>>(a, G);
         else dma_split_kernel<256, 4, false><<<g, kThreads, 0, s>>>(a, G);
         return hipGetLastError();
@@ -891,6 +1129,12 @@ hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s) {
     if (bh == 256) fused_dma_kernel<256, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
     else fused_dma_kernel<128, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
     return hipGetLastError();
+}
+
+const char* decode_kernel_name(const Bf16Args& a, bool gemm1) {
+    const int groups = gemm1 ? a.H / 32 : a.D / 64;
+    static const char* const names[] = {"dma_kmajor_kernel", "dma_split_kernel", "dma_skinny_kernel"};
+    return names[decode_kernel(a, gemm1, groups_per_block(groups, a.T, a.k, a.E))];
 }
 
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s) { return launch_dma(a, true, s); }

@@ -19,15 +19,15 @@ def _kernel(T, D, H, E, k, dtype="bf16", mode="split", gemm=1):
 def test_decode_rule_matches_binomial_tail(T, k, E):
     p = k / E
     want = T * p <= 32 and E * binom.sf(32, T, p) < 0.5
-    got = _kernel(T, 2048, 1024, E, k) == "dma_split_kernel"
+    got = _kernel(T, 2048, 1024, E, k) in ("dma_kmajor_kernel", "dma_split_kernel")
     assert got == want
     mx = _kernel(T, 2048, 1024, E, k, dtype="mxfp8") == "mx_skinny_kernel"
     assert mx == want
 
 
 def test_workload_paths():
-    assert _kernel(64, 6144, 2048, 32, 8) == "dma_split_kernel"              # decode
-    assert _kernel(64, 6144, 2048, 32, 8, gemm=2) == "dma_split_kernel"
+    assert _kernel(64, 6144, 2048, 32, 8) == "dma_kmajor_kernel"             # decode: 8 row groups per block
+    assert _kernel(64, 6144, 2048, 32, 8, gemm=2) == "dma_kmajor_kernel"     # 12 row groups per block
     assert _kernel(64, 384, 2048, 32, 8) == "dma_skinny_kernel"             # K not a multiple of 256
     assert _kernel(4096, 2048, 768, 128, 8) == "big_gemm_kernel<256>"       # mid prefill: 256 rows/expert
     assert _kernel(1024, 2048, 768, 128, 8) == "big_gemm_kernel<128>"       # 64 rows/expert
@@ -47,7 +47,8 @@ def test_workload_paths():
     # ring would get fewer tiles than half of the 256 compute units
     assert _kernel(260, 256, 128, 1, 1) == "dma_split_kernel"              # 3 ring tiles
     assert _kernel(260, 256, 128, 1, 1, gemm=2) == "dma_skinny_kernel"     # K = H = 128
-    assert _kernel(2048, 256, 512, 1, 1) == "dma_split_kernel"             # (16 + 1) x 4 = 68 ring tiles
+    assert _kernel(2048, 256, 512, 1, 1) == "dma_kmajor_kernel"            # (16 + 1) x 4 = 68 ring tiles
+    assert _kernel(2048, 256, 512, 1, 1, gemm=2) == "dma_split_kernel"     # one row group per block
     assert _kernel(4096, 256, 1024, 1, 1) == "big_gemm_kernel<256>"        # (32 + 1) x 8 = 264 ring tiles
     assert _kernel(0, 256, 512, 8, 2) == "none"
     assert _kernel(64, 256, 512, 8, 2, gemm=3) is None

@@ -47,6 +47,7 @@ def _case(cfg, kind, limit, use_alpha, wba, tokens=None):
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("T,D,H,E,k,routing", [
     (64, 256, 512, 8, 2, "softmax"),      # skinny kernels
+    (40, 2048, 768, 128, 8, "zipf"),      # k-major decode kernels (gate/up rows interleaved)
     (300, 384, 256, 6, 3, "zipf"),        # generic kernels (D = 384)
     (500, 512, 384, 8, 2, "zipf"),        # prefill ring, 128-row tiles
     (2100, 256, 512, 3, 2, "zipf"),       # prefill ring, 256-row tiles

@@ -170,6 +170,7 @@ def _duplicate_ids(ids):
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("T,D,H,E,k,kernel", [
     (32, 512, 512, 8, 3, "dma_split_kernel"),       # decode kernels
+    (40, 2048, 768, 128, 8, "dma_kmajor_kernel"),   # decode kernels, k-major
     (500, 512, 384, 8, 2, "big_gemm_kernel<128>"),  # prefill ring, 128-row tiles
     (2100, 256, 384, 3, 2, "big_gemm_kernel<256>"), # prefill ring, 256-row tiles
     (300, 384, 256, 6, 3, "gemm1_swiglu_kernel"),   # generic kernels
@@ -214,6 +215,26 @@ def test_fused_decode_kernel(T, D, H, E, k, routing):
     import grouped_gemm_amd as g
     assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", "fused", 1) == "fused_dma_kernel"
     _case(mi.custom(T, D, H, E, k, routing), "fused")
+
+
+@pytest.mark.parametrize("T,D,H,E,k,routing,gemms", [
+    (64, 1664, 512, 32, 8, "softmax", (2,)),     # GEMM2: 13 row groups per block, super-groups of 7 and 6
+    (64, 512, 1664, 32, 8, "uniform", (1,)),     # GEMM1: the same plan on gate/up rows
+    (64, 3200, 256, 64, 8, "uniform", (2,)),     # GEMM2: 25 groups (9 + 8 + 8), one K chunk per group
+    (2048, 256, 512, 1, 1, "softmax", (1,)),     # GEMM1: 64 m-tiles of one expert, 4 groups per block
+    (1024, 1024, 256, 1, 1, "softmax", (2,)),    # GEMM2: 32 m-tiles of one expert, rotated group order
+    (40, 2048, 768, 128, 8, "zipf", (1, 2)),     # both GEMMs, skewed: hot experts hold several m-tiles
+    (16, 2048, 768, 128, 8, "uniform", (1, 2)),  # both GEMMs, 128 tokens' routes over 128 experts
+])
+def test_kmajor_decode_kernel(T, D, H, E, k, routing, gemms):
+    """The k-major decode GEMMs (token chunk fetched once per K chunk and
+    reused across a block's row groups; rows split over the waves; GEMM1's
+    gate and up rows interleaved per 16-row block) through every super-group
+    plan: minimum size, uneven sizes, several m-tiles per expert."""
+    import grouped_gemm_amd as g
+    for gemm in gemms:
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", "split", gemm) == "dma_kmajor_kernel"
+    _case(mi.custom(T, D, H, E, k, routing), "split")
 
 
 def test_skewed_decode_batch():

@@ -42,6 +42,7 @@ def _case(cfg, Hs, mode, tokens=None):
     (500, 512, 384, 8, 2, 128),     # prefill ring, 128-row tiles
     (2100, 256, 256, 3, 2, 640),    # prefill ring, 256-row tiles; Hs > H
     (90, 192, 320, 4, 2, 192),      # D, H and Hs multiples of 64 only (generic kernels)
+    (1024, 512, 256, 8, 2, 512),    # shared GEMM1 on the k-major decode kernel (32 m-tiles of one group)
 ])
 def test_shared_expert_matches_oracle(mode, T, D, H, E, k, Hs):
     _case(mi.custom(T, D, H, E, k, "zipf"), Hs, mode)
