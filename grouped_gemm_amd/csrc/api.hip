@@ -183,7 +183,7 @@ MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, 
     a.w4 = p->dtype == MOE_FFN_MXFP4;
     a.mtiles = &table_stand_in;
     if (moe::big_mx_supported(a)) return "big_gemm_kernel<256>";
-    if (moe::skinny_mx_supported(a)) return "mx_skinny_kernel";
+    if (moe::skinny_mx_supported(a)) return moe::mx_decode_kernel_name(a, g1);
     return g1 ? "mx_gemm1_kernel" : "mx_gemm2_kernel";
 }
 

@@ -221,6 +221,8 @@ hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
 // Decode-shaped MX GEMM1 / GEMM2, e2m1 or e4m3 weights (streamed on the MFMA's row side).
 bool skinny_mx_supported(const MxArgs& a);
 hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s);
+// Name of the MX decode kernel launch_skinny_mx runs for `a` (gemm1: GEMM1).
+const char* mx_decode_kernel_name(const MxArgs& a, bool gemm1);
 // MXQ4: fp32 [rows, K] -> packed e2m1 codes [rows, K/2] + e8m0 [rows, K/32].
 hipError_t launch_mx4_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);

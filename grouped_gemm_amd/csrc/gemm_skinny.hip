@@ -1481,6 +1481,345 @@ __global__ __launch_bounds__(kThreads) void mx_skinny_kernel(MxArgs a, int G) {
     }
 }
 
+// Four k-steps' operands from LDS and a wait for them: two 16-byte chunks
+// and one scale byte each (e4m3 weights, or the token fragments); asm for
+// the same reason as lds_read6.
+__device__ __forceinline__ void mxk_read4x2(u32x4_t (&lo)[4], u32x4_t (&hi)[4], uint32_t (&sc)[4],
+                                            const uint32_t (&alo)[4], const uint32_t (&ahi)[4],
+                                            const uint32_t (&as)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b128 %4, %16\n\t"
+        "ds_read_b128 %5, %17\n\t"
+        "ds_read_b128 %6, %18\n\t"
+        "ds_read_b128 %7, %19\n\t"
+        "ds_read_u8 %8, %20\n\t"
+        "ds_read_u8 %9, %21\n\t"
+        "ds_read_u8 %10, %22\n\t"
+        "ds_read_u8 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+          "=&v"(hi[3]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3])
+        : "v"(alo[0]), "v"(alo[1]), "v"(alo[2]), "v"(alo[3]), "v"(ahi[0]), "v"(ahi[1]), "v"(ahi[2]), "v"(ahi[3]),
+          "v"(as[0]), "v"(as[1]), "v"(as[2]), "v"(as[3])
+        : "memory");
+}
+// The same with one 16-byte chunk per k-step (e2m1 weights).
+__device__ __forceinline__ void mxk_read4x1(u32x4_t (&w)[4], uint32_t (&sc)[4], const uint32_t (&aw)[4],
+                                            const uint32_t (&as)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_u8 %4, %12\n\t"
+        "ds_read_u8 %5, %13\n\t"
+        "ds_read_u8 %6, %14\n\t"
+        "ds_read_u8 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]),
+          "=&v"(sc[3])
+        : "v"(aw[0]), "v"(aw[1]), "v"(aw[2]), "v"(aw[3]), "v"(as[0]), "v"(as[1]), "v"(as[2]), "v"(as[3])
+        : "memory");
+}
+
+// Plain LDS stores and loads of floats in a ring slot, written as asm: the
+// compiler, which cannot tell that slot from the ones DMAs are filling,
+// would put a vmcnt(0) wait (draining the ring) before its own accesses.
+__device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_load4_f32(float (&v)[4], const uint32_t (&p)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\t"
+        "ds_read_b32 %1, %5\n\t"
+        "ds_read_b32 %2, %6\n\t"
+        "ds_read_b32 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+
+// Most row groups an MX k-major block keeps accumulators for at once (e2m1
+// weights hold twice the token fragments, eight k-steps per wave).
+constexpr int mx_kmajor_groups(bool w4) { return w4 ? 6 : 8; }
+
+// The MX decode GEMMs, k-major (the order of dma_kmajor_kernel): a block
+// (m-tile, G row groups, G >= 4) walks K in 512-value chunks and, within a
+// chunk, up to mx_kmajor_groups groups; a stage is one group's R weight rows
+// (32 KB of e4m3 or e2m1 codes) and their scale bytes, in a 4-slot ring.
+// The m-tile's token chunk (32 rows x 512 e4m3 codes and their scales) rides
+// with the first stage of its chunk into one token slot, which the next
+// chunk's DMA overwrites only four stages later (so every super-group has at
+// least four groups). Each wave owns one 32-row block of a group (e2m1: R =
+// 128, four blocks, all eight 64-value k-steps of a stage; e4m3: R = 64, two
+// blocks, each wave half the k-steps, the halves summed in LDS at the end of
+// a super-group) and keeps its token fragments in registers across the
+// chunk's groups. GEMM1's group is R/2 act columns; within each 8 rows the
+// first 4 are gate rows and the next 4 the up rows of the same columns, so an
+// MFMA lane holding gate sums finds the up sums 32 lanes away, and each
+// 32-row block yields 16 act columns (half an MX scale block: the two waves
+// of a scale block swap their row maxima through LDS).
+template <int R, bool W4, bool GEMM1>
+__global__ __launch_bounds__(kThreads) void mx_kmajor_kernel(MxArgs a, int G, int nsg) {
+    using C = Mx4<R, W4>;
+    constexpr int SW = 4, NB = R / 32, KP = 4 / NB, NSK = 8 / KP;  // k-steps per wave per stage
+    constexpr int GSM = mx_kmajor_groups(W4);
+    constexpr int WSLOT = C::WB + R * 16;   // weight codes, then R scale rows of 16 bytes
+    constexpr int TSLOT = C::TB + 64 * 16;  // token codes, then 32 scale rows (and a 512-byte pad)
+    static_assert(NB * KP == 4 && NSK % 4 == 0, "four waves: row blocks x K parts");
+    static_assert(SW * WSLOT + TSLOT + 2 * 4 * 32 * 4 <= 160 * 1024, "LDS of a CU");
+    static_assert((SW - 2) * C::WINS < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * WSLOT + TSLOT];
+    __shared__ float xamax[2][4][32];  // GEMM1: per token, the act maximum of each wave's 16 columns
+    uint8_t* const tslot = lds + SW * WSLOT;
+    MTile mt;
+    const BlockPos bp = block_pos((GEMM1 ? a.H / (R / 2) : a.D / R) / G);
+    if (!find_mtile<kMx4BM>(a.rv, a.E, bp.mtile, mt)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rb = wave % NB, kp = wave / NB;
+    const int lr = lane & 31, g = lane >> 5;
+    const int K = GEMM1 ? a.D : a.H;
+    const int KB = K / 32;  // scale bytes per row
+    const int grp0 = bp.chunk * G;
+    const uint8_t* wbase = GEMM1 ? a.w1 : a.w2;
+    const uint8_t* wsbase = GEMM1 ? a.w1s : a.w2s;
+    auto wrow = [&](int r) -> int64_t {  // expert weight row of slot row r in group grp0
+        if (GEMM1) {
+            const int col = grp0 * (R / 2) + 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3);
+            return static_cast<int64_t>(mt.expert) * 2 * a.H + ((r & 4) ? a.H + col : col);
+        }
+        return static_cast<int64_t>(mt.expert) * a.D + grp0 * R + r;
+    };
+    const int64_t rowb = W4 ? K / 2 : K;  // weight row bytes
+    // (arrays of a size that does not depend on the template arguments: the
+    // host pass drops the kernel's launch stub when a lambda captures one
+    // whose size does)
+    constexpr int WINS = 8, TINS = 4;
+    static_assert(C::WINS == WINS && C::TINS == TINS, "32 KB weight stages, 16 KB token chunks");
+    const char* wsrc[WINS];
+#pragma unroll
+    for (int j = 0; j < C::WINS; ++j) {
+        const int row = (wave * C::WINS + j) * C::WRPI + lane / C::WCH;
+        const int c = (lane & (C::WCH - 1)) ^ (row & (C::WCH - 1));
+        wsrc[j] = reinterpret_cast<const char*>(wbase) + wrow(row) * rowb + c * 16;
+    }
+    auto trow = [&](int m) -> int64_t {
+        const int mm = m < mt.rows ? m : 0;
+        if (GEMM1) return clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
+        return mt.row0 + mm;
+    };
+    const uint8_t* tbase = GEMM1 ? a.x : a.act;
+    const uint8_t* tsbase = GEMM1 ? a.xs : a.act_s;
+    const char* tsrc[TINS];
+#pragma unroll
+    for (int j = 0; j < C::TINS; ++j) {
+        const int m = (wave * C::TINS + j) * 2 + lane / 32;
+        const int c = (lane & 31) ^ (m & 31);
+        tsrc[j] = reinterpret_cast<const char*>(tbase) + trow(m) * K + c * 16;
+    }
+    // scale DMA: wave w < SWAVES lane i -> scale row of slot row 64w + i; wave SWAVES -> token row i & 31
+    const char* ssrc = wave < C::SWAVES ? reinterpret_cast<const char*>(wsbase) + wrow(64 * wave + lane) * KB
+                                        : reinterpret_cast<const char*>(tsbase) + trow(lane & 31) * KB;
+    const int64_t wgroup_stride = static_cast<int64_t>(GEMM1 ? R / 2 : R) * rowb;
+    const int64_t sgroup_stride = static_cast<int64_t>(GEMM1 ? R / 2 : R) * KB;
+    const int KIT = K / kMx4KC, NIT = G * KIT;
+    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;  // as in dma_skinny_kernel
+    const int kc0 = static_cast<int>(blockIdx.x) % KIT;     // as in dma_kmajor_kernel
+    const KmajorPlan pl{G / nsg, G % nsg, KIT};
+    int ep = 0;
+    float wt = 1.0f;
+    if (!GEMM1) {
+        ep = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (lr < mt.rows ? lr : 0)], a.P);
+        wt = a.wts[ep];
+        asm volatile("" : "+v"(ep), "+v"(wt));
+    }
+    auto issue = [&](int st) {
+        int sg, kc, gi;
+        pl.locate(st, sg, kc, gi);
+        const int gr = (pl.first(sg) + gi + rot) % G;
+        const int kr = (kc + kc0) % KIT;
+        uint8_t* slot = lds + (st % SW) * WSLOT;
+        const int64_t wb = static_cast<int64_t>(kr) * C::WRB + gr * wgroup_stride;
+#pragma unroll
+        for (int j = 0; j < C::WINS; ++j)
+            __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * C::WINS + j) * 1024), 16, 0,
+                                             kWeightDmaAux);
+        if (wave < C::SWAVES)
+            __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kr) * 16 + gr * sgroup_stride,
+                                             (lds_ptr_t)(slot + C::WB + wave * 1024), 16, 0, 0);
+        if (gi == 0) {
+            const int64_t tb = static_cast<int64_t>(kr) * C::TRB;
+#pragma unroll
+            for (int j = 0; j < C::TINS; ++j)
+                __builtin_amdgcn_global_load_lds(tsrc[j] + tb, (lds_ptr_t)(tslot + (wave * C::TINS + j) * 1024), 16,
+                                                 0, 0);
+            if (wave == C::SWAVES)
+                __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kr) * 16, (lds_ptr_t)(tslot + C::TB), 16,
+                                                 0, 0);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < SW - 1; ++j)
+        if (j < NIT) issue(j);
+    const int row = 32 * rb + lr;  // this lane's weight row in the slot
+    int s = 0;
+    for (int sg = 0; sg < nsg; ++sg) {
+        const int gs = pl.size(sg), gfirst = pl.first(sg);
+        f32x16_t acc[GSM];
+#pragma unroll
+        for (int gi = 0; gi < GSM; ++gi) acc[gi] = f32x16_t{};
+        for (int kc = 0; kc < KIT; ++kc) {
+            u32x4_t tlo[NSK], thi[NSK];
+            uint32_t tsc[NSK];
+#pragma unroll
+            for (int gi = 0; gi < GSM; ++gi) {
+                if (gi >= gs) continue;
+                // the stage's DMAs (and at gi = 0 the chunk's token DMAs, issued after them) are this wave's
+                // oldest; every later stage holds at least WINS
+                if (s + SW - 2 < NIT) wait_vm<(SW - 2) * C::WINS>();
+                else wait_vm<0>();
+                ring_barrier();
+                if (s + SW - 1 < NIT) issue(s + SW - 1);
+                if (gi == 0) {
+#pragma unroll
+                    for (int h = 0; h < NSK / 4; ++h) {
+                        uint32_t alo[4], ahi[4], as[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int ks = kp * NSK + 4 * h + i, ct = 4 * ks + g;
+                            alo[i] = lds_addr(tslot + lr * C::TRB + ((ct ^ lr) << 4));
+                            ahi[i] = lds_addr(tslot + lr * C::TRB + (((ct + 2) ^ lr) << 4));
+                            as[i] = lds_addr(tslot + C::TB + lr * 16 + 2 * ks + g);
+                        }
+                        u32x4_t lo[4], hi[4];
+                        uint32_t sc[4];
+                        mxk_read4x2(lo, hi, sc, alo, ahi, as);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            tlo[4 * h + i] = lo[i];
+                            thi[4 * h + i] = hi[i];
+                            tsc[4 * h + i] = sc[i];
+                        }
+                    }
+                }
+                const uint8_t* slot = lds + (s % SW) * WSLOT;
+#pragma unroll
+                for (int h = 0; h < NSK / 4; ++h) {
+                    uint32_t as[4], wsc[4];
+                    i32x8_t aa[4];
+                    if constexpr (W4) {
+                        uint32_t aw[4];
+                        u32x4_t w[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int ks = kp * NSK + 4 * h + i, cw = 2 * ks + g;
+                            aw[i] = lds_addr(slot + row * C::WRB + ((cw ^ (row & (C::WCH - 1))) << 4));
+                            as[i] = lds_addr(slot + C::WB + row * 16 + 2 * ks + g);
+                        }
+                        mxk_read4x1(w, wsc, aw, as);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            aa[i] = i32x8_t{(int)w[i].x, (int)w[i].y, (int)w[i].z, (int)w[i].w, 0, 0, 0, 0};
+                    } else {
+                        uint32_t alo[4], ahi[4];
+                        u32x4_t wl[4], wh[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int ks = kp * NSK + 4 * h + i, ct = 4 * ks + g;
+                            alo[i] = lds_addr(slot + row * C::WRB + ((ct ^ (row & (C::WCH - 1))) << 4));
+                            ahi[i] = lds_addr(slot + row * C::WRB + (((ct + 2) ^ (row & (C::WCH - 1))) << 4));
+                            as[i] = lds_addr(slot + C::WB + row * 16 + 2 * ks + g);
+                        }
+                        mxk_read4x2(wl, wh, wsc, alo, ahi, as);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            aa[i] = i32x8_t{(int)wl[i].x, (int)wl[i].y, (int)wl[i].z, (int)wl[i].w,
+                                            (int)wh[i].x, (int)wh[i].y, (int)wh[i].z, (int)wh[i].w};
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 4 * h + i;
+                        const i32x8_t bt{(int)tlo[t].x, (int)tlo[t].y, (int)tlo[t].z, (int)tlo[t].w,
+                                         (int)thi[t].x, (int)thi[t].y, (int)thi[t].z, (int)thi[t].w};
+                        acc[gi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aa[i], bt, acc[gi], W4 ? 4 : 0, 0, 0,
+                                                                                 (int)wsc[i], 0, (int)tsc[t]);
+                    }
+                }
+                ++s;
+            }
+        }
+        // epilogue of the super-group (acc[gi][v]: token lr, slot row 32 rb + 8 (v / 4) + 4 g + v % 4); the
+        // slot of the stage just consumed is free until the next stage's barrier
+        const uint32_t red = lds_addr(lds + ((s - 1) % SW) * WSLOT);
+#pragma unroll
+        for (int gi = 0; gi < GSM; ++gi) {
+            if (gi >= gs) continue;
+            const int gidx = grp0 + (gfirst + gi + rot) % G;
+            f32x16_t v = acc[gi];
+            if constexpr (KP == 2) {
+                lds_barrier();
+                if (kp == 1) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) lds_store_f32(red + ((rb * 16 + q) * 64 + lane) * 4, v[q]);
+                }
+                lds_barrier();
+                if (kp == 0) {
+#pragma unroll
+                    for (int q0 = 0; q0 < 16; q0 += 4) {
+                        uint32_t p[4];
+                        float o[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) p[i] = red + ((rb * 16 + q0 + i) * 64 + lane) * 4;
+                        lds_load4_f32(o, p);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[q0 + i] += o[i];
+                    }
+                }
+            }
+            if (GEMM1) {
+                float up[16], act[16];
+                float amax = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    up[q] = __shfl_xor(v[q], 32);
+                    act[q] = v[q] / (1.0f + __expf(-v[q])) * up[q];
+                    amax = fmaxf(amax, fabsf(act[q]));
+                }
+                const int buf = gi & 1;
+                if (kp == 0 && g == 0) xamax[buf][rb][lr] = amax;
+                lds_barrier();
+                if (kp == 0 && g == 0 && lr < mt.rows) {
+                    const int sc = mx_scale_exp(fmaxf(amax, xamax[buf][rb ^ 1][lr]));
+                    const float inv = pow2f(-sc);
+                    const int64_t trw = mt.row0 + lr;
+                    const int col0 = gidx * (R / 2) + 16 * rb;  // act column v of this lane: col0 + v
+                    uint32_t code[4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        code[q4] = e4m3_encode(act[4 * q4] * inv, act[4 * q4]) |
+                                   (e4m3_encode(act[4 * q4 + 1] * inv, act[4 * q4 + 1]) << 8) |
+                                   (e4m3_encode(act[4 * q4 + 2] * inv, act[4 * q4 + 2]) << 16) |
+                                   (e4m3_encode(act[4 * q4 + 3] * inv, act[4 * q4 + 3]) << 24);
+                    *reinterpret_cast<uint4*>(a.act + trw * a.H + col0) = uint4{code[0], code[1], code[2], code[3]};
+                    if ((rb & 1) == 0) a.act_s[trw * (a.H / 32) + col0 / 32] = static_cast<uint8_t>(sc + 127);
+                }
+            } else if (kp == 0 && lr < mt.rows) {
+                uint16_t* dst = a.ypair + static_cast<int64_t>(ep) * a.D + gidx * R + 32 * rb + 4 * g;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<uint2*>(dst + 8 * q4) =
+                        uint2{pack_bf16x2(v[4 * q4] * wt, v[4 * q4 + 1] * wt),
+                              pack_bf16x2(v[4 * q4 + 2] * wt, v[4 * q4 + 3] * wt)};
+            }
+        }
+    }
+}
+
 }  // namespace
 
 bool decode_kernels_fit(int64_t T, int k, int E) {
@@ -1511,11 +1850,41 @@ bool skinny_mx_supported(const MxArgs& a) {
            a.D % R == 0;
 }
 
+// The MX decode kernel a GEMM runs: mx_kmajor_kernel when every super-group
+// of a block holds at least four row groups (its token slot is reused every
+// four stages), else mx_skinny_kernel.
+static int mx_groups_per_block(const MxArgs& a, bool gemm1) {
+    const int R = a.w4 ? 128 : 64;
+    return groups_per_block(gemm1 ? a.H / (R / 2) : a.D / R, a.T, a.k, a.E);
+}
+
+static int mx_super_groups(const MxArgs& a, int G) {
+    const int gsm = mx_kmajor_groups(a.w4);
+    return (G + gsm - 1) / gsm;
+}
+
+static bool mx_uses_kmajor(const MxArgs& a, int G) { return G / mx_super_groups(a, G) >= 4; }
+
+const char* mx_decode_kernel_name(const MxArgs& a, bool gemm1) {
+    return mx_uses_kmajor(a, mx_groups_per_block(a, gemm1)) ? "mx_kmajor_kernel" : "mx_skinny_kernel";
+}
+
 hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s) {
     const int R = a.w4 ? 128 : 64;
     const int groups = gemm1 ? a.H / (R / 2) : a.D / R;
-    const int G = groups_per_block(groups, a.T, a.k, a.E);
+    const int G = mx_groups_per_block(a, gemm1);
     const unsigned g = static_cast<unsigned>(mtiles_upper(a.P, a.E, kMx4BM)) * (groups / G);
+    if (mx_uses_kmajor(a, G)) {
+        const int nsg = mx_super_groups(a, G);
+        if (a.w4) {
+            if (gemm1) mx_kmajor_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G, nsg);
+            else mx_kmajor_kernel<128, true, false><<<g, kThreads, 0, s>>>(a, G, nsg);
+        } else {
+            if (gemm1) mx_kmajor_kernel<64, false, true><<<g, kThreads, 0, s>>>(a, G, nsg);
+            else mx_kmajor_kernel<64, false, false><<<g, kThreads, 0, s>>>(a, G, nsg);
+        }
+        return hipGetLastError();
+    }
     if (a.w4) {
         if (gemm1) mx_skinny_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G);
         else mx_skinny_kernel<128, false, true><<<g, kThreads, 0, s>>>(a, G);

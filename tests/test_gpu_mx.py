@@ -109,6 +109,21 @@ def test_mx_decode_kernel(T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
+@pytest.mark.parametrize("T,D,H,E,k,routing,gemms", [
+    (16, 2048, 1024, 32, 8, "uniform", (1, 2)),   # 4 row groups per block (the fewest it takes)
+    (64, 1024, 2048, 32, 8, "softmax", (1,)),     # GEMM1: 8 groups, one super-group
+    (64, 4096, 1536, 64, 6, "zipf", (1, 2)),      # 6 + 6 and 8 + 8 groups, skewed: extra m-tiles
+])
+def test_mx_kmajor_decode_kernel(T, D, H, E, k, routing, gemms):
+    """The k-major MX decode GEMMs (e4m3 weights: two 32-row blocks per group,
+    each wave half the k-steps, the halves summed at the end of a super-group;
+    GEMM1's act requantized from 16-column halves whose maxima meet in LDS)."""
+    import grouped_gemm_amd as g
+    for gemm in gemms:
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp8", "split", gemm) == "mx_kmajor_kernel"
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
 def test_mx_decode_dims_in_full():
     """The MX workload's dims at 64 tokens (D=4096, H=1536, E=64, top-6): the
     decode kernel on every token."""

@@ -115,6 +115,19 @@ def test_mxfp4_decode_kernel_matches_oracle(T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
+@pytest.mark.parametrize("T,D,H,E,k,routing,gemms", [
+    (64, 1024, 2048, 32, 8, "softmax", (1,)),     # GEMM1: 4 row groups per block (the fewest it takes)
+    (64, 4096, 1536, 64, 6, "zipf", (1, 2)),      # 6 groups, and 4 + 4; skewed: extra m-tiles
+])
+def test_mxfp4_kmajor_decode_kernel(T, D, H, E, k, routing, gemms):
+    """The k-major MX decode GEMMs with e2m1 weights (four 32-row blocks per
+    group, one per wave, all k-steps: no cross-wave sum)."""
+    import grouped_gemm_amd as g
+    for gemm in gemms:
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp4", "split", gemm) == "mx_kmajor_kernel"
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
+
+
 def test_mxfp4_decode_workload_in_full():
     """The decode workload's dims (T=64, D=6144, H=2048, E=32, top-8) with fp4 weights, every token."""
     _case(mi.CONFIGS[2])
