@@ -138,7 +138,7 @@ def kernel_work(cfg, mode, hit, dtype):
     }
 
 
-KERNEL_FILES = {"dma_split_kernel": "gemm_skinny.hip", "dma_kmajor_kernel": "gemm_skinny.hip",
+KERNEL_FILES = {"dma_kmajor_kernel": "gemm_skinny.hip",
                 "dma_skinny_kernel": "gemm_skinny.hip",
                 "mx_fused_kernel": "mx.hip", "fused_dma_kernel": "gemm_skinny.hip",
                 "mx_skinny_kernel": "gemm_skinny.hip", "mx_kmajor_kernel": "gemm_skinny.hip",

@@ -22,9 +22,9 @@
 //    and per-wave vmcnt budgets keep the later stages in flight (the
 //    __syncthreads() fence, or a compiler-inserted wait before an LDS read
 //    it cannot tell apart from the slots being filled, would drain it);
-//    with the weights and the tokens on rings of their own, moved by
-//    different waves, the weight ring keeps three stages in flight
-//    (dma_split_kernel).
+//  * k-major order (dma_kmajor_kernel): each token chunk fetched once per K
+//    chunk and kept in registers across a block's row groups, and each
+//    block's K walk started at its own chunk.
 //
 // GEMM1: a block owns 32 act columns h..h+31 of one expert per row group:
 // gate rows h..h+31 and up rows H+h..H+h+31 of W1 (the gate/up pairing of
@@ -379,154 +379,6 @@ __global__ __launch_bounds__(kThreads) void dma_skinny_kernel(Bf16Args a, int G)
     }
 }
 
-// The split-ring kernel's DMAs of stage `it` for this wave (one of the pair
-// that moves them, mw = 0 or 1): weight rows into weight slot it % SW, or
-// token rows into token slot it % 2.
-template <int KC, int SW>
-__device__ __forceinline__ void split_issue_w(uint8_t* lds, int it, int KIT, int G, int rot, int64_t group_stride,
-                                              int mw, const char* const* src) {
-    using T = DmaTile<2, KC, 2>;
-    constexpr int W_INS = 2 * T::W_INS;
-    const int64_t off = static_cast<int64_t>(it % KIT) * T::RB + ((it / KIT + rot) % G) * group_stride;
-    uint8_t* slot = lds + (it % SW) * T::W_BYTES;
-#pragma unroll
-    for (int j = 0; j < W_INS; ++j)
-        __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
-                                         kWeightDmaAux);
-}
-template <int KC>
-__device__ __forceinline__ void split_issue_t(uint8_t* tring, int it, int KIT, int mw, const char* const* src) {
-    using T = DmaTile<2, KC, 2>;
-    constexpr int T_INS = 2 * T::T_INS;
-    const int64_t off = static_cast<int64_t>(it % KIT) * T::RB;
-    uint8_t* slot = tring + (it & 1) * T::T_BYTES;
-#pragma unroll
-    for (int j = 0; j < T_INS; ++j)
-        __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * T_INS + j) * 1024), 16, 0, 0);
-}
-
-// The same GEMMs with the weights and the tokens on separate rings: waves 0-1
-// move the weight rows through an SW-stage ring, waves 2-3 the token rows
-// through a 2-stage ring (tokens come from L2, one stage ahead is enough).
-// s_waitcnt vmcnt counts a wave's own loads in issue order, so when every
-// wave moves both (dma_skinny_kernel) a wait for the next stage's tokens is
-// also a wait for every weight stage issued before them; split by wave, the
-// weight waves keep SW - 1 stages in flight while the token waves wait for
-// their own stage alone. SW = 4: 4 x 32 KB of weights + 2 x 16 KB of tokens,
-// the whole 160 KB of LDS. Same fragments, split-K over the waves, group
-// reduction and epilogue as dma_skinny_kernel (32 token rows, KC = 256).
-template <int KC, int SW, bool GEMM1>
-__global__ __launch_bounds__(kThreads) void dma_split_kernel(Bf16Args a, int G) {
-    using T = DmaTile<2, KC, 2>;
-    constexpr int NB = 4, NT = 2;
-    constexpr int W_INS = 2 * T::W_INS, T_INS = 2 * T::T_INS;  // per wave of the pair that moves them
-    constexpr int NI = W_INS > T_INS ? W_INS : T_INS;
-    static_assert(T::RPI * T::RB == 1024, "one DMA instruction fills 1 KB of LDS");
-    static_assert(T::NS % 4 == 0, "k-steps must split evenly over the four waves");
-    static_assert(SW * T::W_BYTES + 2 * T::T_BYTES <= 160 * 1024 && SW >= 2, "rings must fit the LDS of a CU");
-    static_assert((SW - 2) * W_INS < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES];
-    uint8_t* const tring = lds + SW * T::W_BYTES;
-    MTile mt;
-    const BlockPos bp = block_pos((GEMM1 ? a.H / 32 : a.D / 64) / G);
-    if (!find_mtile<T::BM>(a.rv, a.E, bp.mtile, mt)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const bool wmover = wave < 2;
-    const int mw = wave & 1;  // this wave's half of what its pair moves
-    const int K = GEMM1 ? a.D : a.H;
-    const int grp0 = bp.chunk * G;
-    const int pc = lane % T::CPR;
-    const char* src[NI];
-    if (wmover) {
-#pragma unroll
-        for (int j = 0; j < W_INS; ++j) {
-            const int row = (mw * W_INS + j) * T::RPI + lane / T::CPR;
-            const int c = pc ^ (row & (T::CPR - 1));
-            int64_t grow;
-            if (GEMM1) {
-                const int h0 = grp0 * 32;
-                grow = static_cast<int64_t>(mt.expert) * 2 * a.H + (row < 32 ? h0 + row : a.H + h0 + row - 32);
-            } else {
-                grow = static_cast<int64_t>(mt.expert) * a.D + grp0 * 64 + row;
-            }
-            src[j] = reinterpret_cast<const char*>(GEMM1 ? a.w1 : a.w2) + grow * K * 2 + c * 16;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int m = (mw * T_INS + (j < T_INS ? j : 0)) * T::RPI + lane / T::CPR;
-            const int c = pc ^ (m & (T::CPR - 1));
-            const int mm = m < mt.rows ? m : 0;
-            int64_t grow;
-            if (GEMM1) grow = clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
-            else grow = mt.row0 + mm;
-            src[j] = reinterpret_cast<const char*>(GEMM1 ? a.x : a.act) + grow * K * 2 + c * 16;
-        }
-    }
-    const int64_t group_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * K * 2;
-    const int r = lane & 15, kg = lane >> 4;
-    const int KIT = K / KC, NIT = G * KIT;
-    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;  // as in dma_skinny_kernel
-    f32x4_t acc[NB][NT];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
-    int ep;
-    float esc;
-    dma_epilogue_token<GEMM1>(a, mt, wave, lane, ep, esc);
-    if (wmover) {
-#pragma unroll
-        for (int j = 0; j < SW - 1; ++j)
-            if (j < NIT) split_issue_w<KC, SW>(lds, j, KIT, G, rot, group_stride, mw, src);
-    } else {
-        split_issue_t<KC>(tring, 0, KIT, mw, src);
-    }
-    for (int it = 0; it < NIT; ++it) {
-        if (!wmover || it + SW - 2 >= NIT) wait_vm<0>();
-        else wait_vm<(SW - 2) * W_INS>();
-        ring_barrier();
-        if (wmover) {
-            if (it + SW - 1 < NIT) split_issue_w<KC, SW>(lds, it + SW - 1, KIT, G, rot, group_stride, mw, src);
-        } else if (it + 1 < NIT) {
-            split_issue_t<KC>(tring, it + 1, KIT, mw, src);
-        }
-        uint8_t* wslot = lds + (it % SW) * T::W_BYTES;
-        uint8_t* tslot = tring + (it & 1) * T::T_BYTES;
-#pragma unroll
-        for (int q = 0; q < T::NS / 4; ++q) {
-            const int c = 4 * (wave * (T::NS / 4) + q) + kg;  // logical chunk of this lane's k-group
-            uint32_t pw[4], pt[2];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int row = 16 * b + r;
-                pw[b] = lds_addr(wslot + row * T::RB + ((c ^ (row & (T::CPR - 1))) << 4));
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int m = 16 * t + r;
-                pt[t] = lds_addr(tslot + m * T::RB + ((c ^ (m & (T::CPR - 1))) << 4));
-            }
-            bf16x8_t w[NB], tk[NT];
-            lds_read6(w, tk, pw, pt);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[b][t] = mfma16(w[b], tk[t], acc[b][t]);
-        }
-        if (it % KIT != KIT - 1) continue;
-        // the result stores of waves 0-1 count in their vmcnt too: the next
-        // weight wait may then also wait for a few DMAs of the stage after the
-        // one it needs, never for fewer than that stage's
-        dma_group_end<T::W_BYTES, GEMM1>(a, acc, reinterpret_cast<float*>(wslot), mt,
-                                         grp0 + (it / KIT + rot) % G, wave, lane, ep, esc);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
-    }
-}
-
 // Eight 16-byte LDS reads and a wait for them, in one asm statement (as
 // lds_read6, so that no vmcnt wait for the DMAs in flight comes before them).
 __device__ __forceinline__ void lds_read8(bf16x8_t (&v)[8], const uint32_t (&p)[8]) {
@@ -573,7 +425,51 @@ struct KmajorPlan {
     }
 };
 
-// The decode GEMMs, k-major: a block (m-tile, G row groups) walks K in
+// A decode block's work: m-tile `mtile`, its row groups g0 .. g0 + n - 1.
+struct DecodeWork {
+    int mtile, g0, n;
+};
+
+// The k-major kernels' work, split on the device, where the m-tile count M
+// (32-row tiles of the route just run) is known: the grid's B blocks (one
+// per CU) are dealt out over the M m-tiles as evenly as they go (B mod M of
+// them get one block more), and each m-tile's row groups, in units of UNIT
+// consecutive groups, as evenly over its blocks. A batch with an expert past
+// 32 rows then spreads its extra m-tile over the chip instead of running a
+// second round of blocks after the first. With M >= B (many experts hit),
+// block b takes m-tile b whole (the grid holds at least M blocks).
+template <int UNIT>
+__device__ __forceinline__ bool decode_work(const RouteView& rv, int E, int groups, DecodeWork& w) {
+    const int M = rv.tile_prefix[tile_height_index(32) * (E + 1) + E];
+    const int B = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    if (M <= 0) return false;
+    if (M >= B) {
+        if (b >= M) return false;
+        w = DecodeWork{b, 0, groups};
+        return true;
+    }
+    const int base = B / M, extra = B % M, units = groups / UNIT;
+    int j, q, nb;
+    if (b < extra * (base + 1)) {
+        j = b / (base + 1);
+        q = b - j * (base + 1);
+        nb = base + 1;
+    } else {
+        const int b2 = b - extra * (base + 1);
+        j = extra + b2 / base;
+        q = b2 - (j - extra) * base;
+        nb = base;
+    }
+    if (nb > units) {
+        if (q >= units) return false;
+        nb = units;
+    }
+    const int u0 = q * units / nb, u1 = (q + 1) * units / nb;
+    w = DecodeWork{j, u0 * UNIT, (u1 - u0) * UNIT};
+    return true;
+}
+
+// The decode GEMMs, k-major: a block (m-tile, G row groups: decode_work) walks K in
 // 256-value chunks and, within a chunk, up to kKmajorGroups groups, so each
 // chunk of the m-tile's 32 token rows (16 KB) is fetched once per chunk
 // instead of once per group (with the token rows fetched per group, their
@@ -589,7 +485,7 @@ struct KmajorPlan {
 // 8 up rows of the same act columns: an MFMA lane holding gate rows finds
 // the matching up rows 32 lanes away.
 template <bool GEMM1>
-__global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a, int G, int nsg) {
+__global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a) {
     using T = DmaTile<2, 256, 2>;  // 512-byte row segments: 32 KB weight stages, 16 KB token chunks
     constexpr int SW = 4, NT = 2, NS = T::NS, GSM = kKmajorGroups;
     constexpr int W_INS = T::W_INS, T_INS = T::T_INS;  // per wave per stage / per chunk
@@ -598,13 +494,15 @@ __global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a, int G,
     static_assert((SW - 2) * W_INS < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES];
     uint8_t* const tring = lds + SW * T::W_BYTES;
+    DecodeWork wk;
+    if (!decode_work<2>(a.rv, a.E, GEMM1 ? a.H / 32 : a.D / 64, wk)) return;
     MTile mt;
-    const BlockPos bp = block_pos((GEMM1 ? a.H / 32 : a.D / 64) / G);
-    if (!find_mtile<T::BM>(a.rv, a.E, bp.mtile, mt)) return;
+    if (!find_mtile<T::BM>(a.rv, a.E, wk.mtile, mt)) return;
+    const int G = wk.n, nsg = (G + GSM - 1) / GSM;  // every super-group holds at least two groups
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, kg = lane >> 4;
     const int K = GEMM1 ? a.D : a.H;
-    const int grp0 = bp.chunk * G;
+    const int grp0 = wk.g0;
     const int pc = lane % T::CPR;
     const char* wsrc[W_INS];
 #pragma unroll
@@ -631,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a, int G,
     }
     const int64_t group_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * K * 2;
     const int KIT = K / 256, NIT = G * KIT;
-    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;  // as in dma_skinny_kernel
+    const int rot = GEMM1 ? 0 : static_cast<int>(blockIdx.x) % G;  // as in dma_skinny_kernel
     // The K chunks are walked from chunk kc0 on, wrapping: the blocks run in
     // near lockstep, and if every block read the same 512-byte column of its
     // rows at once, the reads would crowd a few HBM channels.
@@ -758,8 +656,8 @@ __global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a, int G,
 // partial added into a global accumulator) on the decode kernels' rings. A
 // block owns one 32-row m-tile and a slice of BH act columns h0 .. h0 + BH - 1:
 //   phase 1 streams the slice's gate and up rows of W1 (BH/32 row groups of
-//     32 act columns, as GEMM1 of dma_split_kernel) and leaves silu(gate) * up
-//     as bf16 in LDS;
+//     32 act columns: gate rows h..h+31 and up rows H+h..H+h+31, split-K
+//     over the four waves) and leaves silu(gate) * up as bf16 in LDS;
 //   phase 2 streams the slice's columns of every W2 row (groups of R2 output
 //     features, one 32 KB stage each) against that act tile and adds
 //     weight * partial into acc32 [T, D] (fp32).
@@ -1069,31 +967,23 @@ int groups_per_block(int groups, int64_t T, int k, int E) {
     return groups;
 }
 
-// Which decode kernel a GEMM runs: 0 dma_kmajor_kernel (K a multiple of
-// 256, at least 2 row groups per block), 1 dma_split_kernel (K a multiple
-// of 256, one group per block), 2 dma_skinny_kernel (128-value stages).
-int decode_kernel(const Bf16Args& a, bool gemm1, int G) {
-    if ((gemm1 ? a.D : a.H) % 256) return 2;
-    return G >= 2 ? 0 : 1;
-}
+// Which decode kernel a GEMM runs: dma_kmajor_kernel when K is a multiple
+// of 256, else dma_skinny_kernel (128-value stages). (The decode kernels run
+// only with D and H multiples of 128, so a GEMM has at least two row groups,
+// the pair dma_kmajor_kernel's blocks take them in.)
+bool decode_kmajor(const Bf16Args& a, bool gemm1) { return (gemm1 ? a.D : a.H) % 256 == 0; }
 
 hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
     constexpr int NT = 2;  // m-tiles of 32 tokens
     const int groups = gemm1 ? a.H / 32 : a.D / 64;
+    if (decode_kmajor(a, gemm1)) {  // one block per CU, or one per m-tile when they can be more (decode_work)
+        const unsigned gk = static_cast<unsigned>(std::max(device_cu_count(), mtiles_upper(a.P, a.E, 16 * NT)));
+        if (gemm1) dma_kmajor_kernel<true><<<gk, kThreads, 0, s>>>(a);
+        else dma_kmajor_kernel<false><<<gk, kThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
     const int G = groups_per_block(groups, a.T, a.k, a.E);
     const unsigned g = static_cast<unsigned>(mtiles_upper(a.P, a.E, 16 * NT)) * (groups / G);
-    const int kind = decode_kernel(a, gemm1, G);
-    if (kind == 0) {
-        const int nsg = (G + kKmajorGroups - 1) / kKmajorGroups;
-        if (gemm1) dma_kmajor_kernel<true><<<g, kThreads, 0, s>>>(a, G, nsg);
-        else dma_kmajor_kernel<false><<<g, kThreads, 0, s>>>(a, G, nsg);
-        return hipGetLastError();
-    }
-    if (kind == 1) {
-        if (gemm1) dma_split_kernel<256, 4, true><<<g, kThreads, 0, s>>>(a, G);
-        else dma_split_kernel<256, 4, false><<<g, kThreads, 0, s>>>(a, G);
-        return hipGetLastError();
-    }
     if (gemm1) dma_skinny_kernel<NT, 128, 6, true><<<g, kThreads, 0, s>>>(a, G);
     else dma_skinny_kernel<NT, 128, 6, false><<<g, kThreads, 0, s>>>(a, G);
     return hipGetLastError();
@@ -1132,9 +1022,7 @@ hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s) {
 }
 
 const char* decode_kernel_name(const Bf16Args& a, bool gemm1) {
-    const int groups = gemm1 ? a.H / 32 : a.D / 64;
-    static const char* const names[] = {"dma_kmajor_kernel", "dma_split_kernel", "dma_skinny_kernel"};
-    return names[decode_kernel(a, gemm1, groups_per_block(groups, a.T, a.k, a.E))];
+    return decode_kmajor(a, gemm1) ? "dma_kmajor_kernel" : "dma_skinny_kernel";
 }
 
 hipError_t launch_skinny_gemm1(const Bf16Args& a, hipStream_t s) { return launch_dma(a, true, s); }

@@ -19,7 +19,7 @@ def _kernel(T, D, H, E, k, dtype="bf16", mode="split", gemm=1):
 def test_decode_rule_matches_binomial_tail(T, k, E):
     p = k / E
     want = T * p <= 32 and E * binom.sf(32, T, p) < 0.5
-    got = _kernel(T, 2048, 1024, E, k) in ("dma_kmajor_kernel", "dma_split_kernel")
+    got = _kernel(T, 2048, 1024, E, k) == "dma_kmajor_kernel"
     assert got == want
     mx = _kernel(T, 2048, 1024, E, k, dtype="mxfp8") in ("mx_kmajor_kernel", "mx_skinny_kernel")
     assert mx == want
@@ -34,7 +34,7 @@ def test_workload_paths():
     assert _kernel(131072, 2048, 768, 128, 8, gemm=2) == "big_gemm_kernel<256>"
     assert _kernel(300, 384, 640, 16, 4) == "gemm1_swiglu_kernel"           # D not a multiple of 256
     assert _kernel(300, 384, 640, 16, 4, gemm=2) == "gemm2_weight_kernel"
-    assert _kernel(64, 256, 512, 8, 2, mode="auto") == "dma_split_kernel"   # AUTO resolves to split
+    assert _kernel(64, 256, 512, 8, 2, mode="auto") == "dma_kmajor_kernel"  # AUTO resolves to split
     assert _kernel(64, 256, 512, 8, 2, mode="fused") == "fused_dma_kernel"
     assert _kernel(64, 384, 512, 8, 2, mode="fused") == "fused_bf16_kernel"  # D not a multiple of 256
     assert _kernel(16384, 4096, 1536, 64, 6, dtype="mxfp8") == "big_gemm_kernel<256>"
@@ -46,10 +46,10 @@ def test_workload_paths():
     assert _kernel(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == "mx_fused_kernel"
     # E = 1 (one group of every token): the decode kernels while the prefill
     # ring would get fewer tiles than half of the 256 compute units
-    assert _kernel(260, 256, 128, 1, 1) == "dma_split_kernel"              # 3 ring tiles
+    assert _kernel(260, 256, 128, 1, 1) == "dma_kmajor_kernel"             # 3 ring tiles
     assert _kernel(260, 256, 128, 1, 1, gemm=2) == "dma_skinny_kernel"     # K = H = 128
     assert _kernel(2048, 256, 512, 1, 1) == "dma_kmajor_kernel"            # (16 + 1) x 4 = 68 ring tiles
-    assert _kernel(2048, 256, 512, 1, 1, gemm=2) == "dma_split_kernel"     # one row group per block
+    assert _kernel(2048, 256, 512, 1, 1, gemm=2) == "dma_kmajor_kernel"    # 4 row groups over 64 m-tiles
     assert _kernel(4096, 256, 1024, 1, 1) == "big_gemm_kernel<256>"        # (32 + 1) x 8 = 264 ring tiles
     assert _kernel(0, 256, 512, 8, 2) == "none"
     assert _kernel(64, 256, 512, 8, 2, gemm=3) is None

@@ -169,8 +169,8 @@ def _duplicate_ids(ids):
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("T,D,H,E,k,kernel", [
-    (32, 512, 512, 8, 3, "dma_split_kernel"),       # decode kernels
-    (40, 2048, 768, 128, 8, "dma_kmajor_kernel"),   # decode kernels, k-major
+    (32, 512, 512, 8, 3, "dma_kmajor_kernel"),      # decode kernels
+    (40, 2048, 768, 128, 8, "dma_kmajor_kernel"),   # decode kernels, more m-tiles than row-group pairs per CU
     (500, 512, 384, 8, 2, "big_gemm_kernel<128>"),  # prefill ring, 128-row tiles
     (2100, 256, 384, 3, 2, "big_gemm_kernel<256>"), # prefill ring, 256-row tiles
     (300, 384, 256, 6, 3, "gemm1_swiglu_kernel"),   # generic kernels
@@ -225,12 +225,16 @@ def test_fused_decode_kernel(T, D, H, E, k, routing):
     (1024, 1024, 256, 1, 1, "softmax", (2,)),    # GEMM2: 32 m-tiles of one expert, rotated group order
     (40, 2048, 768, 128, 8, "zipf", (1, 2)),     # both GEMMs, skewed: hot experts hold several m-tiles
     (16, 2048, 768, 128, 8, "uniform", (1, 2)),  # both GEMMs, 128 tokens' routes over 128 experts
+    (64, 2048, 1024, 32, 8, "zipf", (1, 2)),     # skewed: the extra m-tiles share the CUs with the rest
+    (64, 256, 256, 512, 8, "uniform", (1, 2)),   # more m-tiles than CUs: a block per m-tile, all its groups
 ])
 def test_kmajor_decode_kernel(T, D, H, E, k, routing, gemms):
     """The k-major decode GEMMs (token chunk fetched once per K chunk and
     reused across a block's row groups; rows split over the waves; GEMM1's
-    gate and up rows interleaved per 16-row block) through every super-group
-    plan: minimum size, uneven sizes, several m-tiles per expert."""
+    gate and up rows interleaved per 16-row block; the work dealt out on the
+    device from the real m-tile count) through every super-group plan and
+    work split: minimum size, uneven sizes, several m-tiles per expert, more
+    m-tiles than compute units."""
     import grouped_gemm_amd as g
     for gemm in gemms:
         assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", "split", gemm) == "dma_kmajor_kernel"
@@ -244,8 +248,8 @@ def test_skewed_decode_batch():
     extra m-tiles of the hot expert."""
     import grouped_gemm_amd as g
     cfg = mi.custom(64, 512, 512, 16, 4, "uniform")
-    assert g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, "bf16", "split", 1) == "dma_split_kernel"
-    assert g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, "bf16", "split", 2) == "dma_split_kernel"
+    assert g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, "bf16", "split", 1) == "dma_kmajor_kernel"
+    assert g.moe_ffn_gemm_kernel(cfg.T, cfg.D, cfg.H, cfg.E, cfg.k, "bf16", "split", 2) == "dma_kmajor_kernel"
     d = mi.make_bf16(cfg, 8)
     ids = d["topk_ids"]
     hot = np.arange(64) < 56
