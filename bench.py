@@ -141,7 +141,7 @@ def kernel_work(cfg, mode, hit, dtype):
 KERNEL_FILES = {"dma_kmajor_kernel": "gemm_skinny.hip",
                 "dma_skinny_kernel": "gemm_skinny.hip",
                 "mx_fused_kernel": "mx.hip", "fused_dma_kernel": "gemm_skinny.hip",
-                "mx_skinny_kernel": "gemm_skinny.hip", "mx_kmajor_kernel": "gemm_skinny.hip",
+                "mx_kmajor_kernel": "gemm_skinny.hip",
                 "big_gemm_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
                 "gemm1_swiglu_kernel": "gemm_bf16.hip", "gemm2_weight_kernel": "gemm_bf16.hip",

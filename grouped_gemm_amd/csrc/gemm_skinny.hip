@@ -433,12 +433,14 @@ struct DecodeWork {
 // The k-major kernels' work, split on the device, where the m-tile count M
 // (32-row tiles of the route just run) is known: the grid's B blocks (one
 // per CU) are dealt out over the M m-tiles as evenly as they go (B mod M of
-// them get one block more), and each m-tile's row groups, in units of UNIT
-// consecutive groups, as evenly over its blocks. A batch with an expert past
-// 32 rows then spreads its extra m-tile over the chip instead of running a
-// second round of blocks after the first. With M >= B (many experts hit),
-// block b takes m-tile b whole (the grid holds at least M blocks).
-template <int UNIT>
+// them get one block more), and each m-tile's row groups as evenly over its
+// blocks, at least MIN groups to a block (the fewest a super-group of the
+// kernel holds; an m-tile takes no more blocks than that allows). A batch
+// with an expert past 32 rows then spreads its extra m-tile over the chip
+// instead of running a second round of blocks after the first. With M >= B
+// (many experts hit), block b takes m-tile b whole (the grid holds at least
+// M blocks).
+template <int MIN>
 __device__ __forceinline__ bool decode_work(const RouteView& rv, int E, int groups, DecodeWork& w) {
     const int M = rv.tile_prefix[tile_height_index(32) * (E + 1) + E];
     const int B = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
@@ -448,7 +450,7 @@ __device__ __forceinline__ bool decode_work(const RouteView& rv, int E, int grou
         w = DecodeWork{b, 0, groups};
         return true;
     }
-    const int base = B / M, extra = B % M, units = groups / UNIT;
+    const int base = B / M, extra = B % M, cap = groups / MIN;
     int j, q, nb;
     if (b < extra * (base + 1)) {
         j = b / (base + 1);
@@ -460,12 +462,12 @@ __device__ __forceinline__ bool decode_work(const RouteView& rv, int E, int grou
         q = b2 - (j - extra) * base;
         nb = base;
     }
-    if (nb > units) {
-        if (q >= units) return false;
-        nb = units;
+    if (nb > cap) {
+        if (q >= cap) return false;
+        nb = cap;
     }
-    const int u0 = q * units / nb, u1 = (q + 1) * units / nb;
-    w = DecodeWork{j, u0 * UNIT, (u1 - u0) * UNIT};
+    const int g0 = q * groups / nb, g1 = (q + 1) * groups / nb;
+    w = DecodeWork{j, g0, g1 - g0};
     return true;
 }
 
@@ -1033,19 +1035,19 @@ hipError_t launch_skinny_gemm2(const Bf16Args& a, hipStream_t s) { return launch
 // Decode-shaped MX GEMMs: MX-fp8 activations ("Prime Flash MoE", section
 // 7) against e2m1 weights ("GC-MoE on SM120", scale formats: a UE8M0
 // exponent per 32 along K) or e4m3 weights. The same streaming design as
-// above: weights on the MFMA's row side, a ring of S stages filled by
-// global->LDS DMA of whole row segments, one barrier per stage, the four
-// waves splitting each stage's K steps and meeting in LDS at the end of a
-// row group. MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 with the weights as A
+// above: weights on the MFMA's row side, a ring of stages filled by
+// global->LDS DMA of whole row segments, one barrier per stage, k-major
+// over a block's row groups (mx_kmajor_kernel). MFMA:
+// v_mfma_scale_f32_32x32x64_f8f6f4 with the weights as A
 // (e2m1: 16 contiguous bytes per lane, K values 32g..32g+31 of the 64-wide
 // step, g = lane >> 5; e4m3: 16-byte chunks g and 2 + g of the step) and the
 // e4m3 tokens as B (chunks g and 2 + g); lane group g supplies the scale of
 // 32-block g (layouts measured on gfx950 with in-bounds probes).
 //
 // Stage (K step of KC = 512 values): R weight rows x 256 (e2m1) or 512
-// (e4m3) bytes, 32 token rows x 512 bytes, and each row's 16 scale bytes.
-// R = 128 e2m1 rows or 64 e4m3 rows make 32 KB of weights per stage, twice
-// the token bytes, so most of the ring's bytes in flight are weights.
+// (e4m3) bytes and each row's 16 scale bytes; R = 128 e2m1 rows or 64 e4m3
+// rows make 32 KB of weights per stage. A token chunk is 32 rows x 512
+// bytes and their scale bytes.
 // Chunks are XOR-swizzled by the row over the row's chunks (^ (row & 15) or
 // ^ (row & 31)), so the rows a fragment read touches hit distinct bank
 // groups. Waves 0 .. R/64 - 1 also move the weight rows' scales, wave R/64
@@ -1057,317 +1059,16 @@ constexpr int kMx4BM = 32;    // token rows per m-tile
 
 template <int R, bool W4>
 struct Mx4 {
-    static constexpr int NB = R / 32;                 // weight row blocks (32-row MFMA tiles)
     static constexpr int WRB = W4 ? kMx4KC / 2 : kMx4KC;  // weight bytes per row per stage (256 or 512)
     static constexpr int WCH = WRB / 16;              // 16-byte chunks per weight row per stage
     static constexpr int WRPI = 64 / WCH;             // weight rows per DMA instruction
     static constexpr int TRB = kMx4KC;                // token bytes per row per stage (512)
-    static constexpr int WB = R * WRB;
+    static constexpr int WB = R * WRB;                // 32 KB
     static constexpr int TB = kMx4BM * TRB;           // 16 KB
-    static constexpr int SW = WB + TB;                // weight scale rows (R x 16 bytes)
-    static constexpr int ST = SW + R * 16;            // token scale rows (32 x 16 bytes, then a 512-byte pad)
-    static constexpr int STAGE = ST + 64 * 16;
-    static constexpr int S = 160 * 1024 / STAGE < 4 ? 160 * 1024 / STAGE : 4;  // ring stages
     static constexpr int WINS = WB / 1024 / 4;        // weight DMA instructions per wave per stage
-    static constexpr int TINS = TB / 1024 / 4;        // token DMA instructions per wave per stage
+    static constexpr int TINS = TB / 1024 / 4;        // token DMA instructions per wave per chunk
     static constexpr int SWAVES = R / 64;             // waves that move weight scale rows
-    static_assert(S >= 3, "the ring needs three stages");
-    static_assert(4 * 2 * 16 * 64 * 4 <= STAGE, "a two-block pass of the group reduction must fit one ring slot");
 };
-
-// this wave's DMAs of ring stage `it` (row group grp relative to the
-// block's first, K step kit) into slot it % S
-template <int R, bool W4>
-__device__ __forceinline__ void mx4_dma_issue(uint8_t* ring, int it, int grp, int kit, int64_t wgroup_stride,
-                                              int64_t sgroup_stride, const char* const* wsrc,
-                                              const char* const* tsrc, const char* ssrc) {
-    using C = Mx4<R, W4>;
-    const int wave = threadIdx.x >> 6;
-    uint8_t* slot = ring + (it % C::S) * C::STAGE;
-    const int64_t wb = static_cast<int64_t>(kit) * C::WRB + grp * wgroup_stride;
-    const int64_t tb = static_cast<int64_t>(kit) * C::TRB;
-#pragma unroll
-    for (int j = 0; j < C::WINS; ++j)
-        __builtin_amdgcn_global_load_lds(wsrc[j] + wb, (lds_ptr_t)(slot + (wave * C::WINS + j) * 1024), 16, 0,
-                                         kWeightDmaAux);
-#pragma unroll
-    for (int j = 0; j < C::TINS; ++j)
-        __builtin_amdgcn_global_load_lds(tsrc[j] + tb, (lds_ptr_t)(slot + C::WB + (wave * C::TINS + j) * 1024), 16, 0,
-                                         0);
-    // waves 0 .. SWAVES-1: 64 weight rows' scale bytes of this K step each; wave SWAVES: the tokens'
-    if (wave < C::SWAVES)
-        __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16 + grp * sgroup_stride,
-                                         (lds_ptr_t)(slot + C::SW + wave * 1024), 16, 0, 0);
-    else if (wave == C::SWAVES)
-        __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kit) * 16, (lds_ptr_t)(slot + C::ST), 16, 0, 0);
-}
-
-// One K step's operands for one wave: NB weight fragments (e2m1), the token
-// fragment (two 16-byte chunks, e4m3) and the NB + 1 scale bytes, then a
-// wait for them; asm for the same reason as lds_read6.
-__device__ __forceinline__ void mx4_lds_read(u32x4_t (&w)[2], u32x4_t& tlo, u32x4_t& thi, uint32_t (&sw)[2],
-                                             uint32_t& st, const uint32_t (&aw)[2], uint32_t atl, uint32_t ath,
-                                             const uint32_t (&as)[2], uint32_t ast) {
-    asm volatile(
-        "ds_read_b128 %0, %7\n\t"
-        "ds_read_b128 %1, %8\n\t"
-        "ds_read_b128 %2, %9\n\t"
-        "ds_read_b128 %3, %10\n\t"
-        "ds_read_u8 %4, %11\n\t"
-        "ds_read_u8 %5, %12\n\t"
-        "ds_read_u8 %6, %13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(tlo), "=&v"(thi), "=&v"(sw[0]), "=&v"(sw[1]), "=&v"(st)
-        : "v"(aw[0]), "v"(aw[1]), "v"(atl), "v"(ath), "v"(as[0]), "v"(as[1]), "v"(ast)
-        : "memory");
-}
-__device__ __forceinline__ void mx4_lds_read(u32x4_t (&w)[4], u32x4_t& tlo, u32x4_t& thi, uint32_t (&sw)[4],
-                                             uint32_t& st, const uint32_t (&aw)[4], uint32_t atl, uint32_t ath,
-                                             const uint32_t (&as)[4], uint32_t ast) {
-    asm volatile(
-        "ds_read_b128 %0, %11\n\t"
-        "ds_read_b128 %1, %12\n\t"
-        "ds_read_b128 %2, %13\n\t"
-        "ds_read_b128 %3, %14\n\t"
-        "ds_read_b128 %4, %15\n\t"
-        "ds_read_b128 %5, %16\n\t"
-        "ds_read_u8 %6, %17\n\t"
-        "ds_read_u8 %7, %18\n\t"
-        "ds_read_u8 %8, %19\n\t"
-        "ds_read_u8 %9, %20\n\t"
-        "ds_read_u8 %10, %21\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(tlo), "=&v"(thi), "=&v"(sw[0]), "=&v"(sw[1]),
-          "=&v"(sw[2]), "=&v"(sw[3]), "=&v"(st)
-        : "v"(aw[0]), "v"(aw[1]), "v"(aw[2]), "v"(aw[3]), "v"(atl), "v"(ath), "v"(as[0]), "v"(as[1]), "v"(as[2]),
-          "v"(as[3]), "v"(ast)
-        : "memory");
-}
-
-// The same for e4m3 weights (two 16-byte chunks per row block, as the tokens).
-__device__ __forceinline__ void mx8_lds_read(u32x4_t (&wlo)[2], u32x4_t (&whi)[2], u32x4_t& tlo, u32x4_t& thi,
-                                             uint32_t (&sw)[2], uint32_t& st, const uint32_t (&awl)[2],
-                                             const uint32_t (&awh)[2], uint32_t atl, uint32_t ath,
-                                             const uint32_t (&as)[2], uint32_t ast) {
-    asm volatile(
-        "ds_read_b128 %0, %9\n\t"
-        "ds_read_b128 %1, %10\n\t"
-        "ds_read_b128 %2, %11\n\t"
-        "ds_read_b128 %3, %12\n\t"
-        "ds_read_b128 %4, %13\n\t"
-        "ds_read_b128 %5, %14\n\t"
-        "ds_read_u8 %6, %15\n\t"
-        "ds_read_u8 %7, %16\n\t"
-        "ds_read_u8 %8, %17\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(wlo[0]), "=&v"(whi[0]), "=&v"(wlo[1]), "=&v"(whi[1]), "=&v"(tlo), "=&v"(thi), "=&v"(sw[0]),
-          "=&v"(sw[1]), "=&v"(st)
-        : "v"(awl[0]), "v"(awh[0]), "v"(awl[1]), "v"(awh[1]), "v"(atl), "v"(ath), "v"(as[0]), "v"(as[1]), "v"(ast)
-        : "memory");
-}
-
-// grid: (m-tiles of 32 rows, row groups / G). GEMM1: a group is R/2 act
-// columns h..h+R/2-1 (gate rows h.., up rows H+h..), requantized to MX-fp8 in
-// the epilogue (each 32 columns are one scale block); GEMM2: R output
-// features, scaled by the routing weight into ypair.
-template <int R, bool GEMM1, bool W4>
-__global__ __launch_bounds__(kThreads) void mx_skinny_kernel(MxArgs a, int G) {
-    using C = Mx4<R, W4>;
-    static_assert(W4 || R == 64, "e4m3 weights: 64 rows per block");
-    constexpr int NB = C::NB, HALF = R / 2;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[C::S * C::STAGE];
-    MTile mt;
-    const BlockPos bp = block_pos((GEMM1 ? a.H / HALF : a.D / R) / G);
-    if (!find_mtile<kMx4BM>(a.rv, a.E, bp.mtile, mt)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int K = GEMM1 ? a.D : a.H;
-    const int KB = K / 32;  // scale bytes per row
-    const int grp0 = bp.chunk * G;
-    const uint8_t* wbase = GEMM1 ? a.w1 : a.w2;
-    const uint8_t* wsbase = GEMM1 ? a.w1s : a.w2s;
-    auto wrow = [&](int row) -> int64_t {  // expert weight row of block row `row` in group grp0
-        if (GEMM1) {
-            const int h0 = grp0 * HALF;
-            return static_cast<int64_t>(mt.expert) * 2 * a.H + (row < HALF ? h0 + row : a.H + h0 + row - HALF);
-        }
-        return static_cast<int64_t>(mt.expert) * a.D + grp0 * R + row;
-    };
-    // weight DMA: instruction j of a wave covers rows (wave * WINS + j) * WRPI + lane / WCH, WCH chunks each
-    const int64_t rowb = W4 ? K / 2 : K;  // weight row bytes
-    const char* wsrc[C::WINS];
-#pragma unroll
-    for (int j = 0; j < C::WINS; ++j) {
-        const int row = (wave * C::WINS + j) * C::WRPI + lane / C::WCH;
-        const int c = (lane & (C::WCH - 1)) ^ (row & (C::WCH - 1));
-        wsrc[j] = reinterpret_cast<const char*>(wbase) + wrow(row) * rowb + c * 16;
-    }
-    // token DMA: rows (wave * TINS + j) * 2 + lane / 32, 32 chunks each
-    auto trow = [&](int m) -> int64_t {
-        const int mm = m < mt.rows ? m : 0;
-        if (GEMM1) return clamp_pair(a.rv.sorted_to_pair[mt.row0 + mm], a.P) / a.k;
-        return mt.row0 + mm;
-    };
-    const uint8_t* tbase = GEMM1 ? a.x : a.act;
-    const uint8_t* tsbase = GEMM1 ? a.xs : a.act_s;
-    const char* tsrc[C::TINS];
-#pragma unroll
-    for (int j = 0; j < C::TINS; ++j) {
-        const int m = (wave * C::TINS + j) * 2 + lane / 32;
-        const int c = (lane & 31) ^ (m & 31);
-        tsrc[j] = reinterpret_cast<const char*>(tbase) + trow(m) * K + c * 16;
-    }
-    // scale DMA source: wave w < SWAVES lane i -> weight row 64w + i; wave SWAVES lane i -> token row i & 31
-    const char* ssrc = wave < C::SWAVES ? reinterpret_cast<const char*>(wsbase) + wrow(64 * wave + lane) * KB
-                                        : reinterpret_cast<const char*>(tsbase) + trow(lane & 31) * KB;
-    const int64_t wgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * rowb;
-    const int64_t sgroup_stride = static_cast<int64_t>(HALF) * (GEMM1 ? 1 : 2) * KB;
-    const int KIT = K / kMx4KC, NIT = G * KIT;
-    // GEMM2 rotates the order of its groups per block (see dma_skinny_kernel)
-    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;
-    const bool scale_wave = wave <= C::SWAVES;  // moves one scale DMA per stage
-
-    const int lr = lane & 31, g = lane >> 5;
-    // GEMM2 epilogue values of token lr (pair index, routing weight), loaded
-    // before the ring starts (a global load in the loop would come with a
-    // vmcnt(0) wait that drains the wave's DMAs in flight)
-    int ep = 0;
-    float wt = 1.0f;
-    if (!GEMM1) {
-        ep = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (lr < mt.rows ? lr : 0)], a.P);
-        wt = a.wts[ep];
-        asm volatile("" : "+v"(ep), "+v"(wt));
-    }
-    f32x16_t acc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x16_t{};
-#pragma unroll
-    for (int j = 0; j < C::S - 1; ++j)
-        if (j < NIT)
-            mx4_dma_issue<R, W4>(ring, j, (j / KIT + rot) % G, j % KIT, wgroup_stride, sgroup_stride, wsrc, tsrc,
-                                 ssrc);
-    for (int it = 0; it < NIT; ++it) {
-        if (it + C::S - 2 < NIT) {
-            if (scale_wave) wait_vm<(C::S - 2) * (C::WINS + C::TINS + 1)>();
-            else wait_vm<(C::S - 2) * (C::WINS + C::TINS)>();
-        } else {
-            wait_vm<0>();
-        }
-        ring_barrier();
-        if (it + C::S - 1 < NIT) {
-            const int nx = it + C::S - 1;
-            mx4_dma_issue<R, W4>(ring, nx, (nx / KIT + rot) % G, nx % KIT, wgroup_stride, sgroup_stride, wsrc,
-                                 tsrc, ssrc);
-        }
-        uint8_t* slot = ring + (it % C::S) * C::STAGE;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int s = 2 * wave + q;  // this wave's 64-wide K step of the stage
-            const int ct = 4 * s + g;    // token chunks ct and ct + 2 (and e4m3 weight chunks)
-            uint32_t sw[NB], st, as[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) as[b] = lds_addr(slot + C::SW + (32 * b + lr) * 16 + 2 * s + g);
-            const uint32_t atl = lds_addr(slot + C::WB + lr * C::TRB + ((ct ^ lr) << 4));
-            const uint32_t ath = lds_addr(slot + C::WB + lr * C::TRB + (((ct + 2) ^ lr) << 4));
-            const uint32_t ast = lds_addr(slot + C::ST + lr * 16 + 2 * s + g);
-            u32x4_t tlo, thi;
-            i32x8_t aa[NB];
-            if constexpr (W4) {
-                const int cw = 2 * s + g;  // weight chunk (16 bytes = 32 e2m1 values)
-                u32x4_t w[NB];
-                uint32_t aw[NB];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int row = 32 * b + lr;
-                    aw[b] = lds_addr(slot + row * C::WRB + ((cw ^ (row & (C::WCH - 1))) << 4));
-                }
-                mx4_lds_read(w, tlo, thi, sw, st, aw, atl, ath, as, ast);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) aa[b] = i32x8_t{(int)w[b].x, (int)w[b].y, (int)w[b].z, (int)w[b].w, 0, 0, 0, 0};
-            } else {
-                u32x4_t wlo[NB], whi[NB];
-                uint32_t awl[NB], awh[NB];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int row = 32 * b + lr;
-                    awl[b] = lds_addr(slot + row * C::WRB + ((ct ^ (row & (C::WCH - 1))) << 4));
-                    awh[b] = lds_addr(slot + row * C::WRB + (((ct + 2) ^ (row & (C::WCH - 1))) << 4));
-                }
-                mx8_lds_read(wlo, whi, tlo, thi, sw, st, awl, awh, atl, ath, as, ast);
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    aa[b] = i32x8_t{(int)wlo[b].x, (int)wlo[b].y, (int)wlo[b].z, (int)wlo[b].w,
-                                    (int)whi[b].x, (int)whi[b].y, (int)whi[b].z, (int)whi[b].w};
-            }
-            const i32x8_t bt{(int)tlo.x, (int)tlo.y, (int)tlo.z, (int)tlo.w, (int)thi.x, (int)thi.y, (int)thi.z, (int)thi.w};
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aa[b], bt, acc[b], W4 ? 4 : 0, 0, 0, (int)sw[b],
-                                                                         0, (int)st);
-        }
-        if (it % KIT != KIT - 1) continue;
-        // group finished: the four waves' partial sums meet in this slot, two
-        // row blocks per pass. acc[b][v]: token lr, row 32b + 8(v/4) + 4g + (v%4).
-        float* red = reinterpret_cast<float*>(slot);
-        const int gidx = grp0 + (it / KIT + rot) % G;
-        const int tok = lr;
-#pragma unroll
-        for (int pass = 0; pass < NB / 2; ++pass) {
-            // GEMM1 pass p holds the gate and up blocks of act columns 32p..32p+31
-            // (blocks p and NB/2 + p); GEMM2 pass p holds blocks 2p and 2p + 1
-            const int b0 = GEMM1 ? pass : 2 * pass, b1 = GEMM1 ? NB / 2 + pass : 2 * pass + 1;
-            lds_barrier();
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                red[(wave * 32 + v) * 64 + lane] = acc[b0][v];
-                red[(wave * 32 + 16 + v) * 64 + lane] = acc[b1][v];
-            }
-            lds_barrier();
-            auto sum = [&](int i) {  // i: 0..31 (16 * half + v)
-                return (red[(0 * 32 + i) * 64 + lane] + red[(1 * 32 + i) * 64 + lane]) +
-                       (red[(2 * 32 + i) * 64 + lane] + red[(3 * 32 + i) * 64 + lane]);
-            };
-            if ((GEMM1 ? wave == 0 : wave < 2) && tok < mt.rows) {
-                if (GEMM1) {
-                    float act[16];
-                    float amax = 0.0f;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float gt = sum(v), up = sum(16 + v);
-                        act[v] = gt / (1.0f + __expf(-gt)) * up;
-                        amax = fmaxf(amax, fabsf(act[v]));
-                    }
-                    amax = fmaxf(amax, __shfl_xor(amax, 32));
-                    const int sc = mx_scale_exp(amax);
-                    const float inv = pow2f(-sc);
-                    const int64_t row = mt.row0 + tok;
-                    const int col0 = gidx * HALF + 32 * pass;  // this pass's 32 act columns: one scale block
-                    uint8_t* dst = a.act + row * a.H + col0 + 4 * g;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const uint32_t code = e4m3_encode(act[4 * q4] * inv, act[4 * q4]) |
-                                              (e4m3_encode(act[4 * q4 + 1] * inv, act[4 * q4 + 1]) << 8) |
-                                              (e4m3_encode(act[4 * q4 + 2] * inv, act[4 * q4 + 2]) << 16) |
-                                              (e4m3_encode(act[4 * q4 + 3] * inv, act[4 * q4 + 3]) << 24);
-                        *reinterpret_cast<uint32_t*>(dst + 8 * q4) = code;
-                    }
-                    if (g == 0) a.act_s[row * (a.H / 32) + col0 / 32] = static_cast<uint8_t>(sc + 127);
-                } else {
-                    const int half = wave;  // wave 0: block b0, wave 1: block b1
-                    uint16_t* dst = a.ypair + static_cast<int64_t>(ep) * a.D + gidx * R + 32 * (half ? b1 : b0) + 4 * g;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        float y[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) y[j] = sum(16 * half + 4 * q4 + j) * wt;
-                        *reinterpret_cast<uint2*>(dst + 8 * q4) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b] = f32x16_t{};
-    }
-}
 
 // Four k-steps' operands from LDS and a wait for them: two 16-byte chunks
 // and one scale byte each (e4m3 weights, or the token fragments); asm for
@@ -1433,8 +1134,10 @@ __device__ __forceinline__ void lds_load4_f32(float (&v)[4], const uint32_t (&p)
 }
 
 // Most row groups an MX k-major block keeps accumulators for at once (e2m1
-// weights hold twice the token fragments, eight k-steps per wave).
-constexpr int mx_kmajor_groups(bool w4) { return w4 ? 6 : 8; }
+// weights hold twice the token fragments, eight k-steps per wave). With at
+// least four groups to a block, cutting them into super-groups of at most 7
+// or 8 leaves at least four in each.
+constexpr int mx_kmajor_groups(bool w4) { return w4 ? 7 : 8; }
 
 // The MX decode GEMMs, k-major (the order of dma_kmajor_kernel): a block
 // (m-tile, G row groups, G >= 4) walks K in 512-value chunks and, within a
@@ -1453,7 +1156,7 @@ constexpr int mx_kmajor_groups(bool w4) { return w4 ? 6 : 8; }
 // 32-row block yields 16 act columns (half an MX scale block: the two waves
 // of a scale block swap their row maxima through LDS).
 template <int R, bool W4, bool GEMM1>
-__global__ __launch_bounds__(kThreads) void mx_kmajor_kernel(MxArgs a, int G, int nsg) {
+__global__ __launch_bounds__(kThreads) void mx_kmajor_kernel(MxArgs a) {
     using C = Mx4<R, W4>;
     constexpr int SW = 4, NB = R / 32, KP = 4 / NB, NSK = 8 / KP;  // k-steps per wave per stage
     constexpr int GSM = mx_kmajor_groups(W4);
@@ -1465,15 +1168,17 @@ __global__ __launch_bounds__(kThreads) void mx_kmajor_kernel(MxArgs a, int G, in
     __shared__ __attribute__((aligned(16))) uint8_t lds[SW * WSLOT + TSLOT];
     __shared__ float xamax[2][4][32];  // GEMM1: per token, the act maximum of each wave's 16 columns
     uint8_t* const tslot = lds + SW * WSLOT;
+    DecodeWork wk;  // at least four row groups: every super-group then holds at least four
+    if (!decode_work<4>(a.rv, a.E, GEMM1 ? a.H / (R / 2) : a.D / R, wk)) return;
     MTile mt;
-    const BlockPos bp = block_pos((GEMM1 ? a.H / (R / 2) : a.D / R) / G);
-    if (!find_mtile<kMx4BM>(a.rv, a.E, bp.mtile, mt)) return;
+    if (!find_mtile<kMx4BM>(a.rv, a.E, wk.mtile, mt)) return;
+    const int G = wk.n, nsg = (G + GSM - 1) / GSM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rb = wave % NB, kp = wave / NB;
     const int lr = lane & 31, g = lane >> 5;
     const int K = GEMM1 ? a.D : a.H;
     const int KB = K / 32;  // scale bytes per row
-    const int grp0 = bp.chunk * G;
+    const int grp0 = wk.g0;
     const uint8_t* wbase = GEMM1 ? a.w1 : a.w2;
     const uint8_t* wsbase = GEMM1 ? a.w1s : a.w2s;
     auto wrow = [&](int r) -> int64_t {  // expert weight row of slot row r in group grp0
@@ -1516,8 +1221,8 @@ __global__ __launch_bounds__(kThreads) void mx_kmajor_kernel(MxArgs a, int G, in
     const int64_t wgroup_stride = static_cast<int64_t>(GEMM1 ? R / 2 : R) * rowb;
     const int64_t sgroup_stride = static_cast<int64_t>(GEMM1 ? R / 2 : R) * KB;
     const int KIT = K / kMx4KC, NIT = G * KIT;
-    const int rot = GEMM1 ? 0 : (bp.mtile + bp.chunk) % G;  // as in dma_skinny_kernel
-    const int kc0 = static_cast<int>(blockIdx.x) % KIT;     // as in dma_kmajor_kernel
+    const int rot = GEMM1 ? 0 : static_cast<int>(blockIdx.x) % G;  // as in dma_skinny_kernel
+    const int kc0 = static_cast<int>(blockIdx.x) % KIT;               // as in dma_kmajor_kernel
     const KmajorPlan pl{G / nsg, G % nsg, KIT};
     int ep = 0;
     float wt = 1.0f;
@@ -1738,47 +1443,17 @@ bool skinny_mx_supported(const MxArgs& a) {
            a.D % R == 0;
 }
 
-// The MX decode kernel a GEMM runs: mx_kmajor_kernel when every super-group
-// of a block holds at least four row groups (its token slot is reused every
-// four stages), else mx_skinny_kernel.
-static int mx_groups_per_block(const MxArgs& a, bool gemm1) {
-    const int R = a.w4 ? 128 : 64;
-    return groups_per_block(gemm1 ? a.H / (R / 2) : a.D / R, a.T, a.k, a.E);
-}
-
-static int mx_super_groups(const MxArgs& a, int G) {
-    const int gsm = mx_kmajor_groups(a.w4);
-    return (G + gsm - 1) / gsm;
-}
-
-static bool mx_uses_kmajor(const MxArgs& a, int G) { return G / mx_super_groups(a, G) >= 4; }
-
-const char* mx_decode_kernel_name(const MxArgs& a, bool gemm1) {
-    return mx_uses_kmajor(a, mx_groups_per_block(a, gemm1)) ? "mx_kmajor_kernel" : "mx_skinny_kernel";
-}
+const char* mx_decode_kernel_name(const MxArgs&, bool) { return "mx_kmajor_kernel"; }
 
 hipError_t launch_skinny_mx(const MxArgs& a, bool gemm1, hipStream_t s) {
-    const int R = a.w4 ? 128 : 64;
-    const int groups = gemm1 ? a.H / (R / 2) : a.D / R;
-    const int G = mx_groups_per_block(a, gemm1);
-    const unsigned g = static_cast<unsigned>(mtiles_upper(a.P, a.E, kMx4BM)) * (groups / G);
-    if (mx_uses_kmajor(a, G)) {
-        const int nsg = mx_super_groups(a, G);
-        if (a.w4) {
-            if (gemm1) mx_kmajor_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G, nsg);
-            else mx_kmajor_kernel<128, true, false><<<g, kThreads, 0, s>>>(a, G, nsg);
-        } else {
-            if (gemm1) mx_kmajor_kernel<64, false, true><<<g, kThreads, 0, s>>>(a, G, nsg);
-            else mx_kmajor_kernel<64, false, false><<<g, kThreads, 0, s>>>(a, G, nsg);
-        }
-        return hipGetLastError();
-    }
+    // one block per CU, or one per m-tile when there can be more (decode_work)
+    const unsigned g = static_cast<unsigned>(std::max(device_cu_count(), mtiles_upper(a.P, a.E, kMx4BM)));
     if (a.w4) {
-        if (gemm1) mx_skinny_kernel<128, true, true><<<g, kThreads, 0, s>>>(a, G);
-        else mx_skinny_kernel<128, false, true><<<g, kThreads, 0, s>>>(a, G);
+        if (gemm1) mx_kmajor_kernel<128, true, true><<<g, kThreads, 0, s>>>(a);
+        else mx_kmajor_kernel<128, true, false><<<g, kThreads, 0, s>>>(a);
     } else {
-        if (gemm1) mx_skinny_kernel<64, true, false><<<g, kThreads, 0, s>>>(a, G);
-        else mx_skinny_kernel<64, false, false><<<g, kThreads, 0, s>>>(a, G);
+        if (gemm1) mx_kmajor_kernel<64, false, true><<<g, kThreads, 0, s>>>(a);
+        else mx_kmajor_kernel<64, false, false><<<g, kThreads, 0, s>>>(a);
     }
     return hipGetLastError();
 }

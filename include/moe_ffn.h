@@ -108,7 +108,7 @@ MOE_FFN_API int moe_ffn_resolve_mode(const moe_ffn_problem* p, int mode);
  * the pipeline `mode` resolves to, as a static NUL-terminated name (owned by
  * the library, never freed): "dma_kmajor_kernel", "dma_skinny_kernel",
  * "big_gemm_kernel<128>", "big_gemm_kernel<256>", "gemm1_swiglu_kernel",
- * "gemm2_weight_kernel", "mx_kmajor_kernel", "mx_skinny_kernel", "mx_gemm1_kernel",
+ * "gemm2_weight_kernel", "mx_kmajor_kernel", "mx_gemm1_kernel",
  * "mx_gemm2_kernel", "fused_dma_kernel", "fused_bf16_kernel",
  * "mx_fused_kernel", or "none" for
  * T = 0. NULL on an invalid problem, mode or gemm. Host only: it evaluates

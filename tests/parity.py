@@ -71,7 +71,7 @@ def sample_tokens(cfg: mi.Config, ids: np.ndarray, n: int, seed: int = 0) -> np.
 # Token rows per m-tile of each GEMM kernel family the dispatch can pick
 # (the names moe_ffn_gemm_kernel reports).
 TILE_ROWS = {
-    "dma_kmajor_kernel": 32, "dma_skinny_kernel": 32, "mx_skinny_kernel": 32, "mx_kmajor_kernel": 32,
+    "dma_kmajor_kernel": 32, "dma_skinny_kernel": 32, "mx_kmajor_kernel": 32,
     "big_gemm_kernel<128>": 128, "big_gemm_kernel<256>": 256,
     "gemm1_swiglu_kernel": 128, "gemm2_weight_kernel": 128,
     "mx_gemm1_kernel": 128, "mx_gemm2_kernel": 128,

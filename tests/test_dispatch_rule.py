@@ -21,7 +21,7 @@ def test_decode_rule_matches_binomial_tail(T, k, E):
     want = T * p <= 32 and E * binom.sf(32, T, p) < 0.5
     got = _kernel(T, 2048, 1024, E, k) == "dma_kmajor_kernel"
     assert got == want
-    mx = _kernel(T, 2048, 1024, E, k, dtype="mxfp8") in ("mx_kmajor_kernel", "mx_skinny_kernel")
+    mx = _kernel(T, 2048, 1024, E, k, dtype="mxfp8") == "mx_kmajor_kernel"
     assert mx == want
 
 
@@ -42,7 +42,7 @@ def test_workload_paths():
     assert _kernel(1024, 4096, 1536, 64, 6, dtype="mxfp8") == "mx_gemm1_kernel"        # 96 rows/expert
     assert _kernel(64, 4096, 1536, 64, 6, dtype="mxfp8") == "mx_kmajor_kernel"     # 12 row groups per block
     assert _kernel(64, 6144, 2048, 32, 8, dtype="mxfp4", gemm=2) == "mx_kmajor_kernel"
-    assert _kernel(64, 512, 512, 32, 8, dtype="mxfp8") == "mx_skinny_kernel"      # 2 row groups per block
+    assert _kernel(64, 512, 512, 32, 8, dtype="mxfp8") == "mx_kmajor_kernel"      # 16 and 8 row groups
     assert _kernel(64, 256, 512, 8, 2, dtype="mxfp8", mode="fused") == "mx_fused_kernel"
     # E = 1 (one group of every token): the decode kernels while the prefill
     # ring would get fewer tiles than half of the 256 compute units

@@ -94,25 +94,26 @@ def test_mx_forward_prefill_tiles(T, D, H, E, k, routing, grid_limit, monkeypatc
 
 
 @pytest.mark.parametrize("T,D,H,E,k,routing", [
-    (64, 512, 512, 8, 2, "softmax"),     # decode kernel: one K stage per 512, one row group per block
+    (64, 512, 512, 8, 2, "softmax"),     # one K stage per 512; 8 m-tiles, each with 4 of its row groups per block
     (1, 512, 512, 4, 2, "uniform"),      # one token
     (60, 1024, 512, 16, 4, "zipf"),      # ragged, several K stages
     (128, 512, 1024, 16, 2, "zipf"),     # skewed: experts with several 32-row m-tiles
-    (64, 512, 512, 32, 8, "softmax"),    # several row groups per block
+    (64, 512, 512, 32, 8, "softmax"),    # 32 m-tiles
 ])
 def test_mx_decode_kernel(T, D, H, E, k, routing):
     """Shapes the decode-shaped MX kernel takes with e4m3 weights (fewer than 0.5
     experts expected past 32 rows, D and H multiples of 512)."""
     import grouped_gemm_amd as g
     for gemm in (1, 2):
-        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp8", "split", gemm) == "mx_skinny_kernel"
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp8", "split", gemm) == "mx_kmajor_kernel"
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
 @pytest.mark.parametrize("T,D,H,E,k,routing,gemms", [
     (16, 2048, 1024, 32, 8, "uniform", (1, 2)),   # 4 row groups per block (the fewest it takes)
     (64, 1024, 2048, 32, 8, "softmax", (1,)),     # GEMM1: 8 groups, one super-group
-    (64, 4096, 1536, 64, 6, "zipf", (1, 2)),      # 6 + 6 and 8 + 8 groups, skewed: extra m-tiles
+    (64, 4096, 1536, 64, 6, "zipf", (1, 2)),      # 12 and 16 groups (6 + 6, 8 + 8) and more; skewed: extra m-tiles
+    (64, 512, 512, 512, 8, "uniform", (1, 2)),    # more m-tiles than CUs: a block per m-tile, all its groups
 ])
 def test_mx_kmajor_decode_kernel(T, D, H, E, k, routing, gemms):
     """The k-major MX decode GEMMs (e4m3 weights: two 32-row blocks per group,
@@ -174,7 +175,7 @@ def test_mx_fused_config_sampled():
 
 @pytest.mark.parametrize("mode", ["split", "fused"])
 @pytest.mark.parametrize("T,D,H,E,k,kernel", [
-    (32, 512, 512, 8, 3, "mx_skinny_kernel"),       # decode kernel
+    (32, 512, 512, 8, 3, "mx_kmajor_kernel"),       # decode kernel
     (2100, 256, 512, 3, 2, "big_gemm_kernel<256>"), # prefill ring
     (300, 384, 640, 16, 4, "mx_gemm1_kernel"),      # generic kernels
 ])

@@ -100,24 +100,24 @@ def test_mxfp4_forward_matches_oracle(T, D, H, E, k, routing):
 
 
 @pytest.mark.parametrize("T,D,H,E,k,routing", [
-    (64, 512, 512, 8, 2, "softmax"),     # decode kernel: one K stage per 512, one group per block
+    (64, 512, 512, 8, 2, "softmax"),     # one K stage per 512; 8 m-tiles, 4 row groups per block
     (1, 512, 512, 4, 2, "uniform"),      # one token
     (60, 1024, 512, 16, 4, "zipf"),      # ragged, several K stages
     (128, 512, 1024, 16, 2, "zipf"),     # skewed: experts with several 32-row m-tiles
-    (64, 512, 512, 32, 8, "softmax"),    # several row groups per block (GEMM1)
+    (64, 512, 512, 32, 8, "softmax"),    # 32 m-tiles
 ])
 def test_mxfp4_decode_kernel_matches_oracle(T, D, H, E, k, routing):
     """Shapes the decode-shaped MXFP4 kernel takes (fewer than 0.5 experts expected
     past 32 rows, D and H multiples of 512)."""
     import grouped_gemm_amd as g
     for gemm in (1, 2):
-        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp4", "split", gemm) == "mx_skinny_kernel"
+        assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp4", "split", gemm) == "mx_kmajor_kernel"
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"))
 
 
 @pytest.mark.parametrize("T,D,H,E,k,routing,gemms", [
     (64, 1024, 2048, 32, 8, "softmax", (1,)),     # GEMM1: 4 row groups per block (the fewest it takes)
-    (64, 4096, 1536, 64, 6, "zipf", (1, 2)),      # 6 groups, and 4 + 4; skewed: extra m-tiles
+    (64, 4096, 1536, 64, 6, "zipf", (1, 2)),      # 4 or 8 groups (4 + 4) per block; skewed: extra m-tiles
 ])
 def test_mxfp4_kmajor_decode_kernel(T, D, H, E, k, routing, gemms):
     """The k-major MX decode GEMMs with e2m1 weights (four 32-row blocks per
