@@ -28,7 +28,7 @@ def _load(dst: dict, d: dict):
     dst["wts"].copy_(to_gpu(d["topk_weights"]))
 
 
-def _graph_case(cfg, mode, seeds=(3, 4, 5)):
+def _graph_case(cfg, mode, seeds=(3, 4, 5), mutate=None):
     import grouped_gemm_amd as g
     print(f"graph {cfg.name} T={cfg.T} D={cfg.D} H={cfg.H} E={cfg.E} k={cfg.k} mode={mode}", flush=True)
     dev = torch.device("cuda:0")
@@ -57,6 +57,8 @@ def _graph_case(cfg, mode, seeds=(3, 4, 5)):
 
     for i, seed in enumerate(seeds):
         d = mi.make_bf16(cfg, seed)
+        if mutate is not None:
+            mutate(i, d)
         _load(buf, d)
         # eager work of the program's own between replays: the same pass eagerly,
         # on other output and workspace buffers
@@ -88,3 +90,17 @@ def _graph_case(cfg, mode, seeds=(3, 4, 5)):
 ])
 def test_forward_graph_replays_match_eager(T, D, H, E, k, routing, mode):
     _graph_case(mi.custom(T, D, H, E, k, routing), mode)
+
+
+def test_graph_replays_follow_the_routing():
+    """One capture, replays whose routing differs in how many m-tiles it makes:
+    the decode kernels read the m-tile count the route step produces and deal
+    their blocks out on the device, so a replay with a hot expert (two 32-row
+    m-tiles) must match an eager pass as bit-exactly as one without."""
+    def hot(i, d):
+        if i % 2 == 1:  # replays 1 (and 3): expert 5 takes 56 of the 64 tokens
+            ids = d["topk_ids"]
+            sel = np.arange(ids.shape[0]) < 56
+            ids[sel, 0] = 5
+            ids[sel, 1:] = np.where(ids[sel, 1:] == 5, 6, ids[sel, 1:])
+    _graph_case(mi.custom(64, 512, 512, 16, 4, "uniform"), "split", seeds=(3, 4, 5, 6), mutate=hot)
