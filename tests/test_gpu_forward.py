@@ -87,6 +87,25 @@ def test_dropped_and_zero_weight_routes(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("T,D,H,E,k", [
+    (64, 512, 512, 16, 4),     # decode kernels: the route leaves no m-tile, every block of the grid exits
+    (2100, 256, 384, 3, 2),    # prefill kernels: an empty tile table
+])
+def test_every_route_dropped(mode, T, D, H, E, k):
+    """Every id out of range: no pair reaches an expert, and the output is all zeros
+    (it is still written in full: it starts as NaN here)."""
+    import grouped_gemm_amd as g
+    d = mi.make_bf16(mi.custom(T, D, H, E, k, "uniform"), 9)
+    d["topk_ids"][:, :] = -1
+    d["topk_ids"][::2, 0] = E               # == E: dropped as well
+    t = upload_bf16(d)
+    out = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    g.moe_ffn_forward(t["x"], t["w1"], t["w2"], t["topk_ids"], t["topk_weights"], out=out, mode=mode)
+    torch.cuda.synchronize()
+    assert np.all(gpu_bf16_to_f64(out) == 0)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_decode_config_full(mode):
     _case(mi.CONFIGS[2], mode)
 
