@@ -173,9 +173,14 @@ def source_digest(symbol: str) -> str:
 def kernel_symbol(cfg, mode, stage):
     """The HIP kernel a stage runs for this workload (the GEMM stages ask the
     library's own dispatch, moe_ffn_gemm_kernel)."""
-    if mode == "fused" and stage != "fused_ffn":
-        return {"acc_fill": "fill_zero_f32_kernel", "acc_to_bf16": "f32_to_bf16_kernel",
-                "route": "route kernels"}[stage]
+    if mode == "fused" and stage == "route":
+        return "route kernels (their extra blocks clear the accumulator)"
+    if mode == "fused" and stage == "acc_fill":
+        return "none (the route kernels clear the accumulator)"
+    if mode == "fused" and stage == "acc_to_bf16":
+        if kernel_symbol(cfg, mode, "fused_ffn") == "fused_dma_kernel":
+            return "none (fused_dma_kernel converts each completed token row)"
+        return "f32_to_bf16_kernel"
     if stage == "route":
         if cfg.P <= 256 and cfg.E <= 64:
             return "route_wave_kernel"

@@ -81,7 +81,7 @@ struct Plan {
     int mode;
     RoutePlan route;
     size_t counts, offsets, s2p, p2s;
-    size_t act, act_s, ypair, acc32, mtiles;
+    size_t act, act_s, ypair, acc32, tcnt, clear_end, mtiles;
     size_t total;
 };
 
@@ -113,8 +113,13 @@ Plan make_plan(const moe_ffn_problem* p, int mode) {
         pl.mtiles = off;
         off = align_up(off + static_cast<size_t>(moe::big_gemm_workspace_bytes(P, p->E)));
     } else {
+        // the accumulator, then the per-token counters; the route step clears both
         pl.acc32 = off;
-        off = align_up(off + 4 * static_cast<size_t>(p->T) * p->D);
+        off += 4 * static_cast<size_t>(p->T) * p->D;
+        pl.tcnt = off;
+        off += (4 * static_cast<size_t>(p->T) + 15) & ~size_t(15);
+        pl.clear_end = off;
+        off = align_up(off);
     }
     pl.total = off;
     return pl;
@@ -452,6 +457,10 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
     moe::RouteBuffers rb{topk_ids, P, p->E, pl.route.S, pl.route.seg, at<int32_t>(ws, pl.route.seg_counts),
                          at<int32_t>(ws, pl.counts), at<int32_t>(ws, pl.offsets),
                          at<int32_t>(ws, pl.route.tile_prefix), at<int32_t>(ws, pl.s2p), at<int32_t>(ws, pl.p2s)};
+    if (m == MOE_FFN_FUSED) {
+        rb.clear = at<float>(ws, pl.acc32);
+        rb.clear_n = static_cast<int64_t>((pl.clear_end - pl.acc32) / 4);
+    }
     const hipError_t re = logits ? moe::launch_router_route(logits, p->T, p->E, p->topk, const_cast<int32_t*>(topk_ids),
                                                             const_cast<float*>(topk_weights), rb, st)
                                  : moe::launch_route(rb, st);
@@ -479,6 +488,7 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
             e = moe::launch_split_bf16(a, st, stage_ev);
         } else {
             a.acc32 = at<float>(ws, pl.acc32);
+            a.tcnt = at<int32_t>(ws, pl.tcnt);
             e = moe::launch_fused_bf16(a, st, stage_ev);
         }
     } else {

@@ -122,6 +122,8 @@ struct RouteBuffers {
     int32_t* tile_prefix;
     int32_t* sorted_to_pair;
     int32_t* pair_to_sorted;
+    float* clear = nullptr;   // clear_n floats (a multiple of 4) the route step sets to zero, or null
+    int64_t clear_n = 0;
 };
 hipError_t launch_route(const RouteBuffers& b, hipStream_t s);
 // True when launch_route takes its multi-kernel path (segment histogram,
@@ -147,6 +149,7 @@ struct Bf16Args {
     uint16_t* ypair;   // [P, D]   split only: weighted expert outputs in pair order
     int32_t* mtiles;   // split only: big_gemm_workspace_bytes for the prefill GEMMs
     float* acc32;      // [T, D]   fused only
+    int32_t* tcnt;     // [T]      fused only: partial rows added per token (zero at entry)
     uint16_t* out;     // [T, D]
     const uint16_t* shared_y;  // [T, D] or null: a shared expert's output, added to each token's sum
     ActVariant av;             // zero: the plain SwiGLU
@@ -236,7 +239,6 @@ hipError_t launch_big_mx(const MxArgs& a, bool gemm1, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* ypair, const int32_t* pair_to_sorted, int32_t T, int32_t k,
                           int32_t D, uint16_t* out, hipStream_t s);
-hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_mx_quantize(const float* src, int64_t rows, int32_t K, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);

@@ -416,11 +416,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_f32_kernel(float4* p, int64_t n4) {
-    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256)
-        p[i] = float4{0.f, 0.f, 0.f, 0.f};
-}
-
 // dst = bf16(src [+ extra]), 4 values per thread; extra (nullable) is bf16.
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* src, const uint2* extra, uint2* dst,
                                                           int64_t n4) {
@@ -526,18 +521,22 @@ hipError_t launch_identity_route(int64_t T, int32_t* counts, int32_t* offsets, i
     return hipGetLastError();
 }
 
+// The route step has cleared acc32 and the token counters. The decode-ring
+// kernel converts each token's row itself once it is complete; the generic
+// kernel leaves the conversion to a kernel of its own.
 hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128, BH = 64;
     const int64_t n = static_cast<int64_t>(a.T) * a.D;
-    fill_zero_f32_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<float4*>(a.acc32), n / 4);
     record(ev, 0, s);
     if (fused_decode_supported(a)) {
         launch_fused_decode(a, s);
-    } else {
-        dim3 g(mtiles_upper(a.P, a.E, BM), a.H / BH);
-        if (a.D % 128 == 0) fused_bf16_kernel<BM, BH, 128><<<g, kThreads, 0, s>>>(a);
-        else fused_bf16_kernel<BM, BH, 64><<<g, kThreads, 0, s>>>(a);
+        record(ev, 1, s);
+        record(ev, 2, s);
+        return hipGetLastError();
     }
+    dim3 g(mtiles_upper(a.P, a.E, BM), a.H / BH);
+    if (a.D % 128 == 0) fused_bf16_kernel<BM, BH, 128><<<g, kThreads, 0, s>>>(a);
+    else fused_bf16_kernel<BM, BH, 64><<<g, kThreads, 0, s>>>(a);
     record(ev, 1, s);
     f32_to_bf16_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<const float4*>(a.acc32),
                                                              reinterpret_cast<const uint2*>(a.shared_y),
@@ -550,11 +549,6 @@ hipError_t launch_combine(const uint16_t* ypair, const int32_t* p2s, int32_t T, 
                           uint16_t* out, hipStream_t s) {
     combine_kernel<<<grid_for(static_cast<int64_t>(T) * D / 8, 256, kCombineMaxBlocks), 256, 0, s>>>(
         ypair, p2s, T, k, D, nullptr, out);
-    return hipGetLastError();
-}
-
-hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s) {
-    fill_zero_f32_kernel<<<grid_for(n / 4, 256), 256, 0, s>>>(reinterpret_cast<float4*>(p), n / 4);
     return hipGetLastError();
 }
 

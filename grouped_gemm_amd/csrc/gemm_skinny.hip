@@ -689,6 +689,22 @@ struct FusedTile {
     static_assert(BH == 128 || BH == 256, "128- or 256-wide slices");
 };
 
+// Plain LDS loads of four floats, written as asm: the compiler, which cannot
+// tell an LDS tile from the ring slots DMAs are filling, would put a
+// vmcnt(0) wait (draining the ring, and any atomics in flight) before its
+// own accesses.
+__device__ __forceinline__ void lds_load4_f32(float (&v)[4], const uint32_t (&p)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\t"
+        "ds_read_b32 %1, %5\n\t"
+        "ds_read_b32 %2, %6\n\t"
+        "ds_read_b32 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+
 __device__ __forceinline__ void lds_read3(bf16x8_t (&f)[3], const uint32_t (&p)[3]) {
     asm volatile(
         "ds_read_b128 %0, %3\n\t"
@@ -712,6 +728,21 @@ __device__ __forceinline__ void lds_read4(bf16x8_t (&f)[4], const uint32_t (&p)[
         : "memory");
 }
 
+// Tokens none of whose routes reach an expert get no partial rows: their
+// output is the shared expert's row, or zeros. Block b takes tokens b,
+// b + gridDim.x, ...
+__device__ void fused_write_unrouted(const Bf16Args& a) {
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+        int nv = 0;
+        for (int j = 0; j < a.k; ++j) nv += a.rv.pair_to_sorted[static_cast<int64_t>(t) * a.k + j] >= 0;
+        if (nv) continue;
+        const int64_t row = static_cast<int64_t>(t) * a.D;
+        for (int c = threadIdx.x; c < a.D / 8; c += kThreads)
+            *reinterpret_cast<u32x4_t*>(a.out + row + 8 * c) =
+                a.shared_y ? *reinterpret_cast<const u32x4_t*>(a.shared_y + row + 8 * c) : u32x4_t{0, 0, 0, 0};
+    }
+}
+
 // grid: (m-tiles x slices), the slices of one m-tile consecutive.
 template <int BH, int SW>
 __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
@@ -726,13 +757,18 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT + F::STG];
     __shared__ int64_t sRow[32];  // acc32 row offset (token * D) of each m-tile row
     __shared__ float sW[32];      // its routing weight (0 past the tile's rows)
+    __shared__ int sTok[32];      // its token
+    __shared__ int sDone[33];     // [32]: count of the tokens whose rows this block completes, then the tokens
     uint8_t* const tring = lds + SW * T::W_BYTES;
     uint8_t* const act = tring + 2 * T::T_BYTES;
     float* const stg = reinterpret_cast<float*>(act + F::ACT);
     const int nslices = a.H / BH;
     const int slice = blockIdx.x % nslices;
     MTile mt;
-    if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+    if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) {
+        fused_write_unrouted(a);
+        return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool wmover = wave < 2;
     const int mw = wave & 1;
@@ -744,6 +780,8 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
         const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
         sRow[m] = static_cast<int64_t>(p / a.k) * a.D;
         sW[m] = m < mt.rows ? a.wts[p] : 0.0f;
+        sTok[m] = p / a.k;
+        if (m == 0) sDone[32] = 0;
     }
     const char* src[W_INS];
     if (wmover) {
@@ -935,13 +973,67 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
         if (!wmover) {
             const int d0 = ((it - NIT1 + rot) % NG2) * F::R2;
             const int i = threadIdx.x - 128;
-#pragma unroll 4
-            for (int j = 0; j < F::R2 / 4; ++j) {
-                const int idx = j * 128 + i, m = idx / F::R2, d = idx % F::R2;
-                if (m < mt.rows) unsafeAtomicAdd(a.acc32 + sRow[m] + d0 + d, sW[m] * stg[m * F::STG_ROW + d]);
+            // the staging reads in asm: the compiler would make each one wait
+            // for every vector memory operation in flight (it cannot tell the
+            // staging tile from the ring slots the DMAs write)
+            for (int j0 = 0; j0 < F::R2 / 4; j0 += 4) {
+                int mm[4], dd[4];
+                uint32_t pa[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int idx = (j0 + u) * 128 + i;
+                    mm[u] = idx / F::R2;
+                    dd[u] = idx % F::R2;
+                    pa[u] = lds_addr(stg + mm[u] * F::STG_ROW + dd[u]);
+                }
+                float v[4];
+                lds_load4_f32(v, pa);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (mm[u] < mt.rows) unsafeAtomicAdd(a.acc32 + sRow[mm[u]] + d0 + dd[u], sW[mm[u]] * v[u]);
             }
         }
     }
+    // A token's row is complete once each of its routed pairs has had all
+    // H / BH slices' partials added. The token waves count this block's
+    // partial rows per token once their adds are acknowledged (the adds and
+    // the counts are device-scope atomics, performed where every XCD sees
+    // them); the block whose count completes a row reads it back with
+    // device-scope loads and converts it to bf16, plus the shared expert's
+    // row, into `out`. No block waits on another, and no cache is written
+    // back or invalidated.
+    if (!wmover) wait_vm<0>();
+    __syncthreads();
+    if (wave == 2 && lane < mt.rows) {
+        const int t = sTok[lane];
+        int nv = 0;
+        for (int j = 0; j < a.k; ++j) nv += a.rv.pair_to_sorted[static_cast<int64_t>(t) * a.k + j] >= 0;
+        if (atomicAdd(a.tcnt + t, 1) + 1 == nv * nslices) sDone[atomicAdd(&sDone[32], 1)] = t;
+    }
+    __syncthreads();
+    const int ndone = sDone[32];
+    if (ndone) {
+        for (int i = 0; i < ndone; ++i) {
+            const int64_t row = static_cast<int64_t>(sDone[i]) * a.D;
+            for (int c = threadIdx.x; c < a.D / 4; c += kThreads) {
+                const float* src = a.acc32 + row + 4 * c;
+                float4 v;
+                v.x = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v.y = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v.z = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v.w = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (a.shared_y) {
+                    const uint2 e = *reinterpret_cast<const uint2*>(a.shared_y + row + 4 * c);
+                    v.x += bf16_to_f32(static_cast<uint16_t>(e.x & 0xffffu));
+                    v.y += bf16_to_f32(static_cast<uint16_t>(e.x >> 16));
+                    v.z += bf16_to_f32(static_cast<uint16_t>(e.y & 0xffffu));
+                    v.w += bf16_to_f32(static_cast<uint16_t>(e.y >> 16));
+                }
+                *reinterpret_cast<uint2*>(a.out + row + 4 * c) = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+            }
+        }
+    }
+    fused_write_unrouted(a);
 }
 
 inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
@@ -1115,22 +1207,10 @@ __device__ __forceinline__ void mxk_read4x1(u32x4_t (&w)[4], uint32_t (&sc)[4], 
         : "memory");
 }
 
-// Plain LDS stores and loads of floats in a ring slot, written as asm: the
-// compiler, which cannot tell that slot from the ones DMAs are filling,
-// would put a vmcnt(0) wait (draining the ring) before its own accesses.
+// A plain LDS store of a float in a ring slot, written as asm (as
+// lds_load4_f32: the compiler would drain the ring before its own access).
 __device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
-}
-__device__ __forceinline__ void lds_load4_f32(float (&v)[4], const uint32_t (&p)[4]) {
-    asm volatile(
-        "ds_read_b32 %0, %4\n\t"
-        "ds_read_b32 %1, %5\n\t"
-        "ds_read_b32 %2, %6\n\t"
-        "ds_read_b32 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
-        : "memory");
 }
 
 // Most row groups an MX k-major block keeps accumulators for at once (e2m1

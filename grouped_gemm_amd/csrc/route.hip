@@ -52,6 +52,24 @@ __device__ __forceinline__ int block_excl_scan(int v, int& total, int* sh) {
     return wbase + incl - v;
 }
 
+// Extra blocks of a route kernel (blockIdx.x >= first) store zeros over n
+// floats at p (n a multiple of 4): the fused pipeline's accumulator and its
+// token counters are cleared alongside the route step, with no kernel of
+// their own.
+__device__ __forceinline__ void clear_blocks(float* p, int64_t n, int first) {
+    float4* q = reinterpret_cast<float4*>(p);
+    const int64_t n4 = n / 4, stride = static_cast<int64_t>(gridDim.x - first) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x - first) * blockDim.x + threadIdx.x; i < n4; i += stride)
+        q[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Blocks of `threads` that clear n floats at about four float4 stores per thread.
+inline int clear_block_count(int64_t n, int threads) {
+    if (n <= 0) return 0;
+    const int64_t b = (n / 4 + 4 * threads - 1) / (4 * threads);
+    return static_cast<int>(b < 2048 ? b : 2048);
+}
+
 __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int64_t P,
                                                           int E, int S, int seg,
                                                           int32_t* __restrict__ seg_counts) {
@@ -70,8 +88,13 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
 }
 
 // Exclusive prefix over segments for expert blockIdx.x, in place.
-__global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ seg_counts, int S,
-                                                         int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ seg_counts, int S, int E,
+                                                         int32_t* __restrict__ counts, float* clear,
+                                                         int64_t clear_n) {
+    if (static_cast<int>(blockIdx.x) >= E) {
+        clear_blocks(clear, clear_n, E);
+        return;
+    }
     __shared__ int sh[4];
     int32_t* row = seg_counts + static_cast<int64_t>(blockIdx.x) * S;
     int carry = 0;
@@ -201,7 +224,12 @@ __global__ __launch_bounds__(64) void route_wave_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ tile_prefix,
                                                         int32_t* __restrict__ sorted_to_pair,
-                                                        int32_t* __restrict__ pair_to_sorted) {
+                                                        int32_t* __restrict__ pair_to_sorted, float* clear,
+                                                        int64_t clear_n) {
+    if (blockIdx.x > 0) {
+        clear_blocks(clear, clear_n, 1);
+        return;
+    }
     __shared__ int32_t run[kWaveMaxExperts + 1];  // [E] collects the dropped pairs
     const int lane = threadIdx.x;
     run[lane] = 0;
@@ -270,7 +298,12 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ tile_prefix,
                                                            int32_t* __restrict__ sorted_to_pair,
-                                                           int32_t* __restrict__ pair_to_sorted) {
+                                                           int32_t* __restrict__ pair_to_sorted, float* clear,
+                                                           int64_t clear_n) {
+    if (blockIdx.x > 0) {
+        clear_blocks(clear, clear_n, 1);
+        return;
+    }
     extern __shared__ int32_t cnt[];  // [kSmallWaves][E]
     __shared__ int sh[16];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -378,7 +411,8 @@ hipError_t launch_route_after_count(const RouteBuffers& b, hipStream_t st) {
     const size_t lds = sizeof(int32_t) * static_cast<size_t>(b.E);
     int nbits = 0;
     while ((1 << nbits) <= b.E) ++nbits;  // enough bits for ids 0..E (E = sentinel)
-    route_scan_kernel<<<b.E, 256, 0, st>>>(b.seg_counts, b.S, b.counts);
+    route_scan_kernel<<<b.E + clear_block_count(b.clear_n, 256), 256, 0, st>>>(b.seg_counts, b.S, b.E, b.counts,
+                                                                              b.clear, b.clear_n);
     route_offsets_kernel<<<1, 1024, 0, st>>>(b.counts, b.E, b.offsets, b.tile_prefix);
     if (b.S > 0) {
         route_scatter_kernel<<<b.S, 64, lds, st>>>(b.ids, b.P, b.E, b.S, b.seg, nbits, b.seg_counts,
@@ -391,16 +425,18 @@ hipError_t launch_route(const RouteBuffers& b, hipStream_t st) {
     if (b.P <= kWaveMaxPairs && b.E <= kWaveMaxExperts) {
         int nbits = 0;
         while ((1 << nbits) <= b.E) ++nbits;
-        route_wave_kernel<<<1, 64, 0, st>>>(b.ids, static_cast<int>(b.P), b.E, nbits, b.counts, b.offsets,
-                                            b.tile_prefix, b.sorted_to_pair, b.pair_to_sorted);
+        route_wave_kernel<<<1 + clear_block_count(b.clear_n, 64), 64, 0, st>>>(
+            b.ids, static_cast<int>(b.P), b.E, nbits, b.counts, b.offsets, b.tile_prefix, b.sorted_to_pair,
+            b.pair_to_sorted, b.clear, b.clear_n);
         return hipGetLastError();
     }
     if (b.P <= kSmallMaxPairs && b.E <= kSmallMaxExperts) {
         int nbits = 0;
         while ((1 << nbits) <= b.E) ++nbits;
         const size_t lds = sizeof(int32_t) * kSmallWaves * static_cast<size_t>(b.E);
-        route_small_kernel<<<1, 1024, lds, st>>>(b.ids, b.P, b.E, nbits, b.counts, b.offsets, b.tile_prefix,
-                                                 b.sorted_to_pair, b.pair_to_sorted);
+        route_small_kernel<<<1 + clear_block_count(b.clear_n, 1024), 1024, lds, st>>>(
+            b.ids, b.P, b.E, nbits, b.counts, b.offsets, b.tile_prefix, b.sorted_to_pair, b.pair_to_sorted,
+            b.clear, b.clear_n);
         return hipGetLastError();
     }
     if (b.S > 0) {

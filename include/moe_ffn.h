@@ -142,9 +142,11 @@ MOE_FFN_API int moe_ffn_forward(const moe_ffn_problem* p, const void* x, const v
  * (hipEvent_t, passed as void*) on `stream` at the boundaries of its four
  * kernel stages, for per-kernel timing without a host synchronization:
  *   events[0] before the route step        events[1] after it
- *   events[2] after stage 2 (SPLIT: GEMM1 + SwiGLU; FUSED: accumulator fill)
+ *   events[2] after stage 2 (SPLIT: GEMM1 + SwiGLU; FUSED: nothing, the
+ *             route step clears the fp32 accumulator)
  *   events[3] after stage 3 (SPLIT: GEMM2 + weight; FUSED: fused kernel)
- *   events[4] after stage 4 (SPLIT: combine;        FUSED: fp32 -> bf16)
+ *   events[4] after stage 4 (SPLIT: combine;        FUSED: fp32 -> bf16, or
+ *             nothing where the fused kernel converts each completed row)
  * n_events must be 5 (or 0, which makes it moe_ffn_forward). The events
  * stay owned by the caller. */
 MOE_FFN_API int moe_ffn_forward_events(const moe_ffn_problem* p, const void* x, const void* w1,

@@ -48,6 +48,34 @@ def test_shared_expert_matches_oracle(mode, T, D, H, E, k, Hs):
     _case(mi.custom(T, D, H, E, k, "zipf"), Hs, mode)
 
 
+@pytest.mark.parametrize("mode", ["split", "fused"])
+@pytest.mark.parametrize("T,D,H,E,k,Hs", [
+    (48, 512, 256, 8, 2, 256),      # fused: the decode-ring kernel writes the unrouted tokens' rows
+    (300, 384, 256, 6, 3, 256),     # fused: the generic kernel and the conversion kernel
+])
+def test_shared_expert_with_unrouted_tokens(mode, T, D, H, E, k, Hs):
+    """Tokens whose routes are all dropped receive the shared expert's row alone
+    (the output starts as NaN, so every row must be written)."""
+    import grouped_gemm_amd as g
+    cfg = mi.custom(T, D, H, E, k, "uniform")
+    print(f"shared + unrouted tokens {cfg.name} Hs={Hs} mode={mode}", flush=True)
+    d = mi.make_bf16(cfg, 4)
+    d["topk_ids"][::5, :] = -1                # every fifth token: no route reaches an expert
+    d["topk_ids"][3, :] = E                   # == E: dropped as well
+    d["topk_ids"][1::7, 0] = -1               # some tokens keep only part of their routes
+    ws1, ws2 = mi.shared_expert(cfg, Hs, 4)
+    t = upload_bf16(d)
+    out = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    g.moe_ffn_forward_shared(t["x"], t["w1"], t["w2"], t["topk_ids"], t["topk_weights"], bf16_to_gpu(ws1),
+                             bf16_to_gpu(ws2), mode=mode, out=out)
+    torch.cuda.synchronize()
+    got = gpu_bf16_to_f64(out)
+    ref = mi.bf16_bits_to_f32(oracle.forward_bf16(d["x"], d["w1"], d["w2"], d["topk_ids"], d["topk_weights"],
+                                                  shared=(ws1, ws2))).astype(np.float64)
+    rel, cos = assert_close(got, ref, what=f"{cfg.name}/shared+unrouted/{mode}")
+    print(f"  max err / max|ref| = {rel:.3e}, cosine = {cos:.7f}", flush=True)
+
+
 def test_shared_expert_decode():
     _case(mi.CONFIGS[2], 2048, "split")
 
