@@ -47,6 +47,12 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32 x 32 x 16: lane l holds A row (and B column) l % 32, k = 8 (l / 32) .. + 7;
+// result v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // wait until at most n vector-memory operations of this wave are in flight
@@ -665,12 +671,16 @@ __global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a) {
 //     weight * partial into acc32 [T, D] (fp32).
 // The weight waves (0-1) run one continuous ring through both phases, so
 // phase 2's first W2 stages are in flight while phase 1 drains. In phase 2
-// each wave owns a quarter of a group's output rows over the whole slice (no
-// cross-wave reduction); the result goes through an LDS staging tile so that
-// each atomic instruction covers 64 consecutive floats of one token row (two
-// whole cache lines: MI355X's L2 atomics cost per line touched), and only the
-// token waves (2-3), which move nothing in phase 2, issue the atomics, so the
-// weight waves' vmcnt budgets count their DMAs alone. The blocks of one
+// only the token waves (2-3), which move nothing then, compute: each owns
+// half of a stage's output rows over the whole slice (no cross-wave
+// reduction) and adds its partials with atomics straight from the MFMA
+// results, so the weight waves' vmcnt budgets count their DMAs alone and a
+// stage needs one barrier. A slice is 64, 128 or 256 act columns (the
+// pages' CPC knob: two 128-wide column groups per block halve the number
+// of partial rows to reduce; 64 doubles the blocks for small batches).
+// A token's row is converted to bf16 by the block that adds its last
+// partial (per-token counters), so the pass is two launches: the route
+// step (whose extra blocks clear the accumulator) and this kernel. The blocks of one
 // m-tile's slices are consecutive in the grid, so they run side by side:
 // their phase-2 reads of W2 fall in the same rows at about the same time,
 // and the m-tile's token rows come from L2.
@@ -681,12 +691,10 @@ struct FusedTile {
     static constexpr int R2 = 32768 / RB2;   // W2 rows per stage (32 KB)
     static constexpr int CPR2 = RB2 / 16;    // 16-byte chunks per W2 (and act) row
     static constexpr int RPI2 = 1024 / RB2;  // W2 rows per DMA instruction
-    static constexpr int NS2 = BH / 32;      // k-steps per phase-2 stage
-    static constexpr int NB2 = R2 / 64;      // 16-row blocks of a wave in phase 2
+    static constexpr int KS2 = BH / 16;      // 32 x 32 x 16 MFMA k-steps over the slice
+    static constexpr int FB2 = R2 / 64;      // 32-feature blocks of a token wave per stage
     static constexpr int ACT = 32 * RB2;     // act tile [32 tokens][BH] bf16
-    static constexpr int STG_ROW = R2 + 4;   // staging row in floats (padded: conflict-free writes)
-    static constexpr int STG = 32 * STG_ROW * 4;
-    static_assert(BH == 128 || BH == 256, "128- or 256-wide slices");
+    static_assert(BH == 64 || BH == 128 || BH == 256, "64-, 128- or 256-wide slices");
 };
 
 // Plain LDS loads of four floats, written as asm: the compiler, which cannot
@@ -729,15 +737,14 @@ __device__ __forceinline__ void lds_read4(bf16x8_t (&f)[4], const uint32_t (&p)[
 }
 
 // Tokens none of whose routes reach an expert get no partial rows: their
-// output is the shared expert's row, or zeros. Block b takes tokens b,
-// b + gridDim.x, ...
-__device__ void fused_write_unrouted(const Bf16Args& a) {
+// output is the shared expert's row, or zeros. One wave of block b takes
+// tokens b, b + gridDim.x, ... (k <= 64: a lane per route).
+__device__ void fused_write_unrouted(const Bf16Args& a, int lane) {
     for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
-        int nv = 0;
-        for (int j = 0; j < a.k; ++j) nv += a.rv.pair_to_sorted[static_cast<int64_t>(t) * a.k + j] >= 0;
-        if (nv) continue;
+        const bool routed = lane < a.k && a.rv.pair_to_sorted[static_cast<int64_t>(t) * a.k + lane] >= 0;
+        if (__ballot(routed)) continue;
         const int64_t row = static_cast<int64_t>(t) * a.D;
-        for (int c = threadIdx.x; c < a.D / 8; c += kThreads)
+        for (int c = lane; c < a.D / 8; c += 64)
             *reinterpret_cast<u32x4_t*>(a.out + row + 8 * c) =
                 a.shared_y ? *reinterpret_cast<const u32x4_t*>(a.shared_y + row + 8 * c) : u32x4_t{0, 0, 0, 0};
     }
@@ -751,25 +758,23 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     constexpr int NB = 4, NT = 2;
     constexpr int W_INS = 2 * T::W_INS, T_INS = 2 * T::T_INS;  // per wave of the pair that moves them
     static_assert(W_INS * 1024 * 2 == T::W_BYTES, "a stage is the two weight waves' DMAs");
-    static_assert(SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT + F::STG <= 160 * 1024 - 512, "LDS of a CU");
+    static_assert(SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT <= 160 * 1024 - 512, "LDS of a CU");
     static_assert((SW - 1) * W_INS < 64, "vmcnt range");
     static_assert(2 * T::T_BYTES == T::W_BYTES, "the token ring holds one weight stage in phase 2");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT + F::STG];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT];
     __shared__ int64_t sRow[32];  // acc32 row offset (token * D) of each m-tile row
     __shared__ float sW[32];      // its routing weight (0 past the tile's rows)
     __shared__ int sTok[32];      // its token
+    __shared__ int sTgt[32];      // partial rows that complete its token's row: H / BH per routed pair
     __shared__ int sDone[33];     // [32]: count of the tokens whose rows this block completes, then the tokens
     uint8_t* const tring = lds + SW * T::W_BYTES;
     uint8_t* const act = tring + 2 * T::T_BYTES;
-    float* const stg = reinterpret_cast<float*>(act + F::ACT);
     const int nslices = a.H / BH;
     const int slice = blockIdx.x % nslices;
-    MTile mt;
-    if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) {
-        fused_write_unrouted(a);
-        return;
-    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 1) fused_write_unrouted(a, lane);  // overlaps wave 0's m-tile lookup
+    MTile mt;
+    if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
     const bool wmover = wave < 2;
     const int mw = wave & 1;
     const int h0 = slice * BH;
@@ -781,6 +786,18 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
         sRow[m] = static_cast<int64_t>(p / a.k) * a.D;
         sW[m] = m < mt.rows ? a.wts[p] : 0.0f;
         sTok[m] = p / a.k;
+        int nv = 0;  // routed pairs of the token (loads issued together with wts[p])
+        if (m < mt.rows) {
+            const int64_t t0 = static_cast<int64_t>(p / a.k) * a.k;
+            for (int j0 = 0; j0 < a.k; j0 += 8) {
+                int v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = j0 + u < a.k ? a.rv.pair_to_sorted[t0 + j0 + u] : -1;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) nv += v[u] >= 0;
+            }
+        }
+        sTgt[m] = nv * nslices;
         if (m == 0) sDone[32] = 0;
     }
     const char* src[W_INS];
@@ -932,65 +949,54 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
                 for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
             continue;
         }
-        // phase 2: wave w owns the group's rows R2/4 * w .. R2/4 * (w + 1) - 1 over the whole slice
-        f32x4_t y[F::NB2][NT];
+        // phase 2, token waves only: act tile x the stage's R2 W2 rows, each
+        // wave half of the rows in 32-feature blocks, on the 32 x 32 MFMA with
+        // the tokens as its rows. A register of its result then holds 32
+        // consecutive output features of two token rows, so weight * partial
+        // goes straight from the accumulators to the atomics, each instruction
+        // covering two whole 128-byte lines (MI355X's L2 atomics cost per line).
+        if (wmover) continue;
+        f32x16_t y[F::FB2];
 #pragma unroll
-        for (int b = 0; b < F::NB2; ++b)
+        for (int fb = 0; fb < F::FB2; ++fb) y[fb] = f32x16_t{};
+        const int f0 = (wave - 2) * (F::R2 / 2) + (lane & 31);  // this lane's feature in block 0
+        const int tm = lane & 31;                                 // this lane's token row (A operand)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) y[b][t] = f32x4_t{};
+        for (int k0 = 0; k0 < F::KS2; k0 += 4) {
+            uint32_t pa[4];
 #pragma unroll
-        for (int q = 0; q < F::NS2; ++q) {
-            const int c = 4 * q + kg;
-            constexpr int NR = F::NB2 + NT;
-            uint32_t p[NR];
-#pragma unroll
-            for (int b = 0; b < F::NB2; ++b) {
-                const int row = F::R2 / 4 * wave + 16 * b + r;
-                p[b] = lds_addr(wslot + row * F::RB2 + ((c ^ (row & (F::CPR2 - 1))) << 4));
+            for (int u = 0; u < 4; ++u) {
+                const int c = 2 * (k0 + u) + (lane >> 5);
+                pa[u] = lds_addr(act + tm * F::RB2 + ((c ^ (tm & (F::CPR2 - 1))) << 4));
             }
+            bf16x8_t af[4];
+            lds_read4(af, pa);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int m = 16 * t + r;
-                p[F::NB2 + t] = lds_addr(act + m * F::RB2 + ((c ^ (m & (F::CPR2 - 1))) << 4));
-            }
-            bf16x8_t f[NR];
-            if constexpr (NR == 3) lds_read3(f, p);
-            else lds_read4(f, p);
-#pragma unroll
-            for (int b = 0; b < F::NB2; ++b)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) y[b][t] = mfma16(f[b], f[F::NB2 + t], y[b][t]);
-        }
-        // stage the R2 x 32 tile as [token][output] and add weight * y with
-        // atomics of 64 consecutive floats per instruction
-#pragma unroll
-        for (int b = 0; b < F::NB2; ++b)
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                *reinterpret_cast<f32x4_t*>(stg + (16 * t + r) * F::STG_ROW + F::R2 / 4 * wave + 16 * b + 4 * kg) =
-                    y[b][t];
-        lds_barrier();
-        if (!wmover) {
-            const int d0 = ((it - NIT1 + rot) % NG2) * F::R2;
-            const int i = threadIdx.x - 128;
-            // the staging reads in asm: the compiler would make each one wait
-            // for every vector memory operation in flight (it cannot tell the
-            // staging tile from the ring slots the DMAs write)
-            for (int j0 = 0; j0 < F::R2 / 4; j0 += 4) {
-                int mm[4], dd[4];
-                uint32_t pa[4];
+            for (int fb = 0; fb < F::FB2; ++fb) {
+                const int row = f0 + 32 * fb;
+                uint32_t pw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int idx = (j0 + u) * 128 + i;
-                    mm[u] = idx / F::R2;
-                    dd[u] = idx % F::R2;
-                    pa[u] = lds_addr(stg + mm[u] * F::STG_ROW + dd[u]);
+                    const int c = 2 * (k0 + u) + (lane >> 5);
+                    pw[u] = lds_addr(wslot + row * F::RB2 + ((c ^ (row & (F::CPR2 - 1))) << 4));
                 }
-                float v[4];
-                lds_load4_f32(v, pa);
+                bf16x8_t wf[4];
+                lds_read4(wf, pw);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (mm[u] < mt.rows) unsafeAtomicAdd(a.acc32 + sRow[mm[u]] + d0 + dd[u], sW[mm[u]] * v[u]);
+                for (int u = 0; u < 4; ++u) y[fb] = mfma32(af[u], wf[u], y[fb]);
+            }
+        }
+        const int d0 = ((it - NIT1 + rot) % NG2) * F::R2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int mlo = ((v >> 2) << 3) + (v & 3);  // lanes 0-31: token row mlo, lanes 32-63: mlo + 4
+            if (mlo >= mt.rows) continue;
+            const int m = mlo + ((lane >> 5) << 2);
+            if (m < mt.rows) {
+                float* dst = a.acc32 + sRow[m] + d0 + f0;
+                const float w = sW[m];
+#pragma unroll
+                for (int fb = 0; fb < F::FB2; ++fb) unsafeAtomicAdd(dst + 32 * fb, w * y[fb][v]);
             }
         }
     }
@@ -1006,9 +1012,7 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     __syncthreads();
     if (wave == 2 && lane < mt.rows) {
         const int t = sTok[lane];
-        int nv = 0;
-        for (int j = 0; j < a.k; ++j) nv += a.rv.pair_to_sorted[static_cast<int64_t>(t) * a.k + j] >= 0;
-        if (atomicAdd(a.tcnt + t, 1) + 1 == nv * nslices) sDone[atomicAdd(&sDone[32], 1)] = t;
+        if (atomicAdd(a.tcnt + t, 1) + 1 == sTgt[lane]) sDone[atomicAdd(&sDone[32], 1)] = t;
     }
     __syncthreads();
     const int ndone = sDone[32];
@@ -1033,7 +1037,6 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
             }
         }
     }
-    fused_write_unrouted(a);
 }
 
 inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
@@ -1091,27 +1094,32 @@ bool fused_decode_supported(const Bf16Args& a) {
 
 // Slice width of the fused kernel: a block (m-tile, slice) is the unit of
 // work, and the blocks run about one per CU, so the width whose block count
-// fills whole rounds of the CUs best wins; 256 (half the atomics, and
-// 512-byte W2 row segments) unless 128 fills the rounds clearly better.
-// Measured at D=2048, H=768, E=128, k=8: 16 tokens (about 250 blocks of
-// 256) 0.164 ms with 256 against 0.18 with 128; 32 tokens (about 340 of
-// 256, 680 of 128) 0.30 against 0.27; the decode shape (256 blocks of 256)
-// 0.50 against 0.58.
+// fills whole rounds of the CUs best wins, the widest of those within 5%
+// of the best fill (wider slices: fewer partial rows to add, longer W2 row
+// segments, fewer blocks to start). Measured (graph replay, ms, widths
+// 64 / 128 / 256): D=2048, H=768, E=128, k=8 at 4 tokens 0.083 / 0.077 /
+// 0.125, at 16 tokens 0.162 / 0.151 / 0.143, at 64 tokens 0.245 / 0.226 /
+// 0.257; D=6144, H=2048, E=32, k=8 at 8 tokens 0.420 / 0.381 / 0.366;
+// D=256, H=512, E=8, k=2 at 16 tokens 0.023 / 0.028 / 0.039.
 int fused_slice(const Bf16Args& a) {
-    if (a.H % 256) return 128;
     const double mt = expected_mtiles32(a.T, a.k, a.E), cus = device_cu_count();
     auto fill = [&](int bh) {
+        if (a.H % bh) return 0.0;
         const double units = mt * (a.H / bh);
         return units / (std::ceil(units / cus) * cus);
     };
-    return fill(256) >= fill(128) - 0.05 ? 256 : 128;
+    const double best = std::max(fill(256), std::max(fill(128), fill(64)));
+    for (int bh : {256, 128})
+        if (fill(bh) >= 0.95 * best) return bh;
+    return 64;
 }
 
 hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s) {
     const int bh = fused_slice(a);
     const int64_t blocks = static_cast<int64_t>(mtiles_upper(a.P, a.E, 32)) * (a.H / bh);
     if (bh == 256) fused_dma_kernel<256, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
-    else fused_dma_kernel<128, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
+    else if (bh == 128) fused_dma_kernel<128, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
+    else fused_dma_kernel<64, 3><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

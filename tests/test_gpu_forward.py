@@ -226,15 +226,19 @@ def test_side_stream_with_int64_ids():
 
 
 @pytest.mark.parametrize("T,D,H,E,k,routing", [
-    (2100, 256, 512, 3, 2, "zipf"),     # many 32-row m-tiles per expert, ragged last tiles
-    (96, 512, 768, 16, 4, "softmax"),   # three 256-wide slices of H, eight W2 row groups
+    (2100, 256, 512, 3, 2, "zipf"),     # many 32-row m-tiles per expert, ragged last tiles (64-wide slices)
+    (96, 512, 768, 16, 4, "softmax"),   # twelve 64-wide slices of H, two W2 row groups
     (1, 256, 256, 4, 2, "uniform"),     # a single token
     (64, 256, 256, 4, 4, "uniform"),    # k = E
     (4096, 256, 512, 8, 2, "zipf"),     # enough m-tiles for 256-wide slices
+    (40, 2048, 768, 128, 8, "zipf"),    # 128-wide slices, hot experts with several m-tiles
+    (16, 2048, 768, 128, 8, "uniform"), # 256-wide slices, three of them
 ])
 def test_fused_decode_kernel(T, D, H, E, k, routing):
     """The fused pass on the decode kernels' rings (32-row m-tiles, act slice in
-    LDS, split-K down projection added into the fp32 accumulator)."""
+    LDS, split-K down projection added into the fp32 accumulator, each token's
+    row converted by the block that adds its last partial; the slice width
+    follows the expected block count)."""
     import grouped_gemm_amd as g
     assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", "fused", 1) == "fused_dma_kernel"
     _case(mi.custom(T, D, H, E, k, routing), "fused")
