@@ -39,18 +39,21 @@ int check_shape(const moe_ffn_problem* p) {
     return MOE_FFN_OK;
 }
 
-// AUTO resolves to the split pipeline: it measured faster than the fused one
-// at every token count tried on MI355X (4 to 4096 tokens at D=2048, H=768,
-// 128 experts; 8 to 128 at the 6144/2048/32-expert decode dims; 16 to 4096
-// at D=256, H=512, 8 experts, where the two are within 5% up to 256 tokens).
-// The fused pipeline's split-K partial rows cost fp32 atomic adds into the
-// accumulator (P * H/slice * D of them), and MI355X's L2 atomics run at
-// about 330 G adds/s, while the split pipeline's decode kernels already
-// stream the weights at close to the HBM rate.
+// AUTO resolves to the fused pipeline for bf16 passes bound by launch
+// latency (moe::fused_preferred: few rows per expert and a few MB of
+// weights, where its two kernels beat the split pipeline's four) and to the
+// split pipeline otherwise: where the weights stream from HBM the split
+// pipeline's decode kernels are as fast or faster, and at prefill sizes the
+// fused pipeline's split-K partial rows cost fp32 atomic adds into the
+// accumulator (P * H/slice * D of them, at about 330 G adds/s on MI355X's
+// L2) and each expert's weights are streamed once per 32-row m-tile.
 int resolve(const moe_ffn_problem* p, int mode) {
     if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
     if (p->dtype == MOE_FFN_MXFP4) return mode == MOE_FFN_FUSED ? MOE_FFN_EUNSUPPORTED : MOE_FFN_SPLIT;
-    return mode == MOE_FFN_FUSED ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
+    if (mode == MOE_FFN_AUTO)
+        return p->dtype == MOE_FFN_BF16 && moe::fused_preferred(p->T, p->D, p->H, p->E, p->topk) ? MOE_FFN_FUSED
+                                                                                                 : MOE_FFN_SPLIT;
+    return mode;
 }
 
 struct RoutePlan {

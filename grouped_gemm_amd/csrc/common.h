@@ -202,6 +202,8 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
 // slices of the intermediate dimension); D and H multiples of 256, no
 // activation variant. Adds into a.acc32, which must hold zeros.
 bool fused_decode_supported(const Bf16Args& a);
+// Whether AUTO runs a bf16 pass (no activation variant) on the fused pipeline.
+bool fused_preferred(int64_t T, int D, int H, int E, int k);
 hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s);
 
 struct MxArgs {

@@ -1088,6 +1088,23 @@ hipError_t launch_dma(const Bf16Args& a, bool gemm1, hipStream_t s) {
 
 }  // namespace
 
+// AUTO's pipeline for a bf16 pass: the fused one where the pass is bound by
+// launch latency, which is where its two kernels (route, fused) beat the
+// split pipeline's four. Measured on MI355X (graph replay): D=256, H=512,
+// E=8, k=2 at 16 tokens 0.022 ms fused against 0.029 split, at 64 tokens
+// (16 rows per expert) 0.028 against 0.029, at 256 tokens (64 rows per
+// expert: each expert's weights streamed once per 32-row m-tile, twice)
+// 0.038 against 0.034; where the weights streamed run to hundreds of MB
+// (D=2048 to 6144) the fused pass is at best within 2% of the split one. So
+// fused while an expert gets at most 16 rows (half an m-tile) and the
+// weights the fused kernel streams, 3 H D bf16 per expected m-tile, stay
+// within 8 MB.
+bool fused_preferred(int64_t T, int D, int H, int E, int k) {
+    if (D % 256 || H % 128) return false;  // the fused decode-ring kernel's shapes
+    if (static_cast<double>(T) * k > 16.0 * E) return false;
+    return expected_mtiles32(T, k, E) * 3.0 * H * D * 2.0 <= 8e6;
+}
+
 bool fused_decode_supported(const Bf16Args& a) {
     return a.D % 256 == 0 && a.H % 128 == 0 && !a.av.on();
 }

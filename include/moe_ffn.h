@@ -53,8 +53,10 @@ enum { MOE_FFN_BF16 = 0, MOE_FFN_MXFP8 = 1, MOE_FFN_MXFP4 = 2 };
  * SwiGLU and GEMM2 in one kernel and never writes the activation; the down
  * projection is then split over H slices whose partial rows are reduced
  * into an fp32 accumulator. SPLIT writes the activation once and runs the
- * down projection as a plain grouped GEMM. AUTO resolves to SPLIT, the faster
- * of the two at every size measured on MI355X. */
+ * down projection as a plain grouped GEMM. AUTO resolves to FUSED for bf16
+ * passes bound by launch latency (at most 16 rows per expert and up to 8 MB
+ * of expert weights streamed, with D a multiple of 256 and H of 128), where
+ * it measured faster on MI355X, and to SPLIT otherwise. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_FUSED = 1, MOE_FFN_SPLIT = 2 };
 
 enum {
