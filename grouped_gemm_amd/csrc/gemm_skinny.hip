@@ -697,6 +697,11 @@ struct FusedTile {
     static_assert(BH == 64 || BH == 128 || BH == 256, "64-, 128- or 256-wide slices");
 };
 
+// An 8-byte LDS store, written as asm (see lds_load4_f32).
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, uint32_t lo, uint32_t hi) {
+    asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(uint2{lo, hi}) : "memory");
+}
+
 // Plain LDS loads of four floats, written as asm: the compiler, which cannot
 // tell an LDS tile from the ring slots DMAs are filling, would put a
 // vmcnt(0) wait (draining the ring, and any atomics in flight) before its
@@ -755,7 +760,8 @@ template <int BH, int SW>
 __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     using T = DmaTile<2, 256, 2>;  // phase 1: 512-byte row segments, KC = 256 values per stage
     using F = FusedTile<BH>;
-    constexpr int NB = 4, NT = 2;
+    constexpr int NT = 2;
+    static_assert(F::G1 >= 2, "a token chunk's slot is refilled at the chunk's second stage");
     constexpr int W_INS = 2 * T::W_INS, T_INS = 2 * T::T_INS;  // per wave of the pair that moves them
     static_assert(W_INS * 1024 * 2 == T::W_BYTES, "a stage is the two weight waves' DMAs");
     static_assert(SW * T::W_BYTES + 2 * T::T_BYTES + F::ACT <= 160 * 1024 - 512, "LDS of a CU");
@@ -778,36 +784,44 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     const bool wmover = wave < 2;
     const int mw = wave & 1;
     const int h0 = slice * BH;
+    const int r = lane & 15, kg = lane >> 4;
     const int KIT1 = a.D / 256, NIT1 = F::G1 * KIT1, NG2 = a.D / F::R2, NIT = NIT1 + NG2;
-    const int rot = (blockIdx.x / nslices + slice) % NG2;  // spread the blocks' W2 reads over HBM channels
+    // each block starts its phase-1 K walk at its own chunk and its phase-2
+    // walk at its own W2 row group, so the blocks' reads spread over the HBM
+    // channels instead of crowding a few
+    const int kc0 = static_cast<int>(blockIdx.x) % KIT1;
+    const int rot = (blockIdx.x / nslices + slice) % NG2;
     if (threadIdx.x < 32) {
         const int m = threadIdx.x;
         const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
         sRow[m] = static_cast<int64_t>(p / a.k) * a.D;
         sW[m] = m < mt.rows ? a.wts[p] : 0.0f;
         sTok[m] = p / a.k;
-        int nv = 0;  // routed pairs of the token (loads issued together with wts[p])
-        if (m < mt.rows) {
-            const int64_t t0 = static_cast<int64_t>(p / a.k) * a.k;
-            for (int j0 = 0; j0 < a.k; j0 += 8) {
-                int v[8];
+        // routed pairs of the token: unconditional loads (indexes clamped to
+        // its k pairs), so they go out together with wts[p]
+        const int64_t t0 = static_cast<int64_t>(p / a.k) * a.k;
+        int nv = 0;
+        for (int j0 = 0; j0 < a.k; j0 += 8) {
+            int v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = j0 + u < a.k ? a.rv.pair_to_sorted[t0 + j0 + u] : -1;
+            for (int u = 0; u < 8; ++u) v[u] = a.rv.pair_to_sorted[t0 + (j0 + u < a.k ? j0 + u : a.k - 1)];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) nv += v[u] >= 0;
-            }
+            for (int u = 0; u < 8; ++u) nv += (j0 + u < a.k && v[u] >= 0) ? 1 : 0;
         }
-        sTgt[m] = nv * nslices;
+        sTgt[m] = m < mt.rows ? nv * nslices : 0;
         if (m == 0) sDone[32] = 0;
     }
     const char* src[W_INS];
     if (wmover) {
+        // W1 rows in the slot as dma_kmajor_kernel lays them out: each 16-row
+        // block holds 8 gate rows and the 8 up rows of the same act columns
         const int pc = lane % T::CPR;
 #pragma unroll
         for (int j = 0; j < W_INS; ++j) {
-            const int row = (mw * W_INS + j) * T::RPI + lane / T::CPR;
+            const int row = (mw * W_INS + j) * T::RPI + lane / T::CPR;  // slot row 0..63
             const int c = pc ^ (row & (T::CPR - 1));
-            const int64_t grow = static_cast<int64_t>(mt.expert) * 2 * a.H + (row < 32 ? h0 + row : a.H + h0 + row - 32);
+            const int jj = row & 15, h = h0 + 8 * (row >> 4) + (jj & 7);
+            const int64_t grow = static_cast<int64_t>(mt.expert) * 2 * a.H + (jj < 8 ? h : a.H + h);
             src[j] = reinterpret_cast<const char*>(a.w1) + grow * a.D * 2 + c * 16;
         }
     } else {
@@ -832,8 +846,9 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
         const int i2 = (it - NIT1) % (SW + 1);
         return i2 == SW ? tring : lds + ((NIT1 + i2) % SW) * T::W_BYTES;
     };
-    // weight stage `it`: phase 1 (W1 rows of group it / KIT1, K step it % KIT1)
-    // or phase 2 (R2 W2 rows of group (it - NIT1 + rot) % NG2, the slice's columns)
+    // weight stage `it`: phase 1 (group it % G1 of K chunk it / G1, the chunks
+    // walked from the block's own chunk kc0) or phase 2 (R2 W2 rows of group
+    // (it - NIT1 + rot) % NG2, the slice's columns)
     auto issue_w = [&](int it) {
         if (it == NIT1) {
             const int pc = lane % F::CPR2;
@@ -845,44 +860,38 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
                          ((static_cast<int64_t>(mt.expert) * a.D + row) * a.H + h0) * 2 + c * 16;
             }
         }
-        const int64_t off = it < NIT1 ? static_cast<int64_t>(it % KIT1) * T::RB + (it / KIT1) * gstride1
-                                      : ((it - NIT1 + rot) % NG2) * gstride2;
+        const int64_t off = it < NIT1
+            ? static_cast<int64_t>((it / F::G1 + kc0) % KIT1) * T::RB + (it % F::G1) * gstride1
+            : ((it - NIT1 + rot) % NG2) * gstride2;
         uint8_t* slot = wslot_of(it);
 #pragma unroll
         for (int j = 0; j < W_INS; ++j)
             __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
                                              kWeightDmaAux);
     };
-    auto issue_t = [&](int it) {
-        const int64_t off = static_cast<int64_t>(it % KIT1) * T::RB;
-        uint8_t* slot = tring + (it & 1) * T::T_BYTES;
+    // the 32 token rows' K chunk kc, into token slot kc & 1
+    auto issue_t = [&](int kc) {
+        const int64_t off = static_cast<int64_t>((kc + kc0) % KIT1) * T::RB;
+        uint8_t* slot = tring + (kc & 1) * T::T_BYTES;
 #pragma unroll
         for (int j = 0; j < T_INS; ++j)
             __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * T_INS + j) * 1024), 16, 0, 0);
     };
-    const int r = lane & 15, kg = lane >> 4;
-    f32x4_t acc[NB][NT];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
-    if (wmover) {
-#pragma unroll
-        for (int j = 0; j < SW - 1; ++j) issue_w(j);
-    } else {
-        issue_t(0);
-    }
-    for (int it = 0; it < NIT; ++it) {
+    // Stage `it` of the ring: each wave waits for its own DMAs of the stage
+    // (the weight waves: later stages keep W_INS each in flight; the token
+    // waves: the chunk's tokens, their only DMAs), one barrier, then the
+    // weight waves issue the stage SW - 1 ahead (SW ahead in phase 2) and the
+    // token waves, at a chunk's second stage, the next chunk's tokens (chunk
+    // kc + 1's slot was last read at chunk kc - 1's first stage).
+    auto ring_step = [&](int it) {
         if (wmover) {
-            // stages issued so far: through it + SW - 2 (phase 1 and the
-            // first phase-2 iteration), through it + SW - 1 after that
             const int ahead = (it > NIT1 ? it + SW - 1 : it + SW - 2) - it;
             const int left = NIT - 1 - it;
             const int n = ahead < left ? ahead : left;
             if (n >= SW - 1) wait_vm<(SW - 1) * W_INS>();
             else if (n == SW - 2) wait_vm<(SW - 2) * W_INS>();
             else wait_vm<0>();
-        } else if (it < NIT1) {
+        } else if (it < NIT1 && it % F::G1 == 0) {
             wait_vm<0>();
         }
         if (it == NIT1) lds_barrier();  // the act tile's last LDS writes are complete
@@ -894,61 +903,83 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
                 if (it == NIT1 && it + SW - 1 < NIT) issue_w(it + SW - 1);  // the token ring is free from here
                 if (it + SW < NIT) issue_w(it + SW);
             }
-        } else if (it + 1 < NIT1) {
-            issue_t(it + 1);
+        } else if (it < NIT1 && it % F::G1 == 1 && it / F::G1 + 1 < KIT1) {
+            issue_t(it / F::G1 + 1);
         }
-        uint8_t* wslot = wslot_of(it);
-        if (it < NIT1) {
-            // phase 1: GEMM1 with the stage's k-steps split over the four waves
-            uint8_t* tslot = tring + (it & 1) * T::T_BYTES;
+    };
+    if (wmover) {
 #pragma unroll
-            for (int q = 0; q < T::NS / 4; ++q) {
-                const int c = 4 * (wave * (T::NS / 4) + q) + kg;
-                uint32_t pw[4], pt[2];
+        for (int j = 0; j < SW - 1; ++j) issue_w(j);
+    } else {
+        issue_t(0);
+    }
+    // Phase 1, k-major as dma_kmajor_kernel: each wave owns 16 of a stage's 64
+    // W1 rows over the whole K chunk (no cross-wave reduction) against the
+    // chunk's token fragments, read once per chunk and kept in registers
+    // across its G1 groups; after the last chunk, silu(gate) * up of each
+    // group (the up rows 32 lanes away) goes into the act tile.
+    int it = 0;
+    {
+        f32x4_t acc[F::G1][NT];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int row = 16 * b + r;
-                    pw[b] = lds_addr(wslot + row * T::RB + ((c ^ (row & (T::CPR - 1))) << 4));
+        for (int g = 0; g < F::G1; ++g)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[g][t] = f32x4_t{};
+        for (int kc = 0; kc < KIT1; ++kc) {
+            bf16x8_t tk0[T::NS], tk1[T::NS];
+#pragma unroll
+            for (int g = 0; g < F::G1; ++g, ++it) {
+                ring_step(it);
+                if (g == 0) {
+                    const uint8_t* ts = tring + (kc & 1) * T::T_BYTES;
+                    uint32_t p0[T::NS], p1[T::NS];
+#pragma unroll
+                    for (int ks = 0; ks < T::NS; ++ks) {
+                        const int c = 4 * ks + kg;
+                        p0[ks] = lds_addr(ts + r * T::RB + ((c ^ r) << 4));
+                        p1[ks] = lds_addr(ts + (16 + r) * T::RB + ((c ^ (16 + r)) << 4));
+                    }
+                    lds_read8(tk0, p0);
+                    lds_read8(tk1, p1);
                 }
+                const uint8_t* slot = wslot_of(it);
+                const int row = 16 * wave + r;
+                uint32_t pw[T::NS];
+#pragma unroll
+                for (int ks = 0; ks < T::NS; ++ks)
+                    pw[ks] = lds_addr(slot + row * T::RB + (((4 * ks + kg) ^ (row & 31)) << 4));
+                bf16x8_t w[T::NS];
+                lds_read8(w, pw);
+#pragma unroll
+                for (int ks = 0; ks < T::NS; ++ks) {
+                    acc[g][0] = mfma16(w[ks], tk0[ks], acc[g][0]);
+                    acc[g][1] = mfma16(w[ks], tk1[ks], acc[g][1]);
+                }
+                if (kc != KIT1 - 1) continue;
+                // acc[g][t][q]: slot row 16 wave + 4 kg + q, token 16 t + r; lanes
+                // kg < 2 hold gate rows, kg >= 2 the matching up rows
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int m = 16 * t + r;
-                    pt[t] = lds_addr(tslot + m * T::RB + ((c ^ (m & (T::CPR - 1))) << 4));
-                }
-                bf16x8_t w[NB], tk[NT];
-                lds_read6(w, tk, pw, pt);
+                    float up[4];
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[b][t] = mfma16(w[b], tk[t], acc[b][t]);
-            }
-            if (it % KIT1 != KIT1 - 1) continue;
-            // group end: silu(gate) * up of act columns 32g .. 32g + 31 into the act tile
-            group_reduce<T::W_BYTES>(acc, reinterpret_cast<float*>(wslot), wave, lane);
-            const int g = it / KIT1;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (t != wave) continue;
-                const int m = 16 * t + r;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                    for (int q = 0; q < 4; ++q) up[q] = __shfl_xor(acc[g][t][q], 32);
+                    if (kg >= 2) continue;
                     float v[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float gt = acc[j][t][q], u = acc[j + 2][t][q];
-                        v[q] = gt / (1.0f + __expf(-gt)) * u;
+                        const float gt = acc[g][t][q];
+                        v[q] = gt / (1.0f + __expf(-gt)) * up[q];
                     }
-                    const int h = 32 * g + 16 * j + 4 * kg;  // act columns h .. h + 3 of the slice
-                    *reinterpret_cast<uint2*>(act + m * F::RB2 + (((h >> 3) ^ (m & (F::CPR2 - 1))) << 4) +
-                                              (h & 7) * 2) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    const int m = 16 * t + r, h = 32 * g + 8 * wave + 4 * kg;  // act columns h .. h + 3
+                    lds_write_b64(lds_addr(act + m * F::RB2 + (((h >> 3) ^ (m & (F::CPR2 - 1))) << 4) + (h & 7) * 2),
+                                  pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
             }
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{};
-            continue;
         }
+    }
+    for (; it < NIT; ++it) {
+        ring_step(it);
+        uint8_t* wslot = wslot_of(it);
         // phase 2, token waves only: act tile x the stage's R2 W2 rows, each
         // wave half of the rows in 32-feature blocks, on the 32 x 32 MFMA with
         // the tokens as its rows. A register of its result then holds 32
