@@ -1047,25 +1047,35 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     }
     __syncthreads();
     const int ndone = sDone[32];
-    if (ndone) {
-        for (int i = 0; i < ndone; ++i) {
-            const int64_t row = static_cast<int64_t>(sDone[i]) * a.D;
-            for (int c = threadIdx.x; c < a.D / 4; c += kThreads) {
-                const float* src = a.acc32 + row + 4 * c;
-                float4 v;
-                v.x = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                v.y = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                v.z = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                v.w = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (a.shared_y) {
-                    const uint2 e = *reinterpret_cast<const uint2*>(a.shared_y + row + 4 * c);
-                    v.x += bf16_to_f32(static_cast<uint16_t>(e.x & 0xffffu));
-                    v.y += bf16_to_f32(static_cast<uint16_t>(e.x >> 16));
-                    v.z += bf16_to_f32(static_cast<uint16_t>(e.y & 0xffffu));
-                    v.w += bf16_to_f32(static_cast<uint16_t>(e.y >> 16));
-                }
-                *reinterpret_cast<uint2*>(a.out + row + 4 * c) = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
-            }
+    // The completed rows, four floats per item and U items per thread in
+    // flight: the loads (device scope, so they bypass caches that may hold
+    // stale lines) go out together from clamped, always valid indexes, and
+    // only the stores are predicated.
+    constexpr int U = 8;
+    const int per = a.D / 4, total = ndone * per;
+    for (int b0 = 0; b0 < total; b0 += U * kThreads) {
+        uint64_t lo[U], hi[U];
+        uint2 sy[U];
+        int64_t off[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int idx = b0 + u * kThreads + static_cast<int>(threadIdx.x);
+            idx = idx < total ? idx : total - 1;
+            const int i = idx / per;
+            off[u] = static_cast<int64_t>(sDone[i]) * a.D + 4 * (idx - i * per);
+            const uint64_t* src = reinterpret_cast<const uint64_t*>(a.acc32 + off[u]);
+            lo[u] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            hi[u] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sy[u] = a.shared_y ? *reinterpret_cast<const uint2*>(a.shared_y + off[u]) : uint2{0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (b0 + u * kThreads + static_cast<int>(threadIdx.x) >= total) continue;
+            const float v0 = __uint_as_float(static_cast<uint32_t>(lo[u])) + bf16_to_f32(static_cast<uint16_t>(sy[u].x & 0xffffu));
+            const float v1 = __uint_as_float(static_cast<uint32_t>(lo[u] >> 32)) + bf16_to_f32(static_cast<uint16_t>(sy[u].x >> 16));
+            const float v2 = __uint_as_float(static_cast<uint32_t>(hi[u])) + bf16_to_f32(static_cast<uint16_t>(sy[u].y & 0xffffu));
+            const float v3 = __uint_as_float(static_cast<uint32_t>(hi[u] >> 32)) + bf16_to_f32(static_cast<uint16_t>(sy[u].y >> 16));
+            *reinterpret_cast<uint2*>(a.out + off[u]) = uint2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
     }
 }
