@@ -140,7 +140,7 @@ def kernel_work(cfg, mode, hit, dtype):
 
 KERNEL_FILES = {"dma_kmajor_kernel": "gemm_skinny.hip",
                 "dma_skinny_kernel": "gemm_skinny.hip",
-                "mx_fused_kernel": "mx.hip", "fused_dma_kernel": "gemm_skinny.hip",
+                "mx_fused_kernel": "mx.hip", "fused_dma_kernel": "gemm_fused.hip",
                 "mx_kmajor_kernel": "gemm_skinny.hip",
                 "big_gemm_kernel": "gemm_big.hip",
                 "mx_gemm1_kernel": "mx.hip", "mx_gemm2_kernel": "mx.hip", "fused_bf16_kernel": "gemm_bf16.hip",
@@ -158,11 +158,14 @@ def _code_only(text: str) -> str:
 
 def source_digest(symbol: str) -> str:
     """Digest of the code (comments and spacing aside) of the source file
-    defining `symbol` plus the shared header: a change to either invalidates
-    counters stored for that kernel."""
+    defining `symbol` plus the shared headers it includes (common.h, and
+    dma_ring.h for the DMA-ring kernels): a change to any of them
+    invalidates counters stored for that kernel."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "grouped_gemm_amd", "csrc")
-    for f in ("common.h", KERNEL_FILES.get(symbol, "")):
+    kf = KERNEL_FILES.get(symbol, "")
+    ring = "dma_ring.h" if kf in ("gemm_skinny.hip", "gemm_fused.hip") else ""
+    for f in ("common.h", ring, kf):
         path = os.path.join(d, f)
         if f and os.path.isfile(path):
             h.update(f.encode())

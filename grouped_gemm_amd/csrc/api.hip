@@ -40,8 +40,8 @@ int check_shape(const moe_ffn_problem* p) {
 }
 
 // AUTO resolves to the fused pipeline for bf16 passes bound by launch
-// latency (moe::fused_preferred: few rows per expert and a few MB of
-// weights, where its two kernels beat the split pipeline's four) and to the
+// latency (moe::fused_preferred: a few MB of expert weights streamed, where
+// its two kernels beat the split pipeline's four) and to the
 // split pipeline otherwise: where the weights stream from HBM the split
 // pipeline's decode kernels are as fast or faster, and at prefill sizes the
 // fused pipeline's split-K partial rows cost fp32 atomic adds into the

@@ -1,0 +1,155 @@
+// Pieces shared by the streaming kernels that fill an LDS ring with
+// global->LDS DMA: the decode-shaped GEMMs (gemm_skinny.hip) and the fused
+// pass (gemm_fused.hip). Everything here sits in an anonymous namespace, so
+// each translation unit holds its own copy.
+#pragma once
+
+#include <cmath>
+
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32 x 32 x 16: lane l holds A row (and B column) l % 32, k = 8 (l / 32) .. + 7;
+// result v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// wait until at most n vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14, expcnt 6:4, lgkmcnt 11:8
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would wait for every outstanding DMA (vmcnt(0)), draining the ring. Each
+// wave has already waited for its own DMAs of the stage (wait_vm), and its
+// LDS reads of the previous stage were consumed by MFMAs before it arrives,
+// so the bare s_barrier orders everything the ring needs; the empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Barrier after this wave's own LDS writes have completed (lgkmcnt(0)),
+// leaving its in-flight global->LDS DMAs (vmcnt) running.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt max, expcnt max, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---------------- tile, DMA and fragment reads ----------------
+// Global->LDS DMA instructions fetch
+// whole row segments (RB = 2*KC bytes of one row per CPR = RB/16 lanes), into
+// a row-major LDS tile whose 16-byte chunks are XOR-swizzled by the row
+// (physical chunk = logical ^ (row mod CPR)), and the MFMA fragments are
+// read from the tile; 16 rows reading one logical chunk hit 16 distinct bank
+// groups. Per stage a block fetches 64 weight rows x RB bytes plus the
+// 16*NT token rows x RB bytes; the four waves split the stage's k-steps and
+// the partial sums meet in LDS at the end. Ring of S stages, one barrier per
+// stage, each wave waits only for its own DMAs of the stage it consumes.
+// Cache policy bits of the weight DMA: 2 = nontemporal (each weight byte is
+// streamed once).
+constexpr int kWeightDmaAux = 2;
+
+template <int NT, int KC, int S>
+struct DmaTile {
+    static constexpr int R = 64;                 // weight rows per block
+    static constexpr int BM = 16 * NT;           // token rows per block
+    static constexpr int RB = 2 * KC;            // bytes per row per stage
+    static constexpr int CPR = RB / 16;          // 16-byte chunks per row per stage
+    static constexpr int RPI = 64 / CPR;         // rows per DMA instruction
+    static constexpr int W_INS = R / RPI / 4;    // weight DMA instructions per wave per stage
+    static constexpr int T_INS = BM / RPI / 4;   // token DMA instructions per wave per stage
+    static constexpr int W_BYTES = R * RB, T_BYTES = BM * RB, STAGE = W_BYTES + T_BYTES;
+    static constexpr int NS = KC / 32;           // MFMA k-steps per stage
+    static_assert(CPR >= 16 && CPR <= 64, "16..64 chunks per row keep the 16-row fragment reads conflict free");
+    static_assert(W_INS * RPI * 4 == R && T_INS * RPI * 4 == BM, "DMA instructions must split evenly over waves");
+    static_assert(S * STAGE <= 160 * 1024 && S >= 2, "ring must fit the LDS of a CU");
+};
+
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// Eight 16-byte LDS reads and a wait for them, in one asm statement (as
+// lds_read6, so that no vmcnt wait for the DMAs in flight comes before them).
+__device__ __forceinline__ void lds_read8(bf16x8_t (&v)[8], const uint32_t (&p)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+        : "memory");
+}
+
+// Four 16-byte LDS reads and a wait for them, as asm (see lds_read8).
+__device__ __forceinline__ void lds_read4(bf16x8_t (&f)[4], const uint32_t (&p)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+
+// Plain LDS loads of four floats, written as asm: the compiler, which cannot
+// tell an LDS tile from the ring slots DMAs are filling, would put a
+// vmcnt(0) wait (draining the ring, and any atomics in flight) before its
+// own accesses.
+__device__ __forceinline__ void lds_load4_f32(float (&v)[4], const uint32_t (&p)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\t"
+        "ds_read_b32 %1, %5\n\t"
+        "ds_read_b32 %2, %6\n\t"
+        "ds_read_b32 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+
+// An 8-byte LDS store, written as asm (see lds_load4_f32).
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, uint32_t lo, uint32_t hi) {
+    asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(uint2{lo, hi}) : "memory");
+}
+
+// 32-row m-tiles expected for T tokens with k routes each over E experts,
+// routes spread uniformly: the experts hit, each with ceil(rows / 32) tiles.
+inline double expected_mtiles32(int64_t T, int k, int E) {
+    const double hit = E * (1.0 - std::pow(1.0 - static_cast<double>(k) / E, static_cast<double>(T)));
+    const double per = std::ceil(static_cast<double>(T) * k / E / 32.0);
+    return hit * (per > 1.0 ? per : 1.0);
+}
+
+}  // namespace
+
+}  // namespace moe

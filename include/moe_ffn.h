@@ -54,9 +54,9 @@ enum { MOE_FFN_BF16 = 0, MOE_FFN_MXFP8 = 1, MOE_FFN_MXFP4 = 2 };
  * projection is then split over H slices whose partial rows are reduced
  * into an fp32 accumulator. SPLIT writes the activation once and runs the
  * down projection as a plain grouped GEMM. AUTO resolves to FUSED for bf16
- * passes bound by launch latency (at most 16 rows per expert and up to 8 MB
- * of expert weights streamed, with D a multiple of 256 and H of 128), where
- * it measured faster on MI355X, and to SPLIT otherwise. */
+ * passes bound by launch latency (up to 16 MB of expert weights streamed,
+ * one expert's weights per 32 routed rows, with D a multiple of 256 and H of
+ * 128), where it measured faster on MI355X, and to SPLIT otherwise. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_FUSED = 1, MOE_FFN_SPLIT = 2 };
 
 enum {

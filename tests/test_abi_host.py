@@ -58,13 +58,13 @@ def test_validate_dtype_and_mode():
 def test_resolve_mode():
     assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="split") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="fused") == g.MOE_FFN_FUSED
-    # measured crossover: fused where the pass is launch-bound (at most 16 rows per
-    # expert and a few MB of weights), split everywhere else
+    # measured crossover: fused where the pass is launch-bound (up to 16 MB of expert
+    # weights streamed, one expert's weights per 32 rows), split everywhere else
     assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_FUSED
     assert g.moe_ffn_resolve_mode(16, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_FUSED
     assert g.moe_ffn_resolve_mode(1, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_FUSED
-    assert g.moe_ffn_resolve_mode(128, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_SPLIT   # 32 rows per expert
-    assert g.moe_ffn_resolve_mode(256, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_resolve_mode(256, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_FUSED   # 64 rows per expert
+    assert g.moe_ffn_resolve_mode(1024, 256, 512, 8, 2, mode="auto") == g.MOE_FFN_SPLIT  # 50 MB streamed
     assert g.moe_ffn_resolve_mode(64, 384, 512, 8, 2, mode="auto") == g.MOE_FFN_SPLIT    # not the fused ring's shapes
     assert g.moe_ffn_resolve_mode(64, 256, 2048, 8, 2, mode="auto") == g.MOE_FFN_SPLIT   # 25 MB of weights
     assert g.moe_ffn_resolve_mode(64, 6144, 2048, 32, 8, mode="auto") == g.MOE_FFN_SPLIT

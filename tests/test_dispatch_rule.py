@@ -35,7 +35,7 @@ def test_workload_paths():
     assert _kernel(300, 384, 640, 16, 4) == "gemm1_swiglu_kernel"           # D not a multiple of 256
     assert _kernel(300, 384, 640, 16, 4, gemm=2) == "gemm2_weight_kernel"
     assert _kernel(64, 256, 512, 8, 2, mode="auto") == "fused_dma_kernel"   # AUTO: fused (launch-bound)
-    assert _kernel(256, 256, 512, 8, 2, mode="auto") == "big_gemm_kernel<128>"  # AUTO: split
+    assert _kernel(1024, 256, 512, 8, 2, mode="auto") == "big_gemm_kernel<256>"  # AUTO: split
     assert _kernel(64, 256, 512, 8, 2, mode="fused") == "fused_dma_kernel"
     assert _kernel(64, 384, 512, 8, 2, mode="fused") == "fused_bf16_kernel"  # D not a multiple of 256
     assert _kernel(16384, 4096, 1536, 64, 6, dtype="mxfp8") == "big_gemm_kernel<256>"

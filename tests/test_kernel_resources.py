@@ -17,8 +17,8 @@ from grouped_gemm_amd import build as b
 
 HIPCC = b.HIPCC
 RING_KERNELS = {"gemm_big.hip": ("big_gemm_kernel",),
-                "gemm_skinny.hip": ("dma_skinny_kernel", "dma_kmajor_kernel",
-                                    "mx_kmajor_kernel", "fused_dma_kernel")}
+                "gemm_skinny.hip": ("dma_skinny_kernel", "dma_kmajor_kernel", "mx_kmajor_kernel"),
+                "gemm_fused.hip": ("fused_dma_kernel",)}
 LDS_BYTES = 160 * 1024
 
 
