@@ -142,6 +142,51 @@ __device__ __forceinline__ void lds_write_b64(uint32_t addr, uint32_t lo, uint32
     asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(uint2{lo, hi}) : "memory");
 }
 
+// A 32-row m-tile found by one wave, its lanes reading the route step's tile
+// prefix sums in parallel. A decode block starts with a chain of dependent
+// loads, and a binary search over the experts' tile counts adds log2(E) of
+// them; here the lookup is one round of loads (two from 64 experts on), then
+// the expert's row count and offset. Lane l holds the sample tp[min(l S, E)],
+// S = 1 below 64 experts, else ceil((E + 1) / 64), so the second round's 64
+// lanes cover one sample's segment while E < 4096 (kWaveLookupMaxExperts);
+// every lane ends with the same result.
+constexpr int kWaveLookupMaxExperts = 4095;
+
+struct TileSamples {
+    int v, S, M;  // this lane's sample, the sample stride, the m-tile count tp[E]
+};
+
+__device__ __forceinline__ TileSamples tile_samples(const RouteView& rv, int E, int lane) {
+    const int32_t* tp = rv.tile_prefix + tile_height_index(32) * (E + 1);
+    TileSamples s;
+    s.S = E < 64 ? 1 : (E + 64) / 64;
+    s.v = tp[lane * s.S < E ? lane * s.S : E];
+    s.M = tp[E];
+    return s;
+}
+
+// m-tile g (0 <= g < s.M) of the samples' route.
+__device__ __forceinline__ void find_mtile_wave(const RouteView& rv, int E, const TileSamples& s, int g, int lane,
+                                                MTile& t) {
+    const int32_t* tp = rv.tile_prefix + tile_height_index(32) * (E + 1);
+    // tp is non-decreasing with tp[0] = 0 <= g < tp[E]: the expert is the last
+    // e < E with tp[e] <= g
+    int e = 63 - __clzll(__ballot(lane * s.S < E && s.v <= g));
+    int tpe = __shfl(s.v, e);
+    if (s.S > 1) {
+        const int e0 = e * s.S, j = e0 + lane;
+        const int v2 = lane < s.S && j < E ? tp[j] : 0x7fffffff;
+        const int l2 = 63 - __clzll(__ballot(v2 <= g));
+        e = e0 + l2;
+        tpe = __shfl(v2, l2);
+    }
+    t.expert = e;
+    t.m0 = (g - tpe) * 32;
+    const int c = rv.counts[e];
+    t.rows = c - t.m0 < 32 ? c - t.m0 : 32;
+    t.row0 = rv.offsets[e] + t.m0;
+}
+
 // 32-row m-tiles expected for T tokens with k routes each over E experts,
 // routes spread uniformly: the experts hit, each with ceil(rows / 32) tiles.
 inline double expected_mtiles32(int64_t T, int k, int E) {

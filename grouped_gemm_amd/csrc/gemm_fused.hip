@@ -93,7 +93,13 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (wave == 1) fused_write_unrouted(a, lane);  // overlaps wave 0's m-tile lookup
     MTile mt;
-    if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+    if (a.E > kWaveLookupMaxExperts) {
+        if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+    } else {
+        const TileSamples ts = tile_samples(a.rv, a.E, lane);
+        if (static_cast<int>(blockIdx.x) / nslices >= ts.M) return;
+        find_mtile_wave(a.rv, a.E, ts, blockIdx.x / nslices, lane, mt);
+    }
     const bool wmover = wave < 2;
     const int mw = wave & 1;
     const int h0 = slice * BH;

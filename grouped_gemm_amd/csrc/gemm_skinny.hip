@@ -355,8 +355,7 @@ struct DecodeWork {
 // (many experts hit), block b takes m-tile b whole (the grid holds at least
 // M blocks).
 template <int MIN>
-__device__ __forceinline__ bool decode_work(const RouteView& rv, int E, int groups, DecodeWork& w) {
-    const int M = rv.tile_prefix[tile_height_index(32) * (E + 1) + E];
+__device__ __forceinline__ bool decode_work_m(int M, int groups, DecodeWork& w) {
     const int B = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
     if (M <= 0) return false;
     if (M >= B) {
@@ -385,6 +384,22 @@ __device__ __forceinline__ bool decode_work(const RouteView& rv, int E, int grou
     return true;
 }
 
+// A decode block's work and its m-tile (the m-tile count and the lookup from
+// one wave-parallel read of the tile prefix sums, find_mtile_wave; a binary
+// search past kWaveLookupMaxExperts experts).
+template <int MIN>
+__device__ __forceinline__ bool decode_lookup(const RouteView& rv, int E, int groups, DecodeWork& w, MTile& mt) {
+    if (E > kWaveLookupMaxExperts) {
+        const int M = rv.tile_prefix[tile_height_index(32) * (E + 1) + E];
+        return decode_work_m<MIN>(M, groups, w) && find_mtile<32>(rv, E, w.mtile, mt);
+    }
+    const int lane = threadIdx.x & 63;
+    const TileSamples s = tile_samples(rv, E, lane);
+    if (!decode_work_m<MIN>(s.M, groups, w)) return false;
+    find_mtile_wave(rv, E, s, w.mtile, lane, mt);
+    return true;
+}
+
 // The decode GEMMs, k-major: a block (m-tile, G row groups: decode_work) walks K in
 // 256-value chunks and, within a chunk, up to kKmajorGroups groups, so each
 // chunk of the m-tile's 32 token rows (16 KB) is fetched once per chunk
@@ -410,10 +425,10 @@ __global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a) {
     static_assert((SW - 2) * W_INS < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) uint8_t lds[SW * T::W_BYTES + 2 * T::T_BYTES];
     uint8_t* const tring = lds + SW * T::W_BYTES;
+    static_assert(T::BM == 32, "32-row m-tiles");
     DecodeWork wk;
-    if (!decode_work<2>(a.rv, a.E, GEMM1 ? a.H / 32 : a.D / 64, wk)) return;
     MTile mt;
-    if (!find_mtile<T::BM>(a.rv, a.E, wk.mtile, mt)) return;
+    if (!decode_lookup<2>(a.rv, a.E, GEMM1 ? a.H / 32 : a.D / 64, wk, mt)) return;
     const int G = wk.n, nsg = (G + GSM - 1) / GSM;  // every super-group holds at least two groups
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, kg = lane >> 4;
@@ -741,10 +756,10 @@ __global__ __launch_bounds__(kThreads) void mx_kmajor_kernel(MxArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[SW * WSLOT + TSLOT];
     __shared__ float xamax[2][4][32];  // GEMM1: per token, the act maximum of each wave's 16 columns
     uint8_t* const tslot = lds + SW * WSLOT;
+    static_assert(kMx4BM == 32, "32-row m-tiles");
     DecodeWork wk;  // at least four row groups: every super-group then holds at least four
-    if (!decode_work<4>(a.rv, a.E, GEMM1 ? a.H / (R / 2) : a.D / R, wk)) return;
     MTile mt;
-    if (!find_mtile<kMx4BM>(a.rv, a.E, wk.mtile, mt)) return;
+    if (!decode_lookup<4>(a.rv, a.E, GEMM1 ? a.H / (R / 2) : a.D / R, wk, mt)) return;
     const int G = wk.n, nsg = (G + GSM - 1) / GSM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rb = wave % NB, kp = wave / NB;
