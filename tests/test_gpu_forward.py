@@ -110,6 +110,19 @@ def test_every_route_dropped(mode, T, D, H, E, k):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("T,D,H,E,k", [
+    (40, 256, 256, 1000, 4),    # the decode kernels' m-tile lookup in two rounds (64 and more experts)
+    (16, 256, 128, 4100, 4),    # past 4095 experts: the lookup falls back to the binary search
+])
+def test_many_experts(mode, T, D, H, E, k):
+    """Decode-shaped passes over many experts, most of them without a routed row."""
+    import grouped_gemm_amd as g
+    assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "bf16", mode, 1) == (
+        "fused_dma_kernel" if mode == "fused" else "dma_kmajor_kernel")
+    _case(mi.custom(T, D, H, E, k, "uniform"), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_decode_config_full(mode):
     _case(mi.CONFIGS[2], mode)
 
