@@ -184,7 +184,12 @@ MOE_FFN_API const char* moe_ffn_gemm_kernel(const moe_ffn_problem* p, int mode, 
             return moe::big_gemm_tile_rows(a) == 256 ? "big_gemm_kernel<256>" : "big_gemm_kernel<128>";
         return g1 ? "gemm1_swiglu_kernel" : "gemm2_weight_kernel";
     }
-    if (m == MOE_FFN_FUSED) return "mx_fused_kernel";
+    if (m == MOE_FFN_FUSED) {
+        moe::MxArgs f{};
+        f.T = p->T; f.D = p->D; f.H = p->H; f.E = p->E; f.k = p->topk;
+        f.w4 = p->dtype == MOE_FFN_MXFP4;
+        return moe::mx_fused_dma_supported(f) ? "mx_fused_dma_kernel" : "mx_fused_kernel";
+    }
     moe::MxArgs a{};
     a.T = p->T; a.D = p->D; a.H = p->H; a.E = p->E; a.k = p->topk;
     a.P = static_cast<int64_t>(p->T) * p->topk;
@@ -515,6 +520,7 @@ int forward_impl(const moe_ffn_problem* p, const void* x, const void* w1, const 
             e = moe::launch_split_mx(a, st, stage_ev);
         } else {
             a.acc32 = at<float>(ws, pl.acc32);
+            a.tcnt = at<int32_t>(ws, pl.tcnt);
             e = moe::launch_fused_mx(a, st, stage_ev);
         }
     }

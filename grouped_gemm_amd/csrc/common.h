@@ -220,6 +220,7 @@ struct MxArgs {
     uint16_t* out;      // [T, D]
     int32_t* mtiles;    // big_gemm_workspace_bytes for the prefill GEMMs
     float* acc32;       // [T, D] fused only
+    int32_t* tcnt;      // [T]    fused only: partial rows added per token (zero at entry)
     bool w4;            // MXFP4 weights: w1, w2 packed e2m1 [E, 2H, D/2], [E, D, H/2]
 };
 hipError_t launch_split_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
@@ -235,6 +236,11 @@ hipError_t launch_mx4_quantize(const float* src, int64_t rows, int32_t K, uint8_
 // split-K down projection over each 64-wide H slice into acc32 (fp32
 // atomics), then the conversion to bf16; `ev` (nullable) gets 3 events.
 hipError_t launch_fused_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev);
+// The fused MX pass on the decode kernels' rings (mx_fused_dma_kernel): e4m3
+// weights, D a multiple of 512, H of 128. Adds into a.acc32 (zero on entry)
+// and converts each token's row itself (a.tcnt zero on entry).
+bool mx_fused_dma_supported(const MxArgs& a);
+hipError_t launch_mx_fused_dma(const MxArgs& a, hipStream_t s);
 // Prefill-shaped MX GEMM1 / GEMM2 (the bf16 prefill kernels' ring on the scaled MFMA).
 bool big_mx_supported(const MxArgs& a);
 hipError_t launch_big_mx(const MxArgs& a, bool gemm1, hipStream_t s);

@@ -142,6 +142,55 @@ __device__ __forceinline__ void lds_write_b64(uint32_t addr, uint32_t lo, uint32
     asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(uint2{lo, hi}) : "memory");
 }
 
+// ---- MX decode geometry (mx_kmajor_kernel, the fused MX kernel) ----
+constexpr int kMx4KC = 512;   // K values per stage
+constexpr int kMx4BM = 32;    // token rows per m-tile
+
+template <int R, bool W4>
+struct Mx4 {
+    static constexpr int WRB = W4 ? kMx4KC / 2 : kMx4KC;  // weight bytes per row per stage (256 or 512)
+    static constexpr int WCH = WRB / 16;              // 16-byte chunks per weight row per stage
+    static constexpr int WRPI = 64 / WCH;             // weight rows per DMA instruction
+    static constexpr int TRB = kMx4KC;                // token bytes per row per stage (512)
+    static constexpr int WB = R * WRB;                // 32 KB
+    static constexpr int TB = kMx4BM * TRB;           // 16 KB
+    static constexpr int WINS = WB / 1024 / 4;        // weight DMA instructions per wave per stage
+    static constexpr int TINS = TB / 1024 / 4;        // token DMA instructions per wave per chunk
+    static constexpr int SWAVES = R / 64;             // waves that move weight scale rows
+};
+
+// Four k-steps' operands from LDS and a wait for them: two 16-byte chunks
+// and one scale byte each (e4m3 weights, or the token fragments); asm for
+// the same reason as lds_read8.
+__device__ __forceinline__ void mxk_read4x2(u32x4_t (&lo)[4], u32x4_t (&hi)[4], uint32_t (&sc)[4],
+                                            const uint32_t (&alo)[4], const uint32_t (&ahi)[4],
+                                            const uint32_t (&as)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b128 %4, %16\n\t"
+        "ds_read_b128 %5, %17\n\t"
+        "ds_read_b128 %6, %18\n\t"
+        "ds_read_b128 %7, %19\n\t"
+        "ds_read_u8 %8, %20\n\t"
+        "ds_read_u8 %9, %21\n\t"
+        "ds_read_u8 %10, %22\n\t"
+        "ds_read_u8 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+          "=&v"(hi[3]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3])
+        : "v"(alo[0]), "v"(alo[1]), "v"(alo[2]), "v"(alo[3]), "v"(ahi[0]), "v"(ahi[1]), "v"(ahi[2]), "v"(ahi[3]),
+          "v"(as[0]), "v"(as[1]), "v"(as[2]), "v"(as[3])
+        : "memory");
+}
+// A plain LDS store of a float in a ring slot, written as asm (as
+// lds_load4_f32: the compiler would drain the ring before its own access).
+__device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 // A 32-row m-tile found by one wave, its lanes reading the route step's tile
 // prefix sums in parallel. A decode block starts with a chain of dependent
 // loads, and a binary search over the experts' tile counts adds log2(E) of

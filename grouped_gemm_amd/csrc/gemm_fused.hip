@@ -32,6 +32,7 @@
 #include <cmath>
 
 #include "dma_ring.h"
+#include "mxq.h"
 
 namespace moe {
 
@@ -54,17 +55,96 @@ struct FusedTile {
 
 
 
+// What the fused kernels' completion steps need of a pass.
+struct FusedOut {
+    int T, D, k;
+    const int32_t* pair_to_sorted;
+    float* acc32;               // [T, D] fp32, the partial rows' sum
+    int32_t* tcnt;              // [T] partial rows added per token
+    uint16_t* out;              // [T, D] bf16
+    const uint16_t* shared_y;   // [T, D] bf16 or null: a shared expert's rows
+};
+
 // Tokens none of whose routes reach an expert get no partial rows: their
 // output is the shared expert's row, or zeros. One wave of block b takes
 // tokens b, b + gridDim.x, ... (k <= 64: a lane per route).
-__device__ void fused_write_unrouted(const Bf16Args& a, int lane) {
-    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
-        const bool routed = lane < a.k && a.rv.pair_to_sorted[static_cast<int64_t>(t) * a.k + lane] >= 0;
+__device__ void fused_write_unrouted(const FusedOut& o, int lane) {
+    for (int t = blockIdx.x; t < o.T; t += gridDim.x) {
+        const bool routed = lane < o.k && o.pair_to_sorted[static_cast<int64_t>(t) * o.k + lane] >= 0;
         if (__ballot(routed)) continue;
-        const int64_t row = static_cast<int64_t>(t) * a.D;
-        for (int c = lane; c < a.D / 8; c += 64)
-            *reinterpret_cast<u32x4_t*>(a.out + row + 8 * c) =
-                a.shared_y ? *reinterpret_cast<const u32x4_t*>(a.shared_y + row + 8 * c) : u32x4_t{0, 0, 0, 0};
+        const int64_t row = static_cast<int64_t>(t) * o.D;
+        for (int c = lane; c < o.D / 8; c += 64)
+            *reinterpret_cast<u32x4_t*>(o.out + row + 8 * c) =
+                o.shared_y ? *reinterpret_cast<const u32x4_t*>(o.shared_y + row + 8 * c) : u32x4_t{0, 0, 0, 0};
+    }
+}
+
+// The partial rows a token needs, H / BH per routed pair (prologue of the
+// fused kernels, by the threads of the m-tile's rows): unconditional loads
+// (indexes clamped to the token's k pairs), so they go out together with
+// the other per-row loads.
+__device__ __forceinline__ int fused_target(const FusedOut& o, int token, int nslices) {
+    const int64_t t0 = static_cast<int64_t>(token) * o.k;
+    int nv = 0;
+    for (int j0 = 0; j0 < o.k; j0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = o.pair_to_sorted[t0 + (j0 + u < o.k ? j0 + u : o.k - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) nv += (j0 + u < o.k && v[u] >= 0) ? 1 : 0;
+    }
+    return nv * nslices;
+}
+
+// The end of a fused block. A token's row is complete once each of its
+// routed pairs has had all H / BH slices' partials added. The token waves
+// (the ones that issued the adds) count this block's partial rows per token
+// once their adds are acknowledged (the adds and the counts are
+// device-scope atomics, performed where every XCD sees them); the block
+// whose count completes a row reads it back with device-scope loads and
+// converts it to bf16, plus the shared expert's row, into `out`. No block
+// waits on another, and no cache is written back or invalidated. sDone has
+// 33 entries; sDone[32] must be zero on entry.
+__device__ __forceinline__ void fused_finish(const FusedOut& o, int rows, bool adder, int wave, int lane,
+                                             const int* sTok, const int* sTgt, int* sDone) {
+    if (adder) wait_vm<0>();
+    __syncthreads();
+    if (wave == 2 && lane < rows) {
+        const int t = sTok[lane];
+        if (atomicAdd(o.tcnt + t, 1) + 1 == sTgt[lane]) sDone[atomicAdd(&sDone[32], 1)] = t;
+    }
+    __syncthreads();
+    const int ndone = sDone[32];
+    // The completed rows, four floats per item and U items per thread in
+    // flight: the loads (device scope, so they bypass caches that may hold
+    // stale lines) go out together from clamped, always valid indexes, and
+    // only the stores are predicated.
+    constexpr int U = 16;
+    const int per = o.D / 4, total = ndone * per;
+    for (int b0 = 0; b0 < total; b0 += U * kThreads) {
+        uint64_t lo[U], hi[U];
+        uint2 sy[U];
+        int64_t off[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int idx = b0 + u * kThreads + static_cast<int>(threadIdx.x);
+            idx = idx < total ? idx : total - 1;
+            const int i = idx / per;
+            off[u] = static_cast<int64_t>(sDone[i]) * o.D + 4 * (idx - i * per);
+            const uint64_t* src = reinterpret_cast<const uint64_t*>(o.acc32 + off[u]);
+            lo[u] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            hi[u] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sy[u] = o.shared_y ? *reinterpret_cast<const uint2*>(o.shared_y + off[u]) : uint2{0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (b0 + u * kThreads + static_cast<int>(threadIdx.x) >= total) continue;
+            const float v0 = __uint_as_float(static_cast<uint32_t>(lo[u])) + bf16_to_f32(static_cast<uint16_t>(sy[u].x & 0xffffu));
+            const float v1 = __uint_as_float(static_cast<uint32_t>(lo[u] >> 32)) + bf16_to_f32(static_cast<uint16_t>(sy[u].x >> 16));
+            const float v2 = __uint_as_float(static_cast<uint32_t>(hi[u])) + bf16_to_f32(static_cast<uint16_t>(sy[u].y & 0xffffu));
+            const float v3 = __uint_as_float(static_cast<uint32_t>(hi[u] >> 32)) + bf16_to_f32(static_cast<uint16_t>(sy[u].y >> 16));
+            *reinterpret_cast<uint2*>(o.out + off[u]) = uint2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
     }
 }
 
@@ -91,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     const int nslices = a.H / BH;
     const int slice = blockIdx.x % nslices;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (wave == 1) fused_write_unrouted(a, lane);  // overlaps wave 0's m-tile lookup
+    const FusedOut fo{a.T, a.D, a.k, a.rv.pair_to_sorted, a.acc32, a.tcnt, a.out, a.shared_y};
+    if (wave == 1) fused_write_unrouted(fo, lane);  // overlaps wave 0's m-tile lookup
     MTile mt;
     if (a.E > kWaveLookupMaxExperts) {
         if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
@@ -116,18 +197,8 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
         sRow[m] = static_cast<int64_t>(p / a.k) * a.D;
         sW[m] = m < mt.rows ? a.wts[p] : 0.0f;
         sTok[m] = p / a.k;
-        // routed pairs of the token: unconditional loads (indexes clamped to
-        // its k pairs), so they go out together with wts[p]
-        const int64_t t0 = static_cast<int64_t>(p / a.k) * a.k;
-        int nv = 0;
-        for (int j0 = 0; j0 < a.k; j0 += 8) {
-            int v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = a.rv.pair_to_sorted[t0 + (j0 + u < a.k ? j0 + u : a.k - 1)];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) nv += (j0 + u < a.k && v[u] >= 0) ? 1 : 0;
-        }
-        sTgt[m] = m < mt.rows ? nv * nslices : 0;
+        const int tg = fused_target(fo, p / a.k, nslices);
+        sTgt[m] = m < mt.rows ? tg : 0;
         if (m == 0) sDone[32] = 0;
     }
     const char* src[W_INS];
@@ -350,53 +421,381 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
             }
         }
     }
-    // A token's row is complete once each of its routed pairs has had all
-    // H / BH slices' partials added. The token waves count this block's
-    // partial rows per token once their adds are acknowledged (the adds and
-    // the counts are device-scope atomics, performed where every XCD sees
-    // them); the block whose count completes a row reads it back with
-    // device-scope loads and converts it to bf16, plus the shared expert's
-    // row, into `out`. No block waits on another, and no cache is written
-    // back or invalidated.
-    if (!wmover) wait_vm<0>();
-    __syncthreads();
-    if (wave == 2 && lane < mt.rows) {
-        const int t = sTok[lane];
-        if (atomicAdd(a.tcnt + t, 1) + 1 == sTgt[lane]) sDone[atomicAdd(&sDone[32], 1)] = t;
+    fused_finish(fo, mt.rows, !wmover, wave, lane, sTok, sTgt, sDone);
+}
+
+// ---------------- the fused MX-fp8 pass on the rings ----------------
+// The same pass with MX-fp8 operands ("Prime Flash MoE", section 7: e4m3
+// codes with an e8m0 scale per 32 along K; the act requantized on chip).
+// Phase 1 is mx_kmajor_kernel's GEMM1 on the slice's row groups: a stage is
+// one group's 64 W1 rows (32 act columns, gate and up rows interleaved
+// 4 + 4 per 8 rows) x 512 codes with their scale bytes, the m-tile's token
+// chunk of 512 codes rides with a chunk's first stage, and the four waves
+// are two 32-row blocks x two halves of the chunk's K (the halves meet in
+// LDS after the last chunk). After the last chunk each group's silu(gate)
+// * up is requantized by MXQ (one scale per token and group: the group's
+// 32 act columns are one MX block) into an act tile of e4m3 codes and
+// scale bytes in LDS. Phase 2 streams the slice's codes of every W2 row
+// (32 KB stages of R2 rows) with their scale bytes; the token waves run
+// the scaled 32 x 32 x 64 MFMA with the tokens as its rows and add the
+// results straight to the accumulator, as in fused_dma_kernel.
+template <int BH>
+struct MxFusedTile {
+    static constexpr int G1 = BH / 32;       // GEMM1 row groups per slice
+    static constexpr int R2 = 32768 / BH;    // W2 rows per stage (32 KB of codes)
+    static constexpr int CPR2 = BH / 16;     // 16-byte chunks per W2 (and act) row
+    static constexpr int RPI2 = 1024 / BH;   // W2 rows per DMA instruction
+    static constexpr int SB2 = BH / 32;      // scale bytes of a W2 (and act) row in the slice
+    static constexpr int KS2 = BH / 64;      // scaled-MFMA k-steps over the slice
+    static constexpr int FB2 = R2 / 64;      // 32-feature blocks of a token wave per stage
+    static constexpr int ACT = 32 * BH;      // act codes [32 tokens][BH]
+    static constexpr int ACTS = 32 * SB2;    // act scale bytes [32 tokens][BH / 32]
+    static_assert(BH == 128, "128-wide slices");
+    static_assert(R2 * SB2 == 1024, "a stage's W2 scales fill the slot's 1 KB scale area");
+};
+
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, u32x4_t v) {
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void lds_write_b8(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b8 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// grid: (m-tiles x slices), the slices of one m-tile consecutive.
+template <int BH, int SW>
+__global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a) {
+    using C = Mx4<64, false>;  // phase 1: 64 e4m3 weight rows x 512 codes per stage, 16 KB token chunks
+    using F = MxFusedTile<BH>;
+    constexpr int WSLOT = C::WB + 64 * 16;        // codes, then 64 scale rows of 16 bytes
+    constexpr int TSLOT = C::TB + 64 * 16;        // token codes, then 32 scale rows (and a 512-byte pad)
+    constexpr int W_INS = 2 * C::WINS, T_INS = 2 * C::TINS;  // per wave of the pair that moves them
+    constexpr int NSK = 4;                        // 64-code k-steps of a wave's half of a stage
+    static_assert(C::WB == 32768 && C::TB == 16384 && C::WRB == 512 && C::WCH == 32 && C::WRPI == 2, "geometry");
+    static_assert(W_INS * 1024 * 2 == C::WB && T_INS * 1024 * 2 == C::TB, "the pairs' DMAs");
+    static_assert(SW * WSLOT + TSLOT + F::ACT + F::ACTS <= 160 * 1024 - 1536, "LDS of a CU");
+    static_assert((SW - 2) * W_INS < 64, "vmcnt range");
+    static_assert(F::G1 >= 2, "a token chunk's slot is refilled at the chunk's second stage");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SW * WSLOT + TSLOT + F::ACT + F::ACTS];
+    __shared__ float xamax[2][2][32];  // per group parity, row block and token: the act maximum of 16 columns
+    __shared__ int64_t sRow[32];
+    __shared__ float sW[32];
+    __shared__ int sTok[32];
+    __shared__ int sTgt[32];
+    __shared__ int sDone[33];
+    uint8_t* const tslot = lds + SW * WSLOT;
+    uint8_t* const act = tslot + TSLOT;
+    uint8_t* const acts = act + F::ACT;
+    const int nslices = a.H / BH;
+    const int slice = blockIdx.x % nslices;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const FusedOut fo{a.T, a.D, a.k, a.rv.pair_to_sorted, a.acc32, a.tcnt, a.out, nullptr};
+    if (wave == 1) fused_write_unrouted(fo, lane);
+    MTile mt;
+    if (a.E > kWaveLookupMaxExperts) {
+        if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+    } else {
+        const TileSamples ts = tile_samples(a.rv, a.E, lane);
+        if (static_cast<int>(blockIdx.x) / nslices >= ts.M) return;
+        find_mtile_wave(a.rv, a.E, ts, blockIdx.x / nslices, lane, mt);
     }
-    __syncthreads();
-    const int ndone = sDone[32];
-    // The completed rows, four floats per item and U items per thread in
-    // flight: the loads (device scope, so they bypass caches that may hold
-    // stale lines) go out together from clamped, always valid indexes, and
-    // only the stores are predicated.
-    constexpr int U = 16;
-    const int per = a.D / 4, total = ndone * per;
-    for (int b0 = 0; b0 < total; b0 += U * kThreads) {
-        uint64_t lo[U], hi[U];
-        uint2 sy[U];
-        int64_t off[U];
+    const bool wmover = wave < 2;
+    const int mw = wave & 1;
+    const int rb = wave & 1, kp = wave >> 1;  // phase 1: row block and K half of this wave
+    const int lr = lane & 31, g = lane >> 5;
+    const int h0 = slice * BH;
+    const int DB = a.D / 32, HB = a.H / 32;   // scale bytes per W1 / W2 row
+    const int KIT1 = a.D / kMx4KC, NIT1 = F::G1 * KIT1, NG2 = a.D / F::R2, NIT = NIT1 + NG2;
+    const int kc0 = static_cast<int>(blockIdx.x) % KIT1;
+    const int rot = (blockIdx.x / nslices + slice) % NG2;
+    if (threadIdx.x < 32) {
+        const int m = threadIdx.x;
+        const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
+        sRow[m] = static_cast<int64_t>(p / a.k) * a.D;
+        sW[m] = m < mt.rows ? a.wts[p] : 0.0f;
+        sTok[m] = p / a.k;
+        const int tg = fused_target(fo, p / a.k, nslices);
+        sTgt[m] = m < mt.rows ? tg : 0;
+        if (m == 0) sDone[32] = 0;
+    }
+    // DMA sources. Weight waves: W1 code rows of group 0 (slot row r: act
+    // column h0 + 16 (r >> 5) + 4 ((r & 31) >> 3) + (r & 3), gate rows where
+    // r & 4 is clear, up rows where it is set), wave 0 also lane r's scale
+    // row. Token waves: the m-tile's token code rows, wave 2 also the token
+    // scale rows (lanes 32..63 repeat rows 0..31 into the slot's pad).
+    const char* src[W_INS];
+    const char* ssrc = nullptr;
+    auto w1row = [&](int r) -> int64_t {
+        const int col = h0 + 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3);
+        return static_cast<int64_t>(mt.expert) * 2 * a.H + ((r & 4) ? a.H + col : col);
+    };
+    auto trow = [&](int m) -> int64_t {
+        return clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P) / a.k;
+    };
+    if (wmover) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int idx = b0 + u * kThreads + static_cast<int>(threadIdx.x);
-            idx = idx < total ? idx : total - 1;
-            const int i = idx / per;
-            off[u] = static_cast<int64_t>(sDone[i]) * a.D + 4 * (idx - i * per);
-            const uint64_t* src = reinterpret_cast<const uint64_t*>(a.acc32 + off[u]);
-            lo[u] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            hi[u] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sy[u] = a.shared_y ? *reinterpret_cast<const uint2*>(a.shared_y + off[u]) : uint2{0, 0};
+        for (int j = 0; j < W_INS; ++j) {
+            const int row = (mw * W_INS + j) * C::WRPI + lane / C::WCH;
+            const int c = (lane & (C::WCH - 1)) ^ (row & (C::WCH - 1));
+            src[j] = reinterpret_cast<const char*>(a.w1) + w1row(row) * a.D + c * 16;
         }
+        if (mw == 0) ssrc = reinterpret_cast<const char*>(a.w1s) + w1row(lane) * DB;
+    } else {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (b0 + u * kThreads + static_cast<int>(threadIdx.x) >= total) continue;
-            const float v0 = __uint_as_float(static_cast<uint32_t>(lo[u])) + bf16_to_f32(static_cast<uint16_t>(sy[u].x & 0xffffu));
-            const float v1 = __uint_as_float(static_cast<uint32_t>(lo[u] >> 32)) + bf16_to_f32(static_cast<uint16_t>(sy[u].x >> 16));
-            const float v2 = __uint_as_float(static_cast<uint32_t>(hi[u])) + bf16_to_f32(static_cast<uint16_t>(sy[u].y & 0xffffu));
-            const float v3 = __uint_as_float(static_cast<uint32_t>(hi[u] >> 32)) + bf16_to_f32(static_cast<uint16_t>(sy[u].y >> 16));
-            *reinterpret_cast<uint2*>(a.out + off[u]) = uint2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        for (int j = 0; j < W_INS; ++j) {
+            const int m = (mw * T_INS + (j < T_INS ? j : 0)) * 2 + lane / 32;
+            const int c = (lane & 31) ^ (m & 31);
+            src[j] = reinterpret_cast<const char*>(a.x) + trow(m) * a.D + c * 16;
+        }
+        if (mw == 0) ssrc = reinterpret_cast<const char*>(a.xs) + trow(lane & 31) * DB;
+    }
+    __syncthreads();  // sRow / sW / sTgt, and every wave's index loads done before the ring starts
+    const int64_t gcode1 = static_cast<int64_t>(32) * a.D, gscale1 = static_cast<int64_t>(32) * DB;
+    const int64_t gcode2 = static_cast<int64_t>(F::R2) * a.H, gscale2 = static_cast<int64_t>(F::R2) * HB;
+    auto wslot_of = [&](int it) -> uint8_t* { return lds + (it % SW) * WSLOT; };
+    // weight stage `it`: phase 1 (group it % G1 of K chunk it / G1, the chunks
+    // walked from kc0) or phase 2 (R2 W2 rows of group (it - NIT1 + rot) %
+    // NG2, the slice's codes; their scale bytes as dwords, 2 x 2 DMAs)
+    auto issue_w = [&](int it) {
+        if (it == NIT1) {
+#pragma unroll
+            for (int j = 0; j < W_INS; ++j) {
+                const int row = (mw * W_INS + j) * F::RPI2 + lane / F::CPR2;
+                const int c = (lane & (F::CPR2 - 1)) ^ (row & (F::CPR2 - 1));
+                src[j] = reinterpret_cast<const char*>(a.w2) + (static_cast<int64_t>(mt.expert) * a.D + row) * a.H + h0 +
+                         c * 16;
+            }
+        }
+        uint8_t* slot = wslot_of(it);
+        if (it < NIT1) {
+            const int kr = (it / F::G1 + kc0) % KIT1, gr = it % F::G1;
+            const int64_t off = static_cast<int64_t>(kr) * kMx4KC + gr * gcode1;
+#pragma unroll
+            for (int j = 0; j < W_INS; ++j)
+                __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
+                                                 kWeightDmaAux);
+            if (mw == 0)
+                __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kr) * 16 + gr * gscale1,
+                                                 (lds_ptr_t)(slot + C::WB), 16, 0, 0);
+        } else {
+            const int gr = (it - NIT1 + rot) % NG2;
+            const int64_t off = gr * gcode2;
+#pragma unroll
+            for (int j = 0; j < W_INS; ++j)
+                __builtin_amdgcn_global_load_lds(src[j] + off, (lds_ptr_t)(slot + (mw * W_INS + j) * 1024), 16, 0,
+                                                 kWeightDmaAux);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int q = (2 * mw + i) * 64 + lane;  // dword q of the stage's 1 KB of scales
+                const int row = q / (F::SB2 / 4), part = q % (F::SB2 / 4);
+                const char* sp = reinterpret_cast<const char*>(a.w2s) +
+                                 (static_cast<int64_t>(mt.expert) * a.D + gr * F::R2 + row) * HB + h0 / 32 + 4 * part;
+                __builtin_amdgcn_global_load_lds(sp, (lds_ptr_t)(slot + C::WB + (2 * mw + i) * 256), 4, 0, 0);
+            }
+        }
+    };
+    // the token rows' K chunk kc (codes and scale bytes) into the token slot
+    auto issue_t = [&](int kc) {
+        const int kr = (kc + kc0) % KIT1;
+#pragma unroll
+        for (int j = 0; j < T_INS; ++j)
+            __builtin_amdgcn_global_load_lds(src[j] + static_cast<int64_t>(kr) * kMx4KC,
+                                             (lds_ptr_t)(tslot + (mw * T_INS + j) * 1024), 16, 0, 0);
+        if (mw == 0)
+            __builtin_amdgcn_global_load_lds(ssrc + static_cast<int64_t>(kr) * 16, (lds_ptr_t)(tslot + C::TB), 16, 0,
+                                             0);
+    };
+    // Stage `it` of the ring: each wave waits for its own DMAs of the stage
+    // (the weight waves: later stages keep at least W_INS each in flight;
+    // the token waves: the chunk's tokens, their only DMAs), one barrier,
+    // then the weight waves issue the stage SW - 1 ahead and the token waves,
+    // at a chunk's second stage, the next chunk (every wave read the token
+    // slot at the chunk's first stage).
+    auto ring_step = [&](int it) {
+        if (wmover) {
+            const int left = NIT - 1 - it;
+            const int n = SW - 2 < left ? SW - 2 : left;
+            if (n == SW - 2) wait_vm<(SW - 2) * W_INS>();
+            else if (n >= 1) wait_vm<W_INS>();
+            else wait_vm<0>();
+        } else if (it < NIT1 && it % F::G1 == 0) {
+            wait_vm<0>();
+        }
+        if (it == NIT1) lds_barrier();  // the act tile's last LDS writes are complete
+        else ring_barrier();
+        if (wmover) {
+            if (it + SW - 1 < NIT) issue_w(it + SW - 1);
+        } else if (it < NIT1 && it % F::G1 == 1 && it / F::G1 + 1 < KIT1) {
+            issue_t(it / F::G1 + 1);
+        }
+    };
+    if (wmover) {
+#pragma unroll
+        for (int j = 0; j < SW - 1; ++j) issue_w(j);
+    } else {
+        issue_t(0);
+    }
+    int it = 0;
+    {
+        f32x16_t acc[F::G1];
+#pragma unroll
+        for (int gi = 0; gi < F::G1; ++gi) acc[gi] = f32x16_t{};
+        const int row = 32 * rb + lr;  // this lane's weight row in the slot
+        for (int kc = 0; kc < KIT1; ++kc) {
+            u32x4_t tlo[NSK], thi[NSK];
+            uint32_t tsc[NSK];
+#pragma unroll
+            for (int gi = 0; gi < F::G1; ++gi, ++it) {
+                ring_step(it);
+                if (gi == 0) {
+                    uint32_t alo[4], ahi[4], as[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ks = kp * NSK + i, ct = 4 * ks + g;
+                        alo[i] = lds_addr(tslot + lr * C::TRB + ((ct ^ lr) << 4));
+                        ahi[i] = lds_addr(tslot + lr * C::TRB + (((ct + 2) ^ lr) << 4));
+                        as[i] = lds_addr(tslot + C::TB + lr * 16 + 2 * ks + g);
+                    }
+                    mxk_read4x2(tlo, thi, tsc, alo, ahi, as);
+                }
+                const uint8_t* slot = wslot_of(it);
+                uint32_t alo[4], ahi[4], as[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ks = kp * NSK + i, ct = 4 * ks + g;
+                    alo[i] = lds_addr(slot + row * C::WRB + ((ct ^ (row & (C::WCH - 1))) << 4));
+                    ahi[i] = lds_addr(slot + row * C::WRB + (((ct + 2) ^ (row & (C::WCH - 1))) << 4));
+                    as[i] = lds_addr(slot + C::WB + row * 16 + 2 * ks + g);
+                }
+                u32x4_t wl[4], wh[4];
+                uint32_t wsc[4];
+                mxk_read4x2(wl, wh, wsc, alo, ahi, as);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const i32x8_t aa{(int)wl[i].x, (int)wl[i].y, (int)wl[i].z, (int)wl[i].w,
+                                     (int)wh[i].x, (int)wh[i].y, (int)wh[i].z, (int)wh[i].w};
+                    const i32x8_t bt{(int)tlo[i].x, (int)tlo[i].y, (int)tlo[i].z, (int)tlo[i].w,
+                                     (int)thi[i].x, (int)thi[i].y, (int)thi[i].z, (int)thi[i].w};
+                    acc[gi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aa, bt, acc[gi], 0, 0, 0, (int)wsc[i],
+                                                                             0, (int)tsc[i]);
+                }
+                if (kc != KIT1 - 1) continue;
+                // group gi complete: the K halves meet in the slot just consumed
+                // (free until the next stage's barrier); acc[gi][v]: slot row
+                // 32 rb + 8 (v / 4) + 4 g + v % 4, token lr
+                f32x16_t v = acc[gi];
+                const uint32_t red = lds_addr(slot);
+                lds_barrier();
+                if (kp == 1) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) lds_store_f32(red + ((rb * 16 + q) * 64 + lane) * 4, v[q]);
+                }
+                lds_barrier();
+                float amax = 0.0f, actv[16];
+                if (kp == 0) {
+#pragma unroll
+                    for (int q0 = 0; q0 < 16; q0 += 4) {
+                        uint32_t pq[4];
+                        float o[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pq[i] = red + ((rb * 16 + q0 + i) * 64 + lane) * 4;
+                        lds_load4_f32(o, pq);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[q0 + i] += o[i];
+                    }
+                }
+                // gate rows in lanes g = 0, the matching up rows 32 lanes away
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const float up = __shfl_xor(v[q], 32);
+                    actv[q] = v[q] / (1.0f + __expf(-v[q])) * up;
+                    amax = fmaxf(amax, fabsf(actv[q]));
+                }
+                const int buf = gi & 1;
+                if (kp == 0 && g == 0) xamax[buf][rb][lr] = amax;
+                lds_barrier();
+                if (kp == 0 && g == 0) {
+                    // MXQ of the group's 32 act columns for token lr: this lane
+                    // holds 16 of them (columns 32 gi + 16 rb + q), the other
+                    // row block's wave the rest
+                    const int sc = mx_scale_exp(fmaxf(amax, xamax[buf][rb ^ 1][lr]));
+                    const float inv = pow2f(-sc);
+                    uint32_t code[4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        code[q4] = e4m3_encode(actv[4 * q4] * inv, actv[4 * q4]) |
+                                   (e4m3_encode(actv[4 * q4 + 1] * inv, actv[4 * q4 + 1]) << 8) |
+                                   (e4m3_encode(actv[4 * q4 + 2] * inv, actv[4 * q4 + 2]) << 16) |
+                                   (e4m3_encode(actv[4 * q4 + 3] * inv, actv[4 * q4 + 3]) << 24);
+                    const int c = 2 * gi + rb;  // the 16-byte chunk of the act row
+                    lds_write_b128(lds_addr(act + lr * BH + ((c ^ (lr & (F::CPR2 - 1))) << 4)),
+                                   u32x4_t{code[0], code[1], code[2], code[3]});
+                    if (rb == 0) lds_write_b8(lds_addr(acts + lr * F::SB2 + gi), static_cast<uint32_t>(sc + 127));
+                }
+            }
         }
     }
+    for (; it < NIT; ++it) {
+        ring_step(it);
+        if (wmover) continue;
+        // phase 2, token waves only: act tile x the stage's R2 W2 rows, each
+        // wave half of the rows in 32-feature blocks, on the scaled 32 x 32 x
+        // 64 MFMA with the tokens as its rows (act the A operand)
+        const uint8_t* slot = wslot_of(it);
+        f32x16_t y[F::FB2];
+#pragma unroll
+        for (int fb = 0; fb < F::FB2; ++fb) y[fb] = f32x16_t{};
+        const int fl = (wave - 2) * (F::R2 / 2) + lr;  // this lane's feature row in block 0
+#pragma unroll
+        for (int s0 = 0; s0 < F::KS2; s0 += 2) {
+            // two k-steps at a time (mxk_read4x2 takes four operands: act and W2 of steps s0, s0 + 1)
+            uint32_t alo[4], ahi[4], as[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int ct = 4 * (s0 + i) + g;
+                alo[i] = lds_addr(act + lr * BH + ((ct ^ (lr & (F::CPR2 - 1))) << 4));
+                ahi[i] = lds_addr(act + lr * BH + (((ct + 2) ^ (lr & (F::CPR2 - 1))) << 4));
+                as[i] = lds_addr(acts + lr * F::SB2 + 2 * (s0 + i) + g);
+            }
+#pragma unroll
+            for (int fb = 0; fb < F::FB2; ++fb) {
+                const int f = fl + 32 * fb;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int ct = 4 * (s0 + i) + g;
+                    alo[2 + i] = lds_addr(slot + f * BH + ((ct ^ (f & (F::CPR2 - 1))) << 4));
+                    ahi[2 + i] = lds_addr(slot + f * BH + (((ct + 2) ^ (f & (F::CPR2 - 1))) << 4));
+                    as[2 + i] = lds_addr(slot + C::WB + f * F::SB2 + 2 * (s0 + i) + g);
+                }
+                u32x4_t lo[4], hi[4];
+                uint32_t sc[4];
+                mxk_read4x2(lo, hi, sc, alo, ahi, as);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const i32x8_t av{(int)lo[i].x, (int)lo[i].y, (int)lo[i].z, (int)lo[i].w,
+                                     (int)hi[i].x, (int)hi[i].y, (int)hi[i].z, (int)hi[i].w};
+                    const i32x8_t bw{(int)lo[2 + i].x, (int)lo[2 + i].y, (int)lo[2 + i].z, (int)lo[2 + i].w,
+                                     (int)hi[2 + i].x, (int)hi[2 + i].y, (int)hi[2 + i].z, (int)hi[2 + i].w};
+                    y[fb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bw, y[fb], 0, 0, 0, (int)sc[i], 0,
+                                                                           (int)sc[2 + i]);
+                }
+            }
+        }
+        const int d0 = ((it - NIT1 + rot) % NG2) * F::R2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int mlo = ((v >> 2) << 3) + (v & 3);  // lanes 0-31: token row mlo, lanes 32-63: mlo + 4
+            if (mlo >= mt.rows) continue;
+            const int m = mlo + (g << 2);
+            if (m < mt.rows) {
+                float* dst = a.acc32 + sRow[m] + d0 + fl;
+                const float w = sW[m];
+#pragma unroll
+                for (int fb = 0; fb < F::FB2; ++fb) unsafeAtomicAdd(dst + 32 * fb, w * y[fb][v]);
+            }
+        }
+    }
+    fused_finish(fo, mt.rows, !wmover, wave, lane, sTok, sTgt, sDone);
 }
 
 inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P + bm - 1) / bm + E); }
@@ -442,6 +841,20 @@ int fused_slice(const Bf16Args& a) {
     for (int bh : {256, 128})
         if (fill(bh) >= 0.95 * best) return bh;
     return 64;
+}
+
+bool mx_fused_dma_supported(const MxArgs& a) {
+    return !a.w4 && a.D % kMx4KC == 0 && a.H % 128 == 0;
+}
+
+// The MX kernel runs 128-wide slices: with 256 its eight groups'
+// accumulators, the token and weight fragments and the requantization
+// would not fit the registers (the compiler spills).
+hipError_t launch_mx_fused_dma(const MxArgs& a, hipStream_t s) {
+    constexpr int BH = 128;
+    const int64_t blocks = static_cast<int64_t>(mtiles_upper(a.P, a.E, 32)) * (a.H / BH);
+    mx_fused_dma_kernel<BH, 4><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s) {

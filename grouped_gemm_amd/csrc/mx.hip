@@ -528,10 +528,19 @@ inline int mtiles_upper(int64_t P, int E, int bm) { return static_cast<int>((P +
 
 }  // namespace
 
+// The route step has cleared acc32 and the token counters. The ring kernel
+// converts each token's row itself; the generic one leaves the conversion to
+// a kernel of its own.
 hipError_t launch_fused_mx(const MxArgs& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int BM = 128;
     const int64_t n = static_cast<int64_t>(a.T) * a.D;
-    record(ev, 0, s);  // the route step has cleared acc32
+    record(ev, 0, s);
+    if (mx_fused_dma_supported(a)) {
+        const hipError_t e = launch_mx_fused_dma(a, s);
+        record(ev, 1, s);
+        record(ev, 2, s);
+        return e;
+    }
     dim3 g(mtiles_upper(a.P, a.E, BM), a.H / kFusedSlice);
     mx_fused_kernel<BM><<<g, kThreads, 0, s>>>(a);
     record(ev, 1, s);

@@ -75,7 +75,7 @@ TILE_ROWS = {
     "big_gemm_kernel<128>": 128, "big_gemm_kernel<256>": 256,
     "gemm1_swiglu_kernel": 128, "gemm2_weight_kernel": 128,
     "mx_gemm1_kernel": 128, "mx_gemm2_kernel": 128,
-    "fused_dma_kernel": 32, "fused_bf16_kernel": 128, "mx_fused_kernel": 128,
+    "fused_dma_kernel": 32, "fused_bf16_kernel": 128, "mx_fused_kernel": 128, "mx_fused_dma_kernel": 32,
 }
 
 

@@ -59,9 +59,11 @@ def _case(cfg, tokens=None, seed=0, mode="split", ids=None):
     if ids is not None:
         src["topk_ids"] = ids
     (xc, xs), (w1c, w1s), (w2c, w2s) = q["x"], q["w1"], q["w2"]
-    out = g.moe_ffn_forward(to_gpu(xc), to_gpu(w1c), to_gpu(w2c), to_gpu(src["topk_ids"]),
-                            to_gpu(src["topk_weights"]), mode=mode, x_scale=to_gpu(xs),
-                            w1_scale=to_gpu(w1s), w2_scale=to_gpu(w2s))
+    # the output starts as NaN, so a row the pass leaves unwritten fails the comparison
+    out = torch.full((cfg.T, cfg.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    g.moe_ffn_forward(to_gpu(xc), to_gpu(w1c), to_gpu(w2c), to_gpu(src["topk_ids"]),
+                      to_gpu(src["topk_weights"]), out=out, mode=mode, x_scale=to_gpu(xs),
+                      w1_scale=to_gpu(w1s), w2_scale=to_gpu(w2s))
     torch.cuda.synchronize()
     out = gpu_bf16_to_f64(out)
     ref = mi.bf16_bits_to_f32(oracle.forward_mx(xc, xs, w1c, w1s, w2c, w2s, src["topk_ids"],
@@ -165,6 +167,36 @@ def test_mx_forward_fused(T, D, H, E, k, routing):
     """The fused MX pipeline: the act requantized in LDS feeds a split-K down
     projection per 64-wide H slice (two scale blocks: one scaled-MFMA K step)."""
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"), mode="fused")
+
+
+@pytest.mark.parametrize("T,D,H,E,k,routing", [
+    (64, 4096, 1536, 64, 6, "softmax"),  # the MX workload's dims at 64 tokens
+    (1, 512, 256, 4, 2, "uniform"),      # a single token
+    (40, 1024, 640, 16, 8, "zipf"),      # five slices of H, hot experts with several m-tiles
+    (64, 512, 384, 4, 4, "uniform"),     # k = E
+    (300, 1024, 256, 8, 2, "zipf"),      # many 32-row m-tiles per expert, ragged last tiles
+])
+def test_mx_fused_ring_kernel(T, D, H, E, k, routing):
+    """The fused MX pass on the decode kernels' rings: GEMM1 k-major, the act
+    requantized by MXQ into LDS per 32 columns, the down projection with the
+    tokens as the scaled MFMA's rows added into the fp32 accumulator, each
+    token's row converted by the block that adds its last partial."""
+    import grouped_gemm_amd as g
+    assert g.moe_ffn_gemm_kernel(T, D, H, E, k, "mxfp8", "fused", 1) == "mx_fused_dma_kernel"
+    _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"), mode="fused")
+
+
+def test_mx_fused_ring_kernel_dropped_routes():
+    """Dropped routes, tokens with no route at all (their rows are zeros) and
+    zero routing weights on the fused MX ring kernel."""
+    cfg = mi.custom(96, 512, 512, 8, 4, "uniform", dtype="mxfp8")
+    ids, _ = mi.routing(cfg, 0)
+    ids = ids.copy()
+    ids[::3, 1] = -1
+    ids[1::5, 2] = 8                      # == E: dropped
+    ids[7, :] = -1                        # no route at all
+    ids[11, :] = 9
+    _case(cfg, ids=ids, mode="fused")
 
 
 def test_mx_fused_config_sampled():
