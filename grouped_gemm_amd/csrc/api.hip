@@ -41,8 +41,9 @@ int check_shape(const moe_ffn_problem* p) {
 
 // AUTO resolves to the fused pipeline for bf16 passes bound by launch
 // latency (moe::fused_preferred: a few MB of expert weights streamed, where
-// its two kernels beat the split pipeline's four) and to the
-// split pipeline otherwise: where the weights stream from HBM the split
+// its two kernels beat the split pipeline's four), for MX-fp8 passes whose
+// fused blocks fit one round of the CUs (moe::mx_fused_preferred), and to
+// the split pipeline otherwise: where the weights stream from HBM the split
 // pipeline's decode kernels are as fast or faster, and at prefill sizes the
 // fused pipeline's split-K partial rows cost fp32 atomic adds into the
 // accumulator (P * H/slice * D of them, at about 330 G adds/s on MI355X's
@@ -50,9 +51,11 @@ int check_shape(const moe_ffn_problem* p) {
 int resolve(const moe_ffn_problem* p, int mode) {
     if (mode != MOE_FFN_AUTO && mode != MOE_FFN_FUSED && mode != MOE_FFN_SPLIT) return MOE_FFN_EUNSUPPORTED;
     if (p->dtype == MOE_FFN_MXFP4) return mode == MOE_FFN_FUSED ? MOE_FFN_EUNSUPPORTED : MOE_FFN_SPLIT;
-    if (mode == MOE_FFN_AUTO)
-        return p->dtype == MOE_FFN_BF16 && moe::fused_preferred(p->T, p->D, p->H, p->E, p->topk) ? MOE_FFN_FUSED
-                                                                                                 : MOE_FFN_SPLIT;
+    if (mode == MOE_FFN_AUTO) {
+        const bool fused = p->dtype == MOE_FFN_BF16 ? moe::fused_preferred(p->T, p->D, p->H, p->E, p->topk)
+                                                    : moe::mx_fused_preferred(p->T, p->D, p->H, p->E, p->topk);
+        return fused ? MOE_FFN_FUSED : MOE_FFN_SPLIT;
+    }
     return mode;
 }
 

@@ -204,6 +204,7 @@ hipError_t launch_fused_bf16(const Bf16Args& a, hipStream_t s, hipEvent_t* ev);
 bool fused_decode_supported(const Bf16Args& a);
 // Whether AUTO runs a bf16 pass (no activation variant) on the fused pipeline.
 bool fused_preferred(int64_t T, int D, int H, int E, int k);
+bool mx_fused_preferred(int64_t T, int D, int H, int E, int k);
 hipError_t launch_fused_decode(const Bf16Args& a, hipStream_t s);
 
 struct MxArgs {

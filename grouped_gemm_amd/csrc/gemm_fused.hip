@@ -817,6 +817,18 @@ bool fused_preferred(int64_t T, int D, int H, int E, int k) {
     return expected_mtiles32(T, k, E) * 3.0 * H * D * 2.0 <= 16e6;
 }
 
+// AUTO's pipeline for an MX-fp8 pass: the fused ring kernel streams the
+// same weights as the split decode kernels in one launch instead of three,
+// and wins while its (m-tile, slice) blocks fit one round of the CUs; past
+// that each further round pays a block start and a ring fill again.
+// Measured (graph replay, fused / split) at D=4096, H=1536, E=64, k=6: 0.93,
+// 0.99, 0.95 at 1, 2 and 4 tokens (72, 138 and 250 expected blocks), 1.04
+// at 8 (419 blocks), 1.15 at 16.
+bool mx_fused_preferred(int64_t T, int D, int H, int E, int k) {
+    if (D % 512 || H % 128) return false;  // the MX fused ring kernel's shapes
+    return expected_mtiles32(T, k, E) * (H / 128) <= device_cu_count();
+}
+
 bool fused_decode_supported(const Bf16Args& a) {
     return a.D % 256 == 0 && a.H % 128 == 0 && !a.av.on();
 }

@@ -56,7 +56,10 @@ enum { MOE_FFN_BF16 = 0, MOE_FFN_MXFP8 = 1, MOE_FFN_MXFP4 = 2 };
  * down projection as a plain grouped GEMM. AUTO resolves to FUSED for bf16
  * passes bound by launch latency (up to 16 MB of expert weights streamed,
  * one expert's weights per 32 routed rows, with D a multiple of 256 and H of
- * 128), where it measured faster on MI355X, and to SPLIT otherwise. */
+ * 128) and for MX-fp8 passes whose fused blocks (expected 32-row m-tiles
+ * times H/128) fit one round of the device's compute units (D a multiple
+ * of 512, H of 128), where it measured faster on MI355X, and to SPLIT
+ * otherwise. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_FUSED = 1, MOE_FFN_SPLIT = 2 };
 
 enum {

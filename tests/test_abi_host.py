@@ -70,7 +70,14 @@ def test_resolve_mode():
     assert g.moe_ffn_resolve_mode(64, 6144, 2048, 32, 8, mode="auto") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(16, 2048, 768, 128, 8, mode="auto") == g.MOE_FFN_SPLIT
     assert g.moe_ffn_resolve_mode(131072, 2048, 768, 128, 8, mode="auto") == g.MOE_FFN_SPLIT
-    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, dtype="mxfp8") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_resolve_mode(64, 256, 512, 8, 2, dtype="mxfp8") == g.MOE_FFN_SPLIT   # not the MX ring's shapes
+    # MX-fp8: fused while its (m-tile, 128-wide slice) blocks fit one round of the 256 CUs
+    # (expected m-tiles x H/128: 72, 250 and 419 blocks at 1, 4 and 8 tokens)
+    assert g.moe_ffn_resolve_mode(1, 4096, 1536, 64, 6, dtype="mxfp8") == g.MOE_FFN_FUSED
+    assert g.moe_ffn_resolve_mode(4, 4096, 1536, 64, 6, dtype="mxfp8") == g.MOE_FFN_FUSED
+    assert g.moe_ffn_resolve_mode(8, 4096, 1536, 64, 6, dtype="mxfp8") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_resolve_mode(16384, 4096, 1536, 64, 6, dtype="mxfp8") == g.MOE_FFN_SPLIT
+    assert g.moe_ffn_resolve_mode(4, 4096, 1536, 64, 6, dtype="mxfp4") == g.MOE_FFN_SPLIT
 
 
 def test_workspace_sizes():
