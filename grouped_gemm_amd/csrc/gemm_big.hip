@@ -513,10 +513,14 @@ __device__ __forceinline__ void issue_stage(uint8_t* tok, uint8_t* wt, ScaleSlot
 // every later step waits for everything. Hand-over: step 0 fetches the next
 // tile's row map (landed by step 1's barrier), step 1 its routing weights,
 // and step KT - 1 builds its DMA sources and issues its stage 0.
+// A wave whose token rows all lie past the tile's rows (`live` false: the
+// short last m-tile of an expert) moves its share of the DMAs and keeps the
+// barriers, but reads no fragments and issues no MFMAs; its accumulators stay
+// zero and its epilogue stores go to the sink.
 template <int BM, bool GEMM1, bool MX, bool VAR, bool W4, int B, bool FIRST, bool SECOND>
 __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, StageBufs<BM>& L, ScaleSlot<BM>* sc,
                                           int kt, int32_t (*pairs)[BM], float (*wrow)[BM], const LaneOff& o,
-                                          Regs<BM, MX>& g, f32x16_t (&acc)[4][Big<BM, MX>::NT]) {
+                                          Regs<BM, MX>& g, f32x16_t (&acc)[4][Big<BM, MX>::NT], bool live) {
     // stage kt is in buffer B (B = kt & 1); stage kt + 1 goes into the other
     const uint8_t* ct = L.tok[B];
     const uint8_t* cw = L.wt[B];
@@ -536,6 +540,7 @@ __device__ __forceinline__ void ring_step(const BigArgs& a, Ring<BM, MX>& r, Sta
         make_src<BM, GEMM1, MX, W4>(a, r.next, pairs[r.nb], r.wave, r.src);
         issue_stage<BM, MX, W4>(L.tok[B ^ 1], L.wt[B ^ 1], osc, r.src, r, 0);
     }
+    if (!live) return;
     if constexpr (!MX) {
         read_q<BM, GEMM1, 0>(ct, cw, o, g.x);
         if (!FIRST) mfma_half<BM>(g.y, acc);
@@ -798,17 +803,20 @@ __global__ __launch_bounds__(kThreads, 1) void big_gemm_kernel(BigArgs a, const 
             r.next = uniform_desc(sDesc[(i + 1) % CAP]);
         }
         r.cont = r.has_next;
+        const bool live = uniform_int(tok_row0 < t.rows ? 1 : 0) != 0;
 
         // KT is even: every tile starts in buffer 0
-        ring_step<BM, GEMM1, MX, VAR, W4, 0, true, false>(a, r, L, sSc, 0, sPair, sW, o, g, acc);
-        ring_step<BM, GEMM1, MX, VAR, W4, 1, false, true>(a, r, L, sSc, 1, sPair, sW, o, g, acc);
+        ring_step<BM, GEMM1, MX, VAR, W4, 0, true, false>(a, r, L, sSc, 0, sPair, sW, o, g, acc, live);
+        ring_step<BM, GEMM1, MX, VAR, W4, 1, false, true>(a, r, L, sSc, 1, sPair, sW, o, g, acc, live);
         for (int kt = 2; kt < r.KT; kt += 2) {
-            ring_step<BM, GEMM1, MX, VAR, W4, 0, false, false>(a, r, L, sSc, kt, sPair, sW, o, g, acc);
-            ring_step<BM, GEMM1, MX, VAR, W4, 1, false, false>(a, r, L, sSc, kt + 1, sPair, sW, o, g, acc);
+            ring_step<BM, GEMM1, MX, VAR, W4, 0, false, false>(a, r, L, sSc, kt, sPair, sW, o, g, acc, live);
+            ring_step<BM, GEMM1, MX, VAR, W4, 1, false, false>(a, r, L, sSc, kt + 1, sPair, sW, o, g, acc, live);
         }
         // the last unit of the last stage
-        if constexpr (MX) mfma_mx<BM, 1, W4>(g.wb, g.t, acc);
-        else mfma_half<BM>(g.y, acc);
+        if (live) {
+            if constexpr (MX) mfma_mx<BM, 1, W4>(g.wb, g.t, acc);
+            else mfma_half<BM>(g.y, acc);
+        }
 
         if constexpr (GEMM1 && MX) epilogue_mx_gemm1<BM>(a, t, tok_row0, wf, sOut[wave_v], acc);
         else epilogue_bf16<BM, GEMM1, MX, VAR>(a, t, sPair[cb], sW[cb], tok_row0, wf, sOut[wave_v], acc);

@@ -189,6 +189,15 @@ def test_mx_fused_ring_kernel(T, D, H, E, k, routing):
     _case(mi.custom(T, D, H, E, k, routing, dtype="mxfp8"), mode="fused")
 
 
+def test_mx_auto_small_batch_runs_fused():
+    """AUTO takes the fused MX pipeline for a batch whose fused blocks fit one
+    round of the CUs (4 tokens: about 13 m-tiles x 8 slices)."""
+    import grouped_gemm_amd as g
+    assert g.moe_ffn_resolve_mode(4, 2048, 1024, 32, 4, dtype="mxfp8") == g.MOE_FFN_FUSED
+    assert g.moe_ffn_gemm_kernel(4, 2048, 1024, 32, 4, "mxfp8", "auto", 1) == "mx_fused_dma_kernel"
+    _case(mi.custom(4, 2048, 1024, 32, 4, "softmax", dtype="mxfp8"), mode="auto")
+
+
 def test_mx_fused_ring_kernel_dropped_routes():
     """Dropped routes, tokens with no route at all (their rows are zeros) and
     zero routing weights on the fused MX ring kernel."""
