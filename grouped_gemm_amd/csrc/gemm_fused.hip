@@ -148,7 +148,17 @@ __device__ __forceinline__ void fused_finish(const FusedOut& o, int rows, bool a
     }
 }
 
-// grid: (m-tiles x slices), the slices of one m-tile consecutive.
+// Logical block of block b among the grid's first G blocks, XCD-major:
+// block b runs on XCD b % 8 (8 XCDs, each with its own L2), and XCD x takes
+// logical blocks S_x .. S_x + n_x - 1 in order, n_x = |{b < G : b % 8 = x}|.
+// The m-tiles of one expert are consecutive logical blocks, so they run side
+// by side on one XCD and its L2 serves the expert's weights to all of them.
+__device__ __forceinline__ int xcd_major(int b, int G) {
+    const int x = b & 7, q = G >> 3, r = G & 7;
+    return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// Logical grid: (m-tiles x slices), the slices of one m-tile consecutive.
 template <int BH, int SW>
 __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     using T = DmaTile<2, 256, 2>;  // phase 1: 512-byte row segments, KC = 256 values per stage
@@ -169,28 +179,33 @@ __global__ __launch_bounds__(kThreads) void fused_dma_kernel(Bf16Args a) {
     uint8_t* const tring = lds + SW * T::W_BYTES;
     uint8_t* const act = tring + 2 * T::T_BYTES;
     const int nslices = a.H / BH;
-    const int slice = blockIdx.x % nslices;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const FusedOut fo{a.T, a.D, a.k, a.rv.pair_to_sorted, a.acc32, a.tcnt, a.out, a.shared_y};
     if (wave == 1) fused_write_unrouted(fo, lane);  // overlaps wave 0's m-tile lookup
     MTile mt;
+    int lb = blockIdx.x;  // logical block
     if (a.E > kWaveLookupMaxExperts) {
-        if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+        if (!find_mtile<32>(a.rv, a.E, lb / nslices, mt)) return;
     } else {
         const TileSamples ts = tile_samples(a.rv, a.E, lane);
-        if (static_cast<int>(blockIdx.x) / nslices >= ts.M) return;
-        find_mtile_wave(a.rv, a.E, ts, blockIdx.x / nslices, lane, mt);
+        const int G = ts.M * nslices;
+        if (static_cast<int>(blockIdx.x) >= G) return;
+        lb = xcd_major(blockIdx.x, G);
+        find_mtile_wave(a.rv, a.E, ts, lb / nslices, lane, mt);
     }
+    const int slice = lb % nslices;
     const bool wmover = wave < 2;
     const int mw = wave & 1;
     const int h0 = slice * BH;
     const int r = lane & 15, kg = lane >> 4;
     const int KIT1 = a.D / 256, NIT1 = F::G1 * KIT1, NG2 = a.D / F::R2, NIT = NIT1 + NG2;
-    // each block starts its phase-1 K walk at its own chunk and its phase-2
-    // walk at its own W2 row group, so the blocks' reads spread over the HBM
-    // channels instead of crowding a few
-    const int kc0 = static_cast<int>(blockIdx.x) % KIT1;
-    const int rot = (blockIdx.x / nslices + slice) % NG2;
+    // the blocks of one (expert, slice) walk K and the W2 row groups in the
+    // same order, so one XCD's L2 serves their common weights; each (expert,
+    // slice) starts at its own chunk and row group, so the reads of different
+    // weights spread over the HBM channels instead of crowding a few
+    const int es = mt.expert * nslices + slice;
+    const int kc0 = es % KIT1;
+    const int rot = es % NG2;
     if (threadIdx.x < 32) {
         const int m = threadIdx.x;
         const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
@@ -487,11 +502,13 @@ __global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a) {
     uint8_t* const act = tslot + TSLOT;
     uint8_t* const acts = act + F::ACT;
     const int nslices = a.H / BH;
-    const int slice = blockIdx.x % nslices;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const FusedOut fo{a.T, a.D, a.k, a.rv.pair_to_sorted, a.acc32, a.tcnt, a.out, nullptr};
     if (wave == 1) fused_write_unrouted(fo, lane);
     MTile mt;
+    // grid order (m-tile-major, slices consecutive): measured faster here
+    // than fused_dma_kernel's XCD-major order from 1024 tokens of the MX
+    // workload's dims on (its twelve 128-wide slices' atomic adds dominate)
     if (a.E > kWaveLookupMaxExperts) {
         if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
     } else {
@@ -499,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a) {
         if (static_cast<int>(blockIdx.x) / nslices >= ts.M) return;
         find_mtile_wave(a.rv, a.E, ts, blockIdx.x / nslices, lane, mt);
     }
+    const int slice = blockIdx.x % nslices;
     const bool wmover = wave < 2;
     const int mw = wave & 1;
     const int rb = wave & 1, kp = wave >> 1;  // phase 1: row block and K half of this wave
