@@ -479,7 +479,7 @@ __device__ __forceinline__ void lds_write_b8(uint32_t addr, uint32_t v) {
 
 // grid: (m-tiles x slices), the slices of one m-tile consecutive.
 template <int BH, int SW>
-__global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a) {
+__global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a, int one_round) {
     using C = Mx4<64, false>;  // phase 1: 64 e4m3 weight rows x 512 codes per stage, 16 KB token chunks
     using F = MxFusedTile<BH>;
     constexpr int WSLOT = C::WB + 64 * 16;        // codes, then 64 scale rows of 16 bytes
@@ -506,17 +506,23 @@ __global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a) {
     const FusedOut fo{a.T, a.D, a.k, a.rv.pair_to_sorted, a.acc32, a.tcnt, a.out, nullptr};
     if (wave == 1) fused_write_unrouted(fo, lane);
     MTile mt;
-    // grid order (m-tile-major, slices consecutive): measured faster here
-    // than fused_dma_kernel's XCD-major order from 1024 tokens of the MX
-    // workload's dims on (its twelve 128-wide slices' atomic adds dominate)
+    // Block order: XCD-major as in fused_dma_kernel while the blocks fit one
+    // round of the CUs (`one_round`, from the expected m-tile count: the
+    // slices of an m-tile then share its token rows in one L2); the plain
+    // grid order (m-tile-major, slices consecutive) otherwise, measured
+    // faster here from 1024 tokens of the MX workload's dims on, where the
+    // twelve 128-wide slices' atomic adds bound the kernel.
+    int lb = blockIdx.x;  // logical block
     if (a.E > kWaveLookupMaxExperts) {
-        if (!find_mtile<32>(a.rv, a.E, blockIdx.x / nslices, mt)) return;
+        if (!find_mtile<32>(a.rv, a.E, lb / nslices, mt)) return;
     } else {
         const TileSamples ts = tile_samples(a.rv, a.E, lane);
-        if (static_cast<int>(blockIdx.x) / nslices >= ts.M) return;
-        find_mtile_wave(a.rv, a.E, ts, blockIdx.x / nslices, lane, mt);
+        const int G = ts.M * nslices;
+        if (static_cast<int>(blockIdx.x) >= G) return;
+        if (one_round) lb = xcd_major(blockIdx.x, G);
+        find_mtile_wave(a.rv, a.E, ts, lb / nslices, lane, mt);
     }
-    const int slice = blockIdx.x % nslices;
+    const int slice = lb % nslices;
     const bool wmover = wave < 2;
     const int mw = wave & 1;
     const int rb = wave & 1, kp = wave >> 1;  // phase 1: row block and K half of this wave
@@ -524,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void mx_fused_dma_kernel(MxArgs a) {
     const int h0 = slice * BH;
     const int DB = a.D / 32, HB = a.H / 32;   // scale bytes per W1 / W2 row
     const int KIT1 = a.D / kMx4KC, NIT1 = F::G1 * KIT1, NG2 = a.D / F::R2, NIT = NIT1 + NG2;
-    const int kc0 = static_cast<int>(blockIdx.x) % KIT1;
-    const int rot = (blockIdx.x / nslices + slice) % NG2;
+    const int kc0 = lb % KIT1;
+    const int rot = (lb / nslices + slice) % NG2;
     if (threadIdx.x < 32) {
         const int m = threadIdx.x;
         const int p = clamp_pair(a.rv.sorted_to_pair[mt.row0 + (m < mt.rows ? m : 0)], a.P);
@@ -883,7 +889,8 @@ bool mx_fused_dma_supported(const MxArgs& a) {
 hipError_t launch_mx_fused_dma(const MxArgs& a, hipStream_t s) {
     constexpr int BH = 128;
     const int64_t blocks = static_cast<int64_t>(mtiles_upper(a.P, a.E, 32)) * (a.H / BH);
-    mx_fused_dma_kernel<BH, 4><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a);
+    const int one_round = expected_mtiles32(a.T, a.k, a.E) * (a.H / BH) <= device_cu_count();
+    mx_fused_dma_kernel<BH, 4><<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(a, one_round);
     return hipGetLastError();
 }
 
