@@ -460,11 +460,15 @@ __global__ __launch_bounds__(kThreads) void dma_kmajor_kernel(Bf16Args a) {
     }
     const int64_t group_stride = static_cast<int64_t>(GEMM1 ? 32 : 64) * K * 2;
     const int KIT = K / 256, NIT = G * KIT;
-    const int rot = GEMM1 ? 0 : static_cast<int>(blockIdx.x) % G;  // as in dma_skinny_kernel
+    const int rot = GEMM1 ? 0 : static_cast<int>(blockIdx.x + blockIdx.x / 8) % G;  // as in dma_skinny_kernel
     // The K chunks are walked from chunk kc0 on, wrapping: the blocks run in
     // near lockstep, and if every block read the same 512-byte column of its
-    // rows at once, the reads would crowd a few HBM channels.
-    const int kc0 = static_cast<int>(blockIdx.x) % KIT;
+    // rows at once, the reads would crowd a few HBM channels. Block b runs on
+    // XCD b % 8, so the start also moves with b / 8: with b % KIT alone the
+    // blocks of one XCD took only KIT / gcd(KIT, 8) distinct starts (one for
+    // GEMM2's 8 chunks at the decode dims), and the XCDs' blocks finished up
+    // to 14% apart; the same for GEMM2's row-group rotation.
+    const int kc0 = static_cast<int>(blockIdx.x + blockIdx.x / 8) % KIT;
     const KmajorPlan pl{G / nsg, G % nsg, KIT};
     // epilogue values of tokens r and 16 + r (every wave stores both tiles)
     int ep[NT];
